@@ -1,0 +1,74 @@
+/*
+ * oracle.h -- interface of the fp64 CPU reference (test infrastructure only; see oracle.c).
+ * All pointers are host pointers.  bf16 tensors are passed as their uint16 bit patterns.
+ * Shapes:
+ *   q            [B][Hq][d]
+ *   k/v_pages    [num_pages][Hkv][C][d]
+ *   page_table   [B][max_chunks]         chunk c of batch b lives in page page_table[b][c]
+ *   gist_k/v     [B][Hkv][gist_cap][g][d] (gist_cap = 0 means M-1)
+ *   gist2_k/v    [B][Hkv][nG][g][d]       nG = ceil((M-1)/J), levels = 2 only
+ *   out          [B][Hq][d],  lse [B][Hq]
+ *   sel          [B][Hkv][k] ascending, -1 padded;  sel_groups [B][Hkv][k2]
+ *   chunk_scores [B][Hkv][M-1] (-inf where a chunk was not scored)
+ *   group_scores [B][Hkv][nG]
+ * Prefill:
+ *   q [B][Hq][T][d], k/v [B][Hkv][T][d], S fp32 [B][Hkv][nb][nb], out [B][Hq][T][d], lse [B][Hq][T],
+ *   sel [B][Hkv][nb][k].
+ */
+#ifndef TCS_ORACLE_H
+#define TCS_ORACLE_H
+#include <stdint.h>
+
+typedef struct {
+    int B, Hq, Hkv, d;
+    int N, C, g, k;
+    int gate;             /* 0 none, 1 SAS log-softmax gate                          */
+    int gists_in_softmax; /* 1: every scored summary enters the softmax; 0: raw only  */
+    int levels, J, k2;
+    int max_chunks;
+    int num_pages;
+    int gist_cap;
+    double scale;         /* <= 0: 1/sqrt(d)                                          */
+} or_decode_shape;
+
+typedef struct {
+    const uint16_t *q, *k_pages, *v_pages;
+    const int32_t* page_table;
+    const uint16_t *gist_k, *gist_v, *gist2_k, *gist2_v;
+    const int32_t* forced_sel;     /* NULL: select by score; else [B][Hkv][k], -1 padded  */
+    const int32_t* forced_groups;  /* NULL or [B][Hkv][k2]                                 */
+    const int32_t* units;          /* NULL: every (b, kv); else n_units flat ids b*Hkv+kv  */
+    int n_units;
+    double* out;
+    double* lse;
+    int32_t* sel;
+    int32_t* sel_groups;
+    double* chunk_scores;
+    double* group_scores;
+    double* weights;               /* optional [B][Hq][weights_cap] softmax weights       */
+    int weights_cap;
+    int32_t* n_tokens;             /* optional [B][Hq] size of the softmax token set       */
+} or_decode_io;
+
+typedef struct {
+    int B, Hq, Hkv, d, T, blk, k, gate;
+    double scale;
+} or_prefill_shape;
+
+typedef struct {
+    const uint16_t *q, *k, *v;
+    const float* S;
+    const int32_t* forced_sel;     /* NULL or [B][Hkv][nb][k]                              */
+    const int32_t* blocks;         /* NULL: all; else flat ids ((b*Hkv+kv)*nb + i)         */
+    int n_blocks;
+    double* out;
+    double* lse;
+    int32_t* sel;
+} or_prefill_io;
+
+int or_decode(const or_decode_shape* p, const or_decode_io* io);
+int or_prefill(const or_prefill_shape* p, const or_prefill_io* io);
+int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand);
+int or_threads(void);
+
+#endif

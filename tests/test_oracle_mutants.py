@@ -1,0 +1,68 @@
+"""Plants plausible mistakes in copies of oracle.c (CPU only) and checks that the pins catch
+every one: a dropped term, a wrong sign, a wrong pooling, a reversed tie-break, an off-by-one
+window.  The default oracle build is untouched; each mutant is compiled into a temp dir."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text, mutated text) -- each original must occur exactly once
+MUTANTS = [
+    ("gate_sign", "gamma = s[j] - lse_s;", "gamma = lse_s - s[j];"),
+    ("gate_unnormalised", "gamma = s[j] - lse_s;", "gamma = s[j];"),
+    ("max_pooling",
+     "    double s = logsumexp(l, G * g);\n",
+     "    double s = l[0]; for (int x = 1; x < G * g; ++x) if (l[x] > s) s = l[x];\n"),
+    ("tie_break_highest", "return (x->c > y->c) - (x->c < y->c);",
+     "return (x->c < y->c) - (x->c > y->c);"),
+    ("drop_current_chunk", "for (int u = 0; u < cur; ++u) {", "for (int u = 0; u < 0; ++u) {"),
+    ("drop_gists", "    if (p->gists_in_softmax) {\n        if (p->levels == 2)\n            for",
+     "    if (0) {\n        if (p->levels == 2)\n            for"),
+    ("diag_not_causal", "for (int u = i * blk; u <= pos; ++u) {",
+     "for (int u = i * blk; u < (i + 1) * blk; ++u) {"),
+    ("diag_off_by_one", "for (int u = i * blk; u <= pos; ++u) {",
+     "for (int u = i * blk; u < pos; ++u) {"),
+    ("prefill_gate_wrong_row", "double gamma = p->gate ? (double)Srow[j] - lse_s : 0.0;",
+     "double gamma = p->gate ? (double)io->S[(unit * nb + j) * nb + i] - lse_s : 0.0;"),
+    ("scale_missing", "    return sigma * s;\n}", "    return s;\n}"),
+    ("lse_log2", "    return m + log(z);\n}\n\ntypedef struct { double s; int c; } scored;",
+     "    return m + log2(z);\n}\n\ntypedef struct { double s; int c; } scored;"),
+    ("top_k_off_by_one", "    int ke = k < n ? k : n;", "    int ke = k < n ? k - 1 : n;"),
+    ("prefill_sees_diagonal_in_selection", "for (int j = 0; j < i; ++j) { s[j]",
+     "for (int j = 0; j < i; ++j) { s[j] = (double)Srow[j + 1]; ids[j] = j; } for (int j = 0; j < 0; ++j) { s[j]"),
+    ("weights_transposed_v", "o[i] += w * bf(t[x].v[i]);", "o[i] += w * bf(t[x].k[i]);"),
+]
+
+
+def _build(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/missing"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / f"lib{name}.so"
+    subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-w",
+                           "-I", os.path.dirname(SRC), "-o", str(so), str(path), "-lm"])
+    return str(so)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    so = _build(tmp_path, name, old, new)
+    prev = oracle.swap_library(so)
+    caught = []
+    try:
+        for pin in pins.PINS:
+            try:
+                pin()
+            except Exception:  # any failure of a pin counts as caught
+                caught.append(pin.__name__)
+    finally:
+        oracle.swap_library(None)
+        if prev is not None:
+            oracle._lib = prev
+    assert caught, f"no pin caught mutant {name}"

@@ -1,0 +1,494 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each pin ties the oracle to something the pages or the mathematics fix:
+  * textbook dense attention (torch scaled_dot_product_attention in float64) for the special
+    cases that reduce to it: every chunk selected, no chunk selected, full causal prefill;
+  * closed forms: pooled chunk score of identical logits, the SAS gate with equal scores
+    (gamma = -log|H|), softmax-set sizes (SSA appendix B.1 counts k gist + kL raw tokens);
+  * invariants: softmax weights sum to one with the gate inside the softmax (SAS abstract),
+    permuting unselected chunks changes nothing, lse is consistent with the weights;
+  * library routines for the selection rule: numpy stable argsort (lowest index on ties);
+  * brute force: a separate numpy evaluation that materialises the token set.
+The functions named pin_* take no fixtures so that test_oracle_mutants.py can re-run them
+against deliberately broken copies of the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from top_chunk_sparse_amd.configs import DecodeConfig, PrefillConfig
+from top_chunk_sparse_amd.synth import make_decode, make_prefill
+from harness import oracle_decode, oracle_prefill, f64
+
+TOL = 1e-12
+
+SMALL = DecodeConfig("pin_small", B=2, Hq=4, Hkv=2, d=16, N=21 * 8 + 5, C=8, g=2, k=3,
+                     n_plant=3, paged=True)
+SMALL_G1 = DecodeConfig("pin_g1", B=1, Hq=2, Hkv=2, d=16, N=30 * 8, C=8, g=1, k=4, n_plant=2)
+SMALL_L2 = DecodeConfig("pin_l2", B=1, Hq=4, Hkv=1, d=16, N=37 * 8 + 3, C=8, g=2, k=5,
+                        levels=2, J=4, k2=2, n_plant=4, plant_groups=2, paged=True)
+PF = PrefillConfig("pin_prefill", B=1, Hq=4, Hkv=2, d=16, T=8 * 10, blk=8, k=3, gate=1)
+
+
+# ----------------------------------------------------------------------------------------
+# brute force (numpy, independent of oracle.c)
+# ----------------------------------------------------------------------------------------
+def _lse(x):
+    x = np.asarray(x, dtype=np.float64).ravel()
+    m = x.max()
+    return m + math.log(np.exp(x - m).sum())
+
+
+def _logical_kv(inp):
+    """K/V as [B][Hkv][M][C][d] float64, through the page table."""
+    c = inp.cfg
+    pt = inp.page_table.cpu().numpy()[:, : c.M]
+    kp, vp = f64(inp.k_pages), f64(inp.v_pages)
+    K = kp[pt].transpose(0, 2, 1, 3, 4)
+    V = vp[pt].transpose(0, 2, 1, 3, 4)
+    return K, V
+
+
+def brute_decode(inp, gists=True):
+    c = inp.cfg
+    G, H, sig = c.G, c.H, 1.0 / math.sqrt(c.d)
+    q = f64(inp.q)
+    K, V = _logical_kv(inp)
+    gk, gv = f64(inp.gist_k), f64(inp.gist_v)
+    out = np.zeros((c.B, c.Hq, c.d))
+    lse = np.zeros((c.B, c.Hq))
+    sels = np.full((c.B, c.Hkv, c.k), -1, np.int32)
+    for b in range(c.B):
+        for kv in range(c.Hkv):
+            qg = q[b, kv * G:(kv + 1) * G]
+            Ks, Vs, bias = [], [], []
+            if c.levels == 2:
+                g2k, g2v = f64(inp.gist2_k)[b, kv], f64(inp.gist2_v)[b, kv]
+                s2 = np.array([_lse(sig * qg @ g2k[r].T) for r in range(c.nG)])
+                order = sorted(range(c.nG), key=lambda r: (-s2[r], r))
+                groups = sorted(order[: c.k2])
+                cand = [x for r in groups for x in range(r * c.J, min((r + 1) * c.J, H))]
+                if gists:
+                    Ks += [g2k.reshape(-1, c.d)]
+                    Vs += [g2v.reshape(-1, c.d)]
+                    bias += [0.0] * (c.nG * c.g)
+            else:
+                cand = list(range(H))
+            s = {x: _lse(sig * qg @ gk[b, kv, x].T) for x in cand}
+            order = sorted(cand, key=lambda x: (-s[x], x))
+            sel = sorted(order[: c.k])
+            sels[b, kv, : len(sel)] = sel
+            lse_s = _lse([s[x] for x in cand]) if cand else 0.0
+            if gists:
+                for x in cand:
+                    Ks.append(gk[b, kv, x])
+                    Vs.append(gv[b, kv, x])
+                    bias += [0.0] * c.g
+            for x in sel:
+                Ks.append(K[b, kv, x])
+                Vs.append(V[b, kv, x])
+                bias += [(s[x] - lse_s) if c.gate else 0.0] * c.C
+            Ks.append(K[b, kv, H, : c.cur_len])
+            Vs.append(V[b, kv, H, : c.cur_len])
+            bias += [0.0] * c.cur_len
+            Kt, Vt, bt = np.concatenate(Ks), np.concatenate(Vs), np.array(bias)
+            for h in range(G):
+                lam = sig * Kt @ qg[h] + bt
+                m = lam.max()
+                w = np.exp(lam - m)
+                out[b, kv * G + h] = w @ Vt / w.sum()
+                lse[b, kv * G + h] = m + math.log(w.sum())
+    return out, lse, sels
+
+
+def brute_prefill(inp):
+    c = inp.cfg
+    G, nb, blk, sig = c.G, c.nb, c.blk, 1.0 / math.sqrt(c.d)
+    q, K, V, S = f64(inp.q), f64(inp.k), f64(inp.v), inp.S.double().numpy()
+    out = np.zeros(q.shape)
+    lse = np.zeros(q.shape[:3])
+    for b in range(c.B):
+        for kv in range(c.Hkv):
+            for i in range(nb):
+                row = S[b, kv, i, :i]
+                sel = sorted(sorted(range(i), key=lambda j: (-row[j], j))[: c.k])
+                ls = _lse(row) if i > 0 else 0.0
+                for h in range(kv * G, (kv + 1) * G):
+                    for r in range(blk):
+                        p = i * blk + r
+                        idx = [u for j in sel for u in range(j * blk, (j + 1) * blk)]
+                        bias = [(row[j] - ls) if c.gate else 0.0 for j in sel for _ in range(blk)]
+                        idx += list(range(i * blk, p + 1))
+                        bias += [0.0] * (r + 1)
+                        lam = sig * K[b, kv, idx] @ q[b, h, p] + np.array(bias)
+                        m = lam.max()
+                        w = np.exp(lam - m)
+                        out[b, h, p] = w @ V[b, kv, idx] / w.sum()
+                        lse[b, h, p] = m + math.log(w.sum())
+    return out, lse
+
+
+# ----------------------------------------------------------------------------------------
+# textbook attention helper (float64 SDPA)
+# ----------------------------------------------------------------------------------------
+def sdpa(qv, Kt, Vt, bias=None):
+    """softmax(q K^T / sqrt(d) + bias) V for one query vector; also returns the natural log
+    normaliser computed by torch.logsumexp."""
+    qt = torch.from_numpy(np.asarray(qv, np.float64))[None, None, None]
+    kt = torch.from_numpy(np.asarray(Kt, np.float64))[None, None]
+    vt = torch.from_numpy(np.asarray(Vt, np.float64))[None, None]
+    mask = None if bias is None else torch.from_numpy(np.asarray(bias, np.float64))[None, None, None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)[0, 0, 0].numpy()
+    lam = (kt[0, 0] @ qt[0, 0, 0]) / math.sqrt(qt.shape[-1])
+    if mask is not None:
+        lam = lam + mask[0, 0, 0]
+    return o, float(torch.logsumexp(lam, 0))
+
+
+# ----------------------------------------------------------------------------------------
+# pins
+# ----------------------------------------------------------------------------------------
+def pin_brute_force_decode():
+    for cfg in (SMALL, SMALL.with_(gate=1), SMALL_G1, SMALL_L2):
+        inp = make_decode(cfg, seed=11, max_chunks=cfg.M + 3, extra_pages=2)
+        r = oracle_decode(inp)
+        o, l, s = brute_decode(inp)
+        assert np.array_equal(r.sel, s), cfg.name
+        assert np.abs(r.out - o).max() < TOL, cfg.name
+        assert np.abs(r.lse - l).max() < TOL, cfg.name
+
+
+def pin_k_all_is_dense():
+    """Every chunk selected: softmax over the whole cache (all gists + every raw token) is
+    textbook attention; without gists it is dense attention over the N raw tokens."""
+    cfg = SMALL.with_(k=SMALL.H, B=1)
+    inp = make_decode(cfg, seed=5)
+    K, V = _logical_kv(inp)
+    q, gk, gv = f64(inp.q), f64(inp.gist_k), f64(inp.gist_v)
+    for gists in (True, False):
+        r = oracle_decode(inp, gists_in_softmax=gists)
+        assert np.array_equal(r.sel[0, 0], np.arange(cfg.H))
+        for h in range(cfg.Hq):
+            kv = h // cfg.G
+            raw_k = K[0, kv].reshape(-1, cfg.d)[: cfg.N]
+            raw_v = V[0, kv].reshape(-1, cfg.d)[: cfg.N]
+            if gists:
+                raw_k = np.concatenate([gk[0, kv].reshape(-1, cfg.d), raw_k])
+                raw_v = np.concatenate([gv[0, kv].reshape(-1, cfg.d), raw_v])
+            o, l = sdpa(q[0, h], raw_k, raw_v)
+            assert np.abs(r.out[0, h] - o).max() < TOL
+            assert abs(r.lse[0, h] - l) < TOL
+
+
+def pin_k_zero_is_gists_plus_current():
+    for gate in (0, 1):
+        cfg = SMALL.with_(k=0, gate=gate, B=1)
+        inp = make_decode(cfg, seed=6)
+        K, V = _logical_kv(inp)
+        q, gk, gv = f64(inp.q), f64(inp.gist_k), f64(inp.gist_v)
+        r = oracle_decode(inp)
+        for h in range(cfg.Hq):
+            kv = h // cfg.G
+            kt = np.concatenate([gk[0, kv].reshape(-1, cfg.d), K[0, kv, cfg.H, : cfg.cur_len]])
+            vt = np.concatenate([gv[0, kv].reshape(-1, cfg.d), V[0, kv, cfg.H, : cfg.cur_len]])
+            o, l = sdpa(q[0, h], kt, vt)
+            assert np.abs(r.out[0, h] - o).max() < TOL
+            assert abs(r.lse[0, h] - l) < TOL
+
+
+def pin_weights_sum_to_one_and_reconstruct():
+    for gate in (0, 1):
+        cfg = SMALL.with_(gate=gate, B=1)
+        inp = make_decode(cfg, seed=7)
+        cap = cfg.H * cfg.g + cfg.k * cfg.C + cfg.C
+        r = oracle_decode(inp, weights_cap=cap)
+        K, V = _logical_kv(inp)
+        gv = f64(inp.gist_v)
+        for h in range(cfg.Hq):
+            kv = h // cfg.G
+            n = r.n_tokens[0, h]
+            w = r.weights[0, h, :n]
+            assert abs(w.sum() - 1.0) < TOL
+            assert (w > 0).all()
+            # token order: gists (chunk, t), selected chunks ascending, current chunk
+            vt = [gv[0, kv].reshape(-1, cfg.d)]
+            vt += [V[0, kv, c] for c in r.sel[0, kv] if c >= 0]
+            vt += [V[0, kv, cfg.H, : cfg.cur_len]]
+            assert np.abs(w @ np.concatenate(vt) - r.out[0, h]).max() < TOL
+
+
+def pin_permutation_invariance():
+    cfg = SMALL.with_(gate=1)
+    inp = make_decode(cfg, seed=8)
+    r = oracle_decode(inp)
+    rng = np.random.default_rng(0)
+    pt = inp.page_table.clone()
+    gk, gv = inp.gist_k.clone(), inp.gist_v.clone()
+    for b in range(cfg.B):
+        # one permutation per batch row, over chunks no KV head of that row selected
+        chosen = set(r.sel[b].ravel().tolist())
+        free = [c for c in range(cfg.H) if c not in chosen]
+        perm = rng.permutation(free)
+        pt[b, free] = inp.page_table[b, perm]
+        gk[b, :, free] = inp.gist_k[b, :, perm]
+        gv[b, :, free] = inp.gist_v[b, :, perm]
+    from dataclasses import replace
+    inp2 = replace(inp, page_table=pt, gist_k=gk, gist_v=gv)
+    r2 = oracle_decode(inp2)
+    assert np.array_equal(r.sel, r2.sel)
+    assert np.abs(r.out - r2.out).max() < TOL
+    assert np.abs(r.lse - r2.lse).max() < TOL
+
+
+def pin_selection_single_gist_single_head():
+    """G = g = 1: the chunk score is sigma q . Kg and the choice is numpy's stable argsort."""
+    inp = make_decode(SMALL_G1, seed=9)
+    r = oracle_decode(inp)
+    q, gk = f64(inp.q), f64(inp.gist_k)
+    for kv in range(SMALL_G1.Hkv):
+        s = gk[0, kv, :, 0] @ q[0, kv] / math.sqrt(SMALL_G1.d)
+        assert np.abs(r.chunk_scores[0, kv] - s).max() < TOL
+        want = np.sort(np.argsort(-s, kind="stable")[: SMALL_G1.k])
+        assert np.array_equal(r.sel[0, kv], want)
+
+
+def pin_pooled_score_closed_form():
+    """Identical queries in a group and identical gists in a chunk: the G*g logits all equal
+    x_c, so the pooled log-sum-exp is x_c + log(G*g)."""
+    cfg = SMALL.with_(B=1, Hkv=1, Hq=4)
+    inp = make_decode(cfg, seed=10)
+    inp.q[0, 1:] = inp.q[0, 0]
+    inp.gist_k[0, 0, :, 1:] = inp.gist_k[0, 0, :, :1]
+    r = oracle_decode(inp)
+    x = f64(inp.gist_k)[0, 0, :, 0] @ f64(inp.q)[0, 0] / math.sqrt(cfg.d)
+    assert np.abs(r.chunk_scores[0, 0] - (x + math.log(cfg.G * cfg.g))).max() < TOL
+
+
+def pin_pooled_score_dominant_term():
+    """One gist logit far above the rest: the pooled score tends to that logit."""
+    cfg = SMALL.with_(B=1, Hkv=1, Hq=2, g=2)
+    inp = make_decode(cfg, seed=12)
+    q = f64(inp.q)[0]
+    inp.gist_k.zero_()
+    c = 5
+    inp.gist_k[0, 0, c, 1] = torch.from_numpy(q[1] * 8.0).to(torch.bfloat16)
+    r = oracle_decode(inp)
+    g = f64(inp.gist_k)[0, 0, c]
+    logits = np.sort((q @ g.T).ravel() / math.sqrt(cfg.d))
+    big, second = logits[-1], logits[-2]
+    # max <= LSE <= max + log(1 + (n-1) e^(second-max))
+    gap = r.chunk_scores[0, 0, c] - big
+    assert 0 <= gap <= math.log1p((cfg.G * cfg.g - 1) * math.exp(second - big)) + 1e-12
+    assert gap < 1e-6
+    others = np.delete(r.chunk_scores[0, 0], c)
+    assert np.abs(others - math.log(cfg.G * cfg.g)).max() < TOL   # all-zero gists: logits 0
+
+
+def pin_tie_break_lowest_index():
+    cfg = SMALL.with_(B=1, k=3)
+    inp = make_decode(cfg, seed=13)
+    # chunks 2, 6, 9, 14 get the same (largest) gists -> exact ties; lowest three win
+    for c in (6, 9, 14):
+        inp.gist_k[0, :, c] = inp.gist_k[0, :, 2]
+    for kv in range(cfg.Hkv):
+        G = cfg.G
+        qs = inp.q[0, kv * G:(kv + 1) * G].float().sum(0)
+        inp.gist_k[0, kv, 2] = (qs * 3).to(torch.bfloat16)
+        for c in (6, 9, 14):
+            inp.gist_k[0, kv, c] = inp.gist_k[0, kv, 2]
+    r = oracle_decode(inp)
+    for kv in range(cfg.Hkv):
+        assert r.sel[0, kv].tolist() == [2, 6, 9]
+
+
+def pin_gate_equal_scores_closed_form():
+    """All historical chunks score the same: the SAS gate is -log|H| on every selected raw
+    token, ties go to the lowest indices, so the result is textbook attention with a
+    constant additive bias of -log|H| on chunks 0..k-1."""
+    cfg = SMALL.with_(B=1, gate=1, k=3)
+    inp = make_decode(cfg, seed=14)
+    inp.gist_k[0, :, :] = inp.gist_k[0, :, :1]
+    r = oracle_decode(inp)
+    K, V = _logical_kv(inp)
+    q, gk, gv = f64(inp.q), f64(inp.gist_k), f64(inp.gist_v)
+    gamma = -math.log(cfg.H)
+    for h in range(cfg.Hq):
+        kv = h // cfg.G
+        assert r.sel[0, kv].tolist() == list(range(cfg.k))
+        kt = np.concatenate([gk[0, kv].reshape(-1, cfg.d), K[0, kv, : cfg.k].reshape(-1, cfg.d),
+                             K[0, kv, cfg.H, : cfg.cur_len]])
+        vt = np.concatenate([gv[0, kv].reshape(-1, cfg.d), V[0, kv, : cfg.k].reshape(-1, cfg.d),
+                             V[0, kv, cfg.H, : cfg.cur_len]])
+        bias = np.zeros(len(kt))
+        bias[cfg.H * cfg.g: cfg.H * cfg.g + cfg.k * cfg.C] = gamma
+        o, l = sdpa(q[0, h], kt, vt, bias)
+        assert np.abs(r.out[0, h] - o).max() < TOL
+        assert abs(r.lse[0, h] - l) < TOL
+
+
+def pin_token_counts():
+    """Softmax-set sizes: (M-1) g gists + k_eff C raw + the current chunk; raw tokens only
+    without gists; at two levels nG g + |candidates| g + k_eff C + current."""
+    cfg = SMALL.with_(B=1)
+    inp = make_decode(cfg, seed=15)
+    r = oracle_decode(inp)
+    assert (r.n_tokens == cfg.H * cfg.g + cfg.k * cfg.C + cfg.cur_len).all()
+    r = oracle_decode(inp, gists_in_softmax=False)
+    assert (r.n_tokens == cfg.k * cfg.C + cfg.cur_len).all()
+    r = oracle_decode(inp, k=cfg.H + 5)
+    assert (r.n_tokens == cfg.H * cfg.g + cfg.H * cfg.C + cfg.cur_len).all()
+    inp2 = make_decode(SMALL_L2, seed=15)
+    r2 = oracle_decode(inp2)
+    c2 = SMALL_L2
+    cand = sum(min(c2.H, (g + 1) * c2.J) - g * c2.J for g in r2.sel_groups[0, 0])
+    assert (r2.n_tokens == c2.nG * c2.g + cand * c2.g + c2.k * c2.C + c2.cur_len).all()
+    # the pages' per-step count: k selected gists + k*L raw when the set is k*(1 + L) (g = 1)
+    assert oracle.token_count(N=8 * 10, C_=8, g=1, k_eff=3, gists_in_softmax=False) == 3 * 8 + 8
+
+
+def pin_two_level_everything_selected_is_dense():
+    c = SMALL_L2.with_(k2=SMALL_L2.nG, k=SMALL_L2.H)
+    inp = make_decode(c, seed=16)
+    r = oracle_decode(inp)
+    K, V = _logical_kv(inp)
+    q = f64(inp.q)
+    for h in range(c.Hq):
+        kt = np.concatenate([f64(inp.gist2_k)[0, 0].reshape(-1, c.d),
+                             f64(inp.gist_k)[0, 0].reshape(-1, c.d),
+                             K[0, 0].reshape(-1, c.d)[: c.N]])
+        vt = np.concatenate([f64(inp.gist2_v)[0, 0].reshape(-1, c.d),
+                             f64(inp.gist_v)[0, 0].reshape(-1, c.d),
+                             V[0, 0].reshape(-1, c.d)[: c.N]])
+        o, l = sdpa(q[0, h], kt, vt)
+        assert np.abs(r.out[0, h] - o).max() < TOL
+        assert abs(r.lse[0, h] - l) < TOL
+
+
+def pin_two_level_all_groups_same_choice_as_one_level():
+    c = SMALL_L2.with_(k2=SMALL_L2.nG)
+    inp = make_decode(c, seed=17)
+    r2 = oracle_decode(inp)
+    r1 = oracle_decode(inp, levels=1, J=0, k2=0, gist2_k=None, gist2_v=None)
+    assert np.array_equal(r1.sel, r2.sel)
+    assert np.abs(r1.chunk_scores - r2.chunk_scores).max() < TOL
+
+
+def pin_two_level_group_selection():
+    """Level-2 selection on group scores with one gist and one head reduces to argsort."""
+    c = SMALL_L2.with_(Hq=1, g=1, n_plant=2, plant_groups=1)
+    inp = make_decode(c, seed=18)
+    r = oracle_decode(inp)
+    s2 = f64(inp.gist2_k)[0, 0, :, 0] @ f64(inp.q)[0, 0] / math.sqrt(c.d)
+    assert np.abs(r.group_scores[0, 0] - s2).max() < TOL
+    assert np.array_equal(r.sel_groups[0, 0], np.sort(np.argsort(-s2, kind="stable")[: c.k2]))
+    members = {x for gr in r.sel_groups[0, 0] for x in range(gr * c.J, min(c.H, (gr + 1) * c.J))}
+    assert set(r.sel[0, 0].tolist()) <= members
+    assert np.isinf(r.chunk_scores[0, 0, [x for x in range(c.H) if x not in members]]).all()
+
+
+def pin_brute_force_prefill():
+    for gate in (0, 1):
+        cfg = PF.with_(gate=gate)
+        inp = make_prefill(cfg, seed=19)
+        r = oracle_prefill(inp)
+        o, l = brute_prefill(inp)
+        assert np.abs(r.out - o).max() < TOL
+        assert np.abs(r.lse - l).max() < TOL
+
+
+def pin_prefill_dense_causal():
+    """Gate off and k >= blocks: textbook causal attention (is_causal)."""
+    cfg = PF.with_(gate=0, k=PF.nb)
+    inp = make_prefill(cfg, seed=20)
+    r = oracle_prefill(inp)
+    q, k, v = (torch.from_numpy(f64(t)) for t in (inp.q, inp.k, inp.v))
+    G = cfg.G
+    k = k.repeat_interleave(G, 1)
+    v = v.repeat_interleave(G, 1)
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True).numpy()
+    assert np.abs(r.out - o).max() < TOL
+    lam = (q @ k.transpose(-1, -2)) / math.sqrt(cfg.d)
+    lam = lam.masked_fill(torch.ones(cfg.T, cfg.T, dtype=torch.bool).triu(1), float("-inf"))
+    assert np.abs(r.lse - torch.logsumexp(lam, -1).numpy()).max() < TOL
+
+
+def pin_prefill_gate_block_bias():
+    """Gate on and every earlier block kept: causal attention with an additive block bias of
+    log_softmax over the selector row (torch.log_softmax), 0 on the diagonal block."""
+    cfg = PF.with_(gate=1, k=PF.nb)
+    inp = make_prefill(cfg, seed=21)
+    r = oracle_prefill(inp)
+    q, k, v = (torch.from_numpy(f64(t)) for t in (inp.q, inp.k, inp.v))
+    G, nb, blk = cfg.G, cfg.nb, cfg.blk
+    S = inp.S.double()
+    for kv in range(cfg.Hkv):
+        bias = torch.full((cfg.T, cfg.T), float("-inf"), dtype=torch.float64)
+        for i in range(nb):
+            rows = slice(i * blk, (i + 1) * blk)
+            if i > 0:
+                ls = torch.log_softmax(S[0, kv, i, :i], 0)
+                bias[rows, : i * blk] = ls.repeat_interleave(blk)[None]
+            bias[rows, rows] = torch.zeros(blk, blk, dtype=torch.float64).masked_fill(
+                torch.ones(blk, blk, dtype=torch.bool).triu(1), float("-inf"))
+        for h in range(kv * G, (kv + 1) * G):
+            o = F.scaled_dot_product_attention(q[0, h][None], k[0, kv][None], v[0, kv][None],
+                                               attn_mask=bias[None])[0].numpy()
+            assert np.abs(r.out[0, h] - o).max() < TOL
+
+
+def pin_prefill_selection_argsort():
+    inp = make_prefill(PF.with_(k=3), seed=22)
+    r = oracle_prefill(inp)
+    S = inp.S.numpy()
+    for kv in range(PF.Hkv):
+        for i in range(PF.nb):
+            want = np.sort(np.argsort(-S[0, kv, i, :i], kind="stable")[: min(3, i)])
+            got = r.sel[0, kv, i]
+            assert np.array_equal(got[: len(want)], want)
+            assert (got[len(want):] == -1).all()
+
+
+PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+def test_forced_selection_matches_free_selection():
+    inp = make_decode(SMALL.with_(gate=1), seed=23)
+    r = oracle_decode(inp)
+    r2 = oracle_decode(inp, forced_sel=np.ascontiguousarray(r.sel))
+    assert np.array_equal(r.out, r2.out)
+    pin = make_prefill(PF, seed=24)
+    p1 = oracle_prefill(pin)
+    p2 = oracle_prefill(pin, forced_sel=np.ascontiguousarray(p1.sel))
+    assert np.array_equal(p1.out, p2.out)
+
+
+def test_unit_subset():
+    inp = make_decode(SMALL, seed=25)
+    r = oracle_decode(inp)
+    r2 = oracle_decode(inp, units=[3, 0])
+    for u in (0, 3):
+        b, kv = divmod(u, SMALL.Hkv)
+        G = SMALL.G
+        assert np.array_equal(r.out[b, kv * G:(kv + 1) * G], r2.out[b, kv * G:(kv + 1) * G])
+    assert np.isnan(r2.out[0, 2]).all()
+
+
+def test_bad_page_gives_nan():
+    inp = make_decode(SMALL, seed=26)
+    r = oracle_decode(inp)
+    pt = inp.page_table.clone()
+    pt[1, r.sel[1, 0, 0]] = 10 ** 6
+    from dataclasses import replace
+    r2 = oracle_decode(replace(inp, page_table=pt))
+    G = SMALL.G
+    assert np.isnan(r2.out[1, :G]).all() and np.isnan(r2.lse[1, :G]).all()
+    assert not np.isnan(r2.out[0]).any()
