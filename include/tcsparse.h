@@ -1,0 +1,184 @@
+/*
+ * tcsparse.h -- C ABI of the MI355X (gfx950) query-guided chunk-sparse attention library
+ * (libtcsparse.so).
+ *
+ * What is computed.
+ *   Decode ("Simplified Sparse Attention via Gist Tokens", sections 3.2, 3.3, 3.5 and
+ *   appendix B; "SAS: Simple Attention Sparsification", abstract).  For each batch row b and
+ *   KV head kv (a "unit"), with G = Hq / Hkv query heads h = kv*G .. kv*G+G-1 reading that
+ *   KV head, sigma = scale (0 -> 1/sqrt(d)), M = ceil(N / C) chunks, historical chunks
+ *   H = {0 .. M-2} and the current chunk c* = M-1 holding tokens [(M-1)C, N):
+ *     1. gist logits l[h][c][t] = sigma * q[b][h] . gist_k[b][kv][c][t] for c in H, t < g
+ *        (section 3.2: chunk relevance from query-key products against learned gist keys);
+ *     2. chunk score s[c] = log sum_{h, t} exp(l[h][c][t])  (the group's pooled
+ *        query->gist attention mass, in log form);
+ *     3. sel = the min(k, |H|) chunks with the largest s, equal scores broken toward the lower
+ *        chunk index, reported in ascending order (section 3.3: top-k selection);
+ *     4. SAS gate (gate_mode = TCS_GATE_SAS): gamma[c] = s[c] - log sum_{c' in H} exp(s[c'])
+ *        is added to the logit of every raw token of a selected chunk c (the gate sits inside
+ *        the softmax in log form; the current chunk and the gists carry no gate);
+ *     5. one softmax per query head over: every historical gist (key gist_k, value gist_v,
+ *        bias 0), the raw tokens of every selected chunk (bias gamma or 0), and the raw tokens
+ *        of the current chunk (bias 0, always kept):
+ *          lambda_x = sigma * q . k_x + bias_x,  out = sum_x softmax(lambda)_x v_x,
+ *          lse = log sum_x exp(lambda_x)  (natural log, gate included).
+ *   Two levels (levels = 2; section 3.5 and appendix B.2): level-2 gists summarise groups of J
+ *   consecutive historical chunks.  The group scores s2[r] (step 2 over gist2_k) pick the top
+ *   k2 groups; the member chunks of the chosen groups are the candidates; steps 1-3 run over
+ *   the candidates only.  The softmax set is: every level-2 gist, the gists of every
+ *   candidate chunk, the raw tokens of the selected chunks and of the current chunk.  The SAS
+ *   gate is not defined for two levels (TCS_ERR_UNSUPPORTED).
+ *
+ *   Prefill ("SAS: Simple Attention Sparsification", abstract: FlashAttention-style forward
+ *   with the gate inside the softmax).  Query block i (blk tokens) of KV head kv keeps the
+ *   top min(k, i) earlier blocks j < i by the selector row S[b][kv][i][j] (ties to the lower
+ *   j) plus its own (diagonal) block, which is token-causal.  Gate (gate_mode = SAS):
+ *   gamma[i][j] = S[i][j] - log sum_{j' < i} exp(S[i][j']) on every key of selected block j;
+ *   bias 0 on the diagonal block.  out = softmax(sigma q K^T + bias) V, lse natural log.
+ *
+ * Layouts (row-major, innermost last).  bf16 = IEEE bfloat16 bit patterns.
+ *   q            bf16 [B][Hq][d]
+ *   k_pages      bf16 [num_pages][Hkv][C][d]   one page holds one chunk of every KV head
+ *   v_pages      bf16 [num_pages][Hkv][C][d]
+ *   page_table   int32 [B][max_chunks]          page of chunk c of batch row b
+ *   gist_k/v     bf16 [B][Hkv][gist_cap][g][d]  rows c < M-1 are read
+ *   gist2_k/v    bf16 [B][Hkv][nG][g][d]        nG = ceil((M-1) / J); levels = 2 only
+ *   out          fp32 [B][Hq][d]
+ *   lse          fp32 [B][Hq]                   optional (NULL)
+ *   sel          int32 [B][Hkv][k]              optional; ascending chunk ids, -1 padded
+ *   sel_groups   int32 [B][Hkv][k2]             optional; levels = 2
+ *   chunk_scores fp32 [B][Hkv][M-1]             optional; -inf for chunks not scored
+ *   Prefill: q bf16 [B][Hq][T][d]; k, v bf16 [B][Hkv][T][d]; S fp32 [B][Hkv][nb][nb] with
+ *   nb = T / blk (entries j >= i are ignored); out fp32 [B][Hq][T][d]; lse fp32 [B][Hq][T]
+ *   (optional); sel int32 [B][Hkv][nb][k] (optional, ascending, -1 padded).
+ *
+ * Ownership, streams, errors.
+ *   All tensor pointers are device pointers owned by the caller, as is the workspace (size
+ *   from tcs_*_workspace_size, 256-byte aligned).  The library allocates, frees and
+ *   synchronises nothing and keeps no global state; every call only enqueues kernels on
+ *   `stream` and returns.  Calls sharing a workspace must be ordered on one stream.
+ *   Argument errors return before any device work and leave every output untouched.  A
+ *   failed launch returns TCS_ERR_HIP.  Inputs must be finite (NaN/Inf inputs give
+ *   unspecified results).  A page id outside [0, num_pages) is never read: the heads of the
+ *   affected unit get NaN in out and lse.
+ *   k larger than the number of candidates is clamped (that is how "all chunks" is asked
+ *   for); k = 0 keeps only the gists and the current chunk.  Results are deterministic:
+ *   no floating-point atomics; the same inputs give bitwise-identical outputs.
+ *
+ * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; prefill blk = 64
+ * and T a multiple of blk.  Other shapes return TCS_ERR_UNSUPPORTED.
+ */
+#ifndef TCSPARSE_H
+#define TCSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TCS_ABI_VERSION 1
+
+typedef enum {
+    TCS_OK = 0,
+    TCS_ERR_NULL = 1,         /* a required pointer is NULL                          */
+    TCS_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes                  */
+    TCS_ERR_UNSUPPORTED = 3,  /* valid, but not built (see supported shapes above)   */
+    TCS_ERR_WORKSPACE = 4,    /* workspace NULL, misaligned or smaller than required  */
+    TCS_ERR_HIP = 5           /* a kernel launch failed                               */
+} tcs_status;
+
+enum { TCS_GATE_NONE = 0, TCS_GATE_SAS = 1 };
+
+typedef struct {
+    int32_t struct_size;   /* = sizeof(tcs_decode_params) */
+    int32_t B, Hq, Hkv, d;
+    int32_t N;             /* tokens in the cache, current token included (>= 1)          */
+    int32_t C;             /* chunk size = page size (tokens)                             */
+    int32_t g;             /* gists per chunk                                             */
+    int32_t k;             /* chunks to select (>= 0; clamped to the candidate count)     */
+    int32_t gate_mode;     /* TCS_GATE_NONE or TCS_GATE_SAS                               */
+    int32_t levels;        /* 1, or 2 for gist-of-gist routing                            */
+    int32_t J;             /* levels = 2: chunks per level-2 group                        */
+    int32_t k2;            /* levels = 2: groups to select                                */
+    int32_t max_chunks;    /* page_table row stride, >= M                                 */
+    int32_t num_pages;     /* pages in k_pages / v_pages                                  */
+    int32_t gist_cap;      /* chunk capacity of gist_k/v per (b, kv); 0 means M-1          */
+    float scale;           /* logit scale; 0 means 1/sqrt(d)                              */
+} tcs_decode_params;
+
+/* Host-only: bytes of workspace sparse_attn_decode needs for these parameters. */
+tcs_status tcs_decode_workspace_size(const tcs_decode_params* p, size_t* bytes);
+
+/* Chunk-sparse decode attention for one decode step of every (b, query head); see above. */
+tcs_status sparse_attn_decode(const tcs_decode_params* p,
+                              const void* q,
+                              const void* k_pages, const void* v_pages,
+                              const int32_t* page_table,
+                              const void* gist_k, const void* gist_v,
+                              const void* gist2_k, const void* gist2_v,
+                              float* out, float* lse,
+                              int32_t* sel, int32_t* sel_groups, float* chunk_scores,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Profiling variant of sparse_attn_decode: identical work and results, and in addition it
+ * records caller-created HIP events (hipEvent_t, passed as void*) on `stream`: events[0]
+ * before the first kernel and events[i] after the i-th kernel of the sequence.  levels = 1:
+ * 1 gist scoring, 2 chunk selection, 3 chunk attention, 4 combine.  levels = 2: 1 level-2
+ * scoring, 2 group selection, 3 candidate scoring, 4 chunk selection, 5 chunk attention,
+ * 6 combine.  Entries beyond n_events, or NULL entries, are skipped.  For profiling tools:
+ * recording events between kernels adds a little time to the call. */
+tcs_status sparse_attn_decode_timed(const tcs_decode_params* p,
+                                    const void* q,
+                                    const void* k_pages, const void* v_pages,
+                                    const int32_t* page_table,
+                                    const void* gist_k, const void* gist_v,
+                                    const void* gist2_k, const void* gist2_v,
+                                    float* out, float* lse,
+                                    int32_t* sel, int32_t* sel_groups, float* chunk_scores,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* const* events, int n_events);
+
+/* Number of kernels sparse_attn_decode enqueues for these parameters (4 or 6), -1 if the
+ * parameters are invalid.  Host-only. */
+int tcs_decode_stage_count(const tcs_decode_params* p);
+
+typedef struct {
+    int32_t struct_size;   /* = sizeof(tcs_prefill_params) */
+    int32_t B, Hq, Hkv, d;
+    int32_t T;             /* tokens (multiple of blk)                                    */
+    int32_t blk;           /* block size (64)                                             */
+    int32_t k;             /* earlier blocks kept per query block (>= 0)                  */
+    int32_t gate_mode;     /* TCS_GATE_NONE or TCS_GATE_SAS                               */
+    float scale;           /* 0 means 1/sqrt(d)                                           */
+} tcs_prefill_params;
+
+tcs_status tcs_prefill_workspace_size(const tcs_prefill_params* p, size_t* bytes);
+
+/* Block-sparse causal attention forward with the SAS gate; see above. */
+tcs_status sparse_attn_prefill(const tcs_prefill_params* p,
+                               const void* q, const void* k, const void* v,
+                               const float* S,
+                               float* out, float* lse, int32_t* sel,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Profiling variant of sparse_attn_prefill (see sparse_attn_decode_timed): events[0] before
+ * the first kernel, events[1] after block selection, events[2] after the attention forward. */
+tcs_status sparse_attn_prefill_timed(const tcs_prefill_params* p,
+                                     const void* q, const void* k, const void* v,
+                                     const float* S,
+                                     float* out, float* lse, int32_t* sel,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events, int n_events);
+
+/* Static string naming a status code. */
+const char* tcs_status_str(tcs_status s);
+
+/* TCS_ABI_VERSION of the built library. */
+int tcs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TCSPARSE_H */

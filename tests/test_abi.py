@@ -1,0 +1,148 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the header
+declares, and rejects bad arguments before touching the device (so these run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+from top_chunk_sparse_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tcsparse.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:tcs_status|const char\s*\*|int)\s+\**\s*(\w+)\s*\(", src, flags=re.M)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"sparse_attn_decode", "sparse_attn_prefill", "tcs_status_str",
+                          "tcs_abi_version", "tcs_decode_workspace_size",
+                          "tcs_prefill_workspace_size"}
+    lib = ops.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ops.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    assert ops.lib().tcs_abi_version() == 1
+    for code in range(6):
+        assert ops.status_str(code)
+    assert ops.status_str(99) == "unknown status"
+
+
+def P(**kw):
+    base = dict(B=2, Hq=8, Hkv=2, d=128, N=1000, C_=64, g=4, k=4, num_pages=32)
+    base.update(kw)
+    return ops.decode_params(**base)
+
+
+def test_workspace_size_grows_with_work():
+    a = ops.decode_workspace_size(P())
+    b = ops.decode_workspace_size(P(k=16))
+    c = ops.decode_workspace_size(P(B=4, num_pages=64))
+    assert 0 < a < b and a < c
+    assert a % 256 == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), ops.TCS_ERR_SHAPE),
+    (dict(d=96), ops.TCS_ERR_UNSUPPORTED),
+    (dict(Hq=24, Hkv=2), ops.TCS_ERR_UNSUPPORTED),       # G = 12
+    (dict(k=-1), ops.TCS_ERR_SHAPE),
+    (dict(N=0), ops.TCS_ERR_SHAPE),
+    (dict(C_=0), ops.TCS_ERR_SHAPE),
+    (dict(g=0), ops.TCS_ERR_SHAPE),
+    (dict(g=65), ops.TCS_ERR_UNSUPPORTED),
+    (dict(max_chunks=10), ops.TCS_ERR_SHAPE),            # M = 16
+    (dict(gist_cap=3), ops.TCS_ERR_SHAPE),
+    (dict(levels=3), ops.TCS_ERR_SHAPE),
+    (dict(levels=2, J=0), ops.TCS_ERR_SHAPE),
+    (dict(levels=2, J=4, k2=2, gate=1), ops.TCS_ERR_UNSUPPORTED),
+    (dict(levels=2, J=4, k2=65), ops.TCS_ERR_UNSUPPORTED),
+    (dict(gate=2), ops.TCS_ERR_SHAPE),
+    (dict(scale=-1.0), ops.TCS_ERR_SHAPE),
+    (dict(num_pages=0), ops.TCS_ERR_SHAPE),
+])
+def test_decode_rejects_bad_params(kw, code):
+    p = P(**kw)
+    n = C.c_size_t(0)
+    assert ops.lib().tcs_decode_workspace_size(C.byref(p), C.byref(n)) == code
+    st = ops.lib().sparse_attn_decode(C.byref(p), *([None] * 14), 0, None)
+    assert st == code
+
+
+def test_decode_struct_size_checked():
+    p = P()
+    p.struct_size = 12
+    n = C.c_size_t(0)
+    assert ops.lib().tcs_decode_workspace_size(C.byref(p), C.byref(n)) == ops.TCS_ERR_SHAPE
+
+
+def test_decode_null_and_workspace_errors():
+    p = P()
+    need = ops.decode_workspace_size(p)
+    fake = 0x100000  # never dereferenced: the checks fail first
+    args = [fake] * 6 + [None, None, fake, None, None, None, None]
+    lib = ops.lib()
+    # q missing
+    assert lib.sparse_attn_decode(C.byref(p), None, *args[1:], fake, need, None) == ops.TCS_ERR_NULL
+    # workspace too small / misaligned / missing
+    assert lib.sparse_attn_decode(C.byref(p), *args, fake, need - 1, None) == ops.TCS_ERR_WORKSPACE
+    assert lib.sparse_attn_decode(C.byref(p), *args, fake + 4, need, None) == ops.TCS_ERR_WORKSPACE
+    assert lib.sparse_attn_decode(C.byref(p), *args, None, need, None) == ops.TCS_ERR_WORKSPACE
+    # gists required when there are historical chunks
+    a2 = list(args)
+    a2[4] = None
+    assert lib.sparse_attn_decode(C.byref(p), *a2, fake, need, None) == ops.TCS_ERR_NULL
+    # two levels need level-2 gists
+    p2 = P(levels=2, J=4, k2=2)
+    need2 = ops.decode_workspace_size(p2)
+    assert lib.sparse_attn_decode(C.byref(p2), *args, fake, need2, None) == ops.TCS_ERR_NULL
+
+
+def PP(**kw):
+    base = dict(B=1, Hq=8, Hkv=2, d=128, T=1024, blk=64, k=4, gate=1)
+    base.update(kw)
+    return ops.prefill_params(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=1000), ops.TCS_ERR_SHAPE),
+    (dict(blk=32), ops.TCS_ERR_UNSUPPORTED),
+    (dict(d=64), ops.TCS_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), ops.TCS_ERR_SHAPE),
+    (dict(k=-2), ops.TCS_ERR_SHAPE),
+    (dict(gate=5), ops.TCS_ERR_SHAPE),
+])
+def test_prefill_rejects_bad_params(kw, code):
+    p = PP(**kw)
+    n = C.c_size_t(0)
+    assert ops.lib().tcs_prefill_workspace_size(C.byref(p), C.byref(n)) == code
+    assert ops.lib().sparse_attn_prefill(C.byref(p), *([None] * 8), 0, None) == code
+
+
+def test_prefill_null_and_workspace_errors():
+    p = PP()
+    need = ops.prefill_workspace_size(p)
+    fake = 0x100000
+    lib = ops.lib()
+    assert lib.sparse_attn_prefill(C.byref(p), None, fake, fake, fake, fake, None, None,
+                                   fake, need, None) == ops.TCS_ERR_NULL
+    assert lib.sparse_attn_prefill(C.byref(p), fake, fake, fake, None, fake, None, None,
+                                   fake, need, None) == ops.TCS_ERR_NULL     # S needed for k > 0
+    assert lib.sparse_attn_prefill(C.byref(p), fake, fake, fake, fake, fake, None, None,
+                                   fake, need - 8, None) == ops.TCS_ERR_WORKSPACE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        ops.lib()

@@ -1,0 +1,133 @@
+"""GPU parity of the chunk-sparse decode path against the fp64 oracle (calls go through the
+C ABI via the ctypes binding).  Selected chunk ids must match exactly (near-ties at the k-th
+boundary with a relative score gap < 1e-5 are excused, counted and re-checked against the
+oracle run on the GPU's selection); out and lse within 1e-2 max-abs."""
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from top_chunk_sparse_amd import configs
+from top_chunk_sparse_amd.configs import DecodeConfig
+from top_chunk_sparse_amd.ops import DecodeCall
+from top_chunk_sparse_amd.synth import make_decode
+from harness import check_decode, oracle_decode
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(cfg, seed, units=None, **kw):
+    say(f"[decode] {cfg.name} seed={seed} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} "
+        f"N={cfg.N} C={cfg.C} g={cfg.g} k={cfg.k} gate={cfg.gate} levels={cfg.levels} {kw}")
+    inp = make_decode(cfg, seed, device=DEV, **kw)
+    call = DecodeCall(inp)()
+    torch.cuda.synchronize()
+    st = check_decode(inp, call, units=units)
+    say("   ", st)
+    return inp, call, st
+
+
+@pytest.mark.parametrize("name", list(configs.DECODE_CONFIGS))
+def test_named_config_full(name):
+    cfg = configs.DECODE_CONFIGS[name]
+    inp, call, st = run_case(cfg, configs.seed_for(name))
+    assert st["excused"] <= max(1, st["units"] // 100)
+    del inp, call
+    torch.cuda.empty_cache()
+
+
+SMALL = DecodeConfig("gpu_small", B=2, Hq=8, Hkv=2, d=128, N=40 * 32 + 7, C=32, g=4, k=5,
+                     n_plant=6, paged=True)
+
+VARIANTS = [
+    SMALL,
+    SMALL.with_(gate=1),
+    SMALL.with_(d=64),
+    SMALL.with_(d=64, gate=1, g=3, C=24, N=61 * 24 + 1),
+    SMALL.with_(Hq=2, Hkv=2),                 # G = 1
+    SMALL.with_(Hq=4, Hkv=2),                 # G = 2
+    SMALL.with_(Hq=16, Hkv=2, gate=1),        # G = 8
+    SMALL.with_(k=0),
+    SMALL.with_(k=0, gate=1),
+    SMALL.with_(k=10 ** 4, gate=1),           # every chunk
+    SMALL.with_(N=20, C=32),                  # only the (partial) current chunk
+    SMALL.with_(N=33, C=32, gate=1),          # one historical chunk
+    SMALL.with_(g=1, C=64, N=300 * 64),       # many chunks, one gist each
+    SMALL.with_(g=16, C=128, N=37 * 128 + 100, d=64),
+    SMALL.with_(levels=2, J=4, k2=3, k=6, n_plant=6, plant_groups=3),
+    SMALL.with_(levels=2, J=5, k2=100, k=7, n_plant=4, plant_groups=2, d=64),
+    SMALL.with_(levels=2, J=3, k2=0, k=4, n_plant=0),
+    SMALL.with_(levels=2, J=4, k2=2, k=0, n_plant=4, plant_groups=2),
+    SMALL.with_(levels=2, J=8, k2=64, k=10 ** 4, n_plant=4, plant_groups=2, Hq=16),
+]
+
+
+@pytest.mark.parametrize("cfg", VARIANTS, ids=[f"v{i}" for i in range(len(VARIANTS))])
+def test_variants(cfg):
+    run_case(cfg, seed=100 + VARIANTS.index(cfg), max_chunks=cfg.M + 5, extra_pages=3)
+
+
+def test_deterministic_bitwise():
+    cfg = configs.LLAMA1B
+    inp = make_decode(cfg, 7, device=DEV)
+    a = DecodeCall(inp)()
+    b = DecodeCall(inp)()
+    a()      # twice on the same workspace as well
+    torch.cuda.synchronize()
+    for x, y in ((a.out, b.out), (a.lse, b.lse), (a.sel, b.sel), (a.chunk_scores, b.chunk_scores)):
+        assert torch.equal(x, y)
+
+
+def test_permutation_invariance_gpu():
+    cfg = SMALL.with_(gate=1)
+    inp = make_decode(cfg, 55, device=DEV)
+    a = DecodeCall(inp)()
+    torch.cuda.synchronize()
+    sel = a.sel.cpu().numpy()
+    rng = np.random.default_rng(1)
+    pt, gk, gv = inp.page_table.clone(), inp.gist_k.clone(), inp.gist_v.clone()
+    for b in range(cfg.B):
+        free = [c for c in range(cfg.H) if c not in set(sel[b].ravel().tolist())]
+        perm = rng.permutation(free)
+        pt[b, free] = inp.page_table[b, perm]
+        gk[b, :, free] = inp.gist_k[b, :, perm]
+        gv[b, :, free] = inp.gist_v[b, :, perm]
+    b2 = DecodeCall(replace(inp, page_table=pt, gist_k=gk, gist_v=gv))()
+    torch.cuda.synchronize()
+    assert torch.equal(a.sel, b2.sel)
+    assert (a.out - b2.out).abs().max().item() <= 1e-6
+    assert (a.lse - b2.lse).abs().max().item() <= 1e-6
+
+
+def test_bad_page_poisons_only_its_unit():
+    cfg = SMALL
+    inp = make_decode(cfg, 56, device=DEV)
+    a = DecodeCall(inp)()
+    torch.cuda.synchronize()
+    c = int(a.sel[1, 0, 0])
+    pt = inp.page_table.clone()
+    pt[1, c] = inp.num_pages + 5
+    b = DecodeCall(replace(inp, page_table=pt))()
+    torch.cuda.synchronize()
+    G = cfg.G
+    heads_bad = [h for kv in range(cfg.Hkv) if c in a.sel[1, kv].tolist()
+                 for h in range(kv * G, (kv + 1) * G)]
+    assert torch.isnan(b.out[1, heads_bad]).all() and torch.isnan(b.lse[1, heads_bad]).all()
+    good = [h for h in range(cfg.Hq) if h not in heads_bad]
+    assert torch.equal(b.out[0], a.out[0]) and torch.equal(b.out[1, good], a.out[1, good])
+
+
+def test_scale_override():
+    cfg = SMALL.with_(gate=1)
+    inp = make_decode(cfg, 57, device=DEV)
+    call = DecodeCall(inp, scale=0.05)()
+    torch.cuda.synchronize()
+    check_decode(inp, call)

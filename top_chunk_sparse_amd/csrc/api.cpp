@@ -1,0 +1,414 @@
+// api.cpp -- the C ABI of libtcsparse.so (declared in include/tcsparse.h): argument checks,
+// workspace carving and the launch sequence.  Everything here is host code; no call
+// allocates, frees or synchronises, and argument errors return before any device work.
+#include "tcsparse.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+using tcs::Partials;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxSliceRows = 1024;   // rows one gist workgroup holds logits for (LDS)
+constexpr int kTargetWorkgroups = 1024;
+constexpr int kMinSliceRows = 64;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+// Split `nchunks` chunks of `g` rows into slices for the gist kernel: enough workgroups to
+// fill the GPU, at least kMinSliceRows rows each, at most kMaxSliceRows.
+void plan_slices(long long units, int nchunks, int g, int* slices, int* cps) {
+    if (nchunks <= 0) { *slices = 0; *cps = 1; return; }
+    long long want = (kTargetWorkgroups + units - 1) / units;
+    if (want < 1) want = 1;
+    long long c = (nchunks + want - 1) / want;
+    long long cmin = (kMinSliceRows + g - 1) / g;
+    if (c < cmin) c = cmin;
+    long long cmax = kMaxSliceRows / g;
+    if (c > cmax) c = cmax;
+    if (c < 1) c = 1;
+    *cps = (int)c;
+    *slices = (int)((nchunks + c - 1) / c);
+}
+
+struct DecodePlan {
+    int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, nslots;
+    float sigma;
+    // workspace offsets (bytes)
+    size_t off_scores, off_sel, off_gamma, off_gscores, off_gsel, off_acc, off_ml, total;
+};
+
+tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
+    if (!p) return TCS_ERR_NULL;
+    if (p->struct_size != (int32_t)sizeof(tcs_decode_params)) return TCS_ERR_SHAPE;
+    if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->d < 1 || p->N < 1 || p->C < 1 || p->g < 1 ||
+        p->k < 0 || p->num_pages < 1)
+        return TCS_ERR_SHAPE;
+    if (p->Hq % p->Hkv) return TCS_ERR_SHAPE;
+    if (p->levels != 1 && p->levels != 2) return TCS_ERR_SHAPE;
+    if (p->gate_mode != TCS_GATE_NONE && p->gate_mode != TCS_GATE_SAS) return TCS_ERR_SHAPE;
+    if (!(p->scale >= 0.f) || std::isinf(p->scale)) return TCS_ERR_SHAPE;
+    const int G = p->Hq / p->Hkv;
+    const long long units = (long long)p->B * p->Hkv;
+    const int M = (int)(((long long)p->N + p->C - 1) / p->C);
+    const int H = M - 1;
+    if (p->max_chunks < M) return TCS_ERR_SHAPE;
+    if (p->gist_cap != 0 && p->gist_cap < H) return TCS_ERR_SHAPE;
+    if (units > 65535) return TCS_ERR_UNSUPPORTED;
+    if (p->d != 64 && p->d != 128) return TCS_ERR_UNSUPPORTED;
+    if (!supported_group(G)) return TCS_ERR_UNSUPPORTED;
+    if (p->g > 64) return TCS_ERR_UNSUPPORTED;
+    pl->G = G;
+    pl->M = M;
+    pl->H = H;
+    pl->sigma = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->d);
+    int ksel;
+    if (p->levels == 2) {
+        if (p->J < 1 || p->k2 < 0) return TCS_ERR_SHAPE;
+        if (p->gate_mode != TCS_GATE_NONE) return TCS_ERR_UNSUPPORTED;
+        if ((long long)p->J * p->g > kMaxSliceRows || p->k2 > 64) return TCS_ERR_UNSUPPORTED;
+        pl->nG = (H + p->J - 1) / p->J;
+        pl->k2e = p->k2 < pl->nG ? p->k2 : pl->nG;
+        plan_slices(units, pl->nG, p->g, &pl->S2, &pl->cps2);
+        pl->S1 = 0;
+        pl->cps1 = 1;
+        const long long ncand = (long long)pl->k2e * p->J;
+        ksel = (int)(p->k < ncand ? p->k : ncand);
+    } else {
+        pl->nG = 0;
+        pl->k2e = 0;
+        pl->S2 = 0;
+        pl->cps2 = 1;
+        plan_slices(units, H, p->g, &pl->S1, &pl->cps1);
+        ksel = p->k < H ? p->k : H;
+    }
+    pl->kslots = ksel;
+    pl->nslots = pl->S1 + pl->S2 + pl->k2e + ksel + 1;
+    const long long BH = (long long)p->B * p->Hq;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    const long long nscore = p->levels == 2 ? (long long)pl->k2e * p->J : H;
+    pl->off_scores = take(sizeof(float) * (size_t)(units * (nscore > 0 ? nscore : 1)));
+    pl->off_sel = take(sizeof(int32_t) * (size_t)(units * (p->k > 0 ? p->k : 1)));
+    pl->off_gamma = take(sizeof(float) * (size_t)(units * (p->k > 0 ? p->k : 1)));
+    pl->off_gscores = take(sizeof(float) * (size_t)(units * (pl->nG > 0 ? pl->nG : 1)));
+    pl->off_gsel = take(sizeof(int32_t) * (size_t)(units * (p->k2 > 0 ? p->k2 : 1)));
+    pl->off_acc = take(sizeof(float) * (size_t)(BH * pl->nslots * p->d));
+    pl->off_ml = take(sizeof(float) * (size_t)(BH * pl->nslots * 2));
+    pl->total = off;
+    return TCS_OK;
+}
+
+struct PrefillPlan {
+    int G, nb;
+    float sigma;
+    size_t off_sel, off_gamma, total;
+};
+
+tcs_status plan_prefill(const tcs_prefill_params* p, PrefillPlan* pl) {
+    if (!p) return TCS_ERR_NULL;
+    if (p->struct_size != (int32_t)sizeof(tcs_prefill_params)) return TCS_ERR_SHAPE;
+    if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->d < 1 || p->T < 1 || p->blk < 1 || p->k < 0)
+        return TCS_ERR_SHAPE;
+    if (p->Hq % p->Hkv || p->T % p->blk) return TCS_ERR_SHAPE;
+    if (p->gate_mode != TCS_GATE_NONE && p->gate_mode != TCS_GATE_SAS) return TCS_ERR_SHAPE;
+    if (!(p->scale >= 0.f) || std::isinf(p->scale)) return TCS_ERR_SHAPE;
+    const int G = p->Hq / p->Hkv;
+    if (p->d != 128 || p->blk != 64 || !supported_group(G)) return TCS_ERR_UNSUPPORTED;
+    const long long units = (long long)p->B * p->Hkv;
+    pl->G = G;
+    pl->nb = p->T / p->blk;
+    if (units * pl->nb > INT_MAX / 2) return TCS_ERR_UNSUPPORTED;
+    pl->sigma = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->d);
+    const int kk = p->k > 0 ? p->k : 1;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    pl->off_sel = take(sizeof(int32_t) * (size_t)(units * pl->nb * kk));
+    pl->off_gamma = take(sizeof(float) * (size_t)(units * pl->nb * kk));
+    pl->total = off;
+    return TCS_OK;
+}
+
+tcs_status check_ws(void* ws, size_t have, size_t need) {
+    if (have < need) return TCS_ERR_WORKSPACE;
+    if (need > 0 && (!ws || ((uintptr_t)ws % kAlign))) return TCS_ERR_WORKSPACE;
+    return TCS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tcs_abi_version(void) { return TCS_ABI_VERSION; }
+
+const char* tcs_status_str(tcs_status s) {
+    switch (s) {
+        case TCS_OK: return "ok";
+        case TCS_ERR_NULL: return "null pointer argument";
+        case TCS_ERR_SHAPE: return "invalid sizes";
+        case TCS_ERR_UNSUPPORTED: return "unsupported configuration";
+        case TCS_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case TCS_ERR_HIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+tcs_status tcs_decode_workspace_size(const tcs_decode_params* p, size_t* bytes) {
+    if (!bytes) return TCS_ERR_NULL;
+    DecodePlan pl;
+    tcs_status st = plan_decode(p, &pl);
+    if (st != TCS_OK) return st;
+    *bytes = pl.total;
+    return TCS_OK;
+}
+
+static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* page_table, const void* gist_k,
+                              const void* gist_v, const void* gist2_k, const void* gist2_v,
+                              float* out, float* lse, int32_t* sel, int32_t* sel_groups,
+                              float* chunk_scores, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events, int n_events) {
+    DecodePlan pl;
+    tcs_status st = plan_decode(p, &pl);
+    if (st != TCS_OK) return st;
+    if (!q || !k_pages || !v_pages || !page_table || !out) return TCS_ERR_NULL;
+    if (pl.H > 0 && (!gist_k || !gist_v)) return TCS_ERR_NULL;
+    if (p->levels == 2 && pl.nG > 0 && (!gist2_k || !gist2_v)) return TCS_ERR_NULL;
+    st = check_ws(workspace, workspace_bytes, pl.total);
+    if (st != TCS_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    int stage = 0;
+    auto mark = [&]() -> bool {   // record events[stage] (if the caller gave one)
+        if (stage < n_events && events && events[stage]) {
+            if (hipEventRecord((hipEvent_t)events[stage], s) != hipSuccess) return false;
+        }
+        ++stage;
+        return true;
+    };
+    if (!mark()) return TCS_ERR_HIP;
+    char* ws = (char*)workspace;
+    const int units = p->B * p->Hkv;
+    const int cap = p->gist_cap > 0 ? p->gist_cap : pl.H;
+    Partials part{(float*)(ws + pl.off_acc), (float*)(ws + pl.off_ml), pl.nslots};
+    int32_t* sel_p = sel ? sel : (int32_t*)(ws + pl.off_sel);
+    float* gamma = p->gate_mode == TCS_GATE_SAS ? (float*)(ws + pl.off_gamma) : nullptr;
+    hipError_t e = hipSuccess;
+    int slot = 0;
+
+    tcs::GistLaunch ga{};
+    ga.q = (const uint16_t*)q;
+    ga.B = p->B; ga.Hq = p->Hq; ga.Hkv = p->Hkv; ga.d = p->d; ga.g = p->g;
+    ga.sigma = pl.sigma;
+    ga.part = part;
+
+    if (p->levels == 1) {
+        float* scores = chunk_scores ? chunk_scores : (float*)(ws + pl.off_scores);
+        ga.gk = (const uint16_t*)gist_k;
+        ga.gv = (const uint16_t*)gist_v;
+        ga.unit_stride = (long long)cap * p->g * p->d;
+        ga.nchunks = pl.H;
+        ga.slices = pl.S1;
+        ga.chunks_per_slice = pl.cps1;
+        ga.groups = nullptr;
+        ga.scores = scores;
+        ga.score_stride = pl.H;
+        ga.slot0 = slot;
+        e = tcs::launch_gist(ga, s);
+        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+        slot += pl.S1;
+
+        tcs::SelectLaunch sa{};
+        sa.units = units; sa.scores = scores; sa.score_stride = pl.H; sa.n = pl.H;
+        sa.k = p->k; sa.sel = sel_p; sa.gamma = gamma;
+        sa.groups = nullptr;
+        e = tcs::launch_select(sa, s);
+        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+    } else {
+        float* gscores = (float*)(ws + pl.off_gscores);
+        int32_t* gsel = sel_groups ? sel_groups : (int32_t*)(ws + pl.off_gsel);
+        float* cscores = (float*)(ws + pl.off_scores);
+        // level 2: every group
+        ga.gk = (const uint16_t*)gist2_k;
+        ga.gv = (const uint16_t*)gist2_v;
+        ga.unit_stride = (long long)pl.nG * p->g * p->d;
+        ga.nchunks = pl.nG;
+        ga.slices = pl.S2;
+        ga.chunks_per_slice = pl.cps2;
+        ga.groups = nullptr;
+        ga.scores = gscores;
+        ga.score_stride = pl.nG;
+        ga.slot0 = slot;
+        e = tcs::launch_gist(ga, s);
+        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+        slot += pl.S2;
+
+        tcs::SelectLaunch sg{};
+        sg.units = units; sg.scores = gscores; sg.score_stride = pl.nG; sg.n = pl.nG;
+        sg.k = p->k2; sg.sel = gsel; sg.gamma = nullptr; sg.groups = nullptr;
+        e = tcs::launch_select(sg, s);
+        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+
+        // level 1: the members of the chosen groups
+        ga.gk = (const uint16_t*)gist_k;
+        ga.gv = (const uint16_t*)gist_v;
+        ga.unit_stride = (long long)cap * p->g * p->d;
+        ga.nchunks = pl.H;
+        ga.slices = pl.k2e;
+        ga.groups = gsel;
+        ga.J = p->J; ga.k2 = p->k2; ga.H = pl.H;
+        ga.scores = cscores;
+        ga.score_stride = pl.k2e * p->J;
+        ga.slot0 = slot;
+        e = tcs::launch_gist(ga, s);
+        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+        slot += pl.k2e;
+
+        tcs::SelectLaunch sa{};
+        sa.units = units; sa.scores = cscores; sa.score_stride = pl.k2e * p->J; sa.n = 0;
+        sa.k = p->k; sa.sel = sel_p; sa.gamma = nullptr;
+        sa.groups = gsel; sa.J = p->J; sa.k2 = p->k2; sa.H = pl.H;
+        sa.chunk_scores_out = chunk_scores;
+        if (p->k > 0) {
+            e = tcs::launch_select(sa, s);
+        } else if (chunk_scores && pl.H > 0) {
+            // nothing selected, but the caller asked for the candidates' scores
+            sa.k = 1;
+            sa.sel = (int32_t*)(ws + pl.off_sel);
+            e = tcs::launch_select(sa, s);
+        }
+        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+    }
+
+    tcs::ChunkLaunch ca{};
+    ca.q = (const uint16_t*)q;
+    ca.kp = (const uint16_t*)k_pages;
+    ca.vp = (const uint16_t*)v_pages;
+    ca.page_table = page_table;
+    ca.B = p->B; ca.Hq = p->Hq; ca.Hkv = p->Hkv; ca.d = p->d; ca.C = p->C; ca.N = p->N;
+    ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
+    ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots;
+    ca.sigma = pl.sigma; ca.part = part; ca.slot0 = slot;
+    e = tcs::launch_chunks(ca, s);
+    if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+
+    tcs::CombineLaunch cb{part, p->B * p->Hq, p->d, out, lse};
+    e = tcs::launch_combine(cb, s);
+    if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+    return TCS_OK;
+}
+
+tcs_status sparse_attn_decode(const tcs_decode_params* p, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* page_table, const void* gist_k,
+                              const void* gist_v, const void* gist2_k, const void* gist2_v,
+                              float* out, float* lse, int32_t* sel, int32_t* sel_groups,
+                              float* chunk_scores, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    return decode_impl(p, q, k_pages, v_pages, page_table, gist_k, gist_v, gist2_k, gist2_v, out,
+                       lse, sel, sel_groups, chunk_scores, workspace, workspace_bytes, stream,
+                       nullptr, 0);
+}
+
+tcs_status sparse_attn_decode_timed(const tcs_decode_params* p, const void* q,
+                                    const void* k_pages, const void* v_pages,
+                                    const int32_t* page_table, const void* gist_k,
+                                    const void* gist_v, const void* gist2_k, const void* gist2_v,
+                                    float* out, float* lse, int32_t* sel, int32_t* sel_groups,
+                                    float* chunk_scores, void* workspace, size_t workspace_bytes,
+                                    void* stream, void* const* events, int n_events) {
+    if (n_events < 0) return TCS_ERR_SHAPE;
+    return decode_impl(p, q, k_pages, v_pages, page_table, gist_k, gist_v, gist2_k, gist2_v, out,
+                       lse, sel, sel_groups, chunk_scores, workspace, workspace_bytes, stream,
+                       events, n_events);
+}
+
+int tcs_decode_stage_count(const tcs_decode_params* p) {
+    DecodePlan pl;
+    if (plan_decode(p, &pl) != TCS_OK) return -1;
+    return p->levels == 2 ? 6 : 4;
+}
+
+tcs_status tcs_prefill_workspace_size(const tcs_prefill_params* p, size_t* bytes) {
+    if (!bytes) return TCS_ERR_NULL;
+    PrefillPlan pl;
+    tcs_status st = plan_prefill(p, &pl);
+    if (st != TCS_OK) return st;
+    *bytes = pl.total;
+    return TCS_OK;
+}
+
+static tcs_status prefill_impl(const tcs_prefill_params* p, const void* q, const void* k,
+                               const void* v, const float* S, float* out, float* lse,
+                               int32_t* sel, void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* events, int n_events) {
+    PrefillPlan pl;
+    tcs_status st = plan_prefill(p, &pl);
+    if (st != TCS_OK) return st;
+    if (!q || !k || !v || !out || (!S && p->k > 0) || (!S && p->gate_mode == TCS_GATE_SAS))
+        return TCS_ERR_NULL;
+    st = check_ws(workspace, workspace_bytes, pl.total);
+    if (st != TCS_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    int stage = 0;
+    auto mark = [&]() -> bool {
+        if (stage < n_events && events && events[stage]) {
+            if (hipEventRecord((hipEvent_t)events[stage], s) != hipSuccess) return false;
+        }
+        ++stage;
+        return true;
+    };
+    if (!mark()) return TCS_ERR_HIP;
+    char* ws = (char*)workspace;
+    const int units = p->B * p->Hkv;
+    const int kk = p->k > 0 ? p->k : 0;
+    int32_t* sel_p = sel ? sel : (int32_t*)(ws + pl.off_sel);
+    float* gamma = p->gate_mode == TCS_GATE_SAS ? (float*)(ws + pl.off_gamma) : nullptr;
+    if (kk > 0) {
+        tcs::PrefillSelectLaunch ps{S, units, pl.nb, kk, sel_p, gamma};
+        if (tcs::launch_prefill_select(ps, s) != hipSuccess) return TCS_ERR_HIP;
+    }
+    if (!mark()) return TCS_ERR_HIP;
+    tcs::PrefillLaunch pa{};
+    pa.q = (const uint16_t*)q;
+    pa.k = (const uint16_t*)k;
+    pa.v = (const uint16_t*)v;
+    pa.B = p->B; pa.Hq = p->Hq; pa.Hkv = p->Hkv; pa.d = p->d; pa.T = p->T; pa.blk = p->blk;
+    pa.ksel = kk;
+    pa.sel = kk > 0 ? sel_p : nullptr;
+    pa.gamma = kk > 0 ? gamma : nullptr;
+    pa.sigma = pl.sigma;
+    pa.out = out;
+    pa.lse = lse;
+    hipError_t e = tcs::launch_prefill(pa, s);
+    if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
+    if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+    return TCS_OK;
+}
+
+tcs_status sparse_attn_prefill(const tcs_prefill_params* p, const void* q, const void* k,
+                               const void* v, const float* S, float* out, float* lse,
+                               int32_t* sel, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return prefill_impl(p, q, k, v, S, out, lse, sel, workspace, workspace_bytes, stream,
+                        nullptr, 0);
+}
+
+tcs_status sparse_attn_prefill_timed(const tcs_prefill_params* p, const void* q, const void* k,
+                                     const void* v, const float* S, float* out, float* lse,
+                                     int32_t* sel, void* workspace, size_t workspace_bytes,
+                                     void* stream, void* const* events, int n_events) {
+    if (n_events < 0) return TCS_ERR_SHAPE;
+    return prefill_impl(p, q, k, v, S, out, lse, sel, workspace, workspace_bytes, stream, events,
+                        n_events);
+}
+
+}  // extern "C"

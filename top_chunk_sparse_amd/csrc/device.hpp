@@ -1,0 +1,193 @@
+// device.hpp -- gfx950 device helpers shared by the decode and prefill kernels:
+// bf16 unpacking, DPP row reductions, order-preserving float keys, block-wide scans and the
+// deterministic top-k used for chunk / block selection.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tcs {
+
+constexpr int kWave = 64;
+
+// ---- bf16 -------------------------------------------------------------------------------
+// A dword holds two bf16 values; each is the upper half of an fp32.
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+    f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// ---- DPP ----------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LPR (8 or 16) lanes; every lane of a group receives the same,
+// bitwise-identical sum (each step adds a lane's value to its partner's, a commutative pair).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(LPR == 8 || LPR == 16, "LPR");
+    x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]: partner lane ^ 1
+    x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]: partner lane ^ 2
+    x += dpp<0x141>(x);   // row_half_mirror: the other quad of the 8-lane half
+    if constexpr (LPR == 16) x += dpp<0x140>(x);  // row_mirror: the other half of the row
+    return x;
+}
+
+// ---- ordered keys -----------------------------------------------------------------------
+// Monotone map fp32 -> uint32 (a < b  <=>  key(a) < key(b)); -0 is folded onto +0.
+__device__ __forceinline__ uint32_t ordered_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---- block scans (blockDim.x == 256) ------------------------------------------------------
+struct ScanSmem { int w[4]; };
+
+__device__ __forceinline__ int block_exclusive_scan(int v, ScanSmem& sm) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) sm.w[w] = x;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < w; ++i) before += sm.w[i];
+    __syncthreads();
+    return before + x - v;
+}
+
+struct ReduceSmem { float v[4]; };
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+// Fixed-order block reductions (deterministic).  Every thread gets the result.
+__device__ __forceinline__ float block_max(float x, ReduceSmem& sm) {
+    x = wave_max(x);
+    if ((threadIdx.x & 63) == 0) sm.v[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float r = fmaxf(fmaxf(sm.v[0], sm.v[1]), fmaxf(sm.v[2], sm.v[3]));
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ float block_sum(float x, ReduceSmem& sm) {
+    x = wave_sum(x);
+    if ((threadIdx.x & 63) == 0) sm.v[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float r = (sm.v[0] + sm.v[1]) + (sm.v[2] + sm.v[3]);
+    __syncthreads();
+    return r;
+}
+
+// ---- deterministic block top-k ------------------------------------------------------------
+// Chooses the min(k, n) largest of n fp32 scores, equal scores going to the lower position,
+// and writes the chosen positions in ascending order.  Radix select on the ordered 32-bit
+// key finds the threshold key T (the k_eff-th largest); every key > T is taken, then the
+// lowest positions holding T until k_eff are reached.  256 threads.
+constexpr int kTopkCache = 4096;   // keys staged in LDS; larger n re-reads global memory
+
+struct TopkSmem {
+    unsigned hist[256];
+    uint32_t keys[kTopkCache];
+    int digit;
+    unsigned above;
+    ScanSmem scan;
+};
+
+// score(i) -> fp32 score of position i; emit(j, i) is called once for the j-th chosen position
+// (j ascending with i).  Returns k_eff.
+template <class ScoreFn, class EmitFn>
+__device__ int block_topk(int n, int k, ScoreFn score, EmitFn emit, TopkSmem& sm) {
+    const int tid = threadIdx.x;
+    const int ke = k < n ? k : n;
+    if (ke <= 0) return 0;
+    const bool cached = n <= kTopkCache;
+    if (cached)
+        for (int i = tid; i < n; i += 256) sm.keys[i] = ordered_key(score(i));
+    __syncthreads();
+    auto key_at = [&](int i) -> uint32_t { return cached ? sm.keys[i] : ordered_key(score(i)); };
+
+    uint32_t prefix = 0, mask = 0;
+    unsigned remaining = (unsigned)ke;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        sm.hist[tid] = 0u;
+        __syncthreads();
+        for (int i = tid; i < n; i += 256) {
+            uint32_t key = key_at(i);
+            if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) {
+            const unsigned c0 = sm.hist[4 * tid], c1 = sm.hist[4 * tid + 1];
+            const unsigned c2 = sm.hist[4 * tid + 2], c3 = sm.hist[4 * tid + 3];
+            const unsigned tot = c0 + c1 + c2 + c3;
+            unsigned S = tot;  // inclusive suffix sum over lanes >= tid
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                unsigned o = __shfl_down(S, off);
+                if (tid + off < 64) S += o;
+            }
+            const unsigned above = S - tot;  // keys whose digit is above this lane's bins
+            if (above < remaining && remaining <= S) {
+                unsigned a = above;
+                int dg;
+                if (a + c3 >= remaining) dg = 4 * tid + 3;
+                else if (a += c3, a + c2 >= remaining) dg = 4 * tid + 2;
+                else if (a += c2, a + c1 >= remaining) dg = 4 * tid + 1;
+                else { a += c1; dg = 4 * tid; }
+                sm.digit = dg;
+                sm.above = a;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sm.digit << shift;
+        mask |= 255u << shift;
+        remaining -= sm.above;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;
+    // Ordered compaction over contiguous per-thread ranges.
+    const int per = (n + 255) / 256;
+    const int lo = tid * per < n ? tid * per : n;
+    const int hi = lo + per < n ? lo + per : n;
+    int gt = 0, eq = 0;
+    for (int i = lo; i < hi; ++i) {
+        uint32_t key = key_at(i);
+        gt += key > T;
+        eq += key == T;
+    }
+    const int eq_before = block_exclusive_scan(eq, sm.scan);
+    int take_eq = (int)remaining - eq_before;
+    take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
+    int pos = block_exclusive_scan(gt + take_eq, sm.scan);
+    int taken = 0;
+    for (int i = lo; i < hi; ++i) {
+        uint32_t key = key_at(i);
+        bool take = key > T;
+        if (key == T && taken < take_eq) { take = true; ++taken; }
+        if (take) emit(pos++, i);
+    }
+    __syncthreads();
+    return ke;
+}
+
+}  // namespace tcs
