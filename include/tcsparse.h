@@ -57,6 +57,10 @@
  *   from tcs_*_workspace_size, 256-byte aligned).  The library allocates, frees and
  *   synchronises nothing and keeps no global state; every call only enqueues kernels on
  *   `stream` and returns.  Calls sharing a workspace must be ordered on one stream.
+ *   A decode workspace holds per-unit arrival counters that must read zero when a call
+ *   starts: zero-fill a new workspace once (tcs_workspace_init, or any zero fill) before its
+ *   first call; every completed call leaves the counters at zero again.  After a call that
+ *   returned TCS_ERR_HIP, initialise the workspace again.
  *   Argument errors return before any device work and leave every output untouched.  A
  *   failed launch returns TCS_ERR_HIP.  Inputs must be finite (NaN/Inf inputs give
  *   unspecified results).  A page id outside [0, num_pages) is never read: the heads of the
@@ -65,8 +69,9 @@
  *   for); k = 0 keeps only the gists and the current chunk.  Results are deterministic:
  *   no floating-point atomics; the same inputs give bitwise-identical outputs.
  *
- * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; prefill blk = 64
- * and T a multiple of blk.  Other shapes return TCS_ERR_UNSUPPORTED.
+ * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; two levels:
+ * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk.
+ * Other shapes return TCS_ERR_UNSUPPORTED.
  */
 #ifndef TCSPARSE_H
 #define TCSPARSE_H
@@ -124,11 +129,12 @@ tcs_status sparse_attn_decode(const tcs_decode_params* p,
 
 /* Profiling variant of sparse_attn_decode: identical work and results, and in addition it
  * records caller-created HIP events (hipEvent_t, passed as void*) on `stream`: events[0]
- * before the first kernel and events[i] after the i-th kernel of the sequence.  levels = 1:
- * 1 gist scoring, 2 chunk selection, 3 chunk attention, 4 combine.  levels = 2: 1 level-2
- * scoring, 2 group selection, 3 candidate scoring, 4 chunk selection, 5 chunk attention,
- * 6 combine.  Entries beyond n_events, or NULL entries, are skipped.  For profiling tools:
- * recording events between kernels adds a little time to the call. */
+ * before the first kernel and events[i] after the i-th stage.  levels = 1: stage 1 gist
+ * scoring with chunk selection, stage 2 chunk attention with the final merge.  levels = 2:
+ * stage 1 level-2 scoring with group selection, stage 2 candidate scoring with chunk
+ * selection, stage 3 chunk attention with the final merge.  Entries beyond n_events, or NULL
+ * entries, are skipped.  For profiling tools: recording events between kernels adds a
+ * little time to the call. */
 tcs_status sparse_attn_decode_timed(const tcs_decode_params* p,
                                     const void* q,
                                     const void* k_pages, const void* v_pages,
@@ -140,9 +146,13 @@ tcs_status sparse_attn_decode_timed(const tcs_decode_params* p,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     void* const* events, int n_events);
 
-/* Number of kernels sparse_attn_decode enqueues for these parameters (4 or 6), -1 if the
- * parameters are invalid.  Host-only. */
+/* Number of stages sparse_attn_decode_timed brackets with events for these parameters
+ * (2 for one level, 3 for two levels), -1 if the parameters are invalid.  Host-only. */
 int tcs_decode_stage_count(const tcs_decode_params* p);
+
+/* Zero-fills `workspace_bytes` bytes of a workspace on `stream` (one small kernel; no
+ * allocation).  Required once before a new decode workspace is first used. */
+tcs_status tcs_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 typedef struct {
     int32_t struct_size;   /* = sizeof(tcs_prefill_params) */

@@ -65,7 +65,8 @@ def test_workspace_size_grows_with_work():
     (dict(levels=3), ops.TCS_ERR_SHAPE),
     (dict(levels=2, J=0), ops.TCS_ERR_SHAPE),
     (dict(levels=2, J=4, k2=2, gate=1), ops.TCS_ERR_UNSUPPORTED),
-    (dict(levels=2, J=4, k2=65), ops.TCS_ERR_UNSUPPORTED),
+    (dict(levels=2, J=4, k2=65, N=64 * 4 * 70), ops.TCS_ERR_UNSUPPORTED),  # 69 groups
+    (dict(levels=2, J=300, k2=1), ops.TCS_ERR_UNSUPPORTED),              # J*g > 1024
     (dict(gate=2), ops.TCS_ERR_SHAPE),
     (dict(scale=-1.0), ops.TCS_ERR_SHAPE),
     (dict(num_pages=0), ops.TCS_ERR_SHAPE),
@@ -146,3 +147,16 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         ops.lib()
+
+
+def test_workspace_init_checks_alignment():
+    lib = ops.lib()
+    assert lib.tcs_workspace_init(None, 0, None) == ops.TCS_OK
+    assert lib.tcs_workspace_init(None, 256, None) == ops.TCS_ERR_WORKSPACE
+    assert lib.tcs_workspace_init(0x100004, 256, None) == ops.TCS_ERR_WORKSPACE
+
+
+def test_stage_counts():
+    assert ops.decode_stage_count(P()) == 2
+    assert ops.decode_stage_count(P(levels=2, J=4, k2=2)) == 3
+    assert ops.decode_stage_count(P(d=96)) == -1

@@ -131,3 +131,20 @@ def test_scale_override():
     call = DecodeCall(inp, scale=0.05)()
     torch.cuda.synchronize()
     check_decode(inp, call)
+
+
+def test_workspace_reused_across_shapes():
+    """One zero-initialised workspace serves calls of different shapes in turn: every call
+    leaves its arrival counters at zero for the next."""
+    from top_chunk_sparse_amd import ops
+    cfgs = [SMALL.with_(levels=2, J=4, k2=3, k=6, n_plant=6, plant_groups=3),
+            SMALL.with_(gate=1), SMALL.with_(d=64, k=3), SMALL.with_(gate=1, B=3)]
+    calls = [DecodeCall(make_decode(c, 300 + i, device=DEV)) for i, c in enumerate(cfgs)]
+    big = max(c.ws.numel() for c in calls)
+    ws = ops.workspace(big, DEV)
+    for rep in range(2):
+        for call in calls:
+            call.ws = ws
+            call()
+            torch.cuda.synchronize()
+            check_decode(call.inp, call)

@@ -41,10 +41,11 @@ void plan_slices(long long units, int nchunks, int g, int* slices, int* cps) {
 }
 
 struct DecodePlan {
-    int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, nslots;
+    int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, nslots, kcap1, kcap2;
     float sigma;
     // workspace offsets (bytes)
-    size_t off_scores, off_sel, off_gamma, off_gscores, off_gsel, off_acc, off_ml, total;
+    size_t off_cnt, off_cs1, off_ci1, off_lse1, off_cs2, off_ci2, off_sel, off_gamma, off_gsel,
+        off_acc, off_ml, total;
 };
 
 tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
@@ -75,14 +76,17 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (p->levels == 2) {
         if (p->J < 1 || p->k2 < 0) return TCS_ERR_SHAPE;
         if (p->gate_mode != TCS_GATE_NONE) return TCS_ERR_UNSUPPORTED;
-        if ((long long)p->J * p->g > kMaxSliceRows || p->k2 > 64) return TCS_ERR_UNSUPPORTED;
+        if ((long long)p->J * p->g > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
         pl->nG = (H + p->J - 1) / p->J;
         pl->k2e = p->k2 < pl->nG ? p->k2 : pl->nG;
+        if (pl->k2e > 64) return TCS_ERR_UNSUPPORTED;   // chosen groups held in LDS
         plan_slices(units, pl->nG, p->g, &pl->S2, &pl->cps2);
         pl->S1 = 0;
         pl->cps1 = 1;
         const long long ncand = (long long)pl->k2e * p->J;
         ksel = (int)(p->k < ncand ? p->k : ncand);
+        pl->kcap2 = p->k2 < pl->cps2 ? p->k2 : pl->cps2;
+        pl->kcap1 = p->k < p->J ? p->k : p->J;
     } else {
         pl->nG = 0;
         pl->k2e = 0;
@@ -90,18 +94,25 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
         pl->cps2 = 1;
         plan_slices(units, H, p->g, &pl->S1, &pl->cps1);
         ksel = p->k < H ? p->k : H;
+        pl->kcap2 = 0;
+        pl->kcap1 = p->k < pl->cps1 ? p->k : pl->cps1;
     }
     pl->kslots = ksel;
     pl->nslots = pl->S1 + pl->S2 + pl->k2e + ksel + 1;
     const long long BH = (long long)p->B * p->Hq;
+    const long long s1 = p->levels == 2 ? pl->k2e : pl->S1;     // slices of the chunk pass
+    auto n1 = [](long long x) { return x > 0 ? x : 1; };
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-    const long long nscore = p->levels == 2 ? (long long)pl->k2e * p->J : H;
-    pl->off_scores = take(sizeof(float) * (size_t)(units * (nscore > 0 ? nscore : 1)));
-    pl->off_sel = take(sizeof(int32_t) * (size_t)(units * (p->k > 0 ? p->k : 1)));
-    pl->off_gamma = take(sizeof(float) * (size_t)(units * (p->k > 0 ? p->k : 1)));
-    pl->off_gscores = take(sizeof(float) * (size_t)(units * (pl->nG > 0 ? pl->nG : 1)));
-    pl->off_gsel = take(sizeof(int32_t) * (size_t)(units * (p->k2 > 0 ? p->k2 : 1)));
+    pl->off_cnt = take(sizeof(unsigned) * (size_t)(3 * units));
+    pl->off_cs1 = take(sizeof(float) * (size_t)n1(units * s1 * pl->kcap1));
+    pl->off_ci1 = take(sizeof(int32_t) * (size_t)n1(units * s1 * pl->kcap1));
+    pl->off_lse1 = take(sizeof(float) * (size_t)n1(units * s1 * 2));
+    pl->off_cs2 = take(sizeof(float) * (size_t)n1(units * pl->S2 * pl->kcap2));
+    pl->off_ci2 = take(sizeof(int32_t) * (size_t)n1(units * pl->S2 * pl->kcap2));
+    pl->off_sel = take(sizeof(int32_t) * (size_t)n1(units * p->k));
+    pl->off_gamma = take(sizeof(float) * (size_t)n1(units * p->k));
+    pl->off_gsel = take(sizeof(int32_t) * (size_t)n1(units * p->k2));
     pl->off_acc = take(sizeof(float) * (size_t)(BH * pl->nslots * p->d));
     pl->off_ml = take(sizeof(float) * (size_t)(BH * pl->nslots * 2));
     pl->total = off;
@@ -199,6 +210,7 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     char* ws = (char*)workspace;
     const int units = p->B * p->Hkv;
     const int cap = p->gist_cap > 0 ? p->gist_cap : pl.H;
+    unsigned* cnt = (unsigned*)(ws + pl.off_cnt);
     Partials part{(float*)(ws + pl.off_acc), (float*)(ws + pl.off_ml), pl.nslots};
     int32_t* sel_p = sel ? sel : (int32_t*)(ws + pl.off_sel);
     float* gamma = p->gate_mode == TCS_GATE_SAS ? (float*)(ws + pl.off_gamma) : nullptr;
@@ -210,83 +222,93 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     ga.B = p->B; ga.Hq = p->Hq; ga.Hkv = p->Hkv; ga.d = p->d; ga.g = p->g;
     ga.sigma = pl.sigma;
     ga.part = part;
+    ga.J = p->J; ga.k2 = p->k2; ga.H = pl.H;
 
+    tcs::SelectOut chunk_sel{};   // the pass that chooses chunks
+    chunk_sel.k = p->k;
+    chunk_sel.sel = sel_p;
+    chunk_sel.cand_score = (float*)(ws + pl.off_cs1);
+    chunk_sel.cand_idx = (int32_t*)(ws + pl.off_ci1);
+    chunk_sel.kcap = pl.kcap1;
+    chunk_sel.J = p->J;
+    chunk_sel.H = pl.H;
+
+    bool chunks_chosen = false;
     if (p->levels == 1) {
-        float* scores = chunk_scores ? chunk_scores : (float*)(ws + pl.off_scores);
+        chunk_sel.gamma = gamma;
+        chunk_sel.slice_lse = gamma ? (float*)(ws + pl.off_lse1) : nullptr;
+        chunk_sel.counter = cnt;
         ga.gk = (const uint16_t*)gist_k;
         ga.gv = (const uint16_t*)gist_v;
         ga.unit_stride = (long long)cap * p->g * p->d;
-        ga.nchunks = pl.H;
+        ga.nitems = pl.H;
         ga.slices = pl.S1;
-        ga.chunks_per_slice = pl.cps1;
+        ga.items_per_slice = pl.cps1;
         ga.groups = nullptr;
-        ga.scores = scores;
+        ga.scores_out = chunk_scores;
         ga.score_stride = pl.H;
         ga.slot0 = slot;
+        ga.selo = chunk_sel;
         e = tcs::launch_gist(ga, s);
         if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
         slot += pl.S1;
-
-        tcs::SelectLaunch sa{};
-        sa.units = units; sa.scores = scores; sa.score_stride = pl.H; sa.n = pl.H;
-        sa.k = p->k; sa.sel = sel_p; sa.gamma = gamma;
-        sa.groups = nullptr;
-        e = tcs::launch_select(sa, s);
-        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+        chunks_chosen = pl.S1 > 0;
     } else {
-        float* gscores = (float*)(ws + pl.off_gscores);
         int32_t* gsel = sel_groups ? sel_groups : (int32_t*)(ws + pl.off_gsel);
-        float* cscores = (float*)(ws + pl.off_scores);
-        // level 2: every group
+        // level 2: every group, choosing k2 of them
+        tcs::SelectOut gs{};
+        gs.k = p->k2;
+        gs.sel = gsel;
+        gs.cand_score = (float*)(ws + pl.off_cs2);
+        gs.cand_idx = (int32_t*)(ws + pl.off_ci2);
+        gs.kcap = pl.kcap2;
+        gs.counter = cnt + units;
+        gs.fill_scores = chunk_scores;
+        gs.J = p->J;
+        gs.H = pl.H;
         ga.gk = (const uint16_t*)gist2_k;
         ga.gv = (const uint16_t*)gist2_v;
         ga.unit_stride = (long long)pl.nG * p->g * p->d;
-        ga.nchunks = pl.nG;
+        ga.nitems = pl.nG;
         ga.slices = pl.S2;
-        ga.chunks_per_slice = pl.cps2;
+        ga.items_per_slice = pl.cps2;
         ga.groups = nullptr;
-        ga.scores = gscores;
-        ga.score_stride = pl.nG;
+        ga.scores_out = nullptr;
+        ga.score_stride = 0;
         ga.slot0 = slot;
+        ga.selo = gs;
         e = tcs::launch_gist(ga, s);
         if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
         slot += pl.S2;
+        if (pl.S2 == 0 && sel_groups && p->k2 > 0) {
+            e = tcs::launch_fill(sel_groups, (long long)units * p->k2, -1, s);
+            if (e != hipSuccess) return TCS_ERR_HIP;
+        }
 
-        tcs::SelectLaunch sg{};
-        sg.units = units; sg.scores = gscores; sg.score_stride = pl.nG; sg.n = pl.nG;
-        sg.k = p->k2; sg.sel = gsel; sg.gamma = nullptr; sg.groups = nullptr;
-        e = tcs::launch_select(sg, s);
-        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
-
-        // level 1: the members of the chosen groups
+        // level 1: the member chunks of the chosen groups
+        chunk_sel.gamma = nullptr;
+        chunk_sel.slice_lse = nullptr;
+        chunk_sel.counter = cnt;
         ga.gk = (const uint16_t*)gist_k;
         ga.gv = (const uint16_t*)gist_v;
         ga.unit_stride = (long long)cap * p->g * p->d;
-        ga.nchunks = pl.H;
+        ga.nitems = pl.H;
         ga.slices = pl.k2e;
+        ga.items_per_slice = p->J;
         ga.groups = gsel;
-        ga.J = p->J; ga.k2 = p->k2; ga.H = pl.H;
-        ga.scores = cscores;
-        ga.score_stride = pl.k2e * p->J;
+        ga.scores_out = chunk_scores;
+        ga.score_stride = pl.H;
         ga.slot0 = slot;
+        ga.selo = chunk_sel;
         e = tcs::launch_gist(ga, s);
         if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
         slot += pl.k2e;
-
-        tcs::SelectLaunch sa{};
-        sa.units = units; sa.scores = cscores; sa.score_stride = pl.k2e * p->J; sa.n = 0;
-        sa.k = p->k; sa.sel = sel_p; sa.gamma = nullptr;
-        sa.groups = gsel; sa.J = p->J; sa.k2 = p->k2; sa.H = pl.H;
-        sa.chunk_scores_out = chunk_scores;
-        if (p->k > 0) {
-            e = tcs::launch_select(sa, s);
-        } else if (chunk_scores && pl.H > 0) {
-            // nothing selected, but the caller asked for the candidates' scores
-            sa.k = 1;
-            sa.sel = (int32_t*)(ws + pl.off_sel);
-            e = tcs::launch_select(sa, s);
-        }
-        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+        chunks_chosen = pl.k2e > 0;
+    }
+    if (!chunks_chosen && p->k > 0) {
+        // no scoring pass ran (no historical chunk, or no group chosen): nothing is selected
+        e = tcs::launch_fill(sel_p, (long long)units * p->k, -1, s);
+        if (e != hipSuccess) return TCS_ERR_HIP;
     }
 
     tcs::ChunkLaunch ca{};
@@ -298,11 +320,10 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
     ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots;
     ca.sigma = pl.sigma; ca.part = part; ca.slot0 = slot;
+    ca.counter = cnt + 2 * units;
+    ca.out = out;
+    ca.lse = lse;
     e = tcs::launch_chunks(ca, s);
-    if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
-
-    tcs::CombineLaunch cb{part, p->B * p->Hq, p->d, out, lse};
-    e = tcs::launch_combine(cb, s);
     if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
     return TCS_OK;
 }
@@ -334,7 +355,15 @@ tcs_status sparse_attn_decode_timed(const tcs_decode_params* p, const void* q,
 int tcs_decode_stage_count(const tcs_decode_params* p) {
     DecodePlan pl;
     if (plan_decode(p, &pl) != TCS_OK) return -1;
-    return p->levels == 2 ? 6 : 4;
+    return p->levels == 2 ? 3 : 2;
+}
+
+tcs_status tcs_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (workspace_bytes == 0) return TCS_OK;
+    if (!workspace || ((uintptr_t)workspace % kAlign)) return TCS_ERR_WORKSPACE;
+    if (tcs::launch_zero(workspace, workspace_bytes, (hipStream_t)stream) != hipSuccess)
+        return TCS_ERR_HIP;
+    return TCS_OK;
 }
 
 tcs_status tcs_prefill_workspace_size(const tcs_prefill_params* p, size_t* bytes) {

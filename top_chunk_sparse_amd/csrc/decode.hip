@@ -190,172 +190,243 @@ __device__ __forceinline__ void write_empty_partial(const Partials& P, int bh0, 
 constexpr int kMaxSliceRows = 1024;
 
 // ---------------------------------------------------------------------------------------
-// gist_kernel: grid (slices, units).  Range mode: slice y covers chunks
-// [y*cps, min((y+1)*cps, nchunks)).  Group mode (a.groups != null): slice y covers the members
-// of level-2 group r = groups[u][y] (chunks [r*J, min((r+1)*J, H))); scores are written at the
-// compact candidate position y*J + offset.
+// Selection epilogue shared by the scoring passes.  Each workgroup keeps the best
+// min(k, items in its slice) of its slice's items (ascending), stores them with their
+// scores, and the last workgroup of the unit to finish merges the slices' lists (which are
+// in ascending item order, slice after slice) into the unit's top-k.  Ties go to the lower
+// item index at both steps, so the result equals a top-k over all items at once.
 // ---------------------------------------------------------------------------------------
+__device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
+                                const float* s_score, int item0, int nitems, int last_items,
+                                float* lse_part_lds, void* scratch, int* s_flag, int* s_chosen,
+                                ReduceSmem& red) {
+    const int tid = threadIdx.x;
+    const int kc = so.k < nitems ? so.k : nitems;
+    float* cs = so.cand_score + ((long long)u * nslices + slot) * so.kcap;
+    int32_t* ci = so.cand_idx + ((long long)u * nslices + slot) * so.kcap;
+    // slice statistics for the gate: max and sum of exp over this slice's scores
+    if (so.slice_lse) {
+        float mx = -INFINITY;
+        for (int i = tid; i < nitems; i += 256) mx = fmaxf(mx, s_score[i]);
+        mx = block_max(mx, red);
+        float z = 0.f;
+        for (int i = tid; i < nitems; i += 256) z += expf(s_score[i] - mx);
+        z = block_sum(z, red);
+        if (tid == 0) {
+            so.slice_lse[((long long)u * nslices + slot) * 2] = mx;
+            so.slice_lse[((long long)u * nslices + slot) * 2 + 1] = z;
+        }
+    }
+    auto emit = [&](int j, int i) { cs[j] = s_score[i]; ci[j] = item0 + i; };
+    auto sc = [&](int i) { return s_score[i]; };
+    if (kc == nitems) {
+        for (int i = tid; i < nitems; i += 256) emit(i, i);
+    } else if (nitems <= 256) {
+        small_topk(nitems, so.k, sc, emit, *reinterpret_cast<SmallTopkSmem*>(scratch));
+    } else {
+        block_topk(nitems, so.k, sc, emit, *reinterpret_cast<TopkSmem*>(scratch));
+    }
+    if (!arrive_last(so.counter + u, (unsigned)nslices, s_flag)) return;
+
+    // ---- last workgroup of the unit: merge ------------------------------------------------
+    const float* ucs = so.cand_score + (long long)u * nslices * so.kcap;
+    const int32_t* uci = so.cand_idx + (long long)u * nslices * so.kcap;
+    const int ncand = (nslices - 1) * so.kcap + (so.k < last_items ? so.k : last_items);
+    float lse = 0.f;
+    if (so.slice_lse && so.gamma) {
+        const float* sl = so.slice_lse + (long long)u * nslices * 2;
+        if (tid == 0) {
+            float mx = -INFINITY;
+            for (int s = 0; s < nslices; ++s) mx = fmaxf(mx, sl[2 * s]);
+            float z = 0.f;
+            for (int s = 0; s < nslices; ++s) z += sl[2 * s + 1] * expf(sl[2 * s] - mx);
+            *lse_part_lds = mx + logf(z);
+        }
+        __syncthreads();
+        lse = *lse_part_lds;
+    }
+    int32_t* sel = so.sel + (long long)u * so.k;
+    float* gam = so.gamma ? so.gamma + (long long)u * so.k : nullptr;
+    auto emit2 = [&](int j, int i) {
+        sel[j] = uci[i];
+        if (gam) gam[j] = ucs[i] - lse;
+        if (j < 64) s_chosen[j] = uci[i];
+    };
+    auto sc2 = [&](int i) { return ucs[i]; };
+    int ke;
+    if (so.k >= ncand) {
+        for (int i = tid; i < ncand; i += 256) emit2(i, i);
+        ke = ncand;
+    } else if (ncand <= 256) {
+        ke = small_topk(ncand, so.k, sc2, emit2, *reinterpret_cast<SmallTopkSmem*>(scratch));
+    } else {
+        ke = block_topk(ncand, so.k, sc2, emit2, *reinterpret_cast<TopkSmem*>(scratch));
+    }
+    for (int j = ke + tid; j < so.k; j += 256) {
+        sel[j] = -1;
+        if (gam) gam[j] = 0.f;
+    }
+    if (so.fill_scores) {
+        // two-level group pass: chunks outside the chosen groups are never scored
+        __syncthreads();
+        float* fs = so.fill_scores + (long long)u * so.H;
+        for (int c = tid; c < so.H; c += 256) {
+            const int r = c / so.J;
+            bool in = false;
+            for (int j = 0; j < ke && j < 64; ++j) in |= s_chosen[j] == r;
+            if (!in) fs[c] = -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// gist_kernel: grid (slices, units).  Range mode: slice y covers items (chunks, or level-2
+// groups) [y*ips, min((y+1)*ips, nitems)).  Group mode (a.groups != null): slice y covers the
+// member chunks of level-2 group groups[u][y].  Streams the slice's gist rows once: logits
+// for the G heads, pooled item scores, the gist softmax partial, then the selection epilogue.
+// ---------------------------------------------------------------------------------------
+template <int D, int G>
+struct GistSmem {
+    union {
+        float logits[kMaxSliceRows * G];
+        float fin[RowAttn<D, G>::NW * G * (D + 2)];
+        TopkSmem topk;
+        SmallTopkSmem small;
+    } x;
+    float score[kMaxSliceRows];
+    ReduceSmem red;
+    float lse;
+    int flag;
+    int chosen[64];
+};
+
 template <int D, int G>
 __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
     using RA = RowAttn<D, G>;
-    __shared__ float s_logits[kMaxSliceRows * G];
-    __shared__ float s_fin[RA::NW * G * (D + 2)];
+    __shared__ GistSmem<D, G> sm;
     const int y = blockIdx.x, u = blockIdx.y;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
-    int c0, c1, spos;
+    int c0, c1, last_items;
     if (a.groups) {
         const int r = a.groups[(long long)u * a.k2 + y];
-        if (r < 0) {
-            write_empty_partial(a.part, bh0, G, D, a.slot0 + y, 0.f, 0.f);
-            return;
-        }
         c0 = r * a.J;
         c1 = min(c0 + a.J, a.H);
-        spos = y * a.J;
+        const int rl = a.groups[(long long)u * a.k2 + a.slices - 1];
+        last_items = min(a.J, a.H - rl * a.J);
     } else {
-        c0 = y * a.chunks_per_slice;
-        c1 = min(c0 + a.chunks_per_slice, a.nchunks);
-        spos = c0;
+        c0 = y * a.items_per_slice;
+        c1 = min(c0 + a.items_per_slice, a.nitems);
+        last_items = a.nitems - (a.slices - 1) * a.items_per_slice;
     }
-    const int nch = max(c1 - c0, 0);
-    const int nrows = nch * a.g;
+    const int nit = max(c1 - c0, 0);
+    const int nrows = nit * a.g;
     RA ra;
     ra.init(a.q + (long long)bh0 * D);
     const uint16_t* K = a.gk + (long long)u * a.unit_stride + (long long)c0 * a.g * D;
     const uint16_t* V = a.gv + (long long)u * a.unit_stride + (long long)c0 * a.g * D;
-    ra.template run<4>(K, V, nrows, a.sigma, 0.f, s_logits);
+    ra.template run<4>(K, V, nrows, a.sigma, 0.f, sm.x.logits);
     __syncthreads();
-    // pooled chunk scores: log-sum-exp over the G heads and g gists of each chunk
-    for (int c = threadIdx.x; c < nch; c += 256) {
-        const float* x = s_logits + (long long)c * a.g * G;
+    // pooled item scores: log-sum-exp over the G heads and g gists of each item
+    for (int c = threadIdx.x; c < nit; c += 256) {
+        const float* x = sm.x.logits + c * a.g * G;
         float mx = -INFINITY;
         for (int i = 0; i < a.g * G; ++i) mx = fmaxf(mx, x[i]);
         float z = 0.f;
         for (int i = 0; i < a.g * G; ++i) z += expf(x[i] - mx);
-        a.scores[(long long)u * a.score_stride + spos + c] = mx + logf(z);
+        const float s = mx + logf(z);
+        sm.score[c] = s;
+        if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
     }
-    ra.finish(s_fin, a.part, bh0, a.slot0 + y);
-}
-
-// ---------------------------------------------------------------------------------------
-// select_kernel: grid (units).  Top-k over a unit's scores and the SAS gate.
-// ---------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) select_kernel(SelectLaunch a) {
-    __shared__ TopkSmem sm;
-    __shared__ ReduceSmem red;
-    __shared__ int s_groups[64];
-    __shared__ int s_ncand;
-    const int u = blockIdx.x;
-    const float* s = a.scores + (long long)u * a.score_stride;
-    int n = a.n;
-    if (a.groups) {
-        // candidates: members of the chosen groups, in ascending group order
-        if (threadIdx.x == 0) {
-            int cnt = 0, ng = 0;
-            for (int y = 0; y < a.k2; ++y) {
-                const int r = a.groups[(long long)u * a.k2 + y];
-                if (y < 64) s_groups[y] = r;
-                if (r >= 0) { ng = y + 1; cnt = y * a.J + min(a.J, a.H - r * a.J); }
-            }
-            (void)ng;
-            s_ncand = cnt;
-        }
-        __syncthreads();
-        n = s_ncand;
-        if (a.chunk_scores_out) {
-            float* cs = a.chunk_scores_out + (long long)u * a.H;
-            for (int c = threadIdx.x; c < a.H; c += 256) cs[c] = -INFINITY;
-            __syncthreads();
-            for (int p = threadIdx.x; p < n; p += 256) {
-                const int r = s_groups[p / a.J];
-                cs[r * a.J + p % a.J] = s[p];
-            }
-        }
-    }
-    int32_t* sel = a.sel + (long long)u * a.k;
-    float* gam = a.gamma ? a.gamma + (long long)u * a.k : nullptr;
-    float lse = 0.f;
-    if (gam && n > 0) {
-        float mx = -INFINITY;
-        for (int i = threadIdx.x; i < n; i += 256) mx = fmaxf(mx, s[i]);
-        mx = block_max(mx, red);
-        float z = 0.f;
-        for (int i = threadIdx.x; i < n; i += 256) z += expf(s[i] - mx);
-        z = block_sum(z, red);
-        lse = mx + logf(z);
-    }
-    const int J = a.J;
-    const bool gm = a.groups != nullptr;
-    const int ke = block_topk(
-        n, a.k, [&](int i) { return s[i]; },
-        [&](int j, int i) {
-            const int c = gm ? s_groups[i / J] * J + i % J : i;
-            sel[j] = c;
-            if (gam) gam[j] = s[i] - lse;
-        },
-        sm);
-    for (int j = max(ke, 0) + threadIdx.x; j < a.k; j += 256) {
-        sel[j] = -1;
-        if (gam) gam[j] = 0.f;
-    }
+    __syncthreads();
+    ra.finish(sm.x.fin, a.part, bh0, a.slot0 + y);
+    __syncthreads();
+    select_epilogue(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.lse, &sm.x,
+                    &sm.flag, sm.chosen, sm.red);
 }
 
 // ---------------------------------------------------------------------------------------
 // chunk_kernel: grid (kslots + 1, units).  Slot j < kslots: selected chunk sel[u][j] (an
-// empty partial for -1); slot kslots: the current chunk (tokens [(M-1)C, N)).
+// empty partial for -1); slot kslots: the current chunk (tokens [(M-1)C, N)).  The last
+// workgroup of a unit merges every partial of the unit's G heads in slot order.
 // ---------------------------------------------------------------------------------------
+template <int D, int G>
+struct ChunkSmem {
+    float fin[RowAttn<D, G>::NW * G * (D + 2)];
+    float M[G], L[G];
+    int flag;
+};
+
 template <int D, int G>
 __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
     using RA = RowAttn<D, G>;
-    __shared__ float s_fin[RA::NW * G * (D + 2)];
+    __shared__ ChunkSmem<D, G> sm;
     const int j = blockIdx.x, u = blockIdx.y;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
-    int c, nrows;
+    int c = -1, nrows = 0;
     float bias = 0.f;
     if (j < a.kslots) {
         c = a.sel[(long long)u * a.k + j];
-        if (c < 0) {
-            write_empty_partial(a.part, bh0, G, D, a.slot0 + j, 0.f, 0.f);
-            return;
-        }
-        if (a.gamma) bias = a.gamma[(long long)u * a.k + j];
+        if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
         nrows = a.C;
     } else {
         c = a.M - 1;
         nrows = a.N - (a.M - 1) * a.C;
     }
-    const int page = a.page_table[(long long)b * a.max_chunks + c];
-    if (page < 0 || page >= a.num_pages) {
-        write_empty_partial(a.part, bh0, G, D, a.slot0 + j, NAN, NAN);
-        return;
+    if (c < 0) {
+        write_empty_partial(a.part, bh0, G, D, a.slot0 + j, 0.f, 0.f);
+    } else {
+        const int page = a.page_table[(long long)b * a.max_chunks + c];
+        if (page < 0 || page >= a.num_pages) {
+            write_empty_partial(a.part, bh0, G, D, a.slot0 + j, NAN, NAN);
+        } else {
+            const long long off = ((long long)page * a.Hkv + kv) * a.C * D;
+            RA ra;
+            ra.init(a.q + (long long)bh0 * D);
+            ra.template run<4>(a.kp + off, a.vp + off, nrows, a.sigma, bias, nullptr);
+            ra.finish(sm.fin, a.part, bh0, a.slot0 + j);
+        }
     }
-    const long long off = ((long long)page * a.Hkv + kv) * a.C * D;
-    RA ra;
-    ra.init(a.q + (long long)bh0 * D);
-    ra.template run<4>(a.kp + off, a.vp + off, nrows, a.sigma, bias, nullptr);
-    ra.finish(s_fin, a.part, bh0, a.slot0 + j);
+    if (!arrive_last(a.counter + u, (unsigned)(a.kslots + 1), &sm.flag)) return;
+
+    // ---- last workgroup of the unit: fixed-order merge of all slots ------------------------
+    const int ns = a.part.nslots;
+    if (threadIdx.x < G) {
+        const float* ml = a.part.ml + (long long)(bh0 + threadIdx.x) * ns * 2;
+        float mx = kNegBig;
+        for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[2 * s]);
+        float L = 0.f;
+        for (int s = 0; s < ns; ++s) L += __expf(ml[2 * s] - mx) * ml[2 * s + 1];
+        sm.M[threadIdx.x] = mx;
+        sm.L[threadIdx.x] = L;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+        const int h = idx / D, col = idx % D;
+        const float* ml = a.part.ml + (long long)(bh0 + h) * ns * 2;
+        const float* acc = a.part.acc + (long long)(bh0 + h) * ns * D + col;
+        const float mx = sm.M[h];
+        float o = 0.f;
+        for (int s = 0; s < ns; ++s) o += __expf(ml[2 * s] - mx) * acc[(long long)s * D];
+        a.out[(long long)(bh0 + h) * D + col] = o / sm.L[h];
+        if (a.lse && col == 0) a.lse[bh0 + h] = mx + logf(sm.L[h]);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
-// combine_kernel: grid (B*Hq), block D.  Fixed-order merge of all slots.
+// zero_kernel: clears a workspace region (used once per workspace, before its first call).
 // ---------------------------------------------------------------------------------------
-__global__ void combine_kernel(CombineLaunch a) {
-    const int bh = blockIdx.x, col = threadIdx.x;
-    const int ns = a.part.nslots, D = a.d;
-    const float* ml = a.part.ml + (long long)bh * ns * 2;
-    const float* acc = a.part.acc + (long long)bh * ns * D;
-    float mx = kNegBig;
-    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[2 * s]);
-    float L = 0.f, o = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float f = __expf(ml[2 * s] - mx);
-        L += f * ml[2 * s + 1];
-        o += f * acc[(long long)s * D + col];
-    }
-    a.out[(long long)bh * D + col] = o / L;
-    if (a.lse && col == 0) a.lse[bh] = mx + logf(L);
+__global__ void zero_kernel(unsigned* p, long long n) {
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+__global__ void fill_kernel(int32_t* p, long long n, int32_t v) {
+    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x)
+        p[i] = v;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -374,15 +445,9 @@ static hipError_t gist_d(const GistLaunch& a, hipStream_t s, dim3 grid) {
 }
 
 hipError_t launch_gist(const GistLaunch& a, hipStream_t s) {
-    dim3 grid(a.slices, a.B * a.Hkv);
     if (a.slices <= 0) return hipSuccess;
+    dim3 grid(a.slices, a.B * a.Hkv);
     return a.d == 128 ? gist_d<128>(a, s, grid) : gist_d<64>(a, s, grid);
-}
-
-hipError_t launch_select(const SelectLaunch& a, hipStream_t s) {
-    if (a.k <= 0 || a.units <= 0) return hipSuccess;
-    select_kernel<<<a.units, 256, 0, s>>>(a);
-    return hipGetLastError();
 }
 
 template <int D>
@@ -402,8 +467,20 @@ hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s) {
     return a.d == 128 ? chunk_d<128>(a, s, grid) : chunk_d<64>(a, s, grid);
 }
 
-hipError_t launch_combine(const CombineLaunch& a, hipStream_t s) {
-    combine_kernel<<<a.BH, a.d, 0, s>>>(a);
+hipError_t launch_fill(int32_t* p, long long n, int32_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    long long blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    fill_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+    const long long n = (long long)(bytes / sizeof(unsigned));
+    if (n <= 0) return hipSuccess;
+    long long blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    zero_kernel<<<(unsigned)blocks, 256, 0, s>>>((unsigned*)p, n);
     return hipGetLastError();
 }
 

@@ -110,6 +110,7 @@ struct TopkSmem {
     uint32_t keys[kTopkCache];
     int digit;
     unsigned above;
+    uint32_t band[4], bor[4];
     ScanSmem scan;
 };
 
@@ -126,9 +127,33 @@ __device__ int block_topk(int n, int k, ScoreFn score, EmitFn emit, TopkSmem& sm
     __syncthreads();
     auto key_at = [&](int i) -> uint32_t { return cached ? sm.keys[i] : ordered_key(score(i)); };
 
-    uint32_t prefix = 0, mask = 0;
+    // Bytes shared by every key need no histogram pass: start at the first byte that differs.
+    uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+    for (int i = tid; i < n; i += 256) {
+        const uint32_t key = key_at(i);
+        kand &= key;
+        kor |= key;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        kand &= (uint32_t)__shfl_xor((int)kand, off);
+        kor |= (uint32_t)__shfl_xor((int)kor, off);
+    }
+    if ((tid & 63) == 0) { sm.band[tid >> 6] = kand; sm.bor[tid >> 6] = kor; }
+    __syncthreads();
+    kand = sm.band[0] & sm.band[1] & sm.band[2] & sm.band[3];
+    kor = sm.bor[0] | sm.bor[1] | sm.bor[2] | sm.bor[3];
+    __syncthreads();
+    const uint32_t diff = kand ^ kor;
+    int start = -8;
+    uint32_t mask = 0xFFFFFFFFu;
+    if (diff) {
+        start = ((31 - __clz(diff)) / 8) * 8;
+        mask = start == 24 ? 0u : (0xFFFFFFFFu << (start + 8));
+    }
+    uint32_t prefix = kand & mask;
     unsigned remaining = (unsigned)ke;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = start; shift >= 0; shift -= 8) {
         sm.hist[tid] = 0u;
         __syncthreads();
         for (int i = tid; i < n; i += 256) {
@@ -188,6 +213,64 @@ __device__ int block_topk(int n, int k, ScoreFn score, EmitFn emit, TopkSmem& sm
     }
     __syncthreads();
     return ke;
+}
+
+
+// ---- small exact top-k by rank counting -------------------------------------------------
+// n <= 256 candidates, candidate i owned by thread i, given in ascending index order.  The
+// ranking key is (ordered score, then lower position first); candidate i is chosen iff fewer
+// than k_eff candidates outrank it, and is emitted at its position among the chosen ones,
+// which keeps the output ascending.
+struct SmallTopkSmem {
+    unsigned long long key[256];
+    int chosen[256];
+};
+
+template <class ScoreFn, class EmitFn>
+__device__ int small_topk(int n, int k, ScoreFn score, EmitFn emit, SmallTopkSmem& sm) {
+    const int t = threadIdx.x;
+    const int ke = k < n ? k : n;
+    if (ke <= 0) return 0;
+    unsigned long long mine = 0ull;
+    if (t < n) {
+        mine = ((unsigned long long)ordered_key(score(t)) << 32) | (0xFFFFFFFFu - (unsigned)t);
+        sm.key[t] = mine;
+    }
+    __syncthreads();
+    bool take = false;
+    if (t < n) {
+        int rank = 0;
+        for (int j = 0; j < n; ++j) rank += sm.key[j] > mine;
+        take = rank < ke;
+    }
+    sm.chosen[t] = take;
+    __syncthreads();
+    if (take) {
+        int pos = 0;
+        for (int j = 0; j < t; ++j) pos += sm.chosen[j];
+        emit(pos, t);
+    }
+    __syncthreads();
+    return ke;
+}
+
+// ---- cross-workgroup hand-off ---------------------------------------------------------------
+// Every workgroup of a unit calls arrive() after writing its results; exactly one -- the last
+// to arrive -- gets true, after which it may read what the others wrote.  The counter is
+// returned to zero by that last workgroup, so a zeroed counter stays zeroed between calls.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, int* s_flag) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = atomicAdd(counter, 1u);
+        const bool last = old == total - 1u;
+        if (last) atomicExch(counter, 0u);
+        *s_flag = last;
+    }
+    __syncthreads();
+    const bool last = *s_flag != 0;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return last;
 }
 
 }  // namespace tcs

@@ -13,36 +13,37 @@ struct Partials {
     int nslots;
 };
 
+// Selection done by the last workgroup of each unit (see select_epilogue).
+struct SelectOut {
+    int k;                    // entries per unit in sel / gamma
+    int32_t* sel;             // [units][k] ascending item ids, -1 padded
+    float* gamma;             // [units][k] SAS gate (log of the softmax over all items) or null
+    float* cand_score;        // [units][slices][kcap] per-slice candidates
+    int32_t* cand_idx;        // [units][slices][kcap]
+    int kcap;                 // min(k, items per slice)
+    float* slice_lse;         // [units][slices][2] (max, sum exp) or null
+    unsigned* counter;        // [units], zero between calls
+    float* fill_scores;       // optional [units][H]: -inf outside the chosen groups (level 2)
+    int J, H;
+};
+
 struct GistLaunch {
     const uint16_t* q;
     const uint16_t* gk;
     const uint16_t* gv;
     long long unit_stride;    // elements between consecutive (b, kv) gist blocks
     int B, Hq, Hkv, d, g;
-    int nchunks;              // chunks (or level-2 groups) in the scored range
-    int slices;               // grid.x: slices of the range (range mode) or k2 (group mode)
-    int chunks_per_slice;     // range mode
-    const int32_t* groups;    // group mode: [units][k2] selected groups (-1 padded)
+    int nitems;               // range mode: items (chunks or level-2 groups) scored
+    int slices;               // grid.x
+    int items_per_slice;      // range mode
+    const int32_t* groups;    // group mode: [units][k2] chosen level-2 groups
     int J, k2, H;             // group mode
     float sigma;
-    float* scores;            // [units][score_stride]
+    float* scores_out;        // optional [units][score_stride], indexed by item id
     int score_stride;
     Partials part;
     int slot0;
-};
-
-struct SelectLaunch {
-    int units;
-    const float* scores;      // [units][score_stride]
-    int score_stride;
-    int n;                    // scores per unit (range mode)
-    int k;                    // slots per unit in sel
-    int32_t* sel;             // [units][k]
-    float* gamma;             // [units][k] or null (SAS gate)
-    // group mode (two-level candidates): position p -> chunk groups[u][p / J]*J + p % J
-    const int32_t* groups;
-    int J, k2, H;
-    float* chunk_scores_out;  // optional [units][H]: candidates' scores, -inf elsewhere
+    SelectOut selo;
 };
 
 struct ChunkLaunch {
@@ -59,19 +60,15 @@ struct ChunkLaunch {
     float sigma;
     Partials part;
     int slot0;
-};
-
-struct CombineLaunch {
-    Partials part;
-    int BH, d;
-    float* out;
-    float* lse;
+    unsigned* counter;        // [units], zero between calls
+    float* out;               // [B*Hq][d]
+    float* lse;               // [B*Hq] or null
 };
 
 hipError_t launch_gist(const GistLaunch& a, hipStream_t s);
-hipError_t launch_select(const SelectLaunch& a, hipStream_t s);
 hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s);
-hipError_t launch_combine(const CombineLaunch& a, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_fill(int32_t* p, long long n, int32_t v, hipStream_t s);
 
 struct PrefillSelectLaunch {
     const float* S;           // [units][nb][nb]

@@ -37,8 +37,8 @@ _V = C.c_void_p
 _lib = None
 
 EXPORTS = ("tcs_abi_version", "tcs_status_str", "tcs_decode_workspace_size", "sparse_attn_decode",
-           "sparse_attn_decode_timed", "tcs_decode_stage_count", "tcs_prefill_workspace_size",
-           "sparse_attn_prefill", "sparse_attn_prefill_timed")
+           "sparse_attn_decode_timed", "tcs_decode_stage_count", "tcs_workspace_init",
+           "tcs_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_prefill_timed")
 
 
 def lib():
@@ -59,6 +59,7 @@ def lib():
         h.sparse_attn_decode_timed.argtypes = h.sparse_attn_decode.argtypes + [_V, C.c_int]
         h.sparse_attn_prefill_timed.argtypes = h.sparse_attn_prefill.argtypes + [_V, C.c_int]
         h.tcs_decode_stage_count.argtypes = [C.POINTER(DecodeParams)]
+        h.tcs_workspace_init.argtypes = [_V, C.c_size_t, _V]
         _lib = h
     return _lib
 
@@ -139,9 +140,14 @@ def sparse_attn_prefill(p: PrefillParams, q, k, v, S, *, out, lse=None, sel=None
     _check(code)
 
 
-def workspace(nbytes: int, device) -> torch.Tensor:
-    """A caller-owned workspace (256-byte aligned by the torch allocator)."""
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+def workspace(nbytes: int, device, stream=None) -> torch.Tensor:
+    """A caller-owned workspace (256-byte aligned by the torch allocator), zero-filled by the
+    library's init kernel as a new decode workspace must be."""
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if stream is None:
+        stream = torch.cuda.current_stream(ws.device)
+    _check(lib().tcs_workspace_init(ws.data_ptr(), ws.numel(), stream.cuda_stream))
+    return ws
 
 
 # ---- convenience wrappers over the generator's input bundles ----------------------------
