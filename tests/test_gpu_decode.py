@@ -148,3 +148,27 @@ def test_workspace_reused_across_shapes():
             call()
             torch.cuda.synchronize()
             check_decode(call.inp, call)
+
+
+def test_repeated_calls_bitwise_identical_full_size():
+    """40 back-to-back calls alternating two full-size (128K-token) instances: every result
+    equals the first call's bit for bit (the cross-workgroup hand-off in the fused kernels
+    sees complete data every time)."""
+    cfg = configs.LLAMA8B
+    insts = [make_decode(cfg, configs.seed_for(cfg.name, r), device=DEV) for r in range(2)]
+    calls = [DecodeCall(i, with_scores=False) for i in insts]
+    ref = []
+    for c in calls:
+        c()
+        torch.cuda.synchronize()
+        ref.append((c.out.clone(), c.lse.clone(), c.sel.clone()))
+    for it in range(40):
+        c = calls[it % 2]
+        c()
+        if it % 8 == 7:
+            torch.cuda.synchronize()
+            o, l, s = ref[it % 2]
+            assert torch.equal(c.out, o) and torch.equal(c.lse, l) and torch.equal(c.sel, s), it
+    torch.cuda.synchronize()
+    del calls, insts
+    torch.cuda.empty_cache()

@@ -165,10 +165,10 @@ struct RowAttn {
                 s += f * lml[(ww * G + h) * 2 + 1];
             }
             const long long o = (long long)(bh0 + h) * P.nslots + slot;
-            P.acc[o * D + col] = a;
+            st_shared_dev(P.acc + o * D + col, a);
             if (col == 0) {
-                P.ml[o * 2] = mx;
-                P.ml[o * 2 + 1] = s;
+                st_shared_dev(P.ml + o * 2, mx);
+                st_shared_dev(P.ml + o * 2 + 1, s);
             }
         }
     }
@@ -179,10 +179,10 @@ __device__ __forceinline__ void write_empty_partial(const Partials& P, int bh0, 
     for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
         const int h = idx / D, col = idx % D;
         const long long o = (long long)(bh0 + h) * P.nslots + slot;
-        P.acc[o * D + col] = fill_acc;
+        st_shared_dev(P.acc + o * D + col, fill_acc);
         if (col == 0) {
-            P.ml[o * 2] = fill_l == fill_l ? kNegBig : 0.f;   // NaN fill: m = 0, l = NaN
-            P.ml[o * 2 + 1] = fill_l;
+            st_shared_dev(P.ml + o * 2, fill_l == fill_l ? kNegBig : 0.f);  // NaN fill: m = 0
+            st_shared_dev(P.ml + o * 2 + 1, fill_l);
         }
     }
 }
@@ -213,11 +213,14 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
         for (int i = tid; i < nitems; i += 256) z += expf(s_score[i] - mx);
         z = block_sum(z, red);
         if (tid == 0) {
-            so.slice_lse[((long long)u * nslices + slot) * 2] = mx;
-            so.slice_lse[((long long)u * nslices + slot) * 2 + 1] = z;
+            st_shared_dev(so.slice_lse + ((long long)u * nslices + slot) * 2, mx);
+            st_shared_dev(so.slice_lse + ((long long)u * nslices + slot) * 2 + 1, z);
         }
     }
-    auto emit = [&](int j, int i) { cs[j] = s_score[i]; ci[j] = item0 + i; };
+    auto emit = [&](int j, int i) {
+        st_shared_dev(cs + j, s_score[i]);
+        st_shared_dev(ci + j, (int32_t)(item0 + i));
+    };
     auto sc = [&](int i) { return s_score[i]; };
     if (kc == nitems) {
         for (int i = tid; i < nitems; i += 256) emit(i, i);
@@ -237,9 +240,10 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
         const float* sl = so.slice_lse + (long long)u * nslices * 2;
         if (tid == 0) {
             float mx = -INFINITY;
-            for (int s = 0; s < nslices; ++s) mx = fmaxf(mx, sl[2 * s]);
+            for (int s = 0; s < nslices; ++s) mx = fmaxf(mx, ld_shared_dev(sl + 2 * s));
             float z = 0.f;
-            for (int s = 0; s < nslices; ++s) z += sl[2 * s + 1] * expf(sl[2 * s] - mx);
+            for (int s = 0; s < nslices; ++s)
+                z += ld_shared_dev(sl + 2 * s + 1) * expf(ld_shared_dev(sl + 2 * s) - mx);
             *lse_part_lds = mx + logf(z);
         }
         __syncthreads();
@@ -248,11 +252,12 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
     int32_t* sel = so.sel + (long long)u * so.k;
     float* gam = so.gamma ? so.gamma + (long long)u * so.k : nullptr;
     auto emit2 = [&](int j, int i) {
-        sel[j] = uci[i];
-        if (gam) gam[j] = ucs[i] - lse;
-        if (j < 64) s_chosen[j] = uci[i];
+        const int32_t c = ld_shared_dev(uci + i);
+        sel[j] = c;
+        if (gam) gam[j] = ld_shared_dev(ucs + i) - lse;
+        if (j < 64) s_chosen[j] = c;
     };
-    auto sc2 = [&](int i) { return ucs[i]; };
+    auto sc2 = [&](int i) { return ld_shared_dev(ucs + i); };
     int ke;
     if (so.k >= ncand) {
         for (int i = tid; i < ncand; i += 256) emit2(i, i);
@@ -395,9 +400,10 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
     if (threadIdx.x < G) {
         const float* ml = a.part.ml + (long long)(bh0 + threadIdx.x) * ns * 2;
         float mx = kNegBig;
-        for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[2 * s]);
+        for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ld_shared_dev(ml + 2 * s));
         float L = 0.f;
-        for (int s = 0; s < ns; ++s) L += __expf(ml[2 * s] - mx) * ml[2 * s + 1];
+        for (int s = 0; s < ns; ++s)
+            L += __expf(ld_shared_dev(ml + 2 * s) - mx) * ld_shared_dev(ml + 2 * s + 1);
         sm.M[threadIdx.x] = mx;
         sm.L[threadIdx.x] = L;
     }
@@ -408,7 +414,8 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
         const float* acc = a.part.acc + (long long)(bh0 + h) * ns * D + col;
         const float mx = sm.M[h];
         float o = 0.f;
-        for (int s = 0; s < ns; ++s) o += __expf(ml[2 * s] - mx) * acc[(long long)s * D];
+        for (int s = 0; s < ns; ++s)
+            o += __expf(ld_shared_dev(ml + 2 * s) - mx) * ld_shared_dev(acc + (long long)s * D);
         a.out[(long long)(bh0 + h) * D + col] = o / sm.L[h];
         if (a.lse && col == 0) a.lse[bh0 + h] = mx + logf(sm.L[h]);
     }

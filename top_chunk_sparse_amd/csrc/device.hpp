@@ -255,11 +255,32 @@ __device__ int small_topk(int n, int k, ScoreFn score, EmitFn emit, SmallTopkSme
 }
 
 // ---- cross-workgroup hand-off ---------------------------------------------------------------
-// Every workgroup of a unit calls arrive() after writing its results; exactly one -- the last
-// to arrive -- gets true, after which it may read what the others wrote.  The counter is
-// returned to zero by that last workgroup, so a zeroed counter stays zeroed between calls.
+// On gfx950 each XCD has its own L2, and an agent-scope fence writes back and invalidates the
+// whole L2 -- far too slow to run in every workgroup.  Data handed from one workgroup to
+// another inside a kernel therefore travels through agent-scope relaxed atomic stores and
+// loads, which are performed at the device coherence point, and the fences below only order
+// (wait for outstanding memory operations); they make nothing visible by themselves.
+template <class T>
+__device__ __forceinline__ void st_shared_dev(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_shared_dev(const T* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt vmcnt(0) with expcnt / lgkmcnt left free (gfx9 encoding)
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+}
+
+// Every workgroup of a unit calls arrive_last() after writing its hand-off data with
+// st_shared_dev; exactly one -- the last to arrive -- gets true and may then read the others'
+// data with ld_shared_dev.  The last workgroup returns the counter to zero, so a zeroed
+// counter stays zeroed between calls.
 __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, int* s_flag) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    wait_vmem();                      // this wave's stores have reached the coherence point
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned old = atomicAdd(counter, 1u);
@@ -269,7 +290,10 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, i
     }
     __syncthreads();
     const bool last = *s_flag != 0;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (last) {
+        wait_vmem();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
     return last;
 }
 
