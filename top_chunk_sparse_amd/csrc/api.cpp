@@ -41,7 +41,7 @@ void plan_slices(long long units, int nchunks, int g, int* slices, int* cps) {
 }
 
 struct DecodePlan {
-    int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, nslots, kcap1, kcap2;
+    int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, cpw, nslots, kcap1, kcap2;
     float sigma;
     // workspace offsets (bytes)
     size_t off_cnt, off_cs1, off_ci1, off_lse1, off_cs2, off_ci2, off_sel, off_gamma, off_gsel,
@@ -98,7 +98,10 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
         pl->kcap1 = p->k < pl->cps1 ? p->k : pl->cps1;
     }
     pl->kslots = ksel;
-    pl->nslots = pl->S1 + pl->S2 + pl->k2e + ksel + 1;
+    // chunk attention: enough workgroups to fill the GPU, one or more chunks each
+    long long cpw = units * (ksel + 1) / kTargetWorkgroups;
+    pl->cpw = (int)(cpw < 1 ? 1 : cpw);
+    pl->nslots = pl->S1 + pl->S2 + pl->k2e + (ksel + 1 + pl->cpw - 1) / pl->cpw;
     const long long BH = (long long)p->B * p->Hq;
     const long long s1 = p->levels == 2 ? pl->k2e : pl->S1;     // slices of the chunk pass
     auto n1 = [](long long x) { return x > 0 ? x : 1; };
@@ -318,7 +321,7 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     ca.page_table = page_table;
     ca.B = p->B; ca.Hq = p->Hq; ca.Hkv = p->Hkv; ca.d = p->d; ca.C = p->C; ca.N = p->N;
     ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
-    ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots;
+    ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots; ca.cpw = pl.cpw;
     ca.sigma = pl.sigma; ca.part = part; ca.slot0 = slot;
     ca.counter = cnt + 2 * units;
     ca.out = out;

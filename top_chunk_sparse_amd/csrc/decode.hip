@@ -237,13 +237,19 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
     const int ncand = (nslices - 1) * so.kcap + (so.k < last_items ? so.k : last_items);
     float lse = 0.f;
     if (so.slice_lse && so.gamma) {
+        // every slice's (max, sum exp) loaded at once, then merged in slice order
         const float* sl = so.slice_lse + (long long)u * nslices * 2;
+        float* st = reinterpret_cast<float*>(scratch);     // 2 * nslices floats if they fit
+        const bool staged = 2 * nslices <= kTopkCache;
+        if (staged)
+            for (int i = tid; i < 2 * nslices; i += 256) st[i] = ld_shared_dev(sl + i);
+        __syncthreads();
+        auto at = [&](int i) { return staged ? st[i] : ld_shared_dev(sl + i); };
         if (tid == 0) {
             float mx = -INFINITY;
-            for (int s = 0; s < nslices; ++s) mx = fmaxf(mx, ld_shared_dev(sl + 2 * s));
+            for (int s = 0; s < nslices; ++s) mx = fmaxf(mx, at(2 * s));
             float z = 0.f;
-            for (int s = 0; s < nslices; ++s)
-                z += ld_shared_dev(sl + 2 * s + 1) * expf(ld_shared_dev(sl + 2 * s) - mx);
+            for (int s = 0; s < nslices; ++s) z += at(2 * s + 1) * expf(at(2 * s) - mx);
             *lse_part_lds = mx + logf(z);
         }
         __syncthreads();
@@ -355,10 +361,109 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
 // empty partial for -1); slot kslots: the current chunk (tokens [(M-1)C, N)).  The last
 // workgroup of a unit merges every partial of the unit's G heads in slot order.
 // ---------------------------------------------------------------------------------------
+constexpr int kMergeStage = 1024;   // (head, slot) softmax statistics staged in LDS
+
+template <int G>
+struct MergeSmem {
+    float w[kMergeStage];    // m, then exp(m - M)
+    float l[kMergeStage];
+    float M[G], L[G];
+};
+
+// Fixed-order merge of every slot's partial for the G heads of one unit -> out, lse.
+// All hand-off loads of a batch are issued before any is used, so the merge costs a few
+// memory round trips rather than one per slot.
+template <int D, int G>
+__device__ void merge_partials(const Partials& P, int bh0, float* out, float* lse,
+                               MergeSmem<G>& sm) {
+    const int ns = P.nslots;
+    const int tid = threadIdx.x;
+    const bool staged = G * ns <= kMergeStage;
+    if (staged) {
+        for (int i = tid; i < G * ns; i += 256) {
+            const float* ml = P.ml + ((long long)(bh0 + i / ns) * ns + i % ns) * 2;
+            sm.w[i] = ld_shared_dev(ml);
+            sm.l[i] = ld_shared_dev(ml + 1);
+        }
+        __syncthreads();
+    }
+    auto m_at = [&](int h, int s) {
+        return staged ? sm.w[h * ns + s] : ld_shared_dev(P.ml + ((long long)(bh0 + h) * ns + s) * 2);
+    };
+    auto l_at = [&](int h, int s) {
+        return staged ? sm.l[h * ns + s]
+                      : ld_shared_dev(P.ml + ((long long)(bh0 + h) * ns + s) * 2 + 1);
+    };
+    if (tid < G) {
+        float mx = kNegBig;
+        for (int s = 0; s < ns; ++s) mx = fmaxf(mx, m_at(tid, s));
+        float L = 0.f;
+        for (int s = 0; s < ns; ++s) L += __expf(m_at(tid, s) - mx) * l_at(tid, s);
+        sm.M[tid] = mx;
+        sm.L[tid] = L;
+    }
+    __syncthreads();
+    if (staged) {
+        for (int i = tid; i < G * ns; i += 256) sm.w[i] = __expf(sm.w[i] - sm.M[i / ns]);
+        __syncthreads();
+    }
+    constexpr int PPT = (G * D + 255) / 256;   // (head, column) outputs per thread
+    constexpr int SB = PPT <= 2 ? 16 : 8;      // slots per batch of loads
+    float o[PPT];
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) o[q] = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += SB) {
+        float v[PPT][SB];
+#pragma unroll
+        for (int q = 0; q < PPT; ++q) {
+            const int p = tid + q * 256;
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int s = s0 + j;
+                v[q][j] = (p < G * D && s < ns)
+                              ? ld_shared_dev(P.acc + ((long long)(bh0 + p / D) * ns + s) * D + p % D)
+                              : 0.f;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < PPT; ++q) {
+            const int p = tid + q * 256;
+            if (p < G * D) {
+                const int h = p / D;
+#pragma unroll
+                for (int j = 0; j < SB; ++j) {
+                    const int s = s0 + j;
+                    if (s < ns) {
+                        const float w = staged ? sm.w[h * ns + s] : __expf(m_at(h, s) - sm.M[h]);
+                        o[q] = fmaf(w, v[q][j], o[q]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+        const int p = tid + q * 256;
+        if (p < G * D) {
+            const int h = p / D, col = p % D;
+            out[(long long)(bh0 + h) * D + col] = o[q] / sm.L[h];
+            if (lse && col == 0) lse[bh0 + h] = sm.M[h] + logf(sm.L[h]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// chunk_kernel: grid (ceil((kslots + 1) / cpw), units).  Workgroup x streams slots
+// [x*cpw, (x+1)*cpw): slot j < kslots is selected chunk sel[u][j] (skipped if -1), slot
+// kslots is the current chunk (tokens [(M-1)C, N)).  Each chunk's raw tokens carry its gate
+// bias.  The last workgroup of a unit merges every partial of the unit's G heads.
+// ---------------------------------------------------------------------------------------
 template <int D, int G>
 struct ChunkSmem {
-    float fin[RowAttn<D, G>::NW * G * (D + 2)];
-    float M[G], L[G];
+    union {
+        float fin[RowAttn<D, G>::NW * G * (D + 2)];
+        MergeSmem<G> merge;
+    } x;
     int flag;
 };
 
@@ -366,59 +471,39 @@ template <int D, int G>
 __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
     using RA = RowAttn<D, G>;
     __shared__ ChunkSmem<D, G> sm;
-    const int j = blockIdx.x, u = blockIdx.y;
+    const int wx = blockIdx.x, u = blockIdx.y;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
-    int c = -1, nrows = 0;
-    float bias = 0.f;
-    if (j < a.kslots) {
-        c = a.sel[(long long)u * a.k + j];
-        if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
-        nrows = a.C;
-    } else {
-        c = a.M - 1;
-        nrows = a.N - (a.M - 1) * a.C;
-    }
-    if (c < 0) {
-        write_empty_partial(a.part, bh0, G, D, a.slot0 + j, 0.f, 0.f);
-    } else {
+    RA ra;
+    ra.init(a.q + (long long)bh0 * D);
+    bool bad_page = false;
+    const int j0 = wx * a.cpw, j1 = min(j0 + a.cpw, a.kslots + 1);
+    for (int j = j0; j < j1; ++j) {
+        int c, nrows;
+        float bias = 0.f;
+        if (j < a.kslots) {
+            c = a.sel[(long long)u * a.k + j];
+            if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
+            nrows = a.C;
+        } else {
+            c = a.M - 1;
+            nrows = a.N - (a.M - 1) * a.C;
+        }
+        if (c < 0) continue;
         const int page = a.page_table[(long long)b * a.max_chunks + c];
         if (page < 0 || page >= a.num_pages) {
-            write_empty_partial(a.part, bh0, G, D, a.slot0 + j, NAN, NAN);
-        } else {
-            const long long off = ((long long)page * a.Hkv + kv) * a.C * D;
-            RA ra;
-            ra.init(a.q + (long long)bh0 * D);
-            ra.template run<4>(a.kp + off, a.vp + off, nrows, a.sigma, bias, nullptr);
-            ra.finish(sm.fin, a.part, bh0, a.slot0 + j);
+            bad_page = true;
+            continue;
         }
+        const long long off = ((long long)page * a.Hkv + kv) * a.C * D;
+        ra.template run<4>(a.kp + off, a.vp + off, nrows, a.sigma, bias, nullptr);
     }
-    if (!arrive_last(a.counter + u, (unsigned)(a.kslots + 1), &sm.flag)) return;
-
-    // ---- last workgroup of the unit: fixed-order merge of all slots ------------------------
-    const int ns = a.part.nslots;
-    if (threadIdx.x < G) {
-        const float* ml = a.part.ml + (long long)(bh0 + threadIdx.x) * ns * 2;
-        float mx = kNegBig;
-        for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ld_shared_dev(ml + 2 * s));
-        float L = 0.f;
-        for (int s = 0; s < ns; ++s)
-            L += __expf(ld_shared_dev(ml + 2 * s) - mx) * ld_shared_dev(ml + 2 * s + 1);
-        sm.M[threadIdx.x] = mx;
-        sm.L[threadIdx.x] = L;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-        const int h = idx / D, col = idx % D;
-        const float* ml = a.part.ml + (long long)(bh0 + h) * ns * 2;
-        const float* acc = a.part.acc + (long long)(bh0 + h) * ns * D + col;
-        const float mx = sm.M[h];
-        float o = 0.f;
-        for (int s = 0; s < ns; ++s)
-            o += __expf(ld_shared_dev(ml + 2 * s) - mx) * ld_shared_dev(acc + (long long)s * D);
-        a.out[(long long)(bh0 + h) * D + col] = o / sm.L[h];
-        if (a.lse && col == 0) a.lse[bh0 + h] = mx + logf(sm.L[h]);
-    }
+    if (bad_page)
+        write_empty_partial(a.part, bh0, G, D, a.slot0 + wx, NAN, NAN);
+    else
+        ra.finish(sm.x.fin, a.part, bh0, a.slot0 + wx);
+    if (!arrive_last(a.counter + u, (unsigned)gridDim.x, &sm.flag)) return;
+    merge_partials<D, G>(a.part, bh0, a.out, a.lse, sm.x.merge);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -470,7 +555,8 @@ static hipError_t chunk_d(const ChunkLaunch& a, hipStream_t s, dim3 grid) {
 }
 
 hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s) {
-    dim3 grid(a.kslots + 1, a.B * a.Hkv);
+    if (a.cpw < 1) return hipErrorInvalidValue;
+    dim3 grid((a.kslots + 1 + a.cpw - 1) / a.cpw, a.B * a.Hkv);
     return a.d == 128 ? chunk_d<128>(a, s, grid) : chunk_d<64>(a, s, grid);
 }
 

@@ -57,6 +57,7 @@ struct ChunkLaunch {
     const float* gamma;       // [units][k] or null
     int k;                    // stride of sel / gamma
     int kslots;               // selected-chunk slots launched (current chunk is slot kslots)
+    int cpw;                  // slots streamed per workgroup
     float sigma;
     Partials part;
     int slot0;
