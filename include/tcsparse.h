@@ -69,7 +69,7 @@
  *   for); k = 0 keeps only the gists and the current chunk.  Results are deterministic:
  *   no floating-point atomics; the same inputs give bitwise-identical outputs.
  *
- * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; two levels:
+ * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024; two levels:
  * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk.
  * Other shapes return TCS_ERR_UNSUPPORTED.
  */

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -17,7 +18,10 @@ using tcs::Partials;
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxSliceRows = 1024;   // rows one gist workgroup holds logits for (LDS)
-constexpr int kTargetWorkgroups = 1024;
+#ifndef TCS_TARGET_WORKGROUPS
+#define TCS_TARGET_WORKGROUPS 1024
+#endif
+constexpr int kTargetWorkgroups = TCS_TARGET_WORKGROUPS;   // grid size the passes aim for
 constexpr int kMinSliceRows = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -67,7 +71,7 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (units > 65535) return TCS_ERR_UNSUPPORTED;
     if (p->d != 64 && p->d != 128) return TCS_ERR_UNSUPPORTED;
     if (!supported_group(G)) return TCS_ERR_UNSUPPORTED;
-    if (p->g > 64) return TCS_ERR_UNSUPPORTED;
+    if (p->g > 64 || p->C > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
     pl->G = G;
     pl->M = M;
     pl->H = H;
@@ -100,7 +104,8 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     pl->kslots = ksel;
     // chunk attention: enough workgroups to fill the GPU, one or more chunks each
     long long cpw = units * (ksel + 1) / kTargetWorkgroups;
-    pl->cpw = (int)(cpw < 1 ? 1 : cpw);
+    const long long cpw_max = std::min<long long>(16, kMaxSliceRows / p->C);  // rows held in LDS
+    pl->cpw = (int)std::max<long long>(1, std::min(cpw, cpw_max));
     pl->nslots = pl->S1 + pl->S2 + pl->k2e + (ksel + 1 + pl->cpw - 1) / pl->cpw;
     const long long BH = (long long)p->B * p->Hq;
     const long long s1 = p->levels == 2 ? pl->k2e : pl->S1;     // slices of the chunk pass

@@ -1,22 +1,24 @@
 // decode.hip -- gfx950 kernels of the chunk-sparse decode path.
 //
-//   gist_kernel    scores every historical chunk of a (b, kv) unit against the G query heads
-//                  of its group through the chunk's gist keys ("Simplified Sparse Attention
-//                  via Gist Tokens", section 3.2), pools them into one log-sum-exp score per
-//                  chunk, and -- because gists are themselves tokens of the softmax set --
-//                  folds the same gist rows into per-slice softmax partials with the gist
-//                  values.
-//   select_kernel  top-k chunk choice per unit (section 3.3), lowest index on ties, plus the
-//                  SAS log-softmax gate over all historical scores ("SAS", abstract).
-//   chunk_kernel   split-K attention over the selected chunks and the current chunk, read
-//                  through the page table (section 3.6: only the selected keys are touched).
-//   combine_kernel merges every partial of a query head in a fixed order.
+//   gist_kernel   scores every historical chunk of a (b, kv) unit against the G query heads of
+//                 its group through the chunk's gist keys ("Simplified Sparse Attention via
+//                 Gist Tokens", section 3.2), pools them into one log-sum-exp score per chunk,
+//                 and -- because gists are tokens of the softmax set themselves -- folds the
+//                 same gist rows into per-slice softmax partials with the gist values.  The
+//                 last workgroup of a unit to finish merges the slices' candidate lists into
+//                 the unit's top-k (section 3.3; ties to the lower index) and, with the SAS
+//                 gate on, the gate log p_c over all historical scores ("SAS", abstract).
+//   chunk_kernel  split-K attention over the selected chunks and the current chunk, read
+//                 through the page table (section 3.6: only the selected keys are touched);
+//                 the last workgroup of a unit merges all partials in a fixed order.
 //
-// Layout of the work: one 256-thread workgroup streams a run of d-element bf16 rows (gist
-// rows or one page's rows).  A row is read by d/8 lanes with one 16-byte load each, so a
-// wave reads 4 (d=128) or 8 (d=64) whole rows per instruction, fully coalesced.  The row
-// dot products are finished with DPP row reductions, softmax state is kept per lane group,
-// and groups are merged once at the end (shuffles within a wave, LDS across waves).
+// Layout of the work: one 256-thread workgroup streams runs of d-element bf16 rows (gist rows
+// or the rows of a page).  A row is read by d/8 lanes with one 16-byte load each, so a wave
+// reads 4 (d=128) or 8 (d=64) whole rows per instruction, fully coalesced.  Each run is read
+// in two phases: the K rows first (dot products with bf16 dot2 instructions, finished by DPP
+// row reductions, logits kept in LDS), then -- with the exact per-head maximum known -- the V
+// rows, weighted by exp(logit - max).  Only one phase's registers are live at a time, which
+// keeps the kernels at high occupancy for latency hiding.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -25,154 +27,184 @@
 namespace tcs {
 
 constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for empty softmax state
+constexpr int kMaxSliceRows = 1024;   // rows (gists, or page rows) one workgroup holds logits for
 
+#ifndef TCS_K_U
+#define TCS_K_U 8       // row passes per batch of loads in the K phase
+#endif
+#ifndef TCS_V_U
+#define TCS_V_U 4       // row passes per batch of loads in the V phase
+#endif
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// ---------------------------------------------------------------------------------------
+// Row streaming for one workgroup (256 threads = 4 waves).
+// ---------------------------------------------------------------------------------------
 template <int D, int G>
-struct RowAttn {
+struct RowStream {
     static constexpr int LPR = D / 8;          // lanes per row (16 B each)
     static constexpr int RPW = kWave / LPR;    // rows per wave per pass
     static constexpr int NW = 4;               // waves per workgroup
     static constexpr int RPP = RPW * NW;       // rows per workgroup per pass
-
-    float q[G][8];
-    float m[G], l[G], acc[G][8];
     int lrow, part;
 
-    __device__ void init(const uint16_t* qg /* [G][D] of this unit */) {
+    __device__ RowStream() {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
         part = lane % LPR;
         lrow = w * RPW + lane / LPR;
+    }
+
+    // The 8 query elements this lane multiplies, for each head, as bf16 pairs.
+    __device__ void load_q(const uint16_t* qg, uint32_t (&q2)[G][4]) const {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            uint4 v = ld16(qg + h * D + part * 8);
-            unpack8(v, q[h]);
-            m[h] = kNegBig;
-            l[h] = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+            const uint4 v = ld16(qg + h * D + part * 8);
+            q2[h][0] = v.x; q2[h][1] = v.y; q2[h][2] = v.z; q2[h][3] = v.w;
         }
     }
 
-    // Stream rows [0, nrows) of K/V (row stride D).  logit = sigma * q.k + bias.
-    // If lds_logits is given, the logit (without bias) of row r for head h goes to
-    // lds_logits[r * G + h].
+    // K phase: lg[(row0 + r) * G + h] = sigma * q_h . K[r] + bias for rows r < nrows.
     template <int U>
-    __device__ void run(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                        int nrows, float sigma, float bias, float* lds_logits) {
+    __device__ void logits(const uint32_t (&q2)[G][4], const uint16_t* __restrict__ K, int nrows,
+                           float sigma, float bias, float* lg, int row0) const {
         for (int base = 0; base < nrows; base += U * RPP) {
-            uint4 kr[U], vr[U];
+            uint4 kr[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int row = base + u * RPP + lrow;
+                kr[u] = row < nrows ? ld16(K + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int row = base + u * RPP + lrow;
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    float s = dot2(q2[h][0], kr[u].x, 0.f);
+                    s = dot2(q2[h][1], kr[u].y, s);
+                    s = dot2(q2[h][2], kr[u].z, s);
+                    s = dot2(q2[h][3], kr[u].w, s);
+                    s = group_sum<LPR>(s);
+                    if (part == 0 && row < nrows) lg[(row0 + row) * G + h] = fmaf(s, sigma, bias);
+                }
+            }
+        }
+    }
+
+    // V phase: acc[h][e] += w[(row0 + r) * G + h] * V[r][part*8 + e] for rows r < nrows.
+    template <int U>
+    __device__ void accumulate(float (&acc)[G][8], const uint16_t* __restrict__ V, int nrows,
+                               const float* w, int row0) const {
+        for (int base = 0; base < nrows; base += U * RPP) {
+            uint4 vr[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int row = base + u * RPP + lrow;
+                vr[u] = row < nrows ? ld16(V + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int row = base + u * RPP + lrow;
                 if (row < nrows) {
-                    kr[u] = ld16(K + (long long)row * D + part * 8);
-                    vr[u] = ld16(V + (long long)row * D + part * 8);
-                } else {
-                    kr[u] = make_uint4(0, 0, 0, 0);
-                    vr[u] = make_uint4(0, 0, 0, 0);
-                }
-            }
-            float x[U][G];
+                    float vf[8];
+                    unpack8(vr[u], vf);
+                    const float* wr = w + (row0 + row) * G;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float kf[8];
-                unpack8(kr[u], kf);
-                const int row = base + u * RPP + lrow;
+                    for (int h = 0; h < G; ++h) {
+                        const float wh = wr[h];
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    float s = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s = fmaf(q[h][e], kf[e], s);
-                    s = group_sum<LPR>(s) * sigma;
-                    if (lds_logits && part == 0 && row < nrows) lds_logits[row * G + h] = s;
-                    x[u][h] = row < nrows ? s + bias : -INFINITY;
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float mx = m[h];
-#pragma unroll
-                for (int u = 0; u < U; ++u) mx = fmaxf(mx, x[u][h]);
-                const float sc = __expf(m[h] - mx);
-                l[h] *= sc;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= sc;
-                m[h] = mx;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float vf[8];
-                unpack8(vr[u], vf);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float w = __expf(x[u][h] - m[h]);
-                    l[h] += w;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+                        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wh, vf[e], acc[h][e]);
+                    }
                 }
             }
         }
     }
 
-    // Merge the lane groups of the workgroup and write one partial per head:
-    // pacc[(bh0 + h) * nslots + slot][0..D), pml[... ][0..2).
-    // lds must hold NW * G * (D + 2) floats.
-    __device__ void finish(float* lds, const Partials& P, int bh0, int slot) {
+    // Sum the lane groups' accumulators and write one partial per head:
+    // acc -> P.acc[(bh0 + h) * nslots + slot][0..D), (M[h], L[h]) -> P.ml[...][0..2).
+    // fin must hold NW * G * D floats.
+    __device__ void finish(float (&acc)[G][8], const float* M, const float* L, float* fin,
+                           const Partials& P, int bh0, int slot) const {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-        // within the wave: lanes part + r * LPR, r = 0 .. RPW-1
 #pragma unroll
-        for (int off = LPR; off < kWave; off <<= 1) {
+        for (int off = LPR; off < kWave; off <<= 1)
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float mo = __shfl_xor(m[h], off);
-                const float lo = __shfl_xor(l[h], off);
-                const float mx = fmaxf(m[h], mo);
-                const float a = __expf(m[h] - mx), b = __expf(mo - mx);
-                l[h] = l[h] * a + lo * b;
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float ao = __shfl_xor(acc[h][e], off);
-                    acc[h][e] = acc[h][e] * a + ao * b;
-                }
-                m[h] = mx;
-            }
-        }
-        float* lacc = lds;                    // [NW][G][D]
-        float* lml = lds + NW * G * D;        // [NW][G][2]
+                for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
         if (lane < LPR) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) lacc[(w * G + h) * D + part * 8 + e] = acc[h][e];
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                lml[(w * G + h) * 2] = m[h];
-                lml[(w * G + h) * 2 + 1] = l[h];
-            }
+                for (int e = 0; e < 8; ++e) fin[(w * G + h) * D + part * 8 + e] = acc[h][e];
         }
         __syncthreads();
         for (int idx = threadIdx.x; idx < G * D; idx += 256) {
             const int h = idx / D, col = idx % D;
-            float mx = kNegBig;
+            float a = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, lml[(ww * G + h) * 2]);
-            float a = 0.f, s = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float f = __expf(lml[(ww * G + h) * 2] - mx);
-                a += f * lacc[(ww * G + h) * D + col];
-                s += f * lml[(ww * G + h) * 2 + 1];
-            }
+            for (int ww = 0; ww < NW; ++ww) a += fin[(ww * G + h) * D + col];
             const long long o = (long long)(bh0 + h) * P.nslots + slot;
             st_shared_dev(P.acc + o * D + col, a);
             if (col == 0) {
-                st_shared_dev(P.ml + o * 2, mx);
-                st_shared_dev(P.ml + o * 2 + 1, s);
+                st_shared_dev(P.ml + o * 2, M[h]);
+                st_shared_dev(P.ml + o * 2 + 1, L[h]);
             }
         }
     }
 };
+
+// Per-head softmax statistics over the logits of n rows (lg[r * G + h]): M[h] = max, then the
+// logits are replaced by exp(logit - M[h]) and L[h] = their sum.  Fixed reduction order.
+template <int G>
+struct HeadStatsSmem {
+    float part[4][G];
+    float M[G], L[G];
+};
+
+template <int G>
+__device__ void head_stats(float* lg, int n, HeadStatsSmem<G>& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    float x[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) x[h] = -INFINITY;
+    for (int r = tid; r < n; r += 256)
+#pragma unroll
+        for (int h = 0; h < G; ++h) x[h] = fmaxf(x[h], lg[r * G + h]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        x[h] = wave_max(x[h]);
+        if (lane == 0) sm.part[w][h] = x[h];
+    }
+    __syncthreads();
+    if (tid < G) {
+        float m = fmaxf(fmaxf(sm.part[0][tid], sm.part[1][tid]), fmaxf(sm.part[2][tid], sm.part[3][tid]));
+        sm.M[tid] = m > kNegBig ? m : kNegBig;   // no finite logit: keep the state finite
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) x[h] = 0.f;
+    for (int r = tid; r < n; r += 256)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float e = __expf(lg[r * G + h] - sm.M[h]);
+            lg[r * G + h] = e;
+            x[h] += e;
+        }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        x[h] = wave_sum(x[h]);
+        if (lane == 0) sm.part[w][h] = x[h];
+    }
+    __syncthreads();
+    if (tid < G) sm.L[tid] = (sm.part[0][tid] + sm.part[1][tid]) + (sm.part[2][tid] + sm.part[3][tid]);
+    __syncthreads();
+}
 
 __device__ __forceinline__ void write_empty_partial(const Partials& P, int bh0, int G, int D,
                                                     int slot, float fill_l, float fill_acc) {
@@ -187,8 +219,6 @@ __device__ __forceinline__ void write_empty_partial(const Partials& P, int bh0, 
     }
 }
 
-constexpr int kMaxSliceRows = 1024;
-
 // ---------------------------------------------------------------------------------------
 // Selection epilogue shared by the scoring passes.  Each workgroup keeps the best
 // min(k, items in its slice) of its slice's items (ascending), stores them with their
@@ -196,10 +226,15 @@ constexpr int kMaxSliceRows = 1024;
 // in ascending item order, slice after slice) into the unit's top-k.  Ties go to the lower
 // item index at both steps, so the result equals a top-k over all items at once.
 // ---------------------------------------------------------------------------------------
+struct MergeCand {
+    float score[256];
+    int32_t idx[256];
+};
+
 __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
                                 const float* s_score, int item0, int nitems, int last_items,
-                                float* lse_part_lds, void* scratch, int* s_flag, int* s_chosen,
-                                ReduceSmem& red) {
+                                float* lse_part_lds, void* scratch, MergeCand& mc, int* s_flag,
+                                int* s_chosen, ReduceSmem& red) {
     const int tid = threadIdx.x;
     const int kc = so.k < nitems ? so.k : nitems;
     float* cs = so.cand_score + ((long long)u * nslices + slot) * so.kcap;
@@ -235,16 +270,22 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
     const float* ucs = so.cand_score + (long long)u * nslices * so.kcap;
     const int32_t* uci = so.cand_idx + (long long)u * nslices * so.kcap;
     const int ncand = (nslices - 1) * so.kcap + (so.k < last_items ? so.k : last_items);
+    const bool staged = ncand <= 256;
+    // one round trip for every hand-off value this workgroup needs
+    const float* sl = so.slice_lse ? so.slice_lse + (long long)u * nslices * 2 : nullptr;
+    float* st = reinterpret_cast<float*>(scratch);     // slice statistics, if they fit
+    const bool gate = sl && so.gamma;
+    const bool lse_staged = 2 * nslices <= kTopkCache;
+    if (staged && tid < ncand) {
+        mc.score[tid] = ld_shared_dev(ucs + tid);
+        mc.idx[tid] = ld_shared_dev(uci + tid);
+    }
+    if (gate && lse_staged)
+        for (int i = tid; i < 2 * nslices; i += 256) st[i] = ld_shared_dev(sl + i);
+    __syncthreads();
     float lse = 0.f;
-    if (so.slice_lse && so.gamma) {
-        // every slice's (max, sum exp) loaded at once, then merged in slice order
-        const float* sl = so.slice_lse + (long long)u * nslices * 2;
-        float* st = reinterpret_cast<float*>(scratch);     // 2 * nslices floats if they fit
-        const bool staged = 2 * nslices <= kTopkCache;
-        if (staged)
-            for (int i = tid; i < 2 * nslices; i += 256) st[i] = ld_shared_dev(sl + i);
-        __syncthreads();
-        auto at = [&](int i) { return staged ? st[i] : ld_shared_dev(sl + i); };
+    if (gate) {
+        auto at = [&](int i) { return lse_staged ? st[i] : ld_shared_dev(sl + i); };
         if (tid == 0) {
             float mx = -INFINITY;
             for (int s = 0; s < nslices; ++s) mx = fmaxf(mx, at(2 * s));
@@ -257,21 +298,21 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
     }
     int32_t* sel = so.sel + (long long)u * so.k;
     float* gam = so.gamma ? so.gamma + (long long)u * so.k : nullptr;
+    auto score_at = [&](int i) { return staged ? mc.score[i] : ld_shared_dev(ucs + i); };
     auto emit2 = [&](int j, int i) {
-        const int32_t c = ld_shared_dev(uci + i);
+        const int32_t c = staged ? mc.idx[i] : ld_shared_dev(uci + i);
         sel[j] = c;
-        if (gam) gam[j] = ld_shared_dev(ucs + i) - lse;
+        if (gam) gam[j] = score_at(i) - lse;
         if (j < 64) s_chosen[j] = c;
     };
-    auto sc2 = [&](int i) { return ld_shared_dev(ucs + i); };
     int ke;
     if (so.k >= ncand) {
         for (int i = tid; i < ncand; i += 256) emit2(i, i);
         ke = ncand;
-    } else if (ncand <= 256) {
-        ke = small_topk(ncand, so.k, sc2, emit2, *reinterpret_cast<SmallTopkSmem*>(scratch));
+    } else if (staged) {
+        ke = small_topk(ncand, so.k, score_at, emit2, *reinterpret_cast<SmallTopkSmem*>(scratch));
     } else {
-        ke = block_topk(ncand, so.k, sc2, emit2, *reinterpret_cast<TopkSmem*>(scratch));
+        ke = block_topk(ncand, so.k, score_at, emit2, *reinterpret_cast<TopkSmem*>(scratch));
     }
     for (int j = ke + tid; j < so.k; j += 256) {
         sel[j] = -1;
@@ -293,18 +334,19 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
 // ---------------------------------------------------------------------------------------
 // gist_kernel: grid (slices, units).  Range mode: slice y covers items (chunks, or level-2
 // groups) [y*ips, min((y+1)*ips, nitems)).  Group mode (a.groups != null): slice y covers the
-// member chunks of level-2 group groups[u][y].  Streams the slice's gist rows once: logits
-// for the G heads, pooled item scores, the gist softmax partial, then the selection epilogue.
+// member chunks of level-2 group groups[u][y].
 // ---------------------------------------------------------------------------------------
 template <int D, int G>
 struct GistSmem {
     union {
-        float logits[kMaxSliceRows * G];
-        float fin[RowAttn<D, G>::NW * G * (D + 2)];
+        float lg[kMaxSliceRows * G];                   // logits, then softmax weights
+        float fin[RowStream<D, G>::NW * G * D];
         TopkSmem topk;
         SmallTopkSmem small;
     } x;
     float score[kMaxSliceRows];
+    MergeCand mc;
+    HeadStatsSmem<G> hs;
     ReduceSmem red;
     float lse;
     int flag;
@@ -313,7 +355,7 @@ struct GistSmem {
 
 template <int D, int G>
 __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
-    using RA = RowAttn<D, G>;
+    using RS = RowStream<D, G>;
     __shared__ GistSmem<D, G> sm;
     const int y = blockIdx.x, u = blockIdx.y;
     const int b = u / a.Hkv, kv = u % a.Hkv;
@@ -332,15 +374,18 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
     }
     const int nit = max(c1 - c0, 0);
     const int nrows = nit * a.g;
-    RA ra;
-    ra.init(a.q + (long long)bh0 * D);
+    const RS rs;
     const uint16_t* K = a.gk + (long long)u * a.unit_stride + (long long)c0 * a.g * D;
     const uint16_t* V = a.gv + (long long)u * a.unit_stride + (long long)c0 * a.g * D;
-    ra.template run<4>(K, V, nrows, a.sigma, 0.f, sm.x.logits);
+    {
+        uint32_t q2[G][4];
+        rs.load_q(a.q + (long long)bh0 * D, q2);
+        rs.template logits<TCS_K_U>(q2, K, nrows, a.sigma, 0.f, sm.x.lg, 0);
+    }
     __syncthreads();
     // pooled item scores: log-sum-exp over the G heads and g gists of each item
     for (int c = threadIdx.x; c < nit; c += 256) {
-        const float* x = sm.x.logits + c * a.g * G;
+        const float* x = sm.x.lg + c * a.g * G;
         float mx = -INFINITY;
         for (int i = 0; i < a.g * G; ++i) mx = fmaxf(mx, x[i]);
         float z = 0.f;
@@ -349,17 +394,25 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
         sm.score[c] = s;
         if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
     }
-    __syncthreads();
-    ra.finish(sm.x.fin, a.part, bh0, a.slot0 + y);
+    head_stats<G>(sm.x.lg, nrows, sm.hs);
+    {
+        float acc[G][8];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+        rs.template accumulate<TCS_V_U>(acc, V, nrows, sm.x.lg, 0);
+        __syncthreads();   // weights dead: fin may reuse the space
+        rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
+    }
     __syncthreads();
     select_epilogue(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.lse, &sm.x,
-                    &sm.flag, sm.chosen, sm.red);
+                    sm.mc, &sm.flag, sm.chosen, sm.red);
 }
 
 // ---------------------------------------------------------------------------------------
-// chunk_kernel: grid (kslots + 1, units).  Slot j < kslots: selected chunk sel[u][j] (an
-// empty partial for -1); slot kslots: the current chunk (tokens [(M-1)C, N)).  The last
-// workgroup of a unit merges every partial of the unit's G heads in slot order.
+// Fixed-order merge of every slot's partial for the G heads of one unit -> out, lse.  All
+// hand-off loads are issued before any is used (one memory round trip when the slots fit).
 // ---------------------------------------------------------------------------------------
 constexpr int kMergeStage = 1024;   // (head, slot) softmax statistics staged in LDS
 
@@ -370,15 +423,29 @@ struct MergeSmem {
     float M[G], L[G];
 };
 
-// Fixed-order merge of every slot's partial for the G heads of one unit -> out, lse.
-// All hand-off loads of a batch are issued before any is used, so the merge costs a few
-// memory round trips rather than one per slot.
 template <int D, int G>
 __device__ void merge_partials(const Partials& P, int bh0, float* out, float* lse,
                                MergeSmem<G>& sm) {
     const int ns = P.nslots;
     const int tid = threadIdx.x;
+    constexpr int PPT = (G * D + 255) / 256;   // (head, column) outputs per thread
+    constexpr int SB = 32 / PPT;               // slots whose values one batch holds
     const bool staged = G * ns <= kMergeStage;
+    float v[PPT][SB];
+    auto load_batch = [&](int s0) {
+#pragma unroll
+        for (int q = 0; q < PPT; ++q) {
+            const int p = tid + q * 256;
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int s = s0 + j;
+                v[q][j] = (p < G * D && s < ns)
+                              ? ld_shared_dev(P.acc + ((long long)(bh0 + p / D) * ns + s) * D + p % D)
+                              : 0.f;
+            }
+        }
+    };
+    load_batch(0);   // in flight together with the statistics below
     if (staged) {
         for (int i = tid; i < G * ns; i += 256) {
             const float* ml = P.ml + ((long long)(bh0 + i / ns) * ns + i % ns) * 2;
@@ -407,24 +474,11 @@ __device__ void merge_partials(const Partials& P, int bh0, float* out, float* ls
         for (int i = tid; i < G * ns; i += 256) sm.w[i] = __expf(sm.w[i] - sm.M[i / ns]);
         __syncthreads();
     }
-    constexpr int PPT = (G * D + 255) / 256;   // (head, column) outputs per thread
-    constexpr int SB = PPT <= 2 ? 16 : 8;      // slots per batch of loads
     float o[PPT];
 #pragma unroll
     for (int q = 0; q < PPT; ++q) o[q] = 0.f;
     for (int s0 = 0; s0 < ns; s0 += SB) {
-        float v[PPT][SB];
-#pragma unroll
-        for (int q = 0; q < PPT; ++q) {
-            const int p = tid + q * 256;
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const int s = s0 + j;
-                v[q][j] = (p < G * D && s < ns)
-                              ? ld_shared_dev(P.acc + ((long long)(bh0 + p / D) * ns + s) * D + p % D)
-                              : 0.f;
-            }
-        }
+        if (s0 > 0) load_batch(s0);
 #pragma unroll
         for (int q = 0; q < PPT; ++q) {
             const int p = tid + q * 256;
@@ -458,56 +512,96 @@ __device__ void merge_partials(const Partials& P, int bh0, float* out, float* ls
 // kslots is the current chunk (tokens [(M-1)C, N)).  Each chunk's raw tokens carry its gate
 // bias.  The last workgroup of a unit merges every partial of the unit's G heads.
 // ---------------------------------------------------------------------------------------
+constexpr int kMaxCpw = 16;
+
 template <int D, int G>
 struct ChunkSmem {
     union {
-        float fin[RowAttn<D, G>::NW * G * (D + 2)];
+        float lg[kMaxSliceRows * G];
+        float fin[RowStream<D, G>::NW * G * D];
         MergeSmem<G> merge;
     } x;
+    HeadStatsSmem<G> hs;
+    int page[kMaxCpw];
+    float bias[kMaxCpw];
+    int rows[kMaxCpw];
     int flag;
 };
 
 template <int D, int G>
 __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
-    using RA = RowAttn<D, G>;
+    using RS = RowStream<D, G>;
     __shared__ ChunkSmem<D, G> sm;
     const int wx = blockIdx.x, u = blockIdx.y;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
-    RA ra;
-    ra.init(a.q + (long long)bh0 * D);
-    bool bad_page = false;
-    const int j0 = wx * a.cpw, j1 = min(j0 + a.cpw, a.kslots + 1);
-    for (int j = j0; j < j1; ++j) {
-        int c, nrows;
+    const int j0 = wx * a.cpw, nj = min(a.cpw, a.kslots + 1 - j0);
+    // this workgroup's chunks: page, gate bias and row count (page -1: none, -2: out of range)
+    if (threadIdx.x < nj) {
+        const int j = j0 + threadIdx.x;
+        int c, rows;
         float bias = 0.f;
         if (j < a.kslots) {
             c = a.sel[(long long)u * a.k + j];
             if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
-            nrows = a.C;
+            rows = a.C;
         } else {
             c = a.M - 1;
-            nrows = a.N - (a.M - 1) * a.C;
+            rows = a.N - (a.M - 1) * a.C;
         }
-        if (c < 0) continue;
-        const int page = a.page_table[(long long)b * a.max_chunks + c];
-        if (page < 0 || page >= a.num_pages) {
-            bad_page = true;
-            continue;
+        int page = -1;
+        if (c >= 0) {
+            page = a.page_table[(long long)b * a.max_chunks + c];
+            if (page < 0 || page >= a.num_pages) page = -2;
         }
-        const long long off = ((long long)page * a.Hkv + kv) * a.C * D;
-        ra.template run<4>(a.kp + off, a.vp + off, nrows, a.sigma, bias, nullptr);
+        sm.page[threadIdx.x] = page;
+        sm.bias[threadIdx.x] = bias;
+        sm.rows[threadIdx.x] = rows;
     }
-    if (bad_page)
+    for (int i = threadIdx.x; i < nj * a.C * G; i += 256) sm.x.lg[i] = -INFINITY;
+    __syncthreads();
+    bool bad = false, any = false;
+    for (int jj = 0; jj < nj; ++jj) {
+        bad |= sm.page[jj] == -2;
+        any |= sm.page[jj] >= 0;
+    }
+    const RS rs;
+    if (bad) {
         write_empty_partial(a.part, bh0, G, D, a.slot0 + wx, NAN, NAN);
-    else
-        ra.finish(sm.x.fin, a.part, bh0, a.slot0 + wx);
+    } else if (!any) {
+        write_empty_partial(a.part, bh0, G, D, a.slot0 + wx, 0.f, 0.f);
+    } else {
+        {
+            uint32_t q2[G][4];
+            rs.load_q(a.q + (long long)bh0 * D, q2);
+            for (int jj = 0; jj < nj; ++jj) {
+                if (sm.page[jj] < 0) continue;
+                const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
+                rs.template logits<TCS_K_U>(q2, a.kp + off, sm.rows[jj], a.sigma, sm.bias[jj],
+                                            sm.x.lg, jj * a.C);
+            }
+        }
+        __syncthreads();
+        head_stats<G>(sm.x.lg, nj * a.C, sm.hs);
+        float acc[G][8];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+        for (int jj = 0; jj < nj; ++jj) {
+            if (sm.page[jj] < 0) continue;
+            const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
+            rs.template accumulate<TCS_V_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, jj * a.C);
+        }
+        __syncthreads();
+        rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + wx);
+    }
     if (!arrive_last(a.counter + u, (unsigned)gridDim.x, &sm.flag)) return;
     merge_partials<D, G>(a.part, bh0, a.out, a.lse, sm.x.merge);
 }
 
 // ---------------------------------------------------------------------------------------
-// zero_kernel: clears a workspace region (used once per workspace, before its first call).
+// small fill kernels (workspace initialisation; empty selections)
 // ---------------------------------------------------------------------------------------
 __global__ void zero_kernel(unsigned* p, long long n) {
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
@@ -555,7 +649,8 @@ static hipError_t chunk_d(const ChunkLaunch& a, hipStream_t s, dim3 grid) {
 }
 
 hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s) {
-    if (a.cpw < 1) return hipErrorInvalidValue;
+    if (a.cpw < 1 || a.cpw > kMaxCpw || (long long)a.cpw * a.C > kMaxSliceRows)
+        return hipErrorInvalidValue;
     dim3 grid((a.kslots + 1 + a.cpw - 1) / a.cpw, a.B * a.Hkv);
     return a.d == 128 ? chunk_d<128>(a, s, grid) : chunk_d<64>(a, s, grid);
 }

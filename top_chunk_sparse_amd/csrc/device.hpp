@@ -19,8 +19,19 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
     f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
 }
 
+#ifndef TCS_NT_LOADS
+#define TCS_NT_LOADS 0   // 1: stream K/V rows with non-temporal loads
+#endif
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+#if TCS_NT_LOADS
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
     return *reinterpret_cast<const uint4*>(p);
+#endif
 }
 
 // ---- DPP ----------------------------------------------------------------------------------
@@ -223,7 +234,7 @@ __device__ int block_topk(int n, int k, ScoreFn score, EmitFn emit, TopkSmem& sm
 // which keeps the output ascending.
 struct SmallTopkSmem {
     unsigned long long key[256];
-    int chosen[256];
+    ScanSmem scan;
 };
 
 template <class ScoreFn, class EmitFn>
@@ -243,13 +254,8 @@ __device__ int small_topk(int n, int k, ScoreFn score, EmitFn emit, SmallTopkSme
         for (int j = 0; j < n; ++j) rank += sm.key[j] > mine;
         take = rank < ke;
     }
-    sm.chosen[t] = take;
-    __syncthreads();
-    if (take) {
-        int pos = 0;
-        for (int j = 0; j < t; ++j) pos += sm.chosen[j];
-        emit(pos, t);
-    }
+    const int pos = block_exclusive_scan(take ? 1 : 0, sm.scan);
+    if (take) emit(pos, t);
     __syncthreads();
     return ke;
 }

@@ -10,7 +10,7 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtcsparse.so")
+LIB_PATH = os.environ.get("TCS_LIB_PATH") or os.path.join(_HERE, "libtcsparse.so")
 
 TCS_OK, TCS_ERR_NULL, TCS_ERR_SHAPE, TCS_ERR_UNSUPPORTED, TCS_ERR_WORKSPACE, TCS_ERR_HIP = range(6)
 GATE_NONE, GATE_SAS = 0, 1
