@@ -69,58 +69,98 @@ struct RowStream {
         }
     }
 
-    // K phase: lg[(row0 + r) * G + h] = sigma * q_h . K[r] + bias for rows r < nrows.
-    template <int U>
-    __device__ void logits(const uint32_t (&q2)[G][4], const uint16_t* __restrict__ K, int nrows,
-                           float sigma, float bias, float* lg, int row0) const {
-        for (int base = 0; base < nrows; base += U * RPP) {
-            uint4 kr[U];
+    // A workgroup's rows come in segments (one gist slice, or one page per chunk); segment j
+    // has seg.rows(j) rows starting at seg.k(j) / seg.v(j) and owns LDS rows
+    // [seg.row0(j), seg.row0(j) + rows).  Each phase walks batches of U row passes, segment
+    // after segment, with the next batch's loads issued before the current batch is used.
+    template <int U, class Seg>
+    __device__ void load_batch(const Seg& seg, int nb, int t, bool v, uint4 (&r)[U]) const {
+        const int j = t / nb, b = t - (t / nb) * nb;
+        const int rows = seg.rows(j);
+        const uint16_t* p = v ? seg.v(j) : seg.k(j);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = base + u * RPP + lrow;
-                kr[u] = row < nrows ? ld16(K + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+            const int row = (b * U + u) * RPP + lrow;
+            r[u] = row < rows ? ld16(p + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    template <int U, class Seg>
+    __device__ void use_k(const uint32_t (&q2)[G][4], const Seg& seg, int nb, int t, float sigma,
+                          const uint4 (&r)[U], float* lg) const {
+        const int j = t / nb, b = t - (t / nb) * nb;
+        const int rows = seg.rows(j), row0 = seg.row0(j);
+        const float bias = seg.bias(j);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int row = (b * U + u) * RPP + lrow;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float s = dot2(q2[h][0], r[u].x, 0.f);
+                s = dot2(q2[h][1], r[u].y, s);
+                s = dot2(q2[h][2], r[u].z, s);
+                s = dot2(q2[h][3], r[u].w, s);
+                s = group_sum<LPR>(s);
+                if (part == 0 && row < rows) lg[(row0 + row) * G + h] = fmaf(s, sigma, bias);
             }
+        }
+    }
+
+    template <int U, class Seg>
+    __device__ void use_v(const Seg& seg, int nb, int t, const uint4 (&r)[U], const float* w,
+                          float (&acc)[G][8]) const {
+        const int j = t / nb, b = t - (t / nb) * nb;
+        const int rows = seg.rows(j), row0 = seg.row0(j);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = base + u * RPP + lrow;
+        for (int u = 0; u < U; ++u) {
+            const int row = (b * U + u) * RPP + lrow;
+            if (row < rows) {
+                float vf[8];
+                unpack8(r[u], vf);
+                const float* wr = w + (row0 + row) * G;
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    float s = dot2(q2[h][0], kr[u].x, 0.f);
-                    s = dot2(q2[h][1], kr[u].y, s);
-                    s = dot2(q2[h][2], kr[u].z, s);
-                    s = dot2(q2[h][3], kr[u].w, s);
-                    s = group_sum<LPR>(s);
-                    if (part == 0 && row < nrows) lg[(row0 + row) * G + h] = fmaf(s, sigma, bias);
+                    const float wh = wr[h];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wh, vf[e], acc[h][e]);
                 }
             }
         }
     }
 
-    // V phase: acc[h][e] += w[(row0 + r) * G + h] * V[r][part*8 + e] for rows r < nrows.
-    template <int U>
-    __device__ void accumulate(float (&acc)[G][8], const uint16_t* __restrict__ V, int nrows,
-                               const float* w, int row0) const {
-        for (int base = 0; base < nrows; base += U * RPP) {
-            uint4 vr[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = base + u * RPP + lrow;
-                vr[u] = row < nrows ? ld16(V + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
+    // K phase over all segments: lg[(row0 + r) * G + h] = sigma * q_h . K[r] + bias.
+    template <int U, class Seg>
+    __device__ void logits(const uint32_t (&q2)[G][4], const Seg& seg, int nseg, int max_rows,
+                           float sigma, float* lg) const {
+        const int nb = (max_rows + U * RPP - 1) / (U * RPP);
+        const int total = nseg * nb;
+        if (total <= 0) return;
+        uint4 b0[U], b1[U];
+        load_batch<U>(seg, nb, 0, false, b0);
+        for (int t = 0; t < total; t += 2) {
+            if (t + 1 < total) load_batch<U>(seg, nb, t + 1, false, b1);
+            use_k<U>(q2, seg, nb, t, sigma, b0, lg);
+            if (t + 1 < total) {
+                if (t + 2 < total) load_batch<U>(seg, nb, t + 2, false, b0);
+                use_k<U>(q2, seg, nb, t + 1, sigma, b1, lg);
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = base + u * RPP + lrow;
-                if (row < nrows) {
-                    float vf[8];
-                    unpack8(vr[u], vf);
-                    const float* wr = w + (row0 + row) * G;
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const float wh = wr[h];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wh, vf[e], acc[h][e]);
-                    }
-                }
+        }
+    }
+
+    // V phase over all segments, weights w[(row0 + r) * G + h]; b0 holds batch 0, loaded by
+    // the caller with load_batch (so its latency can overlap other work).
+    template <int U, class Seg>
+    __device__ void accumulate(const Seg& seg, int nseg, int max_rows, const float* w,
+                               uint4 (&b0)[U], float (&acc)[G][8]) const {
+        const int nb = (max_rows + U * RPP - 1) / (U * RPP);
+        const int total = nseg * nb;
+        uint4 b1[U];
+        for (int t = 0; t < total; t += 2) {
+            if (t + 1 < total) load_batch<U>(seg, nb, t + 1, true, b1);
+            use_v<U>(seg, nb, t, b0, w, acc);
+            if (t + 1 < total) {
+                if (t + 2 < total) load_batch<U>(seg, nb, t + 2, true, b0);
+                use_v<U>(seg, nb, t + 1, b1, w, acc);
             }
         }
     }
@@ -220,21 +260,32 @@ __device__ __forceinline__ void write_empty_partial(const Partials& P, int bh0, 
 }
 
 // ---------------------------------------------------------------------------------------
-// Selection epilogue shared by the scoring passes.  Each workgroup keeps the best
-// min(k, items in its slice) of its slice's items (ascending), stores them with their
-// scores, and the last workgroup of the unit to finish merges the slices' lists (which are
-// in ascending item order, slice after slice) into the unit's top-k.  Ties go to the lower
-// item index at both steps, so the result equals a top-k over all items at once.
+// Selection shared by the scoring passes, in two steps.  select_publish (every workgroup,
+// right after its scores are known): keep the best min(k, items in the slice) of the slice's
+// items (ascending), hand them off with their scores, and count the workgroup in; the
+// atomic's result is only looked at later, so its latency hides under the V stream.
+// select_merge (the workgroup that arrived last, at its end): merge the slices' lists --
+// ascending item order, slice after slice -- into the unit's top-k.  Ties go to the lower item
+// index at both steps, so the result equals a top-k over all items at once.
 // ---------------------------------------------------------------------------------------
 struct MergeCand {
     float score[256];
     int32_t idx[256];
 };
 
-__device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
-                                const float* s_score, int item0, int nitems, int last_items,
-                                float* lse_part_lds, void* scratch, MergeCand& mc, int* s_flag,
-                                int* s_chosen, ReduceSmem& red) {
+struct SelectSmem {
+    TopkSmem topk;
+    SmallTopkSmem small;
+    ReduceSmem red;
+    MergeCand mc;
+    float lse;
+    int flag;
+    int chosen[64];
+};
+
+// Returns, in thread 0, the arrival counter's value before this workgroup's increment.
+__device__ unsigned select_publish(const SelectOut& so, int u, int slot, int nslices,
+                                   const float* s_score, int item0, int nitems, SelectSmem& ss) {
     const int tid = threadIdx.x;
     const int kc = so.k < nitems ? so.k : nitems;
     float* cs = so.cand_score + ((long long)u * nslices + slot) * so.kcap;
@@ -243,10 +294,10 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
     if (so.slice_lse) {
         float mx = -INFINITY;
         for (int i = tid; i < nitems; i += 256) mx = fmaxf(mx, s_score[i]);
-        mx = block_max(mx, red);
+        mx = block_max(mx, ss.red);
         float z = 0.f;
         for (int i = tid; i < nitems; i += 256) z += expf(s_score[i] - mx);
-        z = block_sum(z, red);
+        z = block_sum(z, ss.red);
         if (tid == 0) {
             st_shared_dev(so.slice_lse + ((long long)u * nslices + slot) * 2, mx);
             st_shared_dev(so.slice_lse + ((long long)u * nslices + slot) * 2 + 1, z);
@@ -260,25 +311,45 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
     if (kc == nitems) {
         for (int i = tid; i < nitems; i += 256) emit(i, i);
     } else if (nitems <= 256) {
-        small_topk(nitems, so.k, sc, emit, *reinterpret_cast<SmallTopkSmem*>(scratch));
+        small_topk(nitems, so.k, sc, emit, ss.small);
     } else {
-        block_topk(nitems, so.k, sc, emit, *reinterpret_cast<TopkSmem*>(scratch));
+        block_topk(nitems, so.k, sc, emit, ss.topk);
     }
-    if (!arrive_last(so.counter + u, (unsigned)nslices, s_flag)) return;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    wait_vmem();                      // this wave's hand-off stores have completed
+    __syncthreads();
+    unsigned old = 0;
+    if (tid == 0) old = atomicAdd(so.counter + u, 1u);
+    return old;
+}
 
-    // ---- last workgroup of the unit: merge ------------------------------------------------
+// All threads call this; only the last-arriving workgroup merges.  key_cache (cache_cap
+// entries of LDS that are free by now) serves long candidate lists.
+__device__ void select_merge(const SelectOut& so, int u, int nslices, int last_items,
+                             unsigned old, SelectSmem& ss, uint32_t* key_cache, int cache_cap) {
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        const bool last = old == (unsigned)nslices - 1u;
+        if (last) atomicExch(so.counter + u, 0u);
+        ss.flag = last;
+    }
+    __syncthreads();
+    if (!ss.flag) return;
+    wait_vmem();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
     const float* ucs = so.cand_score + (long long)u * nslices * so.kcap;
     const int32_t* uci = so.cand_idx + (long long)u * nslices * so.kcap;
     const int ncand = (nslices - 1) * so.kcap + (so.k < last_items ? so.k : last_items);
     const bool staged = ncand <= 256;
     // one round trip for every hand-off value this workgroup needs
     const float* sl = so.slice_lse ? so.slice_lse + (long long)u * nslices * 2 : nullptr;
-    float* st = reinterpret_cast<float*>(scratch);     // slice statistics, if they fit
     const bool gate = sl && so.gamma;
-    const bool lse_staged = 2 * nslices <= kTopkCache;
+    float* st = reinterpret_cast<float*>(key_cache);   // slice statistics, if they fit
+    const bool lse_staged = 2 * nslices <= cache_cap;
     if (staged && tid < ncand) {
-        mc.score[tid] = ld_shared_dev(ucs + tid);
-        mc.idx[tid] = ld_shared_dev(uci + tid);
+        ss.mc.score[tid] = ld_shared_dev(ucs + tid);
+        ss.mc.idx[tid] = ld_shared_dev(uci + tid);
     }
     if (gate && lse_staged)
         for (int i = tid; i < 2 * nslices; i += 256) st[i] = ld_shared_dev(sl + i);
@@ -291,28 +362,28 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
             for (int s = 0; s < nslices; ++s) mx = fmaxf(mx, at(2 * s));
             float z = 0.f;
             for (int s = 0; s < nslices; ++s) z += at(2 * s + 1) * expf(at(2 * s) - mx);
-            *lse_part_lds = mx + logf(z);
+            ss.lse = mx + logf(z);
         }
         __syncthreads();
-        lse = *lse_part_lds;
+        lse = ss.lse;
     }
     int32_t* sel = so.sel + (long long)u * so.k;
     float* gam = so.gamma ? so.gamma + (long long)u * so.k : nullptr;
-    auto score_at = [&](int i) { return staged ? mc.score[i] : ld_shared_dev(ucs + i); };
+    auto score_at = [&](int i) { return staged ? ss.mc.score[i] : ld_shared_dev(ucs + i); };
     auto emit2 = [&](int j, int i) {
-        const int32_t c = staged ? mc.idx[i] : ld_shared_dev(uci + i);
+        const int32_t c = staged ? ss.mc.idx[i] : ld_shared_dev(uci + i);
         sel[j] = c;
         if (gam) gam[j] = score_at(i) - lse;
-        if (j < 64) s_chosen[j] = c;
+        if (j < 64) ss.chosen[j] = c;
     };
     int ke;
     if (so.k >= ncand) {
         for (int i = tid; i < ncand; i += 256) emit2(i, i);
         ke = ncand;
     } else if (staged) {
-        ke = small_topk(ncand, so.k, score_at, emit2, *reinterpret_cast<SmallTopkSmem*>(scratch));
+        ke = small_topk(ncand, so.k, score_at, emit2, ss.small);
     } else {
-        ke = block_topk(ncand, so.k, score_at, emit2, *reinterpret_cast<TopkSmem*>(scratch));
+        ke = block_topk(ncand, so.k, score_at, emit2, ss.topk, key_cache, cache_cap);
     }
     for (int j = ke + tid; j < so.k; j += 256) {
         sel[j] = -1;
@@ -325,11 +396,23 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
         for (int c = tid; c < so.H; c += 256) {
             const int r = c / so.J;
             bool in = false;
-            for (int j = 0; j < ke && j < 64; ++j) in |= s_chosen[j] == r;
+            for (int j = 0; j < ke && j < 64; ++j) in |= ss.chosen[j] == r;
             if (!in) fs[c] = -INFINITY;
         }
     }
 }
+
+// One contiguous run of gist rows (K and V), LDS rows from 0.
+struct GistSeg {
+    const uint16_t* kp;
+    const uint16_t* vp;
+    int n;
+    __device__ const uint16_t* k(int) const { return kp; }
+    __device__ const uint16_t* v(int) const { return vp; }
+    __device__ int rows(int) const { return n; }
+    __device__ int row0(int) const { return 0; }
+    __device__ float bias(int) const { return 0.f; }
+};
 
 // ---------------------------------------------------------------------------------------
 // gist_kernel: grid (slices, units).  Range mode: slice y covers items (chunks, or level-2
@@ -341,16 +424,11 @@ struct GistSmem {
     union {
         float lg[kMaxSliceRows * G];                   // logits, then softmax weights
         float fin[RowStream<D, G>::NW * G * D];
-        TopkSmem topk;
-        SmallTopkSmem small;
+        uint32_t key_cache[kMaxSliceRows * G];         // long candidate lists in the merge
     } x;
     float score[kMaxSliceRows];
-    MergeCand mc;
     HeadStatsSmem<G> hs;
-    ReduceSmem red;
-    float lse;
-    int flag;
-    int chosen[64];
+    SelectSmem ss;
 };
 
 template <int D, int G>
@@ -375,12 +453,12 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
     const int nit = max(c1 - c0, 0);
     const int nrows = nit * a.g;
     const RS rs;
-    const uint16_t* K = a.gk + (long long)u * a.unit_stride + (long long)c0 * a.g * D;
-    const uint16_t* V = a.gv + (long long)u * a.unit_stride + (long long)c0 * a.g * D;
+    const GistSeg seg{a.gk + (long long)u * a.unit_stride + (long long)c0 * a.g * D,
+                      a.gv + (long long)u * a.unit_stride + (long long)c0 * a.g * D, nrows};
     {
         uint32_t q2[G][4];
         rs.load_q(a.q + (long long)bh0 * D, q2);
-        rs.template logits<TCS_K_U>(q2, K, nrows, a.sigma, 0.f, sm.x.lg, 0);
+        rs.template logits<TCS_K_U>(q2, seg, 1, nrows, a.sigma, sm.x.lg);
     }
     __syncthreads();
     // pooled item scores: log-sum-exp over the G heads and g gists of each item
@@ -394,6 +472,11 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
         sm.score[c] = s;
         if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
     }
+    __syncthreads();
+    const unsigned old = select_publish(a.selo, u, y, a.slices, sm.score, c0, nit, sm.ss);
+    uint4 vb[TCS_V_U];
+    rs.template load_batch<TCS_V_U>(seg, (nrows + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP), 0,
+                                    true, vb);   // first V batch in flight from here on
     head_stats<G>(sm.x.lg, nrows, sm.hs);
     {
         float acc[G][8];
@@ -401,13 +484,13 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        rs.template accumulate<TCS_V_U>(acc, V, nrows, sm.x.lg, 0);
+        rs.template accumulate<TCS_V_U>(seg, 1, nrows, sm.x.lg, vb, acc);
         __syncthreads();   // weights dead: fin may reuse the space
         rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
     }
     __syncthreads();
-    select_epilogue(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.lse, &sm.x,
-                    sm.mc, &sm.flag, sm.chosen, sm.red);
+    select_merge(a.selo, u, a.slices, last_items, old, sm.ss, sm.x.key_cache,
+                 kMaxSliceRows * G);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -429,7 +512,10 @@ __device__ void merge_partials(const Partials& P, int bh0, float* out, float* ls
     const int ns = P.nslots;
     const int tid = threadIdx.x;
     constexpr int PPT = (G * D + 255) / 256;   // (head, column) outputs per thread
-    constexpr int SB = 32 / PPT;               // slots whose values one batch holds
+#ifndef TCS_MERGE_SB
+#define TCS_MERGE_SB 32
+#endif
+    constexpr int SB = TCS_MERGE_SB / PPT;     // slots whose values one batch holds
     const bool staged = G * ns <= kMergeStage;
     float v[PPT][SB];
     auto load_batch = [&](int s0) {
@@ -514,6 +600,26 @@ __device__ void merge_partials(const Partials& P, int bh0, float* out, float* ls
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxCpw = 16;
 
+struct PageSegs {
+    const uint16_t* kp;
+    const uint16_t* vp;
+    long long slab;           // elements per (page, kv head) slab: C * d
+    int kv_off;               // kv * C * d
+    int hkv;
+    int C;
+    const int* page;          // LDS: page of each chunk (< 0: no rows)
+    const int* nrows;
+    const float* gbias;
+    __device__ long long off(int j) const {
+        return ((long long)page[j] * hkv) * slab + kv_off;
+    }
+    __device__ const uint16_t* k(int j) const { return kp + (page[j] >= 0 ? off(j) : 0); }
+    __device__ const uint16_t* v(int j) const { return vp + (page[j] >= 0 ? off(j) : 0); }
+    __device__ int rows(int j) const { return page[j] >= 0 ? nrows[j] : 0; }
+    __device__ int row0(int j) const { return j * C; }
+    __device__ float bias(int j) const { return gbias[j]; }
+};
+
 template <int D, int G>
 struct ChunkSmem {
     union {
@@ -566,6 +672,8 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
         any |= sm.page[jj] >= 0;
     }
     const RS rs;
+    const PageSegs seg{a.kp, a.vp, (long long)a.C * D, kv * a.C * D, a.Hkv, a.C,
+                       sm.page, sm.rows, sm.bias};
     if (bad) {
         write_empty_partial(a.part, bh0, G, D, a.slot0 + wx, NAN, NAN);
     } else if (!any) {
@@ -574,13 +682,11 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
         {
             uint32_t q2[G][4];
             rs.load_q(a.q + (long long)bh0 * D, q2);
-            for (int jj = 0; jj < nj; ++jj) {
-                if (sm.page[jj] < 0) continue;
-                const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
-                rs.template logits<TCS_K_U>(q2, a.kp + off, sm.rows[jj], a.sigma, sm.bias[jj],
-                                            sm.x.lg, jj * a.C);
-            }
+            rs.template logits<TCS_K_U>(q2, seg, nj, a.C, a.sigma, sm.x.lg);
         }
+        uint4 vb[TCS_V_U];
+        rs.template load_batch<TCS_V_U>(seg, (a.C + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP),
+                                        0, true, vb);   // first V batch in flight from here on
         __syncthreads();
         head_stats<G>(sm.x.lg, nj * a.C, sm.hs);
         float acc[G][8];
@@ -588,11 +694,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        for (int jj = 0; jj < nj; ++jj) {
-            if (sm.page[jj] < 0) continue;
-            const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
-            rs.template accumulate<TCS_V_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, jj * a.C);
-        }
+        rs.template accumulate<TCS_V_U>(seg, nj, a.C, sm.x.lg, vb, acc);
         __syncthreads();
         rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + wx);
     }

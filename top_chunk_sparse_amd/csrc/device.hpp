@@ -113,12 +113,10 @@ __device__ __forceinline__ float block_sum(float x, ReduceSmem& sm) {
 // Chooses the min(k, n) largest of n fp32 scores, equal scores going to the lower position,
 // and writes the chosen positions in ascending order.  Radix select on the ordered 32-bit
 // key finds the threshold key T (the k_eff-th largest); every key > T is taken, then the
-// lowest positions holding T until k_eff are reached.  256 threads.
-constexpr int kTopkCache = 4096;   // keys staged in LDS; larger n re-reads global memory
-
+// lowest positions holding T until k_eff are reached.  256 threads.  Keys are recomputed
+// from score(i) on every pass unless a cache of at least n entries is supplied.
 struct TopkSmem {
     unsigned hist[256];
-    uint32_t keys[kTopkCache];
     int digit;
     unsigned above;
     uint32_t band[4], bor[4];
@@ -128,15 +126,16 @@ struct TopkSmem {
 // score(i) -> fp32 score of position i; emit(j, i) is called once for the j-th chosen position
 // (j ascending with i).  Returns k_eff.
 template <class ScoreFn, class EmitFn>
-__device__ int block_topk(int n, int k, ScoreFn score, EmitFn emit, TopkSmem& sm) {
+__device__ int block_topk(int n, int k, ScoreFn score, EmitFn emit, TopkSmem& sm,
+                          uint32_t* key_cache = nullptr, int cache_cap = 0) {
     const int tid = threadIdx.x;
     const int ke = k < n ? k : n;
     if (ke <= 0) return 0;
-    const bool cached = n <= kTopkCache;
+    const bool cached = key_cache != nullptr && n <= cache_cap;
     if (cached)
-        for (int i = tid; i < n; i += 256) sm.keys[i] = ordered_key(score(i));
+        for (int i = tid; i < n; i += 256) key_cache[i] = ordered_key(score(i));
     __syncthreads();
-    auto key_at = [&](int i) -> uint32_t { return cached ? sm.keys[i] : ordered_key(score(i)); };
+    auto key_at = [&](int i) -> uint32_t { return cached ? key_cache[i] : ordered_key(score(i)); };
 
     // Bytes shared by every key need no histogram pass: start at the first byte that differs.
     uint32_t kand = 0xFFFFFFFFu, kor = 0u;

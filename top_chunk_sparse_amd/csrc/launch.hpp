@@ -13,7 +13,8 @@ struct Partials {
     int nslots;
 };
 
-// Selection done by the last workgroup of each unit (see select_epilogue).
+// Selection handed from every workgroup of a unit to the last one (select_publish /
+// select_merge).
 struct SelectOut {
     int k;                    // entries per unit in sel / gamma
     int32_t* sel;             // [units][k] ascending item ids, -1 padded
