@@ -112,7 +112,9 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     auto n1 = [](long long x) { return x > 0 ? x : 1; };
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-    pl->off_cnt = take(sizeof(unsigned) * (size_t)(3 * units));
+    // counters: select (pass 1), select (level 2), chunk merge, ready flags, done counts,
+    // then queue[2] and the error word -- all zero between calls
+    pl->off_cnt = take(sizeof(unsigned) * (size_t)(5 * units + 3));
     pl->off_cs1 = take(sizeof(float) * (size_t)n1(units * s1 * pl->kcap1));
     pl->off_ci1 = take(sizeof(int32_t) * (size_t)n1(units * s1 * pl->kcap1));
     pl->off_lse1 = take(sizeof(float) * (size_t)n1(units * s1 * 2));
@@ -241,6 +243,49 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     chunk_sel.J = p->J;
     chunk_sel.H = pl.H;
 
+    tcs::ChunkLaunch ca{};
+    ca.q = (const uint16_t*)q;
+    ca.kp = (const uint16_t*)k_pages;
+    ca.vp = (const uint16_t*)v_pages;
+    ca.page_table = page_table;
+    ca.B = p->B; ca.Hq = p->Hq; ca.Hkv = p->Hkv; ca.d = p->d; ca.C = p->C; ca.N = p->N;
+    ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
+    ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots; ca.cpw = pl.cpw;
+    ca.sigma = pl.sigma; ca.part = part;
+    ca.counter = cnt + 2 * units;
+    ca.out = out;
+    ca.lse = lse;
+
+    if (p->levels == 1 && pl.S1 > 0) {
+        // one persistent launch: gist slices, selection, chunk attention, merge
+        chunk_sel.gamma = gamma;
+        chunk_sel.slice_lse = gamma ? (float*)(ws + pl.off_lse1) : nullptr;
+        chunk_sel.counter = cnt;
+        ga.gk = (const uint16_t*)gist_k;
+        ga.gv = (const uint16_t*)gist_v;
+        ga.unit_stride = (long long)cap * p->g * p->d;
+        ga.nitems = pl.H;
+        ga.slices = pl.S1;
+        ga.items_per_slice = pl.cps1;
+        ga.groups = nullptr;
+        ga.scores_out = chunk_scores;
+        ga.score_stride = pl.H;
+        ga.slot0 = 0;
+        ga.selo = chunk_sel;
+        ca.slot0 = pl.S1;
+        tcs::FusedLaunch fa{};
+        fa.g = ga;
+        fa.c = ca;
+        fa.ctl.ready = cnt + 3 * units;
+        fa.ctl.done = cnt + 4 * units;
+        fa.ctl.queue = cnt + 5 * units;
+        fa.ctl.error = cnt + 5 * units + 2;
+        fa.ctl.spin_limit = 1u << 20;
+        e = tcs::launch_fused(fa, s);
+        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+        return TCS_OK;
+    }
+
     bool chunks_chosen = false;
     if (p->levels == 1) {
         chunk_sel.gamma = gamma;
@@ -319,18 +364,7 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         if (e != hipSuccess) return TCS_ERR_HIP;
     }
 
-    tcs::ChunkLaunch ca{};
-    ca.q = (const uint16_t*)q;
-    ca.kp = (const uint16_t*)k_pages;
-    ca.vp = (const uint16_t*)v_pages;
-    ca.page_table = page_table;
-    ca.B = p->B; ca.Hq = p->Hq; ca.Hkv = p->Hkv; ca.d = p->d; ca.C = p->C; ca.N = p->N;
-    ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
-    ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots; ca.cpw = pl.cpw;
-    ca.sigma = pl.sigma; ca.part = part; ca.slot0 = slot;
-    ca.counter = cnt + 2 * units;
-    ca.out = out;
-    ca.lse = lse;
+    ca.slot0 = slot;
     e = tcs::launch_chunks(ca, s);
     if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
     return TCS_OK;
@@ -363,7 +397,7 @@ tcs_status sparse_attn_decode_timed(const tcs_decode_params* p, const void* q,
 int tcs_decode_stage_count(const tcs_decode_params* p) {
     DecodePlan pl;
     if (plan_decode(p, &pl) != TCS_OK) return -1;
-    return p->levels == 2 ? 3 : 2;
+    return p->levels == 2 ? 3 : 1;
 }
 
 tcs_status tcs_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {

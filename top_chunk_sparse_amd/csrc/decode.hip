@@ -24,6 +24,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace tcs {
 
 constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for empty softmax state
@@ -208,7 +210,7 @@ struct HeadStatsSmem {
 };
 
 template <int G>
-__device__ void head_stats(float* lg, int n, HeadStatsSmem<G>& sm) {
+__device__ __forceinline__ void head_stats(float* lg, int n, HeadStatsSmem<G>& sm) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     float x[G];
 #pragma unroll
@@ -273,18 +275,21 @@ struct MergeCand {
     int32_t idx[256];
 };
 
+constexpr int kStagedSlices = 128;   // slice statistics the merge stages in LDS
+
 struct SelectSmem {
     TopkSmem topk;
     SmallTopkSmem small;
     ReduceSmem red;
     MergeCand mc;
+    float slse[2 * kStagedSlices];
     float lse;
     int flag;
     int chosen[64];
 };
 
 // Returns, in thread 0, the arrival counter's value before this workgroup's increment.
-__device__ unsigned select_publish(const SelectOut& so, int u, int slot, int nslices,
+__device__ __forceinline__ unsigned select_publish(const SelectOut& so, int u, int slot, int nslices,
                                    const float* s_score, int item0, int nitems, SelectSmem& ss) {
     const int tid = threadIdx.x;
     const int kc = so.k < nitems ? so.k : nitems;
@@ -323,21 +328,29 @@ __device__ unsigned select_publish(const SelectOut& so, int u, int slot, int nsl
     return old;
 }
 
-// All threads call this; only the last-arriving workgroup merges.  key_cache (cache_cap
-// entries of LDS that are free by now) serves long candidate lists.
-__device__ void select_merge(const SelectOut& so, int u, int nslices, int last_items,
-                             unsigned old, SelectSmem& ss, uint32_t* key_cache, int cache_cap) {
-    const int tid = threadIdx.x;
-    if (tid == 0) {
+// All threads call this with the counter value select_publish returned.  True in the
+// workgroup that arrived last (which also returns the counter to zero).
+__device__ __forceinline__ bool select_is_last(const SelectOut& so, int u, int nslices, unsigned old,
+                               SelectSmem& ss) {
+    if (threadIdx.x == 0) {
         const bool last = old == (unsigned)nslices - 1u;
         if (last) atomicExch(so.counter + u, 0u);
         ss.flag = last;
     }
     __syncthreads();
-    if (!ss.flag) return;
-    wait_vmem();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const bool last = ss.flag != 0;
+    if (last) {
+        wait_vmem();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    return last;
+}
 
+// The last workgroup merges the slices' candidates into sel (and the gate), written with
+// hand-off stores so that workgroups of the same kernel may read them.
+__device__ __forceinline__ void select_merge(const SelectOut& so, int u, int nslices, int last_items,
+                             SelectSmem& ss) {
+    const int tid = threadIdx.x;
     const float* ucs = so.cand_score + (long long)u * nslices * so.kcap;
     const int32_t* uci = so.cand_idx + (long long)u * nslices * so.kcap;
     const int ncand = (nslices - 1) * so.kcap + (so.k < last_items ? so.k : last_items);
@@ -345,18 +358,17 @@ __device__ void select_merge(const SelectOut& so, int u, int nslices, int last_i
     // one round trip for every hand-off value this workgroup needs
     const float* sl = so.slice_lse ? so.slice_lse + (long long)u * nslices * 2 : nullptr;
     const bool gate = sl && so.gamma;
-    float* st = reinterpret_cast<float*>(key_cache);   // slice statistics, if they fit
-    const bool lse_staged = 2 * nslices <= cache_cap;
+    const bool lse_staged = nslices <= kStagedSlices;
     if (staged && tid < ncand) {
         ss.mc.score[tid] = ld_shared_dev(ucs + tid);
         ss.mc.idx[tid] = ld_shared_dev(uci + tid);
     }
     if (gate && lse_staged)
-        for (int i = tid; i < 2 * nslices; i += 256) st[i] = ld_shared_dev(sl + i);
+        for (int i = tid; i < 2 * nslices; i += 256) ss.slse[i] = ld_shared_dev(sl + i);
     __syncthreads();
     float lse = 0.f;
     if (gate) {
-        auto at = [&](int i) { return lse_staged ? st[i] : ld_shared_dev(sl + i); };
+        auto at = [&](int i) { return lse_staged ? ss.slse[i] : ld_shared_dev(sl + i); };
         if (tid == 0) {
             float mx = -INFINITY;
             for (int s = 0; s < nslices; ++s) mx = fmaxf(mx, at(2 * s));
@@ -372,8 +384,8 @@ __device__ void select_merge(const SelectOut& so, int u, int nslices, int last_i
     auto score_at = [&](int i) { return staged ? ss.mc.score[i] : ld_shared_dev(ucs + i); };
     auto emit2 = [&](int j, int i) {
         const int32_t c = staged ? ss.mc.idx[i] : ld_shared_dev(uci + i);
-        sel[j] = c;
-        if (gam) gam[j] = score_at(i) - lse;
+        st_shared_dev(sel + j, c);
+        if (gam) st_shared_dev(gam + j, score_at(i) - lse);
         if (j < 64) ss.chosen[j] = c;
     };
     int ke;
@@ -383,11 +395,11 @@ __device__ void select_merge(const SelectOut& so, int u, int nslices, int last_i
     } else if (staged) {
         ke = small_topk(ncand, so.k, score_at, emit2, ss.small);
     } else {
-        ke = block_topk(ncand, so.k, score_at, emit2, ss.topk, key_cache, cache_cap);
+        ke = block_topk(ncand, so.k, score_at, emit2, ss.topk);
     }
     for (int j = ke + tid; j < so.k; j += 256) {
-        sel[j] = -1;
-        if (gam) gam[j] = 0.f;
+        st_shared_dev(sel + j, (int32_t)-1);
+        if (gam) st_shared_dev(gam + j, 0.f);
     }
     if (so.fill_scores) {
         // two-level group pass: chunks outside the chosen groups are never scored
@@ -400,6 +412,34 @@ __device__ void select_merge(const SelectOut& so, int u, int nslices, int last_i
             if (!in) fs[c] = -INFINITY;
         }
     }
+}
+
+// Bounded wait until *flag != 0 (thread 0 polls, the workgroup waits at a barrier).  Returns
+// false if the flag did not come up within `limit` polls; the caller then poisons its result
+// instead of waiting on.
+__device__ __forceinline__ bool wait_flag(const unsigned* flag, unsigned limit, int* s_ok) {
+    if (threadIdx.x == 0) {
+        unsigned n = 0;
+        int ok = 1;
+        while (ld_shared_dev(flag) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++n >= limit) { ok = 0; break; }
+        }
+        *s_ok = ok;
+    }
+    __syncthreads();
+    const bool ok = *s_ok != 0;
+    wait_vmem();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return ok;
+}
+
+// Raise *flag after this workgroup's hand-off stores have completed.
+__device__ __forceinline__ void raise_flag(unsigned* flag) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) st_shared_dev(flag, 1u);
 }
 
 // One contiguous run of gist rows (K and V), LDS rows from 0.
@@ -415,85 +455,6 @@ struct GistSeg {
 };
 
 // ---------------------------------------------------------------------------------------
-// gist_kernel: grid (slices, units).  Range mode: slice y covers items (chunks, or level-2
-// groups) [y*ips, min((y+1)*ips, nitems)).  Group mode (a.groups != null): slice y covers the
-// member chunks of level-2 group groups[u][y].
-// ---------------------------------------------------------------------------------------
-template <int D, int G>
-struct GistSmem {
-    union {
-        float lg[kMaxSliceRows * G];                   // logits, then softmax weights
-        float fin[RowStream<D, G>::NW * G * D];
-        uint32_t key_cache[kMaxSliceRows * G];         // long candidate lists in the merge
-    } x;
-    float score[kMaxSliceRows];
-    HeadStatsSmem<G> hs;
-    SelectSmem ss;
-};
-
-template <int D, int G>
-__global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
-    using RS = RowStream<D, G>;
-    __shared__ GistSmem<D, G> sm;
-    const int y = blockIdx.x, u = blockIdx.y;
-    const int b = u / a.Hkv, kv = u % a.Hkv;
-    const int bh0 = b * a.Hq + kv * G;
-    int c0, c1, last_items;
-    if (a.groups) {
-        const int r = a.groups[(long long)u * a.k2 + y];
-        c0 = r * a.J;
-        c1 = min(c0 + a.J, a.H);
-        const int rl = a.groups[(long long)u * a.k2 + a.slices - 1];
-        last_items = min(a.J, a.H - rl * a.J);
-    } else {
-        c0 = y * a.items_per_slice;
-        c1 = min(c0 + a.items_per_slice, a.nitems);
-        last_items = a.nitems - (a.slices - 1) * a.items_per_slice;
-    }
-    const int nit = max(c1 - c0, 0);
-    const int nrows = nit * a.g;
-    const RS rs;
-    const GistSeg seg{a.gk + (long long)u * a.unit_stride + (long long)c0 * a.g * D,
-                      a.gv + (long long)u * a.unit_stride + (long long)c0 * a.g * D, nrows};
-    {
-        uint32_t q2[G][4];
-        rs.load_q(a.q + (long long)bh0 * D, q2);
-        rs.template logits<TCS_K_U>(q2, seg, 1, nrows, a.sigma, sm.x.lg);
-    }
-    __syncthreads();
-    // pooled item scores: log-sum-exp over the G heads and g gists of each item
-    for (int c = threadIdx.x; c < nit; c += 256) {
-        const float* x = sm.x.lg + c * a.g * G;
-        float mx = -INFINITY;
-        for (int i = 0; i < a.g * G; ++i) mx = fmaxf(mx, x[i]);
-        float z = 0.f;
-        for (int i = 0; i < a.g * G; ++i) z += expf(x[i] - mx);
-        const float s = mx + logf(z);
-        sm.score[c] = s;
-        if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
-    }
-    __syncthreads();
-    const unsigned old = select_publish(a.selo, u, y, a.slices, sm.score, c0, nit, sm.ss);
-    uint4 vb[TCS_V_U];
-    rs.template load_batch<TCS_V_U>(seg, (nrows + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP), 0,
-                                    true, vb);   // first V batch in flight from here on
-    head_stats<G>(sm.x.lg, nrows, sm.hs);
-    {
-        float acc[G][8];
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        rs.template accumulate<TCS_V_U>(seg, 1, nrows, sm.x.lg, vb, acc);
-        __syncthreads();   // weights dead: fin may reuse the space
-        rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
-    }
-    __syncthreads();
-    select_merge(a.selo, u, a.slices, last_items, old, sm.ss, sm.x.key_cache,
-                 kMaxSliceRows * G);
-}
-
-// ---------------------------------------------------------------------------------------
 // Fixed-order merge of every slot's partial for the G heads of one unit -> out, lse.  All
 // hand-off loads are issued before any is used (one memory round trip when the slots fit).
 // ---------------------------------------------------------------------------------------
@@ -507,7 +468,7 @@ struct MergeSmem {
 };
 
 template <int D, int G>
-__device__ void merge_partials(const Partials& P, int bh0, float* out, float* lse,
+__device__ __forceinline__ void merge_partials(const Partials& P, int bh0, float* out, float* lse,
                                MergeSmem<G>& sm) {
     const int ns = P.nslots;
     const int tid = threadIdx.x;
@@ -592,6 +553,110 @@ __device__ void merge_partials(const Partials& P, int bh0, float* out, float* ls
     }
 }
 
+// Final merge: which counter, how many arrivals, and where the result goes.
+struct FinalMerge {
+    unsigned* counter;    // [units]
+    unsigned total;       // arrivals per unit
+    float* out;
+    float* lse;
+    unsigned* ready;      // persistent kernel: the selection flags to lower again, else null
+};
+
+// ---------------------------------------------------------------------------------------
+// gist item: one slice of a unit.  Range mode: slice y covers items (chunks, or level-2
+// groups) [y*ips, min((y+1)*ips, nitems)).  Group mode (a.groups != null): slice y covers the
+// member chunks of level-2 group groups[u][y].  With `fm` the slice also counts towards the
+// unit's final merge (persistent kernel), and `ready` is raised once the selection is made.
+// ---------------------------------------------------------------------------------------
+template <int D, int G>
+struct GistSmem {
+    union {
+        float lg[kMaxSliceRows * G];                   // logits, then softmax weights
+        float fin[RowStream<D, G>::NW * G * D];
+        MergeSmem<G> merge;
+    } x;
+    float score[kMaxSliceRows];
+    HeadStatsSmem<G> hs;
+    SelectSmem ss;
+    int flag;
+};
+
+template <int D, int G>
+__device__ __forceinline__ void gist_item(const GistLaunch& a, int u, int y, GistSmem<D, G>& sm,
+                          const FinalMerge fm) {
+    using RS = RowStream<D, G>;
+    const int b = u / a.Hkv, kv = u % a.Hkv;
+    const int bh0 = b * a.Hq + kv * G;
+    int c0, c1, last_items;
+    if (a.groups) {
+        const int r = ld_shared_dev(a.groups + (long long)u * a.k2 + y);
+        c0 = r * a.J;
+        c1 = min(c0 + a.J, a.H);
+        const int rl = ld_shared_dev(a.groups + (long long)u * a.k2 + a.slices - 1);
+        last_items = min(a.J, a.H - rl * a.J);
+    } else {
+        c0 = y * a.items_per_slice;
+        c1 = min(c0 + a.items_per_slice, a.nitems);
+        last_items = a.nitems - (a.slices - 1) * a.items_per_slice;
+    }
+    const int nit = max(c1 - c0, 0);
+    const int nrows = nit * a.g;
+    const RS rs;
+    const GistSeg seg{a.gk + (long long)u * a.unit_stride + (long long)c0 * a.g * D,
+                      a.gv + (long long)u * a.unit_stride + (long long)c0 * a.g * D, nrows};
+    {
+        uint32_t q2[G][4];
+        rs.load_q(a.q + (long long)bh0 * D, q2);
+        rs.template logits<TCS_K_U>(q2, seg, 1, nrows, a.sigma, sm.x.lg);
+    }
+    __syncthreads();
+    // pooled item scores: log-sum-exp over the G heads and g gists of each item
+    for (int c = threadIdx.x; c < nit; c += 256) {
+        const float* x = sm.x.lg + c * a.g * G;
+        float mx = -INFINITY;
+        for (int i = 0; i < a.g * G; ++i) mx = fmaxf(mx, x[i]);
+        float z = 0.f;
+        for (int i = 0; i < a.g * G; ++i) z += expf(x[i] - mx);
+        const float s = mx + logf(z);
+        sm.score[c] = s;
+        if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
+    }
+    __syncthreads();
+    const unsigned old = select_publish(a.selo, u, y, a.slices, sm.score, c0, nit, sm.ss);
+    uint4 vb[TCS_V_U];
+    rs.template load_batch<TCS_V_U>(seg, (nrows + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP), 0,
+                                    true, vb);   // first V batch in flight from here on
+    if (select_is_last(a.selo, u, a.slices, old, sm.ss)) {
+        select_merge(a.selo, u, a.slices, last_items, sm.ss);
+        if (fm.ready) raise_flag(fm.ready + u);
+    }
+    head_stats<G>(sm.x.lg, nrows, sm.hs);
+    {
+        float acc[G][8];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+        rs.template accumulate<TCS_V_U>(seg, 1, nrows, sm.x.lg, vb, acc);
+        __syncthreads();   // weights dead: fin may reuse the space
+        rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
+    }
+    if (fm.counter) {
+        __syncthreads();
+        if (arrive_last(fm.counter + u, fm.total, &sm.flag)) {
+            merge_partials<D, G>(a.part, bh0, fm.out, fm.lse, sm.x.merge);
+            if (fm.ready) st_shared_dev(fm.ready + u, 0u);
+        }
+    }
+}
+
+// gist_kernel: grid (slices, units), one gist item per workgroup (two-level routing).
+template <int D, int G>
+__global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
+    __shared__ GistSmem<D, G> sm;
+    gist_item<D, G>(a, blockIdx.y, blockIdx.x, sm, FinalMerge{nullptr, 0u, nullptr, nullptr, nullptr});
+}
+
 // ---------------------------------------------------------------------------------------
 // chunk_kernel: grid (ceil((kslots + 1) / cpw), units).  Workgroup x streams slots
 // [x*cpw, (x+1)*cpw): slot j < kslots is selected chunk sel[u][j] (skipped if -1), slot
@@ -634,22 +699,29 @@ struct ChunkSmem {
     int flag;
 };
 
+// chunk item: workgroup wx of unit u streams chunk slots [wx*cpw, (wx+1)*cpw).  In the
+// persistent kernel (`wait` non-null) it first waits for the unit's selection.
 template <int D, int G>
-__global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
+__device__ __forceinline__ void chunk_item(const ChunkLaunch& a, int u, int wx, ChunkSmem<D, G>& sm,
+                           const FinalMerge fm, const unsigned* wait, unsigned spin_limit,
+                           unsigned* error) {
     using RS = RowStream<D, G>;
-    __shared__ ChunkSmem<D, G> sm;
-    const int wx = blockIdx.x, u = blockIdx.y;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
     const int j0 = wx * a.cpw, nj = min(a.cpw, a.kslots + 1 - j0);
-    // this workgroup's chunks: page, gate bias and row count (page -1: none, -2: out of range)
+    bool stalled = false;
+    if (wait && !wait_flag(wait + u, spin_limit, &sm.flag)) {
+        stalled = true;
+        if (threadIdx.x == 0) atomicOr(error, 1u);
+    }
+    // this workgroup's chunks: page, gate bias and row count (page -1: none, -2: unusable)
     if (threadIdx.x < nj) {
         const int j = j0 + threadIdx.x;
         int c, rows;
         float bias = 0.f;
         if (j < a.kslots) {
-            c = a.sel[(long long)u * a.k + j];
-            if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
+            c = ld_shared_dev(a.sel + (long long)u * a.k + j);
+            if (c >= 0 && a.gamma) bias = ld_shared_dev(a.gamma + (long long)u * a.k + j);
             rows = a.C;
         } else {
             c = a.M - 1;
@@ -660,7 +732,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
             page = a.page_table[(long long)b * a.max_chunks + c];
             if (page < 0 || page >= a.num_pages) page = -2;
         }
-        sm.page[threadIdx.x] = page;
+        sm.page[threadIdx.x] = stalled ? -2 : page;
         sm.bias[threadIdx.x] = bias;
         sm.rows[threadIdx.x] = rows;
     }
@@ -698,8 +770,61 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
         __syncthreads();
         rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + wx);
     }
-    if (!arrive_last(a.counter + u, (unsigned)gridDim.x, &sm.flag)) return;
-    merge_partials<D, G>(a.part, bh0, a.out, a.lse, sm.x.merge);
+    __syncthreads();
+    if (!arrive_last(fm.counter + u, fm.total, &sm.flag)) return;
+    merge_partials<D, G>(a.part, bh0, fm.out, fm.lse, sm.x.merge);
+    if (fm.ready) st_shared_dev(fm.ready + u, 0u);
+}
+
+// chunk_kernel: grid (chunk workgroups per unit, units).
+template <int D, int G>
+__global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
+    __shared__ ChunkSmem<D, G> sm;
+    const FinalMerge fm{a.counter, gridDim.x, a.out, a.lse, nullptr};
+    chunk_item<D, G>(a, blockIdx.y, blockIdx.x, sm, fm, nullptr, 0u, nullptr);
+}
+
+// ---------------------------------------------------------------------------------------
+// fused_kernel: the whole one-level decode in one launch of one workgroup per work item.
+// Each workgroup takes a ticket from a queue when it starts running and does that item:
+// tickets below n_gist are the gist slices of every unit, the rest the chunk workgroups of
+// every unit (unit-major both).  A chunk item waits (bounded) until its unit's selection is
+// published.  That flag is raised by a gist item; gist items never wait, and every gist
+// ticket is taken -- by a workgroup that is already running -- before any chunk ticket, so
+// each wait has a running producer whatever order the hardware starts workgroups in.  The
+// unit's final merge runs in whichever of its items finishes last.
+// ---------------------------------------------------------------------------------------
+template <int D, int G>
+union FusedSmem {
+    GistSmem<D, G> g;
+    ChunkSmem<D, G> c;
+};
+
+template <int D, int G>
+__global__ void __launch_bounds__(256) fused_kernel(GistLaunch g, ChunkLaunch c, FusedCtl ctl) {
+    __shared__ FusedSmem<D, G> sm;
+    __shared__ int s_item;
+    if (threadIdx.x == 0) s_item = (int)atomicAdd(ctl.queue, 1u);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar branch
+    const int units = g.B * g.Hkv;
+    const int ncw = (c.kslots + 1 + c.cpw - 1) / c.cpw;
+    const int n_gist = units * g.slices;
+    const FinalMerge fm{ctl.done, (unsigned)(g.slices + ncw), c.out, c.lse, ctl.ready};
+    if (item < n_gist) {
+        gist_item<D, G>(g, item / g.slices, item % g.slices, sm.g, fm);
+    } else if (item < n_gist + units * ncw) {
+        const int ci = item - n_gist;
+        chunk_item<D, G>(c, ci / ncw, ci % ncw, sm.c, fm, ctl.ready, ctl.spin_limit, ctl.error);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = atomicAdd(ctl.queue + 1, 1u);
+        if (old == gridDim.x - 1u) {     // every workgroup has taken its ticket and finished
+            atomicExch(ctl.queue, 0u);
+            atomicExch(ctl.queue + 1, 0u);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -755,6 +880,48 @@ hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s) {
         return hipErrorInvalidValue;
     dim3 grid((a.kslots + 1 + a.cpw - 1) / a.cpw, a.B * a.Hkv);
     return a.d == 128 ? chunk_d<128>(a, s, grid) : chunk_d<64>(a, s, grid);
+}
+
+template <int D>
+static hipError_t fused_d(const FusedLaunch& a, hipStream_t s, int grid) {
+    switch (a.g.Hq / a.g.Hkv) {
+        case 1: fused_kernel<D, 1><<<grid, 256, 0, s>>>(a.g, a.c, a.ctl); break;
+        case 2: fused_kernel<D, 2><<<grid, 256, 0, s>>>(a.g, a.c, a.ctl); break;
+        case 4: fused_kernel<D, 4><<<grid, 256, 0, s>>>(a.g, a.c, a.ctl); break;
+        case 8: fused_kernel<D, 8><<<grid, 256, 0, s>>>(a.g, a.c, a.ctl); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int D, int G>
+static int resident_workgroups() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<D, G>, 256, 0) !=
+            hipSuccess)
+        return 1024;
+    return cus * (per_cu > 0 ? per_cu : 1);
+}
+
+hipError_t launch_fused(const FusedLaunch& a, hipStream_t s) {
+    const ChunkLaunch& c = a.c;
+    if (c.cpw < 1 || c.cpw > kMaxCpw || (long long)c.cpw * c.C > kMaxSliceRows || a.g.slices < 1)
+        return hipErrorInvalidValue;
+    const int G = a.g.Hq / a.g.Hkv;
+    int cap = 0;
+    if (a.g.d == 128)
+        cap = G == 1 ? resident_workgroups<128, 1>() : G == 2 ? resident_workgroups<128, 2>()
+            : G == 4 ? resident_workgroups<128, 4>() : resident_workgroups<128, 8>();
+    else
+        cap = G == 1 ? resident_workgroups<64, 1>() : G == 2 ? resident_workgroups<64, 2>()
+            : G == 4 ? resident_workgroups<64, 4>() : resident_workgroups<64, 8>();
+    const long long units = (long long)a.g.B * a.g.Hkv;
+    const long long items = units * a.g.slices + units * ((c.kslots + 1 + c.cpw - 1) / c.cpw);
+    if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+    (void)cap;
+    return a.g.d == 128 ? fused_d<128>(a, s, (int)items) : fused_d<64>(a, s, (int)items);
 }
 
 hipError_t launch_fill(int32_t* p, long long n, int32_t v, hipStream_t s) {

@@ -67,7 +67,23 @@ struct ChunkLaunch {
     float* lse;               // [B*Hq] or null
 };
 
+// The persistent one-level decode: gist slices, then chunk workgroups, from one queue.
+struct FusedCtl {
+    unsigned* queue;          // [2]: next work item, workgroups finished; zero between calls
+    unsigned* ready;          // [units]: selection published; zero between calls
+    unsigned* done;           // [units]: items finished, for the final merge; zero between calls
+    unsigned* error;          // [1]: set if a wait ran out (the unit's output is NaN)
+    unsigned spin_limit;      // polls before a wait gives up
+};
+
+struct FusedLaunch {
+    GistLaunch g;             // range mode over the historical chunks
+    ChunkLaunch c;
+    FusedCtl ctl;
+};
+
 hipError_t launch_gist(const GistLaunch& a, hipStream_t s);
+hipError_t launch_fused(const FusedLaunch& a, hipStream_t s);
 hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t v, hipStream_t s);
