@@ -894,33 +894,13 @@ static hipError_t fused_d(const FusedLaunch& a, hipStream_t s, int grid) {
     return hipGetLastError();
 }
 
-template <int D, int G>
-static int resident_workgroups() {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<D, G>, 256, 0) !=
-            hipSuccess)
-        return 1024;
-    return cus * (per_cu > 0 ? per_cu : 1);
-}
-
 hipError_t launch_fused(const FusedLaunch& a, hipStream_t s) {
     const ChunkLaunch& c = a.c;
     if (c.cpw < 1 || c.cpw > kMaxCpw || (long long)c.cpw * c.C > kMaxSliceRows || a.g.slices < 1)
         return hipErrorInvalidValue;
-    const int G = a.g.Hq / a.g.Hkv;
-    int cap = 0;
-    if (a.g.d == 128)
-        cap = G == 1 ? resident_workgroups<128, 1>() : G == 2 ? resident_workgroups<128, 2>()
-            : G == 4 ? resident_workgroups<128, 4>() : resident_workgroups<128, 8>();
-    else
-        cap = G == 1 ? resident_workgroups<64, 1>() : G == 2 ? resident_workgroups<64, 2>()
-            : G == 4 ? resident_workgroups<64, 4>() : resident_workgroups<64, 8>();
     const long long units = (long long)a.g.B * a.g.Hkv;
     const long long items = units * a.g.slices + units * ((c.kslots + 1 + c.cpw - 1) / c.cpw);
     if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-    (void)cap;
     return a.g.d == 128 ? fused_d<128>(a, s, (int)items) : fused_d<64>(a, s, (int)items);
 }
 
