@@ -113,8 +113,8 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
     // counters: select (pass 1), select (level 2), chunk merge, ready flags, done counts,
-    // then queue[2] and the error word -- all zero between calls
-    pl->off_cnt = take(sizeof(unsigned) * (size_t)(5 * units + 3));
+    // then the ticket queues and the error word -- all zero between calls
+    pl->off_cnt = take(sizeof(unsigned) * (size_t)(5 * units + 2 * tcs::kMaxQueues + 1));
     pl->off_cs1 = take(sizeof(float) * (size_t)n1(units * s1 * pl->kcap1));
     pl->off_ci1 = take(sizeof(int32_t) * (size_t)n1(units * s1 * pl->kcap1));
     pl->off_lse1 = take(sizeof(float) * (size_t)n1(units * s1 * 2));
@@ -279,7 +279,8 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         fa.ctl.ready = cnt + 3 * units;
         fa.ctl.done = cnt + 4 * units;
         fa.ctl.queue = cnt + 5 * units;
-        fa.ctl.error = cnt + 5 * units + 2;
+        fa.ctl.nq = units < tcs::kMaxQueues ? units : tcs::kMaxQueues;
+        fa.ctl.error = cnt + 5 * units + 2 * tcs::kMaxQueues;
         fa.ctl.spin_limit = 1u << 20;
         e = tcs::launch_fused(fa, s);
         if (e != hipSuccess || !mark()) return TCS_ERR_HIP;

@@ -786,13 +786,16 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
 
 // ---------------------------------------------------------------------------------------
 // fused_kernel: the whole one-level decode in one launch of one workgroup per work item.
-// Each workgroup takes a ticket from a queue when it starts running and does that item:
-// tickets below n_gist are the gist slices of every unit, the rest the chunk workgroups of
-// every unit (unit-major both).  A chunk item waits (bounded) until its unit's selection is
-// published.  That flag is raised by a gist item; gist items never wait, and every gist
-// ticket is taken -- by a workgroup that is already running -- before any chunk ticket, so
-// each wait has a running producer whatever order the hardware starts workgroups in.  The
-// unit's final merge runs in whichever of its items finishes last.
+// Units are dealt round-robin to nq queues; queue q owns a contiguous range of workgroup ids
+// exactly as long as its list of items: first every gist slice of its units, then every
+// chunk workgroup of its units (unit-major both).  Each workgroup takes the next ticket of
+// its queue when it starts running and does that item.  A chunk item waits (bounded) until
+// its unit's selection is published by a gist item of the same queue; gist items never wait,
+// and within a queue every gist ticket is taken -- by a workgroup that is already running --
+// before any chunk ticket, so each wait has a running producer whatever order the hardware
+// starts workgroups in.  Spreading the tickets over nq counters keeps the ticket atomics from
+// serialising on one address.  The unit's final merge runs in whichever of its items
+// finishes last; the last item of a queue returns the queue's counters to zero.
 // ---------------------------------------------------------------------------------------
 template <int D, int G>
 union FusedSmem {
@@ -804,25 +807,33 @@ template <int D, int G>
 __global__ void __launch_bounds__(256) fused_kernel(GistLaunch g, ChunkLaunch c, FusedCtl ctl) {
     __shared__ FusedSmem<D, G> sm;
     __shared__ int s_item;
-    if (threadIdx.x == 0) s_item = (int)atomicAdd(ctl.queue, 1u);
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar branch
     const int units = g.B * g.Hkv;
     const int ncw = (c.kslots + 1 + c.cpw - 1) / c.cpw;
-    const int n_gist = units * g.slices;
-    const FinalMerge fm{ctl.done, (unsigned)(g.slices + ncw), c.out, c.lse, ctl.ready};
-    if (item < n_gist) {
-        gist_item<D, G>(g, item / g.slices, item % g.slices, sm.g, fm);
-    } else if (item < n_gist + units * ncw) {
-        const int ci = item - n_gist;
-        chunk_item<D, G>(c, ci / ncw, ci % ncw, sm.c, fm, ctl.ready, ctl.spin_limit, ctl.error);
+    const int per = g.slices + ncw;                 // items per unit
+    const int nq = ctl.nq;
+    const int ua = units / nq, ur = units % nq;     // queues q < ur hold ua + 1 units
+    const int w = blockIdx.x;
+    const int big = ur * (ua + 1) * per;
+    const int q = w < big ? w / ((ua + 1) * per) : ur + (w - big) / (ua * per);
+    const int uq = ua + (q < ur ? 1 : 0);           // units of queue q
+    const int nitems = uq * per;
+    if (threadIdx.x == 0) s_item = (int)atomicAdd(ctl.queue + q, 1u);
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar branch
+    const FinalMerge fm{ctl.done, (unsigned)per, c.out, c.lse, ctl.ready};
+    if (t < uq * g.slices) {
+        gist_item<D, G>(g, q + (t / g.slices) * nq, t % g.slices, sm.g, fm);
+    } else if (t < nitems) {
+        const int ci = t - uq * g.slices;
+        chunk_item<D, G>(c, q + (ci / ncw) * nq, ci % ncw, sm.c, fm, ctl.ready, ctl.spin_limit,
+                         ctl.error);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned old = atomicAdd(ctl.queue + 1, 1u);
-        if (old == gridDim.x - 1u) {     // every workgroup has taken its ticket and finished
-            atomicExch(ctl.queue, 0u);
-            atomicExch(ctl.queue + 1, 0u);
+        const unsigned old = atomicAdd(ctl.queue + nq + q, 1u);
+        if (old == (unsigned)nitems - 1u) {   // every ticket of this queue is taken and done
+            atomicExch(ctl.queue + q, 0u);
+            atomicExch(ctl.queue + nq + q, 0u);
         }
     }
 }
@@ -900,7 +911,7 @@ hipError_t launch_fused(const FusedLaunch& a, hipStream_t s) {
         return hipErrorInvalidValue;
     const long long units = (long long)a.g.B * a.g.Hkv;
     const long long items = units * a.g.slices + units * ((c.kslots + 1 + c.cpw - 1) / c.cpw);
-    if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (items > 0x7fffffffLL || a.ctl.nq < 1 || a.ctl.nq > units) return hipErrorInvalidValue;
     return a.g.d == 128 ? fused_d<128>(a, s, (int)items) : fused_d<64>(a, s, (int)items);
 }
 

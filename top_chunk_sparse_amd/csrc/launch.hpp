@@ -68,8 +68,11 @@ struct ChunkLaunch {
 };
 
 // The persistent one-level decode: gist slices, then chunk workgroups, from one queue.
+constexpr int kMaxQueues = 16;
+
 struct FusedCtl {
-    unsigned* queue;          // [2]: next work item, workgroups finished; zero between calls
+    unsigned* queue;          // [2 * nq]: next ticket, items finished, per queue; zero between calls
+    int nq;                   // ticket queues (units are dealt round-robin to them)
     unsigned* ready;          // [units]: selection published; zero between calls
     unsigned* done;           // [units]: items finished, for the final merge; zero between calls
     unsigned* error;          // [1]: set if a wait ran out (the unit's output is NaN)
