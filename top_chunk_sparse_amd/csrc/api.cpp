@@ -279,7 +279,9 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         fa.ctl.ready = cnt + 3 * units;
         fa.ctl.done = cnt + 4 * units;
         fa.ctl.queue = cnt + 5 * units;
-        fa.ctl.nq = units < tcs::kMaxQueues ? units : tcs::kMaxQueues;
+        fa.ctl.nq = 1;   // the largest divisor of the unit count up to kMaxQueues
+        for (int d = tcs::kMaxQueues; d >= 1; --d)
+            if (units % d == 0) { fa.ctl.nq = d; break; }
         fa.ctl.error = cnt + 5 * units + 2 * tcs::kMaxQueues;
         fa.ctl.spin_limit = 1u << 20;
         e = tcs::launch_fused(fa, s);

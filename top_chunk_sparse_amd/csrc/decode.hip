@@ -786,10 +786,11 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
 
 // ---------------------------------------------------------------------------------------
 // fused_kernel: the whole one-level decode in one launch of one workgroup per work item.
-// Units are dealt round-robin to nq queues; queue q owns a contiguous range of workgroup ids
-// exactly as long as its list of items: first every gist slice of its units, then every
-// chunk workgroup of its units (unit-major both).  Each workgroup takes the next ticket of
-// its queue when it starts running and does that item.  A chunk item waits (bounded) until
+// Units are dealt round-robin to nq queues, nq dividing the unit count, so every queue has
+// the same list length: first every gist slice of its units, then every chunk workgroup of
+// its units (unit-major both).  Workgroup w belongs to queue w % nq -- interleaved, so that
+// workgroups starting early take the gist tickets of every queue -- and takes the next
+// ticket of its queue when it starts running and does that item.  A chunk item waits (bounded) until
 // its unit's selection is published by a gist item of the same queue; gist items never wait,
 // and within a queue every gist ticket is taken -- by a workgroup that is already running --
 // before any chunk ticket, so each wait has a running producer whatever order the hardware
@@ -810,12 +811,9 @@ __global__ void __launch_bounds__(256) fused_kernel(GistLaunch g, ChunkLaunch c,
     const int units = g.B * g.Hkv;
     const int ncw = (c.kslots + 1 + c.cpw - 1) / c.cpw;
     const int per = g.slices + ncw;                 // items per unit
-    const int nq = ctl.nq;
-    const int ua = units / nq, ur = units % nq;     // queues q < ur hold ua + 1 units
-    const int w = blockIdx.x;
-    const int big = ur * (ua + 1) * per;
-    const int q = w < big ? w / ((ua + 1) * per) : ur + (w - big) / (ua * per);
-    const int uq = ua + (q < ur ? 1 : 0);           // units of queue q
+    const int nq = ctl.nq;                          // divides units
+    const int q = blockIdx.x % nq;
+    const int uq = units / nq;                      // units of each queue
     const int nitems = uq * per;
     if (threadIdx.x == 0) s_item = (int)atomicAdd(ctl.queue + q, 1u);
     __syncthreads();
@@ -911,7 +909,7 @@ hipError_t launch_fused(const FusedLaunch& a, hipStream_t s) {
         return hipErrorInvalidValue;
     const long long units = (long long)a.g.B * a.g.Hkv;
     const long long items = units * a.g.slices + units * ((c.kslots + 1 + c.cpw - 1) / c.cpw);
-    if (items > 0x7fffffffLL || a.ctl.nq < 1 || a.ctl.nq > units) return hipErrorInvalidValue;
+    if (items > 0x7fffffffLL || a.ctl.nq < 1 || units % a.ctl.nq) return hipErrorInvalidValue;
     return a.g.d == 128 ? fused_d<128>(a, s, (int)items) : fused_d<64>(a, s, (int)items);
 }
 

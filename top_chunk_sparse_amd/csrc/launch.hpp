@@ -72,7 +72,7 @@ constexpr int kMaxQueues = 16;
 
 struct FusedCtl {
     unsigned* queue;          // [2 * nq]: next ticket, items finished, per queue; zero between calls
-    int nq;                   // ticket queues (units are dealt round-robin to them)
+    int nq;                   // ticket queues; divides the unit count (units dealt round-robin)
     unsigned* ready;          // [units]: selection published; zero between calls
     unsigned* done;           // [units]: items finished, for the final merge; zero between calls
     unsigned* error;          // [1]: set if a wait ran out (the unit's output is NaN)
