@@ -49,7 +49,7 @@ struct DecodePlan {
     float sigma;
     // workspace offsets (bytes)
     size_t off_cnt, off_cs1, off_ci1, off_lse1, off_cs2, off_ci2, off_sel, off_gamma, off_gsel,
-        off_acc, off_ml, total;
+        off_acc, off_ml, off_wstash, off_sstash, total;
 };
 
 tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
@@ -114,7 +114,8 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
     // counters: select (pass 1), select (level 2), chunk merge, ready flags, done counts,
     // then the ticket queues and the error word -- all zero between calls
-    pl->off_cnt = take(sizeof(unsigned) * (size_t)(5 * units + 2 * tcs::kMaxQueues + 1));
+    pl->off_cnt = take(sizeof(unsigned) *
+                       (size_t)(5 * units + 2 * tcs::kMaxQueues + 1 + units * pl->S1));
     pl->off_cs1 = take(sizeof(float) * (size_t)n1(units * s1 * pl->kcap1));
     pl->off_ci1 = take(sizeof(int32_t) * (size_t)n1(units * s1 * pl->kcap1));
     pl->off_lse1 = take(sizeof(float) * (size_t)n1(units * s1 * 2));
@@ -125,6 +126,9 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     pl->off_gsel = take(sizeof(int32_t) * (size_t)n1(units * p->k2));
     pl->off_acc = take(sizeof(float) * (size_t)(BH * pl->nslots * p->d));
     pl->off_ml = take(sizeof(float) * (size_t)(BH * pl->nslots * 2));
+    // one-level persistent launch: softmax weights and statistics of every gist slice
+    pl->off_wstash = take(sizeof(float) * (size_t)n1(units * pl->S1 * pl->cps1 * p->g * G));
+    pl->off_sstash = take(sizeof(float) * (size_t)n1(units * pl->S1 * G * 2));
     pl->total = off;
     return TCS_OK;
 }
@@ -283,6 +287,10 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         for (int d = tcs::kMaxQueues; d >= 1; --d)
             if (units % d == 0) { fa.ctl.nq = d; break; }
         fa.ctl.error = cnt + 5 * units + 2 * tcs::kMaxQueues;
+        fa.ctl.kdone = cnt + 5 * units + 2 * tcs::kMaxQueues + 1;
+        fa.ctl.wstash = (float*)(ws + pl.off_wstash);
+        fa.ctl.sstash = (float*)(ws + pl.off_sstash);
+        fa.ctl.stash_rows = pl.cps1 * p->g;
         fa.ctl.spin_limit = 1u << 20;
         e = tcs::launch_fused(fa, s);
         if (e != hipSuccess || !mark()) return TCS_ERR_HIP;

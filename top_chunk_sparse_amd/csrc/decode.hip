@@ -581,72 +581,156 @@ struct GistSmem {
     int flag;
 };
 
-template <int D, int G>
-__device__ __forceinline__ void gist_item(const GistLaunch& a, int u, int y, GistSmem<D, G>& sm,
-                          const FinalMerge fm) {
-    using RS = RowStream<D, G>;
-    const int b = u / a.Hkv, kv = u % a.Hkv;
-    const int bh0 = b * a.Hq + kv * G;
-    int c0, c1, last_items;
+// The chunks (or level-2 groups) of slice y of unit u.
+struct SliceRange {
+    int c0, nit, nrows, last_items;
+};
+
+__device__ __forceinline__ SliceRange slice_range(const GistLaunch& a, int u, int y) {
+    SliceRange r;
+    int c1;
     if (a.groups) {
-        const int r = ld_shared_dev(a.groups + (long long)u * a.k2 + y);
-        c0 = r * a.J;
-        c1 = min(c0 + a.J, a.H);
-        const int rl = ld_shared_dev(a.groups + (long long)u * a.k2 + a.slices - 1);
-        last_items = min(a.J, a.H - rl * a.J);
+        const int g = ld_shared_dev(a.groups + (long long)u * a.k2 + y);
+        r.c0 = g * a.J;
+        c1 = min(r.c0 + a.J, a.H);
+        const int gl = ld_shared_dev(a.groups + (long long)u * a.k2 + a.slices - 1);
+        r.last_items = min(a.J, a.H - gl * a.J);
     } else {
-        c0 = y * a.items_per_slice;
-        c1 = min(c0 + a.items_per_slice, a.nitems);
-        last_items = a.nitems - (a.slices - 1) * a.items_per_slice;
+        r.c0 = y * a.items_per_slice;
+        c1 = min(r.c0 + a.items_per_slice, a.nitems);
+        r.last_items = a.nitems - (a.slices - 1) * a.items_per_slice;
     }
-    const int nit = max(c1 - c0, 0);
-    const int nrows = nit * a.g;
+    r.nit = max(c1 - r.c0, 0);
+    r.nrows = r.nit * a.g;
+    return r;
+}
+
+template <int D>
+__device__ __forceinline__ GistSeg gist_seg(const GistLaunch& a, int u, const SliceRange& r) {
+    return GistSeg{a.gk + (long long)u * a.unit_stride + (long long)r.c0 * a.g * D,
+                   a.gv + (long long)u * a.unit_stride + (long long)r.c0 * a.g * D, r.nrows};
+}
+
+// Scoring part of a gist item: logits of the slice's gist keys (LDS), pooled item scores,
+// and the selection hand-off.  Returns (thread 0) the selection counter's old value.
+template <int D, int G>
+__device__ __forceinline__ unsigned gist_front(const GistLaunch& a, int u, int y,
+                                               const SliceRange& r, GistSmem<D, G>& sm) {
+    using RS = RowStream<D, G>;
+    const int bh0 = (u / a.Hkv) * a.Hq + (u % a.Hkv) * G;
     const RS rs;
-    const GistSeg seg{a.gk + (long long)u * a.unit_stride + (long long)c0 * a.g * D,
-                      a.gv + (long long)u * a.unit_stride + (long long)c0 * a.g * D, nrows};
+    const GistSeg seg = gist_seg<D>(a, u, r);
     {
         uint32_t q2[G][4];
         rs.load_q(a.q + (long long)bh0 * D, q2);
-        rs.template logits<TCS_K_U>(q2, seg, 1, nrows, a.sigma, sm.x.lg);
+        rs.template logits<TCS_K_U>(q2, seg, 1, r.nrows, a.sigma, sm.x.lg);
     }
     __syncthreads();
     // pooled item scores: log-sum-exp over the G heads and g gists of each item
-    for (int c = threadIdx.x; c < nit; c += 256) {
+    for (int c = threadIdx.x; c < r.nit; c += 256) {
         const float* x = sm.x.lg + c * a.g * G;
         float mx = -INFINITY;
         for (int i = 0; i < a.g * G; ++i) mx = fmaxf(mx, x[i]);
         float z = 0.f;
         for (int i = 0; i < a.g * G; ++i) z += expf(x[i] - mx);
-        const float s = mx + logf(z);
-        sm.score[c] = s;
-        if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
+        const float sc = mx + logf(z);
+        sm.score[c] = sc;
+        if (a.scores_out) a.scores_out[(long long)u * a.score_stride + r.c0 + c] = sc;
     }
     __syncthreads();
-    const unsigned old = select_publish(a.selo, u, y, a.slices, sm.score, c0, nit, sm.ss);
+    return select_publish(a.selo, u, y, a.slices, sm.score, r.c0, r.nit, sm.ss);
+}
+
+// Whole gist item (scoring, selection, then the V rows of the slice) for the separate-kernel
+// path.
+template <int D, int G>
+__device__ __forceinline__ void gist_item(const GistLaunch& a, int u, int y, GistSmem<D, G>& sm) {
+    using RS = RowStream<D, G>;
+    const int bh0 = (u / a.Hkv) * a.Hq + (u % a.Hkv) * G;
+    const SliceRange r = slice_range(a, u, y);
+    const unsigned old = gist_front<D, G>(a, u, y, r, sm);
+    const RS rs;
+    const GistSeg seg = gist_seg<D>(a, u, r);
     uint4 vb[TCS_V_U];
-    rs.template load_batch<TCS_V_U>(seg, (nrows + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP), 0,
-                                    true, vb);   // first V batch in flight from here on
-    if (select_is_last(a.selo, u, a.slices, old, sm.ss)) {
-        select_merge(a.selo, u, a.slices, last_items, sm.ss);
-        if (fm.ready) raise_flag(fm.ready + u);
+    rs.template load_batch<TCS_V_U>(seg, (r.nrows + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP),
+                                    0, true, vb);   // first V batch in flight from here on
+    if (select_is_last(a.selo, u, a.slices, old, sm.ss)) select_merge(a.selo, u, a.slices, r.last_items, sm.ss);
+    head_stats<G>(sm.x.lg, r.nrows, sm.hs);
+    float acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    rs.template accumulate<TCS_V_U>(seg, 1, r.nrows, sm.x.lg, vb, acc);
+    __syncthreads();   // weights dead: fin may reuse the space
+    rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
+}
+
+// Persistent-kernel K item: scoring and selection, then the slice's softmax weights and
+// statistics go to the stash for its V item, and the slice's flag is raised.
+template <int D, int G>
+__device__ __forceinline__ void gist_k_item(const GistLaunch& a, const FusedCtl& ctl, int u,
+                                            int y, GistSmem<D, G>& sm) {
+    const SliceRange r = slice_range(a, u, y);
+    const unsigned old = gist_front<D, G>(a, u, y, r, sm);
+    head_stats<G>(sm.x.lg, r.nrows, sm.hs);
+    const long long sl = (long long)u * a.slices + y;
+    float* w = ctl.wstash + sl * ctl.stash_rows * G;
+    for (int i = threadIdx.x; i < r.nrows * G; i += 256) st_shared_dev(w + i, sm.x.lg[i]);
+    if (threadIdx.x < G) {
+        st_shared_dev(ctl.sstash + (sl * G + threadIdx.x) * 2, sm.hs.M[threadIdx.x]);
+        st_shared_dev(ctl.sstash + (sl * G + threadIdx.x) * 2 + 1, sm.hs.L[threadIdx.x]);
     }
-    head_stats<G>(sm.x.lg, nrows, sm.hs);
-    {
+    raise_flag(ctl.kdone + sl);
+    if (select_is_last(a.selo, u, a.slices, old, sm.ss)) {
+        select_merge(a.selo, u, a.slices, r.last_items, sm.ss);
+        raise_flag(ctl.ready + u);
+    }
+}
+
+// Persistent-kernel V item: the V rows of a slice, weighted by the stashed softmax weights,
+// into the slice's partial; counts towards the unit's final merge.
+template <int D, int G>
+__device__ __forceinline__ void gist_v_item(const GistLaunch& a, const FusedCtl& ctl,
+                                            const FinalMerge& fm, int u, int y,
+                                            GistSmem<D, G>& sm) {
+    using RS = RowStream<D, G>;
+    const int bh0 = (u / a.Hkv) * a.Hq + (u % a.Hkv) * G;
+    const SliceRange r = slice_range(a, u, y);
+    const RS rs;
+    const GistSeg seg = gist_seg<D>(a, u, r);
+    uint4 vb[TCS_V_U];
+    rs.template load_batch<TCS_V_U>(seg, (r.nrows + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP),
+                                    0, true, vb);   // independent of the wait below
+    const long long sl = (long long)u * a.slices + y;
+    const bool ok = wait_flag(ctl.kdone + sl, ctl.spin_limit, &sm.flag);
+    const float* w = ctl.wstash + sl * ctl.stash_rows * G;
+    for (int i = threadIdx.x; i < r.nrows * G; i += 256) sm.x.lg[i] = ld_shared_dev(w + i);
+    if (threadIdx.x < G) {
+        sm.hs.M[threadIdx.x] = ld_shared_dev(ctl.sstash + (sl * G + threadIdx.x) * 2);
+        sm.hs.L[threadIdx.x] = ld_shared_dev(ctl.sstash + (sl * G + threadIdx.x) * 2 + 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        st_shared_dev(ctl.kdone + sl, 0u);    // this item is the flag's only reader
+        if (!ok) atomicOr(ctl.error, 1u);
+    }
+    if (!ok) {
+        write_empty_partial(a.part, bh0, G, D, a.slot0 + y, NAN, NAN);
+    } else {
         float acc[G][8];
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        rs.template accumulate<TCS_V_U>(seg, 1, nrows, sm.x.lg, vb, acc);
+        rs.template accumulate<TCS_V_U>(seg, 1, r.nrows, sm.x.lg, vb, acc);
         __syncthreads();   // weights dead: fin may reuse the space
         rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
     }
-    if (fm.counter) {
-        __syncthreads();
-        if (arrive_last(fm.counter + u, fm.total, &sm.flag)) {
-            merge_partials<D, G>(a.part, bh0, fm.out, fm.lse, sm.x.merge);
-            if (fm.ready) st_shared_dev(fm.ready + u, 0u);
-        }
+    __syncthreads();
+    if (arrive_last(fm.counter + u, fm.total, &sm.flag)) {
+        merge_partials<D, G>(a.part, bh0, fm.out, fm.lse, sm.x.merge);
+        st_shared_dev(fm.ready + u, 0u);
     }
 }
 
@@ -654,7 +738,7 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, int u, int y, Gis
 template <int D, int G>
 __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
     __shared__ GistSmem<D, G> sm;
-    gist_item<D, G>(a, blockIdx.y, blockIdx.x, sm, FinalMerge{nullptr, 0u, nullptr, nullptr, nullptr});
+    gist_item<D, G>(a, blockIdx.y, blockIdx.x, sm);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -787,13 +871,15 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
 // ---------------------------------------------------------------------------------------
 // fused_kernel: the whole one-level decode in one launch of one workgroup per work item.
 // Units are dealt round-robin to nq queues, nq dividing the unit count, so every queue has
-// the same list length: first every gist slice of its units, then every chunk workgroup of
-// its units (unit-major both).  Workgroup w belongs to queue w % nq -- interleaved, so that
+// the same list length: first the K item of every gist slice of its units (scoring and
+// selection), then the V item of every slice (which waits for its own K item), then every
+// chunk workgroup of its units (unit-major each) -- so the scoring of all units, on which
+// the selections depend, is read first.  Workgroup w belongs to queue w % nq -- interleaved, so that
 // workgroups starting early take the gist tickets of every queue -- and takes the next
-// ticket of its queue when it starts running and does that item.  A chunk item waits (bounded) until
-// its unit's selection is published by a gist item of the same queue; gist items never wait,
-// and within a queue every gist ticket is taken -- by a workgroup that is already running --
-// before any chunk ticket, so each wait has a running producer whatever order the hardware
+// ticket of its queue when it starts running and does that item.  A V item waits (bounded) for
+// its K item, a chunk item for its unit's selection, which the K items publish; K items never
+// wait, and within a queue every K ticket is taken -- by a workgroup that is already running --
+// before any other ticket, so each wait has a running producer whatever order the hardware
 // starts workgroups in.  Spreading the tickets over nq counters keeps the ticket atomics from
 // serialising on one address.  The unit's final merge runs in whichever of its items
 // finishes last; the last item of a queue returns the queue's counters to zero.
@@ -810,19 +896,22 @@ __global__ void __launch_bounds__(256) fused_kernel(GistLaunch g, ChunkLaunch c,
     __shared__ int s_item;
     const int units = g.B * g.Hkv;
     const int ncw = (c.kslots + 1 + c.cpw - 1) / c.cpw;
-    const int per = g.slices + ncw;                 // items per unit
     const int nq = ctl.nq;                          // divides units
     const int q = blockIdx.x % nq;
     const int uq = units / nq;                      // units of each queue
-    const int nitems = uq * per;
+    const int nk = uq * g.slices;                   // K items, then as many V items, then chunks
+    const int nitems = 2 * nk + uq * ncw;
     if (threadIdx.x == 0) s_item = (int)atomicAdd(ctl.queue + q, 1u);
     __syncthreads();
     const int t = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar branch
-    const FinalMerge fm{ctl.done, (unsigned)per, c.out, c.lse, ctl.ready};
-    if (t < uq * g.slices) {
-        gist_item<D, G>(g, q + (t / g.slices) * nq, t % g.slices, sm.g, fm);
+    const FinalMerge fm{ctl.done, (unsigned)(g.slices + ncw), c.out, c.lse, ctl.ready};
+    if (t < nk) {
+        gist_k_item<D, G>(g, ctl, q + (t / g.slices) * nq, t % g.slices, sm.g);
+    } else if (t < 2 * nk) {
+        const int v = t - nk;
+        gist_v_item<D, G>(g, ctl, fm, q + (v / g.slices) * nq, v % g.slices, sm.g);
     } else if (t < nitems) {
-        const int ci = t - uq * g.slices;
+        const int ci = t - 2 * nk;
         chunk_item<D, G>(c, q + (ci / ncw) * nq, ci % ncw, sm.c, fm, ctl.ready, ctl.spin_limit,
                          ctl.error);
     }
@@ -908,7 +997,7 @@ hipError_t launch_fused(const FusedLaunch& a, hipStream_t s) {
     if (c.cpw < 1 || c.cpw > kMaxCpw || (long long)c.cpw * c.C > kMaxSliceRows || a.g.slices < 1)
         return hipErrorInvalidValue;
     const long long units = (long long)a.g.B * a.g.Hkv;
-    const long long items = units * a.g.slices + units * ((c.kslots + 1 + c.cpw - 1) / c.cpw);
+    const long long items = 2 * units * a.g.slices + units * ((c.kslots + 1 + c.cpw - 1) / c.cpw);
     if (items > 0x7fffffffLL || a.ctl.nq < 1 || units % a.ctl.nq) return hipErrorInvalidValue;
     return a.g.d == 128 ? fused_d<128>(a, s, (int)items) : fused_d<64>(a, s, (int)items);
 }

@@ -77,6 +77,10 @@ struct FusedCtl {
     unsigned* done;           // [units]: items finished, for the final merge; zero between calls
     unsigned* error;          // [1]: set if a wait ran out (the unit's output is NaN)
     unsigned spin_limit;      // polls before a wait gives up
+    unsigned* kdone;          // [units * slices]: K item done; zero between calls
+    float* wstash;            // [units * slices][stash_rows * G] softmax weights of a slice
+    float* sstash;            // [units * slices][G][2] (max, sum) of a slice
+    int stash_rows;           // rows per slice in wstash
 };
 
 struct FusedLaunch {
