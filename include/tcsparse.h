@@ -57,10 +57,12 @@
  *   from tcs_*_workspace_size, 256-byte aligned).  The library allocates, frees and
  *   synchronises nothing and keeps no global state; every call only enqueues kernels on
  *   `stream` and returns.  Calls sharing a workspace must be ordered on one stream.
- *   A decode workspace holds per-unit arrival counters that must read zero when a call
- *   starts: zero-fill a new workspace once (tcs_workspace_init, or any zero fill) before its
- *   first call; every completed call leaves the counters at zero again.  After a call that
- *   returned TCS_ERR_HIP, initialise the workspace again.
+ *   A decode workspace starts with a block of arrival counters and flags, laid out the same
+ *   way for every shape, that must read zero when a call starts: zero-fill a new workspace
+ *   once (tcs_workspace_init, or any zero fill) before its first call; every completed call
+ *   leaves them at zero again, so one workspace (as large as the largest shape needs) serves
+ *   calls of any shape in turn.  After a call that returned TCS_ERR_HIP, initialise the
+ *   workspace again.
  *   Argument errors return before any device work and leave every output untouched.  A
  *   failed launch returns TCS_ERR_HIP.  Inputs must be finite (NaN/Inf inputs give
  *   unspecified results).  A page id outside [0, num_pages) is never read: the heads of the
@@ -69,7 +71,8 @@
  *   for); k = 0 keeps only the gists and the current chunk.  Results are deterministic:
  *   no floating-point atomics; the same inputs give bitwise-identical outputs.
  *
- * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024; two levels:
+ * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024;
+ * B * Hkv <= 16384; two levels:
  * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk.
  * Other shapes return TCS_ERR_UNSUPPORTED.
  */

@@ -70,6 +70,7 @@ def test_workspace_size_grows_with_work():
     (dict(gate=2), ops.TCS_ERR_SHAPE),
     (dict(scale=-1.0), ops.TCS_ERR_SHAPE),
     (dict(num_pages=0), ops.TCS_ERR_SHAPE),
+    (dict(B=4097, Hkv=4, Hq=16), ops.TCS_ERR_UNSUPPORTED),   # 16388 units
 ])
 def test_decode_rejects_bad_params(kw, code):
     p = P(**kw)

@@ -17,6 +17,21 @@ namespace {
 using tcs::Partials;
 
 constexpr size_t kAlign = 256;
+
+// Every decode workspace starts with a counter block of fixed layout -- the same for every
+// shape -- so that one zeroed workspace serves calls of any shape in turn: each call leaves
+// every counter it used at zero.  Units are (batch row, KV head) pairs.
+constexpr int kMaxUnits = 16384;
+constexpr int kSliceFlags = 32;            // per-unit flags for one-level persistent launches
+constexpr size_t kCntSelect1 = 0;          // [kMaxUnits] selection arrivals (chunk pass)
+constexpr size_t kCntSelect2 = kCntSelect1 + kMaxUnits;   // level-2 group pass
+constexpr size_t kCntChunk = kCntSelect2 + kMaxUnits;     // chunk-kernel final merge
+constexpr size_t kCntReady = kCntChunk + kMaxUnits;       // selection published
+constexpr size_t kCntDone = kCntReady + kMaxUnits;        // persistent final merge
+constexpr size_t kCntQueue = kCntDone + kMaxUnits;        // 2 * kMaxQueues tickets
+constexpr size_t kCntError = kCntQueue + 2 * tcs::kMaxQueues;
+constexpr size_t kCntKdone = kCntError + 1;               // [kMaxUnits][kSliceFlags]
+constexpr size_t kCounterWords = kCntKdone + (size_t)kMaxUnits * kSliceFlags;
 constexpr int kMaxSliceRows = 1024;   // rows one gist workgroup holds logits for (LDS)
 #ifndef TCS_TARGET_WORKGROUPS
 #define TCS_TARGET_WORKGROUPS 1024
@@ -68,7 +83,7 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     const int H = M - 1;
     if (p->max_chunks < M) return TCS_ERR_SHAPE;
     if (p->gist_cap != 0 && p->gist_cap < H) return TCS_ERR_SHAPE;
-    if (units > 65535) return TCS_ERR_UNSUPPORTED;
+    if (units > kMaxUnits) return TCS_ERR_UNSUPPORTED;
     if (p->d != 64 && p->d != 128) return TCS_ERR_UNSUPPORTED;
     if (!supported_group(G)) return TCS_ERR_UNSUPPORTED;
     if (p->g > 64 || p->C > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
@@ -114,8 +129,7 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
     // counters: select (pass 1), select (level 2), chunk merge, ready flags, done counts,
     // then the ticket queues and the error word -- all zero between calls
-    pl->off_cnt = take(sizeof(unsigned) *
-                       (size_t)(5 * units + 2 * tcs::kMaxQueues + 1 + units * pl->S1));
+    pl->off_cnt = take(sizeof(unsigned) * kCounterWords);
     pl->off_cs1 = take(sizeof(float) * (size_t)n1(units * s1 * pl->kcap1));
     pl->off_ci1 = take(sizeof(int32_t) * (size_t)n1(units * s1 * pl->kcap1));
     pl->off_lse1 = take(sizeof(float) * (size_t)n1(units * s1 * 2));
@@ -256,11 +270,11 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
     ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots; ca.cpw = pl.cpw;
     ca.sigma = pl.sigma; ca.part = part;
-    ca.counter = cnt + 2 * units;
+    ca.counter = cnt + kCntChunk;
     ca.out = out;
     ca.lse = lse;
 
-    if (p->levels == 1 && pl.S1 > 0) {
+    if (p->levels == 1 && pl.S1 > 0 && pl.S1 <= kSliceFlags) {
         // one persistent launch: gist slices, selection, chunk attention, merge
         chunk_sel.gamma = gamma;
         chunk_sel.slice_lse = gamma ? (float*)(ws + pl.off_lse1) : nullptr;
@@ -280,14 +294,14 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         tcs::FusedLaunch fa{};
         fa.g = ga;
         fa.c = ca;
-        fa.ctl.ready = cnt + 3 * units;
-        fa.ctl.done = cnt + 4 * units;
-        fa.ctl.queue = cnt + 5 * units;
+        fa.ctl.ready = cnt + kCntReady;
+        fa.ctl.done = cnt + kCntDone;
+        fa.ctl.queue = cnt + kCntQueue;
         fa.ctl.nq = 1;   // the largest divisor of the unit count up to kMaxQueues
         for (int d = tcs::kMaxQueues; d >= 1; --d)
             if (units % d == 0) { fa.ctl.nq = d; break; }
-        fa.ctl.error = cnt + 5 * units + 2 * tcs::kMaxQueues;
-        fa.ctl.kdone = cnt + 5 * units + 2 * tcs::kMaxQueues + 1;
+        fa.ctl.error = cnt + kCntError;
+        fa.ctl.kdone = cnt + kCntKdone;
         fa.ctl.wstash = (float*)(ws + pl.off_wstash);
         fa.ctl.sstash = (float*)(ws + pl.off_sstash);
         fa.ctl.stash_rows = pl.cps1 * p->g;
@@ -326,7 +340,7 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         gs.cand_score = (float*)(ws + pl.off_cs2);
         gs.cand_idx = (int32_t*)(ws + pl.off_ci2);
         gs.kcap = pl.kcap2;
-        gs.counter = cnt + units;
+        gs.counter = cnt + kCntSelect2;
         gs.fill_scores = chunk_scores;
         gs.J = p->J;
         gs.H = pl.H;
