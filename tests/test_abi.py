@@ -158,6 +158,6 @@ def test_workspace_init_checks_alignment():
 
 
 def test_stage_counts():
-    assert ops.decode_stage_count(P()) == 1
+    assert ops.decode_stage_count(P()) == 2
     assert ops.decode_stage_count(P(levels=2, J=4, k2=2)) == 3
     assert ops.decode_stage_count(P(d=96)) == -1

@@ -18,20 +18,14 @@ using tcs::Partials;
 
 constexpr size_t kAlign = 256;
 
-// Every decode workspace starts with a counter block of fixed layout -- the same for every
-// shape -- so that one zeroed workspace serves calls of any shape in turn: each call leaves
-// every counter it used at zero.  Units are (batch row, KV head) pairs.
+// Every decode workspace starts with a block of arrival counters laid out the same way for
+// every shape, so that one zeroed workspace serves calls of any shape in turn: each call
+// leaves every counter it used at zero.  Units are (batch row, KV head) pairs.
 constexpr int kMaxUnits = 16384;
-constexpr int kSliceFlags = 32;            // per-unit flags for one-level persistent launches
-constexpr size_t kCntSelect1 = 0;          // [kMaxUnits] selection arrivals (chunk pass)
+constexpr size_t kCntSelect1 = 0;                         // selection arrivals (chunk pass)
 constexpr size_t kCntSelect2 = kCntSelect1 + kMaxUnits;   // level-2 group pass
-constexpr size_t kCntChunk = kCntSelect2 + kMaxUnits;     // chunk-kernel final merge
-constexpr size_t kCntReady = kCntChunk + kMaxUnits;       // selection published
-constexpr size_t kCntDone = kCntReady + kMaxUnits;        // persistent final merge
-constexpr size_t kCntQueue = kCntDone + kMaxUnits;        // 2 * kMaxQueues tickets
-constexpr size_t kCntError = kCntQueue + 2 * tcs::kMaxQueues;
-constexpr size_t kCntKdone = kCntError + 1;               // [kMaxUnits][kSliceFlags]
-constexpr size_t kCounterWords = kCntKdone + (size_t)kMaxUnits * kSliceFlags;
+constexpr size_t kCntChunk = kCntSelect2 + kMaxUnits;     // chunk attention final merge
+constexpr size_t kCounterWords = kCntChunk + kMaxUnits;
 constexpr int kMaxSliceRows = 1024;   // rows one gist workgroup holds logits for (LDS)
 #ifndef TCS_TARGET_WORKGROUPS
 #define TCS_TARGET_WORKGROUPS 1024
@@ -64,7 +58,7 @@ struct DecodePlan {
     float sigma;
     // workspace offsets (bytes)
     size_t off_cnt, off_cs1, off_ci1, off_lse1, off_cs2, off_ci2, off_sel, off_gamma, off_gsel,
-        off_acc, off_ml, off_wstash, off_sstash, total;
+        off_acc, off_ml, total;
 };
 
 tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
@@ -127,8 +121,6 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     auto n1 = [](long long x) { return x > 0 ? x : 1; };
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-    // counters: select (pass 1), select (level 2), chunk merge, ready flags, done counts,
-    // then the ticket queues and the error word -- all zero between calls
     pl->off_cnt = take(sizeof(unsigned) * kCounterWords);
     pl->off_cs1 = take(sizeof(float) * (size_t)n1(units * s1 * pl->kcap1));
     pl->off_ci1 = take(sizeof(int32_t) * (size_t)n1(units * s1 * pl->kcap1));
@@ -140,9 +132,6 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     pl->off_gsel = take(sizeof(int32_t) * (size_t)n1(units * p->k2));
     pl->off_acc = take(sizeof(float) * (size_t)(BH * pl->nslots * p->d));
     pl->off_ml = take(sizeof(float) * (size_t)(BH * pl->nslots * 2));
-    // one-level persistent launch: softmax weights and statistics of every gist slice
-    pl->off_wstash = take(sizeof(float) * (size_t)n1(units * pl->S1 * pl->cps1 * p->g * G));
-    pl->off_sstash = take(sizeof(float) * (size_t)n1(units * pl->S1 * G * 2));
     pl->total = off;
     return TCS_OK;
 }
@@ -261,56 +250,6 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     chunk_sel.J = p->J;
     chunk_sel.H = pl.H;
 
-    tcs::ChunkLaunch ca{};
-    ca.q = (const uint16_t*)q;
-    ca.kp = (const uint16_t*)k_pages;
-    ca.vp = (const uint16_t*)v_pages;
-    ca.page_table = page_table;
-    ca.B = p->B; ca.Hq = p->Hq; ca.Hkv = p->Hkv; ca.d = p->d; ca.C = p->C; ca.N = p->N;
-    ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
-    ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots; ca.cpw = pl.cpw;
-    ca.sigma = pl.sigma; ca.part = part;
-    ca.counter = cnt + kCntChunk;
-    ca.out = out;
-    ca.lse = lse;
-
-    if (p->levels == 1 && pl.S1 > 0 && pl.S1 <= kSliceFlags) {
-        // one persistent launch: gist slices, selection, chunk attention, merge
-        chunk_sel.gamma = gamma;
-        chunk_sel.slice_lse = gamma ? (float*)(ws + pl.off_lse1) : nullptr;
-        chunk_sel.counter = cnt;
-        ga.gk = (const uint16_t*)gist_k;
-        ga.gv = (const uint16_t*)gist_v;
-        ga.unit_stride = (long long)cap * p->g * p->d;
-        ga.nitems = pl.H;
-        ga.slices = pl.S1;
-        ga.items_per_slice = pl.cps1;
-        ga.groups = nullptr;
-        ga.scores_out = chunk_scores;
-        ga.score_stride = pl.H;
-        ga.slot0 = 0;
-        ga.selo = chunk_sel;
-        ca.slot0 = pl.S1;
-        tcs::FusedLaunch fa{};
-        fa.g = ga;
-        fa.c = ca;
-        fa.ctl.ready = cnt + kCntReady;
-        fa.ctl.done = cnt + kCntDone;
-        fa.ctl.queue = cnt + kCntQueue;
-        fa.ctl.nq = 1;   // the largest divisor of the unit count up to kMaxQueues
-        for (int d = tcs::kMaxQueues; d >= 1; --d)
-            if (units % d == 0) { fa.ctl.nq = d; break; }
-        fa.ctl.error = cnt + kCntError;
-        fa.ctl.kdone = cnt + kCntKdone;
-        fa.ctl.wstash = (float*)(ws + pl.off_wstash);
-        fa.ctl.sstash = (float*)(ws + pl.off_sstash);
-        fa.ctl.stash_rows = pl.cps1 * p->g;
-        fa.ctl.spin_limit = 1u << 20;
-        e = tcs::launch_fused(fa, s);
-        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
-        return TCS_OK;
-    }
-
     bool chunks_chosen = false;
     if (p->levels == 1) {
         chunk_sel.gamma = gamma;
@@ -389,7 +328,18 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         if (e != hipSuccess) return TCS_ERR_HIP;
     }
 
-    ca.slot0 = slot;
+    tcs::ChunkLaunch ca{};
+    ca.q = (const uint16_t*)q;
+    ca.kp = (const uint16_t*)k_pages;
+    ca.vp = (const uint16_t*)v_pages;
+    ca.page_table = page_table;
+    ca.B = p->B; ca.Hq = p->Hq; ca.Hkv = p->Hkv; ca.d = p->d; ca.C = p->C; ca.N = p->N;
+    ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
+    ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots; ca.cpw = pl.cpw;
+    ca.sigma = pl.sigma; ca.part = part; ca.slot0 = slot;
+    ca.counter = cnt + kCntChunk;
+    ca.out = out;
+    ca.lse = lse;
     e = tcs::launch_chunks(ca, s);
     if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
     return TCS_OK;
@@ -422,7 +372,7 @@ tcs_status sparse_attn_decode_timed(const tcs_decode_params* p, const void* q,
 int tcs_decode_stage_count(const tcs_decode_params* p) {
     DecodePlan pl;
     if (plan_decode(p, &pl) != TCS_OK) return -1;
-    return p->levels == 2 ? 3 : 1;
+    return p->levels == 2 ? 3 : 2;
 }
 
 tcs_status tcs_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {

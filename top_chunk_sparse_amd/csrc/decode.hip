@@ -24,15 +24,13 @@
 
 #include <math.h>
 
-#include <algorithm>
-
 namespace tcs {
 
 constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for empty softmax state
 constexpr int kMaxSliceRows = 1024;   // rows (gists, or page rows) one workgroup holds logits for
 
 #ifndef TCS_K_U
-#define TCS_K_U 8       // row passes per batch of loads in the K phase
+#define TCS_K_U 4       // row passes per batch of loads in the K phase
 #endif
 #ifndef TCS_V_U
 #define TCS_V_U 4       // row passes per batch of loads in the V phase
@@ -71,98 +69,58 @@ struct RowStream {
         }
     }
 
-    // A workgroup's rows come in segments (one gist slice, or one page per chunk); segment j
-    // has seg.rows(j) rows starting at seg.k(j) / seg.v(j) and owns LDS rows
-    // [seg.row0(j), seg.row0(j) + rows).  Each phase walks batches of U row passes, segment
-    // after segment, with the next batch's loads issued before the current batch is used.
-    template <int U, class Seg>
-    __device__ void load_batch(const Seg& seg, int nb, int t, bool v, uint4 (&r)[U]) const {
-        const int j = t / nb, b = t - (t / nb) * nb;
-        const int rows = seg.rows(j);
-        const uint16_t* p = v ? seg.v(j) : seg.k(j);
+    // K phase: lg[(row0 + r) * G + h] = sigma * q_h . K[r] + bias for rows r < nrows.
+    template <int U>
+    __device__ void logits(const uint32_t (&q2)[G][4], const uint16_t* __restrict__ K, int nrows,
+                           float sigma, float bias, float* lg, int row0) const {
+        for (int base = 0; base < nrows; base += U * RPP) {
+            uint4 kr[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int row = (b * U + u) * RPP + lrow;
-            r[u] = row < rows ? ld16(p + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
-        }
-    }
-
-    template <int U, class Seg>
-    __device__ void use_k(const uint32_t (&q2)[G][4], const Seg& seg, int nb, int t, float sigma,
-                          const uint4 (&r)[U], float* lg) const {
-        const int j = t / nb, b = t - (t / nb) * nb;
-        const int rows = seg.rows(j), row0 = seg.row0(j);
-        const float bias = seg.bias(j);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int row = (b * U + u) * RPP + lrow;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float s = dot2(q2[h][0], r[u].x, 0.f);
-                s = dot2(q2[h][1], r[u].y, s);
-                s = dot2(q2[h][2], r[u].z, s);
-                s = dot2(q2[h][3], r[u].w, s);
-                s = group_sum<LPR>(s);
-                if (part == 0 && row < rows) lg[(row0 + row) * G + h] = fmaf(s, sigma, bias);
+            for (int u = 0; u < U; ++u) {
+                const int row = base + u * RPP + lrow;
+                kr[u] = row < nrows ? ld16(K + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
             }
-        }
-    }
-
-    template <int U, class Seg>
-    __device__ void use_v(const Seg& seg, int nb, int t, const uint4 (&r)[U], const float* w,
-                          float (&acc)[G][8]) const {
-        const int j = t / nb, b = t - (t / nb) * nb;
-        const int rows = seg.rows(j), row0 = seg.row0(j);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int row = (b * U + u) * RPP + lrow;
-            if (row < rows) {
-                float vf[8];
-                unpack8(r[u], vf);
-                const float* wr = w + (row0 + row) * G;
+            for (int u = 0; u < U; ++u) {
+                const int row = base + u * RPP + lrow;
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    const float wh = wr[h];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wh, vf[e], acc[h][e]);
+                    float s = dot2(q2[h][0], kr[u].x, 0.f);
+                    s = dot2(q2[h][1], kr[u].y, s);
+                    s = dot2(q2[h][2], kr[u].z, s);
+                    s = dot2(q2[h][3], kr[u].w, s);
+                    s = group_sum<LPR>(s);
+                    if (part == 0 && row < nrows) lg[(row0 + row) * G + h] = fmaf(s, sigma, bias);
                 }
             }
         }
     }
 
-    // K phase over all segments: lg[(row0 + r) * G + h] = sigma * q_h . K[r] + bias.
-    template <int U, class Seg>
-    __device__ void logits(const uint32_t (&q2)[G][4], const Seg& seg, int nseg, int max_rows,
-                           float sigma, float* lg) const {
-        const int nb = (max_rows + U * RPP - 1) / (U * RPP);
-        const int total = nseg * nb;
-        if (total <= 0) return;
-        uint4 b0[U], b1[U];
-        load_batch<U>(seg, nb, 0, false, b0);
-        for (int t = 0; t < total; t += 2) {
-            if (t + 1 < total) load_batch<U>(seg, nb, t + 1, false, b1);
-            use_k<U>(q2, seg, nb, t, sigma, b0, lg);
-            if (t + 1 < total) {
-                if (t + 2 < total) load_batch<U>(seg, nb, t + 2, false, b0);
-                use_k<U>(q2, seg, nb, t + 1, sigma, b1, lg);
+    // V phase: acc[h][e] += w[(row0 + r) * G + h] * V[r][part*8 + e] for rows r < nrows.
+    template <int U>
+    __device__ void accumulate(float (&acc)[G][8], const uint16_t* __restrict__ V, int nrows,
+                               const float* w, int row0) const {
+        for (int base = 0; base < nrows; base += U * RPP) {
+            uint4 vr[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int row = base + u * RPP + lrow;
+                vr[u] = row < nrows ? ld16(V + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
             }
-        }
-    }
-
-    // V phase over all segments, weights w[(row0 + r) * G + h]; b0 holds batch 0, loaded by
-    // the caller with load_batch (so its latency can overlap other work).
-    template <int U, class Seg>
-    __device__ void accumulate(const Seg& seg, int nseg, int max_rows, const float* w,
-                               uint4 (&b0)[U], float (&acc)[G][8]) const {
-        const int nb = (max_rows + U * RPP - 1) / (U * RPP);
-        const int total = nseg * nb;
-        uint4 b1[U];
-        for (int t = 0; t < total; t += 2) {
-            if (t + 1 < total) load_batch<U>(seg, nb, t + 1, true, b1);
-            use_v<U>(seg, nb, t, b0, w, acc);
-            if (t + 1 < total) {
-                if (t + 2 < total) load_batch<U>(seg, nb, t + 2, true, b0);
-                use_v<U>(seg, nb, t + 1, b1, w, acc);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int row = base + u * RPP + lrow;
+                if (row < nrows) {
+                    float vf[8];
+                    unpack8(vr[u], vf);
+                    const float* wr = w + (row0 + row) * G;
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float wh = wr[h];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wh, vf[e], acc[h][e]);
+                    }
+                }
             }
         }
     }
@@ -210,7 +168,7 @@ struct HeadStatsSmem {
 };
 
 template <int G>
-__device__ __forceinline__ void head_stats(float* lg, int n, HeadStatsSmem<G>& sm) {
+__device__ void head_stats(float* lg, int n, HeadStatsSmem<G>& sm) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     float x[G];
 #pragma unroll
@@ -262,35 +220,21 @@ __device__ __forceinline__ void write_empty_partial(const Partials& P, int bh0, 
 }
 
 // ---------------------------------------------------------------------------------------
-// Selection shared by the scoring passes, in two steps.  select_publish (every workgroup,
-// right after its scores are known): keep the best min(k, items in the slice) of the slice's
-// items (ascending), hand them off with their scores, and count the workgroup in; the
-// atomic's result is only looked at later, so its latency hides under the V stream.
-// select_merge (the workgroup that arrived last, at its end): merge the slices' lists --
-// ascending item order, slice after slice -- into the unit's top-k.  Ties go to the lower item
-// index at both steps, so the result equals a top-k over all items at once.
+// Selection epilogue shared by the scoring passes.  Each workgroup keeps the best
+// min(k, items in its slice) of its slice's items (ascending), stores them with their
+// scores, and the last workgroup of the unit to finish merges the slices' lists (which are
+// in ascending item order, slice after slice) into the unit's top-k.  Ties go to the lower
+// item index at both steps, so the result equals a top-k over all items at once.
 // ---------------------------------------------------------------------------------------
 struct MergeCand {
     float score[256];
     int32_t idx[256];
 };
 
-constexpr int kStagedSlices = 128;   // slice statistics the merge stages in LDS
-
-struct SelectSmem {
-    TopkSmem topk;
-    SmallTopkSmem small;
-    ReduceSmem red;
-    MergeCand mc;
-    float slse[2 * kStagedSlices];
-    float lse;
-    int flag;
-    int chosen[64];
-};
-
-// Returns, in thread 0, the arrival counter's value before this workgroup's increment.
-__device__ __forceinline__ unsigned select_publish(const SelectOut& so, int u, int slot, int nslices,
-                                   const float* s_score, int item0, int nitems, SelectSmem& ss) {
+__device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
+                                const float* s_score, int item0, int nitems, int last_items,
+                                float* lse_part_lds, void* scratch, MergeCand& mc, int* s_flag,
+                                int* s_chosen, ReduceSmem& red) {
     const int tid = threadIdx.x;
     const int kc = so.k < nitems ? so.k : nitems;
     float* cs = so.cand_score + ((long long)u * nslices + slot) * so.kcap;
@@ -299,10 +243,10 @@ __device__ __forceinline__ unsigned select_publish(const SelectOut& so, int u, i
     if (so.slice_lse) {
         float mx = -INFINITY;
         for (int i = tid; i < nitems; i += 256) mx = fmaxf(mx, s_score[i]);
-        mx = block_max(mx, ss.red);
+        mx = block_max(mx, red);
         float z = 0.f;
         for (int i = tid; i < nitems; i += 256) z += expf(s_score[i] - mx);
-        z = block_sum(z, ss.red);
+        z = block_sum(z, red);
         if (tid == 0) {
             st_shared_dev(so.slice_lse + ((long long)u * nslices + slot) * 2, mx);
             st_shared_dev(so.slice_lse + ((long long)u * nslices + slot) * 2 + 1, z);
@@ -316,90 +260,63 @@ __device__ __forceinline__ unsigned select_publish(const SelectOut& so, int u, i
     if (kc == nitems) {
         for (int i = tid; i < nitems; i += 256) emit(i, i);
     } else if (nitems <= 256) {
-        small_topk(nitems, so.k, sc, emit, ss.small);
+        small_topk(nitems, so.k, sc, emit, *reinterpret_cast<SmallTopkSmem*>(scratch));
     } else {
-        block_topk(nitems, so.k, sc, emit, ss.topk);
+        block_topk(nitems, so.k, sc, emit, *reinterpret_cast<TopkSmem*>(scratch));
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    wait_vmem();                      // this wave's hand-off stores have completed
-    __syncthreads();
-    unsigned old = 0;
-    if (tid == 0) old = atomicAdd(so.counter + u, 1u);
-    return old;
-}
+    if (!arrive_last(so.counter + u, (unsigned)nslices, s_flag)) return;
 
-// All threads call this with the counter value select_publish returned.  True in the
-// workgroup that arrived last (which also returns the counter to zero).
-__device__ __forceinline__ bool select_is_last(const SelectOut& so, int u, int nslices, unsigned old,
-                               SelectSmem& ss) {
-    if (threadIdx.x == 0) {
-        const bool last = old == (unsigned)nslices - 1u;
-        if (last) atomicExch(so.counter + u, 0u);
-        ss.flag = last;
-    }
-    __syncthreads();
-    const bool last = ss.flag != 0;
-    if (last) {
-        wait_vmem();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
-    return last;
-}
-
-// The last workgroup merges the slices' candidates into sel (and the gate), written with
-// hand-off stores so that workgroups of the same kernel may read them.
-__device__ __forceinline__ void select_merge(const SelectOut& so, int u, int nslices, int last_items,
-                             SelectSmem& ss) {
-    const int tid = threadIdx.x;
+    // ---- last workgroup of the unit: merge ------------------------------------------------
     const float* ucs = so.cand_score + (long long)u * nslices * so.kcap;
     const int32_t* uci = so.cand_idx + (long long)u * nslices * so.kcap;
     const int ncand = (nslices - 1) * so.kcap + (so.k < last_items ? so.k : last_items);
     const bool staged = ncand <= 256;
     // one round trip for every hand-off value this workgroup needs
     const float* sl = so.slice_lse ? so.slice_lse + (long long)u * nslices * 2 : nullptr;
+    float* st = reinterpret_cast<float*>(scratch);     // slice statistics, if they fit
     const bool gate = sl && so.gamma;
-    const bool lse_staged = nslices <= kStagedSlices;
+    const bool lse_staged = 2 * nslices <= kTopkCache;
     if (staged && tid < ncand) {
-        ss.mc.score[tid] = ld_shared_dev(ucs + tid);
-        ss.mc.idx[tid] = ld_shared_dev(uci + tid);
+        mc.score[tid] = ld_shared_dev(ucs + tid);
+        mc.idx[tid] = ld_shared_dev(uci + tid);
     }
     if (gate && lse_staged)
-        for (int i = tid; i < 2 * nslices; i += 256) ss.slse[i] = ld_shared_dev(sl + i);
+        for (int i = tid; i < 2 * nslices; i += 256) st[i] = ld_shared_dev(sl + i);
     __syncthreads();
     float lse = 0.f;
     if (gate) {
-        auto at = [&](int i) { return lse_staged ? ss.slse[i] : ld_shared_dev(sl + i); };
+        auto at = [&](int i) { return lse_staged ? st[i] : ld_shared_dev(sl + i); };
         if (tid == 0) {
             float mx = -INFINITY;
             for (int s = 0; s < nslices; ++s) mx = fmaxf(mx, at(2 * s));
             float z = 0.f;
             for (int s = 0; s < nslices; ++s) z += at(2 * s + 1) * expf(at(2 * s) - mx);
-            ss.lse = mx + logf(z);
+            *lse_part_lds = mx + logf(z);
         }
         __syncthreads();
-        lse = ss.lse;
+        lse = *lse_part_lds;
     }
     int32_t* sel = so.sel + (long long)u * so.k;
     float* gam = so.gamma ? so.gamma + (long long)u * so.k : nullptr;
-    auto score_at = [&](int i) { return staged ? ss.mc.score[i] : ld_shared_dev(ucs + i); };
+    auto score_at = [&](int i) { return staged ? mc.score[i] : ld_shared_dev(ucs + i); };
     auto emit2 = [&](int j, int i) {
-        const int32_t c = staged ? ss.mc.idx[i] : ld_shared_dev(uci + i);
-        st_shared_dev(sel + j, c);
-        if (gam) st_shared_dev(gam + j, score_at(i) - lse);
-        if (j < 64) ss.chosen[j] = c;
+        const int32_t c = staged ? mc.idx[i] : ld_shared_dev(uci + i);
+        sel[j] = c;
+        if (gam) gam[j] = score_at(i) - lse;
+        if (j < 64) s_chosen[j] = c;
     };
     int ke;
     if (so.k >= ncand) {
         for (int i = tid; i < ncand; i += 256) emit2(i, i);
         ke = ncand;
     } else if (staged) {
-        ke = small_topk(ncand, so.k, score_at, emit2, ss.small);
+        ke = small_topk(ncand, so.k, score_at, emit2, *reinterpret_cast<SmallTopkSmem*>(scratch));
     } else {
-        ke = block_topk(ncand, so.k, score_at, emit2, ss.topk);
+        ke = block_topk(ncand, so.k, score_at, emit2, *reinterpret_cast<TopkSmem*>(scratch));
     }
     for (int j = ke + tid; j < so.k; j += 256) {
-        st_shared_dev(sel + j, (int32_t)-1);
-        if (gam) st_shared_dev(gam + j, 0.f);
+        sel[j] = -1;
+        if (gam) gam[j] = 0.f;
     }
     if (so.fill_scores) {
         // two-level group pass: chunks outside the chosen groups are never scored
@@ -408,51 +325,90 @@ __device__ __forceinline__ void select_merge(const SelectOut& so, int u, int nsl
         for (int c = tid; c < so.H; c += 256) {
             const int r = c / so.J;
             bool in = false;
-            for (int j = 0; j < ke && j < 64; ++j) in |= ss.chosen[j] == r;
+            for (int j = 0; j < ke && j < 64; ++j) in |= s_chosen[j] == r;
             if (!in) fs[c] = -INFINITY;
         }
     }
 }
 
-// Bounded wait until *flag != 0 (thread 0 polls, the workgroup waits at a barrier).  Returns
-// false if the flag did not come up within `limit` polls; the caller then poisons its result
-// instead of waiting on.
-__device__ __forceinline__ bool wait_flag(const unsigned* flag, unsigned limit, int* s_ok) {
-    if (threadIdx.x == 0) {
-        unsigned n = 0;
-        int ok = 1;
-        while (ld_shared_dev(flag) == 0u) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++n >= limit) { ok = 0; break; }
-        }
-        *s_ok = ok;
+// ---------------------------------------------------------------------------------------
+// gist_kernel: grid (slices, units).  Range mode: slice y covers items (chunks, or level-2
+// groups) [y*ips, min((y+1)*ips, nitems)).  Group mode (a.groups != null): slice y covers the
+// member chunks of level-2 group groups[u][y].
+// ---------------------------------------------------------------------------------------
+template <int D, int G>
+struct GistSmem {
+    union {
+        float lg[kMaxSliceRows * G];                   // logits, then softmax weights
+        float fin[RowStream<D, G>::NW * G * D];
+        TopkSmem topk;
+        SmallTopkSmem small;
+    } x;
+    float score[kMaxSliceRows];
+    MergeCand mc;
+    HeadStatsSmem<G> hs;
+    ReduceSmem red;
+    float lse;
+    int flag;
+    int chosen[64];
+};
+
+template <int D, int G>
+__global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
+    using RS = RowStream<D, G>;
+    __shared__ GistSmem<D, G> sm;
+    const int y = blockIdx.x, u = blockIdx.y;
+    const int b = u / a.Hkv, kv = u % a.Hkv;
+    const int bh0 = b * a.Hq + kv * G;
+    int c0, c1, last_items;
+    if (a.groups) {
+        const int r = a.groups[(long long)u * a.k2 + y];
+        c0 = r * a.J;
+        c1 = min(c0 + a.J, a.H);
+        const int rl = a.groups[(long long)u * a.k2 + a.slices - 1];
+        last_items = min(a.J, a.H - rl * a.J);
+    } else {
+        c0 = y * a.items_per_slice;
+        c1 = min(c0 + a.items_per_slice, a.nitems);
+        last_items = a.nitems - (a.slices - 1) * a.items_per_slice;
+    }
+    const int nit = max(c1 - c0, 0);
+    const int nrows = nit * a.g;
+    const RS rs;
+    const uint16_t* K = a.gk + (long long)u * a.unit_stride + (long long)c0 * a.g * D;
+    const uint16_t* V = a.gv + (long long)u * a.unit_stride + (long long)c0 * a.g * D;
+    {
+        uint32_t q2[G][4];
+        rs.load_q(a.q + (long long)bh0 * D, q2);
+        rs.template logits<TCS_K_U>(q2, K, nrows, a.sigma, 0.f, sm.x.lg, 0);
     }
     __syncthreads();
-    const bool ok = *s_ok != 0;
-    wait_vmem();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return ok;
-}
-
-// Raise *flag after this workgroup's hand-off stores have completed.
-__device__ __forceinline__ void raise_flag(unsigned* flag) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    wait_vmem();
+    // pooled item scores: log-sum-exp over the G heads and g gists of each item
+    for (int c = threadIdx.x; c < nit; c += 256) {
+        const float* x = sm.x.lg + c * a.g * G;
+        float mx = -INFINITY;
+        for (int i = 0; i < a.g * G; ++i) mx = fmaxf(mx, x[i]);
+        float z = 0.f;
+        for (int i = 0; i < a.g * G; ++i) z += expf(x[i] - mx);
+        const float s = mx + logf(z);
+        sm.score[c] = s;
+        if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
+    }
+    head_stats<G>(sm.x.lg, nrows, sm.hs);
+    {
+        float acc[G][8];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+        rs.template accumulate<TCS_V_U>(acc, V, nrows, sm.x.lg, 0);
+        __syncthreads();   // weights dead: fin may reuse the space
+        rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
+    }
     __syncthreads();
-    if (threadIdx.x == 0) st_shared_dev(flag, 1u);
+    select_epilogue(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.lse, &sm.x,
+                    sm.mc, &sm.flag, sm.chosen, sm.red);
 }
-
-// One contiguous run of gist rows (K and V), LDS rows from 0.
-struct GistSeg {
-    const uint16_t* kp;
-    const uint16_t* vp;
-    int n;
-    __device__ const uint16_t* k(int) const { return kp; }
-    __device__ const uint16_t* v(int) const { return vp; }
-    __device__ int rows(int) const { return n; }
-    __device__ int row0(int) const { return 0; }
-    __device__ float bias(int) const { return 0.f; }
-};
 
 // ---------------------------------------------------------------------------------------
 // Fixed-order merge of every slot's partial for the G heads of one unit -> out, lse.  All
@@ -468,15 +424,12 @@ struct MergeSmem {
 };
 
 template <int D, int G>
-__device__ __forceinline__ void merge_partials(const Partials& P, int bh0, float* out, float* lse,
+__device__ void merge_partials(const Partials& P, int bh0, float* out, float* lse,
                                MergeSmem<G>& sm) {
     const int ns = P.nslots;
     const int tid = threadIdx.x;
     constexpr int PPT = (G * D + 255) / 256;   // (head, column) outputs per thread
-#ifndef TCS_MERGE_SB
-#define TCS_MERGE_SB 32
-#endif
-    constexpr int SB = TCS_MERGE_SB / PPT;     // slots whose values one batch holds
+    constexpr int SB = 32 / PPT;               // slots whose values one batch holds
     const bool staged = G * ns <= kMergeStage;
     float v[PPT][SB];
     auto load_batch = [&](int s0) {
@@ -553,194 +506,6 @@ __device__ __forceinline__ void merge_partials(const Partials& P, int bh0, float
     }
 }
 
-// Final merge: which counter, how many arrivals, and where the result goes.
-struct FinalMerge {
-    unsigned* counter;    // [units]
-    unsigned total;       // arrivals per unit
-    float* out;
-    float* lse;
-    unsigned* ready;      // persistent kernel: the selection flags to lower again, else null
-};
-
-// ---------------------------------------------------------------------------------------
-// gist item: one slice of a unit.  Range mode: slice y covers items (chunks, or level-2
-// groups) [y*ips, min((y+1)*ips, nitems)).  Group mode (a.groups != null): slice y covers the
-// member chunks of level-2 group groups[u][y].  With `fm` the slice also counts towards the
-// unit's final merge (persistent kernel), and `ready` is raised once the selection is made.
-// ---------------------------------------------------------------------------------------
-template <int D, int G>
-struct GistSmem {
-    union {
-        float lg[kMaxSliceRows * G];                   // logits, then softmax weights
-        float fin[RowStream<D, G>::NW * G * D];
-        MergeSmem<G> merge;
-    } x;
-    float score[kMaxSliceRows];
-    HeadStatsSmem<G> hs;
-    SelectSmem ss;
-    int flag;
-};
-
-// The chunks (or level-2 groups) of slice y of unit u.
-struct SliceRange {
-    int c0, nit, nrows, last_items;
-};
-
-__device__ __forceinline__ SliceRange slice_range(const GistLaunch& a, int u, int y) {
-    SliceRange r;
-    int c1;
-    if (a.groups) {
-        const int g = ld_shared_dev(a.groups + (long long)u * a.k2 + y);
-        r.c0 = g * a.J;
-        c1 = min(r.c0 + a.J, a.H);
-        const int gl = ld_shared_dev(a.groups + (long long)u * a.k2 + a.slices - 1);
-        r.last_items = min(a.J, a.H - gl * a.J);
-    } else {
-        r.c0 = y * a.items_per_slice;
-        c1 = min(r.c0 + a.items_per_slice, a.nitems);
-        r.last_items = a.nitems - (a.slices - 1) * a.items_per_slice;
-    }
-    r.nit = max(c1 - r.c0, 0);
-    r.nrows = r.nit * a.g;
-    return r;
-}
-
-template <int D>
-__device__ __forceinline__ GistSeg gist_seg(const GistLaunch& a, int u, const SliceRange& r) {
-    return GistSeg{a.gk + (long long)u * a.unit_stride + (long long)r.c0 * a.g * D,
-                   a.gv + (long long)u * a.unit_stride + (long long)r.c0 * a.g * D, r.nrows};
-}
-
-// Scoring part of a gist item: logits of the slice's gist keys (LDS), pooled item scores,
-// and the selection hand-off.  Returns (thread 0) the selection counter's old value.
-template <int D, int G>
-__device__ __forceinline__ unsigned gist_front(const GistLaunch& a, int u, int y,
-                                               const SliceRange& r, GistSmem<D, G>& sm) {
-    using RS = RowStream<D, G>;
-    const int bh0 = (u / a.Hkv) * a.Hq + (u % a.Hkv) * G;
-    const RS rs;
-    const GistSeg seg = gist_seg<D>(a, u, r);
-    {
-        uint32_t q2[G][4];
-        rs.load_q(a.q + (long long)bh0 * D, q2);
-        rs.template logits<TCS_K_U>(q2, seg, 1, r.nrows, a.sigma, sm.x.lg);
-    }
-    __syncthreads();
-    // pooled item scores: log-sum-exp over the G heads and g gists of each item
-    for (int c = threadIdx.x; c < r.nit; c += 256) {
-        const float* x = sm.x.lg + c * a.g * G;
-        float mx = -INFINITY;
-        for (int i = 0; i < a.g * G; ++i) mx = fmaxf(mx, x[i]);
-        float z = 0.f;
-        for (int i = 0; i < a.g * G; ++i) z += expf(x[i] - mx);
-        const float sc = mx + logf(z);
-        sm.score[c] = sc;
-        if (a.scores_out) a.scores_out[(long long)u * a.score_stride + r.c0 + c] = sc;
-    }
-    __syncthreads();
-    return select_publish(a.selo, u, y, a.slices, sm.score, r.c0, r.nit, sm.ss);
-}
-
-// Whole gist item (scoring, selection, then the V rows of the slice) for the separate-kernel
-// path.
-template <int D, int G>
-__device__ __forceinline__ void gist_item(const GistLaunch& a, int u, int y, GistSmem<D, G>& sm) {
-    using RS = RowStream<D, G>;
-    const int bh0 = (u / a.Hkv) * a.Hq + (u % a.Hkv) * G;
-    const SliceRange r = slice_range(a, u, y);
-    const unsigned old = gist_front<D, G>(a, u, y, r, sm);
-    const RS rs;
-    const GistSeg seg = gist_seg<D>(a, u, r);
-    uint4 vb[TCS_V_U];
-    rs.template load_batch<TCS_V_U>(seg, (r.nrows + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP),
-                                    0, true, vb);   // first V batch in flight from here on
-    if (select_is_last(a.selo, u, a.slices, old, sm.ss)) select_merge(a.selo, u, a.slices, r.last_items, sm.ss);
-    head_stats<G>(sm.x.lg, r.nrows, sm.hs);
-    float acc[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    rs.template accumulate<TCS_V_U>(seg, 1, r.nrows, sm.x.lg, vb, acc);
-    __syncthreads();   // weights dead: fin may reuse the space
-    rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
-}
-
-// Persistent-kernel K item: scoring and selection, then the slice's softmax weights and
-// statistics go to the stash for its V item, and the slice's flag is raised.
-template <int D, int G>
-__device__ __forceinline__ void gist_k_item(const GistLaunch& a, const FusedCtl& ctl, int u,
-                                            int y, GistSmem<D, G>& sm) {
-    const SliceRange r = slice_range(a, u, y);
-    const unsigned old = gist_front<D, G>(a, u, y, r, sm);
-    head_stats<G>(sm.x.lg, r.nrows, sm.hs);
-    const long long sl = (long long)u * a.slices + y;
-    float* w = ctl.wstash + sl * ctl.stash_rows * G;
-    for (int i = threadIdx.x; i < r.nrows * G; i += 256) st_shared_dev(w + i, sm.x.lg[i]);
-    if (threadIdx.x < G) {
-        st_shared_dev(ctl.sstash + (sl * G + threadIdx.x) * 2, sm.hs.M[threadIdx.x]);
-        st_shared_dev(ctl.sstash + (sl * G + threadIdx.x) * 2 + 1, sm.hs.L[threadIdx.x]);
-    }
-    raise_flag(ctl.kdone + sl);
-    if (select_is_last(a.selo, u, a.slices, old, sm.ss)) {
-        select_merge(a.selo, u, a.slices, r.last_items, sm.ss);
-        raise_flag(ctl.ready + u);
-    }
-}
-
-// Persistent-kernel V item: the V rows of a slice, weighted by the stashed softmax weights,
-// into the slice's partial; counts towards the unit's final merge.
-template <int D, int G>
-__device__ __forceinline__ void gist_v_item(const GistLaunch& a, const FusedCtl& ctl,
-                                            const FinalMerge& fm, int u, int y,
-                                            GistSmem<D, G>& sm) {
-    using RS = RowStream<D, G>;
-    const int bh0 = (u / a.Hkv) * a.Hq + (u % a.Hkv) * G;
-    const SliceRange r = slice_range(a, u, y);
-    const RS rs;
-    const GistSeg seg = gist_seg<D>(a, u, r);
-    uint4 vb[TCS_V_U];
-    rs.template load_batch<TCS_V_U>(seg, (r.nrows + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP),
-                                    0, true, vb);   // independent of the wait below
-    const long long sl = (long long)u * a.slices + y;
-    const bool ok = wait_flag(ctl.kdone + sl, ctl.spin_limit, &sm.flag);
-    const float* w = ctl.wstash + sl * ctl.stash_rows * G;
-    for (int i = threadIdx.x; i < r.nrows * G; i += 256) sm.x.lg[i] = ld_shared_dev(w + i);
-    if (threadIdx.x < G) {
-        sm.hs.M[threadIdx.x] = ld_shared_dev(ctl.sstash + (sl * G + threadIdx.x) * 2);
-        sm.hs.L[threadIdx.x] = ld_shared_dev(ctl.sstash + (sl * G + threadIdx.x) * 2 + 1);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        st_shared_dev(ctl.kdone + sl, 0u);    // this item is the flag's only reader
-        if (!ok) atomicOr(ctl.error, 1u);
-    }
-    if (!ok) {
-        write_empty_partial(a.part, bh0, G, D, a.slot0 + y, NAN, NAN);
-    } else {
-        float acc[G][8];
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        rs.template accumulate<TCS_V_U>(seg, 1, r.nrows, sm.x.lg, vb, acc);
-        __syncthreads();   // weights dead: fin may reuse the space
-        rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
-    }
-    __syncthreads();
-    if (arrive_last(fm.counter + u, fm.total, &sm.flag)) {
-        merge_partials<D, G>(a.part, bh0, fm.out, fm.lse, sm.x.merge);
-        st_shared_dev(fm.ready + u, 0u);
-    }
-}
-
-// gist_kernel: grid (slices, units), one gist item per workgroup (two-level routing).
-template <int D, int G>
-__global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
-    __shared__ GistSmem<D, G> sm;
-    gist_item<D, G>(a, blockIdx.y, blockIdx.x, sm);
-}
-
 // ---------------------------------------------------------------------------------------
 // chunk_kernel: grid (ceil((kslots + 1) / cpw), units).  Workgroup x streams slots
 // [x*cpw, (x+1)*cpw): slot j < kslots is selected chunk sel[u][j] (skipped if -1), slot
@@ -748,26 +513,6 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
 // bias.  The last workgroup of a unit merges every partial of the unit's G heads.
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxCpw = 16;
-
-struct PageSegs {
-    const uint16_t* kp;
-    const uint16_t* vp;
-    long long slab;           // elements per (page, kv head) slab: C * d
-    int kv_off;               // kv * C * d
-    int hkv;
-    int C;
-    const int* page;          // LDS: page of each chunk (< 0: no rows)
-    const int* nrows;
-    const float* gbias;
-    __device__ long long off(int j) const {
-        return ((long long)page[j] * hkv) * slab + kv_off;
-    }
-    __device__ const uint16_t* k(int j) const { return kp + (page[j] >= 0 ? off(j) : 0); }
-    __device__ const uint16_t* v(int j) const { return vp + (page[j] >= 0 ? off(j) : 0); }
-    __device__ int rows(int j) const { return page[j] >= 0 ? nrows[j] : 0; }
-    __device__ int row0(int j) const { return j * C; }
-    __device__ float bias(int j) const { return gbias[j]; }
-};
 
 template <int D, int G>
 struct ChunkSmem {
@@ -783,29 +528,22 @@ struct ChunkSmem {
     int flag;
 };
 
-// chunk item: workgroup wx of unit u streams chunk slots [wx*cpw, (wx+1)*cpw).  In the
-// persistent kernel (`wait` non-null) it first waits for the unit's selection.
 template <int D, int G>
-__device__ __forceinline__ void chunk_item(const ChunkLaunch& a, int u, int wx, ChunkSmem<D, G>& sm,
-                           const FinalMerge fm, const unsigned* wait, unsigned spin_limit,
-                           unsigned* error) {
+__global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
     using RS = RowStream<D, G>;
+    __shared__ ChunkSmem<D, G> sm;
+    const int wx = blockIdx.x, u = blockIdx.y;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
     const int j0 = wx * a.cpw, nj = min(a.cpw, a.kslots + 1 - j0);
-    bool stalled = false;
-    if (wait && !wait_flag(wait + u, spin_limit, &sm.flag)) {
-        stalled = true;
-        if (threadIdx.x == 0) atomicOr(error, 1u);
-    }
-    // this workgroup's chunks: page, gate bias and row count (page -1: none, -2: unusable)
+    // this workgroup's chunks: page, gate bias and row count (page -1: none, -2: out of range)
     if (threadIdx.x < nj) {
         const int j = j0 + threadIdx.x;
         int c, rows;
         float bias = 0.f;
         if (j < a.kslots) {
-            c = ld_shared_dev(a.sel + (long long)u * a.k + j);
-            if (c >= 0 && a.gamma) bias = ld_shared_dev(a.gamma + (long long)u * a.k + j);
+            c = a.sel[(long long)u * a.k + j];
+            if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
             rows = a.C;
         } else {
             c = a.M - 1;
@@ -816,7 +554,7 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, int u, int wx, 
             page = a.page_table[(long long)b * a.max_chunks + c];
             if (page < 0 || page >= a.num_pages) page = -2;
         }
-        sm.page[threadIdx.x] = stalled ? -2 : page;
+        sm.page[threadIdx.x] = page;
         sm.bias[threadIdx.x] = bias;
         sm.rows[threadIdx.x] = rows;
     }
@@ -828,8 +566,6 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, int u, int wx, 
         any |= sm.page[jj] >= 0;
     }
     const RS rs;
-    const PageSegs seg{a.kp, a.vp, (long long)a.C * D, kv * a.C * D, a.Hkv, a.C,
-                       sm.page, sm.rows, sm.bias};
     if (bad) {
         write_empty_partial(a.part, bh0, G, D, a.slot0 + wx, NAN, NAN);
     } else if (!any) {
@@ -838,11 +574,13 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, int u, int wx, 
         {
             uint32_t q2[G][4];
             rs.load_q(a.q + (long long)bh0 * D, q2);
-            rs.template logits<TCS_K_U>(q2, seg, nj, a.C, a.sigma, sm.x.lg);
+            for (int jj = 0; jj < nj; ++jj) {
+                if (sm.page[jj] < 0) continue;
+                const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
+                rs.template logits<TCS_K_U>(q2, a.kp + off, sm.rows[jj], a.sigma, sm.bias[jj],
+                                            sm.x.lg, jj * a.C);
+            }
         }
-        uint4 vb[TCS_V_U];
-        rs.template load_batch<TCS_V_U>(seg, (a.C + TCS_V_U * RS::RPP - 1) / (TCS_V_U * RS::RPP),
-                                        0, true, vb);   // first V batch in flight from here on
         __syncthreads();
         head_stats<G>(sm.x.lg, nj * a.C, sm.hs);
         float acc[G][8];
@@ -850,79 +588,16 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, int u, int wx, 
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        rs.template accumulate<TCS_V_U>(seg, nj, a.C, sm.x.lg, vb, acc);
+        for (int jj = 0; jj < nj; ++jj) {
+            if (sm.page[jj] < 0) continue;
+            const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
+            rs.template accumulate<TCS_V_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, jj * a.C);
+        }
         __syncthreads();
         rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + wx);
     }
-    __syncthreads();
-    if (!arrive_last(fm.counter + u, fm.total, &sm.flag)) return;
-    merge_partials<D, G>(a.part, bh0, fm.out, fm.lse, sm.x.merge);
-    if (fm.ready) st_shared_dev(fm.ready + u, 0u);
-}
-
-// chunk_kernel: grid (chunk workgroups per unit, units).
-template <int D, int G>
-__global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
-    __shared__ ChunkSmem<D, G> sm;
-    const FinalMerge fm{a.counter, gridDim.x, a.out, a.lse, nullptr};
-    chunk_item<D, G>(a, blockIdx.y, blockIdx.x, sm, fm, nullptr, 0u, nullptr);
-}
-
-// ---------------------------------------------------------------------------------------
-// fused_kernel: the whole one-level decode in one launch of one workgroup per work item.
-// Units are dealt round-robin to nq queues, nq dividing the unit count, so every queue has
-// the same list length: first the K item of every gist slice of its units (scoring and
-// selection), then the V item of every slice (which waits for its own K item), then every
-// chunk workgroup of its units (unit-major each) -- so the scoring of all units, on which
-// the selections depend, is read first.  Workgroup w belongs to queue w % nq -- interleaved, so that
-// workgroups starting early take the gist tickets of every queue -- and takes the next
-// ticket of its queue when it starts running and does that item.  A V item waits (bounded) for
-// its K item, a chunk item for its unit's selection, which the K items publish; K items never
-// wait, and within a queue every K ticket is taken -- by a workgroup that is already running --
-// before any other ticket, so each wait has a running producer whatever order the hardware
-// starts workgroups in.  Spreading the tickets over nq counters keeps the ticket atomics from
-// serialising on one address.  The unit's final merge runs in whichever of its items
-// finishes last; the last item of a queue returns the queue's counters to zero.
-// ---------------------------------------------------------------------------------------
-template <int D, int G>
-union FusedSmem {
-    GistSmem<D, G> g;
-    ChunkSmem<D, G> c;
-};
-
-template <int D, int G>
-__global__ void __launch_bounds__(256) fused_kernel(GistLaunch g, ChunkLaunch c, FusedCtl ctl) {
-    __shared__ FusedSmem<D, G> sm;
-    __shared__ int s_item;
-    const int units = g.B * g.Hkv;
-    const int ncw = (c.kslots + 1 + c.cpw - 1) / c.cpw;
-    const int nq = ctl.nq;                          // divides units
-    const int q = blockIdx.x % nq;
-    const int uq = units / nq;                      // units of each queue
-    const int nk = uq * g.slices;                   // K items, then as many V items, then chunks
-    const int nitems = 2 * nk + uq * ncw;
-    if (threadIdx.x == 0) s_item = (int)atomicAdd(ctl.queue + q, 1u);
-    __syncthreads();
-    const int t = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar branch
-    const FinalMerge fm{ctl.done, (unsigned)(g.slices + ncw), c.out, c.lse, ctl.ready};
-    if (t < nk) {
-        gist_k_item<D, G>(g, ctl, q + (t / g.slices) * nq, t % g.slices, sm.g);
-    } else if (t < 2 * nk) {
-        const int v = t - nk;
-        gist_v_item<D, G>(g, ctl, fm, q + (v / g.slices) * nq, v % g.slices, sm.g);
-    } else if (t < nitems) {
-        const int ci = t - 2 * nk;
-        chunk_item<D, G>(c, q + (ci / ncw) * nq, ci % ncw, sm.c, fm, ctl.ready, ctl.spin_limit,
-                         ctl.error);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = atomicAdd(ctl.queue + nq + q, 1u);
-        if (old == (unsigned)nitems - 1u) {   // every ticket of this queue is taken and done
-            atomicExch(ctl.queue + q, 0u);
-            atomicExch(ctl.queue + nq + q, 0u);
-        }
-    }
+    if (!arrive_last(a.counter + u, (unsigned)gridDim.x, &sm.flag)) return;
+    merge_partials<D, G>(a.part, bh0, a.out, a.lse, sm.x.merge);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -978,28 +653,6 @@ hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s) {
         return hipErrorInvalidValue;
     dim3 grid((a.kslots + 1 + a.cpw - 1) / a.cpw, a.B * a.Hkv);
     return a.d == 128 ? chunk_d<128>(a, s, grid) : chunk_d<64>(a, s, grid);
-}
-
-template <int D>
-static hipError_t fused_d(const FusedLaunch& a, hipStream_t s, int grid) {
-    switch (a.g.Hq / a.g.Hkv) {
-        case 1: fused_kernel<D, 1><<<grid, 256, 0, s>>>(a.g, a.c, a.ctl); break;
-        case 2: fused_kernel<D, 2><<<grid, 256, 0, s>>>(a.g, a.c, a.ctl); break;
-        case 4: fused_kernel<D, 4><<<grid, 256, 0, s>>>(a.g, a.c, a.ctl); break;
-        case 8: fused_kernel<D, 8><<<grid, 256, 0, s>>>(a.g, a.c, a.ctl); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_fused(const FusedLaunch& a, hipStream_t s) {
-    const ChunkLaunch& c = a.c;
-    if (c.cpw < 1 || c.cpw > kMaxCpw || (long long)c.cpw * c.C > kMaxSliceRows || a.g.slices < 1)
-        return hipErrorInvalidValue;
-    const long long units = (long long)a.g.B * a.g.Hkv;
-    const long long items = 2 * units * a.g.slices + units * ((c.kslots + 1 + c.cpw - 1) / c.cpw);
-    if (items > 0x7fffffffLL || a.ctl.nq < 1 || units % a.ctl.nq) return hipErrorInvalidValue;
-    return a.g.d == 128 ? fused_d<128>(a, s, (int)items) : fused_d<64>(a, s, (int)items);
 }
 
 hipError_t launch_fill(int32_t* p, long long n, int32_t v, hipStream_t s) {

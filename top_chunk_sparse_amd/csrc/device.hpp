@@ -20,7 +20,7 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
 }
 
 #ifndef TCS_NT_LOADS
-#define TCS_NT_LOADS 0   // 1: stream K/V rows with non-temporal loads
+#define TCS_NT_LOADS 1   // stream K/V rows with non-temporal loads (read once)
 #endif
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -113,10 +113,12 @@ __device__ __forceinline__ float block_sum(float x, ReduceSmem& sm) {
 // Chooses the min(k, n) largest of n fp32 scores, equal scores going to the lower position,
 // and writes the chosen positions in ascending order.  Radix select on the ordered 32-bit
 // key finds the threshold key T (the k_eff-th largest); every key > T is taken, then the
-// lowest positions holding T until k_eff are reached.  256 threads.  Keys are recomputed
-// from score(i) on every pass unless a cache of at least n entries is supplied.
+// lowest positions holding T until k_eff are reached.  256 threads.
+constexpr int kTopkCache = 4096;   // keys staged in LDS; larger n re-reads global memory
+
 struct TopkSmem {
     unsigned hist[256];
+    uint32_t keys[kTopkCache];
     int digit;
     unsigned above;
     uint32_t band[4], bor[4];
@@ -126,16 +128,15 @@ struct TopkSmem {
 // score(i) -> fp32 score of position i; emit(j, i) is called once for the j-th chosen position
 // (j ascending with i).  Returns k_eff.
 template <class ScoreFn, class EmitFn>
-__device__ int block_topk(int n, int k, ScoreFn score, EmitFn emit, TopkSmem& sm,
-                          uint32_t* key_cache = nullptr, int cache_cap = 0) {
+__device__ int block_topk(int n, int k, ScoreFn score, EmitFn emit, TopkSmem& sm) {
     const int tid = threadIdx.x;
     const int ke = k < n ? k : n;
     if (ke <= 0) return 0;
-    const bool cached = key_cache != nullptr && n <= cache_cap;
+    const bool cached = n <= kTopkCache;
     if (cached)
-        for (int i = tid; i < n; i += 256) key_cache[i] = ordered_key(score(i));
+        for (int i = tid; i < n; i += 256) sm.keys[i] = ordered_key(score(i));
     __syncthreads();
-    auto key_at = [&](int i) -> uint32_t { return cached ? key_cache[i] : ordered_key(score(i)); };
+    auto key_at = [&](int i) -> uint32_t { return cached ? sm.keys[i] : ordered_key(score(i)); };
 
     // Bytes shared by every key need no histogram pass: start at the first byte that differs.
     uint32_t kand = 0xFFFFFFFFu, kor = 0u;

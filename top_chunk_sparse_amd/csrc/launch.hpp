@@ -13,8 +13,7 @@ struct Partials {
     int nslots;
 };
 
-// Selection handed from every workgroup of a unit to the last one (select_publish /
-// select_merge).
+// Selection done by the last workgroup of each unit (see select_epilogue).
 struct SelectOut {
     int k;                    // entries per unit in sel / gamma
     int32_t* sel;             // [units][k] ascending item ids, -1 padded
@@ -67,30 +66,7 @@ struct ChunkLaunch {
     float* lse;               // [B*Hq] or null
 };
 
-// The persistent one-level decode: gist slices, then chunk workgroups, from one queue.
-constexpr int kMaxQueues = 16;
-
-struct FusedCtl {
-    unsigned* queue;          // [2 * nq]: next ticket, items finished, per queue; zero between calls
-    int nq;                   // ticket queues; divides the unit count (units dealt round-robin)
-    unsigned* ready;          // [units]: selection published; zero between calls
-    unsigned* done;           // [units]: items finished, for the final merge; zero between calls
-    unsigned* error;          // [1]: set if a wait ran out (the unit's output is NaN)
-    unsigned spin_limit;      // polls before a wait gives up
-    unsigned* kdone;          // [units * slices]: K item done; zero between calls
-    float* wstash;            // [units * slices][stash_rows * G] softmax weights of a slice
-    float* sstash;            // [units * slices][G][2] (max, sum) of a slice
-    int stash_rows;           // rows per slice in wstash
-};
-
-struct FusedLaunch {
-    GistLaunch g;             // range mode over the historical chunks
-    ChunkLaunch c;
-    FusedCtl ctl;
-};
-
 hipError_t launch_gist(const GistLaunch& a, hipStream_t s);
-hipError_t launch_fused(const FusedLaunch& a, hipStream_t s);
 hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t v, hipStream_t s);

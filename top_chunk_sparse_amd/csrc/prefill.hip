@@ -14,7 +14,6 @@ namespace tcs {
 
 __global__ void __launch_bounds__(256) prefill_select_kernel(PrefillSelectLaunch a) {
     __shared__ TopkSmem sm;
-    __shared__ uint32_t key_cache[4096];
     __shared__ ReduceSmem red;
     const int row = blockIdx.x;                 // (unit * nb + i)
     const int i = row % a.nb;
@@ -37,7 +36,7 @@ __global__ void __launch_bounds__(256) prefill_select_kernel(PrefillSelectLaunch
             sel[x] = j;
             if (gam) gam[x] = s[j] - lse;
         },
-        sm, key_cache, 4096);
+        sm);
     for (int x = ke + threadIdx.x; x < a.k; x += 256) {
         sel[x] = -1;
         if (gam) gam[x] = 0.f;
