@@ -112,3 +112,94 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
         report.update(stats)
     assert err_out <= tol and err_lse <= tol, stats
     return stats
+
+
+# ---------------------------------------------------------------------------------------
+# GPU-vs-oracle parity (prefill)
+# ---------------------------------------------------------------------------------------
+def check_prefill_selection(inp: PrefillInputs, gsel: np.ndarray, k: int):
+    """Property check of the block selection on every (b, kv, i) row, any size: ascending,
+    in range, -1 padded to min(k, i) entries, and the chosen set is a top set of S[i][j < i]
+    under (score desc, index asc) -- every chosen score beats every unchosen one, and a tie
+    at the boundary goes to the lower index.  Returns the number of rows checked."""
+    c = inp.cfg
+    S = inp.S.cpu().numpy().astype(np.float32)
+    nb = c.nb
+    gsel = gsel.reshape(c.B * c.Hkv, nb, k)
+    S = S.reshape(c.B * c.Hkv, nb, nb)
+    for i in range(nb):
+        ke = min(k, i)
+        rows = gsel[:, i, :]
+        assert (rows[:, ke:] == -1).all(), f"block {i}: padding"
+        if ke == 0:
+            continue
+        chosen = rows[:, :ke]
+        assert ((chosen >= 0) & (chosen < i)).all(), f"block {i}: index out of range"
+        assert (np.diff(chosen, axis=1) > 0).all(), f"block {i}: not ascending"
+        if ke == i:
+            continue
+        s_i = S[:, i, :i]
+        mask = np.zeros((len(rows), i), bool)
+        np.put_along_axis(mask, chosen.astype(np.int64), True, axis=1)
+        ch_min = np.where(mask, s_i, np.inf).min(axis=1)
+        un_max = np.where(mask, -np.inf, s_i).max(axis=1)
+        assert (ch_min >= un_max).all(), f"block {i}: a better block was left out"
+        tie = ch_min == un_max
+        for u in np.nonzero(tie)[0]:
+            v = ch_min[u]
+            hi_ch = np.nonzero(mask[u] & (s_i[u] == v))[0].max()
+            lo_un = np.nonzero(~mask[u] & (s_i[u] == v))[0].min()
+            assert hi_ch < lo_un, f"block {i} unit {u}: tie not broken to the lower index"
+    return c.B * c.Hkv * nb
+
+
+def check_prefill(inp: PrefillInputs, call, blocks=None, tol=OUT_TOL, report=None):
+    """Compare one finished GPU prefill call with the oracle on the query blocks ``blocks``
+    (flat ids unit * nb + i; all when None).  Selections must match exactly except where the
+    oracle's boundary gap on S[i][j < i] is below GAP_EXCUSE (counted; the oracle then runs
+    on the GPU's selection)."""
+    c = inp.cfg
+    G, nb, blk = c.G, c.nb, c.blk
+    k = call.p.k
+    allb = np.arange(c.B * c.Hkv * nb) if blocks is None else np.asarray(blocks, np.int64)
+    ref = oracle_prefill(inp, k=k, blocks=None if blocks is None else allb.astype(np.int32),
+                         scale=float(call.p.scale))
+    gout = call.out.cpu().numpy()
+    glse = call.lse.cpu().numpy()
+    S = inp.S.cpu().numpy().astype(np.float32)
+    excused = []
+    if k > 0:
+        gsel = call.sel.cpu().numpy()
+        for x in allb:
+            u, i = divmod(int(x), nb)
+            b, kv = divmod(u, c.Hkv)
+            if np.array_equal(gsel[b, kv, i], ref.sel[b, kv, i]):
+                continue
+            gap = boundary_gap(S[b, kv, i, :i].astype(np.float64), min(k, i))
+            assert gap < GAP_EXCUSE, (
+                f"block {x}: selection differs (gpu {gsel[b, kv, i].tolist()} vs oracle "
+                f"{ref.sel[b, kv, i].tolist()}) with boundary gap {gap:.3g}")
+            excused.append(int(x))
+        if excused:
+            forced = np.ascontiguousarray(gsel.astype(np.int32))
+            ref2 = oracle_prefill(inp, k=k, blocks=np.array(excused, np.int32), forced_sel=forced,
+                                  scale=float(call.p.scale))
+            for x in excused:
+                u, i = divmod(x, nb)
+                b, kv = divmod(u, c.Hkv)
+                hs, ts = slice(kv * G, (kv + 1) * G), slice(i * blk, (i + 1) * blk)
+                ref.out[b, hs, ts] = ref2.out[b, hs, ts]
+                ref.lse[b, hs, ts] = ref2.lse[b, hs, ts]
+    err_out = err_lse = 0.0
+    for x in allb:
+        u, i = divmod(int(x), nb)
+        b, kv = divmod(u, c.Hkv)
+        hs, ts = slice(kv * G, (kv + 1) * G), slice(i * blk, (i + 1) * blk)
+        err_out = max(err_out, float(np.abs(gout[b, hs, ts] - ref.out[b, hs, ts]).max()))
+        err_lse = max(err_lse, float(np.abs(glse[b, hs, ts] - ref.lse[b, hs, ts]).max()))
+    stats = dict(blocks=len(allb), excused=len(excused), max_abs_out=err_out,
+                 max_abs_lse=err_lse)
+    if report is not None:
+        report.update(stats)
+    assert err_out <= tol and err_lse <= tol, stats
+    return stats

@@ -79,15 +79,15 @@ struct PrefillSelectLaunch {
 };
 
 struct PrefillLaunch {
-    const uint16_t* q;
-    const uint16_t* k;
-    const uint16_t* v;
+    const uint16_t* q;        // [B][Hq][T][d]
+    const uint16_t* k;        // [B][Hkv][T][d]
+    const uint16_t* v;        // [B][Hkv][T][d]
     int B, Hq, Hkv, d, T, blk, ksel;
-    const int32_t* sel;       // [B*Hkv][nb][ksel]
+    const int32_t* sel;       // [B*Hkv][nb][ksel] ascending, -1 padded (null when ksel == 0)
     const float* gamma;       // [B*Hkv][nb][ksel] or null
     float sigma;
-    float* out;
-    float* lse;
+    float* out;               // [B][Hq][T][d]
+    float* lse;               // [B][Hq][T] or null
 };
 
 hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s);
