@@ -55,277 +55,353 @@ hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s) {
 
 // ---- block-sparse forward ------------------------------------------------------------------
 //
-// Workgroup: 4 waves, wave w owns query head 4*hg + w of the KV group and the 64 rows of query
-// block i.  All products use v_mfma_f32_32x32x16_bf16 (A: 32x16, lane l holds row l%32,
-// k = 8*(l/32)..+7; B: 16x32, lane l holds column l%32, same k; D: 32x32, lane l holds
-// column l%32, rows 8*i + 4*(l/32) + j in register 4*i + j).
+// Workgroup: 4 waves for one (unit, query block i, row half rh, group of up to 4 heads); wave w
+// owns query head 4*hg + w and the 32 query rows 32*rh .. 32*rh + 31 of block i.  Two
+// workgroups share a CU (at most 256 registers per lane each), so the matrix work of one and
+// the softmax of the other overlap on every SIMD.  All products are
+// v_mfma_f32_32x32x16_bf16 (A: 32x16, lane l holds row l%32, k = 8*(l/32)..+7; B: 16x32, lane
+// l holds column l%32, same k; D: 32x32, lane l holds column l%32, rows 8*i + 4*(l/32) + j in
+// register 4*i + j).
 //
-//   S^T = K * Q^T   64 keys x 64 queries per wave: a lane owns whole query columns, so the
-//                   running max / sum of a query row live in one lane pair (l, l ^ 32).
-//   O^T += V^T P^T  128 dims x 64 queries: the B operand (P^T) is the S^T accumulator of the
-//                   same lane, converted to bf16; the A operand (V^T) comes from row-major V
-//                   in LDS through the transposing read ds_read_b64_tr_b16.
+//   S^T = K * Q^T   64 keys x 32 queries: a lane owns one query column, so the running max and
+//                   sum of a query row live in the lane pair (l, l ^ 32).
+//   O^T += V^T P^T  128 dims x 32 queries: the B operand (P^T) is the S^T accumulator of the
+//                   same lane rounded to bf16; the A operand (V^T) is read from row-major V in
+//                   LDS with the transposing ds_read_b64_tr_b16.
 //
-// K and V blocks (64 rows x 256 B) are copied straight into LDS (global_load_lds_dwordx4),
-// double buffered: the next block's copy is in flight while the current one is consumed.  The
-// 16-byte unit u of row r is stored at unit u ^ swz(r) so that both the K reads (8 rows per
-// bank sweep) and the transposing V reads (4 rows x 32 B) are free of bank conflicts.
+// LDS tile of one 64 x 128 block (K or V): four sub-tiles of 32 dims, each 64 rows x 64 B, so
+// every operand address is one per-lane base plus a compile-time offset.  Within a 64-byte
+// sub-row the 16-byte unit u of row r is stored at u ^ swz(r): for K, ((r >> 1) & 3) ^
+// ((r >> 3) & 1) puts the 16 rows that one 128-bit read serves per cycle (and each half of
+// them) on distinct banks; for V, (r & 2) keeps the 4 rows x 32 B of a transposing read on
+// distinct banks.  Blocks are double buffered: the next block's global loads are issued into
+// registers at the top of an iteration and written to the other LDS buffer at its end.  (A
+// direct global-to-LDS copy would save those registers, but the compiler then cannot count
+// LDS reads precisely and makes every operand read wait for all earlier ones.)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kPD = 128;                     // head dim
 constexpr int kPBlk = 64;                    // block rows
-constexpr int kPRow = kPD * 2;               // bytes per K / V row
-constexpr int kPTile = kPBlk * kPRow;        // bytes per K or V block
+constexpr int kPSub = 64 * 64;               // bytes per 32-dim sub-tile (64 rows x 64 B)
+constexpr int kPTile = 4 * kPSub;            // bytes per K or V block
+constexpr int kRing = 128;                   // entries of the chosen-block ring (power of 2)
 constexpr int kPLds = 4 * kPTile;            // K0 K1 V0 V1
+constexpr int kPLdsAll = kPLds + kRing * 8;  // + the ring (block ids, gates)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;         // log2 units a stale running max may lag
 
-__device__ __forceinline__ int swz_k(int r) { return r & 7; }
-__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_v(int r) { return r & 2; }
 
-// Copy one block (64 rows x 128 bf16, rows contiguous) into an LDS tile.  Each wave issues 4
-// instructions of 64 x 16 B; slot s of the tile is row s/16, stored unit s%16.
-template <bool IS_V>
-__device__ __forceinline__ void copy_block(const uint16_t* src, char* tile, int w, int lane) {
+// Copy one block (64 rows x 128 bf16, rows contiguous in global memory) into an LDS tile.
+// Slot s (16 B) of the tile is sub-tile s / 256, row (s / 4) % 64, stored unit s % 4.  Wave w
+// issues instruction c for slots (4 c + w) * 64 + lane, i.e. sub-tile c, row 16 w + lane / 4,
+// so a lane's source offset is the same for all four instructions but for c * 64 bytes.
+struct CopyOffsets { uint32_t c[4]; };   // per-lane source byte offsets, one per chunk
+
+// A block (64 rows x 128 bf16, rows contiguous in global memory) is copied through registers:
+// each thread moves four 16-byte chunks of K and four of V.  Chunk c of wave w is tile slot
+// s = (4 c + w) * 64 + lane: sub-tile c, row 16 w + lane / 4, stored unit lane % 4, so the
+// LDS writes of one instruction are 1 KB contiguous and a lane's source offsets differ only by
+// c * 64 bytes.
+__device__ __forceinline__ CopyOffsets copy_offsets(bool is_v, int w, int lane) {
+    const int r = 16 * w + (lane >> 2);
+    const int lu = (lane & 3) ^ (is_v ? swz_v(r) : swz_k(r));
+    CopyOffsets o;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int slot0 = (c * 4 + w) * 64;
-        const int slot = slot0 + lane;
-        const int r = slot >> 4;
-        const int lu = (slot & 15) ^ (IS_V ? swz_v(r) : swz_k(r));
-        __builtin_amdgcn_global_load_lds(src + r * kPD + lu * 8, (lds_void*)(tile + slot0 * 16),
-                                         16, 0, 0);
-    }
+    for (int c = 0; c < 4; ++c) o.c[c] = (uint32_t)(r * kPD * 2 + c * 64 + lu * 16);
+    return o;
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Staged copy of one block: eight 16-byte chunks per thread, held in named registers.
+#define TCS_STAGE_LOAD(kb, vb)                                                                  \
+    do {                                                                                        \
+        const char* kc_ = reinterpret_cast<const char*>(kb);                                    \
+        const char* vc_ = reinterpret_cast<const char*>(vb);                                    \
+        sk0 = *reinterpret_cast<const uint4*>(kc_ + gk.c[0]);                                   \
+        sk1 = *reinterpret_cast<const uint4*>(kc_ + gk.c[1]);                                   \
+        sk2 = *reinterpret_cast<const uint4*>(kc_ + gk.c[2]);                                   \
+        sk3 = *reinterpret_cast<const uint4*>(kc_ + gk.c[3]);                                   \
+        sv0 = *reinterpret_cast<const uint4*>(vc_ + gv.c[0]);                                   \
+        sv1 = *reinterpret_cast<const uint4*>(vc_ + gv.c[1]);                                   \
+        sv2 = *reinterpret_cast<const uint4*>(vc_ + gv.c[2]);                                   \
+        sv3 = *reinterpret_cast<const uint4*>(vc_ + gv.c[3]);                                   \
+    } while (0)
+#define TCS_STAGE_STORE(ktile, vtile)                                                           \
+    do {                                                                                        \
+        char* kd_ = (ktile) + w * 1024 + lane * 16;                                             \
+        char* vd_ = (vtile) + w * 1024 + lane * 16;                                             \
+        *reinterpret_cast<uint4*>(kd_ + 0 * 4096) = sk0;                                        \
+        *reinterpret_cast<uint4*>(kd_ + 1 * 4096) = sk1;                                        \
+        *reinterpret_cast<uint4*>(kd_ + 2 * 4096) = sk2;                                        \
+        *reinterpret_cast<uint4*>(kd_ + 3 * 4096) = sk3;                                        \
+        *reinterpret_cast<uint4*>(vd_ + 0 * 4096) = sv0;                                        \
+        *reinterpret_cast<uint4*>(vd_ + 1 * 4096) = sv1;                                        \
+        *reinterpret_cast<uint4*>(vd_ + 2 * 4096) = sv2;                                        \
+        *reinterpret_cast<uint4*>(vd_ + 3 * 4096) = sv3;                                        \
+    } while (0)
 
-__global__ void __launch_bounds__(256) prefill_fwd_kernel(PrefillLaunch a) {
+// max / sum of a value over the lane pair (l, l ^ 32), identical in both lanes: one
+// v_permlane32_swap exchanges the two 32-lane halves.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// V^T operand of (dim tile dt, key step st): two transposing reads of 4 rows each.
+__device__ __forceinline__ bf16x8 v_operand(const char* vt, int dt, int st) {
+    const char* ap = vt + dt * kPSub + st * 1024;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)ap);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ap + 512));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// S^T (keys NX * 32 x 32 queries) = K Q^T from the K tile kt.  Eight operand reads ahead,
+// then one read per product, so each product waits only for its own operand.
+template <int NX>
+__device__ __forceinline__ void qk_product(const char* kt, int koff0, int koff1,
+                                           const bf16x8 (&qf)[8], f32x16 (&s)[2]) {
+    bf16x8 kr[8][NX];
+#pragma unroll
+    for (int kd = 0; kd < 8; ++kd)
+#pragma unroll
+        for (int x = 0; x < NX; ++x)
+            kr[kd][x] = *reinterpret_cast<const bf16x8*>(
+                kt + (kd >> 1) * kPSub + ((kd & 1) ? koff1 : koff0) + x * 32 * 64);
+#pragma unroll
+    for (int kd = 0; kd < 8; ++kd)
+#pragma unroll
+        for (int x = 0; x < NX; ++x)
+            s[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kd][x], qf[kd], s[x], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int x = 0; x < 8 * NX - 8; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+}
+
+__global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
     extern __shared__ __align__(16) char lds[];
     const int G = a.Hq / a.Hkv;
     const int nb = a.T / kPBlk;
     const int nhg = (G + 3) >> 2;
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous range of
-    // (unit, head group, block) so one KV head's blocks stay in one L2.  Within a range the
-    // query blocks run from last to first, the longest (most earlier blocks) first.
+    // (unit, head group, block, row half) so one KV head's blocks stay in one L2.  Within a
+    // range the query blocks run from last to first, the longest (most earlier blocks) first,
+    // and the two row halves of a block run side by side, reading the same K/V blocks.
     int bid = blockIdx.x;
     const int W = gridDim.x;
     if ((W & 7) == 0) bid = (bid & 7) * (W >> 3) + (bid >> 3);
-    const int i = nb - 1 - bid % nb;
-    const int rest = bid / nb;
+    const int rh = bid & 1;
+    const int i = nb - 1 - (bid >> 1) % nb;
+    const int rest = (bid >> 1) / nb;
     const int hg = rest % nhg;
     const int unit = rest / nhg;
     const int b = unit / a.Hkv, kv = unit % a.Hkv;
 
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int lane = threadIdx.x & 63;
     const int h = lane >> 5, c32 = lane & 31;
     const int head = hg * 4 + w;
     const bool active = head < G;
 
     const uint16_t* kbase = a.k + (size_t)unit * a.T * kPD;
     const uint16_t* vbase = a.v + (size_t)unit * a.T * kPD;
-    // LDS: K tiles at [0, 2 kPTile), V tiles at [2 kPTile, 4 kPTile).
+    // LDS: K tiles at [0, 2 kPTile), V tiles at [2 kPTile, 4 kPTile), then the ring.
 
     const int ke = a.ksel > 0 ? min(a.ksel, i) : 0;
     const int32_t* selrow = a.sel ? a.sel + ((size_t)unit * nb + i) * a.ksel : nullptr;
     const float* grow = a.gamma ? a.gamma + ((size_t)unit * nb + i) * a.ksel : nullptr;
 
-    // Block 0 of the list is the diagonal block; blocks 1..ke are the chosen earlier ones.
-    copy_block<false>(kbase + (size_t)i * kPBlk * kPD, lds, w, lane);
-    copy_block<true>(vbase + (size_t)i * kPBlk * kPD, lds + 2 * kPTile, w, lane);
+    // The chosen blocks and their gates pass through a ring of kRing entries in LDS, refilled
+    // kRing / 2 entries at a time well ahead of use.
+    int* ring_j = reinterpret_cast<int*>(lds + kPLds);
+    float* ring_g = reinterpret_cast<float*>(lds + kPLds + kRing * 4);
+    auto fill_ring = [&](int x0) {   // entries x0 .. x0 + kRing/2 - 1 (those < ke)
+        const int x = x0 + threadIdx.x;
+        if (threadIdx.x < kRing / 2 && x < ke) {
+            ring_j[x & (kRing - 1)] = min(max(selrow[x], 0), i - 1);
+            ring_g[x & (kRing - 1)] = grow ? grow[x] * kLog2e : 0.f;
+        }
+    };
+    fill_ring(0);
+    fill_ring(kRing / 2);
 
-    // Q^T operand: q[qt][kd] = Q[32 qt + c32][16 kd + 8 h .. +7] of this wave's head.
-    const size_t qrow0 = ((size_t)(b * a.Hq + kv * G + (active ? head : 0)) * a.T + (size_t)i * kPBlk);
-    bf16x8 qf[2][8];
+    // Block 0 of the list is the diagonal block; blocks 1..ke are the chosen earlier ones.
+    const CopyOffsets gk = copy_offsets(false, w, lane), gv = copy_offsets(true, w, lane);
+    uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
+    TCS_STAGE_LOAD(kbase + (size_t)i * kPBlk * kPD, vbase + (size_t)i * kPBlk * kPD);
+
+    // Q^T operand: qf[kd] = Q[32 rh + c32][16 kd + 8 h .. +7] of this wave's head.
+    const size_t qrow = ((size_t)(b * a.Hq + kv * G + (active ? head : 0)) * a.T +
+                         (size_t)i * kPBlk + 32 * rh + c32);
+    bf16x8 qf[8];
     {
-        const uint16_t* qp = a.q + qrow0 * kPD;
+        const uint16_t* qp = a.q + qrow * kPD + 8 * h;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int kd = 0; kd < 8; ++kd)
-                qf[qt][kd] = *reinterpret_cast<const bf16x8*>(qp + (32 * qt + c32) * kPD + 16 * kd + 8 * h);
+        for (int kd = 0; kd < 8; ++kd) qf[kd] = *reinterpret_cast<const bf16x8*>(qp + 16 * kd);
     }
+    TCS_STAGE_STORE(lds, lds + 2 * kPTile);
+
+    // Per-lane LDS offsets (bytes) of the operand reads; everything else is an immediate.
+    //   K: row r = 32 x + c32, d = 16 kd + 8 h: sub-tile kd / 2, unit (2 (kd & 1) + h) ^ swz.
+    const int koff0 = c32 * 64 + (((0 + h) ^ swz_k(c32)) << 4);
+    const int koff1 = c32 * 64 + (((2 + h) ^ swz_k(c32)) << 4);
+    //   V (transposing read, 16-lane group g, lane L = 4 rr + cc of the group): row
+    //   16 st + 8 rho + 4 h + rr, sub-tile dt, unit (2 (g & 1) + (cc >> 1)) ^ swz, half cc & 1.
+    const int g = lane >> 4, L = lane & 15, rr = L >> 2, cc = L & 3;
+    const int voff = (4 * h + rr) * 64 + (((2 * (g & 1) + (cc >> 1)) ^ swz_v(rr)) << 4) + ((cc & 1) << 3);
 
     const float cs = a.sigma * kLog2e;
-    f32x16 o[4][2];
+    f32x16 o[4];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) o[dt][qt] = f32x16{};
-    float m[2] = {0.f, 0.f}, l[2] = {0.f, 0.f};
-
-    int jn = 0;          // block of list entry t + 1
-    float gn = 0.f;      // its gate (log2 units)
-    if (ke > 0) {
-        jn = min(max(selrow[0], 0), i - 1);
-        gn = grow ? grow[0] * kLog2e : 0.f;
-    }
-    float gcur = 0.f;
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    float m = 0.f, l = 0.f;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
     for (int t = 0; t <= ke; ++t) {
-        wait_vmem();
+        // Block t is in buffer t & 1; every wave is done with buffer (t + 1) & 1.
         __syncthreads();
         const int buf = t & 1;
+        float bias = 0.f;
+        if (t > 0)
+            bias = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(ring_g[(t - 1) & (kRing - 1)])));
         if (t < ke) {
-            copy_block<false>(kbase + (size_t)jn * kPBlk * kPD, lds + (buf ^ 1) * kPTile, w, lane);
-            copy_block<true>(vbase + (size_t)jn * kPBlk * kPD, lds + (2 + (buf ^ 1)) * kPTile, w, lane);
+            const int jn = __builtin_amdgcn_readfirstlane(ring_j[t & (kRing - 1)]);
+            TCS_STAGE_LOAD(kbase + (size_t)jn * kPBlk * kPD, vbase + (size_t)jn * kPBlk * kPD);
         }
-        const float bias = gcur;
-        gcur = gn;
-        if (t + 1 < ke) {
-            jn = min(max(selrow[t + 1], 0), i - 1);
-            gn = grow ? grow[t + 1] * kLog2e : 0.f;
-        }
-        if (!active) continue;
+        // Iteration t reads entries t - 1 and t.  Past this iteration's barrier every entry
+        // below t is dead, so at t = 1 + n kRing/2 (n >= 1) the slots of entries
+        // t - 1 - kRing/2 .. t - 2 take entries t - 1 + kRing/2 .. t - 2 + kRing, first read
+        // kRing/2 - 1 iterations later.
+        if (t > kRing / 2 && ((t - 1) & (kRing / 2 - 1)) == 0 && t - 1 + kRing / 2 < ke)
+            fill_ring(t - 1 + kRing / 2);
+        if (active) {
+            // On the diagonal block, rows of the first half see only keys 0..31.
+            const bool half = (t == 0) && rh == 0;
+            const char* kt = lds + buf * kPTile;
+            const char* vt = lds + (2 + buf) * kPTile + voff;
 
-        // ---- S^T = K Q^T ----
-        const char* kt = lds + buf * kPTile;
-        f32x16 s[2][2];
+            // ---- S^T = K Q^T ----
+            f32x16 s[2];
+            s[0] = s[1] = f32x16{};
+            if (half) qk_product<1>(kt, koff0, koff1, qf, s);
+            else qk_product<2>(kt, koff0, koff1, qf, s);
+            // V operands are read now; their latency hides under the softmax.
+            bf16x8 va[4][4];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) s[x][0] = s[x][1] = f32x16{};
+            for (int st = 0; st < 4; ++st) {
+                if (half && st >= 2) break;
 #pragma unroll
-        for (int kd = 0; kd < 8; ++kd) {
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int r = 32 * x + c32;
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-                    kt + r * kPRow + (((2 * kd + h) ^ swz_k(r)) << 4));
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
-                    s[x][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qt][kd], s[x][qt], 0, 0, 0);
+                for (int dt = 0; dt < 4; ++dt) va[st][dt] = v_operand(vt, dt, st);
             }
-        }
 
-        // ---- online softmax (log2 domain) ----
-        if (t == 0) {   // diagonal block: key row r sees query column c only if r <= c
+            // ---- online softmax (log2 domain) ----
+            if (t == 0) {   // diagonal block: key row r sees query row q only if r <= q
+                const int q = 32 * rh + c32;
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
+                for (int x = 0; x < 2; ++x)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = 32 * x + 8 * (e >> 2) + 4 * h + (e & 3);
-                        if (key > 32 * qt + c32) s[x][qt][e] = -INFINITY;
+                        if (key > q) s[x][e] = -INFINITY;
                     }
-        }
-        float mb[2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            float mx = s[0][qt][0];
+            }
+            float mx = s[0][0];
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[x][qt][e]);
-            mx = fmaxf(mx, xor32(mx));
-            mb[qt] = mx * cs + bias;
-        }
-        if (t == 0) {
-            m[0] = mb[0];
-            m[1] = mb[1];
-        } else {
-            const bool need = (mb[0] > m[0] + kRescaleSlack) || (mb[1] > m[1] + kRescaleSlack);
-            if (__builtin_amdgcn_ballot_w64(need)) {
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[x][e]);
+            mx = pair_max(mx);
+            const float mb = mx * cs + bias;
+            if (t == 0) {
+                m = mb;
+            } else if (__builtin_amdgcn_ballot_w64(mb > m + kRescaleSlack)) {
+                const float mn = fmaxf(m, mb);
+                const float al = __builtin_amdgcn_exp2f(m - mn);
+                m = mn;
+                l *= al;
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    const float mn = fmaxf(m[qt], mb[qt]);
-                    const float al = __builtin_amdgcn_exp2f(m[qt] - mn);
-                    m[qt] = mn;
-                    l[qt] *= al;
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= al;
-                }
+                for (int dt = 0; dt < 4; ++dt) o[dt] *= al;
             }
-        }
-        bf16x8 p[4][2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const float off = bias - m[qt];
+            const float off = bias - m;
+            bf16x8 p[4];
             float sum = 0.f;
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+            for (int st = 0; st < 4; ++st) {
+                bf16x8 pv;
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    bf16x8 pv;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float pe = __builtin_amdgcn_exp2f(s[x][qt][8 * hf + e] * cs + off);
-                        sum += pe;
-                        pv[e] = (__bf16)pe;
-                    }
-                    p[2 * x + hf][qt] = pv;
-                }
-            l[qt] += sum;
-        }
+                for (int e = 0; e < 8; ++e)
+                    pv[e] = (__bf16)__builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + e] * cs + off);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), ones, sum, false);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, sum, false);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, sum, false);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, sum, false);
+                p[st] = pv;
+            }
+            l += sum;
 
-        // ---- O^T += V^T P^T ----
-        const char* vt = lds + (2 + buf) * kPTile;
-        const int g = lane >> 4, L = lane & 15;
-        const int rr = L >> 2, cc = L & 3;
+            // ---- O^T += V^T P^T ----
+            const int nst = half ? 2 : 4;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+            for (int st = 0; st < 4; ++st) {
+                if (st >= nst) break;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                s16x4 part[2];
-#pragma unroll
-                for (int rho = 0; rho < 2; ++rho) {
-                    const int r = 16 * st + 8 * rho + 4 * h + rr;
-                    const int lu = 4 * dt + 2 * (g & 1) + (cc >> 1);
-                    const char* ap = vt + r * kPRow + ((lu ^ swz_v(r)) << 4) + ((cc & 1) << 3);
-                    part[rho] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)ap);
+                for (int dt = 0; dt < 4; ++dt) {
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st][dt], p[st], o[dt], 0, 0, 0);
                 }
-                const s16x8 va16 = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                const bf16x8 va = __builtin_bit_cast(bf16x8, va16);
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
-                    o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[st][qt], o[dt][qt], 0, 0, 0);
             }
         }
+        if (t < ke) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
     }
     if (!active) return;
 
     // ---- epilogue: O = O^T / l, lse = m + log2 l (back to natural log) ----
+    const float lt = pair_sum(l);
+    const float inv = 1.f / lt;
+    float* op = a.out + qrow * kPD;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const float lt = l[qt] + xor32(l[qt]);
-        const float inv = 1.f / lt;
-        const size_t row = qrow0 + 32 * qt + c32;
-        float* op = a.out + row * kPD;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                float4 v;
-                v.x = o[dt][qt][4 * e4 + 0] * inv;
-                v.y = o[dt][qt][4 * e4 + 1] * inv;
-                v.z = o[dt][qt][4 * e4 + 2] * inv;
-                v.w = o[dt][qt][4 * e4 + 3] * inv;
-                *reinterpret_cast<float4*>(op + 32 * dt + 8 * e4 + 4 * h) = v;
-            }
-        if (a.lse && h == 0) a.lse[row] = (m[qt] + log2f(lt)) * kLn2;
-    }
+        for (int e4 = 0; e4 < 4; ++e4) {
+            float4 v;
+            v.x = o[dt][4 * e4 + 0] * inv;
+            v.y = o[dt][4 * e4 + 1] * inv;
+            v.z = o[dt][4 * e4 + 2] * inv;
+            v.w = o[dt][4 * e4 + 3] * inv;
+            *reinterpret_cast<float4*>(op + 32 * dt + 8 * e4 + 4 * h) = v;
+        }
+    if (a.lse && h == 0) a.lse[qrow] = (m + log2f(lt)) * kLn2;
 }
 
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s) {
     if (a.d != kPD || a.blk != kPBlk || a.T % kPBlk) return hipErrorNotSupported;
     const int G = a.Hq / a.Hkv;
-    const long long W = (long long)a.B * a.Hkv * (a.T / kPBlk) * ((G + 3) / 4);
+    const long long W = 2LL * a.B * a.Hkv * (a.T / kPBlk) * ((G + 3) / 4);
     if (W <= 0) return hipSuccess;
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)prefill_fwd_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kPLdsAll);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    prefill_fwd_kernel<<<(unsigned)W, 256, kPLds, s>>>(a);
+    prefill_fwd_kernel<<<(unsigned)W, 256, kPLdsAll, s>>>(a);
     return hipGetLastError();
 }
 
