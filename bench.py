@@ -1,14 +1,19 @@
 #!/usr/bin/env python3
-"""Benchmark of the chunk-sparse decode path on one MI355X.
+"""Benchmark of the chunk-sparse attention path on one MI355X.
 
-One step = one sparse_attn_decode call over the whole batch (every query head of one layer
-at one decode step) on the Llama-3.1-8B-shaped 128K-token workload: B=16, Hq=32, Hkv=8, d=128,
-C=128, g=4 gists per chunk, k=16 chunks + the current chunk, SAS gate on, paged KV.
-Inputs are resident in HBM before the timed region; steps rotate over R independent
-instances (>= 1 GiB of algorithmic bytes in the rotation) so that the 256 MB last-level
-cache cannot serve them.  Prints one JSON line.
+Default workload (decode): one step = one sparse_attn_decode call over the whole batch (every
+query head of one layer at one decode step) on the Llama-3.1-8B-shaped 128K-token workload:
+B=16, Hq=32, Hkv=8, d=128, C=128, g=4 gists per chunk, k=16 chunks + the current chunk, SAS
+gate on, paged KV.  Inputs are resident in HBM before the timed region; steps rotate over R
+independent instances (>= 1 GiB of algorithmic bytes in the rotation) so that the 256 MB
+last-level cache cannot serve them.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--instances R] [--no-cpu-baseline]
+--workload sas_prefill_16k: one step = one sparse_attn_prefill call (block selection + the
+MFMA block-sparse causal forward) on B=1, Hq=32, Hkv=8, d=128, T=16384, 64-token blocks,
+top-16 earlier blocks + the diagonal block, SAS gate; reported as algorithmic TFLOP/s.
+
+    python bench.py [--steps K] [--warmup W] [--instances R] [--workload NAME]
+                    [--no-cpu-baseline] [--cpu-seconds S]
 """
 import argparse
 import json
@@ -17,7 +22,9 @@ import sys
 import time
 
 METRIC = "decode attn calls/s and effective HBM GB/s (% of peak) at 128K ctx, k=16"
+PREFILL_METRIC = "SAS block-sparse causal prefill forward, algorithmic TFLOP/s at 16K tokens, k=16"
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, vendor figure
 
 
 def decode_bytes(cfg, k=None):
@@ -52,6 +59,28 @@ def gist_kernel_bytes(cfg):
     return units * cfg.H * cfg.g * cfg.d * 2 * 2 + cfg.B * cfg.Hq * cfg.d * 2
 
 
+def prefill_pairs(cfg):
+    """Attended (query, key) pairs of one prefill call: per query head, every row of block i
+    sees min(k, i) whole earlier blocks plus the causal part of its own block."""
+    nb, blk = cfg.nb, cfg.blk
+    per_head = sum(min(cfg.k, i) for i in range(nb)) * blk * blk + nb * blk * (blk + 1) // 2
+    return cfg.B * cfg.Hq * per_head
+
+
+def prefill_flops(cfg):
+    """Algorithmic FLOPs: 2 d for q.k and 2 d for p.v per attended pair."""
+    return 4 * cfg.d * prefill_pairs(cfg)
+
+
+def prefill_bytes(cfg):
+    """Algorithmic bytes of one prefill call: q, K and V (bf16), S (fp32) read once; out (fp32),
+    lse (fp32) and the selection (int32) written once."""
+    nb = cfg.nb
+    return (cfg.B * cfg.Hq * cfg.T * cfg.d * 2 + 2 * cfg.B * cfg.Hkv * cfg.T * cfg.d * 2
+            + cfg.B * cfg.Hkv * nb * nb * 4 + cfg.B * cfg.Hq * cfg.T * (cfg.d + 1) * 4
+            + cfg.B * cfg.Hkv * nb * cfg.k * 4)
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -78,6 +107,7 @@ def cpu_baseline(inp, budget_s):
                 levels=c.levels, J=c.J, k2=c.k2, **host)
     units = c.B * c.Hkv
     probe = list(range(0, units, max(1, units // 8)))[:8]
+    oracle.decode(units=probe[:1], **args)          # untimed: library load, first touch
     t0 = time.perf_counter()
     oracle.decode(units=probe, **args)
     per_unit = (time.perf_counter() - t0) / len(probe)
@@ -87,7 +117,7 @@ def cpu_baseline(inp, budget_s):
         while True:
             oracle.decode(**args)
             n += 1
-            if time.perf_counter() - t0 >= budget_s * 0.5 or n >= 50:
+            if time.perf_counter() - t0 >= budget_s:
                 break
         dt = time.perf_counter() - t0
         value, sample = n / dt, f"{n} full call(s) of instance 0 ({units} units each)"
@@ -103,6 +133,39 @@ def cpu_baseline(inp, budget_s):
             "sample": sample, "seconds": round(dt, 3), "cpu": cpu_model()}
 
 
+def cpu_baseline_prefill(inp, budget_s):
+    """Time the fp64 CPU oracle (as it stands) on a seeded sample of query blocks of instance 0,
+    scaled to the metric's unit (algorithmic TFLOP/s of whole calls)."""
+    import numpy as np
+    import oracle
+    from top_chunk_sparse_amd.synth import bf16_bits
+    c = inp.cfg
+    args = dict(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, T=c.T, blk=c.blk, k=c.k, gate=c.gate,
+                q=bf16_bits(inp.q), k_=bf16_bits(inp.k), v=bf16_bits(inp.v),
+                S=inp.S.cpu().numpy().astype(np.float32))
+    nblocks = c.B * c.Hkv * c.nb
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(nblocks).astype(np.int32)
+    # pairs attended by the sampled blocks (block i of any unit: G heads x rows)
+    def pairs(ids):
+        i = ids % c.nb
+        return int(sum(c.G * (np.minimum(c.k, i) * c.blk * c.blk + c.blk * (c.blk + 1) // 2)))
+    oracle.prefill(blocks=order[:1], **args)       # untimed: library load, first touch
+    n, t0 = 8, time.perf_counter()
+    oracle.prefill(blocks=order[:n], **args)
+    dt = time.perf_counter() - t0
+    while dt < budget_s * 0.5 and n < nblocks:    # grow the timed sample to ~budget
+        n = min(nblocks, int(n * max(2.0, budget_s / max(dt, 1e-3) * 0.9)))
+        t0 = time.perf_counter()
+        oracle.prefill(blocks=order[:n], **args)
+        dt = time.perf_counter() - t0
+    flops = 4 * c.d * pairs(order[:n])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "sample": f"{n} of {nblocks} query blocks (all heads of each) of "
+            f"instance 0, seeded random choice", "seconds": round(dt, 3), "cpu": cpu_model(),
+            "calls_per_s": round(flops / dt / prefill_flops(c), 6)}
+
+
 def load_traffic(kernel_name, workload):
     """HBM traffic per launch from committed rocprofv3 counter runs, only if the kernel
     sources are unchanged since the counters were taken."""
@@ -112,11 +175,94 @@ def load_traffic(kernel_name, workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(here, "top_chunk_sparse_amd", "csrc", rec.get("source", "decode.hip"))
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if sha != rec.get("source_sha256"):
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        h.update(open(os.path.join(here, f), "rb").read())
+    if h.hexdigest() != rec.get("sources_sha256"):
         return None
     return rec.get("bytes_per_launch")
+
+
+def run_prefill(args, torch, configs, ops):
+    from top_chunk_sparse_amd.synth import make_prefill
+    import ctypes
+    cfg = configs.PREFILL_CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    R = max(1, min(args.instances, 2))
+    print(f"# generating {R} instance(s) of {cfg.name}", file=sys.stderr, flush=True)
+    insts = [make_prefill(cfg, configs.seed_for(cfg.name, r), device=dev) for r in range(R)]
+    calls = [ops.PrefillCall(inp) for inp in insts]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        calls[i % R]()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        calls[i % R]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # per-kernel durations: back-to-back calls with events between the two kernels
+    evs = []
+    for _ in range(args.steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for e in row:
+            e.record(stream)
+        evs.append(row)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        arr = (ctypes.c_void_p * 3)(*[e.cuda_event for e in evs[i]])
+        calls[i % R](events=arr)
+    torch.cuda.synchronize()
+    stage_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+                for j in range(2)]
+    print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
+    flops = prefill_flops(cfg)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    fwd_ms = stage_ms[1]
+    ach = flops / (fwd_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": "prefill_fwd_kernel", "achieved": round(ach, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": load_traffic("prefill_fwd_kernel", cfg.name),
+            "algorithmic_flops": flops, "avg_ms": round(fwd_ms, 5)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_prefill(insts[0], args.cpu_seconds)
+    rec = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
+                   "T": cfg.T, "blk": cfg.blk, "k": cfg.k, "gate": "sas" if cfg.gate else "none",
+                   "inputs": "bf16", "accumulation": "fp32", "instances_rotated": R},
+        "calls_per_s": round(args.steps / wall, 2),
+        "algorithmic_flops_per_call": flops,
+        "attended_pairs_per_call": prefill_pairs(cfg),
+        "algorithmic_bytes_per_call": prefill_bytes(cfg),
+        "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 5),
+        "stage_ms": [round(x, 5) for x in stage_ms],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -127,7 +273,7 @@ def main():
     ap.add_argument("--instances", type=int, default=3)
     ap.add_argument("--workload", default="llama31_8b_decode_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -141,6 +287,16 @@ def main():
     from top_chunk_sparse_amd import configs, ops
     from top_chunk_sparse_amd.synth import make_decode
 
+    torch.cuda.set_device(0)
+    if args.copy_probe:   # a copy of known size, to scale the HBM byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.workload in configs.PREFILL_CONFIGS:
+        return run_prefill(args, torch, configs, ops)
     cfg = configs.DECODE_CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -150,14 +306,6 @@ def main():
     calls = [ops.DecodeCall(inp, with_scores=False) for inp in insts]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-
-    if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     for i in range(args.warmup):
         calls[i % R]()
