@@ -31,6 +31,10 @@ constexpr int kMaxSliceRows = 1024;   // rows one gist workgroup holds logits fo
 #define TCS_TARGET_WORKGROUPS 1024
 #endif
 constexpr int kTargetWorkgroups = TCS_TARGET_WORKGROUPS;   // grid size the passes aim for
+#ifndef TCS_CHUNK_TARGET_WORKGROUPS
+#define TCS_CHUNK_TARGET_WORKGROUPS 1024
+#endif
+constexpr int kChunkTargetWorkgroups = TCS_CHUNK_TARGET_WORKGROUPS;   // chunk-attention grid
 constexpr int kMinSliceRows = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -112,9 +116,12 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     }
     pl->kslots = ksel;
     // chunk attention: enough workgroups to fill the GPU, one or more chunks each
-    long long cpw = units * (ksel + 1) / kTargetWorkgroups;
+    long long cpw = units * (ksel + 1) / kChunkTargetWorkgroups;
     const long long cpw_max = std::min<long long>(16, kMaxSliceRows / p->C);  // rows held in LDS
-    pl->cpw = (int)std::max<long long>(1, std::min(cpw, cpw_max));
+    // At least two slots per workgroup once there are enough of them: a workgroup's fixed costs
+    // (dispatch, query load, partial write, arrival) then pay for twice the bytes.
+    const long long cpw_min = units * (ksel + 1) >= 512 ? 2 : 1;
+    pl->cpw = (int)std::max<long long>(std::min(cpw_min, cpw_max), std::min(cpw, cpw_max));
     pl->nslots = pl->S1 + pl->S2 + pl->k2e + (ksel + 1 + pl->cpw - 1) / pl->cpw;
     const long long BH = (long long)p->B * p->Hq;
     const long long s1 = p->levels == 2 ? pl->k2e : pl->S1;     // slices of the chunk pass

@@ -35,6 +35,12 @@ constexpr int kMaxSliceRows = 1024;   // rows (gists, or page rows) one workgrou
 #ifndef TCS_V_U
 #define TCS_V_U 4       // row passes per batch of loads in the V phase
 #endif
+#ifndef TCS_CK_U
+#define TCS_CK_U TCS_K_U   // the same, for the chunk kernel's K phase
+#endif
+#ifndef TCS_CV_U
+#define TCS_CV_U TCS_V_U   // the same, for the chunk kernel's V phase
+#endif
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -577,7 +583,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
             for (int jj = 0; jj < nj; ++jj) {
                 if (sm.page[jj] < 0) continue;
                 const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
-                rs.template logits<TCS_K_U>(q2, a.kp + off, sm.rows[jj], a.sigma, sm.bias[jj],
+                rs.template logits<TCS_CK_U>(q2, a.kp + off, sm.rows[jj], a.sigma, sm.bias[jj],
                                             sm.x.lg, jj * a.C);
             }
         }
@@ -591,7 +597,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
         for (int jj = 0; jj < nj; ++jj) {
             if (sm.page[jj] < 0) continue;
             const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
-            rs.template accumulate<TCS_V_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, jj * a.C);
+            rs.template accumulate<TCS_CV_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, jj * a.C);
         }
         __syncthreads();
         rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + wx);
