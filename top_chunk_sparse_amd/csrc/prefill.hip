@@ -277,9 +277,9 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
         // Block t is in buffer t & 1; every wave is done with buffer (t + 1) & 1.
         __syncthreads();
         const int buf = t & 1;
-        float bias = 0.f;
-        if (t > 0)
-            bias = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(ring_g[(t - 1) & (kRing - 1)])));
+        const float bias = t > 0 ? __int_as_float(__builtin_amdgcn_readfirstlane(
+                                       __float_as_int(ring_g[(t - 1) & (kRing - 1)])))
+                                 : 0.f;
         if (t < ke) {
             const int jn = __builtin_amdgcn_readfirstlane(ring_j[t & (kRing - 1)]);
             TCS_STAGE_LOAD(kbase + (size_t)jn * kPBlk * kPD, vbase + (size_t)jn * kPBlk * kPD);
@@ -339,10 +339,8 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
                 for (int dt = 0; dt < 4; ++dt) o[dt] *= al;
             }
             const float off = bias - m;
-            bf16x8 p[4];
             float sum = 0.f;
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            auto p_step = [&](int st) {   // P^T for key step st (bf16) and its row-sum share
                 bf16x8 pv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -351,20 +349,42 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
                 sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, sum, false);
                 sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, sum, false);
                 sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, sum, false);
-                p[st] = pv;
+                return pv;
+            };
+            auto pv_mfma = [&](int st, const bf16x8& pst) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st][dt], pst, o[dt], 0, 0, 0);
+            };
+            // ---- O^T += V^T P^T, the products of one key step overlapping the exponentials of
+            // the next ----
+            if (half) {
+                const bf16x8 p0 = p_step(0);
+                const bf16x8 p1 = p_step(1);
+                pv_mfma(0, p0);
+                pv_mfma(1, p1);
+            } else {
+                const bf16x8 p0 = p_step(0);
+                const bf16x8 p1 = p_step(1);
+                pv_mfma(0, p0);
+                const bf16x8 p2 = p_step(2);
+                // 4 products of step 0 against the 8 exponentials (+ arithmetic) of step 2
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+                }
+                pv_mfma(1, p1);
+                const bf16x8 p3 = p_step(3);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 2);
+                }
+                pv_mfma(2, p2);
+                pv_mfma(3, p3);
             }
             l += sum;
-
-            // ---- O^T += V^T P^T ----
-            const int nst = half ? 2 : 4;
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                if (st >= nst) break;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st][dt], p[st], o[dt], 0, 0, 0);
-                }
-            }
         }
         if (t < ke) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
     }
