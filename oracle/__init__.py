@@ -113,6 +113,14 @@ class DecodeResult:
     n_tokens: np.ndarray       # int32 [B][Hq]
 
 
+def _gist_mode(x) -> int:
+    """True/"all": every scored gist; False/"none": raw tokens only; "selected": the gists of the
+    selected chunks only ("Simplified Sparse Attention via Gist Tokens", section 3.3)."""
+    if isinstance(x, str):
+        return {"none": 0, "all": 1, "selected": 2}[x]
+    return int(bool(x))
+
+
 def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_k, gist_v,
            gate=0, levels=1, J=0, k2=0, gist2_k=None, gist2_v=None, scale=0.0,
            gists_in_softmax=True, gist_cap=0, forced_sel=None, forced_groups=None,
@@ -123,7 +131,7 @@ def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_
     nG = -(-H // J) if levels == 2 else 0
     u16 = np.uint16
     sh = _DecodeShape(B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, C=C_, g=g, k=k, gate=gate,
-                      gists_in_softmax=int(gists_in_softmax), levels=levels, J=J, k2=k2,
+                      gists_in_softmax=_gist_mode(gists_in_softmax), levels=levels, J=J, k2=k2,
                       max_chunks=page_table.shape[-1], num_pages=k_pages.shape[0],
                       gist_cap=gist_cap, scale=scale)
     out = np.full((B, Hq, d), np.nan)
@@ -151,7 +159,7 @@ def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_
 
 
 def token_count(*, N, C_, g, k_eff, levels=1, J=0, n_cand=0, gists_in_softmax=True) -> int:
-    sh = _DecodeShape(N=N, C=C_, g=g, levels=levels, J=J, gists_in_softmax=int(gists_in_softmax))
+    sh = _DecodeShape(N=N, C=C_, g=g, levels=levels, J=J, gists_in_softmax=_gist_mode(gists_in_softmax))
     return int(lib().or_decode_token_count(C.byref(sh), k_eff, n_cand))
 
 

@@ -146,9 +146,11 @@ int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand)
     int H = M - 1;
     int cur = p->N - H * p->C;
     int summaries = 0;
-    if (p->gists_in_softmax) {
+    if (p->gists_in_softmax == 1) {
         if (p->levels == 2) summaries = ((H + p->J - 1) / p->J) * p->g + n_cand * p->g;
         else summaries = H * p->g;
+    } else if (p->gists_in_softmax == 2) {
+        summaries = k_eff * p->g;   /* each selected chunk brings its own gists */
     }
     return summaries + k_eff * p->C + cur;
 }
@@ -239,7 +241,7 @@ static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, 
     int cap = or_decode_token_count(p, ke, n_cand);
     token* tk = (token*)malloc(sizeof(token) * (size_t)cap);
     int n = 0;
-    if (p->gists_in_softmax) {
+    if (p->gists_in_softmax == 1) {
         if (p->levels == 2)
             for (int r = 0; r < nG; ++r)
                 for (int t = 0; t < g; ++t) {
@@ -261,6 +263,12 @@ static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, 
         if (p->gate) {
             for (int j = 0; j < n_cand; ++j) if (cand[j] == c) gamma = s[j] - lse_s;
         }
+        if (p->gists_in_softmax == 2)   /* the chunk's gists, unbiased ("SSA", section 3.3) */
+            for (int t = 0; t < g; ++t) {
+                tk[n].k = gk + ((size_t)c * g + t) * d;
+                tk[n].v = gv + ((size_t)c * g + t) * d;
+                tk[n++].bias = 0.0;
+            }
         int page = pt[c];
         if (page < 0 || page >= p->num_pages) { bad_page = 1; continue; }
         const uint16_t* kr = io->k_pages + ((size_t)page * p->Hkv + kv) * (size_t)C * d;
@@ -311,6 +319,8 @@ int or_decode(const or_decode_shape* p, const or_decode_io* io)
     if (!p || !io) return 1;
     if (p->Hkv <= 0 || p->Hq % p->Hkv || p->C <= 0 || p->g <= 0 || p->N < 1) return 2;
     if (p->levels == 2 && (p->J <= 0 || p->gate)) return 3;
+    if (p->gists_in_softmax < 0 || p->gists_in_softmax > 2) return 4;
+    if (p->gists_in_softmax == 2 && p->levels != 1) return 4;
     const int total = p->B * p->Hkv;
     const int n = io->units ? io->n_units : total;
     int rc = 0;

@@ -23,7 +23,8 @@ typedef struct {
     int B, Hq, Hkv, d;
     int N, C, g, k;
     int gate;             /* 0 none, 1 SAS log-softmax gate                          */
-    int gists_in_softmax; /* 1: every scored summary enters the softmax; 0: raw only  */
+    int gists_in_softmax; /* 1: every scored summary enters the softmax; 0: raw only;
+                             2: only the selected chunks' gists (one level)            */
     int levels, J, k2;
     int max_chunks;
     int num_pages;

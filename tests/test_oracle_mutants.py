@@ -21,7 +21,7 @@ MUTANTS = [
     ("tie_break_highest", "return (x->c > y->c) - (x->c < y->c);",
      "return (x->c < y->c) - (x->c > y->c);"),
     ("drop_current_chunk", "for (int u = 0; u < cur; ++u) {", "for (int u = 0; u < 0; ++u) {"),
-    ("drop_gists", "    if (p->gists_in_softmax) {\n        if (p->levels == 2)\n            for",
+    ("drop_gists", "    if (p->gists_in_softmax == 1) {\n        if (p->levels == 2)\n            for",
      "    if (0) {\n        if (p->levels == 2)\n            for"),
     ("diag_not_causal", "for (int u = i * blk; u <= pos; ++u) {",
      "for (int u = i * blk; u < (i + 1) * blk; ++u) {"),
@@ -36,6 +36,10 @@ MUTANTS = [
     ("prefill_sees_diagonal_in_selection", "for (int j = 0; j < i; ++j) { s[j]",
      "for (int j = 0; j < i; ++j) { s[j] = (double)Srow[j + 1]; ids[j] = j; } for (int j = 0; j < 0; ++j) { s[j]"),
     ("weights_transposed_v", "o[i] += w * bf(t[x].v[i]);", "o[i] += w * bf(t[x].k[i]);"),
+    ("selected_gists_first_only", "tk[n].k = gk + ((size_t)c * g + t) * d;",
+     "tk[n].k = gk + ((size_t)c * g + 0) * d;"),
+    ("selected_gists_gated", "                tk[n].v = gv + ((size_t)c * g + t) * d;\n                tk[n++].bias = 0.0;",
+     "                tk[n].v = gv + ((size_t)c * g + t) * d;\n                tk[n++].bias = p->gate ? 0.5 : 0.0;"),
 ]
 
 

@@ -72,7 +72,7 @@ def brute_decode(inp, gists=True):
                 order = sorted(range(c.nG), key=lambda r: (-s2[r], r))
                 groups = sorted(order[: c.k2])
                 cand = [x for r in groups for x in range(r * c.J, min((r + 1) * c.J, H))]
-                if gists:
+                if gists is True:
                     Ks += [g2k.reshape(-1, c.d)]
                     Vs += [g2v.reshape(-1, c.d)]
                     bias += [0.0] * (c.nG * c.g)
@@ -83,8 +83,13 @@ def brute_decode(inp, gists=True):
             sel = sorted(order[: c.k])
             sels[b, kv, : len(sel)] = sel
             lse_s = _lse([s[x] for x in cand]) if cand else 0.0
-            if gists:
+            if gists is True:
                 for x in cand:
+                    Ks.append(gk[b, kv, x])
+                    Vs.append(gv[b, kv, x])
+                    bias += [0.0] * c.g
+            if gists == "selected":
+                for x in sel:
                     Ks.append(gk[b, kv, x])
                     Vs.append(gv[b, kv, x])
                     bias += [0.0] * c.g
@@ -450,6 +455,58 @@ def pin_prefill_selection_argsort():
             got = r.sel[0, kv, i]
             assert np.array_equal(got[: len(want)], want)
             assert (got[len(want):] == -1).all()
+
+
+def pin_selected_gists_brute_force():
+    """Token set of the selected chunks' gists + their raw tokens + the current chunk ("SSA",
+    section 3.3), against the independent numpy evaluation, gate off and on."""
+    for cfg in (SMALL, SMALL.with_(gate=1), SMALL_G1):
+        inp = make_decode(cfg, seed=13, max_chunks=cfg.M + 1, extra_pages=1)
+        r = oracle_decode(inp, gists_in_softmax="selected")
+        o, l, s_ = brute_decode(inp, gists="selected")
+        assert np.array_equal(r.sel, s_), cfg.name
+        assert np.abs(r.out - o).max() < TOL, cfg.name
+        assert np.abs(r.lse - l).max() < TOL, cfg.name
+
+
+def pin_selected_gists_k_all_equals_all_gists():
+    """With every chunk selected the selected-gist set is the whole cache again."""
+    for gate in (0, 1):
+        cfg = SMALL.with_(k=SMALL.H, gate=gate)
+        inp = make_decode(cfg, seed=14)
+        a = oracle_decode(inp, gists_in_softmax=True)
+        b = oracle_decode(inp, gists_in_softmax="selected")
+        assert np.abs(a.out - b.out).max() < TOL and np.abs(a.lse - b.lse).max() < TOL
+
+
+def pin_selected_gists_k_zero_is_current_chunk():
+    """No chunk selected: only the current chunk's raw tokens remain (textbook attention)."""
+    cfg = SMALL.with_(k=0, B=1)
+    inp = make_decode(cfg, seed=15)
+    K, V = _logical_kv(inp)
+    q = f64(inp.q)
+    r = oracle_decode(inp, gists_in_softmax="selected")
+    for h in range(cfg.Hq):
+        kv = h // cfg.G
+        o, l = sdpa(q[0, h], K[0, kv, cfg.H, : cfg.cur_len], V[0, kv, cfg.H, : cfg.cur_len])
+        assert np.abs(r.out[0, h] - o).max() < TOL
+        assert abs(r.lse[0, h] - l) < TOL
+
+
+def pin_selected_gists_token_count_and_weights():
+    """|V_t| = k (g + C) + |current chunk|, which is the page's k (1 + L) at g = 1 plus the
+    current chunk; the weights sum to one with the gate inside the softmax."""
+    assert oracle.token_count(N=100, C_=8, g=1, k_eff=4, gists_in_softmax="selected") == 4 * 9 + 4
+    assert oracle.token_count(N=96, C_=8, g=3, k_eff=5, gists_in_softmax="selected") == 5 * 11 + 8
+    cfg = SMALL.with_(gate=1, B=1)
+    inp = make_decode(cfg, seed=16)
+    cap = cfg.k * (cfg.g + cfg.C) + cfg.C
+    r = oracle_decode(inp, gists_in_softmax="selected", weights_cap=cap)
+    for h in range(cfg.Hq):
+        n = r.n_tokens[0, h]
+        assert n == cfg.k * (cfg.g + cfg.C) + cfg.cur_len
+        w = r.weights[0, h, :n]
+        assert abs(w.sum() - 1.0) < TOL and (w > 0).all()
 
 
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]
