@@ -27,10 +27,12 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, vendor figure
 
 
-def decode_bytes(cfg, k=None):
+def decode_bytes(cfg, k=None, gist_mode="all"):
     """Algorithmic bytes of one decode call: every byte the method must touch, once.
     Gist rows scored (and attended), the selected chunks' K and V, the current chunk's K and
-    V, q, out (fp32), and the page-table entries read."""
+    V, q, out (fp32), and the page-table entries read.  gist_mode "selected": every gist key is
+    read for the scores, but only the selected chunks' gist values (and keys, already read)
+    enter the softmax."""
     k = cfg.k if k is None else k
     units = cfg.B * cfg.Hkv
     row = cfg.d * 2                               # one bf16 row
@@ -41,22 +43,26 @@ def decode_bytes(cfg, k=None):
     else:
         gist_rows = cfg.H * cfg.g
         k_eff = min(k, cfg.H)
-    parts = {
-        "gists_kv": units * gist_rows * row * 2,
+    if gist_mode == "selected":
+        parts = {"gists_k": units * gist_rows * row, "selected_gists_v": units * k_eff * cfg.g * row}
+    else:
+        parts = {"gists_kv": units * gist_rows * row * 2}
+    parts.update({
         "selected_kv": units * k_eff * cfg.C * row * 2,
         "current_kv": units * cfg.cur_len * row * 2,
         "q": cfg.B * cfg.Hq * row,
         "out": cfg.B * cfg.Hq * cfg.d * 4,
         "page_table": units * (k_eff + 1) * 4,
-    }
+    })
     return sum(parts.values()), parts
 
 
-def gist_kernel_bytes(cfg):
+def gist_kernel_bytes(cfg, gist_mode="all"):
     """Algorithmic bytes of the gist-scoring kernel (levels = 1): every historical gist row
-    (K and V) of every unit, plus q."""
+    (K, and V unless only the selected chunks' gists enter the softmax) of every unit, plus q."""
     units = cfg.B * cfg.Hkv
-    return units * cfg.H * cfg.g * cfg.d * 2 * 2 + cfg.B * cfg.Hq * cfg.d * 2
+    kv = 1 if gist_mode == "selected" else 2
+    return units * cfg.H * cfg.g * cfg.d * 2 * kv + cfg.B * cfg.Hq * cfg.d * 2
 
 
 def prefill_pairs(cfg):
@@ -272,6 +278,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--instances", type=int, default=3)
     ap.add_argument("--workload", default="llama31_8b_decode_128k")
+    ap.add_argument("--gist-mode", choices=["all", "selected"], default="all",
+                    help="decode softmax set: every historical gist (default) or only the "
+                         "selected chunks' gists")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -303,7 +312,8 @@ def main():
     R = max(1, args.instances)
     print(f"# generating {R} instance(s) of {cfg.name}", file=sys.stderr, flush=True)
     insts = [make_decode(cfg, configs.seed_for(cfg.name, r), device=dev) for r in range(R)]
-    calls = [ops.DecodeCall(inp, with_scores=False) for inp in insts]
+    gmode = ops.GISTS_SELECTED if args.gist_mode == "selected" else ops.GISTS_ALL
+    calls = [ops.DecodeCall(inp, with_scores=False, gist_mode=gmode) for inp in insts]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
@@ -345,17 +355,17 @@ def main():
                 for j in range(nst)]
     print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
 
-    total_bytes, parts = decode_bytes(cfg)
+    total_bytes, parts = decode_bytes(cfg, gist_mode=args.gist_mode)
     eff_gbps = total_bytes / (ms_per_step * 1e-3) / 1e9
     # dominant kernel: gist scoring (stage 1) -- the largest byte stream of the call
-    gk_bytes = gist_kernel_bytes(cfg) if cfg.levels == 1 else None
+    gk_bytes = gist_kernel_bytes(cfg, args.gist_mode) if cfg.levels == 1 else None
     roof = None
     if gk_bytes:
         gk_ms = stage_ms[0]
         ach = gk_bytes / (gk_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "gist_kernel", "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                "traffic": load_traffic("gist_kernel", cfg.name),
+                "traffic": load_traffic("gist_kernel", cfg.name) if args.gist_mode == "all" else None,
                 "algorithmic_bytes": gk_bytes, "avg_ms": round(gk_ms, 5)}
 
     cpu = None
@@ -378,7 +388,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "N": cfg.N, "C": cfg.C, "g": cfg.g, "k": cfg.k, "gate": "sas" if cfg.gate else
-                   "none", "levels": cfg.levels, "paged": cfg.paged, "inputs": "bf16",
+                   "none", "levels": cfg.levels, "paged": cfg.paged, "gists": args.gist_mode, "inputs": "bf16",
                    "instances_rotated": R},
         "effective_GBps": round(eff_gbps, 1),
         "pct_of_hbm_peak": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),

@@ -22,6 +22,10 @@
  *        of the current chunk (bias 0, always kept):
  *          lambda_x = sigma * q . k_x + bias_x,  out = sum_x softmax(lambda)_x v_x,
  *          lse = log sum_x exp(lambda_x)  (natural log, gate included).
+ *   gist_mode = TCS_GISTS_SELECTED (one level only) replaces "every historical gist" in step 5
+ *   by the gists of the selected chunks only, each next to its chunk's raw tokens: the set
+ *   section 3.3 describes, in which an unselected chunk contributes nothing.  The scores and
+ *   the selection (steps 1-4) are unchanged.
  *   Two levels (levels = 2; section 3.5 and appendix B.2): level-2 gists summarise groups of J
  *   consecutive historical chunks.  The group scores s2[r] (step 2 over gist2_k) pick the top
  *   k2 groups; the member chunks of the chosen groups are the candidates; steps 1-3 run over
@@ -68,11 +72,12 @@
  *   unspecified results).  A page id outside [0, num_pages) is never read: the heads of the
  *   affected unit get NaN in out and lse.
  *   k larger than the number of candidates is clamped (that is how "all chunks" is asked
- *   for); k = 0 keeps only the gists and the current chunk.  Results are deterministic:
+ *   for); k = 0 keeps only the gists and the current chunk (only the current chunk with
+ *   TCS_GISTS_SELECTED).  Results are deterministic:
  *   no floating-point atomics; the same inputs give bitwise-identical outputs.
  *
  * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024;
- * B * Hkv <= 16384; two levels:
+ * B * Hkv <= 16384; TCS_GISTS_SELECTED: one level and C + g <= 1024; two levels:
  * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk.
  * Other shapes return TCS_ERR_UNSUPPORTED.
  */
@@ -86,7 +91,7 @@
 extern "C" {
 #endif
 
-#define TCS_ABI_VERSION 1
+#define TCS_ABI_VERSION 2
 
 typedef enum {
     TCS_OK = 0,
@@ -98,6 +103,7 @@ typedef enum {
 } tcs_status;
 
 enum { TCS_GATE_NONE = 0, TCS_GATE_SAS = 1 };
+enum { TCS_GISTS_ALL = 0, TCS_GISTS_SELECTED = 1 };   /* which gists enter the softmax */
 
 typedef struct {
     int32_t struct_size;   /* = sizeof(tcs_decode_params) */
@@ -107,6 +113,7 @@ typedef struct {
     int32_t g;             /* gists per chunk                                             */
     int32_t k;             /* chunks to select (>= 0; clamped to the candidate count)     */
     int32_t gate_mode;     /* TCS_GATE_NONE or TCS_GATE_SAS                               */
+    int32_t gist_mode;     /* TCS_GISTS_ALL or TCS_GISTS_SELECTED                         */
     int32_t levels;        /* 1, or 2 for gist-of-gist routing                            */
     int32_t J;             /* levels = 2: chunks per level-2 group                        */
     int32_t k2;            /* levels = 2: groups to select                                */

@@ -58,8 +58,10 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
     selection instead."""
     c = inp.cfg
     G = c.G
+    gmode = "selected" if getattr(call, "gist_mode", 0) == 1 else True
     if ref is None:
-        ref = oracle_decode(inp, k=call.p.k, units=units, scale=float(call.p.scale))
+        ref = oracle_decode(inp, k=call.p.k, units=units, scale=float(call.p.scale),
+                            gists_in_softmax=gmode)
     all_units = list(range(c.B * c.Hkv)) if units is None else list(units)
     gsel = call.sel.cpu().numpy()
     gout = call.out.cpu().double().numpy()
@@ -86,7 +88,7 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
         forced = np.ascontiguousarray(gsel.astype(np.int32))
         fg = np.ascontiguousarray(ggrp.astype(np.int32)) if ggrp is not None else None
         ref2 = oracle_decode(inp, k=k, units=excused, forced_sel=forced, forced_groups=fg,
-                             scale=float(call.p.scale))
+                             scale=float(call.p.scale), gists_in_softmax=gmode)
         for u in excused:
             b, kv = divmod(u, c.Hkv)
             ref.out[b, kv * G:(kv + 1) * G] = ref2.out[b, kv * G:(kv + 1) * G]

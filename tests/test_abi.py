@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ops.lib().tcs_abi_version() == 1
+    assert ops.lib().tcs_abi_version() == 2
     for code in range(6):
         assert ops.status_str(code)
     assert ops.status_str(99) == "unknown status"
@@ -41,6 +41,14 @@ def P(**kw):
     base = dict(B=2, Hq=8, Hkv=2, d=128, N=1000, C_=64, g=4, k=4, num_pages=32)
     base.update(kw)
     return ops.decode_params(**base)
+
+
+def test_selected_gists_need_fewer_partial_slots():
+    # without gist slices the partial buffer shrinks; the scores, selection and chunk
+    # attention parts are unchanged
+    a = ops.decode_workspace_size(P(N=64 * 500))
+    b = ops.decode_workspace_size(P(N=64 * 500, gist_mode=1))
+    assert 0 < b < a
 
 
 def test_workspace_size_grows_with_work():
@@ -71,6 +79,9 @@ def test_workspace_size_grows_with_work():
     (dict(scale=-1.0), ops.TCS_ERR_SHAPE),
     (dict(num_pages=0), ops.TCS_ERR_SHAPE),
     (dict(B=4097, Hkv=4, Hq=16), ops.TCS_ERR_UNSUPPORTED),   # 16388 units
+    (dict(gist_mode=2), ops.TCS_ERR_SHAPE),
+    (dict(gist_mode=1, levels=2, J=4, k2=2), ops.TCS_ERR_UNSUPPORTED),
+    (dict(gist_mode=1, C_=1024, g=8, N=5000), ops.TCS_ERR_UNSUPPORTED),  # C + g > 1024
 ])
 def test_decode_rejects_bad_params(kw, code):
     p = P(**kw)

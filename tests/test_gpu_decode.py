@@ -24,11 +24,12 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_case(cfg, seed, units=None, **kw):
+def run_case(cfg, seed, units=None, gist_mode=0, **kw):
     say(f"[decode] {cfg.name} seed={seed} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} "
-        f"N={cfg.N} C={cfg.C} g={cfg.g} k={cfg.k} gate={cfg.gate} levels={cfg.levels} {kw}")
+        f"N={cfg.N} C={cfg.C} g={cfg.g} k={cfg.k} gate={cfg.gate} levels={cfg.levels} "
+        f"gist_mode={gist_mode} {kw}")
     inp = make_decode(cfg, seed, device=DEV, **kw)
-    call = DecodeCall(inp)()
+    call = DecodeCall(inp, gist_mode=gist_mode)()
     torch.cuda.synchronize()
     st = check_decode(inp, call, units=units)
     say("   ", st)
@@ -73,6 +74,25 @@ VARIANTS = [
 @pytest.mark.parametrize("cfg", VARIANTS, ids=[f"v{i}" for i in range(len(VARIANTS))])
 def test_variants(cfg):
     run_case(cfg, seed=100 + VARIANTS.index(cfg), max_chunks=cfg.M + 5, extra_pages=3)
+
+
+# Selected-gist token set (each selected chunk's gists next to its raw tokens).
+SEL_GISTS = [v for v in VARIANTS if v.levels == 1 and v.C + v.g <= 1024]
+
+
+@pytest.mark.parametrize("cfg", SEL_GISTS, ids=[f"sg{i}" for i in range(len(SEL_GISTS))])
+def test_selected_gists_variants(cfg):
+    run_case(cfg, seed=300 + SEL_GISTS.index(cfg), gist_mode=1, max_chunks=cfg.M + 2,
+             extra_pages=1)
+
+
+@pytest.mark.parametrize("name", ["llama32_1b_decode_32k", "llama31_8b_decode_128k"])
+def test_selected_gists_full(name):
+    cfg = configs.DECODE_CONFIGS[name]
+    inp, call, st = run_case(cfg, configs.seed_for(name), gist_mode=1)
+    assert st["excused"] <= max(1, st["units"] // 100)
+    del inp, call
+    torch.cuda.empty_cache()
 
 
 def test_deterministic_bitwise():

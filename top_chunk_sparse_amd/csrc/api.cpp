@@ -74,6 +74,7 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (p->Hq % p->Hkv) return TCS_ERR_SHAPE;
     if (p->levels != 1 && p->levels != 2) return TCS_ERR_SHAPE;
     if (p->gate_mode != TCS_GATE_NONE && p->gate_mode != TCS_GATE_SAS) return TCS_ERR_SHAPE;
+    if (p->gist_mode != TCS_GISTS_ALL && p->gist_mode != TCS_GISTS_SELECTED) return TCS_ERR_SHAPE;
     if (!(p->scale >= 0.f) || std::isinf(p->scale)) return TCS_ERR_SHAPE;
     const int G = p->Hq / p->Hkv;
     const long long units = (long long)p->B * p->Hkv;
@@ -85,6 +86,8 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (p->d != 64 && p->d != 128) return TCS_ERR_UNSUPPORTED;
     if (!supported_group(G)) return TCS_ERR_UNSUPPORTED;
     if (p->g > 64 || p->C > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
+    const bool sel_gists = p->gist_mode == TCS_GISTS_SELECTED;
+    if (sel_gists && (p->levels != 1 || p->C + p->g > kMaxSliceRows)) return TCS_ERR_UNSUPPORTED;
     pl->G = G;
     pl->M = M;
     pl->H = H;
@@ -117,12 +120,15 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     pl->kslots = ksel;
     // chunk attention: enough workgroups to fill the GPU, one or more chunks each
     long long cpw = units * (ksel + 1) / kChunkTargetWorkgroups;
-    const long long cpw_max = std::min<long long>(16, kMaxSliceRows / p->C);  // rows held in LDS
+    const long long slot_rows = p->C + (sel_gists ? p->g : 0);   // rows a slot holds in LDS
+    const long long cpw_max = std::min<long long>(16, kMaxSliceRows / slot_rows);
     // At least two slots per workgroup once there are enough of them: a workgroup's fixed costs
     // (dispatch, query load, partial write, arrival) then pay for twice the bytes.
     const long long cpw_min = units * (ksel + 1) >= 512 ? 2 : 1;
     pl->cpw = (int)std::max<long long>(std::min(cpw_min, cpw_max), std::min(cpw, cpw_max));
-    pl->nslots = pl->S1 + pl->S2 + pl->k2e + (ksel + 1 + pl->cpw - 1) / pl->cpw;
+    // softmax partial slots per query head: gist slices (none with selected gists), chosen
+    // level-2 groups' slices, then the chunk-attention workgroups
+    pl->nslots = (sel_gists ? 0 : pl->S1) + pl->S2 + pl->k2e + (ksel + 1 + pl->cpw - 1) / pl->cpw;
     const long long BH = (long long)p->B * p->Hq;
     const long long s1 = p->levels == 2 ? pl->k2e : pl->S1;     // slices of the chunk pass
     auto n1 = [](long long x) { return x > 0 ? x : 1; };
@@ -273,9 +279,10 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         ga.score_stride = pl.H;
         ga.slot0 = slot;
         ga.selo = chunk_sel;
+        ga.scores_only = p->gist_mode == TCS_GISTS_SELECTED;
         e = tcs::launch_gist(ga, s);
         if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
-        slot += pl.S1;
+        if (!ga.scores_only) slot += pl.S1;
         chunks_chosen = pl.S1 > 0;
     } else {
         int32_t* gsel = sel_groups ? sel_groups : (int32_t*)(ws + pl.off_gsel);
@@ -347,6 +354,12 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     ca.counter = cnt + kCntChunk;
     ca.out = out;
     ca.lse = lse;
+    if (p->gist_mode == TCS_GISTS_SELECTED) {
+        ca.gk = (const uint16_t*)gist_k;
+        ca.gv = (const uint16_t*)gist_v;
+        ca.gist_stride = (long long)cap * p->g * p->d;
+        ca.g = p->g;
+    }
     e = tcs::launch_chunks(ca, s);
     if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
     return TCS_OK;

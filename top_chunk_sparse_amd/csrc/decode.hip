@@ -400,8 +400,8 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
         sm.score[c] = s;
         if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
     }
-    head_stats<G>(sm.x.lg, nrows, sm.hs);
-    {
+    if (!a.scores_only) {   // the gists are tokens of the softmax set: fold them in here
+        head_stats<G>(sm.x.lg, nrows, sm.hs);
         float acc[G][8];
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -531,6 +531,7 @@ struct ChunkSmem {
     int page[kMaxCpw];
     float bias[kMaxCpw];
     int rows[kMaxCpw];
+    int chunk[kMaxCpw];   // selected chunk of the slot, -1 for the current chunk
     int flag;
 };
 
@@ -563,8 +564,13 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
         sm.page[threadIdx.x] = page;
         sm.bias[threadIdx.x] = bias;
         sm.rows[threadIdx.x] = rows;
+        sm.chunk[threadIdx.x] = j < a.kslots ? c : -1;
     }
-    for (int i = threadIdx.x; i < nj * a.C * G; i += 256) sm.x.lg[i] = -INFINITY;
+    // LDS rows: the raw rows of slot jj at [jj C, jj C + rows), then (selected-gist token set)
+    // the g gist rows of slot jj at [nj C + jj g, nj C + jj g + g)
+    const int graw = nj * a.C;
+    const int nrows_all = graw + (a.gk ? nj * a.g : 0);
+    for (int i = threadIdx.x; i < nrows_all * G; i += 256) sm.x.lg[i] = -INFINITY;
     __syncthreads();
     bool bad = false, any = false;
     for (int jj = 0; jj < nj; ++jj) {
@@ -585,10 +591,14 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
                 const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
                 rs.template logits<TCS_CK_U>(q2, a.kp + off, sm.rows[jj], a.sigma, sm.bias[jj],
                                             sm.x.lg, jj * a.C);
+                if (a.gk && sm.chunk[jj] >= 0)
+                    rs.template logits<TCS_CK_U>(
+                        q2, a.gk + (long long)u * a.gist_stride + (long long)sm.chunk[jj] * a.g * D,
+                        a.g, a.sigma, 0.f, sm.x.lg, graw + jj * a.g);
             }
         }
         __syncthreads();
-        head_stats<G>(sm.x.lg, nj * a.C, sm.hs);
+        head_stats<G>(sm.x.lg, nrows_all, sm.hs);
         float acc[G][8];
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -598,6 +608,10 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
             if (sm.page[jj] < 0) continue;
             const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
             rs.template accumulate<TCS_CV_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, jj * a.C);
+            if (a.gk && sm.chunk[jj] >= 0)
+                rs.template accumulate<TCS_CV_U>(
+                    acc, a.gv + (long long)u * a.gist_stride + (long long)sm.chunk[jj] * a.g * D,
+                    a.g, sm.x.lg, graw + jj * a.g);
         }
         __syncthreads();
         rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + wx);

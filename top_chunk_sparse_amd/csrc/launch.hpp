@@ -44,6 +44,7 @@ struct GistLaunch {
     Partials part;
     int slot0;
     SelectOut selo;
+    int scores_only;          // 1: score and select only (no gist softmax partials)
 };
 
 struct ChunkLaunch {
@@ -64,6 +65,11 @@ struct ChunkLaunch {
     unsigned* counter;        // [units], zero between calls
     float* out;               // [B*Hq][d]
     float* lse;               // [B*Hq] or null
+    // selected-gist token set: each selected chunk's g gist rows join its raw rows
+    const uint16_t* gk;       // [units][gist_cap][g][d] or null
+    const uint16_t* gv;
+    long long gist_stride;    // elements between consecutive units' gists
+    int g;
 };
 
 hipError_t launch_gist(const GistLaunch& a, hipStream_t s);
