@@ -33,7 +33,8 @@ def build(force: bool = True) -> str:
 class _DecodeShape(C.Structure):
     _fields_ = [(n, C.c_int) for n in ("B", "Hq", "Hkv", "d", "N", "C", "g", "k", "gate",
                                        "gists_in_softmax", "levels", "J", "k2", "max_chunks",
-                                       "num_pages", "gist_cap")] + [("scale", C.c_double)]
+                                       "num_pages", "gist_cap")] + [("scale", C.c_double),
+                                                                    ("top_p", C.c_double)]
 
 
 _P = C.c_void_p
@@ -124,7 +125,7 @@ def _gist_mode(x) -> int:
 def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_k, gist_v,
            gate=0, levels=1, J=0, k2=0, gist2_k=None, gist2_v=None, scale=0.0,
            gists_in_softmax=True, gist_cap=0, forced_sel=None, forced_groups=None,
-           units=None, weights_cap=0) -> DecodeResult:
+           units=None, weights_cap=0, top_p=0.0) -> DecodeResult:
     """Decode attention for every (b, kv) (or the flat ids in ``units``)."""
     M = -(-N // C_)
     H = M - 1
@@ -133,7 +134,7 @@ def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_
     sh = _DecodeShape(B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, C=C_, g=g, k=k, gate=gate,
                       gists_in_softmax=_gist_mode(gists_in_softmax), levels=levels, J=J, k2=k2,
                       max_chunks=page_table.shape[-1], num_pages=k_pages.shape[0],
-                      gist_cap=gist_cap, scale=scale)
+                      gist_cap=gist_cap, scale=scale, top_p=top_p)
     out = np.full((B, Hq, d), np.nan)
     lse = np.full((B, Hq), np.nan)
     sel = np.full((B, Hkv, max(k, 1)), -7, np.int32)

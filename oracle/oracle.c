@@ -127,6 +127,32 @@ static double attend(const uint16_t* q, const token* t, int n, int d, double sig
     return m + log(z);
 }
 
+/* Top-p with a cap: rank n scored items by (score desc, index asc); p_i = exp(s_i - lse) is an
+ * item's share of the softmax over all n items.  Keep the shortest ranked prefix whose shares
+ * add up to at least p (p >= 1 keeps everything), then at most k of them; indices ascending.
+ * Returns the number kept. */
+static int top_p(const double* s, const int* idx, int n, double p, int k, int* chosen)
+{
+    if (n <= 0 || k <= 0) return 0;
+    scored* v = (scored*)malloc(sizeof(scored) * (size_t)n);
+    for (int i = 0; i < n; ++i) { v[i].s = s[i]; v[i].c = idx[i]; }
+    qsort(v, (size_t)n, sizeof(scored), by_rank);
+    const double lse = logsumexp(s, n);
+    int r = n;
+    if (p < 1.0) {
+        double mass = 0.0;
+        for (int i = 0; i < n; ++i) {
+            mass += exp(v[i].s - lse);
+            if (mass >= p) { r = i + 1; break; }
+        }
+    }
+    int ke = r < k ? r : k;
+    for (int i = 0; i < ke; ++i) chosen[i] = v[i].c;
+    qsort(chosen, (size_t)ke, sizeof(int), ascending);
+    free(v);
+    return ke;
+}
+
 /* Pooled chunk score: LSE over the G heads of the group and g gists at `gist` ([g][d]). */
 static double pooled_score(const uint16_t* q_group, int G, const uint16_t* gist, int g, int d,
                            double sigma)
@@ -227,6 +253,8 @@ static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, 
             int c = io->forced_sel[unit * p->k + i];
             if (c >= 0) sel[ke++] = c;
         }
+    } else if (p->top_p > 0.0) {
+        ke = top_p(s, cand, n_cand, p->top_p, p->k, sel);
     } else {
         ke = top_k(s, cand, n_cand, p->k, sel);
     }
@@ -321,6 +349,7 @@ int or_decode(const or_decode_shape* p, const or_decode_io* io)
     if (p->levels == 2 && (p->J <= 0 || p->gate)) return 3;
     if (p->gists_in_softmax < 0 || p->gists_in_softmax > 2) return 4;
     if (p->gists_in_softmax == 2 && p->levels != 1) return 4;
+    if (!(p->top_p >= 0.0 && p->top_p <= 1.0) || (p->top_p > 0.0 && p->levels != 1)) return 5;
     const int total = p->B * p->Hkv;
     const int n = io->units ? io->n_units : total;
     int rc = 0;

@@ -30,6 +30,8 @@ typedef struct {
     int num_pages;
     int gist_cap;
     double scale;         /* <= 0: 1/sqrt(d)                                          */
+    double top_p;         /* 0: top-k; in (0, 1]: shortest ranked prefix with softmax
+                             mass >= top_p, at most k chunks (one level)               */
 } or_decode_shape;
 
 typedef struct {

@@ -36,6 +36,11 @@ MUTANTS = [
     ("prefill_sees_diagonal_in_selection", "for (int j = 0; j < i; ++j) { s[j]",
      "for (int j = 0; j < i; ++j) { s[j] = (double)Srow[j + 1]; ids[j] = j; } for (int j = 0; j < 0; ++j) { s[j]"),
     ("weights_transposed_v", "o[i] += w * bf(t[x].v[i]);", "o[i] += w * bf(t[x].k[i]);"),
+    ("top_p_cap_off_by_one", "    int ke = r < k ? r : k;\n    for (int i = 0; i < ke; ++i) chosen[i] = v[i].c;\n    qsort(chosen, (size_t)ke, sizeof(int), ascending);\n    free(v);\n    return ke;\n}\n\n/* Pooled",
+     "    int ke = r < k ? r : k - 1;\n    for (int i = 0; i < ke; ++i) chosen[i] = v[i].c;\n    qsort(chosen, (size_t)ke, sizeof(int), ascending);\n    free(v);\n    return ke;\n}\n\n/* Pooled"),
+    ("top_p_unranked", "    qsort(v, (size_t)n, sizeof(scored), by_rank);\n    const double lse = logsumexp(s, n);",
+     "    const double lse = logsumexp(s, n);"),
+    ("top_p_shares_of_first_half", "    const double lse = logsumexp(s, n);", "    const double lse = logsumexp(s, (n + 1) / 2);"),
     ("selected_gists_first_only", "tk[n].k = gk + ((size_t)c * g + t) * d;",
      "tk[n].k = gk + ((size_t)c * g + 0) * d;"),
     ("selected_gists_gated", "                tk[n].v = gv + ((size_t)c * g + t) * d;\n                tk[n++].bias = 0.0;",

@@ -53,7 +53,7 @@ def _logical_kv(inp):
     return K, V
 
 
-def brute_decode(inp, gists=True):
+def brute_decode(inp, gists=True, top_p=0.0):
     c = inp.cfg
     G, H, sig = c.G, c.H, 1.0 / math.sqrt(c.d)
     q = f64(inp.q)
@@ -80,7 +80,11 @@ def brute_decode(inp, gists=True):
                 cand = list(range(H))
             s = {x: _lse(sig * qg @ gk[b, kv, x].T) for x in cand}
             order = sorted(cand, key=lambda x: (-s[x], x))
-            sel = sorted(order[: c.k])
+            r = len(order)
+            if 0.0 < top_p < 1.0:
+                shares = np.exp(np.array([s[x] for x in order]) - _lse([s[x] for x in cand]))
+                r = int(np.argmax(np.cumsum(shares) >= top_p)) + 1
+            sel = sorted(order[: min(c.k, r)])
             sels[b, kv, : len(sel)] = sel
             lse_s = _lse([s[x] for x in cand]) if cand else 0.0
             if gists is True:
@@ -507,6 +511,56 @@ def pin_selected_gists_token_count_and_weights():
         assert n == cfg.k * (cfg.g + cfg.C) + cfg.cur_len
         w = r.weights[0, h, :n]
         assert abs(w.sum() - 1.0) < TOL and (w > 0).all()
+
+
+def pin_top_p_brute_force():
+    """Top-p with a cap of k chunks: the shortest ranked prefix whose share of the softmax over
+    all historical chunk scores reaches p, against the numpy evaluation."""
+    for cfg, tp in ((SMALL.with_(k=12), 0.3), (SMALL.with_(k=12, gate=1), 0.8),
+                    (SMALL_G1.with_(k=25), 0.55), (SMALL.with_(k=2), 0.95)):
+        inp = make_decode(cfg, seed=17)
+        r = oracle_decode(inp, top_p=tp)
+        o, l, s_ = brute_decode(inp, top_p=tp)
+        assert np.array_equal(r.sel, s_), (cfg.name, tp)
+        assert np.abs(r.out - o).max() < TOL and np.abs(r.lse - l).max() < TOL
+
+
+def pin_top_p_one_is_top_k():
+    cfg = SMALL.with_(k=7, gate=1)
+    inp = make_decode(cfg, seed=18)
+    a, b = oracle_decode(inp), oracle_decode(inp, top_p=1.0)
+    assert np.array_equal(a.sel, b.sel) and np.abs(a.out - b.out).max() == 0.0
+
+
+def pin_top_p_equal_scores_closed_form():
+    """All chunk scores equal: each chunk holds 1/|H| of the mass, so top-p keeps the
+    ceil(p |H|) lowest-index chunks (|H| = 21: p = 0.3 -> 7, p = 0.5 -> 11), capped at k;
+    a tiny p keeps exactly one chunk."""
+    cfg = SMALL.with_(B=1, k=30, N=22 * 8)
+    inp = make_decode(cfg, seed=19)
+    from dataclasses import replace
+    gk = inp.gist_k.clone()
+    gk[:] = gk[:, :, :1]
+    inp2 = replace(inp, gist_k=gk)
+    assert cfg.H == 21
+    for tp, want in ((0.3, 7), (0.5, 11), (1e-9, 1)):
+        r = oracle_decode(inp2, top_p=tp)
+        for kv in range(cfg.Hkv):
+            assert r.sel[0, kv].tolist() == list(range(want)) + [-1] * (cfg.k - want), (tp, kv)
+    r = oracle_decode(inp2, top_p=0.5, k=4)
+    assert r.sel[0, 0].tolist() == [0, 1, 2, 3]
+
+
+def pin_top_p_tiny_is_argmax():
+    cfg = SMALL.with_(k=5)
+    inp = make_decode(cfg, seed=20)
+    r = oracle_decode(inp, top_p=1e-12)
+    full = oracle_decode(inp, k=cfg.H)
+    for b in range(cfg.B):
+        for kv in range(cfg.Hkv):
+            sc = full.chunk_scores[b, kv]
+            best = int(np.argmax(sc))   # first maximum: lowest index on ties
+            assert r.sel[b, kv].tolist() == [best] + [-1] * (cfg.k - 1)
 
 
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]
