@@ -27,7 +27,7 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, vendor figure
 
 
-def decode_bytes(cfg, k=None, gist_mode="all"):
+def decode_bytes(cfg, k=None, gist_mode="all", k_eff_mean=None):
     """Algorithmic bytes of one decode call: every byte the method must touch, once.
     Gist rows scored (and attended), the selected chunks' K and V, the current chunk's K and
     V, q, out (fp32), and the page-table entries read.  gist_mode "selected": every gist key is
@@ -43,16 +43,18 @@ def decode_bytes(cfg, k=None, gist_mode="all"):
     else:
         gist_rows = cfg.H * cfg.g
         k_eff = min(k, cfg.H)
+    if k_eff_mean is not None:          # top-p: chunks actually kept, averaged over units
+        k_eff = k_eff_mean
     if gist_mode == "selected":
-        parts = {"gists_k": units * gist_rows * row, "selected_gists_v": units * k_eff * cfg.g * row}
+        parts = {"gists_k": units * gist_rows * row, "selected_gists_v": int(units * k_eff * cfg.g * row)}
     else:
         parts = {"gists_kv": units * gist_rows * row * 2}
     parts.update({
-        "selected_kv": units * k_eff * cfg.C * row * 2,
+        "selected_kv": int(units * k_eff * cfg.C * row * 2),
         "current_kv": units * cfg.cur_len * row * 2,
         "q": cfg.B * cfg.Hq * row,
         "out": cfg.B * cfg.Hq * cfg.d * 4,
-        "page_table": units * (k_eff + 1) * 4,
+        "page_table": int(units * (k_eff + 1) * 4),
     })
     return sum(parts.values()), parts
 
@@ -281,6 +283,8 @@ def main():
     ap.add_argument("--gist-mode", choices=["all", "selected"], default="all",
                     help="decode softmax set: every historical gist (default) or only the "
                          "selected chunks' gists")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="decode selection: 0 = top-k; in (0, 1] = top-p with a cap of k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -313,7 +317,8 @@ def main():
     print(f"# generating {R} instance(s) of {cfg.name}", file=sys.stderr, flush=True)
     insts = [make_decode(cfg, configs.seed_for(cfg.name, r), device=dev) for r in range(R)]
     gmode = ops.GISTS_SELECTED if args.gist_mode == "selected" else ops.GISTS_ALL
-    calls = [ops.DecodeCall(inp, with_scores=False, gist_mode=gmode) for inp in insts]
+    calls = [ops.DecodeCall(inp, with_scores=False, gist_mode=gmode, top_p=args.top_p)
+             for inp in insts]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
@@ -355,7 +360,11 @@ def main():
                 for j in range(nst)]
     print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
 
-    total_bytes, parts = decode_bytes(cfg, gist_mode=args.gist_mode)
+    k_eff_mean = None
+    if args.top_p > 0:   # chunks each unit kept, from the calls' own selections
+        import numpy as np
+        k_eff_mean = float(np.mean([(c.sel >= 0).sum(-1).float().mean().item() for c in calls]))
+    total_bytes, parts = decode_bytes(cfg, gist_mode=args.gist_mode, k_eff_mean=k_eff_mean)
     eff_gbps = total_bytes / (ms_per_step * 1e-3) / 1e9
     # dominant kernel: gist scoring (stage 1) -- the largest byte stream of the call
     gk_bytes = gist_kernel_bytes(cfg, args.gist_mode) if cfg.levels == 1 else None
@@ -388,9 +397,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "N": cfg.N, "C": cfg.C, "g": cfg.g, "k": cfg.k, "gate": "sas" if cfg.gate else
-                   "none", "levels": cfg.levels, "paged": cfg.paged, "gists": args.gist_mode, "inputs": "bf16",
+                   "none", "levels": cfg.levels, "paged": cfg.paged, "gists": args.gist_mode,
+                   "top_p": args.top_p or None, "inputs": "bf16",
                    "instances_rotated": R},
         "effective_GBps": round(eff_gbps, 1),
+        "chunks_selected_mean": k_eff_mean,
         "pct_of_hbm_peak": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_call": total_bytes,
         "event_ms_per_step": round(ev_ms / args.steps, 5),

@@ -26,6 +26,12 @@
  *   by the gists of the selected chunks only, each next to its chunk's raw tokens: the set
  *   section 3.3 describes, in which an unselected chunk contributes nothing.  The scores and
  *   the selection (steps 1-4) are unchanged.
+ *   top_p in (0, 1] (one level) replaces step 3: rank H as in step 3 and keep the shortest
+ *   ranked prefix whose shares p[c] = exp(s[c] - log sum_{c' in H} exp(s[c'])) add up to at
+ *   least top_p (top_p = 1 keeps every chunk), at most k of them, reported ascending.  The
+ *   pages compare against top-p (SSA figure 2) without spelling the rule out; this is the
+ *   reading used here.  The shares are summed in fp32 in rank order, so a selection may differ
+ *   from an exact evaluation when the running share crosses top_p within rounding.
  *   Two levels (levels = 2; section 3.5 and appendix B.2): level-2 gists summarise groups of J
  *   consecutive historical chunks.  The group scores s2[r] (step 2 over gist2_k) pick the top
  *   k2 groups; the member chunks of the chosen groups are the candidates; steps 1-3 run over
@@ -77,7 +83,8 @@
  *   no floating-point atomics; the same inputs give bitwise-identical outputs.
  *
  * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024;
- * B * Hkv <= 16384; TCS_GISTS_SELECTED: one level and C + g <= 1024; two levels:
+ * B * Hkv <= 16384; TCS_GISTS_SELECTED: one level and C + g <= 1024; top_p > 0: one level
+ * and k <= 256; two levels:
  * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk.
  * Other shapes return TCS_ERR_UNSUPPORTED.
  */
@@ -91,7 +98,7 @@
 extern "C" {
 #endif
 
-#define TCS_ABI_VERSION 2
+#define TCS_ABI_VERSION 3
 
 typedef enum {
     TCS_OK = 0,
@@ -121,6 +128,7 @@ typedef struct {
     int32_t num_pages;     /* pages in k_pages / v_pages                                  */
     int32_t gist_cap;      /* chunk capacity of gist_k/v per (b, kv); 0 means M-1          */
     float scale;           /* logit scale; 0 means 1/sqrt(d)                              */
+    float top_p;           /* 0: top-k.  In (0, 1]: top-p with a cap of k (one level)     */
 } tcs_decode_params;
 
 /* Host-only: bytes of workspace sparse_attn_decode needs for these parameters. */

@@ -51,6 +51,26 @@ def boundary_gap(scores: np.ndarray, k: int) -> float:
     return float((a - b) / max(abs(a), abs(b), 1.0))
 
 
+def top_p_margin(scores: np.ndarray, p: float, k: int) -> float:
+    """Distance of the running share from p at the top-p cut (fp64, rank order): the cut is a
+    floating-point decision, so a selection that differs only where the running share is
+    within GAP_EXCUSE of p is excused (and counted)."""
+    s = scores[np.isfinite(scores)]
+    if p >= 1.0 or len(s) == 0:
+        return float("inf")
+    order = np.lexsort((np.arange(len(s)), -s))
+    m = s.max()
+    share = np.exp(s[order] - (m + np.log(np.exp(s - m).sum())))
+    cum = np.cumsum(share)
+    r = int(np.argmax(cum >= p)) if (cum >= p).any() else len(s) - 1
+    if r >= k:
+        return float("inf")   # the cap decided, not the share
+    near = [abs(cum[r] - p)]
+    if r > 0:
+        near.append(abs(cum[r - 1] - p))
+    return float(min(near))
+
+
 def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, report=None):
     """Compare one finished GPU decode call with the oracle.  Returns a dict of statistics.
     Selected indices must match exactly except where the oracle's boundary gap is below
@@ -59,9 +79,10 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
     c = inp.cfg
     G = c.G
     gmode = "selected" if getattr(call, "gist_mode", 0) == 1 else True
+    top_p = float(call.p.top_p)
     if ref is None:
         ref = oracle_decode(inp, k=call.p.k, units=units, scale=float(call.p.scale),
-                            gists_in_softmax=gmode)
+                            gists_in_softmax=gmode, top_p=top_p)
     all_units = list(range(c.B * c.Hkv)) if units is None else list(units)
     gsel = call.sel.cpu().numpy()
     gout = call.out.cpu().double().numpy()
@@ -79,7 +100,12 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
         gaps = []
         if c.levels == 2:
             gaps.append(boundary_gap(ref.group_scores[b, kv], c.k2))
-        gaps.append(boundary_gap(ref.chunk_scores[b, kv], k))
+        if top_p > 0:
+            ke_ref = int((ref.sel[b, kv] >= 0).sum())
+            gaps.append(boundary_gap(ref.chunk_scores[b, kv], ke_ref))
+            gaps.append(top_p_margin(ref.chunk_scores[b, kv], top_p, k))
+        else:
+            gaps.append(boundary_gap(ref.chunk_scores[b, kv], k))
         assert min(gaps) < GAP_EXCUSE, (
             f"unit {u}: selection differs (gpu {gsel[b, kv].tolist()} vs oracle "
             f"{ref.sel[b, kv].tolist()}) with boundary gap {min(gaps):.3g}")

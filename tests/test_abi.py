@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ops.lib().tcs_abi_version() == 2
+    assert ops.lib().tcs_abi_version() == 3
     for code in range(6):
         assert ops.status_str(code)
     assert ops.status_str(99) == "unknown status"
@@ -80,6 +80,11 @@ def test_workspace_size_grows_with_work():
     (dict(num_pages=0), ops.TCS_ERR_SHAPE),
     (dict(B=4097, Hkv=4, Hq=16), ops.TCS_ERR_UNSUPPORTED),   # 16388 units
     (dict(gist_mode=2), ops.TCS_ERR_SHAPE),
+    (dict(top_p=-0.1), ops.TCS_ERR_SHAPE),
+    (dict(top_p=1.5), ops.TCS_ERR_SHAPE),
+    (dict(top_p=float("nan")), ops.TCS_ERR_SHAPE),
+    (dict(top_p=0.5, levels=2, J=4, k2=2), ops.TCS_ERR_UNSUPPORTED),
+    (dict(top_p=0.5, k=257), ops.TCS_ERR_UNSUPPORTED),
     (dict(gist_mode=1, levels=2, J=4, k2=2), ops.TCS_ERR_UNSUPPORTED),
     (dict(gist_mode=1, C_=1024, g=8, N=5000), ops.TCS_ERR_UNSUPPORTED),  # C + g > 1024
 ])

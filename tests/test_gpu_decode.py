@@ -24,12 +24,12 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_case(cfg, seed, units=None, gist_mode=0, **kw):
+def run_case(cfg, seed, units=None, gist_mode=0, top_p=0.0, **kw):
     say(f"[decode] {cfg.name} seed={seed} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} "
         f"N={cfg.N} C={cfg.C} g={cfg.g} k={cfg.k} gate={cfg.gate} levels={cfg.levels} "
-        f"gist_mode={gist_mode} {kw}")
+        f"gist_mode={gist_mode} top_p={top_p} {kw}")
     inp = make_decode(cfg, seed, device=DEV, **kw)
-    call = DecodeCall(inp, gist_mode=gist_mode)()
+    call = DecodeCall(inp, gist_mode=gist_mode, top_p=top_p)()
     torch.cuda.synchronize()
     st = check_decode(inp, call, units=units)
     say("   ", st)
@@ -90,6 +90,32 @@ def test_selected_gists_variants(cfg):
 def test_selected_gists_full(name):
     cfg = configs.DECODE_CONFIGS[name]
     inp, call, st = run_case(cfg, configs.seed_for(name), gist_mode=1)
+    assert st["excused"] <= max(1, st["units"] // 100)
+    del inp, call
+    torch.cuda.empty_cache()
+
+
+# Top-p selection with a cap of k chunks (one level).
+TOP_P = [
+    (SMALL.with_(k=20), 0.3),
+    (SMALL.with_(k=20, gate=1), 0.8),
+    (SMALL.with_(k=20, gate=1, d=64, Hq=16), 0.95),
+    (SMALL.with_(k=3), 0.9),                         # the cap decides
+    (SMALL.with_(k=40, gate=1), 1.0),                # every chunk
+    (SMALL.with_(k=20, g=1, C=64, N=300 * 64), 0.5),
+    (SMALL.with_(k=20), 1e-6),                       # the best chunk only
+]
+
+
+@pytest.mark.parametrize("cfg,tp", TOP_P, ids=[f"tp{i}" for i in range(len(TOP_P))])
+def test_top_p_variants(cfg, tp):
+    run_case(cfg, seed=400 + [c for c, _ in TOP_P].index(cfg), top_p=tp)
+
+
+@pytest.mark.parametrize("name,tp", [("llama32_1b_decode_32k", 0.9), ("llama31_8b_decode_128k", 0.5)])
+def test_top_p_full(name, tp):
+    cfg = configs.DECODE_CONFIGS[name]
+    inp, call, st = run_case(cfg, configs.seed_for(name), top_p=tp)
     assert st["excused"] <= max(1, st["units"] // 100)
     del inp, call
     torch.cuda.empty_cache()

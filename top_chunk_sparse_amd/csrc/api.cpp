@@ -35,6 +35,7 @@ constexpr int kTargetWorkgroups = TCS_TARGET_WORKGROUPS;   // grid size the pass
 #define TCS_CHUNK_TARGET_WORKGROUPS 1024
 #endif
 constexpr int kChunkTargetWorkgroups = TCS_CHUNK_TARGET_WORKGROUPS;   // chunk-attention grid
+constexpr int kMaxTopPK = 256;   // top-p: the capped top-k is ranked in one workgroup's LDS
 constexpr int kMinSliceRows = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -76,6 +77,7 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (p->gate_mode != TCS_GATE_NONE && p->gate_mode != TCS_GATE_SAS) return TCS_ERR_SHAPE;
     if (p->gist_mode != TCS_GISTS_ALL && p->gist_mode != TCS_GISTS_SELECTED) return TCS_ERR_SHAPE;
     if (!(p->scale >= 0.f) || std::isinf(p->scale)) return TCS_ERR_SHAPE;
+    if (!(p->top_p >= 0.f && p->top_p <= 1.f)) return TCS_ERR_SHAPE;
     const int G = p->Hq / p->Hkv;
     const long long units = (long long)p->B * p->Hkv;
     const int M = (int)(((long long)p->N + p->C - 1) / p->C);
@@ -88,6 +90,7 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (p->g > 64 || p->C > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
     const bool sel_gists = p->gist_mode == TCS_GISTS_SELECTED;
     if (sel_gists && (p->levels != 1 || p->C + p->g > kMaxSliceRows)) return TCS_ERR_UNSUPPORTED;
+    if (p->top_p > 0.f && (p->levels != 1 || p->k > kMaxTopPK)) return TCS_ERR_UNSUPPORTED;
     pl->G = G;
     pl->M = M;
     pl->H = H;
@@ -266,7 +269,9 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     bool chunks_chosen = false;
     if (p->levels == 1) {
         chunk_sel.gamma = gamma;
-        chunk_sel.slice_lse = gamma ? (float*)(ws + pl.off_lse1) : nullptr;
+        // the log-sum-exp over every historical score: for the gate and for top-p's shares
+        chunk_sel.slice_lse = (gamma || p->top_p > 0.f) ? (float*)(ws + pl.off_lse1) : nullptr;
+        chunk_sel.top_p = p->top_p;
         chunk_sel.counter = cnt;
         ga.gk = (const uint16_t*)gist_k;
         ga.gv = (const uint16_t*)gist_v;

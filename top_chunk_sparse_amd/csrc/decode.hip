@@ -237,10 +237,19 @@ struct MergeCand {
     int32_t idx[256];
 };
 
+static_assert(kMaxSliceRows * sizeof(float) >= 4 * 256 * 4, "top-p staging fits the slice scores");
+
+struct TopPSmem {             // the capped top-k of one unit, for the top-p cut (4 KB)
+    float score[256];
+    int32_t idx[256];
+    float share[256];         // by rank
+    int rank[256];            // by position
+};
+
 __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
                                 const float* s_score, int item0, int nitems, int last_items,
                                 float* lse_part_lds, void* scratch, MergeCand& mc, int* s_flag,
-                                int* s_chosen, ReduceSmem& red) {
+                                int* s_chosen, ReduceSmem& red, TopPSmem& tps, int* s_keep) {
     const int tid = threadIdx.x;
     const int kc = so.k < nitems ? so.k : nitems;
     float* cs = so.cand_score + ((long long)u * nslices + slot) * so.kcap;
@@ -280,17 +289,17 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
     // one round trip for every hand-off value this workgroup needs
     const float* sl = so.slice_lse ? so.slice_lse + (long long)u * nslices * 2 : nullptr;
     float* st = reinterpret_cast<float*>(scratch);     // slice statistics, if they fit
-    const bool gate = sl && so.gamma;
+    const bool need_lse = sl != nullptr;   // gate, or top-p shares
     const bool lse_staged = 2 * nslices <= kTopkCache;
     if (staged && tid < ncand) {
         mc.score[tid] = ld_shared_dev(ucs + tid);
         mc.idx[tid] = ld_shared_dev(uci + tid);
     }
-    if (gate && lse_staged)
+    if (need_lse && lse_staged)
         for (int i = tid; i < 2 * nslices; i += 256) st[i] = ld_shared_dev(sl + i);
     __syncthreads();
     float lse = 0.f;
-    if (gate) {
+    if (need_lse) {
         auto at = [&](int i) { return lse_staged ? st[i] : ld_shared_dev(sl + i); };
         if (tid == 0) {
             float mx = -INFINITY;
@@ -305,8 +314,14 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
     int32_t* sel = so.sel + (long long)u * so.k;
     float* gam = so.gamma ? so.gamma + (long long)u * so.k : nullptr;
     auto score_at = [&](int i) { return staged ? mc.score[i] : ld_shared_dev(ucs + i); };
+    const bool top_p = so.top_p > 0.f;
     auto emit2 = [&](int j, int i) {
         const int32_t c = staged ? mc.idx[i] : ld_shared_dev(uci + i);
+        if (top_p) {   // held back for the cut below (j < k <= 256)
+            tps.idx[j] = c;
+            tps.score[j] = score_at(i);
+            return;
+        }
         sel[j] = c;
         if (gam) gam[j] = score_at(i) - lse;
         if (j < 64) s_chosen[j] = c;
@@ -319,6 +334,43 @@ __device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslice
         ke = small_topk(ncand, so.k, score_at, emit2, *reinterpret_cast<SmallTopkSmem*>(scratch));
     } else {
         ke = block_topk(ncand, so.k, score_at, emit2, *reinterpret_cast<TopkSmem*>(scratch));
+    }
+    if (top_p) {
+        // The capped top-k (ascending chunk id in tps) is ranked by (score desc, id asc); the
+        // shares exp(s - lse) are summed in rank order and the shortest prefix reaching top_p
+        // is kept (all of it for top_p = 1), written ascending by chunk id.
+        __syncthreads();
+        int rank = 0;
+        if (tid < ke) {
+            const float sj = tps.score[tid];
+            for (int i = 0; i < ke; ++i) {
+                const float si = tps.score[i];
+                rank += (si > sj) || (si == sj && i < tid);
+            }
+            tps.share[rank] = expf(sj - lse);
+            tps.rank[tid] = rank;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int keep = ke;
+            if (so.top_p < 1.f) {
+                float mass = 0.f;
+                for (int r = 0; r < ke; ++r) {
+                    mass += tps.share[r];
+                    if (mass >= so.top_p) { keep = r + 1; break; }
+                }
+            }
+            *s_keep = keep;
+        }
+        __syncthreads();
+        const int keep = *s_keep;
+        if (tid < ke && rank < keep) {
+            int pos = 0;   // kept entries before this one in chunk-id order
+            for (int i = 0; i < tid; ++i) pos += tps.rank[i] < keep;
+            sel[pos] = tps.idx[tid];
+            if (gam) gam[pos] = tps.score[tid] - lse;
+        }
+        ke = keep;
     }
     for (int j = ke + tid; j < so.k; j += 256) {
         sel[j] = -1;
@@ -350,13 +402,14 @@ struct GistSmem {
         TopkSmem topk;
         SmallTopkSmem small;
     } x;
-    float score[kMaxSliceRows];
+    float score[kMaxSliceRows];   // also the top-p staging of the last workgroup
     MergeCand mc;
     HeadStatsSmem<G> hs;
     ReduceSmem red;
     float lse;
     int flag;
     int chosen[64];
+    int tp_keep;
 };
 
 template <int D, int G>
@@ -413,7 +466,10 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
     }
     __syncthreads();
     select_epilogue(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.lse, &sm.x,
-                    sm.mc, &sm.flag, sm.chosen, sm.red);
+                    sm.mc, &sm.flag, sm.chosen, sm.red,
+                    // the slice scores are dead once the slice's list is out: the unit's
+                    // top-p cut reuses their space
+                    *reinterpret_cast<TopPSmem*>(sm.score), &sm.tp_keep);
 }
 
 // ---------------------------------------------------------------------------------------

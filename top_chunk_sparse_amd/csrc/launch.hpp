@@ -25,6 +25,7 @@ struct SelectOut {
     unsigned* counter;        // [units], zero between calls
     float* fill_scores;       // optional [units][H]: -inf outside the chosen groups (level 2)
     int J, H;
+    float top_p;              // > 0: keep the shortest ranked prefix with this share (k <= 256)
 };
 
 struct GistLaunch {

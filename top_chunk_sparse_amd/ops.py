@@ -26,7 +26,8 @@ class DecodeParams(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("struct_size", "B", "Hq", "Hkv", "d", "N", "C", "g",
                                          "k", "gate_mode", "gist_mode", "levels", "J", "k2",
                                          "max_chunks",
-                                         "num_pages", "gist_cap")] + [("scale", C.c_float)]
+                                         "num_pages", "gist_cap")] + [("scale", C.c_float),
+                                                                      ("top_p", C.c_float)]
 
 
 class PrefillParams(C.Structure):
@@ -82,12 +83,13 @@ GISTS_ALL, GISTS_SELECTED = 0, 1   # TCS_GISTS_*
 
 
 def decode_params(*, B, Hq, Hkv, d, N, C_, g, k, gate=0, levels=1, J=0, k2=0, max_chunks=None,
-                  num_pages, gist_cap=0, scale=0.0, gist_mode=GISTS_ALL) -> DecodeParams:
+                  num_pages, gist_cap=0, scale=0.0, gist_mode=GISTS_ALL,
+                  top_p=0.0) -> DecodeParams:
     M = -(-N // C_) if C_ > 0 else 1
     return DecodeParams(struct_size=C.sizeof(DecodeParams), B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, C=C_,
                         g=g, k=k, gate_mode=gate, gist_mode=gist_mode, levels=levels, J=J, k2=k2,
                         max_chunks=M if max_chunks is None else max_chunks,
-                        num_pages=num_pages, gist_cap=gist_cap, scale=scale)
+                        num_pages=num_pages, gist_cap=gist_cap, scale=scale, top_p=top_p)
 
 
 def decode_workspace_size(p: DecodeParams) -> int:
@@ -158,7 +160,8 @@ def workspace(nbytes: int, device, stream=None) -> torch.Tensor:
 class DecodeCall:
     """Outputs and workspace for repeated decode calls on one input bundle."""
 
-    def __init__(self, inp, with_scores=True, k=None, scale=0.0, gist_mode=GISTS_ALL):
+    def __init__(self, inp, with_scores=True, k=None, scale=0.0, gist_mode=GISTS_ALL,
+                 top_p=0.0):
         c = inp.cfg
         dev = inp.q.device
         self.inp = inp
@@ -167,7 +170,7 @@ class DecodeCall:
                                k=c.k if k is None else k, gate=c.gate, levels=c.levels, J=c.J,
                                k2=c.k2, max_chunks=inp.page_table.shape[1],
                                num_pages=inp.num_pages, gist_cap=inp.gist_k.shape[2],
-                               scale=scale, gist_mode=gist_mode)
+                               scale=scale, gist_mode=gist_mode, top_p=top_p)
         kk = self.p.k
         self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
