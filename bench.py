@@ -283,6 +283,10 @@ def main():
     ap.add_argument("--gist-mode", choices=["all", "selected"], default="all",
                     help="decode softmax set: every historical gist (default) or only the "
                          "selected chunks' gists")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="decode: override the workload's context length N (tokens)")
+    ap.add_argument("--k", type=int, default=-1,
+                    help="decode: override k (a value >= the chunk count selects every chunk)")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="decode selection: 0 = top-k; in (0, 1] = top-p with a cap of k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -311,6 +315,10 @@ def main():
     if args.workload in configs.PREFILL_CONFIGS:
         return run_prefill(args, torch, configs, ops)
     cfg = configs.DECODE_CONFIGS[args.workload]
+    if args.tokens > 0:
+        cfg = cfg.with_(N=args.tokens)
+    if args.k >= 0:
+        cfg = cfg.with_(k=args.k)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     R = max(1, args.instances)
@@ -395,7 +403,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
+        "config": {"workload": cfg.name + ("" if args.tokens <= 0 and args.k < 0 else
+                                           f"@N={cfg.N},k={cfg.k}"),
+                   "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "N": cfg.N, "C": cfg.C, "g": cfg.g, "k": cfg.k, "gate": "sas" if cfg.gate else
                    "none", "levels": cfg.levels, "paged": cfg.paged, "gists": args.gist_mode,
                    "top_p": args.top_p or None, "inputs": "bf16",
