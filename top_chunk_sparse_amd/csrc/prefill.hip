@@ -266,6 +266,11 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
     const int g = lane >> 4, L = lane & 15, rr = L >> 2, cc = L & 3;
     const int voff = (4 * h + rr) * 64 + (((2 * (g & 1) + (cc >> 1)) ^ swz_v(rr)) << 4) + ((cc & 1) << 3);
 
+    // The query operands must have landed before the loop: otherwise the compiler's wait
+    // counting at the loop head cannot tell them from the next block's loads and makes every
+    // iteration's first products wait for that block's global loads.
+    wait_vmem();
+
     const float cs = a.sigma * kLog2e;
     f32x16 o[4];
 #pragma unroll
