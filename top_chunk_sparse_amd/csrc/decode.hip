@@ -30,10 +30,10 @@ constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for empty softm
 constexpr int kMaxSliceRows = 1024;   // rows (gists, or page rows) one workgroup holds logits for
 
 #ifndef TCS_K_U
-#define TCS_K_U 4       // row passes per batch of loads in the K phase
+#define TCS_K_U 2       // row passes per batch of loads in the K phase (two batches in flight)
 #endif
 #ifndef TCS_V_U
-#define TCS_V_U 4       // row passes per batch of loads in the V phase
+#define TCS_V_U 2       // row passes per batch of loads in the V phase (two batches in flight)
 #endif
 #ifndef TCS_CK_U
 #define TCS_CK_U TCS_K_U   // the same, for the chunk kernel's K phase
@@ -75,17 +75,53 @@ struct RowStream {
         }
     }
 
+    // Streams rows [0, nrows) in batches of U passes through two register buffers: the next
+    // batch's loads are issued before the current batch is used, so a batch is always in
+    // flight while the workgroup computes.
+    // Rows past the end re-read the last row (their results are discarded): unconditional
+    // loads keep the wait counts exact, so waiting for one buffer leaves the other in flight.
+    template <int U>
+    __device__ __forceinline__ void load_batch(const uint16_t* __restrict__ X, int nrows, int base,
+                                               uint4 (&r)[U]) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int row = min(base + u * RPP + lrow, nrows - 1);
+            r[u] = ld16(X + (long long)row * D + part * 8);
+        }
+    }
+
+    // The first batch of rows, issued early (pre = true in the streaming call that follows).
+    template <int U>
+    __device__ __forceinline__ void prefetch(const uint16_t* __restrict__ X, int nrows,
+                                             uint4 (&r)[U]) const {
+        if (nrows > 0) load_batch<U>(X, nrows, 0, r);
+    }
+
+    template <int U, class Use>
+    __device__ __forceinline__ void stream_rows(const uint16_t* __restrict__ X, int nrows,
+                                                Use use, uint4 (&ra)[U], bool pre) const {
+        constexpr int STEP = U * RPP;
+        uint4 rb[U];
+        auto load = [&](uint4 (&r)[U], int base) __attribute__((always_inline)) {
+            load_batch<U>(X, nrows, base, r);
+        };
+        if (nrows <= 0) return;
+        if (!pre) load(ra, 0);
+        for (int base = 0; base < nrows; base += 2 * STEP) {
+            if (base + STEP < nrows) load(rb, base + STEP);
+            use(ra, base);
+            if (base + STEP >= nrows) break;
+            if (base + 2 * STEP < nrows) load(ra, base + 2 * STEP);
+            use(rb, base + STEP);
+        }
+    }
+
     // K phase: lg[(row0 + r) * G + h] = sigma * q_h . K[r] + bias for rows r < nrows.
     template <int U>
-    __device__ void logits(const uint32_t (&q2)[G][4], const uint16_t* __restrict__ K, int nrows,
+    __device__ __forceinline__ void logits(const uint32_t (&q2)[G][4], const uint16_t* __restrict__ K, int nrows,
                            float sigma, float bias, float* lg, int row0) const {
-        for (int base = 0; base < nrows; base += U * RPP) {
-            uint4 kr[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = base + u * RPP + lrow;
-                kr[u] = row < nrows ? ld16(K + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
-            }
+        uint4 ra[U];
+        stream_rows<U>(K, nrows, [&](const uint4 (&kr)[U], int base) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int row = base + u * RPP + lrow;
@@ -99,20 +135,16 @@ struct RowStream {
                     if (part == 0 && row < nrows) lg[(row0 + row) * G + h] = fmaf(s, sigma, bias);
                 }
             }
-        }
+        }, ra, false);
     }
 
     // V phase: acc[h][e] += w[(row0 + r) * G + h] * V[r][part*8 + e] for rows r < nrows.
+    // pre: the first batch is already in `first` (prefetch); else `first` is scratch space.
     template <int U>
-    __device__ void accumulate(float (&acc)[G][8], const uint16_t* __restrict__ V, int nrows,
-                               const float* w, int row0) const {
-        for (int base = 0; base < nrows; base += U * RPP) {
-            uint4 vr[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = base + u * RPP + lrow;
-                vr[u] = row < nrows ? ld16(V + (long long)row * D + part * 8) : make_uint4(0, 0, 0, 0);
-            }
+    __device__ __forceinline__ void accumulate(float (&acc)[G][8], const uint16_t* __restrict__ V,
+                                               int nrows, const float* w, int row0,
+                                               uint4 (&first)[U], bool pre = false) const {
+        stream_rows<U>(V, nrows, [&](const uint4 (&vr)[U], int base) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int row = base + u * RPP + lrow;
@@ -128,7 +160,7 @@ struct RowStream {
                     }
                 }
             }
-        }
+        }, first, pre);
     }
 
     // Sum the lane groups' accumulators and write one partial per head:
@@ -246,7 +278,7 @@ struct TopPSmem {             // the capped top-k of one unit, for the top-p cut
     int rank[256];            // by position
 };
 
-__device__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
+__device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
                                 const float* s_score, int item0, int nitems, int last_items,
                                 float* lse_part_lds, void* scratch, MergeCand& mc, int* s_flag,
                                 int* s_chosen, ReduceSmem& red, TopPSmem& tps, int* s_keep) {
@@ -413,10 +445,8 @@ struct GistSmem {
 };
 
 template <int D, int G>
-__global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
+__device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& sm, int y, int u) {
     using RS = RowStream<D, G>;
-    __shared__ GistSmem<D, G> sm;
-    const int y = blockIdx.x, u = blockIdx.y;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
     int c0, c1, last_items;
@@ -441,6 +471,9 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
         rs.load_q(a.q + (long long)bh0 * D, q2);
         rs.template logits<TCS_K_U>(q2, K, nrows, a.sigma, 0.f, sm.x.lg, 0);
     }
+    // the first V batch travels while the scores and the softmax statistics are computed
+    uint4 vfirst[TCS_V_U];
+    if (!a.scores_only) rs.template prefetch<TCS_V_U>(V, nrows, vfirst);
     __syncthreads();
     // pooled item scores: log-sum-exp over the G heads and g gists of each item
     for (int c = threadIdx.x; c < nit; c += 256) {
@@ -460,7 +493,7 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        rs.template accumulate<TCS_V_U>(acc, V, nrows, sm.x.lg, 0);
+        rs.template accumulate<TCS_V_U>(acc, V, nrows, sm.x.lg, 0, vfirst, true);
         __syncthreads();   // weights dead: fin may reuse the space
         rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
     }
@@ -470,6 +503,12 @@ __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
                     // the slice scores are dead once the slice's list is out: the unit's
                     // top-p cut reuses their space
                     *reinterpret_cast<TopPSmem*>(sm.score), &sm.tp_keep);
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
+    __shared__ GistSmem<D, G> sm;
+    gist_item<D, G>(a, sm, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -486,12 +525,14 @@ struct MergeSmem {
 };
 
 template <int D, int G>
-__device__ void merge_partials(const Partials& P, int bh0, float* out, float* lse,
+__device__ __forceinline__ void merge_partials(const Partials& P, int bh0, float* out, float* lse,
                                MergeSmem<G>& sm) {
     const int ns = P.nslots;
     const int tid = threadIdx.x;
     constexpr int PPT = (G * D + 255) / 256;   // (head, column) outputs per thread
-    constexpr int SB = 32 / PPT;               // slots whose values one batch holds
+    // slots whose values one batch holds: the unit's whole set in one round trip for the
+    // usual slot counts (up to 24 for G = 4, d = 128)
+    constexpr int SB = 48 / PPT < 32 ? 48 / PPT : 32;
     const bool staged = G * ns <= kMergeStage;
     float v[PPT][SB];
     auto load_batch = [&](int s0) {
@@ -523,13 +564,20 @@ __device__ void merge_partials(const Partials& P, int bh0, float* out, float* ls
         return staged ? sm.l[h * ns + s]
                       : ld_shared_dev(P.ml + ((long long)(bh0 + h) * ns + s) * 2 + 1);
     };
-    if (tid < G) {
-        float mx = kNegBig;
-        for (int s = 0; s < ns; ++s) mx = fmaxf(mx, m_at(tid, s));
-        float L = 0.f;
-        for (int s = 0; s < ns; ++s) L += __expf(m_at(tid, s) - mx) * l_at(tid, s);
-        sm.M[tid] = mx;
-        sm.L[tid] = L;
+    {   // per head: M = max of the slots' m, L = sum of exp(m - M) l; one wave per head
+        const int lane = tid & 63;
+        for (int h = tid >> 6; h < G; h += 4) {
+            float mx = kNegBig;
+            for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, m_at(h, s));
+            mx = wave_max(mx);
+            float L = 0.f;
+            for (int s = lane; s < ns; s += 64) L += __expf(m_at(h, s) - mx) * l_at(h, s);
+            L = wave_sum(L);
+            if (lane == 0) {
+                sm.M[h] = mx;
+                sm.L[h] = L;
+            }
+        }
     }
     __syncthreads();
     if (staged) {
@@ -591,11 +639,11 @@ struct ChunkSmem {
     int flag;
 };
 
+// Workgroup wx of unit u (nwx workgroups per unit).
 template <int D, int G>
-__global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
+__device__ __forceinline__ void chunk_item(const ChunkLaunch& a, ChunkSmem<D, G>& sm, int wx,
+                                           int u, int nwx) {
     using RS = RowStream<D, G>;
-    __shared__ ChunkSmem<D, G> sm;
-    const int wx = blockIdx.x, u = blockIdx.y;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
     const int j0 = wx * a.cpw, nj = min(a.cpw, a.kslots + 1 - j0);
@@ -653,6 +701,12 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
                         a.g, a.sigma, 0.f, sm.x.lg, graw + jj * a.g);
             }
         }
+        // the first slot's first V batch travels while the softmax statistics are computed
+        int jfirst = 0;
+        while (sm.page[jfirst] < 0) ++jfirst;   // `any` holds: some slot has a page
+        uint4 vb[TCS_CV_U];
+        rs.template prefetch<TCS_CV_U>(
+            a.vp + ((long long)sm.page[jfirst] * a.Hkv + kv) * a.C * D, sm.rows[jfirst], vb);
         __syncthreads();
         head_stats<G>(sm.x.lg, nrows_all, sm.hs);
         float acc[G][8];
@@ -660,20 +714,27 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        for (int jj = 0; jj < nj; ++jj) {
+        for (int jj = jfirst; jj < nj; ++jj) {
             if (sm.page[jj] < 0) continue;
             const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
-            rs.template accumulate<TCS_CV_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, jj * a.C);
+            rs.template accumulate<TCS_CV_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, jj * a.C, vb,
+                                             jj == jfirst);
             if (a.gk && sm.chunk[jj] >= 0)
                 rs.template accumulate<TCS_CV_U>(
                     acc, a.gv + (long long)u * a.gist_stride + (long long)sm.chunk[jj] * a.g * D,
-                    a.g, sm.x.lg, graw + jj * a.g);
+                    a.g, sm.x.lg, graw + jj * a.g, vb);
         }
         __syncthreads();
         rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + wx);
     }
-    if (!arrive_last(a.counter + u, (unsigned)gridDim.x, &sm.flag)) return;
+    if (!arrive_last(a.counter + u, (unsigned)nwx, &sm.flag)) return;
     merge_partials<D, G>(a.part, bh0, a.out, a.lse, sm.x.merge);
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(256) chunk_kernel(ChunkLaunch a) {
+    __shared__ ChunkSmem<D, G> sm;
+    chunk_item<D, G>(a, sm, blockIdx.x, blockIdx.y, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -81,15 +81,27 @@ __device__ __forceinline__ int block_exclusive_scan(int v, ScanSmem& sm) {
 
 struct ReduceSmem { float v[4]; };
 
+// Whole-wave reductions: DPP steps within each 16-lane row (every lane of a row ends with
+// the same bits: each step combines a lane with its partner, a commutative pair), then the
+// four rows' values are read with readlane and combined in a fixed order.  All 64 lanes must
+// be active.
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    x = fmaxf(x, dpp<0x140>(x));
+    return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)),
+                 fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
 // Fixed-order block reductions (deterministic).  Every thread gets the result.
 __device__ __forceinline__ float block_max(float x, ReduceSmem& sm) {
