@@ -170,11 +170,9 @@ struct RowStream {
                            const Partials& P, int bh0, int slot) const {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-        for (int off = LPR; off < kWave; off <<= 1)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+            for (int e = 0; e < 8; ++e) acc[h][e] = lane_groups_sum<LPR>(acc[h][e]);
         if (lane < LPR) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
@@ -428,7 +426,7 @@ __device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int 
 // ---------------------------------------------------------------------------------------
 template <int D, int G>
 struct GistSmem {
-    union {
+    union alignas(16) {   // 16-byte aligned: the score pooling reads logits as float4
         float lg[kMaxSliceRows * G];                   // logits, then softmax weights
         float fin[RowStream<D, G>::NW * G * D];
         TopkSmem topk;
@@ -476,12 +474,28 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
     if (!a.scores_only) rs.template prefetch<TCS_V_U>(V, nrows, vfirst);
     __syncthreads();
     // pooled item scores: log-sum-exp over the G heads and g gists of each item
+    const int ng = a.g * G;   // logits per item
     for (int c = threadIdx.x; c < nit; c += 256) {
-        const float* x = sm.x.lg + c * a.g * G;
-        float mx = -INFINITY;
-        for (int i = 0; i < a.g * G; ++i) mx = fmaxf(mx, x[i]);
-        float z = 0.f;
-        for (int i = 0; i < a.g * G; ++i) z += expf(x[i] - mx);
+        const float* x = sm.x.lg + c * ng;
+        float mx = -INFINITY, z = 0.f;
+        if (ng % 4 == 0) {   // 16-byte LDS reads, several in flight; same summation order
+#pragma unroll 4
+            for (int i = 0; i < ng; i += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(x + i);
+                mx = fmaxf(fmaxf(mx, fmaxf(v.x, v.y)), fmaxf(v.z, v.w));
+            }
+#pragma unroll 4
+            for (int i = 0; i < ng; i += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(x + i);
+                z += expf(v.x - mx);
+                z += expf(v.y - mx);
+                z += expf(v.z - mx);
+                z += expf(v.w - mx);
+            }
+        } else {
+            for (int i = 0; i < ng; ++i) mx = fmaxf(mx, x[i]);
+            for (int i = 0; i < ng; ++i) z += expf(x[i] - mx);
+        }
         const float s = mx + logf(z);
         sm.score[c] = s;
         if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;

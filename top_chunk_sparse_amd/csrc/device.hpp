@@ -52,6 +52,20 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Sum over the lanes l, l + LPR, l + 2 LPR, ... of a wave (the same position in every
+// LPR-lane group); every such lane receives the same bits.  Steps: lanes l ^ 8 (LPR = 8;
+// DPP row_ror:8 swaps the halves of a 16-lane row), then l ^ 16 and l ^ 32 (v_permlane16_swap
+// and v_permlane32_swap, whose two results are the lower lane's value, then the upper one's).
+template <int LPR>
+__device__ __forceinline__ float lane_groups_sum(float x) {
+    static_assert(LPR == 8 || LPR == 16, "LPR");
+    if constexpr (LPR == 8) x += dpp<0x128>(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---- ordered keys -----------------------------------------------------------------------
 // Monotone map fp32 -> uint32 (a < b  <=>  key(a) < key(b)); -0 is folded onto +0.
 __device__ __forceinline__ uint32_t ordered_key(float x) {
