@@ -419,13 +419,11 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s) {
     const long long W = 2LL * a.B * a.Hkv * (a.T / kPBlk) * ((G + 3) / 4);
     if (W <= 0) return hipSuccess;
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_fwd_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kPLdsAll);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // the dynamic LDS (tiles + ring) is above the 64 KB default limit; set on every call (no
+    // library state, and it holds for whichever device is current)
+    const hipError_t e = hipFuncSetAttribute((const void*)prefill_fwd_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kPLdsAll);
+    if (e != hipSuccess) return e;
     prefill_fwd_kernel<<<(unsigned)W, 256, kPLdsAll, s>>>(a);
     return hipGetLastError();
 }
