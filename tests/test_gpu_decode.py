@@ -121,6 +121,34 @@ def test_top_p_full(name, tp):
     torch.cuda.empty_cache()
 
 
+# The largest documented shapes: C = 1024 rows per chunk with g = 64 gists; C + g = 1024 for the
+# selected-gist set; k = 256 for top-p; B * Hkv = 16384 units.
+LIMITS = [
+    (SMALL.with_(C=1024, g=64, d=64, N=9 * 1024 + 300, k=3, n_plant=2), 0, 0.0),
+    (SMALL.with_(C=1024, g=8, N=5 * 1024 + 1, k=2, gate=1, n_plant=2), 0, 0.0),
+    (SMALL.with_(C=960, g=64, d=64, N=7 * 960 + 5, k=2, n_plant=2), 1, 0.0),
+    (SMALL.with_(C=16, g=1, d=64, N=300 * 16 + 3, k=256, n_plant=4, gate=1), 0, 0.95),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(LIMITS)), ids=[f"lim{i}" for i in range(len(LIMITS))])
+def test_limit_shapes(idx):
+    cfg, gmode, tp = LIMITS[idx]
+    run_case(cfg, seed=500 + idx, gist_mode=gmode, top_p=tp)
+
+
+def test_max_units():
+    cfg = DecodeConfig("max_units", B=2048, Hq=16, Hkv=8, d=64, N=100, C=16, g=2, k=3,
+                       n_plant=1, paged=True)
+    rng = np.random.default_rng(0)
+    n = cfg.B * cfg.Hkv   # 16384, the most one call takes
+    units = sorted(set(rng.choice(n, 384, replace=False).tolist()) | {0, n - 1})
+    inp, call, st = run_case(cfg, seed=600, units=units)
+    assert st["units"] == len(units)
+    del inp, call
+    torch.cuda.empty_cache()
+
+
 def test_deterministic_bitwise():
     cfg = configs.LLAMA1B
     inp = make_decode(cfg, 7, device=DEV)
