@@ -61,6 +61,20 @@ def test_prefill_full_size_sampled():
     torch.cuda.empty_cache()
 
 
+def test_prefill_long_block_lists():
+    # more than 128 chosen blocks per query block: the kernel's block-list ring (128 entries) is
+    # refilled while it runs; sampled late blocks (up to 150 chosen) against the oracle
+    cfg = PrefillConfig("gpu_prefill_long_lists", B=1, Hq=4, Hkv=2, d=128, T=200 * 64, blk=64,
+                        k=150, gate=1)
+    nb = cfg.nb
+    blocks = [u * nb + i for u in range(cfg.B * cfg.Hkv)
+              for i in (0, 1, 64, 127, 128, 129, 130, 150, 151, 190, nb - 1)]
+    inp, call, st = run_case(cfg, 88, blocks=blocks)
+    assert st["excused"] <= 1
+    del inp, call
+    torch.cuda.empty_cache()
+
+
 SMALL = PrefillConfig("gpu_prefill_small", B=2, Hq=8, Hkv=2, d=128, T=1024, blk=64, k=4, gate=1)
 
 VARIANTS = [
