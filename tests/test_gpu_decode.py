@@ -137,6 +137,22 @@ def test_limit_shapes(idx):
     run_case(cfg, seed=500 + idx, gist_mode=gmode, top_p=tp)
 
 
+# One unit over many chunks: ~94 and ~141 gist slices, so the final merge takes its partials in
+# several batches and (G * slots > 1024) its statistics from global memory, and the selection
+# merge ranks more than 256 candidates with the radix path.
+MANY_SLICES = [
+    DecodeConfig("many_slices", B=1, Hq=8, Hkv=1, d=64, N=16 * 6000 + 5, C=16, g=1, k=8,
+                 n_plant=4, paged=True),
+    DecodeConfig("many_slices_big", B=1, Hq=8, Hkv=1, d=64, N=16 * 9000 + 3, C=16, g=1, k=8,
+                 gate=1, n_plant=4, paged=True),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MANY_SLICES)), ids=["ms0", "ms1"])
+def test_many_slices(idx):
+    run_case(MANY_SLICES[idx], seed=700 + idx)
+
+
 def test_max_units():
     cfg = DecodeConfig("max_units", B=2048, Hq=16, Hkv=8, d=64, N=100, C=16, g=2, k=3,
                        n_plant=1, paged=True)
