@@ -153,6 +153,20 @@ def test_many_slices(idx):
     run_case(MANY_SLICES[idx], seed=700 + idx)
 
 
+def test_radix_slice_selection():
+    # 1024 units: one slice per unit holding all 400 chunks (g = 1), so each slice picks its
+    # candidates with the radix select (more than 256 items); sampled units against the oracle
+    cfg = DecodeConfig("radix_slices", B=128, Hq=16, Hkv=8, d=64, N=16 * 400 + 7, C=16, g=1,
+                       k=8, gate=1, n_plant=4, paged=True)
+    rng = np.random.default_rng(1)
+    n = cfg.B * cfg.Hkv
+    units = sorted(set(rng.choice(n, 96, replace=False).tolist()) | {0, n - 1})
+    inp, call, st = run_case(cfg, seed=650, units=units)
+    assert st["excused"] <= 1
+    del inp, call
+    torch.cuda.empty_cache()
+
+
 def test_max_units():
     cfg = DecodeConfig("max_units", B=2048, Hq=16, Hkv=8, d=64, N=100, C=16, g=2, k=3,
                        n_plant=1, paged=True)
