@@ -166,7 +166,7 @@ struct RowStream {
     // Sum the lane groups' accumulators and write one partial per head:
     // acc -> P.acc[(bh0 + h) * nslots + slot][0..D), (M[h], L[h]) -> P.ml[...][0..2).
     // fin must hold NW * G * D floats.
-    __device__ void finish(float (&acc)[G][8], const float* M, const float* L, float* fin,
+    __device__ __forceinline__ void finish(float (&acc)[G][8], const float* M, const float* L, float* fin,
                            const Partials& P, int bh0, int slot) const {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
