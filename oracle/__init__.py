@@ -66,7 +66,7 @@ def _open(path):
     h = C.CDLL(path)
     h.or_decode.argtypes = [C.POINTER(_DecodeShape), C.POINTER(_DecodeIO)]
     h.or_prefill.argtypes = [C.POINTER(_PrefillShape), C.POINTER(_PrefillIO)]
-    h.or_decode_token_count.argtypes = [C.POINTER(_DecodeShape), C.c_int, C.c_int]
+    h.or_decode_token_count.argtypes = [C.POINTER(_DecodeShape), C.c_int, C.c_int, C.c_int]
     return h
 
 
@@ -116,7 +116,8 @@ class DecodeResult:
 
 def _gist_mode(x) -> int:
     """True/"all": every scored gist; False/"none": raw tokens only; "selected": the gists of the
-    selected chunks only ("Simplified Sparse Attention via Gist Tokens", section 3.3)."""
+    selected chunks only and, at two levels, the meta-gists of the selected groups
+    ("Simplified Sparse Attention via Gist Tokens", sections 3.3 and B.2)."""
     if isinstance(x, str):
         return {"none": 0, "all": 1, "selected": 2}[x]
     return int(bool(x))
@@ -159,9 +160,9 @@ def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_
                         cs[..., :H], gs, w, nt)
 
 
-def token_count(*, N, C_, g, k_eff, levels=1, J=0, n_cand=0, gists_in_softmax=True) -> int:
+def token_count(*, N, C_, g, k_eff, levels=1, J=0, n_cand=0, k2_eff=0, gists_in_softmax=True) -> int:
     sh = _DecodeShape(N=N, C=C_, g=g, levels=levels, J=J, gists_in_softmax=_gist_mode(gists_in_softmax))
-    return int(lib().or_decode_token_count(C.byref(sh), k_eff, n_cand))
+    return int(lib().or_decode_token_count(C.byref(sh), k_eff, n_cand, k2_eff))
 
 
 @dataclass

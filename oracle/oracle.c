@@ -30,7 +30,9 @@
  *     every raw token of c; gists and the current chunk carry bias 0;
  *   - softmax token set: every scored summary (all historical gists, or at two levels all
  *     meta-gists plus the candidates' gists), the raw tokens of the selected chunks, and the
- *     raw tokens of the current chunk (the last, possibly partial, chunk);
+ *     raw tokens of the current chunk (the last, possibly partial, chunk); in the selected-
+ *     summary mode the summaries are only the gists of the selected chunks and, at two
+ *     levels, the meta-gists of the selected groups (section B.2);
  *   - prefill: per query block i, top-min(k, i) earlier blocks by the selector row S[i][j<i];
  *     gate log_softmax over all j < i; the diagonal block is token-causal with bias 0.
  */
@@ -166,7 +168,7 @@ static double pooled_score(const uint16_t* q_group, int G, const uint16_t* gist,
     return s;
 }
 
-int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand)
+int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand, int k2_eff)
 {
     int M = (p->N + p->C - 1) / p->C;
     int H = M - 1;
@@ -177,6 +179,7 @@ int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand)
         else summaries = H * p->g;
     } else if (p->gists_in_softmax == 2) {
         summaries = k_eff * p->g;   /* each selected chunk brings its own gists */
+        if (p->levels == 2) summaries += k2_eff * p->g;   /* and each selected group its own */
     }
     return summaries + k_eff * p->C + cur;
 }
@@ -266,9 +269,18 @@ static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, 
     if (p->gate && n_cand > 0) lse_s = logsumexp(s, n_cand);
 
     /* Token set. */
-    int cap = or_decode_token_count(p, ke, n_cand);
+    int cap = or_decode_token_count(p, ke, n_cand, k2e);
     token* tk = (token*)malloc(sizeof(token) * (size_t)cap);
     int n = 0;
+    if (p->gists_in_softmax == 2 && p->levels == 2)
+        /* Selected summaries at the upper level: the meta-gists of the chosen groups
+         * ("SSA", B.2: every level contributes its selected summary tokens). */
+        for (int i = 0; i < k2e; ++i)
+            for (int t = 0; t < g; ++t) {
+                tk[n].k = g2k + ((size_t)groups[i] * g + t) * d;
+                tk[n].v = g2v + ((size_t)groups[i] * g + t) * d;
+                tk[n++].bias = 0.0;
+            }
     if (p->gists_in_softmax == 1) {
         if (p->levels == 2)
             for (int r = 0; r < nG; ++r)
@@ -348,7 +360,6 @@ int or_decode(const or_decode_shape* p, const or_decode_io* io)
     if (p->Hkv <= 0 || p->Hq % p->Hkv || p->C <= 0 || p->g <= 0 || p->N < 1) return 2;
     if (p->levels == 2 && (p->J <= 0 || p->gate)) return 3;
     if (p->gists_in_softmax < 0 || p->gists_in_softmax > 2) return 4;
-    if (p->gists_in_softmax == 2 && p->levels != 1) return 4;
     if (!(p->top_p >= 0.0 && p->top_p <= 1.0) || (p->top_p > 0.0 && p->levels != 1)) return 5;
     const int total = p->B * p->Hkv;
     const int n = io->units ? io->n_units : total;

@@ -24,7 +24,8 @@ typedef struct {
     int N, C, g, k;
     int gate;             /* 0 none, 1 SAS log-softmax gate                          */
     int gists_in_softmax; /* 1: every scored summary enters the softmax; 0: raw only;
-                             2: only the selected chunks' gists (one level)            */
+                             2: only the selected chunks' gists (and, at two levels,
+                                the selected groups' meta-gists)                         */
     int levels, J, k2;
     int max_chunks;
     int num_pages;
@@ -71,7 +72,7 @@ typedef struct {
 
 int or_decode(const or_decode_shape* p, const or_decode_io* io);
 int or_prefill(const or_prefill_shape* p, const or_prefill_io* io);
-int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand);
+int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand, int k2_eff);
 int or_threads(void);
 
 #endif

@@ -45,6 +45,10 @@ MUTANTS = [
      "tk[n].k = gk + ((size_t)c * g + 0) * d;"),
     ("selected_gists_gated", "                tk[n].v = gv + ((size_t)c * g + t) * d;\n                tk[n++].bias = 0.0;",
      "                tk[n].v = gv + ((size_t)c * g + t) * d;\n                tk[n++].bias = p->gate ? 0.5 : 0.0;"),
+    ("selected_meta_gists_dropped", "        for (int i = 0; i < k2e; ++i)\n            for (int t = 0; t < g; ++t) {",
+     "        for (int i = 0; i < 0; ++i)\n            for (int t = 0; t < g; ++t) {"),
+    ("selected_meta_gists_by_position", "tk[n].k = g2k + ((size_t)groups[i] * g + t) * d;",
+     "tk[n].k = g2k + ((size_t)i * g + t) * d;"),
 ]
 
 

@@ -76,6 +76,10 @@ def brute_decode(inp, gists=True, top_p=0.0):
                     Ks += [g2k.reshape(-1, c.d)]
                     Vs += [g2v.reshape(-1, c.d)]
                     bias += [0.0] * (c.nG * c.g)
+                if gists == "selected":
+                    Ks += [g2k[r] for r in groups]
+                    Vs += [g2v[r] for r in groups]
+                    bias += [0.0] * (len(groups) * c.g)
             else:
                 cand = list(range(H))
             s = {x: _lse(sig * qg @ gk[b, kv, x].T) for x in cand}
@@ -511,6 +515,63 @@ def pin_selected_gists_token_count_and_weights():
         assert n == cfg.k * (cfg.g + cfg.C) + cfg.cur_len
         w = r.weights[0, h, :n]
         assert abs(w.sum() - 1.0) < TOL and (w > 0).all()
+
+
+def pin_selected_gists_two_level_brute_force():
+    """Two levels, selected summaries: the chosen groups' meta-gists + the chosen chunks' gists
+    and raw tokens + the current chunk ("SSA", section B.2: each level contributes its selected
+    summaries and the bottom level the raw tokens), against the numpy evaluation."""
+    for cfg in (SMALL_L2, SMALL_L2.with_(g=1, Hq=2, k2=3, k=7), SMALL_L2.with_(B=2, Hkv=2, J=3)):
+        inp = make_decode(cfg, seed=21, max_chunks=cfg.M + 1, extra_pages=1)
+        r = oracle_decode(inp, gists_in_softmax="selected")
+        o, l, s_ = brute_decode(inp, gists="selected")
+        assert np.array_equal(r.sel, s_), cfg.name
+        assert np.abs(r.out - o).max() < TOL, cfg.name
+        assert np.abs(r.lse - l).max() < TOL, cfg.name
+
+
+def pin_selected_gists_two_level_everything_selected_is_dense():
+    """Every group and every chunk chosen: the two-level selected set is the whole cache with
+    all meta-gists and gists again (textbook attention over that set)."""
+    c = SMALL_L2.with_(k2=SMALL_L2.nG, k=SMALL_L2.H)
+    inp = make_decode(c, seed=22)
+    r = oracle_decode(inp, gists_in_softmax="selected")
+    K, V = _logical_kv(inp)
+    q = f64(inp.q)
+    kt = np.concatenate([f64(inp.gist2_k)[0, 0].reshape(-1, c.d),
+                         f64(inp.gist_k)[0, 0].reshape(-1, c.d), K[0, 0].reshape(-1, c.d)[: c.N]])
+    vt = np.concatenate([f64(inp.gist2_v)[0, 0].reshape(-1, c.d),
+                         f64(inp.gist_v)[0, 0].reshape(-1, c.d), V[0, 0].reshape(-1, c.d)[: c.N]])
+    for h in range(c.Hq):
+        o, l = sdpa(q[0, h], kt, vt)
+        assert np.abs(r.out[0, h] - o).max() < TOL
+        assert abs(r.lse[0, h] - l) < TOL
+
+
+def pin_selected_gists_two_level_count_and_weights():
+    """|V_t| = k2 g + k (g + C) + |current chunk| at two levels; weights sum to one."""
+    assert oracle.token_count(N=100, C_=8, g=2, k_eff=4, levels=2, J=3, k2_eff=2,
+                              gists_in_softmax="selected") == 2 * 2 + 4 * 10 + 4
+    c = SMALL_L2
+    inp = make_decode(c, seed=23)
+    cap = c.k2 * c.g + c.k * (c.g + c.C) + c.C
+    r = oracle_decode(inp, gists_in_softmax="selected", weights_cap=cap)
+    for h in range(c.Hq):
+        n = r.n_tokens[0, h]
+        assert n == c.k2 * c.g + c.k * (c.g + c.C) + c.cur_len
+        w = r.weights[0, h, :n]
+        assert abs(w.sum() - 1.0) < TOL and (w > 0).all()
+    # a chosen group's meta-gists are present: an exact reconstruction of the output from the
+    # weights over the materialised set, meta-gists first in chosen-group order
+    K, V = _logical_kv(inp)
+    g2v, gv = f64(inp.gist2_v)[0, 0], f64(inp.gist_v)[0, 0]
+    groups, sel = r.sel_groups[0, 0], r.sel[0, 0]
+    vt = np.concatenate([g2v[groups].reshape(-1, c.d)] +
+                        [np.concatenate([gv[x], V[0, 0, x]]) for x in sel] +
+                        [V[0, 0, c.H, : c.cur_len]])
+    for h in range(c.Hq):
+        n = r.n_tokens[0, h]
+        assert np.abs(r.weights[0, h, :n] @ vt - r.out[0, h]).max() < 1e-10
 
 
 def pin_top_p_brute_force():
