@@ -32,7 +32,7 @@ def decode_bytes(cfg, k=None, gist_mode="all", k_eff_mean=None):
     Gist rows scored (and attended), the selected chunks' K and V, the current chunk's K and
     V, q, out (fp32), and the page-table entries read.  gist_mode "selected": every gist key is
     read for the scores, but only the selected chunks' gist values (and keys, already read)
-    enter the softmax."""
+    enter the softmax, and at two levels the chosen groups' level-2 gist values."""
     k = cfg.k if k is None else k
     units = cfg.B * cfg.Hkv
     row = cfg.d * 2                               # one bf16 row
@@ -46,7 +46,8 @@ def decode_bytes(cfg, k=None, gist_mode="all", k_eff_mean=None):
     if k_eff_mean is not None:          # top-p: chunks actually kept, averaged over units
         k_eff = k_eff_mean
     if gist_mode == "selected":
-        parts = {"gists_k": units * gist_rows * row, "selected_gists_v": int(units * k_eff * cfg.g * row)}
+        sel_v = k_eff * cfg.g + (min(cfg.k2, cfg.nG) * cfg.g if cfg.levels == 2 else 0)
+        parts = {"gists_k": units * gist_rows * row, "selected_gists_v": int(units * sel_v * row)}
     else:
         parts = {"gists_kv": units * gist_rows * row * 2}
     parts.update({

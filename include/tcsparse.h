@@ -22,10 +22,10 @@
  *        of the current chunk (bias 0, always kept):
  *          lambda_x = sigma * q . k_x + bias_x,  out = sum_x softmax(lambda)_x v_x,
  *          lse = log sum_x exp(lambda_x)  (natural log, gate included).
- *   gist_mode = TCS_GISTS_SELECTED (one level only) replaces "every historical gist" in step 5
- *   by the gists of the selected chunks only, each next to its chunk's raw tokens: the set
- *   section 3.3 describes, in which an unselected chunk contributes nothing.  The scores and
- *   the selection (steps 1-4) are unchanged.
+ *   gist_mode = TCS_GISTS_SELECTED replaces "every historical gist" in step 5 by the gists of
+ *   the selected chunks only, each next to its chunk's raw tokens: the set section 3.3
+ *   describes, in which an unselected chunk contributes nothing.  The scores and the selection
+ *   (steps 1-4) are unchanged.
  *   top_p in (0, 1] (one level) replaces step 3: rank H as in step 3 and keep the shortest
  *   ranked prefix whose shares p[c] = exp(s[c] - log sum_{c' in H} exp(s[c'])) add up to at
  *   least top_p (top_p = 1 keeps every chunk), at most k of them, reported ascending.  The
@@ -36,8 +36,11 @@
  *   consecutive historical chunks.  The group scores s2[r] (step 2 over gist2_k) pick the top
  *   k2 groups; the member chunks of the chosen groups are the candidates; steps 1-3 run over
  *   the candidates only.  The softmax set is: every level-2 gist, the gists of every
- *   candidate chunk, the raw tokens of the selected chunks and of the current chunk.  The SAS
- *   gate is not defined for two levels (TCS_ERR_UNSUPPORTED).
+ *   candidate chunk, the raw tokens of the selected chunks and of the current chunk; with
+ *   TCS_GISTS_SELECTED it is the level-2 gists of the chosen groups, the gists and raw tokens
+ *   of the selected chunks and the current chunk (appendix B.2: every level contributes the
+ *   summaries it selected, the lowest level also the raw tokens).  The SAS gate is not defined
+ *   for two levels (TCS_ERR_UNSUPPORTED).
  *
  *   Prefill ("SAS: Simple Attention Sparsification", abstract: FlashAttention-style forward
  *   with the gate inside the softmax).  Query block i (blk tokens) of KV head kv keeps the
@@ -78,12 +81,13 @@
  *   unspecified results).  A page id outside [0, num_pages) is never read: the heads of the
  *   affected unit get NaN in out and lse.
  *   k larger than the number of candidates is clamped (that is how "all chunks" is asked
- *   for); k = 0 keeps only the gists and the current chunk (only the current chunk with
- *   TCS_GISTS_SELECTED).  Results are deterministic:
+ *   for); k = 0 keeps only the gists and the current chunk (with TCS_GISTS_SELECTED only the
+ *   current chunk, plus the chosen groups' level-2 gists at two levels).  Results are
+ *   deterministic:
  *   no floating-point atomics; the same inputs give bitwise-identical outputs.
  *
  * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024;
- * B * Hkv <= 16384; TCS_GISTS_SELECTED: one level and C + g <= 1024; top_p > 0: one level
+ * B * Hkv <= 16384; TCS_GISTS_SELECTED: C + g <= 1024; top_p > 0: one level
  * and k <= 256; two levels:
  * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk.
  * Other shapes return TCS_ERR_UNSUPPORTED.

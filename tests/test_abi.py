@@ -51,6 +51,15 @@ def test_selected_gists_need_fewer_partial_slots():
     assert 0 < b < a
 
 
+def test_selected_gists_two_levels_slots():
+    # two levels with selected gists: no level-2 slices among the partial slots, one slot per
+    # chosen group (its own level-2 gists) as with every gist
+    kw = dict(N=64 * 500, levels=2, J=8, k2=4)
+    a = ops.decode_workspace_size(P(**kw))
+    b = ops.decode_workspace_size(P(gist_mode=1, **kw))
+    assert 0 < b < a
+
+
 def test_workspace_size_grows_with_work():
     a = ops.decode_workspace_size(P())
     b = ops.decode_workspace_size(P(k=16))
@@ -85,7 +94,6 @@ def test_workspace_size_grows_with_work():
     (dict(top_p=float("nan")), ops.TCS_ERR_SHAPE),
     (dict(top_p=0.5, levels=2, J=4, k2=2), ops.TCS_ERR_UNSUPPORTED),
     (dict(top_p=0.5, k=257), ops.TCS_ERR_UNSUPPORTED),
-    (dict(gist_mode=1, levels=2, J=4, k2=2), ops.TCS_ERR_UNSUPPORTED),
     (dict(gist_mode=1, C_=1024, g=8, N=5000), ops.TCS_ERR_UNSUPPORTED),  # C + g > 1024
 ])
 def test_decode_rejects_bad_params(kw, code):

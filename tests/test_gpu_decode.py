@@ -76,8 +76,14 @@ def test_variants(cfg):
     run_case(cfg, seed=100 + VARIANTS.index(cfg), max_chunks=cfg.M + 5, extra_pages=3)
 
 
-# Selected-gist token set (each selected chunk's gists next to its raw tokens).
-SEL_GISTS = [v for v in VARIANTS if v.levels == 1 and v.C + v.g <= 1024]
+# Selected-gist token set (each selected chunk's gists next to its raw tokens; at two levels
+# also the chosen groups' level-2 gists).
+SEL_GISTS = [v for v in VARIANTS if v.C + v.g <= 1024] + [
+    SMALL.with_(levels=2, J=4, k2=3, k=6, n_plant=6, plant_groups=3, g=1, Hq=2),   # G = 1
+    SMALL.with_(levels=2, J=7, k2=5, k=9, n_plant=6, plant_groups=3, g=8, Hq=16),  # G = 8
+    SMALL.with_(levels=2, J=6, k2=1, k=3, n_plant=3, plant_groups=1, d=64, C=64, g=64,
+                N=30 * 64 + 63),                                                     # g = 64
+]
 
 
 @pytest.mark.parametrize("cfg", SEL_GISTS, ids=[f"sg{i}" for i in range(len(SEL_GISTS))])
@@ -86,7 +92,8 @@ def test_selected_gists_variants(cfg):
              extra_pages=1)
 
 
-@pytest.mark.parametrize("name", ["llama32_1b_decode_32k", "llama31_8b_decode_128k"])
+@pytest.mark.parametrize("name", ["llama32_1b_decode_32k", "llama31_8b_decode_128k",
+                                  "hssa_decode_512k"])
 def test_selected_gists_full(name):
     cfg = configs.DECODE_CONFIGS[name]
     inp, call, st = run_case(cfg, configs.seed_for(name), gist_mode=1)
@@ -122,12 +129,16 @@ def test_top_p_full(name, tp):
 
 
 # The largest documented shapes: C = 1024 rows per chunk with g = 64 gists; C + g = 1024 for the
-# selected-gist set; k = 256 for top-p; B * Hkv = 16384 units.
+# selected-gist set; k = 256 for top-p; J * g = 1024 and 64 chosen groups at two levels.
 LIMITS = [
     (SMALL.with_(C=1024, g=64, d=64, N=9 * 1024 + 300, k=3, n_plant=2), 0, 0.0),
     (SMALL.with_(C=1024, g=8, N=5 * 1024 + 1, k=2, gate=1, n_plant=2), 0, 0.0),
     (SMALL.with_(C=960, g=64, d=64, N=7 * 960 + 5, k=2, n_plant=2), 1, 0.0),
     (SMALL.with_(C=16, g=1, d=64, N=300 * 16 + 3, k=256, n_plant=4, gate=1), 0, 0.95),
+    # two levels, selected summaries: J * g = 1024 rows per group slice, all 64 groups chosen,
+    # 64 level-2 gist rows in each group's partial
+    (SMALL.with_(levels=2, J=16, k2=64, k=40, g=64, C=64, d=64, N=1024 * 64 + 10, n_plant=8,
+                 plant_groups=4), 1, 0.0),
 ]
 
 

@@ -89,7 +89,7 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (!supported_group(G)) return TCS_ERR_UNSUPPORTED;
     if (p->g > 64 || p->C > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
     const bool sel_gists = p->gist_mode == TCS_GISTS_SELECTED;
-    if (sel_gists && (p->levels != 1 || p->C + p->g > kMaxSliceRows)) return TCS_ERR_UNSUPPORTED;
+    if (sel_gists && p->C + p->g > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
     if (p->top_p > 0.f && (p->levels != 1 || p->k > kMaxTopPK)) return TCS_ERR_UNSUPPORTED;
     pl->G = G;
     pl->M = M;
@@ -129,9 +129,10 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     // (dispatch, query load, partial write, arrival) then pay for twice the bytes.
     const long long cpw_min = units * (ksel + 1) >= 512 ? 2 : 1;
     pl->cpw = (int)std::max<long long>(std::min(cpw_min, cpw_max), std::min(cpw, cpw_max));
-    // softmax partial slots per query head: gist slices (none with selected gists), chosen
-    // level-2 groups' slices, then the chunk-attention workgroups
-    pl->nslots = (sel_gists ? 0 : pl->S1) + pl->S2 + pl->k2e + (ksel + 1 + pl->cpw - 1) / pl->cpw;
+    // softmax partial slots per query head: gist slices and level-2 slices (none with selected
+    // gists), one per chosen level-2 group (its members' gists, or with selected gists its own
+    // level-2 gists), then the chunk-attention workgroups
+    pl->nslots = (sel_gists ? 0 : pl->S1 + pl->S2) + pl->k2e + (ksel + 1 + pl->cpw - 1) / pl->cpw;
     const long long BH = (long long)p->B * p->Hq;
     const long long s1 = p->levels == 2 ? pl->k2e : pl->S1;     // slices of the chunk pass
     auto n1 = [](long long x) { return x > 0 ? x : 1; };
@@ -313,9 +314,10 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         ga.score_stride = 0;
         ga.slot0 = slot;
         ga.selo = gs;
+        ga.scores_only = p->gist_mode == TCS_GISTS_SELECTED;
         e = tcs::launch_gist(ga, s);
         if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
-        slot += pl.S2;
+        if (!ga.scores_only) slot += pl.S2;
         if (pl.S2 == 0 && sel_groups && p->k2 > 0) {
             e = tcs::launch_fill(sel_groups, (long long)units * p->k2, -1, s);
             if (e != hipSuccess) return TCS_ERR_HIP;
@@ -336,6 +338,11 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         ga.score_stride = pl.H;
         ga.slot0 = slot;
         ga.selo = chunk_sel;
+        if (ga.scores_only) {   // the chosen groups' level-2 gists are the slices' tokens
+            ga.pk = (const uint16_t*)gist2_k;
+            ga.pv = (const uint16_t*)gist2_v;
+            ga.p_unit_stride = (long long)pl.nG * p->g * p->d;
+        }
         e = tcs::launch_gist(ga, s);
         if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
         slot += pl.k2e;

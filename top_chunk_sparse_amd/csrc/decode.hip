@@ -442,7 +442,29 @@ struct GistSmem {
     int tp_keep;
 };
 
+// Softmax partial of the G heads over `nrows` rows whose logits sit in sm.x.lg (values V, the
+// first batch already in vfirst) -> slot `slot`.
 template <int D, int G>
+__device__ __forceinline__ void fold_rows(GistSmem<D, G>& sm, const Partials& part,
+                                          const uint16_t* V, int nrows,
+                                          uint4 (&vfirst)[TCS_V_U], int bh0, int slot) {
+    using RS = RowStream<D, G>;
+    const RS rs;
+    head_stats<G>(sm.x.lg, nrows, sm.hs);
+    float acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    rs.template accumulate<TCS_V_U>(acc, V, nrows, sm.x.lg, 0, vfirst, true);
+    __syncthreads();   // weights dead: fin may reuse the space
+    rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, part, bh0, slot);
+}
+
+// META: the group-mode slices of the selected-summary set at two levels, whose softmax tokens
+// are their groups' own level-2 gists (a.pk / a.pv); a separate instantiation, so the other
+// passes compile as if it did not exist.
+template <int D, int G, bool META>
 __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& sm, int y, int u) {
     using RS = RowStream<D, G>;
     const int b = u / a.Hkv, kv = u % a.Hkv;
@@ -501,15 +523,20 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
         if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
     }
     if (!a.scores_only) {   // the gists are tokens of the softmax set: fold them in here
-        head_stats<G>(sm.x.lg, nrows, sm.hs);
-        float acc[G][8];
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        rs.template accumulate<TCS_V_U>(acc, V, nrows, sm.x.lg, 0, vfirst, true);
-        __syncthreads();   // weights dead: fin may reuse the space
-        rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, a.part, bh0, a.slot0 + y);
+        fold_rows<D, G>(sm, a.part, V, nrows, vfirst, bh0, a.slot0 + y);
+    } else if constexpr (META) {
+        // selected summaries at two levels: this group's own level-2 gists are the tokens
+        const int r = a.groups[(long long)u * a.k2 + y];
+        const long long off = (long long)u * a.p_unit_stride + (long long)r * a.g * D;
+        __syncthreads();   // every pooled score has read its logits: lg may be overwritten
+        {
+            uint32_t q2[G][4];
+            rs.load_q(a.q + (long long)bh0 * D, q2);
+            rs.template logits<TCS_K_U>(q2, a.pk + off, a.g, a.sigma, 0.f, sm.x.lg, 0);
+        }
+        rs.template prefetch<TCS_V_U>(a.pv + off, a.g, vfirst);
+        __syncthreads();
+        fold_rows<D, G>(sm, a.part, a.pv + off, a.g, vfirst, bh0, a.slot0 + y);
     }
     __syncthreads();
     select_epilogue(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.lse, &sm.x,
@@ -519,10 +546,10 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
                     *reinterpret_cast<TopPSmem*>(sm.score), &sm.tp_keep);
 }
 
-template <int D, int G>
+template <int D, int G, bool META>
 __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
     __shared__ GistSmem<D, G> sm;
-    gist_item<D, G>(a, sm, blockIdx.x, blockIdx.y);
+    gist_item<D, G, META>(a, sm, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -769,13 +796,13 @@ __global__ void fill_kernel(int32_t* p, long long n, int32_t v) {
 // ---------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool META>
 static hipError_t gist_d(const GistLaunch& a, hipStream_t s, dim3 grid) {
     switch (a.Hq / a.Hkv) {
-        case 1: gist_kernel<D, 1><<<grid, 256, 0, s>>>(a); break;
-        case 2: gist_kernel<D, 2><<<grid, 256, 0, s>>>(a); break;
-        case 4: gist_kernel<D, 4><<<grid, 256, 0, s>>>(a); break;
-        case 8: gist_kernel<D, 8><<<grid, 256, 0, s>>>(a); break;
+        case 1: gist_kernel<D, 1, META><<<grid, 256, 0, s>>>(a); break;
+        case 2: gist_kernel<D, 2, META><<<grid, 256, 0, s>>>(a); break;
+        case 4: gist_kernel<D, 4, META><<<grid, 256, 0, s>>>(a); break;
+        case 8: gist_kernel<D, 8, META><<<grid, 256, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -784,7 +811,11 @@ static hipError_t gist_d(const GistLaunch& a, hipStream_t s, dim3 grid) {
 hipError_t launch_gist(const GistLaunch& a, hipStream_t s) {
     if (a.slices <= 0) return hipSuccess;
     dim3 grid(a.slices, a.B * a.Hkv);
-    return a.d == 128 ? gist_d<128>(a, s, grid) : gist_d<64>(a, s, grid);
+    if (a.pk) {   // only group mode with scores_only carries level-2 gists for the partials
+        if (!a.groups || !a.scores_only || !a.pv) return hipErrorInvalidValue;
+        return a.d == 128 ? gist_d<128, true>(a, s, grid) : gist_d<64, true>(a, s, grid);
+    }
+    return a.d == 128 ? gist_d<128, false>(a, s, grid) : gist_d<64, false>(a, s, grid);
 }
 
 template <int D>

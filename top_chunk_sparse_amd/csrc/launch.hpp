@@ -46,6 +46,11 @@ struct GistLaunch {
     int slot0;
     SelectOut selo;
     int scores_only;          // 1: score and select only (no gist softmax partials)
+    // group mode with scores_only: slice y's softmax partial covers the g level-2 gist rows of
+    // its own group groups[u][y] (the selected-summary set at two levels) when pk is not null
+    const uint16_t* pk;
+    const uint16_t* pv;
+    long long p_unit_stride;  // elements between consecutive (b, kv) level-2 gist blocks
 };
 
 struct ChunkLaunch {
