@@ -34,7 +34,8 @@ class _DecodeShape(C.Structure):
     _fields_ = [(n, C.c_int) for n in ("B", "Hq", "Hkv", "d", "N", "C", "g", "k", "gate",
                                        "gists_in_softmax", "levels", "J", "k2", "max_chunks",
                                        "num_pages", "gist_cap")] + [("scale", C.c_double),
-                                                                    ("top_p", C.c_double)]
+                                                                    ("top_p", C.c_double),
+                                                                    ("head_select", C.c_int)]
 
 
 _P = C.c_void_p
@@ -126,8 +127,10 @@ def _gist_mode(x) -> int:
 def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_k, gist_v,
            gate=0, levels=1, J=0, k2=0, gist2_k=None, gist2_v=None, scale=0.0,
            gists_in_softmax=True, gist_cap=0, forced_sel=None, forced_groups=None,
-           units=None, weights_cap=0, top_p=0.0) -> DecodeResult:
-    """Decode attention for every (b, kv) (or the flat ids in ``units``)."""
+           units=None, weights_cap=0, top_p=0.0, head_select=0) -> DecodeResult:
+    """Decode attention for every (b, kv) (or the flat ids in ``units``).  head_select = 1:
+    per-head selection with the union unfolded; sel then holds G * k entries per unit and
+    chunk_scores one row per query head."""
     M = -(-N // C_)
     H = M - 1
     nG = -(-H // J) if levels == 2 else 0
@@ -135,12 +138,14 @@ def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_
     sh = _DecodeShape(B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, C=C_, g=g, k=k, gate=gate,
                       gists_in_softmax=_gist_mode(gists_in_softmax), levels=levels, J=J, k2=k2,
                       max_chunks=page_table.shape[-1], num_pages=k_pages.shape[0],
-                      gist_cap=gist_cap, scale=scale, top_p=top_p)
+                      gist_cap=gist_cap, scale=scale, top_p=top_p, head_select=head_select)
+    G = Hq // Hkv
+    sk = G * k if head_select else k
     out = np.full((B, Hq, d), np.nan)
     lse = np.full((B, Hq), np.nan)
-    sel = np.full((B, Hkv, max(k, 1)), -7, np.int32)
+    sel = np.full((B, Hkv, max(sk, 1)), -7, np.int32)
     selg = np.full((B, Hkv, max(k2, 1)), -7, np.int32) if levels == 2 else None
-    cs = np.full((B, Hkv, max(H, 1)), np.nan)
+    cs = np.full((B, Hq if head_select else Hkv, max(H, 1)), np.nan)
     gs = np.full((B, Hkv, max(nG, 1)), np.nan) if levels == 2 else None
     w = np.zeros((B, Hq, weights_cap)) if weights_cap else None
     nt = np.zeros((B, Hq), np.int32)
@@ -156,7 +161,7 @@ def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_
     rc = lib().or_decode(C.byref(sh), C.byref(io))
     if rc:
         raise ValueError(f"oracle decode rejected the arguments (code {rc})")
-    return DecodeResult(out, lse, sel[..., :k], None if selg is None else selg[..., :k2],
+    return DecodeResult(out, lse, sel[..., :sk], None if selg is None else selg[..., :k2],
                         cs[..., :H], gs, w, nt)
 
 

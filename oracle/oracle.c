@@ -33,6 +33,10 @@
  *     raw tokens of the current chunk (the last, possibly partial, chunk); in the selected-
  *     summary mode the summaries are only the gists of the selected chunks and, at two
  *     levels, the meta-gists of the selected groups (section B.2);
+ *   - per-head selection (appendix A: each head selects its chunks on its own, then the union
+ *     is unfolded into the shared KV): head h's score of chunk c is the log-sum-exp of its own
+ *     g gist logits, each head takes its top-k by the same ranking key, and every head of the
+ *     group attends to the union of the G selections (ascending); no gate is defined for it;
  *   - prefill: per query block i, top-min(k, i) earlier blocks by the selector row S[i][j<i];
  *     gate log_softmax over all j < i; the diagonal block is token-causal with bias 0.
  */
@@ -243,26 +247,47 @@ static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, 
     for (int i = 0; i < n_cand; ++i) {
         s[i] = pooled_score(qg, G, gk + (size_t)cand[i] * g * d, g, d, sigma);
     }
-    if (io->chunk_scores) {
+    if (io->chunk_scores && !p->head_select) {
         for (int c = 0; c < H; ++c) io->chunk_scores[unit * H + c] = -INFINITY;
         for (int i = 0; i < n_cand; ++i) io->chunk_scores[unit * H + cand[i]] = s[i];
     }
 
     /* Selection. */
-    int* sel = (int*)malloc(sizeof(int) * (size_t)(p->k > 0 ? p->k : 1));
+    const int sk = p->head_select ? G * p->k : p->k;   /* entries per unit in sel */
+    int* sel = (int*)malloc(sizeof(int) * (size_t)(sk > 0 ? sk : 1));
     int ke = 0;
     if (io->forced_sel) {
-        for (int i = 0; i < p->k; ++i) {
-            int c = io->forced_sel[unit * p->k + i];
+        for (int i = 0; i < sk; ++i) {
+            int c = io->forced_sel[unit * sk + i];
             if (c >= 0) sel[ke++] = c;
         }
+    } else if (p->head_select) {
+        /* each head's own score and own top-k; the union, ascending */
+        char* in_union = (char*)calloc((size_t)(H > 0 ? H : 1), 1);
+        double* sh = (double*)malloc(sizeof(double) * (size_t)(n_cand > 0 ? n_cand : 1));
+        int* pick = (int*)malloc(sizeof(int) * (size_t)(p->k > 0 ? p->k : 1));
+        for (int h = 0; h < G; ++h) {
+            for (int i = 0; i < n_cand; ++i) {
+                sh[i] = pooled_score(qg + (size_t)h * d, 1, gk + (size_t)cand[i] * g * d, g, d,
+                                     sigma);
+                if (io->chunk_scores)
+                    io->chunk_scores[(unit * G + h) * (size_t)H + cand[i]] = sh[i];
+            }
+            const int kh = top_k(sh, cand, n_cand, p->k, pick);
+            for (int j = 0; j < kh; ++j) in_union[pick[j]] = 1;
+        }
+        for (int c = 0; c < H; ++c)
+            if (in_union[c]) sel[ke++] = c;
+        free(pick);
+        free(sh);
+        free(in_union);
     } else if (p->top_p > 0.0) {
         ke = top_p(s, cand, n_cand, p->top_p, p->k, sel);
     } else {
         ke = top_k(s, cand, n_cand, p->k, sel);
     }
     if (io->sel)
-        for (int i = 0; i < p->k; ++i) io->sel[unit * p->k + i] = i < ke ? sel[i] : -1;
+        for (int i = 0; i < sk; ++i) io->sel[unit * sk + i] = i < ke ? sel[i] : -1;
 
     /* SAS gate: log of the softmax over all historical chunk scores (one level only). */
     double lse_s = 0.0;
@@ -361,6 +386,9 @@ int or_decode(const or_decode_shape* p, const or_decode_io* io)
     if (p->levels == 2 && (p->J <= 0 || p->gate)) return 3;
     if (p->gists_in_softmax < 0 || p->gists_in_softmax > 2) return 4;
     if (!(p->top_p >= 0.0 && p->top_p <= 1.0) || (p->top_p > 0.0 && p->levels != 1)) return 5;
+    if (p->head_select < 0 || p->head_select > 1 ||
+        (p->head_select && (p->levels != 1 || p->gate || p->top_p > 0.0)))
+        return 6;
     const int total = p->B * p->Hkv;
     const int n = io->units ? io->n_units : total;
     int rc = 0;

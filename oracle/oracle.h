@@ -8,8 +8,10 @@
  *   gist_k/v     [B][Hkv][gist_cap][g][d] (gist_cap = 0 means M-1)
  *   gist2_k/v    [B][Hkv][nG][g][d]       nG = ceil((M-1)/J), levels = 2 only
  *   out          [B][Hq][d],  lse [B][Hq]
- *   sel          [B][Hkv][k] ascending, -1 padded;  sel_groups [B][Hkv][k2]
- *   chunk_scores [B][Hkv][M-1] (-inf where a chunk was not scored)
+ *   sel          [B][Hkv][k] ascending, -1 padded ([B][Hkv][G*k] with head_select);
+ *   sel_groups   [B][Hkv][k2]
+ *   chunk_scores [B][Hkv][M-1] (-inf where a chunk was not scored; [B][Hq][M-1] per query
+ *                head with head_select)
  *   group_scores [B][Hkv][nG]
  * Prefill:
  *   q [B][Hq][T][d], k/v [B][Hkv][T][d], S fp32 [B][Hkv][nb][nb], out [B][Hq][T][d], lse [B][Hq][T],
@@ -33,6 +35,10 @@ typedef struct {
     double scale;         /* <= 0: 1/sqrt(d)                                          */
     double top_p;         /* 0: top-k; in (0, 1]: shortest ranked prefix with softmax
                              mass >= top_p, at most k chunks (one level)               */
+    int head_select;      /* 0: one selection per KV head from the group-pooled score;
+                             1: every query head picks its own top-k by its own score and
+                                the union is unfolded for the whole group (one level, no
+                                gate, no top-p)                                          */
 } or_decode_shape;
 
 typedef struct {

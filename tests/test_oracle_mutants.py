@@ -49,6 +49,11 @@ MUTANTS = [
      "        for (int i = 0; i < 0; ++i)\n            for (int t = 0; t < g; ++t) {"),
     ("selected_meta_gists_by_position", "tk[n].k = g2k + ((size_t)groups[i] * g + t) * d;",
      "tk[n].k = g2k + ((size_t)i * g + t) * d;"),
+    ("head_select_first_head_only", "        for (int h = 0; h < G; ++h) {\n            for (int i = 0; i < n_cand; ++i) {\n                sh[i]",
+     "        for (int h = 0; h < 1; ++h) {\n            for (int i = 0; i < n_cand; ++i) {\n                sh[i]"),
+    ("head_select_pooled_score", "sh[i] = pooled_score(qg + (size_t)h * d, 1,", "sh[i] = pooled_score(qg, G,"),
+    ("head_select_last_pick_dropped", "for (int j = 0; j < kh; ++j) in_union[pick[j]] = 1;",
+     "for (int j = 0; j + 1 < kh; ++j) in_union[pick[j]] = 1;"),
 ]
 
 

@@ -53,7 +53,7 @@ def _logical_kv(inp):
     return K, V
 
 
-def brute_decode(inp, gists=True, top_p=0.0):
+def brute_decode(inp, gists=True, top_p=0.0, head_select=False):
     c = inp.cfg
     G, H, sig = c.G, c.H, 1.0 / math.sqrt(c.d)
     q = f64(inp.q)
@@ -61,7 +61,7 @@ def brute_decode(inp, gists=True, top_p=0.0):
     gk, gv = f64(inp.gist_k), f64(inp.gist_v)
     out = np.zeros((c.B, c.Hq, c.d))
     lse = np.zeros((c.B, c.Hq))
-    sels = np.full((c.B, c.Hkv, c.k), -1, np.int32)
+    sels = np.full((c.B, c.Hkv, G * c.k if head_select else c.k), -1, np.int32)
     for b in range(c.B):
         for kv in range(c.Hkv):
             qg = q[b, kv * G:(kv + 1) * G]
@@ -89,6 +89,12 @@ def brute_decode(inp, gists=True, top_p=0.0):
                 shares = np.exp(np.array([s[x] for x in order]) - _lse([s[x] for x in cand]))
                 r = int(np.argmax(np.cumsum(shares) >= top_p)) + 1
             sel = sorted(order[: min(c.k, r)])
+            if head_select:   # every head's own top-k by its own score; the union
+                union = set()
+                for h in range(G):
+                    sh = {x: _lse(sig * gk[b, kv, x] @ qg[h]) for x in cand}
+                    union |= set(sorted(cand, key=lambda x: (-sh[x], x))[: c.k])
+                sel = sorted(union)
             sels[b, kv, : len(sel)] = sel
             lse_s = _lse([s[x] for x in cand]) if cand else 0.0
             if gists is True:
@@ -572,6 +578,78 @@ def pin_selected_gists_two_level_count_and_weights():
     for h in range(c.Hq):
         n = r.n_tokens[0, h]
         assert np.abs(r.weights[0, h, :n] @ vt - r.out[0, h]).max() < 1e-10
+
+
+def pin_head_select_brute_force():
+    """Per-head selection (SSA appendix A: each head selects on its own, the union is unfolded
+    into the shared KV) against the numpy evaluation, with every gist and with the selected
+    gists; the per-head scores against their definition."""
+    for cfg, gm in ((SMALL, True), (SMALL.with_(Hq=8, k=2), "selected"), (SMALL_G1, True),
+                    (SMALL.with_(Hq=8, g=1, k=4), True)):
+        inp = make_decode(cfg, seed=31, max_chunks=cfg.M + 1, extra_pages=1)
+        r = oracle_decode(inp, head_select=1, gists_in_softmax=gm)
+        o, l, s_ = brute_decode(inp, gists=gm, head_select=True)
+        assert r.sel.shape[-1] == cfg.G * cfg.k
+        assert np.array_equal(r.sel, s_), cfg.name
+        assert np.abs(r.out - o).max() < TOL, cfg.name
+        assert np.abs(r.lse - l).max() < TOL, cfg.name
+        q, gk = f64(inp.q), f64(inp.gist_k)
+        for b in range(cfg.B):
+            for h in range(cfg.Hq):
+                want = [_lse(gk[b, h // cfg.G, x] @ q[b, h] / math.sqrt(cfg.d)) for x in range(cfg.H)]
+                assert np.abs(r.chunk_scores[b, h] - want).max() < TOL
+
+
+def pin_head_select_one_head_per_group_is_kv_select():
+    """G = 1: a head's own score is the pooled score, so per-head selection is the KV-head
+    selection."""
+    cfg = SMALL.with_(Hq=2, Hkv=2)
+    inp = make_decode(cfg, seed=32)
+    a = oracle_decode(inp)
+    b = oracle_decode(inp, head_select=1)
+    assert np.array_equal(a.sel, b.sel)
+    assert np.abs(a.out - b.out).max() < TOL and np.abs(a.lse - b.lse).max() < TOL
+
+
+def pin_head_select_shared_query():
+    """Every head of a group with the same query: the heads pick the same chunks, so the union
+    is one head's top-k, which ranks like the pooled score (pooled = own score + log G)."""
+    cfg = SMALL.with_(Hq=8)
+    inp = make_decode(cfg, seed=33)
+    q = inp.q.view(cfg.B, cfg.Hkv, cfg.G, cfg.d)
+    q[:] = q[:, :, :1, :].clone()
+    a = oracle_decode(inp)
+    b = oracle_decode(inp, head_select=1)
+    assert np.array_equal(b.sel[..., : cfg.k], a.sel) and (b.sel[..., cfg.k:] == -1).all()
+    assert np.abs(a.out - b.out).max() < TOL
+    assert np.abs(b.chunk_scores.reshape(cfg.B, cfg.Hkv, cfg.G, -1)[:, :, 0] + math.log(cfg.G)
+                  - a.chunk_scores).max() < 1e-10
+
+
+def pin_head_select_union_bounds_and_dense():
+    """k_eff <= |union| <= min(G k, H), ascending; each head's own argsort top-k (g = 1) is in
+    the union; with k = all the set is the whole cache (textbook attention)."""
+    cfg = SMALL.with_(Hq=8, g=1, k=3, B=1)
+    inp = make_decode(cfg, seed=34)
+    r = oracle_decode(inp, head_select=1)
+    q, gk = f64(inp.q), f64(inp.gist_k)
+    for kv in range(cfg.Hkv):
+        u = r.sel[0, kv][r.sel[0, kv] >= 0]
+        assert cfg.k <= len(u) <= min(cfg.G * cfg.k, cfg.H) and (np.diff(u) > 0).all()
+        for h in range(kv * cfg.G, (kv + 1) * cfg.G):
+            s = gk[0, kv, :, 0] @ q[0, h]
+            assert set(np.argsort(-s, kind="stable")[: cfg.k]) <= set(u.tolist())
+    c = SMALL.with_(k=SMALL.H, B=1)
+    inp = make_decode(c, seed=35)
+    r = oracle_decode(inp, head_select=1)
+    K, V = _logical_kv(inp)
+    q = f64(inp.q)
+    for h in range(c.Hq):
+        kv = h // c.G
+        kt = np.concatenate([f64(inp.gist_k)[0, kv].reshape(-1, c.d), K[0, kv].reshape(-1, c.d)[: c.N]])
+        vt = np.concatenate([f64(inp.gist_v)[0, kv].reshape(-1, c.d), V[0, kv].reshape(-1, c.d)[: c.N]])
+        o, l = sdpa(q[0, h], kt, vt)
+        assert np.abs(r.out[0, h] - o).max() < TOL and abs(r.lse[0, h] - l) < TOL
 
 
 def pin_top_p_brute_force():
