@@ -43,7 +43,7 @@ def decode_bytes(cfg, k=None, gist_mode="all", k_eff_mean=None):
     else:
         gist_rows = cfg.H * cfg.g
         k_eff = min(k, cfg.H)
-    if k_eff_mean is not None:          # top-p: chunks actually kept, averaged over units
+    if k_eff_mean is not None:   # top-p, per-head union: chunks actually unfolded, unit mean
         k_eff = k_eff_mean
     if gist_mode == "selected":
         sel_v = k_eff * cfg.g + (min(cfg.k2, cfg.nG) * cfg.g if cfg.levels == 2 else 0)
@@ -100,9 +100,11 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(inp, budget_s):
-    """Time the fp64 CPU oracle (as it stands) on this workload's instance 0.  Full calls if
-    one fits the budget, else a seeded subset of units scaled to whole calls."""
+def cpu_baseline(inp, budget_s, **mode):
+    """Time the fp64 CPU oracle (as it stands) on this workload's instance 0, in the same
+    token-set and selection mode as the GPU calls (``mode``: the oracle's gists_in_softmax,
+    top_p and head_select).  Full calls if one fits the budget, else a seeded subset of units
+    scaled to whole calls."""
     import numpy as np
     import oracle
     from top_chunk_sparse_amd.synth import bf16_bits
@@ -113,7 +115,7 @@ def cpu_baseline(inp, budget_s):
                 gist2_k=None if inp.gist2_k is None else bf16_bits(inp.gist2_k),
                 gist2_v=None if inp.gist2_v is None else bf16_bits(inp.gist2_v))
     args = dict(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, N=c.N, C_=c.C, g=c.g, k=c.k, gate=c.gate,
-                levels=c.levels, J=c.J, k2=c.k2, **host)
+                levels=c.levels, J=c.J, k2=c.k2, **host, **mode)
     units = c.B * c.Hkv
     probe = list(range(0, units, max(1, units // 8)))[:8]
     oracle.decode(units=probe[:1], **args)          # untimed: library load, first touch
@@ -290,6 +292,9 @@ def main():
                     help="decode: override k (a value >= the chunk count selects every chunk)")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="decode selection: 0 = top-k; in (0, 1] = top-p with a cap of k")
+    ap.add_argument("--head-select", action="store_true",
+                    help="decode selection: every query head picks its own top-k and the union "
+                         "is unfolded (one level; runs the workload with the gate off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -320,13 +325,16 @@ def main():
         cfg = cfg.with_(N=args.tokens)
     if args.k >= 0:
         cfg = cfg.with_(k=args.k)
+    if args.head_select:
+        cfg = cfg.with_(gate=0)   # per-head selection carries no gate
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     R = max(1, args.instances)
     print(f"# generating {R} instance(s) of {cfg.name}", file=sys.stderr, flush=True)
     insts = [make_decode(cfg, configs.seed_for(cfg.name, r), device=dev) for r in range(R)]
     gmode = ops.GISTS_SELECTED if args.gist_mode == "selected" else ops.GISTS_ALL
-    calls = [ops.DecodeCall(inp, with_scores=False, gist_mode=gmode, top_p=args.top_p)
+    calls = [ops.DecodeCall(inp, with_scores=False, gist_mode=gmode, top_p=args.top_p,
+                            head_select=int(args.head_select))
              for inp in insts]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
@@ -370,7 +378,7 @@ def main():
     print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
 
     k_eff_mean = None
-    if args.top_p > 0:   # chunks each unit kept, from the calls' own selections
+    if args.top_p > 0 or args.head_select:   # chunks each unit kept, from the calls' own selections
         import numpy as np
         k_eff_mean = float(np.mean([(c.sel >= 0).sum(-1).float().mean().item() for c in calls]))
     total_bytes, parts = decode_bytes(cfg, gist_mode=args.gist_mode, k_eff_mean=k_eff_mean)
@@ -389,7 +397,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(insts[0], args.cpu_seconds)
+        cpu = cpu_baseline(insts[0], args.cpu_seconds,
+                           gists_in_softmax="selected" if args.gist_mode == "selected" else True,
+                           top_p=args.top_p, head_select=int(args.head_select))
 
     rec = {
         "metric": METRIC,
@@ -409,7 +419,9 @@ def main():
                    "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "N": cfg.N, "C": cfg.C, "g": cfg.g, "k": cfg.k, "gate": "sas" if cfg.gate else
                    "none", "levels": cfg.levels, "paged": cfg.paged, "gists": args.gist_mode,
-                   "top_p": args.top_p or None, "inputs": "bf16",
+                   "top_p": args.top_p or None,
+                   "select": "per-head union" if args.head_select else "per KV head",
+                   "inputs": "bf16",
                    "instances_rotated": R},
         "effective_GBps": round(eff_gbps, 1),
         "chunks_selected_mean": k_eff_mean,

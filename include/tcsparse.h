@@ -32,6 +32,13 @@
  *   pages compare against top-p (SSA figure 2) without spelling the rule out; this is the
  *   reading used here.  The shares are summed in fp32 in rank order, so a selection may differ
  *   from an exact evaluation when the running share crosses top_p within rounding.
+ *   select_mode = TCS_SELECT_PER_HEAD (one level, no gate, top_p = 0) replaces steps 2-3 by
+ *   per-head selection (appendix A: each head selects its chunks on its own and their union is
+ *   unfolded into the shared KV): query head h of the group scores chunk c by
+ *   s_h[c] = log sum_t exp(l[h][c][t]), takes its own top min(k, |H|) as in step 3, and every
+ *   head of the group attends, in step 5, to the raw tokens of the union U of the G heads'
+ *   choices (k_eff <= |U| <= min(G k, |H|)).  sel then holds U ascending with G * k entries per
+ *   (b, kv) (-1 padded), and chunk_scores holds s_h, one row per query head.
  *   Two levels (levels = 2; section 3.5 and appendix B.2): level-2 gists summarise groups of J
  *   consecutive historical chunks.  The group scores s2[r] (step 2 over gist2_k) pick the top
  *   k2 groups; the member chunks of the chosen groups are the candidates; steps 1-3 run over
@@ -59,8 +66,10 @@
  *   out          fp32 [B][Hq][d]
  *   lse          fp32 [B][Hq]                   optional (NULL)
  *   sel          int32 [B][Hkv][k]              optional; ascending chunk ids, -1 padded
+ *                                               ([B][Hkv][G*k] with TCS_SELECT_PER_HEAD)
  *   sel_groups   int32 [B][Hkv][k2]             optional; levels = 2
  *   chunk_scores fp32 [B][Hkv][M-1]             optional; -inf for chunks not scored
+ *                                               ([B][Hq][M-1] with TCS_SELECT_PER_HEAD)
  *   Prefill: q bf16 [B][Hq][T][d]; k, v bf16 [B][Hkv][T][d]; S fp32 [B][Hkv][nb][nb] with
  *   nb = T / blk (entries j >= i are ignored); out fp32 [B][Hq][T][d]; lse fp32 [B][Hq][T]
  *   (optional); sel int32 [B][Hkv][nb][k] (optional, ascending, -1 padded).
@@ -88,7 +97,7 @@
  *
  * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024;
  * B * Hkv <= 16384; TCS_GISTS_SELECTED: C + g <= 1024; top_p > 0: one level
- * and k <= 256; two levels:
+ * and k <= 256; TCS_SELECT_PER_HEAD: one level, no gate, top_p = 0, M - 1 <= 65536; two levels:
  * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk.
  * Other shapes return TCS_ERR_UNSUPPORTED.
  */
@@ -102,7 +111,7 @@
 extern "C" {
 #endif
 
-#define TCS_ABI_VERSION 3
+#define TCS_ABI_VERSION 4
 
 typedef enum {
     TCS_OK = 0,
@@ -115,6 +124,7 @@ typedef enum {
 
 enum { TCS_GATE_NONE = 0, TCS_GATE_SAS = 1 };
 enum { TCS_GISTS_ALL = 0, TCS_GISTS_SELECTED = 1 };   /* which gists enter the softmax */
+enum { TCS_SELECT_KV_HEAD = 0, TCS_SELECT_PER_HEAD = 1 };   /* who selects the chunks      */
 
 typedef struct {
     int32_t struct_size;   /* = sizeof(tcs_decode_params) */
@@ -133,6 +143,7 @@ typedef struct {
     int32_t gist_cap;      /* chunk capacity of gist_k/v per (b, kv); 0 means M-1          */
     float scale;           /* logit scale; 0 means 1/sqrt(d)                              */
     float top_p;           /* 0: top-k.  In (0, 1]: top-p with a cap of k (one level)     */
+    int32_t select_mode;   /* TCS_SELECT_KV_HEAD or TCS_SELECT_PER_HEAD                   */
 } tcs_decode_params;
 
 /* Host-only: bytes of workspace sparse_attn_decode needs for these parameters. */

@@ -80,9 +80,10 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
     G = c.G
     gmode = "selected" if getattr(call, "gist_mode", 0) == 1 else True
     top_p = float(call.p.top_p)
+    heads = int(getattr(call, "head_select", 0))
     if ref is None:
         ref = oracle_decode(inp, k=call.p.k, units=units, scale=float(call.p.scale),
-                            gists_in_softmax=gmode, top_p=top_p)
+                            gists_in_softmax=gmode, top_p=top_p, head_select=heads)
     all_units = list(range(c.B * c.Hkv)) if units is None else list(units)
     gsel = call.sel.cpu().numpy()
     gout = call.out.cpu().double().numpy()
@@ -100,7 +101,9 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
         gaps = []
         if c.levels == 2:
             gaps.append(boundary_gap(ref.group_scores[b, kv], c.k2))
-        if top_p > 0:
+        if heads:   # every head's own boundary decides its part of the union
+            gaps += [boundary_gap(ref.chunk_scores[b, kv * G + h], k) for h in range(G)]
+        elif top_p > 0:
             ke_ref = int((ref.sel[b, kv] >= 0).sum())
             gaps.append(boundary_gap(ref.chunk_scores[b, kv], ke_ref))
             gaps.append(top_p_margin(ref.chunk_scores[b, kv], top_p, k))
@@ -114,7 +117,8 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
         forced = np.ascontiguousarray(gsel.astype(np.int32))
         fg = np.ascontiguousarray(ggrp.astype(np.int32)) if ggrp is not None else None
         ref2 = oracle_decode(inp, k=k, units=excused, forced_sel=forced, forced_groups=fg,
-                             scale=float(call.p.scale), gists_in_softmax=gmode)
+                             scale=float(call.p.scale), gists_in_softmax=gmode,
+                             head_select=heads)
         for u in excused:
             b, kv = divmod(u, c.Hkv)
             ref.out[b, kv * G:(kv + 1) * G] = ref2.out[b, kv * G:(kv + 1) * G]
@@ -129,9 +133,13 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
     scored_units = [u for u in all_units if not (c.levels == 2 and u in excused)]
     if call.chunk_scores is not None and c.H > 0 and scored_units:
         gs = call.chunk_scores.cpu().double().numpy()
+        rs = ref.chunk_scores
+        if heads:   # one row per query head: view as [B][Hkv][G * H]
+            gs = gs.reshape(c.B, c.Hkv, -1)
+            rs = rs.reshape(c.B, c.Hkv, -1)
         ub = np.array([u // c.Hkv for u in scored_units])
         uk = np.array([u % c.Hkv for u in scored_units])
-        a, r_ = gs[ub, uk], ref.chunk_scores[ub, uk]
+        a, r_ = gs[ub, uk], rs[ub, uk]
         fin = np.isfinite(r_)
         assert (np.isfinite(a) == fin).all(), "chunk_scores: scored set differs"
         if fin.any():

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ops.lib().tcs_abi_version() == 3
+    assert ops.lib().tcs_abi_version() == 4
     for code in range(6):
         assert ops.status_str(code)
     assert ops.status_str(99) == "unknown status"
@@ -58,6 +58,14 @@ def test_selected_gists_two_levels_slots():
     a = ops.decode_workspace_size(P(**kw))
     b = ops.decode_workspace_size(P(gist_mode=1, **kw))
     assert 0 < b < a
+
+
+def test_per_head_selection_workspace():
+    # G candidate lists per slice and G * k union entries per unit
+    a = ops.decode_workspace_size(P(N=64 * 500))
+    b = ops.decode_workspace_size(P(N=64 * 500, select_mode=1))
+    assert 0 < a < b
+    assert ops.decode_workspace_size(P(select_mode=1, C_=16, g=1, N=16 * 65536 + 1)) > 0
 
 
 def test_workspace_size_grows_with_work():
@@ -95,6 +103,11 @@ def test_workspace_size_grows_with_work():
     (dict(top_p=0.5, levels=2, J=4, k2=2), ops.TCS_ERR_UNSUPPORTED),
     (dict(top_p=0.5, k=257), ops.TCS_ERR_UNSUPPORTED),
     (dict(gist_mode=1, C_=1024, g=8, N=5000), ops.TCS_ERR_UNSUPPORTED),  # C + g > 1024
+    (dict(select_mode=1, gate=1), ops.TCS_ERR_UNSUPPORTED),       # per-head selection: no gate
+    (dict(select_mode=1, top_p=0.5), ops.TCS_ERR_UNSUPPORTED),    # ... no top-p
+    (dict(select_mode=1, levels=2, J=4, k2=2), ops.TCS_ERR_UNSUPPORTED),   # ... one level
+    (dict(select_mode=1, C_=16, g=1, N=16 * 65537 + 1), ops.TCS_ERR_UNSUPPORTED),   # H > 65536
+    (dict(select_mode=2), ops.TCS_ERR_SHAPE),
 ])
 def test_decode_rejects_bad_params(kw, code):
     p = P(**kw)

@@ -24,12 +24,12 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_case(cfg, seed, units=None, gist_mode=0, top_p=0.0, **kw):
+def run_case(cfg, seed, units=None, gist_mode=0, top_p=0.0, head_select=0, **kw):
     say(f"[decode] {cfg.name} seed={seed} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} "
         f"N={cfg.N} C={cfg.C} g={cfg.g} k={cfg.k} gate={cfg.gate} levels={cfg.levels} "
-        f"gist_mode={gist_mode} top_p={top_p} {kw}")
+        f"gist_mode={gist_mode} top_p={top_p} head_select={head_select} {kw}")
     inp = make_decode(cfg, seed, device=DEV, **kw)
-    call = DecodeCall(inp, gist_mode=gist_mode, top_p=top_p)()
+    call = DecodeCall(inp, gist_mode=gist_mode, top_p=top_p, head_select=head_select)()
     torch.cuda.synchronize()
     st = check_decode(inp, call, units=units)
     say("   ", st)
@@ -102,6 +102,46 @@ def test_selected_gists_full(name):
     torch.cuda.empty_cache()
 
 
+# Per-head selection with the union unfolded (one level, no gate), every gist or the selected
+# chunks' gists in the softmax.
+HEADS = [
+    (SMALL, 0),
+    (SMALL.with_(Hq=16), 0),                                          # G = 8
+    (SMALL.with_(Hq=4), 1),                                           # G = 2, selected gists
+    (SMALL.with_(Hq=2, Hkv=2), 0),                                    # G = 1
+    (SMALL.with_(d=64, g=3, C=24, N=61 * 24 + 1), 1),
+    (SMALL.with_(k=0), 0),
+    (SMALL.with_(k=10 ** 4), 0),                                      # every chunk
+    (SMALL.with_(N=20, C=32), 0),                                     # no historical chunk
+    (SMALL.with_(N=33, C=32), 1),                                     # one historical chunk
+    (SMALL.with_(g=1, C=64, N=300 * 64), 0),                          # 2 slices of 256 chunks
+    # G = 8, 128 chunks per slice, 24 slices: 475 candidates per head reach the merge, which
+    # then ranks them from global memory
+    (SMALL.with_(g=1, C=16, N=16 * 3000 + 5, k=20, Hq=16, d=64), 0),
+    (SMALL.with_(g=16, C=128, N=37 * 128 + 100, d=64), 1),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(HEADS)), ids=[f"hs{i}" for i in range(len(HEADS))])
+def test_head_select_variants(idx):
+    cfg, gmode = HEADS[idx]
+    run_case(cfg, seed=700 + idx, head_select=1, gist_mode=gmode, max_chunks=cfg.M + 2,
+             extra_pages=1)
+
+
+@pytest.mark.parametrize("name", ["llama32_1b_decode_32k", "llama31_8b_decode_128k"])
+def test_head_select_full(name):
+    cfg = configs.DECODE_CONFIGS[name].with_(gate=0)
+    inp, call, st = run_case(cfg, configs.seed_for(name), head_select=1)
+    assert st["excused"] <= max(1, st["units"] // 100)
+    u = call.sel.cpu().numpy()
+    n = (u >= 0).sum(-1)
+    say(f"    union size: min {n.min()} mean {n.mean():.1f} max {n.max()} (k = {cfg.k}, G = {cfg.G})")
+    assert (n >= min(cfg.k, cfg.H)).all() and (n <= min(cfg.G * cfg.k, cfg.H)).all()
+    del inp, call
+    torch.cuda.empty_cache()
+
+
 # Top-p selection with a cap of k chunks (one level).
 TOP_P = [
     (SMALL.with_(k=20), 0.3),
@@ -140,12 +180,18 @@ LIMITS = [
     (SMALL.with_(levels=2, J=16, k2=64, k=40, g=64, C=64, d=64, N=1024 * 64 + 10, n_plant=8,
                  plant_groups=4), 1, 0.0),
 ]
+# per-head selection over the largest union bitmap: 65536 historical chunks
+HEAD_LIMIT = SMALL.with_(B=1, Hkv=1, Hq=8, g=1, C=16, d=64, N=16 * 65536 + 7, k=50, n_plant=4)
 
 
 @pytest.mark.parametrize("idx", range(len(LIMITS)), ids=[f"lim{i}" for i in range(len(LIMITS))])
 def test_limit_shapes(idx):
     cfg, gmode, tp = LIMITS[idx]
     run_case(cfg, seed=500 + idx, gist_mode=gmode, top_p=tp)
+
+
+def test_head_select_limit():
+    run_case(HEAD_LIMIT, seed=520, head_select=1)
 
 
 # One unit over many chunks: ~94 and ~141 gist slices, so the final merge takes its partials in

@@ -37,6 +37,7 @@ constexpr int kTargetWorkgroups = TCS_TARGET_WORKGROUPS;   // grid size the pass
 constexpr int kChunkTargetWorkgroups = TCS_CHUNK_TARGET_WORKGROUPS;   // chunk-attention grid
 constexpr int kMaxTopPK = 256;   // top-p: the capped top-k is ranked in one workgroup's LDS
 constexpr int kMinSliceRows = 64;
+constexpr int kMaxHeadSelectChunks = 65536;   // per-head selection: union bitmap held in LDS
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -60,6 +61,7 @@ void plan_slices(long long units, int nchunks, int g, int* slices, int* cps) {
 
 struct DecodePlan {
     int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, cpw, nslots, kcap1, kcap2;
+    int sk;   // entries per unit in sel: k, or G * k with per-head selection
     float sigma;
     // workspace offsets (bytes)
     size_t off_cnt, off_cs1, off_ci1, off_lse1, off_cs2, off_ci2, off_sel, off_gamma, off_gsel,
@@ -78,6 +80,8 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (p->gist_mode != TCS_GISTS_ALL && p->gist_mode != TCS_GISTS_SELECTED) return TCS_ERR_SHAPE;
     if (!(p->scale >= 0.f) || std::isinf(p->scale)) return TCS_ERR_SHAPE;
     if (!(p->top_p >= 0.f && p->top_p <= 1.f)) return TCS_ERR_SHAPE;
+    if (p->select_mode != TCS_SELECT_KV_HEAD && p->select_mode != TCS_SELECT_PER_HEAD)
+        return TCS_ERR_SHAPE;
     const int G = p->Hq / p->Hkv;
     const long long units = (long long)p->B * p->Hkv;
     const int M = (int)(((long long)p->N + p->C - 1) / p->C);
@@ -91,6 +95,10 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     const bool sel_gists = p->gist_mode == TCS_GISTS_SELECTED;
     if (sel_gists && p->C + p->g > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
     if (p->top_p > 0.f && (p->levels != 1 || p->k > kMaxTopPK)) return TCS_ERR_UNSUPPORTED;
+    const bool heads = p->select_mode == TCS_SELECT_PER_HEAD;
+    if (heads && (p->levels != 1 || p->gate_mode != TCS_GATE_NONE || p->top_p > 0.f ||
+                  H > kMaxHeadSelectChunks))
+        return TCS_ERR_UNSUPPORTED;
     pl->G = G;
     pl->M = M;
     pl->H = H;
@@ -115,12 +123,15 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
         pl->k2e = 0;
         pl->S2 = 0;
         pl->cps2 = 1;
-        plan_slices(units, H, p->g, &pl->S1, &pl->cps1);
+        // per-head selection keeps G scores per chunk of a slice in LDS
+        plan_slices(units, H, heads ? std::max(p->g, G) : p->g, &pl->S1, &pl->cps1);
         ksel = p->k < H ? p->k : H;
         pl->kcap2 = 0;
         pl->kcap1 = p->k < pl->cps1 ? p->k : pl->cps1;
+        if (heads) ksel = (int)std::min<long long>((long long)G * ksel, H);   // union size bound
     }
     pl->kslots = ksel;
+    pl->sk = heads ? G * p->k : p->k;
     // chunk attention: enough workgroups to fill the GPU, one or more chunks each
     long long cpw = units * (ksel + 1) / kChunkTargetWorkgroups;
     const long long slot_rows = p->C + (sel_gists ? p->g : 0);   // rows a slot holds in LDS
@@ -139,12 +150,13 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
     pl->off_cnt = take(sizeof(unsigned) * kCounterWords);
-    pl->off_cs1 = take(sizeof(float) * (size_t)n1(units * s1 * pl->kcap1));
-    pl->off_ci1 = take(sizeof(int32_t) * (size_t)n1(units * s1 * pl->kcap1));
+    const long long nl = heads ? G : 1;   // candidate lists per slice: one per selecting head
+    pl->off_cs1 = take(sizeof(float) * (size_t)n1(units * nl * s1 * pl->kcap1));
+    pl->off_ci1 = take(sizeof(int32_t) * (size_t)n1(units * nl * s1 * pl->kcap1));
     pl->off_lse1 = take(sizeof(float) * (size_t)n1(units * s1 * 2));
     pl->off_cs2 = take(sizeof(float) * (size_t)n1(units * pl->S2 * pl->kcap2));
     pl->off_ci2 = take(sizeof(int32_t) * (size_t)n1(units * pl->S2 * pl->kcap2));
-    pl->off_sel = take(sizeof(int32_t) * (size_t)n1(units * p->k));
+    pl->off_sel = take(sizeof(int32_t) * (size_t)n1(units * pl->sk));
     pl->off_gamma = take(sizeof(float) * (size_t)n1(units * p->k));
     pl->off_gsel = take(sizeof(int32_t) * (size_t)n1(units * p->k2));
     pl->off_acc = take(sizeof(float) * (size_t)(BH * pl->nslots * p->d));
@@ -286,6 +298,7 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         ga.slot0 = slot;
         ga.selo = chunk_sel;
         ga.scores_only = p->gist_mode == TCS_GISTS_SELECTED;
+        ga.heads = p->select_mode == TCS_SELECT_PER_HEAD;
         e = tcs::launch_gist(ga, s);
         if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
         if (!ga.scores_only) slot += pl.S1;
@@ -348,9 +361,9 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         slot += pl.k2e;
         chunks_chosen = pl.k2e > 0;
     }
-    if (!chunks_chosen && p->k > 0) {
+    if (!chunks_chosen && pl.sk > 0) {
         // no scoring pass ran (no historical chunk, or no group chosen): nothing is selected
-        e = tcs::launch_fill(sel_p, (long long)units * p->k, -1, s);
+        e = tcs::launch_fill(sel_p, (long long)units * pl.sk, -1, s);
         if (e != hipSuccess) return TCS_ERR_HIP;
     }
 
@@ -361,7 +374,7 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     ca.page_table = page_table;
     ca.B = p->B; ca.Hq = p->Hq; ca.Hkv = p->Hkv; ca.d = p->d; ca.C = p->C; ca.N = p->N;
     ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
-    ca.sel = sel_p; ca.gamma = gamma; ca.k = p->k; ca.kslots = pl.kslots; ca.cpw = pl.cpw;
+    ca.sel = sel_p; ca.gamma = gamma; ca.k = pl.sk; ca.kslots = pl.kslots; ca.cpw = pl.cpw;
     ca.sigma = pl.sigma; ca.part = part; ca.slot0 = slot;
     ca.counter = cnt + kCntChunk;
     ca.out = out;

@@ -419,6 +419,90 @@ __device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int 
     }
 }
 
+// Per-head selection.  Each slice keeps, for every head h of the group, that head's top-k of
+// its items in the hand-off lists [unit][h][slice][kcap] (one head's lists are contiguous).
+// The last workgroup of the unit merges each head's lists into that head's top-k, marks the
+// chosen chunks in an LDS bitmap over the unit's chunks, and writes the union in ascending
+// order, -1 padded to G * k entries.
+constexpr int kMaxHeadWords = 2048;   // bitmap words: up to 65536 historical chunks
+
+template <int G>
+__device__ __forceinline__ void select_epilogue_heads(const SelectOut& so, int u, int slot,
+                                                      int nslices, const float* s_score,
+                                                      int item0, int nitems, int last_items,
+                                                      void* scratch, MergeCand& mc, int* s_flag,
+                                                      unsigned* bits) {
+    const int tid = threadIdx.x;
+    const int kc = so.k < nitems ? so.k : nitems;
+    for (int h = 0; h < G; ++h) {
+        const float* sh = s_score + h * nitems;   // this head's scores, [item]
+        const long long base = (((long long)u * G + h) * nslices + slot) * so.kcap;
+        auto emit = [&](int j, int i) {
+            st_shared_dev(so.cand_score + base + j, sh[i]);
+            st_shared_dev(so.cand_idx + base + j, (int32_t)(item0 + i));
+        };
+        auto sc = [&](int i) { return sh[i]; };
+        if (kc == nitems) {
+            for (int i = tid; i < nitems; i += 256) emit(i, i);
+        } else if (nitems <= 256) {
+            small_topk(nitems, so.k, sc, emit, *reinterpret_cast<SmallTopkSmem*>(scratch));
+        } else {
+            block_topk(nitems, so.k, sc, emit, *reinterpret_cast<TopkSmem*>(scratch));
+        }
+        __syncthreads();   // the next head reuses the top-k scratch
+    }
+    if (!arrive_last(so.counter + u, (unsigned)nslices, s_flag)) return;
+
+    // ---- last workgroup of the unit: every head's top-k, then the union -------------------
+    const int nw = (so.H + 31) >> 5;
+    for (int w = tid; w < nw; w += 256) bits[w] = 0u;
+    const int ncand = (nslices - 1) * so.kcap + (so.k < last_items ? so.k : last_items);
+    const bool staged = ncand <= 256;
+    for (int h = 0; h < G; ++h) {
+        const long long base = ((long long)u * G + h) * nslices * so.kcap;
+        const float* ucs = so.cand_score + base;
+        const int32_t* uci = so.cand_idx + base;
+        if (staged && tid < ncand) {
+            mc.score[tid] = ld_shared_dev(ucs + tid);
+            mc.idx[tid] = ld_shared_dev(uci + tid);
+        }
+        __syncthreads();   // staged candidates (and, for h = 0, the cleared bitmap) visible
+        auto score_at = [&](int i) { return staged ? mc.score[i] : ld_shared_dev(ucs + i); };
+        auto mark = [&](int, int i) {
+            const int32_t c = staged ? mc.idx[i] : ld_shared_dev(uci + i);
+            atomicOr(&bits[c >> 5], 1u << (c & 31));
+        };
+        if (so.k >= ncand) {
+            for (int i = tid; i < ncand; i += 256) mark(i, i);
+        } else if (staged) {
+            small_topk(ncand, so.k, score_at, mark, *reinterpret_cast<SmallTopkSmem*>(scratch));
+        } else {
+            block_topk(ncand, so.k, score_at, mark, *reinterpret_cast<TopkSmem*>(scratch));
+        }
+        __syncthreads();   // the next head reuses the staging and the top-k scratch
+    }
+    // compaction: thread t owns a run of bitmap words; its first position is the number of
+    // chosen chunks in the words before its run
+    const int sk = G * so.k;
+    int32_t* sel = so.sel + (long long)u * sk;
+    const int wpt = (nw + 255) / 256;
+    const int w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
+    const int first = block_exclusive_scan(cnt, reinterpret_cast<SmallTopkSmem*>(scratch)->scan);
+    if (tid == 255) *s_flag = first + cnt;   // the union's size
+    int pos = first;
+    for (int w = w0; w < w1; ++w) {
+        unsigned m = bits[w];
+        while (m) {
+            sel[pos++] = w * 32 + (__ffs(m) - 1);
+            m &= m - 1u;
+        }
+    }
+    __syncthreads();
+    for (int j = *s_flag + tid; j < sk; j += 256) sel[j] = -1;
+}
+
 // ---------------------------------------------------------------------------------------
 // gist_kernel: grid (slices, units).  Range mode: slice y covers items (chunks, or level-2
 // groups) [y*ips, min((y+1)*ips, nitems)).  Group mode (a.groups != null): slice y covers the
@@ -461,11 +545,15 @@ __device__ __forceinline__ void fold_rows(GistSmem<D, G>& sm, const Partials& pa
     rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, part, bh0, slot);
 }
 
-// META: the group-mode slices of the selected-summary set at two levels, whose softmax tokens
-// are their groups' own level-2 gists (a.pk / a.pv); a separate instantiation, so the other
-// passes compile as if it did not exist.
-template <int D, int G, bool META>
-__device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& sm, int y, int u) {
+// Kernel variants, each its own instantiation so that the others compile as if it did not
+// exist.  kGistMeta: the group-mode slices of the selected-summary set at two levels, whose
+// softmax tokens are their groups' own level-2 gists (a.pk / a.pv).  kGistHeads: per-head
+// selection (a.heads), with the union bitmap in `bits`.
+constexpr int kGistPlain = 0, kGistMeta = 1, kGistHeads = 2;
+
+template <int D, int G, int MODE>
+__device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& sm, unsigned* bits,
+                                          int y, int u) {
     using RS = RowStream<D, G>;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
@@ -495,8 +583,23 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
     uint4 vfirst[TCS_V_U];
     if (!a.scores_only) rs.template prefetch<TCS_V_U>(V, nrows, vfirst);
     __syncthreads();
-    // pooled item scores: log-sum-exp over the G heads and g gists of each item
     const int ng = a.g * G;   // logits per item
+    if constexpr (MODE == kGistHeads) {
+        // each head's own item scores, [h][item]: log-sum-exp over the item's g gist logits of
+        // that head (logit of row t, head h at lg[(item g + t) G + h])
+        for (int x = threadIdx.x; x < nit * G; x += 256) {
+            const int c = x / G, h = x - c * G;
+            const float* l = sm.x.lg + c * ng + h;
+            float mx = -INFINITY, z = 0.f;
+            for (int t = 0; t < a.g; ++t) mx = fmaxf(mx, l[t * G]);
+            for (int t = 0; t < a.g; ++t) z += expf(l[t * G] - mx);
+            const float sc = mx + logf(z);
+            sm.score[h * nit + c] = sc;
+            if (a.scores_out)
+                a.scores_out[((long long)u * G + h) * a.score_stride + c0 + c] = sc;
+        }
+    } else
+    // pooled item scores: log-sum-exp over the G heads and g gists of each item
     for (int c = threadIdx.x; c < nit; c += 256) {
         const float* x = sm.x.lg + c * ng;
         float mx = -INFINITY, z = 0.f;
@@ -524,7 +627,7 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
     }
     if (!a.scores_only) {   // the gists are tokens of the softmax set: fold them in here
         fold_rows<D, G>(sm, a.part, V, nrows, vfirst, bh0, a.slot0 + y);
-    } else if constexpr (META) {
+    } else if constexpr (MODE == kGistMeta) {
         // selected summaries at two levels: this group's own level-2 gists are the tokens
         const int r = a.groups[(long long)u * a.k2 + y];
         const long long off = (long long)u * a.p_unit_stride + (long long)r * a.g * D;
@@ -539,17 +642,33 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
         fold_rows<D, G>(sm, a.part, a.pv + off, a.g, vfirst, bh0, a.slot0 + y);
     }
     __syncthreads();
-    select_epilogue(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.lse, &sm.x,
-                    sm.mc, &sm.flag, sm.chosen, sm.red,
-                    // the slice scores are dead once the slice's list is out: the unit's
-                    // top-p cut reuses their space
-                    *reinterpret_cast<TopPSmem*>(sm.score), &sm.tp_keep);
+    if constexpr (MODE == kGistHeads) {
+        select_epilogue_heads<G>(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.x,
+                                 sm.mc, &sm.flag, bits);
+    } else {
+        select_epilogue(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.lse, &sm.x,
+                        sm.mc, &sm.flag, sm.chosen, sm.red,
+                        // the slice scores are dead once the slice's list is out: the unit's
+                        // top-p cut reuses their space
+                        *reinterpret_cast<TopPSmem*>(sm.score), &sm.tp_keep);
+    }
 }
 
-template <int D, int G, bool META>
+template <int D, int G>
+struct GistHeadsSmem {
+    GistSmem<D, G> base;
+    unsigned bits[kMaxHeadWords];
+};
+
+template <int D, int G, int MODE>
 __global__ void __launch_bounds__(256) gist_kernel(GistLaunch a) {
-    __shared__ GistSmem<D, G> sm;
-    gist_item<D, G, META>(a, sm, blockIdx.x, blockIdx.y);
+    if constexpr (MODE == kGistHeads) {
+        __shared__ GistHeadsSmem<D, G> sm;
+        gist_item<D, G, MODE>(a, sm.base, sm.bits, blockIdx.x, blockIdx.y);
+    } else {
+        __shared__ GistSmem<D, G> sm;
+        gist_item<D, G, MODE>(a, sm, nullptr, blockIdx.x, blockIdx.y);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -796,26 +915,40 @@ __global__ void fill_kernel(int32_t* p, long long n, int32_t v) {
 // ---------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------
-template <int D, bool META>
+template <int D, int MODE>
 static hipError_t gist_d(const GistLaunch& a, hipStream_t s, dim3 grid) {
     switch (a.Hq / a.Hkv) {
-        case 1: gist_kernel<D, 1, META><<<grid, 256, 0, s>>>(a); break;
-        case 2: gist_kernel<D, 2, META><<<grid, 256, 0, s>>>(a); break;
-        case 4: gist_kernel<D, 4, META><<<grid, 256, 0, s>>>(a); break;
-        case 8: gist_kernel<D, 8, META><<<grid, 256, 0, s>>>(a); break;
+        case 1: gist_kernel<D, 1, MODE><<<grid, 256, 0, s>>>(a); break;
+        case 2: gist_kernel<D, 2, MODE><<<grid, 256, 0, s>>>(a); break;
+        case 4: gist_kernel<D, 4, MODE><<<grid, 256, 0, s>>>(a); break;
+        case 8: gist_kernel<D, 8, MODE><<<grid, 256, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t gist_mode(const GistLaunch& a, hipStream_t s, dim3 grid) {
+    return a.d == 128 ? gist_d<128, MODE>(a, s, grid) : gist_d<64, MODE>(a, s, grid);
 }
 
 hipError_t launch_gist(const GistLaunch& a, hipStream_t s) {
     if (a.slices <= 0) return hipSuccess;
     dim3 grid(a.slices, a.B * a.Hkv);
     if (a.pk) {   // only group mode with scores_only carries level-2 gists for the partials
-        if (!a.groups || !a.scores_only || !a.pv) return hipErrorInvalidValue;
-        return a.d == 128 ? gist_d<128, true>(a, s, grid) : gist_d<64, true>(a, s, grid);
+        if (!a.groups || !a.scores_only || !a.pv || a.heads) return hipErrorInvalidValue;
+        return gist_mode<kGistMeta>(a, s, grid);
     }
-    return a.d == 128 ? gist_d<128, false>(a, s, grid) : gist_d<64, false>(a, s, grid);
+    if (a.heads) {
+        // range mode only; every head's scores of a slice fit the score buffer; the union
+        // bitmap covers every chunk
+        const int G = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
+        if (a.groups || (long long)a.items_per_slice * G > kMaxSliceRows ||
+            a.nitems > kMaxHeadWords * 32 || a.selo.H != a.nitems)
+            return hipErrorInvalidValue;
+        return gist_mode<kGistHeads>(a, s, grid);
+    }
+    return gist_mode<kGistPlain>(a, s, grid);
 }
 
 template <int D>

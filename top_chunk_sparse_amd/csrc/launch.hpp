@@ -46,6 +46,10 @@ struct GistLaunch {
     int slot0;
     SelectOut selo;
     int scores_only;          // 1: score and select only (no gist softmax partials)
+    // range mode, one level: every query head of the group selects its own top-k (score =
+    // log-sum-exp of its own g gist logits) and the union is written to selo.sel (G * selo.k
+    // entries per unit); scores_out then holds one row per query head
+    int heads;
     // group mode with scores_only: slice y's softmax partial covers the g level-2 gist rows of
     // its own group groups[u][y] (the selected-summary set at two levels) when pk is not null
     const uint16_t* pk;

@@ -27,7 +27,8 @@ class DecodeParams(C.Structure):
                                          "k", "gate_mode", "gist_mode", "levels", "J", "k2",
                                          "max_chunks",
                                          "num_pages", "gist_cap")] + [("scale", C.c_float),
-                                                                      ("top_p", C.c_float)]
+                                                                      ("top_p", C.c_float),
+                                                                      ("select_mode", C.c_int32)]
 
 
 class PrefillParams(C.Structure):
@@ -80,16 +81,18 @@ def _p(t: Optional[torch.Tensor]):
 
 
 GISTS_ALL, GISTS_SELECTED = 0, 1   # TCS_GISTS_*
+SELECT_KV_HEAD, SELECT_PER_HEAD = 0, 1   # TCS_SELECT_*
 
 
 def decode_params(*, B, Hq, Hkv, d, N, C_, g, k, gate=0, levels=1, J=0, k2=0, max_chunks=None,
                   num_pages, gist_cap=0, scale=0.0, gist_mode=GISTS_ALL,
-                  top_p=0.0) -> DecodeParams:
+                  top_p=0.0, select_mode=SELECT_KV_HEAD) -> DecodeParams:
     M = -(-N // C_) if C_ > 0 else 1
     return DecodeParams(struct_size=C.sizeof(DecodeParams), B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, C=C_,
                         g=g, k=k, gate_mode=gate, gist_mode=gist_mode, levels=levels, J=J, k2=k2,
                         max_chunks=M if max_chunks is None else max_chunks,
-                        num_pages=num_pages, gist_cap=gist_cap, scale=scale, top_p=top_p)
+                        num_pages=num_pages, gist_cap=gist_cap, scale=scale, top_p=top_p,
+                        select_mode=select_mode)
 
 
 def decode_workspace_size(p: DecodeParams) -> int:
@@ -161,24 +164,27 @@ class DecodeCall:
     """Outputs and workspace for repeated decode calls on one input bundle."""
 
     def __init__(self, inp, with_scores=True, k=None, scale=0.0, gist_mode=GISTS_ALL,
-                 top_p=0.0):
+                 top_p=0.0, head_select=0):
         c = inp.cfg
         dev = inp.q.device
         self.inp = inp
         self.gist_mode = gist_mode
+        self.head_select = head_select
         self.p = decode_params(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, N=c.N, C_=c.C, g=c.g,
                                k=c.k if k is None else k, gate=c.gate, levels=c.levels, J=c.J,
                                k2=c.k2, max_chunks=inp.page_table.shape[1],
                                num_pages=inp.num_pages, gist_cap=inp.gist_k.shape[2],
-                               scale=scale, gist_mode=gist_mode, top_p=top_p)
-        kk = self.p.k
+                               scale=scale, gist_mode=gist_mode, top_p=top_p,
+                               select_mode=SELECT_PER_HEAD if head_select else SELECT_KV_HEAD)
+        kk = self.p.k * (c.G if head_select else 1)   # sel entries per (b, kv)
         self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
         self.sel = torch.empty((c.B, c.Hkv, max(kk, 1)), dtype=torch.int32, device=dev)[..., :kk]
         self.sel_groups = (torch.empty((c.B, c.Hkv, max(c.k2, 1)), dtype=torch.int32,
                                        device=dev)[..., :c.k2] if c.levels == 2 else None)
-        self.chunk_scores = (torch.empty((c.B, c.Hkv, max(c.H, 1)), dtype=torch.float32,
-                                         device=dev) if with_scores else None)
+        self.chunk_scores = (torch.empty((c.B, c.Hq if head_select else c.Hkv, max(c.H, 1)),
+                                         dtype=torch.float32, device=dev)
+                             if with_scores else None)
         self.ws = workspace(decode_workspace_size(self.p), dev)
 
     def __call__(self, stream=None, events=None):
