@@ -55,6 +55,11 @@ class _PrefillShape(C.Structure):
                [("scale", C.c_double)]
 
 
+class _PrefillBwdIO(C.Structure):
+    _fields_ = [("q", _P), ("k", _P), ("v", _P), ("S", _P), ("dout", _P), ("dlse", _P),
+                ("forced_sel", _P), ("dq", _P), ("dk", _P), ("dv", _P), ("dS", _P)]
+
+
 class _PrefillIO(C.Structure):
     _fields_ = [("q", _P), ("k", _P), ("v", _P), ("S", _P), ("forced_sel", _P),
                 ("blocks", _P), ("n_blocks", C.c_int), ("out", _P), ("lse", _P), ("sel", _P)]
@@ -67,6 +72,7 @@ def _open(path):
     h = C.CDLL(path)
     h.or_decode.argtypes = [C.POINTER(_DecodeShape), C.POINTER(_DecodeIO)]
     h.or_prefill.argtypes = [C.POINTER(_PrefillShape), C.POINTER(_PrefillIO)]
+    h.or_prefill_backward.argtypes = [C.POINTER(_PrefillShape), C.POINTER(_PrefillBwdIO)]
     h.or_decode_token_count.argtypes = [C.POINTER(_DecodeShape), C.c_int, C.c_int, C.c_int]
     return h
 
@@ -194,3 +200,32 @@ def prefill(*, B, Hq, Hkv, d, T, blk, k, gate, q, k_, v, S, scale=0.0, forced_se
     if rc:
         raise ValueError(f"oracle prefill rejected the arguments (code {rc})")
     return PrefillResult(out, lse, sel[..., :k])
+
+
+@dataclass
+class PrefillGrads:
+    dq: np.ndarray    # float64 [B][Hq][T][d]
+    dk: np.ndarray    # float64 [B][Hkv][T][d]
+    dv: np.ndarray    # float64 [B][Hkv][T][d]
+    dS: np.ndarray    # float64 [B][Hkv][nb][nb]
+
+
+def prefill_backward(*, B, Hq, Hkv, d, T, blk, k, gate, q, k_, v, S, dout, dlse=None, scale=0.0,
+                     forced_sel=None) -> PrefillGrads:
+    """Gradients of L = sum dout . out + sum dlse . lse of the block-sparse causal prefill with
+    respect to q, k, v and the selector scores S (bf16 inputs as uint16 bit patterns)."""
+    nb = T // blk
+    u16 = np.uint16
+    sh = _PrefillShape(B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, blk=blk, k=k, gate=gate, scale=scale)
+    dq = np.full((B, Hq, T, d), np.nan)
+    dk = np.full((B, Hkv, T, d), np.nan)
+    dv = np.full((B, Hkv, T, d), np.nan)
+    dS = np.full((B, Hkv, nb, nb), np.nan)
+    io = _PrefillBwdIO(q=_ptr(q, u16), k=_ptr(k_, u16), v=_ptr(v, u16), S=_ptr(S, np.float32),
+                       dout=_ptr(dout, u16), dlse=_ptr(dlse, np.float32),
+                       forced_sel=_ptr(forced_sel, np.int32), dq=_ptr(dq), dk=_ptr(dk),
+                       dv=_ptr(dv), dS=_ptr(dS))
+    rc = lib().or_prefill_backward(C.byref(sh), C.byref(io))
+    if rc:
+        raise ValueError(f"oracle prefill backward rejected the arguments (code {rc})")
+    return PrefillGrads(dq, dk, dv, dS)

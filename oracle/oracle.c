@@ -476,6 +476,136 @@ int or_prefill(const or_prefill_shape* p, const or_prefill_io* io)
     return 0;
 }
 
+/* Gradients for one (b, kv): every query block in turn, every head and row of it.
+ * For a query row with softmax weights P over its token set and output o:
+ *   dP_x = dout . v_x,   D = dout . o - dlse,   dlambda_x = P_x (dP_x - D)
+ *   dq += sigma dlambda_x k_x,   dk_x += sigma dlambda_x q,   dv_x += P_x dout
+ * (the chain rule through lambda_x = sigma q . k_x + bias_x, the softmax and lse).  The gate
+ * bias of chosen block j is gamma_ij = S[i][j] - log sum_{j' < i} exp S[i][j'], so
+ *   dgamma_ij = sum of dlambda over every head, row and key of (i, j), and
+ *   dS[i][j'] = [j' chosen] dgamma_ij' - softmax(S[i][. < i])_j' sum_j dgamma_ij   (j' < i).
+ * The selection itself is piecewise constant in S and contributes nothing. */
+static void prefill_backward_unit(const or_prefill_shape* p, const or_prefill_bwd_io* io,
+                                  int b, int kv)
+{
+    const int G = p->Hq / p->Hkv, d = p->d, blk = p->blk, nb = p->T / p->blk;
+    const double sigma = p->scale > 0 ? p->scale : 1.0 / sqrt((double)d);
+    const size_t unit = (size_t)b * p->Hkv + kv;
+    const uint16_t* K = io->k + unit * (size_t)p->T * d;
+    const uint16_t* V = io->v + unit * (size_t)p->T * d;
+    double* dK = io->dk + unit * (size_t)p->T * d;
+    double* dV = io->dv + unit * (size_t)p->T * d;
+    for (size_t e = 0; e < (size_t)p->T * d; ++e) dK[e] = dV[e] = 0.0;
+
+    const int n_max = (p->k > 0 ? p->k : 0) * blk + blk;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(nb > 0 ? nb : 1));
+    int* id = (int*)malloc(sizeof(int) * (size_t)(nb > 0 ? nb : 1));
+    int* chosen = (int*)malloc(sizeof(int) * (size_t)(p->k > 0 ? p->k : 1));
+    double* dgam = (double*)malloc(sizeof(double) * (size_t)(p->k > 0 ? p->k : 1));
+    int* key = (int*)malloc(sizeof(int) * (size_t)n_max);      /* token -> key position  */
+    int* slot = (int*)malloc(sizeof(int) * (size_t)n_max);     /* token -> chosen slot   */
+    double* bias = (double*)malloc(sizeof(double) * (size_t)n_max);
+    double* lam = (double*)malloc(sizeof(double) * (size_t)n_max);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+
+    for (int i = 0; i < nb; ++i) {
+        const float* Srow = io->S + (unit * nb + i) * nb;
+        int ke = 0;
+        if (io->forced_sel) {
+            const int32_t* f = io->forced_sel + (unit * nb + i) * p->k;
+            for (int x = 0; x < p->k; ++x) if (f[x] >= 0) chosen[ke++] = f[x];
+        } else {
+            for (int j = 0; j < i; ++j) { sc[j] = (double)Srow[j]; id[j] = j; }
+            ke = top_k(sc, id, i, p->k, chosen);
+        }
+        for (int j = 0; j < i; ++j) sc[j] = (double)Srow[j];
+        const double norm = (p->gate && i > 0) ? logsumexp(sc, i) : 0.0;
+        for (int x = 0; x < ke; ++x) dgam[x] = 0.0;
+
+        for (int h = 0; h < G; ++h) {
+            const size_t head = (size_t)b * p->Hq + (size_t)kv * G + h;
+            for (int r = 0; r < blk; ++r) {
+                const int pos = i * blk + r;
+                const size_t qrow = head * (size_t)p->T + pos;
+                const uint16_t* qr = io->q + qrow * d;
+                const uint16_t* gr = io->dout + qrow * d;
+                /* the row's token set: the chosen blocks, then the causal part of block i */
+                int n = 0;
+                for (int x = 0; x < ke; ++x)
+                    for (int u = chosen[x] * blk; u < (chosen[x] + 1) * blk; ++u) {
+                        key[n] = u;
+                        slot[n] = x;
+                        bias[n++] = p->gate ? (double)Srow[chosen[x]] - norm : 0.0;
+                    }
+                for (int u = i * blk; u <= pos; ++u) {
+                    key[n] = u;
+                    slot[n] = -1;
+                    bias[n++] = 0.0;
+                }
+                double m = -INFINITY;
+                for (int x = 0; x < n; ++x) {
+                    lam[x] = dotq(qr, K + (size_t)key[x] * d, d, sigma) + bias[x];
+                    if (lam[x] > m) m = lam[x];
+                }
+                double z = 0.0;
+                for (int x = 0; x < n; ++x) z += exp(lam[x] - m);
+                const double lse = m + log(z);
+                for (int e = 0; e < d; ++e) o[e] = 0.0;
+                for (int x = 0; x < n; ++x) {
+                    lam[x] = exp(lam[x] - lse);   /* from here on: the weight P_x */
+                    for (int e = 0; e < d; ++e) o[e] += lam[x] * bf(V[(size_t)key[x] * d + e]);
+                }
+                double D = io->dlse ? -(double)io->dlse[qrow] : 0.0;
+                for (int e = 0; e < d; ++e) D += bf(gr[e]) * o[e];
+                double* dq = io->dq + qrow * d;
+                for (int e = 0; e < d; ++e) dq[e] = 0.0;
+                for (int x = 0; x < n; ++x) {
+                    const uint16_t* kx = K + (size_t)key[x] * d;
+                    const uint16_t* vx = V + (size_t)key[x] * d;
+                    double dP = 0.0;
+                    for (int e = 0; e < d; ++e) dP += bf(gr[e]) * bf(vx[e]);
+                    const double dl = lam[x] * (dP - D);
+                    for (int e = 0; e < d; ++e) {
+                        dq[e] += sigma * dl * bf(kx[e]);
+                        dK[(size_t)key[x] * d + e] += sigma * dl * bf(qr[e]);
+                        dV[(size_t)key[x] * d + e] += lam[x] * bf(gr[e]);
+                    }
+                    if (slot[x] >= 0) dgam[slot[x]] += dl;
+                }
+            }
+        }
+
+        /* through the gate to the selector scores */
+        double* dS = io->dS + (unit * nb + i) * nb;
+        for (int j = 0; j < nb; ++j) dS[j] = 0.0;
+        if (p->gate && ke > 0) {
+            double tot = 0.0;
+            for (int x = 0; x < ke; ++x) tot += dgam[x];
+            for (int j = 0; j < i; ++j) dS[j] = -exp(sc[j] - norm) * tot;
+            for (int x = 0; x < ke; ++x) dS[chosen[x]] += dgam[x];
+        }
+    }
+    free(o);
+    free(lam);
+    free(bias);
+    free(slot);
+    free(key);
+    free(dgam);
+    free(chosen);
+    free(id);
+    free(sc);
+}
+
+int or_prefill_backward(const or_prefill_shape* p, const or_prefill_bwd_io* io)
+{
+    if (!p || !io || !io->dout || !io->dq || !io->dk || !io->dv || !io->dS) return 1;
+    if (p->Hkv <= 0 || p->Hq % p->Hkv || p->blk <= 0 || p->T % p->blk) return 2;
+    const int units = p->B * p->Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < units; ++u) prefill_backward_unit(p, io, u / p->Hkv, u % p->Hkv);
+    return 0;
+}
+
 int or_threads(void)
 {
 #ifdef _OPENMP

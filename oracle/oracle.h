@@ -16,6 +16,8 @@
  * Prefill:
  *   q [B][Hq][T][d], k/v [B][Hkv][T][d], S fp32 [B][Hkv][nb][nb], out [B][Hq][T][d], lse [B][Hq][T],
  *   sel [B][Hkv][nb][k].
+ * Prefill backward: dout [B][Hq][T][d] (bf16), dlse [B][Hq][T], dq [B][Hq][T][d],
+ *   dk/dv [B][Hkv][T][d], dS [B][Hkv][nb][nb].
  */
 #ifndef TCS_ORACLE_H
 #define TCS_ORACLE_H
@@ -76,8 +78,23 @@ typedef struct {
     int32_t* sel;
 } or_prefill_io;
 
+/* Gradients of the block-sparse causal prefill (same shape and selection as the forward) for
+ * the loss L = sum dout . out + sum dlse . lse. */
+typedef struct {
+    const uint16_t *q, *k, *v;
+    const float* S;
+    const uint16_t* dout;          /* bf16 [B][Hq][T][d]                                   */
+    const float* dlse;             /* NULL (zero) or fp32 [B][Hq][T]                       */
+    const int32_t* forced_sel;     /* NULL or [B][Hkv][nb][k]                              */
+    double* dq;                    /* [B][Hq][T][d]                                        */
+    double* dk;                    /* [B][Hkv][T][d]                                       */
+    double* dv;                    /* [B][Hkv][T][d]                                       */
+    double* dS;                    /* [B][Hkv][nb][nb]; zero where S has no effect         */
+} or_prefill_bwd_io;
+
 int or_decode(const or_decode_shape* p, const or_decode_io* io);
 int or_prefill(const or_prefill_shape* p, const or_prefill_io* io);
+int or_prefill_backward(const or_prefill_shape* p, const or_prefill_bwd_io* io);
 int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand, int k2_eff);
 int or_threads(void);
 

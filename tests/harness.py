@@ -31,6 +31,16 @@ def oracle_prefill(inp: PrefillInputs, **kw) -> "oracle.PrefillResult":
     return oracle.prefill(**args)
 
 
+def oracle_prefill_backward(inp: PrefillInputs, dout, dlse, **kw) -> "oracle.PrefillGrads":
+    c = inp.cfg
+    args = dict(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, T=c.T, blk=c.blk, k=c.k, gate=c.gate,
+                q=host(inp.q), k_=host(inp.k), v=host(inp.v),
+                S=inp.S.cpu().numpy().astype(np.float32), dout=host(dout),
+                dlse=None if dlse is None else dlse.cpu().numpy().astype(np.float32))
+    args.update(kw)
+    return oracle.prefill_backward(**args)
+
+
 def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().double().numpy()
 

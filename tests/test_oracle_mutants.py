@@ -23,10 +23,10 @@ MUTANTS = [
     ("drop_current_chunk", "for (int u = 0; u < cur; ++u) {", "for (int u = 0; u < 0; ++u) {"),
     ("drop_gists", "    if (p->gists_in_softmax == 1) {\n        if (p->levels == 2)\n            for",
      "    if (0) {\n        if (p->levels == 2)\n            for"),
-    ("diag_not_causal", "for (int u = i * blk; u <= pos; ++u) {",
-     "for (int u = i * blk; u < (i + 1) * blk; ++u) {"),
-    ("diag_off_by_one", "for (int u = i * blk; u <= pos; ++u) {",
-     "for (int u = i * blk; u < pos; ++u) {"),
+    ("diag_not_causal", "for (int u = i * blk; u <= pos; ++u) {\n                tk[n].k",
+     "for (int u = i * blk; u < (i + 1) * blk; ++u) {\n                tk[n].k"),
+    ("diag_off_by_one", "for (int u = i * blk; u <= pos; ++u) {\n                tk[n].k",
+     "for (int u = i * blk; u < pos; ++u) {\n                tk[n].k"),
     ("prefill_gate_wrong_row", "double gamma = p->gate ? (double)Srow[j] - lse_s : 0.0;",
      "double gamma = p->gate ? (double)io->S[(unit * nb + j) * nb + i] - lse_s : 0.0;"),
     ("scale_missing", "    return sigma * s;\n}", "    return s;\n}"),
@@ -54,6 +54,15 @@ MUTANTS = [
     ("head_select_pooled_score", "sh[i] = pooled_score(qg + (size_t)h * d, 1,", "sh[i] = pooled_score(qg, G,"),
     ("head_select_last_pick_dropped", "for (int j = 0; j < kh; ++j) in_union[pick[j]] = 1;",
      "for (int j = 0; j + 1 < kh; ++j) in_union[pick[j]] = 1;"),
+    ("bwd_drop_D", "const double dl = lam[x] * (dP - D);", "const double dl = lam[x] * dP;"),
+    ("bwd_gate_jacobian_sign", "dS[j] = -exp(sc[j] - norm) * tot;", "dS[j] = exp(sc[j] - norm) * tot;"),
+    ("bwd_dk_unscaled", "dK[(size_t)key[x] * d + e] += sigma * dl * bf(qr[e]);",
+     "dK[(size_t)key[x] * d + e] += dl * bf(qr[e]);"),
+    ("bwd_dv_from_dlambda", "dV[(size_t)key[x] * d + e] += lam[x] * bf(gr[e]);",
+     "dV[(size_t)key[x] * d + e] += dl * bf(gr[e]);"),
+    ("bwd_dlse_ignored", "double D = io->dlse ? -(double)io->dlse[qrow] : 0.0;", "double D = 0.0;"),
+    ("bwd_diag_noncausal", "for (int u = i * blk; u <= pos; ++u) {\n                    key[n] = u;",
+     "for (int u = i * blk; u < (i + 1) * blk; ++u) {\n                    key[n] = u;"),
 ]
 
 

@@ -21,8 +21,8 @@ import torch.nn.functional as F
 
 import oracle
 from top_chunk_sparse_amd.configs import DecodeConfig, PrefillConfig
-from top_chunk_sparse_amd.synth import make_decode, make_prefill
-from harness import oracle_decode, oracle_prefill, f64
+from top_chunk_sparse_amd.synth import make_decode, make_prefill, make_prefill_grads
+from harness import oracle_decode, oracle_prefill, oracle_prefill_backward, f64
 
 TOL = 1e-12
 
@@ -700,6 +700,118 @@ def pin_top_p_tiny_is_argmax():
             sc = full.chunk_scores[b, kv]
             best = int(np.argmax(sc))   # first maximum: lowest index on ties
             assert r.sel[b, kv].tolist() == [best] + [-1] * (cfg.k - 1)
+
+
+# ----------------------------------------------------------------------------------------
+# prefill backward
+# ----------------------------------------------------------------------------------------
+PFB = PrefillConfig("pin_prefill_bwd", B=1, Hq=4, Hkv=2, d=16, T=8 * 6, blk=8, k=2, gate=1)
+
+
+def torch_prefill_grads(inp, dout, dlse, sel):
+    """The prefill written densely in torch float64 (a [T][T] mask with the gate bias of every
+    chosen block built from log_softmax(S[i][:i])), differentiated by autograd."""
+    c = inp.cfg
+    G, blk, nb, T = c.G, c.blk, c.nb, c.T
+    q = torch.tensor(f64(inp.q), requires_grad=True)
+    k = torch.tensor(f64(inp.k), requires_grad=True)
+    v = torch.tensor(f64(inp.v), requires_grad=True)
+    S = torch.tensor(inp.S.double().numpy(), requires_grad=True)
+    bias = torch.full((c.B, c.Hkv, T, T), -math.inf, dtype=torch.float64)
+    for b in range(c.B):
+        for kv in range(c.Hkv):
+            for i in range(nb):
+                rows = slice(i * blk, (i + 1) * blk)
+                if i > 0 and c.k > 0:
+                    g = torch.log_softmax(S[b, kv, i, :i], 0)
+                    for j in sel[b, kv, i]:
+                        if j >= 0:
+                            val = g[j] if c.gate else torch.zeros((), dtype=torch.float64)
+                            bias[b, kv, rows, j * blk:(j + 1) * blk] = val
+                diag = torch.zeros(blk, blk, dtype=torch.float64)
+                diag[torch.triu(torch.ones(blk, blk, dtype=torch.bool), 1)] = -math.inf
+                bias[b, kv, rows, rows] = diag
+    qg = q.view(c.B, c.Hkv, G, T, c.d)
+    lam = torch.matmul(qg, k.unsqueeze(2).transpose(-1, -2)) / math.sqrt(c.d) + bias.unsqueeze(2)
+    lse = torch.logsumexp(lam, -1)
+    out = torch.matmul(torch.softmax(lam, -1), v.unsqueeze(2))
+    loss = (out.reshape(c.B, c.Hq, T, c.d) * torch.tensor(f64(dout))).sum()
+    if dlse is not None:
+        loss = loss + (lse.reshape(c.B, c.Hq, T) * dlse.double()).sum()
+    loss.backward()
+    dS = S.grad.numpy() if S.grad is not None else np.zeros(S.shape)   # S unused: no gradient
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy(), dS
+
+
+def pin_prefill_backward_autograd():
+    """Every gradient against torch autograd of the dense float64 formulation (gate on and off,
+    with and without dlse, k = 0)."""
+    for cfg, with_dlse in ((PFB, True), (PFB.with_(gate=0), True), (PFB, False),
+                           (PFB.with_(k=0), True), (PFB.with_(k=4, Hq=2), True)):
+        inp = make_prefill(cfg, seed=41)
+        dout, dlse = make_prefill_grads(cfg, seed=41)
+        dlse = dlse if with_dlse else None
+        r = oracle_prefill_backward(inp, dout, dlse)
+        sel = oracle_prefill(inp).sel
+        dq, dk, dv, dS = torch_prefill_grads(inp, dout, dlse, sel)
+        for name, a, b in (("dq", r.dq, dq), ("dk", r.dk, dk), ("dv", r.dv, dv), ("dS", r.dS, dS)):
+            assert np.abs(a - b).max() < 1e-10 * max(1.0, np.abs(b).max()), (cfg.name, name)
+
+
+def pin_prefill_backward_finite_differences_S():
+    """dL/dS against central differences of the oracle forward (L = sum dout . out + sum dlse .
+    lse), at entries whose perturbation leaves the selection unchanged."""
+    cfg = PFB
+    inp = make_prefill(cfg, seed=42)
+    dout, dlse = make_prefill_grads(cfg, seed=42)
+    r = oracle_prefill_backward(inp, dout, dlse)
+    go, gl = f64(dout), dlse.double().numpy()
+    base = oracle_prefill(inp)
+    S0 = inp.S.clone()
+    rng = np.random.default_rng(0)
+    checked = 0
+    for _ in range(12):
+        i = int(rng.integers(1, cfg.nb))
+        j = int(rng.integers(0, i))
+        kv = int(rng.integers(0, cfg.Hkv))
+        vals = []
+        for sgn in (1.0, -1.0):
+            inp.S = S0.clone()
+            inp.S[0, kv, i, j] = float(np.float32(S0[0, kv, i, j].item() + sgn * 2.0 ** -9))
+            f = oracle_prefill(inp)
+            if not np.array_equal(f.sel, base.sel):
+                vals = None
+                break
+            vals.append(((f.out * go).sum() + (f.lse * gl).sum(), inp.S[0, kv, i, j].item()))
+        inp.S = S0
+        if vals is None:
+            continue
+        fd = (vals[0][0] - vals[1][0]) / (vals[0][1] - vals[1][1])
+        assert abs(fd - r.dS[0, kv, i, j]) < 1e-5 * max(1.0, abs(fd)), (i, j, fd, r.dS[0, kv, i, j])
+        checked += 1
+    assert checked >= 8
+
+
+def pin_prefill_backward_closed_forms():
+    """Every query row's weights sum to one, so per KV head the dv rows add up to the group's
+    dout rows and the dk rows to sigma * sum dlse * q; with the gate, each dS row sums to zero
+    (the log-softmax Jacobian); without it dS is zero."""
+    cfg = PFB.with_(k=3)
+    inp = make_prefill(cfg, seed=43)
+    dout, dlse = make_prefill_grads(cfg, seed=43)
+    r = oracle_prefill_backward(inp, dout, dlse)
+    go, q = f64(dout), f64(inp.q)
+    gl = dlse.double().numpy()
+    sig = 1.0 / math.sqrt(cfg.d)
+    for kv in range(cfg.Hkv):
+        hs = slice(kv * cfg.G, (kv + 1) * cfg.G)
+        assert np.abs(r.dv[0, kv].sum(0) - go[0, hs].sum((0, 1))).max() < 1e-9
+        want_dk = sig * (gl[0, hs, :, None] * q[0, hs]).sum((0, 1))
+        assert np.abs(r.dk[0, kv].sum(0) - want_dk).max() < 1e-9
+    assert np.abs(r.dS.sum(-1)).max() < 1e-10
+    assert np.abs(np.triu(r.dS[0, 0])).max() == 0.0
+    r0 = oracle_prefill_backward(make_prefill(cfg.with_(gate=0), seed=43), dout, dlse)
+    assert (r0.dS == 0).all()
 
 
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

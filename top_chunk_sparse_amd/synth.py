@@ -15,6 +15,8 @@ Recipe (decode):
     (batch, chunk) to a page, a random permutation of all pages when ``paged``.
 Recipe (prefill): q, K, V ~ N(0, 1) -> bf16; selector scores S ~ N(0, 1) fp32 of shape
 [B][Hkv][nb][nb] (entries on or above the diagonal are left random on purpose).
+Recipe (prefill gradients): upstream dout ~ N(0, 1) -> bf16 [B][Hq][T][d] and dlse ~ N(0, 1)
+fp32 [B][Hq][T], drawn from a generator seeded apart from the forward inputs.
 
 Random values depend on the device the generator runs on (torch's CPU and GPU generators
 differ); a given (config, seed, device) always yields identical bytes.
@@ -168,6 +170,16 @@ def make_prefill(cfg: PrefillConfig, seed: int, device="cpu") -> PrefillInputs:
     v = _randn((B, Hkv, T, d), gen, device).to(torch.bfloat16)
     S = _randn((B, Hkv, nb, nb), gen, device)
     return PrefillInputs(cfg, q, k, v, S)
+
+
+def make_prefill_grads(cfg: PrefillConfig, seed: int, device="cpu"):
+    """Upstream gradients (dout bf16 [B][Hq][T][d], dlse fp32 [B][Hq][T]) for a backward call."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 7919)
+    dout = _randn((cfg.B, cfg.Hq, cfg.T, cfg.d), gen, device).to(torch.bfloat16)
+    dlse = _randn((cfg.B, cfg.Hq, cfg.T), gen, device)
+    return dout, dlse
 
 
 def bf16_bits(t: torch.Tensor):
