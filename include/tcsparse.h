@@ -56,6 +56,17 @@
  *   gamma[i][j] = S[i][j] - log sum_{j' < i} exp(S[i][j']) on every key of selected block j;
  *   bias 0 on the diagonal block.  out = softmax(sigma q K^T + bias) V, lse natural log.
  *
+ *   Prefill backward (the SAS training form: the gate is trained end to end through the
+ *   softmax).  Gradients of L = sum dout . out + sum dlse . lse with respect to q, k, v and the
+ *   selector scores S, with the selection of the forward (recomputed from S; it is piecewise
+ *   constant in S and passes no gradient).  For query row r with weights P over its visible
+ *   keys and D_r = dout_r . out_r - dlse_r: dlambda_rx = P_rx (dout_r . v_x - D_r);
+ *   dq_r = sigma sum_x dlambda_rx k_x; dk_x = sigma sum_r dlambda_rx q_r; dv_x = sum_r P_rx
+ *   dout_r (sums over every query head of the group).  With the gate, g_ij = sum of
+ *   dlambda over every head, row and key of (query block i, chosen block j), and
+ *   dS[i][j'] = [j' chosen] g_ij' - softmax_{j < i}(S[i][j])_j' sum_j g_ij for j' < i, 0 for
+ *   j' >= i; without the gate dS = 0.
+ *
  * Layouts (row-major, innermost last).  bf16 = IEEE bfloat16 bit patterns.
  *   q            bf16 [B][Hq][d]
  *   k_pages      bf16 [num_pages][Hkv][C][d]   one page holds one chunk of every KV head
@@ -73,6 +84,9 @@
  *   Prefill: q bf16 [B][Hq][T][d]; k, v bf16 [B][Hkv][T][d]; S fp32 [B][Hkv][nb][nb] with
  *   nb = T / blk (entries j >= i are ignored); out fp32 [B][Hq][T][d]; lse fp32 [B][Hq][T]
  *   (optional); sel int32 [B][Hkv][nb][k] (optional, ascending, -1 padded).
+ *   Prefill backward: out, lse fp32 as the forward wrote them (both required); dout bf16
+ *   [B][Hq][T][d]; dlse fp32 [B][Hq][T] (optional: NULL means 0); dq fp32 [B][Hq][T][d];
+ *   dk, dv fp32 [B][Hkv][T][d]; dS fp32 [B][Hkv][nb][nb] (optional).
  *
  * Ownership, streams, errors.
  *   All tensor pointers are device pointers owned by the caller, as is the workspace (size
@@ -111,7 +125,7 @@
 extern "C" {
 #endif
 
-#define TCS_ABI_VERSION 4
+#define TCS_ABI_VERSION 5
 
 typedef enum {
     TCS_OK = 0,
@@ -214,6 +228,31 @@ tcs_status sparse_attn_prefill_timed(const tcs_prefill_params* p,
                                      float* out, float* lse, int32_t* sel,
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      void* const* events, int n_events);
+
+tcs_status tcs_prefill_backward_workspace_size(const tcs_prefill_params* p, size_t* bytes);
+
+/* Gradients of the block-sparse causal prefill (see above).  q, k, v, S and p must be those of
+ * the forward call that produced out and lse.  Every output element is written (dq, dk, dv
+ * in full; dS in full when not NULL).  Sums run in a fixed order: the same inputs give the
+ * same bits. */
+tcs_status sparse_attn_prefill_backward(const tcs_prefill_params* p,
+                                        const void* q, const void* k, const void* v,
+                                        const float* S, const float* out, const float* lse,
+                                        const void* dout, const float* dlse,
+                                        float* dq, float* dk, float* dv, float* dS,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Profiling variant of sparse_attn_prefill_backward: events[0] before the first kernel, then
+ * after block selection (1), the row terms D and the chosen-by lists (2), the dq kernel (3),
+ * the dk / dv kernel (4) and the dS kernel (5). */
+tcs_status sparse_attn_prefill_backward_timed(const tcs_prefill_params* p,
+                                              const void* q, const void* k, const void* v,
+                                              const float* S, const float* out,
+                                              const float* lse, const void* dout,
+                                              const float* dlse, float* dq, float* dk,
+                                              float* dv, float* dS, void* workspace,
+                                              size_t workspace_bytes, void* stream,
+                                              void* const* events, int n_events);
 
 /* Static string naming a status code. */
 const char* tcs_status_str(tcs_status s);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ops.lib().tcs_abi_version() == 4
+    assert ops.lib().tcs_abi_version() == 5
     for code in range(6):
         assert ops.status_str(code)
     assert ops.status_str(99) == "unknown status"
@@ -178,6 +178,35 @@ def test_prefill_null_and_workspace_errors():
                                    fake, need, None) == ops.TCS_ERR_NULL     # S needed for k > 0
     assert lib.sparse_attn_prefill(C.byref(p), fake, fake, fake, fake, fake, None, None,
                                    fake, need - 8, None) == ops.TCS_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=1000), ops.TCS_ERR_SHAPE),
+    (dict(blk=32), ops.TCS_ERR_UNSUPPORTED),
+    (dict(d=64), ops.TCS_ERR_UNSUPPORTED),
+    (dict(k=-2), ops.TCS_ERR_SHAPE),
+])
+def test_prefill_backward_rejects_bad_params(kw, code):
+    p = PP(**kw)
+    n = C.c_size_t(0)
+    assert ops.lib().tcs_prefill_backward_workspace_size(C.byref(p), C.byref(n)) == code
+    assert ops.lib().sparse_attn_prefill_backward(C.byref(p), *([None] * 13), 0, None) == code
+
+
+def test_prefill_backward_null_and_workspace_errors():
+    p = PP()
+    need = ops.prefill_backward_workspace_size(p)
+    assert need > ops.prefill_workspace_size(p)
+    fake = 0x100000   # never dereferenced: the checks fail first
+    lib = ops.lib()
+    full = [fake] * 7 + [None] + [fake] * 4   # q k v S out lse dout, dlse, dq dk dv dS
+    assert lib.sparse_attn_prefill_backward(C.byref(p), *full, fake, need - 8,
+                                            None) == ops.TCS_ERR_WORKSPACE
+    for miss in (0, 1, 2, 3, 4, 5, 6, 8, 9, 10):   # every required pointer
+        args = list(full)
+        args[miss] = None
+        assert lib.sparse_attn_prefill_backward(C.byref(p), *args, fake, need,
+                                                None) == ops.TCS_ERR_NULL, miss
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

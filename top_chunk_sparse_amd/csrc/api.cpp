@@ -195,6 +195,29 @@ tcs_status plan_prefill(const tcs_prefill_params* p, PrefillPlan* pl) {
     return TCS_OK;
 }
 
+struct PrefillBwdPlan {
+    PrefillPlan f;
+    size_t off_D, off_inv_i, off_inv_g, off_inv_n, off_dgp, total;
+};
+
+tcs_status plan_prefill_backward(const tcs_prefill_params* p, PrefillBwdPlan* pl) {
+    tcs_status st = plan_prefill(p, &pl->f);
+    if (st != TCS_OK) return st;
+    const long long units = (long long)p->B * p->Hkv;
+    const long long nb = pl->f.nb;
+    const long long nh = 4LL * ((pl->f.G + 3) / 4);
+    const long long kk = p->k > 0 ? p->k : 1;
+    size_t off = pl->f.total;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    pl->off_D = take(sizeof(float) * (size_t)((long long)p->B * p->Hq * p->T));
+    pl->off_inv_i = take(sizeof(int32_t) * (size_t)(units * nb * nb));
+    pl->off_inv_g = take(sizeof(float) * (size_t)(units * nb * nb));
+    pl->off_inv_n = take(sizeof(int32_t) * (size_t)(units * nb));
+    pl->off_dgp = take(sizeof(float) * (size_t)(units * nb * 2 * nh * kk));
+    pl->total = off;
+    return TCS_OK;
+}
+
 tcs_status check_ws(void* ws, size_t have, size_t need) {
     if (have < need) return TCS_ERR_WORKSPACE;
     if (need > 0 && (!ws || ((uintptr_t)ws % kAlign))) return TCS_ERR_WORKSPACE;
@@ -483,6 +506,107 @@ static tcs_status prefill_impl(const tcs_prefill_params* p, const void* q, const
     if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
     if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
     return TCS_OK;
+}
+
+tcs_status tcs_prefill_backward_workspace_size(const tcs_prefill_params* p, size_t* bytes) {
+    if (!bytes) return TCS_ERR_NULL;
+    PrefillBwdPlan pl;
+    tcs_status st = plan_prefill_backward(p, &pl);
+    if (st != TCS_OK) return st;
+    *bytes = pl.total;
+    return TCS_OK;
+}
+
+static tcs_status prefill_backward_impl(const tcs_prefill_params* p, const void* q,
+                                        const void* k, const void* v, const float* S,
+                                        const float* out, const float* lse, const void* dout,
+                                        const float* dlse, float* dq, float* dk, float* dv,
+                                        float* dS, void* workspace, size_t workspace_bytes,
+                                        void* stream, void* const* events, int n_events) {
+    PrefillBwdPlan pl;
+    tcs_status st = plan_prefill_backward(p, &pl);
+    if (st != TCS_OK) return st;
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv ||
+        (!S && (p->k > 0 || p->gate_mode == TCS_GATE_SAS || dS)))
+        return TCS_ERR_NULL;
+    st = check_ws(workspace, workspace_bytes, pl.total);
+    if (st != TCS_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    int stage = 0;
+    auto mark = [&]() -> bool {
+        if (stage < n_events && events && events[stage]) {
+            if (hipEventRecord((hipEvent_t)events[stage], s) != hipSuccess) return false;
+        }
+        ++stage;
+        return true;
+    };
+    if (!mark()) return TCS_ERR_HIP;
+    char* ws = (char*)workspace;
+    const int units = p->B * p->Hkv;
+    const int kk = p->k > 0 ? p->k : 0;
+    int32_t* sel = (int32_t*)(ws + pl.f.off_sel);
+    float* gamma = p->gate_mode == TCS_GATE_SAS ? (float*)(ws + pl.f.off_gamma) : nullptr;
+    if (kk > 0) {
+        tcs::PrefillSelectLaunch ps{S, units, pl.f.nb, kk, sel, gamma};
+        if (tcs::launch_prefill_select(ps, s) != hipSuccess) return TCS_ERR_HIP;
+    }
+    if (!mark()) return TCS_ERR_HIP;
+    tcs::PrefillBwdLaunch a{};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.dout = (const uint16_t*)dout;
+    a.out = out;
+    a.lse = lse;
+    a.dlse = dlse;
+    a.S = S;
+    a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.d = p->d; a.T = p->T; a.blk = p->blk;
+    a.ksel = kk;
+    a.gate = p->gate_mode == TCS_GATE_SAS;
+    a.sel = kk > 0 ? sel : nullptr;
+    a.gamma = kk > 0 ? gamma : nullptr;
+    a.sigma = pl.f.sigma;
+    a.D = (float*)(ws + pl.off_D);
+    a.inv_i = (int32_t*)(ws + pl.off_inv_i);
+    a.inv_g = (float*)(ws + pl.off_inv_g);
+    a.inv_n = (int32_t*)(ws + pl.off_inv_n);
+    a.dgp = (float*)(ws + pl.off_dgp);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dS = dS;
+    hipError_t e = tcs::launch_prefill_bwd_prep(a, s);
+    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
+    if (e == hipSuccess) e = tcs::launch_prefill_bwd_dq(a, s);
+    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
+    if (e == hipSuccess) e = tcs::launch_prefill_bwd_dkv(a, s);
+    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
+    if (e == hipSuccess) e = tcs::launch_prefill_bwd_ds(a, s);
+    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
+    if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
+    return e == hipSuccess ? TCS_OK : TCS_ERR_HIP;
+}
+
+tcs_status sparse_attn_prefill_backward(const tcs_prefill_params* p, const void* q,
+                                        const void* k, const void* v, const float* S,
+                                        const float* out, const float* lse, const void* dout,
+                                        const float* dlse, float* dq, float* dk, float* dv,
+                                        float* dS, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+    return prefill_backward_impl(p, q, k, v, S, out, lse, dout, dlse, dq, dk, dv, dS,
+                                 workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+tcs_status sparse_attn_prefill_backward_timed(const tcs_prefill_params* p, const void* q,
+                                              const void* k, const void* v, const float* S,
+                                              const float* out, const float* lse,
+                                              const void* dout, const float* dlse, float* dq,
+                                              float* dk, float* dv, float* dS, void* workspace,
+                                              size_t workspace_bytes, void* stream,
+                                              void* const* events, int n_events) {
+    if (n_events < 0) return TCS_ERR_SHAPE;
+    return prefill_backward_impl(p, q, k, v, S, out, lse, dout, dlse, dq, dk, dv, dS,
+                                 workspace, workspace_bytes, stream, events, n_events);
 }
 
 tcs_status sparse_attn_prefill(const tcs_prefill_params* p, const void* q, const void* k,

@@ -106,7 +106,36 @@ struct PrefillLaunch {
     float* lse;               // [B][Hq][T] or null
 };
 
+// Backward of the block-sparse prefill (gradients of sum dout . out + sum dlse . lse).
+struct PrefillBwdLaunch {
+    const uint16_t* q;        // [B][Hq][T][d]
+    const uint16_t* k;        // [B][Hkv][T][d]
+    const uint16_t* v;        // [B][Hkv][T][d]
+    const uint16_t* dout;     // [B][Hq][T][d]
+    const float* out;         // [B][Hq][T][d] (the forward's output)
+    const float* lse;         // [B][Hq][T]    (the forward's natural-log lse)
+    const float* dlse;        // [B][Hq][T] or null
+    const float* S;           // [B*Hkv][nb][nb]
+    int B, Hq, Hkv, d, T, blk, ksel, gate;
+    const int32_t* sel;       // [B*Hkv][nb][ksel] ascending, -1 padded (ksel > 0)
+    const float* gamma;       // [B*Hkv][nb][ksel] or null (gate off)
+    float sigma;
+    float* D;                 // [B][Hq][T]: dout . out - dlse
+    int32_t* inv_i;           // [B*Hkv][nb][nb]: query blocks i > j that chose key block j
+    float* inv_g;             // [B*Hkv][nb][nb]: their gates
+    int32_t* inv_n;           // [B*Hkv][nb]: list lengths
+    float* dgp;               // [B*Hkv][nb][2][4 * head groups][ksel]: gate-gradient partials
+    float* dq;                // [B][Hq][T][d]
+    float* dk;                // [B][Hkv][T][d]
+    float* dv;                // [B][Hkv][T][d]
+    float* dS;                // [B*Hkv][nb][nb] or null
+};
+
 hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s);
+hipError_t launch_prefill_bwd_prep(const PrefillBwdLaunch& a, hipStream_t s);
+hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s);
+hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s);
+hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s);
 
 }  // namespace tcs

@@ -41,7 +41,9 @@ _lib = None
 
 EXPORTS = ("tcs_abi_version", "tcs_status_str", "tcs_decode_workspace_size", "sparse_attn_decode",
            "sparse_attn_decode_timed", "tcs_decode_stage_count", "tcs_workspace_init",
-           "tcs_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_prefill_timed")
+           "tcs_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_prefill_timed",
+           "tcs_prefill_backward_workspace_size", "sparse_attn_prefill_backward",
+           "sparse_attn_prefill_backward_timed")
 
 
 def lib():
@@ -61,6 +63,12 @@ def lib():
         h.sparse_attn_prefill.argtypes = [C.POINTER(PrefillParams)] + [_V] * 8 + [C.c_size_t, _V]
         h.sparse_attn_decode_timed.argtypes = h.sparse_attn_decode.argtypes + [_V, C.c_int]
         h.sparse_attn_prefill_timed.argtypes = h.sparse_attn_prefill.argtypes + [_V, C.c_int]
+        h.tcs_prefill_backward_workspace_size.argtypes = [C.POINTER(PrefillParams),
+                                                          C.POINTER(C.c_size_t)]
+        h.sparse_attn_prefill_backward.argtypes = ([C.POINTER(PrefillParams)] + [_V] * 13 +
+                                                   [C.c_size_t, _V])
+        h.sparse_attn_prefill_backward_timed.argtypes = (h.sparse_attn_prefill_backward.argtypes +
+                                                         [_V, C.c_int])
         h.tcs_decode_stage_count.argtypes = [C.POINTER(DecodeParams)]
         h.tcs_workspace_init.argtypes = [_V, C.c_size_t, _V]
         _lib = h
@@ -149,6 +157,29 @@ def sparse_attn_prefill(p: PrefillParams, q, k, v, S, *, out, lse=None, sel=None
     _check(code)
 
 
+def prefill_backward_workspace_size(p: PrefillParams) -> int:
+    n = C.c_size_t(0)
+    _check(lib().tcs_prefill_backward_workspace_size(C.byref(p), C.byref(n)))
+    return n.value
+
+
+def sparse_attn_prefill_backward(p: PrefillParams, q, k, v, S, out, lse, dout, dlse=None, *,
+                                 dq, dk, dv, dS=None, workspace, stream=None,
+                                 events=None) -> None:
+    """Enqueue the prefill gradients on ``stream`` (default: torch's current stream)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(dq.device)
+    args = (C.byref(p), _p(q), _p(k), _p(v), _p(S), _p(out), _p(lse), _p(dout), _p(dlse),
+            _p(dq), _p(dk), _p(dv), _p(dS), _p(workspace),
+            workspace.numel() * workspace.element_size() if workspace is not None else 0,
+            stream.cuda_stream)
+    if events is None:
+        code = lib().sparse_attn_prefill_backward(*args)
+    else:
+        code = lib().sparse_attn_prefill_backward_timed(*args, C.cast(events, _V), len(events))
+    _check(code)
+
+
 def workspace(nbytes: int, device, stream=None) -> torch.Tensor:
     """A caller-owned workspace (256-byte aligned by the torch allocator), zero-filled by the
     library's init kernel as a new decode workspace must be."""
@@ -216,4 +247,30 @@ class PrefillCall:
         sparse_attn_prefill(self.p, i.q, i.k, i.v, i.S, out=self.out, lse=self.lse,
                             sel=self.sel if self.p.k > 0 else None,
                             workspace=self.ws, stream=stream, events=events)
+        return self
+
+
+class PrefillBwdCall:
+    """Gradient buffers and workspace for repeated backward calls on one input bundle; the
+    forward's out and lse come from a finished PrefillCall on the same inputs."""
+
+    def __init__(self, inp, fwd, dout, dlse=None, k=None, scale=0.0, with_dS=True):
+        c = inp.cfg
+        dev = inp.q.device
+        self.inp, self.fwd, self.dout, self.dlse = inp, fwd, dout, dlse
+        self.p = prefill_params(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, T=c.T, blk=c.blk,
+                                k=c.k if k is None else k, gate=c.gate, scale=scale)
+        self.dq = torch.empty((c.B, c.Hq, c.T, c.d), dtype=torch.float32, device=dev)
+        self.dk = torch.empty((c.B, c.Hkv, c.T, c.d), dtype=torch.float32, device=dev)
+        self.dv = torch.empty((c.B, c.Hkv, c.T, c.d), dtype=torch.float32, device=dev)
+        self.dS = (torch.empty((c.B, c.Hkv, c.nb, c.nb), dtype=torch.float32, device=dev)
+                   if with_dS else None)
+        self.ws = torch.empty(max(prefill_backward_workspace_size(self.p), 1), dtype=torch.uint8,
+                              device=dev)
+
+    def __call__(self, stream=None, events=None):
+        i = self.inp
+        sparse_attn_prefill_backward(self.p, i.q, i.k, i.v, i.S, self.fwd.out, self.fwd.lse,
+                                     self.dout, self.dlse, dq=self.dq, dk=self.dk, dv=self.dv,
+                                     dS=self.dS, workspace=self.ws, stream=stream, events=events)
         return self
