@@ -23,6 +23,8 @@ import time
 
 METRIC = "decode attn calls/s and effective HBM GB/s (% of peak) at 128K ctx, k=16"
 PREFILL_METRIC = "SAS block-sparse causal prefill forward, algorithmic TFLOP/s at 16K tokens, k=16"
+PREFILL_BWD_METRIC = ("SAS block-sparse causal prefill backward (dq, dk, dv, dS), algorithmic "
+                      "TFLOP/s at 16K tokens, k=16")
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, vendor figure
 
@@ -79,6 +81,13 @@ def prefill_pairs(cfg):
 def prefill_flops(cfg):
     """Algorithmic FLOPs: 2 d for q.k and 2 d for p.v per attended pair."""
     return 4 * cfg.d * prefill_pairs(cfg)
+
+
+def prefill_bwd_flops(cfg, products=5):
+    """Algorithmic FLOPs of the gradients: 2 d per attended pair for each product -- q.k and
+    dout.v recomputed, and the dq, dk and dv products (5; the dq kernel alone does 3: q.k,
+    dout.v, dq; the dk / dv kernel 4: q.k, dout.v, dk, dv)."""
+    return 2 * products * cfg.d * prefill_pairs(cfg)
 
 
 def prefill_bytes(cfg):
@@ -175,6 +184,38 @@ def cpu_baseline_prefill(inp, budget_s):
             "kind": "oracle", "sample": f"{n} of {nblocks} query blocks (all heads of each) of "
             f"instance 0, seeded random choice", "seconds": round(dt, 3), "cpu": cpu_model(),
             "calls_per_s": round(flops / dt / prefill_flops(c), 6)}
+
+
+def cpu_baseline_prefill_backward(inp, dout, dlse, budget_s):
+    """Time the fp64 CPU oracle's backward (as it stands) on instance 0, restricted to the first
+    n query blocks of every unit (the oracle's timing sample), grown to about the budget and
+    scaled to the metric's unit (algorithmic TFLOP/s)."""
+    import numpy as np
+    import oracle
+    from top_chunk_sparse_amd.synth import bf16_bits
+    c = inp.cfg
+    args = dict(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, T=c.T, blk=c.blk, k=c.k, gate=c.gate,
+                q=bf16_bits(inp.q), k_=bf16_bits(inp.k), v=bf16_bits(inp.v),
+                S=inp.S.cpu().numpy().astype(np.float32), dout=bf16_bits(dout),
+                dlse=dlse.cpu().numpy().astype(np.float32))
+    def pairs(n):   # attended pairs of query blocks 0 .. n-1 of every unit
+        i = np.arange(n)
+        return int(c.B * c.Hkv * c.G * (np.minimum(c.k, i) * c.blk * c.blk
+                                         + c.blk * (c.blk + 1) // 2).sum())
+    oracle.prefill_backward(n_blocks=1, **args)    # untimed: library load, first touch
+    n, t0 = 2, time.perf_counter()
+    oracle.prefill_backward(n_blocks=n, **args)
+    dt = time.perf_counter() - t0
+    while dt < budget_s * 0.5 and n < c.nb:        # grow the timed sample to ~budget
+        n = min(c.nb, int(n * max(1.5, (budget_s / max(dt, 1e-3)) ** 0.5)))
+        t0 = time.perf_counter()
+        oracle.prefill_backward(n_blocks=n, **args)
+        dt = time.perf_counter() - t0
+    flops = 10 * c.d * pairs(n)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "sample": f"query blocks 0..{n - 1} of each of the {c.B * c.Hkv} "
+            f"units of instance 0 ({n} of {c.nb} per unit)", "seconds": round(dt, 3),
+            "cpu": cpu_model(), "calls_per_s": round(flops / dt / prefill_bwd_flops(c), 6)}
 
 
 def load_traffic(kernel_name, workload):
@@ -276,6 +317,94 @@ def run_prefill(args, torch, configs, ops):
     print(json.dumps(rec), flush=True)
 
 
+def run_prefill_backward(args, torch, configs, ops):
+    from top_chunk_sparse_amd.synth import make_prefill, make_prefill_grads
+    import ctypes
+    cfg = configs.PREFILL_CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    R = max(1, min(args.instances, 2))
+    print(f"# generating {R} instance(s) of {cfg.name} (+ upstream gradients)", file=sys.stderr,
+          flush=True)
+    insts = [make_prefill(cfg, configs.seed_for(cfg.name, r), device=dev) for r in range(R)]
+    grads = [make_prefill_grads(cfg, configs.seed_for(cfg.name, r), device=dev) for r in range(R)]
+    fwds = [ops.PrefillCall(inp)() for inp in insts]   # out and lse for the backward (untimed)
+    calls = [ops.PrefillBwdCall(inp, f, g[0], g[1]) for inp, f, g in zip(insts, fwds, grads)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        calls[i % R]()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        calls[i % R]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # per-kernel durations: events between the stages (select, prep, dq, dk / dv, dS)
+    nst = 5
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+           for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        arr = (ctypes.c_void_p * (nst + 1))(*[e.cuda_event for e in evs[i]])
+        calls[i % R](events=arr)
+    torch.cuda.synchronize()
+    stage_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+                for j in range(nst)]
+    print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
+    flops = prefill_bwd_flops(cfg)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    # dominant kernel: the dk / dv kernel or the dq kernel, whichever takes longer
+    dom = 3 if stage_ms[3] >= stage_ms[2] else 2
+    name, kflops = (("prefill_bwd_dkv_kernel", prefill_bwd_flops(cfg, 4)) if dom == 3 else
+                    ("prefill_bwd_dq_kernel", prefill_bwd_flops(cfg, 3)))
+    ach = kflops / (stage_ms[dom] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": name, "achieved": round(ach, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": load_traffic(name, cfg.name),
+            "algorithmic_flops": kflops, "avg_ms": round(stage_ms[dom], 5)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_prefill_backward(insts[0], grads[0][0], grads[0][1], args.cpu_seconds)
+    rec = {
+        "metric": PREFILL_BWD_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + "_backward", "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                   "d": cfg.d, "T": cfg.T, "blk": cfg.blk, "k": cfg.k,
+                   "gate": "sas" if cfg.gate else "none", "inputs": "bf16",
+                   "accumulation": "fp32", "instances_rotated": R},
+        "calls_per_s": round(args.steps / wall, 2),
+        "algorithmic_flops_per_call": flops,
+        "attended_pairs_per_call": prefill_pairs(cfg),
+        "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 5),
+        "stage_ms": [round(x, 5) for x in stage_ms],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +424,9 @@ def main():
     ap.add_argument("--head-select", action="store_true",
                     help="decode selection: every query head picks its own top-k and the union "
                          "is unfolded (one level; runs the workload with the gate off)")
+    ap.add_argument("--backward", action="store_true",
+                    help="prefill workloads: time the gradients (dq, dk, dv, dS) instead of "
+                         "the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -319,6 +451,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.workload in configs.PREFILL_CONFIGS:
+        if args.backward:
+            return run_prefill_backward(args, torch, configs, ops)
         return run_prefill(args, torch, configs, ops)
     cfg = configs.DECODE_CONFIGS[args.workload]
     if args.tokens > 0:

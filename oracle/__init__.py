@@ -57,7 +57,8 @@ class _PrefillShape(C.Structure):
 
 class _PrefillBwdIO(C.Structure):
     _fields_ = [("q", _P), ("k", _P), ("v", _P), ("S", _P), ("dout", _P), ("dlse", _P),
-                ("forced_sel", _P), ("dq", _P), ("dk", _P), ("dv", _P), ("dS", _P)]
+                ("forced_sel", _P), ("dq", _P), ("dk", _P), ("dv", _P), ("dS", _P),
+                ("n_blocks", C.c_int)]
 
 
 class _PrefillIO(C.Structure):
@@ -211,9 +212,10 @@ class PrefillGrads:
 
 
 def prefill_backward(*, B, Hq, Hkv, d, T, blk, k, gate, q, k_, v, S, dout, dlse=None, scale=0.0,
-                     forced_sel=None) -> PrefillGrads:
+                     forced_sel=None, n_blocks=0) -> PrefillGrads:
     """Gradients of L = sum dout . out + sum dlse . lse of the block-sparse causal prefill with
-    respect to q, k, v and the selector scores S (bf16 inputs as uint16 bit patterns)."""
+    respect to q, k, v and the selector scores S (bf16 inputs as uint16 bit patterns).
+    n_blocks > 0 limits the work to query blocks i < n_blocks of each unit (timing samples)."""
     nb = T // blk
     u16 = np.uint16
     sh = _PrefillShape(B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, blk=blk, k=k, gate=gate, scale=scale)
@@ -224,7 +226,7 @@ def prefill_backward(*, B, Hq, Hkv, d, T, blk, k, gate, q, k_, v, S, dout, dlse=
     io = _PrefillBwdIO(q=_ptr(q, u16), k=_ptr(k_, u16), v=_ptr(v, u16), S=_ptr(S, np.float32),
                        dout=_ptr(dout, u16), dlse=_ptr(dlse, np.float32),
                        forced_sel=_ptr(forced_sel, np.int32), dq=_ptr(dq), dk=_ptr(dk),
-                       dv=_ptr(dv), dS=_ptr(dS))
+                       dv=_ptr(dv), dS=_ptr(dS), n_blocks=n_blocks)
     rc = lib().or_prefill_backward(C.byref(sh), C.byref(io))
     if rc:
         raise ValueError(f"oracle prefill backward rejected the arguments (code {rc})")

@@ -508,7 +508,8 @@ static void prefill_backward_unit(const or_prefill_shape* p, const or_prefill_bw
     double* lam = (double*)malloc(sizeof(double) * (size_t)n_max);
     double* o = (double*)malloc(sizeof(double) * (size_t)d);
 
-    for (int i = 0; i < nb; ++i) {
+    const int n_i = io->n_blocks > 0 && io->n_blocks < nb ? io->n_blocks : nb;
+    for (int i = 0; i < n_i; ++i) {
         const float* Srow = io->S + (unit * nb + i) * nb;
         int ke = 0;
         if (io->forced_sel) {

@@ -90,6 +90,9 @@ typedef struct {
     double* dk;                    /* [B][Hkv][T][d]                                       */
     double* dv;                    /* [B][Hkv][T][d]                                       */
     double* dS;                    /* [B][Hkv][nb][nb]; zero where S has no effect         */
+    int n_blocks;                  /* 0: every query block; else only blocks i < n_blocks of
+                                      each unit (a timing sample: dk, dv and dS then hold
+                                      those blocks' contributions only)                    */
 } or_prefill_bwd_io;
 
 int or_decode(const or_decode_shape* p, const or_decode_io* io);

@@ -443,10 +443,9 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s) {
 //   prefill_bwd_dq_kernel       the forward's work split (unit, i, row half, head group): per
 //                               visible block S^T = K Q^T and dP^T = V dO^T, dS^T = P^T (dP^T - D),
 //                               dQ^T += K^T dS^T, and the block's sum of dS^T (gate partial).
-//   prefill_bwd_dkv_kernel      per (unit, key block j, key half): for each head and each query
-//                               block that sees j, S = Q K^T and dP = dO V^T with a lane per key,
-//                               dV^T += dO^T P and dK^T += Q^T dS; the four waves (heads) are
-//                               summed through LDS at the end.
+//   prefill_bwd_dkv_kernel      per (unit, key block j), a wave per 32 keys: for each head and
+//                               each query block that sees j, S = Q K^T and dP = dO V^T with a
+//                               lane per key, dV^T += dO^T P and dK^T += Q^T dS, in registers.
 //   prefill_bwd_ds_kernel       per (unit, i): dS[i][j'] = [j' chosen] dg_ij' -
 //                               softmax(S[i][. < i])_j' sum_j dg_ij.
 // =============================================================================================
@@ -658,28 +657,30 @@ __global__ void __launch_bounds__(256, 1) prefill_bwd_dq_kernel(PrefillBwdLaunch
         }
 }
 
-constexpr int kBwdWaveLds = 2 * kPTile + 2 * kPBlk * 4;   // Q tile, dO tile, lse2 and D rows
-constexpr int kBwdDkvLds = 4 * kBwdWaveLds;
-static_assert(2 * 32 * kPD * 4 <= kBwdWaveLds, "a wave's dK and dV partials fit its region");
+// dk / dv: a workgroup of two waves per (unit, key block j); wave w owns keys 32 w .. 32 w + 31
+// of the block and accumulates their dK^T and dV^T over every (head, query block) pair that
+// sees j, in registers, to the end.  The two waves share each pair's Q and dO tiles; the next
+// pair's tiles travel into registers while the current pair is computed (two LDS buffers).
+constexpr int kBwdBuf = 2 * kPTile + 2 * kPBlk * 4;   // Q tile, dO tile, lse2 and D of 64 rows
+constexpr int kBwdDkvLds = 2 * kBwdBuf;
 
-__global__ void __launch_bounds__(256, 1) prefill_bwd_dkv_kernel(PrefillBwdLaunch a) {
+__global__ void __launch_bounds__(128, 1) prefill_bwd_dkv_kernel(PrefillBwdLaunch a) {
     extern __shared__ __align__(16) char lds[];
     const int G = a.Hq / a.Hkv;
     const int nb = a.T / kPBlk;
-    const int kh = blockIdx.x & 1;
-    const int j = (blockIdx.x >> 1) % nb;   // low j first: the blocks most query blocks choose
-    const int unit = (blockIdx.x >> 1) / nb;
+    const int units = a.B * a.Hkv;
+    // key-block major: the blocks that most query blocks choose (low j) start first, and with
+    // eight KV heads each XCD keeps one head's queries in its L2
+    const int j = blockIdx.x / units;
+    const int unit = blockIdx.x % units;
     const int b = unit / a.Hkv, kv = unit % a.Hkv;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int h = lane >> 5, c32 = lane & 31;
-    char* qt = lds + w * kBwdWaveLds;   // this wave's Q tile, dO tile, lse2 and D
-    char* gt = qt + kPTile;
-    float* l2 = reinterpret_cast<float*>(gt + kPTile);
-    float* Dl = l2 + kPBlk;
 
     // K^T and V^T operands of this lane's key row (kept for the whole kernel)
-    const size_t kfirst = (size_t)unit * a.T + (size_t)j * kPBlk + 32 * kh;
+    const size_t kfirst = (size_t)unit * a.T + (size_t)j * kPBlk + 32 * w;
     bf16x8 kf[8], vf[8];
     {
         const uint16_t* kp = a.k + (kfirst + c32) * kPD + 8 * h;
@@ -694,126 +695,167 @@ __global__ void __launch_bounds__(256, 1) prefill_bwd_dkv_kernel(PrefillBwdLaunc
     const int qoff1 = c32 * 64 + (((2 + h) ^ swz_v(c32)) << 4);
     const int toff = tr_offset(lane);
     const size_t lrow = (size_t)unit * nb + j;
-    const int nlist = 1 + a.inv_n[lrow];
+    const int nlist = 1 + a.inv_n[lrow];     // the diagonal block, then the choosers
+    const int nitems = G * nlist;             // (head, query block) pairs, head-major
     const float cs = a.sigma * kLog2e;
-    const int key = 32 * kh + c32;   // this lane's key row within block j
-    // tile slot c * 64 + lane of a 64-row block: sub-tile c / 4, row 16 (c % 4) + lane / 4,
-    // stored unit lane % 4 holding source unit (lane % 4) ^ swz_v(row); swz_v(row) = (lane >> 2) & 2
-    const int src_lane = ((lane >> 2) * kPD * 2) + ((((lane & 3) ^ ((lane >> 2) & 2))) << 4);
+    const int key = 32 * w + c32;             // this lane's key row within block j
+    // Tile slot c * 128 + tid (c < 8) of a 64-row block: sub-tile c / 2, row 32 (c % 2) +
+    // tid / 4, stored unit tid % 4 holding source unit (tid % 4) ^ swz_v(row), swz_v(row) =
+    // (tid >> 2) & 2; thread tid's source offset is the same for every c but for the row and
+    // sub-tile terms.
+    const int src_t = (tid >> 2) * kPD * 2 + (((tid & 3) ^ ((tid >> 2) & 2)) << 4);
+
+    // (head, query block) pair it: head it / nlist; query block j itself first, then the
+    // choosers of j in ascending order
+#define TCS_BWD_ITEM(it, i, bias, qrow0)                                                        \
+    do {                                                                                        \
+        const int hd_ = (it) / nlist, t_ = (it) - hd_ * nlist;                                  \
+        i = t_ == 0 ? j : a.inv_i[lrow * nb + t_ - 1];                                          \
+        bias = t_ == 0 ? 0.f : a.inv_g[lrow * nb + t_ - 1] * kLog2e;                            \
+        qrow0 = (size_t)(b * a.Hq + kv * G + hd_) * a.T + (size_t)i * kPBlk;                    \
+    } while (0)
+    // staged copy of a pair's Q and dO tiles (8 + 8 chunks of 16 B per thread) and of its
+    // rows' lse2 (threads 0..63) or D (threads 64..127)
+#define TCS_BWD_LOAD(qrow0)                                                                     \
+    do {                                                                                        \
+        const char* qs_ = reinterpret_cast<const char*>(a.q + (qrow0) * kPD) + src_t;           \
+        const char* gs_ = reinterpret_cast<const char*>(a.dout + (qrow0) * kPD) + src_t;        \
+        xq0 = *reinterpret_cast<const uint4*>(qs_ + 0 * 8192 + 0 * 64);                         \
+        xq1 = *reinterpret_cast<const uint4*>(qs_ + 1 * 8192 + 0 * 64);                         \
+        xq2 = *reinterpret_cast<const uint4*>(qs_ + 0 * 8192 + 1 * 64);                         \
+        xq3 = *reinterpret_cast<const uint4*>(qs_ + 1 * 8192 + 1 * 64);                         \
+        xq4 = *reinterpret_cast<const uint4*>(qs_ + 0 * 8192 + 2 * 64);                         \
+        xq5 = *reinterpret_cast<const uint4*>(qs_ + 1 * 8192 + 2 * 64);                         \
+        xq6 = *reinterpret_cast<const uint4*>(qs_ + 0 * 8192 + 3 * 64);                         \
+        xq7 = *reinterpret_cast<const uint4*>(qs_ + 1 * 8192 + 3 * 64);                         \
+        xg0 = *reinterpret_cast<const uint4*>(gs_ + 0 * 8192 + 0 * 64);                         \
+        xg1 = *reinterpret_cast<const uint4*>(gs_ + 1 * 8192 + 0 * 64);                         \
+        xg2 = *reinterpret_cast<const uint4*>(gs_ + 0 * 8192 + 1 * 64);                         \
+        xg3 = *reinterpret_cast<const uint4*>(gs_ + 1 * 8192 + 1 * 64);                         \
+        xg4 = *reinterpret_cast<const uint4*>(gs_ + 0 * 8192 + 2 * 64);                         \
+        xg5 = *reinterpret_cast<const uint4*>(gs_ + 1 * 8192 + 2 * 64);                         \
+        xg6 = *reinterpret_cast<const uint4*>(gs_ + 0 * 8192 + 3 * 64);                         \
+        xg7 = *reinterpret_cast<const uint4*>(gs_ + 1 * 8192 + 3 * 64);                         \
+        xl = tid < 64 ? a.lse[(qrow0) + tid] * kLog2e : a.D[(qrow0) + tid - 64];                \
+    } while (0)
+#define TCS_BWD_STORE(buf)                                                                      \
+    do {                                                                                        \
+        char* d_ = (buf) + tid * 16;                                                            \
+        *reinterpret_cast<uint4*>(d_ + 0 * 2048) = xq0;                                         \
+        *reinterpret_cast<uint4*>(d_ + 1 * 2048) = xq1;                                         \
+        *reinterpret_cast<uint4*>(d_ + 2 * 2048) = xq2;                                         \
+        *reinterpret_cast<uint4*>(d_ + 3 * 2048) = xq3;                                         \
+        *reinterpret_cast<uint4*>(d_ + 4 * 2048) = xq4;                                         \
+        *reinterpret_cast<uint4*>(d_ + 5 * 2048) = xq5;                                         \
+        *reinterpret_cast<uint4*>(d_ + 6 * 2048) = xq6;                                         \
+        *reinterpret_cast<uint4*>(d_ + 7 * 2048) = xq7;                                         \
+        *reinterpret_cast<uint4*>(d_ + kPTile + 0 * 2048) = xg0;                                \
+        *reinterpret_cast<uint4*>(d_ + kPTile + 1 * 2048) = xg1;                                \
+        *reinterpret_cast<uint4*>(d_ + kPTile + 2 * 2048) = xg2;                                \
+        *reinterpret_cast<uint4*>(d_ + kPTile + 3 * 2048) = xg3;                                \
+        *reinterpret_cast<uint4*>(d_ + kPTile + 4 * 2048) = xg4;                                \
+        *reinterpret_cast<uint4*>(d_ + kPTile + 5 * 2048) = xg5;                                \
+        *reinterpret_cast<uint4*>(d_ + kPTile + 6 * 2048) = xg6;                                \
+        *reinterpret_cast<uint4*>(d_ + kPTile + 7 * 2048) = xg7;                                \
+        reinterpret_cast<float*>((buf) + 2 * kPTile)[tid] = xl;                                 \
+    } while (0)
+    uint4 xq0, xq1, xq2, xq3, xq4, xq5, xq6, xq7, xg0, xg1, xg2, xg3, xg4, xg5, xg6, xg7;
+    float xl;   // thread < 64: lse2 of row tid; thread >= 64: D of row tid - 64
 
     f32x16 dk[4], dv[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) dk[dt] = dv[dt] = f32x16{};
 
-    for (int hd = w; hd < G; hd += 4) {
-        for (int t = 0; t < nlist; ++t) {
-            const int i = t == 0 ? j : a.inv_i[lrow * nb + t - 1];
-            const float bias = t == 0 ? 0.f : a.inv_g[lrow * nb + t - 1] * kLog2e;
-            const size_t qrow0 = (size_t)(b * a.Hq + kv * G + hd) * a.T + (size_t)i * kPBlk;
-            const char* qsrc = reinterpret_cast<const char*>(a.q + qrow0 * kPD) + src_lane;
-            const char* gsrc = reinterpret_cast<const char*>(a.dout + qrow0 * kPD) + src_lane;
-#pragma unroll
-            for (int c0 = 0; c0 < 16; c0 += 4) {
-                uint4 xq[4], xg[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int cc = c0 + c;   // sub-tile cc / 4 (64 B of dims), rows + 16 (cc % 4)
-                    const int so = (cc & 3) * 16 * kPD * 2 + (cc >> 2) * 64;
-                    xq[c] = *reinterpret_cast<const uint4*>(qsrc + so);
-                    xg[c] = *reinterpret_cast<const uint4*>(gsrc + so);
-                }
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    *reinterpret_cast<uint4*>(qt + (c0 + c) * 1024 + lane * 16) = xq[c];
-                    *reinterpret_cast<uint4*>(gt + (c0 + c) * 1024 + lane * 16) = xg[c];
-                }
-            }
-            l2[lane] = a.lse[qrow0 + lane] * kLog2e;
-            Dl[lane] = a.D[qrow0 + lane];
-            wait_lds();
-            __builtin_amdgcn_wave_barrier();
+    int i_cur;
+    float bias_cur;
+    size_t qrow_cur;
+    TCS_BWD_ITEM(0, i_cur, bias_cur, qrow_cur);
+    TCS_BWD_LOAD(qrow_cur);
+    TCS_BWD_STORE(lds);
+    wait_vmem();
+    for (int it = 0; it < nitems; ++it) {
+        __syncthreads();   // buffer it & 1 is filled; both waves are done with the other one
+        const char* qt = lds + (it & 1) * kBwdBuf;
+        const char* gt = qt + kPTile;
+        const float* l2 = reinterpret_cast<const float*>(gt + kPTile);
+        const float* Dl = l2 + kPBlk;
+        const bool diag = i_cur == j;
+        const float bias = bias_cur;
+        int i_nx = 0;
+        float bias_nx = 0.f;
+        size_t qrow_nx = 0;
+        if (it + 1 < nitems) {
+            TCS_BWD_ITEM(it + 1, i_nx, bias_nx, qrow_nx);
+            TCS_BWD_LOAD(qrow_nx);
+        }
 
-            f32x16 s[2], dp[2];
-            s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-            qk_product<2>(qt, qoff0, qoff1, kf, s);    // S = Q K^T (lane: key; rows: queries)
-            qk_product<2>(gt, qoff0, qoff1, vf, dp);   // dP = dO V^T
+        f32x16 s[2], dp[2];
+        s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+        qk_product<2>(qt, qoff0, qoff1, kf, s);    // S = Q K^T (lane: key; rows: queries)
+        qk_product<2>(gt, qoff0, qoff1, vf, dp);   // dP = dO V^T
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int q0 = 32 * x + 8 * e4 + 4 * h;   // query rows q0 .. q0 + 3
-                    const float4 lq = *reinterpret_cast<const float4*>(l2 + q0);
-                    const float4 dd = *reinterpret_cast<const float4*>(Dl + q0);
-                    const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
-                    const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int q0 = 32 * x + 8 * e4 + 4 * h;   // query rows q0 .. q0 + 3
+                const float4 lq = *reinterpret_cast<const float4*>(l2 + q0);
+                const float4 dd = *reinterpret_cast<const float4*>(Dl + q0);
+                const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
+                const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int e = 4 * e4 + jj;
-                        float p = __builtin_amdgcn_exp2f(s[x][e] * cs + bias - lv[jj]);
-                        if (t == 0 && key > q0 + jj) p = 0.f;   // diagonal: token-causal
-                        s[x][e] = p;
-                        dp[x][e] = p * (dp[x][e] - dv4[jj]);
-                    }
-                }
-            // dV^T += dO^T P and dK^T += Q^T dS over the block's queries (16 per step)
-            const char* gtT = gt + toff;
-            const char* qtT = qt + toff;
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                bf16x8 pb, db;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pb[e] = (__bf16)s[st >> 1][8 * (st & 1) + e];
-                    db[e] = (__bf16)dp[st >> 1][8 * (st & 1) + e];
-                }
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(gtT, dt, st), pb,
-                                                                     dv[dt], 0, 0, 0);
-                    dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(qtT, dt, st), db,
-                                                                     dk[dt], 0, 0, 0);
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int e = 4 * e4 + jj;
+                    float p = __builtin_amdgcn_exp2f(s[x][e] * cs + bias - lv[jj]);
+                    if (diag && key > q0 + jj) p = 0.f;   // diagonal block: token-causal
+                    s[x][e] = p;
+                    dp[x][e] = p * (dp[x][e] - dv4[jj]);
                 }
             }
-            wait_lds();
-            __builtin_amdgcn_wave_barrier();   // the tiles are rewritten for the next block
+        // dV^T += dO^T P and dK^T += Q^T dS over the block's queries (16 per step)
+        const char* gtT = gt + toff;
+        const char* qtT = qt + toff;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            bf16x8 pb, db;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pb[e] = (__bf16)s[st >> 1][8 * (st & 1) + e];
+                db[e] = (__bf16)dp[st >> 1][8 * (st & 1) + e];
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(gtT, dt, st), pb,
+                                                                 dv[dt], 0, 0, 0);
+                dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(qtT, dt, st), db,
+                                                                 dk[dt], 0, 0, 0);
+            }
+        }
+        if (it + 1 < nitems) {
+            TCS_BWD_STORE(lds + ((it + 1) & 1) * kBwdBuf);
+            i_cur = i_nx;
+            bias_cur = bias_nx;
+            qrow_cur = qrow_nx;
         }
     }
 
-    // Sum the four waves' partials (fixed order): each wave parks dK^T and dV^T as [key][dim]
-    // in its own region, then every thread adds up 4-float groups across the regions.
-    __syncthreads();
-    float* part = reinterpret_cast<float*>(lds + w * kBwdWaveLds);
+    // this wave's 32 key rows: dK = sigma dK^T, dV = dV^T (lane: key row; registers: dims)
+    float* kp = a.dk + (kfirst + c32) * kPD;
+    float* vp = a.dv + (kfirst + c32) * kPD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-            const int dim = 32 * dt + 8 * e4 + 4 * h;
             float4 x, y;
-            x.x = dk[dt][4 * e4 + 0]; x.y = dk[dt][4 * e4 + 1];
-            x.z = dk[dt][4 * e4 + 2]; x.w = dk[dt][4 * e4 + 3];
+            x.x = dk[dt][4 * e4 + 0] * a.sigma; x.y = dk[dt][4 * e4 + 1] * a.sigma;
+            x.z = dk[dt][4 * e4 + 2] * a.sigma; x.w = dk[dt][4 * e4 + 3] * a.sigma;
             y.x = dv[dt][4 * e4 + 0]; y.y = dv[dt][4 * e4 + 1];
             y.z = dv[dt][4 * e4 + 2]; y.w = dv[dt][4 * e4 + 3];
-            *reinterpret_cast<float4*>(part + c32 * kPD + dim) = x;
-            *reinterpret_cast<float4*>(part + 32 * kPD + c32 * kPD + dim) = y;
+            *reinterpret_cast<float4*>(kp + 32 * dt + 8 * e4 + 4 * h) = x;
+            *reinterpret_cast<float4*>(vp + 32 * dt + 8 * e4 + 4 * h) = y;
         }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 2 * 32 * (kPD / 4); idx += 256) {
-        const int tsr = idx / (32 * (kPD / 4));   // 0: dK, 1: dV
-        const int f4 = idx % (32 * (kPD / 4));
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int wv = 0; wv < 4; ++wv) {
-            const float4 x = reinterpret_cast<const float4*>(
-                lds + wv * kBwdWaveLds + tsr * 32 * kPD * 4)[f4];
-            acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
-        }
-        const int kr = f4 / (kPD / 4), d4 = f4 % (kPD / 4);
-        if (tsr == 0) {
-            acc.x *= a.sigma; acc.y *= a.sigma; acc.z *= a.sigma; acc.w *= a.sigma;
-        }
-        float* dst = (tsr == 0 ? a.dk : a.dv) + (kfirst + kr) * kPD + 4 * d4;
-        *reinterpret_cast<float4*>(dst) = acc;
-    }
+#undef TCS_BWD_ITEM
+#undef TCS_BWD_LOAD
+#undef TCS_BWD_STORE
 }
 
 __global__ void __launch_bounds__(256) prefill_bwd_ds_kernel(PrefillBwdLaunch a) {
@@ -899,13 +941,13 @@ hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s) {
 hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s) {
     hipError_t e = bwd_check(a);
     if (e != hipSuccess) return e;
-    const long long W = 2LL * a.B * a.Hkv * (a.T / kPBlk);
+    const long long W = (long long)a.B * a.Hkv * (a.T / kPBlk);
     if (W <= 0) return hipSuccess;
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
     e = hipFuncSetAttribute((const void*)prefill_bwd_dkv_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kBwdDkvLds);
     if (e != hipSuccess) return e;
-    prefill_bwd_dkv_kernel<<<(unsigned)W, 256, kBwdDkvLds, s>>>(a);
+    prefill_bwd_dkv_kernel<<<(unsigned)W, 128, kBwdDkvLds, s>>>(a);
     return hipGetLastError();
 }
 
