@@ -55,6 +55,16 @@ class _PrefillShape(C.Structure):
                [("scale", C.c_double)]
 
 
+class _GistPrefillShape(C.Structure):
+    _fields_ = [(n, C.c_int) for n in ("B", "Hq", "Hkv", "d", "M", "L", "g")] + \
+               [("scale", C.c_double)]
+
+
+class _GistPrefillIO(C.Structure):
+    _fields_ = [("q", _P), ("k", _P), ("v", _P), ("rows", _P), ("n_rows", C.c_int),
+                ("out", _P), ("lse", _P)]
+
+
 class _PrefillBwdIO(C.Structure):
     _fields_ = [("q", _P), ("k", _P), ("v", _P), ("S", _P), ("dout", _P), ("dlse", _P),
                 ("forced_sel", _P), ("dq", _P), ("dk", _P), ("dv", _P), ("dS", _P),
@@ -74,6 +84,7 @@ def _open(path):
     h.or_decode.argtypes = [C.POINTER(_DecodeShape), C.POINTER(_DecodeIO)]
     h.or_prefill.argtypes = [C.POINTER(_PrefillShape), C.POINTER(_PrefillIO)]
     h.or_prefill_backward.argtypes = [C.POINTER(_PrefillShape), C.POINTER(_PrefillBwdIO)]
+    h.or_gist_prefill.argtypes = [C.POINTER(_GistPrefillShape), C.POINTER(_GistPrefillIO)]
     h.or_decode_token_count.argtypes = [C.POINTER(_DecodeShape), C.c_int, C.c_int, C.c_int]
     return h
 
@@ -231,3 +242,21 @@ def prefill_backward(*, B, Hq, Hkv, d, T, blk, k, gate, q, k_, v, S, dout, dlse=
     if rc:
         raise ValueError(f"oracle prefill backward rejected the arguments (code {rc})")
     return PrefillGrads(dq, dk, dv, dS)
+
+
+def gist_prefill(*, B, Hq, Hkv, d, M, L, g, q, k_, v, scale=0.0, rows=None):
+    """SSA gist-masked prefill over the interleaved sequence (M chunks of L raw tokens, each
+    followed by its g gist tokens).  Returns (out [B][Hq][T'][d], lse [B][Hq][T']) in float64,
+    NaN where a row was not computed (``rows``: flat ids (b * Hq + h) * T' + p)."""
+    Tp = M * (L + g)
+    u16 = np.uint16
+    sh = _GistPrefillShape(B=B, Hq=Hq, Hkv=Hkv, d=d, M=M, L=L, g=g, scale=scale)
+    out = np.full((B, Hq, Tp, d), np.nan)
+    lse = np.full((B, Hq, Tp), np.nan)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    io = _GistPrefillIO(q=_ptr(q, u16), k=_ptr(k_, u16), v=_ptr(v, u16), rows=_ptr(r),
+                        n_rows=0 if r is None else len(r), out=_ptr(out), lse=_ptr(lse))
+    rc = lib().or_gist_prefill(C.byref(sh), C.byref(io))
+    if rc:
+        raise ValueError(f"oracle gist prefill rejected the arguments (code {rc})")
+    return out, lse

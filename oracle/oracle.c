@@ -607,6 +607,62 @@ int or_prefill_backward(const or_prefill_shape* p, const or_prefill_bwd_io* io)
     return 0;
 }
 
+/* SSA gist-masked prefill for one query position (section 3.1: chunk tokens attend to their
+ * own chunk and to the preceding gist tokens; later tokens reach a chunk only through its
+ * gists).  The visible set is enumerated in sequence order, straight from the rule. */
+static void gist_prefill_row(const or_gist_prefill_shape* p, const or_gist_prefill_io* io,
+                             size_t row, token* tk)
+{
+    const int W = p->L + p->g;                  /* positions per chunk */
+    const size_t Tp = (size_t)p->M * W;
+    const int G = p->Hq / p->Hkv, d = p->d;
+    const double sigma = p->scale > 0 ? p->scale : 1.0 / sqrt((double)d);
+    const size_t bh = row / Tp;
+    const int pos = (int)(row % Tp);
+    const int b = (int)(bh / p->Hq), h = (int)(bh % p->Hq), kv = h / G;
+    const int cp = pos / W;
+    const uint16_t* K = io->k + ((size_t)b * p->Hkv + kv) * Tp * d;
+    const uint16_t* V = io->v + ((size_t)b * p->Hkv + kv) * Tp * d;
+    int n = 0;
+    for (int x = 0; x <= pos; ++x) {
+        const int cx = x / W;
+        const int is_gist = (x % W) >= p->L;
+        if (cx == cp || is_gist) {
+            tk[n].k = K + (size_t)x * d;
+            tk[n].v = V + (size_t)x * d;
+            tk[n++].bias = 0.0;
+        }
+    }
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    const double l = attend(io->q + row * d, tk, n, d, sigma, o, NULL);
+    for (int e = 0; e < d; ++e) io->out[row * d + e] = o[e];
+    if (io->lse) io->lse[row] = l;
+    free(o);
+}
+
+int or_gist_prefill(const or_gist_prefill_shape* p, const or_gist_prefill_io* io)
+{
+    if (!p || !io || !io->q || !io->k || !io->v || !io->out) return 1;
+    if (p->Hkv <= 0 || p->Hq % p->Hkv || p->M < 1 || p->L < 1 || p->g < 0 || p->d < 1) return 2;
+    const size_t Tp = (size_t)p->M * (p->L + p->g);
+    const size_t total = (size_t)p->B * p->Hq * Tp;
+    const size_t n = io->rows ? (size_t)io->n_rows : total;
+    int rc = 0;
+#pragma omp parallel reduction(| : rc)
+    {
+        token* tk = (token*)malloc(sizeof(token) * Tp);
+        if (!tk) rc = 1;
+#pragma omp for schedule(dynamic, 64)
+        for (size_t x = 0; x < n; ++x) {
+            if (!tk) continue;
+            const size_t row = io->rows ? (size_t)io->rows[x] : x;
+            gist_prefill_row(p, io, row, tk);
+        }
+        free(tk);
+    }
+    return rc;
+}
+
 int or_threads(void)
 {
 #ifdef _OPENMP

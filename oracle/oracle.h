@@ -95,6 +95,27 @@ typedef struct {
                                       those blocks' contributions only)                    */
 } or_prefill_bwd_io;
 
+/* SSA gist-masked prefill ("Simplified Sparse Attention via Gist Tokens", section 3.1): the
+ * sequence interleaves M chunks of L raw tokens, each followed by its g gist tokens
+ * (T' = M (L + g) positions).  Position x of chunk c(x) is visible to position p of chunk c(p)
+ * iff x <= p and (c(x) == c(p) or x is a gist token): a chunk's own tokens causally, and the
+ * gist tokens of every earlier chunk.
+ *   q [B][Hq][T'][d], k/v [B][Hkv][T'][d], out [B][Hq][T'][d], lse [B][Hq][T'] */
+typedef struct {
+    int B, Hq, Hkv, d, M, L, g;
+    double scale;                  /* <= 0: 1/sqrt(d) */
+} or_gist_prefill_shape;
+
+typedef struct {
+    const uint16_t *q, *k, *v;
+    const int32_t* rows;           /* NULL: every (b, head, position); else flat ids
+                                      ((b * Hq + h) * T' + p)                               */
+    int n_rows;
+    double* out;
+    double* lse;
+} or_gist_prefill_io;
+
+int or_gist_prefill(const or_gist_prefill_shape* p, const or_gist_prefill_io* io);
 int or_decode(const or_decode_shape* p, const or_decode_io* io);
 int or_prefill(const or_prefill_shape* p, const or_prefill_io* io);
 int or_prefill_backward(const or_prefill_shape* p, const or_prefill_bwd_io* io);

@@ -41,6 +41,14 @@ def oracle_prefill_backward(inp: PrefillInputs, dout, dlse, **kw) -> "oracle.Pre
     return oracle.prefill_backward(**args)
 
 
+def oracle_gist_prefill(inp, **kw):
+    c = inp.cfg
+    args = dict(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, M=c.M, L=c.L, g=c.g, q=host(inp.q),
+                k_=host(inp.k), v=host(inp.v))
+    args.update(kw)
+    return oracle.gist_prefill(**args)
+
+
 def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().double().numpy()
 

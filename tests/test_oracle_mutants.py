@@ -63,6 +63,10 @@ MUTANTS = [
     ("bwd_dlse_ignored", "double D = io->dlse ? -(double)io->dlse[qrow] : 0.0;", "double D = 0.0;"),
     ("bwd_diag_noncausal", "for (int u = i * blk; u <= pos; ++u) {\n                    key[n] = u;",
      "for (int u = i * blk; u < (i + 1) * blk; ++u) {\n                    key[n] = u;"),
+    ("gist_prefill_raw_leak", "if (cx == cp || is_gist) {", "if (1) {"),
+    ("gist_prefill_no_earlier_gists", "if (cx == cp || is_gist) {", "if (cx == cp) {"),
+    ("gist_prefill_first_gist_as_raw", "const int is_gist = (x % W) >= p->L;",
+     "const int is_gist = (x % W) > p->L;"),
 ]
 
 

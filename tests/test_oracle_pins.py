@@ -21,8 +21,11 @@ import torch.nn.functional as F
 
 import oracle
 from top_chunk_sparse_amd.configs import DecodeConfig, PrefillConfig
-from top_chunk_sparse_amd.synth import make_decode, make_prefill, make_prefill_grads
-from harness import oracle_decode, oracle_prefill, oracle_prefill_backward, f64
+from top_chunk_sparse_amd.configs import GistPrefillConfig
+from top_chunk_sparse_amd.synth import (make_decode, make_gist_prefill, make_prefill,
+                                        make_prefill_grads)
+from harness import (oracle_decode, oracle_gist_prefill, oracle_prefill, oracle_prefill_backward,
+                     f64)
 
 TOL = 1e-12
 
@@ -812,6 +815,74 @@ def pin_prefill_backward_closed_forms():
     assert np.abs(np.triu(r.dS[0, 0])).max() == 0.0
     r0 = oracle_prefill_backward(make_prefill(cfg.with_(gate=0), seed=43), dout, dlse)
     assert (r0.dS == 0).all()
+
+
+# ----------------------------------------------------------------------------------------
+# SSA gist-masked prefill
+# ----------------------------------------------------------------------------------------
+GP = GistPrefillConfig("pin_gist_prefill", B=1, Hq=4, Hkv=2, d=16, M=5, L=6, g=2)
+
+
+def dense_masked(q, k, v, allowed):
+    """Textbook attention of every row over the keys its mask row allows (float64)."""
+    lam = q @ k.T / math.sqrt(q.shape[-1])
+    lam = np.where(allowed, lam, -np.inf)
+    m = lam.max(-1, keepdims=True)
+    w = np.exp(lam - m)
+    return (w @ v) / w.sum(-1, keepdims=True), (m + np.log(w.sum(-1, keepdims=True)))[:, 0]
+
+
+def pin_gist_prefill_dense_mask():
+    """Against dense attention under the mask of section 3.1, built as a [T'][T'] boolean array
+    from chunk ids and gist flags (causal, and same chunk or gist key), G = 1 and 2, g = 1..3."""
+    for cfg in (GP, GP.with_(Hq=2, g=1, L=7), GP.with_(g=3, L=4, M=6)):
+        inp = make_gist_prefill(cfg, seed=51)
+        out, lse = oracle_gist_prefill(inp)
+        pos = np.arange(cfg.Tp)
+        chunk, gist = pos // cfg.W, (pos % cfg.W) >= cfg.L
+        allowed = (pos[None, :] <= pos[:, None]) & ((chunk[None, :] == chunk[:, None]) | gist[None, :])
+        q, k, v = f64(inp.q), f64(inp.k), f64(inp.v)
+        for h in range(cfg.Hq):
+            o, l = dense_masked(q[0, h], k[0, h // cfg.G], v[0, h // cfg.G], allowed)
+            assert np.abs(out[0, h] - o).max() < TOL and np.abs(lse[0, h] - l).max() < TOL
+
+
+def pin_gist_prefill_special_cases():
+    """One chunk: causal attention over the chunk (torch sdpa); no gists: each chunk causal on
+    its own (block-diagonal)."""
+    for cfg in (GP.with_(M=1), GP.with_(g=0)):
+        inp = make_gist_prefill(cfg, seed=52)
+        out, lse = oracle_gist_prefill(inp)
+        q, k, v = (torch.tensor(f64(t)) for t in (inp.q, inp.k, inp.v))
+        for h in range(cfg.Hq):
+            for c in range(cfg.M):
+                rs = slice(c * cfg.W, (c + 1) * cfg.W)
+                want = F.scaled_dot_product_attention(q[0, h, rs][None], k[0, h // cfg.G, rs][None],
+                                                      v[0, h // cfg.G, rs][None], is_causal=True)[0]
+                assert np.abs(out[0, h, rs] - want.numpy()).max() < TOL
+
+
+def pin_gist_prefill_bottleneck():
+    """Later tokens reach a chunk only through its gists: new raw K/V in chunk 1 change no output
+    outside chunk 1 (bitwise) but do change chunk 1's own later rows; new gist K/V of chunk 1
+    change the outputs of later chunks."""
+    cfg = GP
+    inp = make_gist_prefill(cfg, seed=53)
+    base, _ = oracle_gist_prefill(inp)
+    raw = slice(1 * cfg.W, 1 * cfg.W + cfg.L)
+    k0, v0 = inp.k.clone(), inp.v.clone()
+    inp.k[:, :, raw] = -inp.k[:, :, raw]
+    inp.v[:, :, raw] = inp.v[:, :, raw] * 2
+    out, _ = oracle_gist_prefill(inp)
+    outside = np.r_[0:cfg.W, 2 * cfg.W:cfg.Tp]
+    assert np.array_equal(out[:, :, outside], base[:, :, outside])
+    assert np.abs(out[:, :, raw] - base[:, :, raw]).max() > 1e-3
+    inp.k, inp.v = k0.clone(), v0.clone()
+    gist = slice(1 * cfg.W + cfg.L, 2 * cfg.W)
+    inp.v[:, :, gist] = inp.v[:, :, gist] * 3
+    out, _ = oracle_gist_prefill(inp)
+    assert np.array_equal(out[:, :, : 1 * cfg.W + cfg.L], base[:, :, : 1 * cfg.W + cfg.L])
+    assert np.abs(out[:, :, 2 * cfg.W:] - base[:, :, 2 * cfg.W:]).max() > 1e-3
 
 
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

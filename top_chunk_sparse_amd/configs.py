@@ -97,13 +97,50 @@ LLAMA8B = DecodeConfig("llama31_8b_decode_128k", B=16, Hq=32, Hkv=8, d=128, N=13
 HSSA = DecodeConfig("hssa_decode_512k", B=4, Hq=32, Hkv=8, d=128, N=524288, C=128, g=4, k=32,
                     levels=2, J=16, k2=4, n_plant=32, plant_groups=4)
 # Block-sparse causal prefill (SAS training-form forward) at 16K tokens, 64-token blocks.
+@dataclass(frozen=True)
+class GistPrefillConfig:
+    """SSA gist-masked prefill: M chunks of L raw tokens, each followed by its g gist tokens."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    M: int
+    L: int
+    g: int
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def W(self) -> int:
+        """Positions per chunk (raw tokens, then gists)."""
+        return self.L + self.g
+
+    @property
+    def Tp(self) -> int:
+        """Positions of the interleaved sequence."""
+        return self.M * self.W
+
+    def with_(self, **kw) -> "GistPrefillConfig":
+        return replace(self, **kw)
+
+
 PREFILL = PrefillConfig("sas_prefill_16k", B=1, Hq=32, Hkv=8, d=128, T=16384, blk=64, k=16,
                         gate=1)
 
+# SSA gist-masked prefill of 16K raw tokens with the Llama-3.1-8B head layout: 128 chunks of
+# 128 tokens, 4 gists each (32x compression), 16,896 positions in the interleaved sequence.
+GIST_PREFILL = GistPrefillConfig("ssa_gist_prefill_16k", B=1, Hq=32, Hkv=8, d=128, M=128, L=128,
+                                 g=4)
+
 DECODE_CONFIGS = {c.name: c for c in (TINY, LLAMA1B, LLAMA8B, HSSA)}
 PREFILL_CONFIGS = {PREFILL.name: PREFILL}
+GIST_PREFILL_CONFIGS = {GIST_PREFILL.name: GIST_PREFILL}
 # Index of each preset in the published list of workloads (seed = 1000 * index + instance).
-CONFIG_INDEX = {TINY.name: 1, LLAMA1B.name: 2, LLAMA8B.name: 3, HSSA.name: 4, PREFILL.name: 5}
+CONFIG_INDEX = {TINY.name: 1, LLAMA1B.name: 2, LLAMA8B.name: 3, HSSA.name: 4, PREFILL.name: 5,
+                GIST_PREFILL.name: 6}
 
 
 def seed_for(name: str, instance: int = 0) -> int:

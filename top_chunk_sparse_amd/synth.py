@@ -15,6 +15,9 @@ Recipe (decode):
     (batch, chunk) to a page, a random permutation of all pages when ``paged``.
 Recipe (prefill): q, K, V ~ N(0, 1) -> bf16; selector scores S ~ N(0, 1) fp32 of shape
 [B][Hkv][nb][nb] (entries on or above the diagonal are left random on purpose).
+Recipe (SSA gist-masked prefill): the interleaved sequence of M chunks, each L raw tokens then
+g gist tokens; q, K, V ~ N(0, 1) -> bf16 at every position (raw and gist alike: the kernel's
+work does not depend on what the gists learned).
 Recipe (prefill gradients): upstream dout ~ N(0, 1) -> bf16 [B][Hq][T][d] and dlse ~ N(0, 1)
 fp32 [B][Hq][T], drawn from a generator seeded apart from the forward inputs.
 
@@ -26,7 +29,7 @@ from typing import Optional, List
 
 import torch
 
-from .configs import DecodeConfig, PrefillConfig
+from .configs import DecodeConfig, GistPrefillConfig, PrefillConfig
 
 
 @dataclass
@@ -170,6 +173,24 @@ def make_prefill(cfg: PrefillConfig, seed: int, device="cpu") -> PrefillInputs:
     v = _randn((B, Hkv, T, d), gen, device).to(torch.bfloat16)
     S = _randn((B, Hkv, nb, nb), gen, device)
     return PrefillInputs(cfg, q, k, v, S)
+
+
+@dataclass
+class GistPrefillInputs:
+    cfg: GistPrefillConfig
+    q: torch.Tensor            # bf16 [B][Hq][T'][d], T' = M (L + g)
+    k: torch.Tensor            # bf16 [B][Hkv][T'][d]
+    v: torch.Tensor
+
+
+def make_gist_prefill(cfg: GistPrefillConfig, seed: int, device="cpu") -> GistPrefillInputs:
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    q = _randn((cfg.B, cfg.Hq, cfg.Tp, cfg.d), gen, device).to(torch.bfloat16)
+    k = _randn((cfg.B, cfg.Hkv, cfg.Tp, cfg.d), gen, device).to(torch.bfloat16)
+    v = _randn((cfg.B, cfg.Hkv, cfg.Tp, cfg.d), gen, device).to(torch.bfloat16)
+    return GistPrefillInputs(cfg, q, k, v)
 
 
 def make_prefill_grads(cfg: PrefillConfig, seed: int, device="cpu"):
