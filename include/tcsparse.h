@@ -56,6 +56,17 @@
  *   gamma[i][j] = S[i][j] - log sum_{j' < i} exp(S[i][j']) on every key of selected block j;
  *   bias 0 on the diagonal block.  out = softmax(sigma q K^T + bias) V, lse natural log.
  *
+ *   SSA gist-masked prefill ("Simplified Sparse Attention via Gist Tokens", section 3.1).  The
+ *   sequence interleaves M chunks of L raw tokens, each followed by its g gist tokens
+ *   (T' = M (L + g) positions; position p lies in chunk p / (L + g) and is a gist token when
+ *   p % (L + g) >= L).  Position x is visible to position p iff x <= p and (x is in p's chunk
+ *   or x is a gist token): chunk tokens see their own chunk and every earlier chunk's gists,
+ *   and later tokens reach a chunk only through its gists.  out = softmax(sigma q K^T) V over
+ *   the visible set, lse natural log.  Section 3.6's key-column permutation (summary columns
+ *   first) is how it runs: the gists are gathered into a contiguous prefix each call, and the
+ *   visible blocks of a query block are a closed form of its chunk and position, so no mask is
+ *   stored and nothing needs sharing across layers.
+ *
  *   Prefill backward (the SAS training form: the gate is trained end to end through the
  *   softmax).  Gradients of L = sum dout . out + sum dlse . lse with respect to q, k, v and the
  *   selector scores S, with the selection of the forward (recomputed from S; it is piecewise
@@ -84,6 +95,8 @@
  *   Prefill: q bf16 [B][Hq][T][d]; k, v bf16 [B][Hkv][T][d]; S fp32 [B][Hkv][nb][nb] with
  *   nb = T / blk (entries j >= i are ignored); out fp32 [B][Hq][T][d]; lse fp32 [B][Hq][T]
  *   (optional); sel int32 [B][Hkv][nb][k] (optional, ascending, -1 padded).
+ *   Gist prefill: q bf16 [B][Hq][T'][d]; k, v bf16 [B][Hkv][T'][d] (the interleaved
+ *   sequence); out fp32 [B][Hq][T'][d]; lse fp32 [B][Hq][T'] (optional).
  *   Prefill backward: out, lse fp32 as the forward wrote them (both required); dout bf16
  *   [B][Hq][T][d]; dlse fp32 [B][Hq][T] (optional: NULL means 0); dq fp32 [B][Hq][T][d];
  *   dk, dv fp32 [B][Hkv][T][d]; dS fp32 [B][Hkv][nb][nb] (optional).
@@ -112,7 +125,8 @@
  * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024;
  * B * Hkv <= 16384; TCS_GISTS_SELECTED: C + g <= 1024; top_p > 0: one level
  * and k <= 256; TCS_SELECT_PER_HEAD: one level, no gate, top_p = 0, M - 1 <= 65536; two levels:
- * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk.
+ * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk; gist
+ * prefill d = 128, L a multiple of 64, 1 <= g <= 64 with 64 a multiple of g.
  * Other shapes return TCS_ERR_UNSUPPORTED.
  */
 #ifndef TCSPARSE_H
@@ -125,7 +139,7 @@
 extern "C" {
 #endif
 
-#define TCS_ABI_VERSION 5
+#define TCS_ABI_VERSION 6
 
 typedef enum {
     TCS_OK = 0,
@@ -253,6 +267,31 @@ tcs_status sparse_attn_prefill_backward_timed(const tcs_prefill_params* p,
                                               float* dv, float* dS, void* workspace,
                                               size_t workspace_bytes, void* stream,
                                               void* const* events, int n_events);
+
+typedef struct {
+    int32_t struct_size;   /* = sizeof(tcs_gist_prefill_params) */
+    int32_t B, Hq, Hkv, d;
+    int32_t M;             /* chunks                                                      */
+    int32_t L;             /* raw tokens per chunk                                        */
+    int32_t g;             /* gist tokens per chunk (they follow the chunk's raw tokens)  */
+    float scale;           /* 0 means 1/sqrt(d)                                           */
+} tcs_gist_prefill_params;
+
+tcs_status tcs_gist_prefill_workspace_size(const tcs_gist_prefill_params* p, size_t* bytes);
+
+/* SSA gist-masked prefill forward; see above.  Writes every row of out (and of lse). */
+tcs_status sparse_attn_gist_prefill(const tcs_gist_prefill_params* p,
+                                    const void* q, const void* k, const void* v,
+                                    float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Profiling variant: events[0] before the first kernel, then after the gist gather (1), the
+ * raw query rows (2) and the gist query rows (3). */
+tcs_status sparse_attn_gist_prefill_timed(const tcs_gist_prefill_params* p,
+                                          const void* q, const void* k, const void* v,
+                                          float* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream,
+                                          void* const* events, int n_events);
 
 /* Static string naming a status code. */
 const char* tcs_status_str(tcs_status s);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ops.lib().tcs_abi_version() == 5
+    assert ops.lib().tcs_abi_version() == 6
     for code in range(6):
         assert ops.status_str(code)
     assert ops.status_str(99) == "unknown status"
@@ -207,6 +207,44 @@ def test_prefill_backward_null_and_workspace_errors():
         args[miss] = None
         assert lib.sparse_attn_prefill_backward(C.byref(p), *args, fake, need,
                                                 None) == ops.TCS_ERR_NULL, miss
+
+
+def GP(**kw):
+    base = dict(B=1, Hq=8, Hkv=2, d=128, M=8, L=128, g=4)
+    base.update(kw)
+    return ops.gist_prefill_params(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=100), ops.TCS_ERR_UNSUPPORTED),      # L not a multiple of 64
+    (dict(g=3), ops.TCS_ERR_UNSUPPORTED),        # 64 not a multiple of g
+    (dict(g=128), ops.TCS_ERR_UNSUPPORTED),
+    (dict(d=64), ops.TCS_ERR_UNSUPPORTED),
+    (dict(g=0), ops.TCS_ERR_SHAPE),
+    (dict(M=0), ops.TCS_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), ops.TCS_ERR_SHAPE),
+    (dict(scale=-1.0), ops.TCS_ERR_SHAPE),
+])
+def test_gist_prefill_rejects_bad_params(kw, code):
+    p = GP(**kw)
+    n = C.c_size_t(0)
+    assert ops.lib().tcs_gist_prefill_workspace_size(C.byref(p), C.byref(n)) == code
+    assert ops.lib().sparse_attn_gist_prefill(C.byref(p), *([None] * 6), 0, None) == code
+
+
+def test_gist_prefill_null_and_workspace_errors():
+    p = GP()
+    need = ops.gist_prefill_workspace_size(p)
+    assert need == 2 * 2 * 2 * 64 * 128   # gathered gist K and V: 2 heads x 64 rows, padded
+    fake = 0x100000
+    lib = ops.lib()
+    for miss in (0, 1, 2, 3):
+        args = [fake] * 4 + [None]
+        args[miss] = None
+        assert lib.sparse_attn_gist_prefill(C.byref(p), *args, fake, need,
+                                            None) == ops.TCS_ERR_NULL
+    assert lib.sparse_attn_gist_prefill(C.byref(p), *([fake] * 4), None, fake, need - 8,
+                                        None) == ops.TCS_ERR_WORKSPACE
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -218,6 +218,36 @@ tcs_status plan_prefill_backward(const tcs_prefill_params* p, PrefillBwdPlan* pl
     return TCS_OK;
 }
 
+struct GistPrefillPlan {
+    int G, Gp;
+    float sigma;
+    size_t off_gk, off_gv, total;
+};
+
+tcs_status plan_gist_prefill(const tcs_gist_prefill_params* p, GistPrefillPlan* pl) {
+    if (!p) return TCS_ERR_NULL;
+    if (p->struct_size != (int32_t)sizeof(tcs_gist_prefill_params)) return TCS_ERR_SHAPE;
+    if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->d < 1 || p->M < 1 || p->L < 1 || p->g < 1)
+        return TCS_ERR_SHAPE;
+    if (p->Hq % p->Hkv) return TCS_ERR_SHAPE;
+    if (!(p->scale >= 0.f) || std::isinf(p->scale)) return TCS_ERR_SHAPE;
+    const int G = p->Hq / p->Hkv;
+    if (p->d != 128 || p->L % 64 || p->g > 64 || 64 % p->g || !supported_group(G))
+        return TCS_ERR_UNSUPPORTED;
+    const long long Tp = (long long)p->M * (p->L + p->g);
+    if (Tp > INT_MAX / 2 || (long long)p->B * p->Hq * Tp > (1LL << 40)) return TCS_ERR_UNSUPPORTED;
+    pl->G = G;
+    pl->Gp = (int)(((long long)p->M * p->g + 63) / 64 * 64);
+    pl->sigma = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->d);
+    const size_t rows = (size_t)p->B * p->Hkv * pl->Gp;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    pl->off_gk = take(sizeof(uint16_t) * rows * p->d);
+    pl->off_gv = take(sizeof(uint16_t) * rows * p->d);
+    pl->total = off;
+    return TCS_OK;
+}
+
 tcs_status check_ws(void* ws, size_t have, size_t need) {
     if (have < need) return TCS_ERR_WORKSPACE;
     if (need > 0 && (!ws || ((uintptr_t)ws % kAlign))) return TCS_ERR_WORKSPACE;
@@ -506,6 +536,72 @@ static tcs_status prefill_impl(const tcs_prefill_params* p, const void* q, const
     if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
     if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
     return TCS_OK;
+}
+
+tcs_status tcs_gist_prefill_workspace_size(const tcs_gist_prefill_params* p, size_t* bytes) {
+    if (!bytes) return TCS_ERR_NULL;
+    GistPrefillPlan pl;
+    tcs_status st = plan_gist_prefill(p, &pl);
+    if (st != TCS_OK) return st;
+    *bytes = pl.total;
+    return TCS_OK;
+}
+
+static tcs_status gist_prefill_impl(const tcs_gist_prefill_params* p, const void* q,
+                                    const void* k, const void* v, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* const* events, int n_events) {
+    GistPrefillPlan pl;
+    tcs_status st = plan_gist_prefill(p, &pl);
+    if (st != TCS_OK) return st;
+    if (!q || !k || !v || !out) return TCS_ERR_NULL;
+    st = check_ws(workspace, workspace_bytes, pl.total);
+    if (st != TCS_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    int stage = 0;
+    auto mark = [&]() -> bool {
+        if (stage < n_events && events && events[stage]) {
+            if (hipEventRecord((hipEvent_t)events[stage], s) != hipSuccess) return false;
+        }
+        ++stage;
+        return true;
+    };
+    if (!mark()) return TCS_ERR_HIP;
+    char* ws = (char*)workspace;
+    tcs::GistPrefillLaunch a{};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.d = p->d; a.M = p->M; a.L = p->L; a.g = p->g;
+    a.Gp = pl.Gp;
+    a.gk = (uint16_t*)(ws + pl.off_gk);
+    a.gv = (uint16_t*)(ws + pl.off_gv);
+    a.sigma = pl.sigma;
+    a.out = out;
+    a.lse = lse;
+    hipError_t e = tcs::launch_gist_gather(a, s);
+    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
+    if (e == hipSuccess) e = tcs::launch_gist_prefill_raw(a, s);
+    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
+    if (e == hipSuccess) e = tcs::launch_gist_prefill_gists(a, s);
+    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
+    if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
+    return e == hipSuccess ? TCS_OK : TCS_ERR_HIP;
+}
+
+tcs_status sparse_attn_gist_prefill(const tcs_gist_prefill_params* p, const void* q,
+                                    const void* k, const void* v, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    return gist_prefill_impl(p, q, k, v, out, lse, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+tcs_status sparse_attn_gist_prefill_timed(const tcs_gist_prefill_params* p, const void* q,
+                                          const void* k, const void* v, float* out, float* lse,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* const* events, int n_events) {
+    if (n_events < 0) return TCS_ERR_SHAPE;
+    return gist_prefill_impl(p, q, k, v, out, lse, workspace, workspace_bytes, stream, events,
+                             n_events);
 }
 
 tcs_status tcs_prefill_backward_workspace_size(const tcs_prefill_params* p, size_t* bytes) {

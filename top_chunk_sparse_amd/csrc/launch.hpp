@@ -131,6 +131,23 @@ struct PrefillBwdLaunch {
     float* dS;                // [B*Hkv][nb][nb] or null
 };
 
+// SSA gist-masked prefill over the interleaved sequence (M chunks of L raw + g gist rows).
+struct GistPrefillLaunch {
+    const uint16_t* q;        // [B][Hq][T'][d], T' = M (L + g)
+    const uint16_t* k;        // [B][Hkv][T'][d]
+    const uint16_t* v;        // [B][Hkv][T'][d]
+    int B, Hq, Hkv, d, M, L, g;
+    int Gp;                   // rows of the gathered gist arrays: M g rounded up to 64
+    uint16_t* gk;             // [B*Hkv][Gp][d]: every chunk's gist keys, chunk-major, zero pad
+    uint16_t* gv;             // [B*Hkv][Gp][d]
+    float sigma;
+    float* out;               // [B][Hq][T'][d]
+    float* lse;               // [B][Hq][T'] or null
+};
+
+hipError_t launch_gist_gather(const GistPrefillLaunch& a, hipStream_t s);
+hipError_t launch_gist_prefill_raw(const GistPrefillLaunch& a, hipStream_t s);
+hipError_t launch_gist_prefill_gists(const GistPrefillLaunch& a, hipStream_t s);
 hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s);
 hipError_t launch_prefill_bwd_prep(const PrefillBwdLaunch& a, hipStream_t s);

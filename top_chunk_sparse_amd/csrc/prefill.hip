@@ -961,4 +961,344 @@ hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// =============================================================================================
+// SSA gist-masked prefill ("Simplified Sparse Attention via Gist Tokens", section 3.1: chunk
+// tokens see their own chunk and the preceding gist tokens; later tokens reach a chunk only
+// through its gists).  Section 3.6's key-column permutation puts the summary columns first:
+// gist_gather_kernel copies every chunk's g gist K/V rows into one contiguous array, after
+// which the keys a raw query block sees are two dense runs -- the gist prefix [0, c g) and the
+// causal part of its own chunk -- and every other key block is skipped.  The block list is a
+// closed form of (chunk, block), so no mask is stored.
+//   gist_prefill_raw_kernel   raw query rows: the forward's MFMA machinery over the diagonal
+//                             block (token-causal), the chunk's earlier raw blocks and the
+//                             gist prefix blocks (the last one cut at column c g).
+//   gist_prefill_gist_kernel  gist query rows (g per chunk, a g / L share of the work): one
+//                             wave per row over the gist prefix [0, c g + t] and its chunk's
+//                             raw rows, online softmax in fp32.
+// =============================================================================================
+
+__global__ void __launch_bounds__(256) gist_gather_kernel(GistPrefillLaunch a) {
+    const int nrb = a.Gp / kPBlk;
+    const int unit = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+    const int W = a.L + a.g;
+    const size_t Tp = (size_t)a.M * W;
+    const uint16_t* ks = a.k + (size_t)unit * Tp * kPD;
+    const uint16_t* vs = a.v + (size_t)unit * Tp * kPD;
+    uint16_t* kd = a.gk + ((size_t)unit * a.Gp + (size_t)rb * kPBlk) * kPD;
+    uint16_t* vd = a.gv + ((size_t)unit * a.Gp + (size_t)rb * kPBlk) * kPD;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {   // 64 rows x 256 B = 1024 16-byte pieces per array
+        const int piece = x * 256 + threadIdx.x;
+        const int r = piece >> 4, col = (piece & 15) * 8;
+        const int gi = rb * kPBlk + r;   // gist index: chunk gi / g, gist gi % g
+        uint4 kx = make_uint4(0u, 0u, 0u, 0u), vx = kx;
+        if (gi < a.M * a.g) {
+            const size_t src = ((size_t)(gi / a.g) * W + a.L + gi % a.g) * kPD + col;
+            kx = *reinterpret_cast<const uint4*>(ks + src);
+            vx = *reinterpret_cast<const uint4*>(vs + src);
+        }
+        *reinterpret_cast<uint4*>(kd + (size_t)r * kPD + col) = kx;
+        *reinterpret_cast<uint4*>(vd + (size_t)r * kPD + col) = vx;
+    }
+}
+
+__global__ void __launch_bounds__(256, 2) gist_prefill_raw_kernel(GistPrefillLaunch a) {
+    extern __shared__ __align__(16) char lds[];
+    const int G = a.Hq / a.Hkv;
+    const int nhg = (G + 3) >> 2;
+    const int nrb = a.L / kPBlk;                 // raw blocks per chunk
+    const int nq = a.M * nrb;                    // raw query blocks per (unit, head group)
+    const int W = a.L + a.g;
+    const size_t Tp = (size_t)a.M * W;
+    // XCD-contiguous ranges as in the forward; within a range the last chunks (longest gist
+    // prefix) first, the two row halves of a block side by side
+    int bid = blockIdx.x;
+    const int Wg = gridDim.x;
+    if ((Wg & 7) == 0) bid = (bid & 7) * (Wg >> 3) + (bid >> 3);
+    const int rh = bid & 1;
+    const int qb = nq - 1 - (bid >> 1) % nq;
+    const int c = qb / nrb, rb = qb % nrb;
+    const int rest = (bid >> 1) / nq;
+    const int hg = rest % nhg;
+    const int unit = rest / nhg;
+    const int b = unit / a.Hkv, kv = unit % a.Hkv;
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, c32 = lane & 31;
+    const int head = hg * 4 + w;
+    const bool active = head < G;
+
+    const uint16_t* kraw = a.k + ((size_t)unit * Tp + (size_t)c * W) * kPD;   // chunk c's rows
+    const uint16_t* vraw = a.v + ((size_t)unit * Tp + (size_t)c * W) * kPD;
+    const uint16_t* kgst = a.gk + (size_t)unit * a.Gp * kPD;
+    const uint16_t* vgst = a.gv + (size_t)unit * a.Gp * kPD;
+    const int ngist = c * a.g;                         // visible gist columns
+    const int nbg = (ngist + kPBlk - 1) / kPBlk;       // gist prefix blocks
+    const int last_valid = ngist - (nbg - 1) * kPBlk;  // columns of the last gist block
+    const int nblk = 1 + rb + nbg;
+    // block t: 0 = the diagonal (raw block rb, token-causal), 1..rb = raw blocks 0..rb-1,
+    // rb+1.. = gist prefix blocks
+    auto kblock = [&](int t) -> const uint16_t* {
+        return t == 0 ? kraw + (size_t)rb * kPBlk * kPD
+               : t <= rb ? kraw + (size_t)(t - 1) * kPBlk * kPD
+                         : kgst + (size_t)(t - 1 - rb) * kPBlk * kPD;
+    };
+    auto vblock = [&](int t) -> const uint16_t* {
+        return t == 0 ? vraw + (size_t)rb * kPBlk * kPD
+               : t <= rb ? vraw + (size_t)(t - 1) * kPBlk * kPD
+                         : vgst + (size_t)(t - 1 - rb) * kPBlk * kPD;
+    };
+
+    const CopyOffsets gk = copy_offsets(false, w, lane), gv = copy_offsets(true, w, lane);
+    uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
+    TCS_STAGE_LOAD(kblock(0), vblock(0));
+
+    const size_t qrow = (size_t)(b * a.Hq + kv * G + (active ? head : 0)) * Tp +
+                        (size_t)c * W + (size_t)rb * kPBlk + 32 * rh + c32;
+    bf16x8 qf[8];
+    {
+        const uint16_t* qp = a.q + qrow * kPD + 8 * h;
+#pragma unroll
+        for (int kd = 0; kd < 8; ++kd) qf[kd] = *reinterpret_cast<const bf16x8*>(qp + 16 * kd);
+    }
+    TCS_STAGE_STORE(lds, lds + 2 * kPTile);
+
+    const int koff0 = c32 * 64 + (((0 + h) ^ swz_k(c32)) << 4);
+    const int koff1 = c32 * 64 + (((2 + h) ^ swz_k(c32)) << 4);
+    const int g16 = lane >> 4, L16 = lane & 15, rr = L16 >> 2, cc = L16 & 3;
+    const int voff = (4 * h + rr) * 64 + (((2 * (g16 & 1) + (cc >> 1)) ^ swz_v(rr)) << 4) +
+                     ((cc & 1) << 3);
+    wait_vmem();
+
+    const float cs = a.sigma * kLog2e;
+    f32x16 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    float m = 0.f, l = 0.f;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+
+    for (int t = 0; t < nblk; ++t) {
+        __syncthreads();
+        const int buf = t & 1;
+        if (t + 1 < nblk) TCS_STAGE_LOAD(kblock(t + 1), vblock(t + 1));
+        if (active) {
+            const bool half = (t == 0) && rh == 0;
+            const int cut = (t == nblk - 1 && t > rb) ? last_valid : kPBlk;   // valid keys
+            const char* kt = lds + buf * kPTile;
+            const char* vt = lds + (2 + buf) * kPTile + voff;
+            f32x16 s[2];
+            s[0] = s[1] = f32x16{};
+            if (half) qk_product<1>(kt, koff0, koff1, qf, s);
+            else qk_product<2>(kt, koff0, koff1, qf, s);
+            bf16x8 va[4][4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                if (half && st >= 2) break;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) va[st][dt] = v_operand(vt, dt, st);
+            }
+            const int q = 32 * rh + c32;
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = 32 * x + 8 * (e >> 2) + 4 * h + (e & 3);
+                    if ((t == 0 && key > q) || key >= cut) s[x][e] = -INFINITY;
+                }
+            float mx = s[0][0];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[x][e]);
+            mx = pair_max(mx);
+            const float mb = mx * cs;
+            if (t == 0) {
+                m = mb;
+            } else if (__builtin_amdgcn_ballot_w64(mb > m + kRescaleSlack)) {
+                const float mn = fmaxf(m, mb);
+                const float al = __builtin_amdgcn_exp2f(m - mn);
+                m = mn;
+                l *= al;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) o[dt] *= al;
+            }
+            const float off = -m;
+            float sum = 0.f;
+            auto p_step = [&](int st) {
+                bf16x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pv[e] = (__bf16)__builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + e] * cs + off);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), ones, sum, false);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, sum, false);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, sum, false);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, sum, false);
+                return pv;
+            };
+            auto pv_mfma = [&](int st, const bf16x8& pst) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st][dt], pst, o[dt], 0, 0, 0);
+            };
+            if (half) {
+                const bf16x8 p0 = p_step(0);
+                const bf16x8 p1 = p_step(1);
+                pv_mfma(0, p0);
+                pv_mfma(1, p1);
+            } else {
+                const bf16x8 p0 = p_step(0);
+                const bf16x8 p1 = p_step(1);
+                pv_mfma(0, p0);
+                const bf16x8 p2 = p_step(2);
+                pv_mfma(1, p1);
+                const bf16x8 p3 = p_step(3);
+                pv_mfma(2, p2);
+                pv_mfma(3, p3);
+            }
+            l += sum;
+        }
+        if (t + 1 < nblk) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
+    }
+    if (!active) return;
+    const float lt = pair_sum(l);
+    const float inv = 1.f / lt;
+    float* op = a.out + qrow * kPD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            float4 v;
+            v.x = o[dt][4 * e4 + 0] * inv;
+            v.y = o[dt][4 * e4 + 1] * inv;
+            v.z = o[dt][4 * e4 + 2] * inv;
+            v.w = o[dt][4 * e4 + 3] * inv;
+            *reinterpret_cast<float4*>(op + 32 * dt + 8 * e4 + 4 * h) = v;
+        }
+    if (a.lse && h == 0) a.lse[qrow] = (m + log2f(lt)) * kLn2;
+}
+
+// Gist query rows: wave w of the workgroup for (unit, chunk c) takes rows (head, gist t) in
+// turn.  Keys: the gist prefix [0, c g + t] of the gathered arrays, then chunk c's L raw rows.
+// Keys go in pieces of 64, one per lane: logit of the lane's key, piece max and sum over the
+// wave, then every lane accumulates its two output dims over the piece's keys.
+constexpr int kGistRowsKeysPerPiece = 64;
+
+__global__ void __launch_bounds__(256) gist_prefill_gist_kernel(GistPrefillLaunch a) {
+    __shared__ float qs[4][kPD];                       // the wave's query row (fp32)
+    __shared__ float ps[4][kGistRowsKeysPerPiece];     // the piece's weights
+    const int G = a.Hq / a.Hkv;
+    const int unit = blockIdx.x / a.M, c = blockIdx.x % a.M;
+    const int b = unit / a.Hkv, kv = unit % a.Hkv;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int W = a.L + a.g;
+    const size_t Tp = (size_t)a.M * W;
+    const uint16_t* kraw = a.k + ((size_t)unit * Tp + (size_t)c * W) * kPD;
+    const uint16_t* vraw = a.v + ((size_t)unit * Tp + (size_t)c * W) * kPD;
+    const uint16_t* kgst = a.gk + (size_t)unit * a.Gp * kPD;
+    const uint16_t* vgst = a.gv + (size_t)unit * a.Gp * kPD;
+    const float cs = a.sigma * kLog2e;
+    for (int r = w; r < G * a.g; r += 4) {
+        const int hd = r / a.g, t = r % a.g;
+        const size_t qrow = (size_t)(b * a.Hq + kv * G + hd) * Tp + (size_t)c * W + a.L + t;
+        {
+            const uint32_t qw = reinterpret_cast<const uint32_t*>(a.q + qrow * kPD)[lane];
+            qs[w][2 * lane] = bf16_lo(qw);
+            qs[w][2 * lane + 1] = bf16_hi(qw);
+        }
+        wait_lds();
+        __builtin_amdgcn_wave_barrier();
+        const int ngk = c * a.g + t + 1;     // visible gists (gathered order)
+        const int nk = ngk + a.L;            // then the chunk's raw rows
+        float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+        for (int k0 = 0; k0 < nk; k0 += kGistRowsKeysPerPiece) {
+            const int x = k0 + lane;
+            float lg = -INFINITY;
+            if (x < nk) {
+                const uint16_t* kr = x < ngk ? kgst + (size_t)x * kPD : kraw + (size_t)(x - ngk) * kPD;
+                float acc = 0.f;
+#pragma unroll 4
+                for (int e = 0; e < kPD; e += 8) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(kr + e);
+                    acc += bf16_lo(u.x) * qs[w][e + 0] + bf16_hi(u.x) * qs[w][e + 1] +
+                           bf16_lo(u.y) * qs[w][e + 2] + bf16_hi(u.y) * qs[w][e + 3] +
+                           bf16_lo(u.z) * qs[w][e + 4] + bf16_hi(u.z) * qs[w][e + 5] +
+                           bf16_lo(u.w) * qs[w][e + 6] + bf16_hi(u.w) * qs[w][e + 7];
+                }
+                lg = acc * cs;
+            }
+            const float pm = wave_max(lg);
+            const float mn = fmaxf(m, pm);
+            const float al = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first piece
+            const float p = x < nk ? __builtin_amdgcn_exp2f(lg - mn) : 0.f;
+            l = l * al + wave_sum(p);
+            o0 *= al;
+            o1 *= al;
+            m = mn;
+            ps[w][lane] = p;
+            wait_lds();
+            __builtin_amdgcn_wave_barrier();
+            const int np = min(kGistRowsKeysPerPiece, nk - k0);
+            for (int y = 0; y < np; ++y) {
+                const int xk = k0 + y;
+                const uint16_t* vr = xk < ngk ? vgst + (size_t)xk * kPD : vraw + (size_t)(xk - ngk) * kPD;
+                const uint32_t vw = reinterpret_cast<const uint32_t*>(vr)[lane];
+                const float py = ps[w][y];
+                o0 += py * bf16_lo(vw);
+                o1 += py * bf16_hi(vw);
+            }
+            wait_lds();
+            __builtin_amdgcn_wave_barrier();   // ps is rewritten by the next piece
+        }
+        const float inv = 1.f / l;
+        float2 ov;
+        ov.x = o0 * inv;
+        ov.y = o1 * inv;
+        *reinterpret_cast<float2*>(a.out + qrow * kPD + 2 * lane) = ov;
+        if (a.lse && lane == 0) a.lse[qrow] = (m + log2f(l)) * kLn2;
+    }
+}
+
+static hipError_t gist_check(const GistPrefillLaunch& a) {
+    if (a.d != kPD || a.L % kPBlk || a.g < 1 || a.g > kPBlk || kPBlk % a.g || a.Hkv <= 0 ||
+        a.Hq % a.Hkv || a.Gp % kPBlk || a.Gp < a.M * a.g)
+        return hipErrorNotSupported;
+    return hipSuccess;
+}
+
+hipError_t launch_gist_gather(const GistPrefillLaunch& a, hipStream_t s) {
+    hipError_t e = gist_check(a);
+    if (e != hipSuccess) return e;
+    const long long W = (long long)a.B * a.Hkv * (a.Gp / kPBlk);
+    if (W <= 0) return hipSuccess;
+    if (W > 0x7fffffffLL) return hipErrorNotSupported;
+    gist_gather_kernel<<<(unsigned)W, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gist_prefill_raw(const GistPrefillLaunch& a, hipStream_t s) {
+    hipError_t e = gist_check(a);
+    if (e != hipSuccess) return e;
+    const int G = a.Hq / a.Hkv;
+    const long long W = 2LL * a.B * a.Hkv * a.M * (a.L / kPBlk) * ((G + 3) / 4);
+    if (W <= 0) return hipSuccess;
+    if (W > 0x7fffffffLL) return hipErrorNotSupported;
+    e = hipFuncSetAttribute((const void*)gist_prefill_raw_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
+    if (e != hipSuccess) return e;
+    gist_prefill_raw_kernel<<<(unsigned)W, 256, kPLds, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gist_prefill_gists(const GistPrefillLaunch& a, hipStream_t s) {
+    hipError_t e = gist_check(a);
+    if (e != hipSuccess) return e;
+    const long long W = (long long)a.B * a.Hkv * a.M;
+    if (W <= 0) return hipSuccess;
+    if (W > 0x7fffffffLL) return hipErrorNotSupported;
+    gist_prefill_gist_kernel<<<(unsigned)W, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace tcs

@@ -31,6 +31,11 @@ class DecodeParams(C.Structure):
                                                                       ("select_mode", C.c_int32)]
 
 
+class GistPrefillParams(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("struct_size", "B", "Hq", "Hkv", "d", "M", "L",
+                                         "g")] + [("scale", C.c_float)]
+
+
 class PrefillParams(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("struct_size", "B", "Hq", "Hkv", "d", "T", "blk", "k",
                                          "gate_mode")] + [("scale", C.c_float)]
@@ -43,7 +48,8 @@ EXPORTS = ("tcs_abi_version", "tcs_status_str", "tcs_decode_workspace_size", "sp
            "sparse_attn_decode_timed", "tcs_decode_stage_count", "tcs_workspace_init",
            "tcs_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_prefill_timed",
            "tcs_prefill_backward_workspace_size", "sparse_attn_prefill_backward",
-           "sparse_attn_prefill_backward_timed")
+           "sparse_attn_prefill_backward_timed", "tcs_gist_prefill_workspace_size",
+           "sparse_attn_gist_prefill", "sparse_attn_gist_prefill_timed")
 
 
 def lib():
@@ -63,6 +69,12 @@ def lib():
         h.sparse_attn_prefill.argtypes = [C.POINTER(PrefillParams)] + [_V] * 8 + [C.c_size_t, _V]
         h.sparse_attn_decode_timed.argtypes = h.sparse_attn_decode.argtypes + [_V, C.c_int]
         h.sparse_attn_prefill_timed.argtypes = h.sparse_attn_prefill.argtypes + [_V, C.c_int]
+        h.tcs_gist_prefill_workspace_size.argtypes = [C.POINTER(GistPrefillParams),
+                                                      C.POINTER(C.c_size_t)]
+        h.sparse_attn_gist_prefill.argtypes = ([C.POINTER(GistPrefillParams)] + [_V] * 6 +
+                                               [C.c_size_t, _V])
+        h.sparse_attn_gist_prefill_timed.argtypes = (h.sparse_attn_gist_prefill.argtypes +
+                                                     [_V, C.c_int])
         h.tcs_prefill_backward_workspace_size.argtypes = [C.POINTER(PrefillParams),
                                                           C.POINTER(C.c_size_t)]
         h.sparse_attn_prefill_backward.argtypes = ([C.POINTER(PrefillParams)] + [_V] * 13 +
@@ -180,6 +192,31 @@ def sparse_attn_prefill_backward(p: PrefillParams, q, k, v, S, out, lse, dout, d
     _check(code)
 
 
+def gist_prefill_params(*, B, Hq, Hkv, d, M, L, g, scale=0.0) -> GistPrefillParams:
+    return GistPrefillParams(struct_size=C.sizeof(GistPrefillParams), B=B, Hq=Hq, Hkv=Hkv, d=d,
+                             M=M, L=L, g=g, scale=scale)
+
+
+def gist_prefill_workspace_size(p: GistPrefillParams) -> int:
+    n = C.c_size_t(0)
+    _check(lib().tcs_gist_prefill_workspace_size(C.byref(p), C.byref(n)))
+    return n.value
+
+
+def sparse_attn_gist_prefill(p: GistPrefillParams, q, k, v, *, out, lse=None, workspace,
+                             stream=None, events=None) -> None:
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device)
+    args = (C.byref(p), _p(q), _p(k), _p(v), _p(out), _p(lse), _p(workspace),
+            workspace.numel() * workspace.element_size() if workspace is not None else 0,
+            stream.cuda_stream)
+    if events is None:
+        code = lib().sparse_attn_gist_prefill(*args)
+    else:
+        code = lib().sparse_attn_gist_prefill_timed(*args, C.cast(events, _V), len(events))
+    _check(code)
+
+
 def workspace(nbytes: int, device, stream=None) -> torch.Tensor:
     """A caller-owned workspace (256-byte aligned by the torch allocator), zero-filled by the
     library's init kernel as a new decode workspace must be."""
@@ -273,4 +310,25 @@ class PrefillBwdCall:
         sparse_attn_prefill_backward(self.p, i.q, i.k, i.v, i.S, self.fwd.out, self.fwd.lse,
                                      self.dout, self.dlse, dq=self.dq, dk=self.dk, dv=self.dv,
                                      dS=self.dS, workspace=self.ws, stream=stream, events=events)
+        return self
+
+
+class GistPrefillCall:
+    """Outputs and workspace for repeated SSA gist-masked prefill calls on one input bundle."""
+
+    def __init__(self, inp, scale=0.0):
+        c = inp.cfg
+        dev = inp.q.device
+        self.inp = inp
+        self.p = gist_prefill_params(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, M=c.M, L=c.L, g=c.g,
+                                     scale=scale)
+        self.out = torch.empty((c.B, c.Hq, c.Tp, c.d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((c.B, c.Hq, c.Tp), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(max(gist_prefill_workspace_size(self.p), 1), dtype=torch.uint8,
+                              device=dev)
+
+    def __call__(self, stream=None, events=None):
+        i = self.inp
+        sparse_attn_gist_prefill(self.p, i.q, i.k, i.v, out=self.out, lse=self.lse,
+                                 workspace=self.ws, stream=stream, events=events)
         return self
