@@ -23,6 +23,8 @@ import time
 
 METRIC = "decode attn calls/s and effective HBM GB/s (% of peak) at 128K ctx, k=16"
 PREFILL_METRIC = "SAS block-sparse causal prefill forward, algorithmic TFLOP/s at 16K tokens, k=16"
+GIST_PREFILL_METRIC = ("SSA gist-masked prefill forward, algorithmic TFLOP/s at 16K raw tokens "
+                       "(128 chunks of 128 + 4 gists)")
 PREFILL_BWD_METRIC = ("SAS block-sparse causal prefill backward (dq, dk, dv, dS), algorithmic "
                       "TFLOP/s at 16K tokens, k=16")
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, vendor figure
@@ -88,6 +90,16 @@ def prefill_bwd_flops(cfg, products=5):
     dout.v recomputed, and the dq, dk and dv products (5; the dq kernel alone does 3: q.k,
     dout.v, dq; the dk / dv kernel 4: q.k, dout.v, dk, dv)."""
     return 2 * products * cfg.d * prefill_pairs(cfg)
+
+
+def gist_prefill_pairs(cfg):
+    """Attended (query, key) pairs of one SSA gist-masked prefill call, raw rows and gist rows:
+    raw row r of chunk c sees c g gists and r + 1 raw keys; gist t of chunk c sees c g + t + 1
+    gists and the chunk's L raw keys."""
+    M, L, g = cfg.M, cfg.L, cfg.g
+    raw = L * g * M * (M - 1) // 2 + M * L * (L + 1) // 2
+    gist = g * g * M * (M - 1) // 2 + M * g * (g + 1) // 2 + M * g * L
+    return cfg.B * cfg.Hq * raw, cfg.B * cfg.Hq * gist
 
 
 def prefill_bytes(cfg):
@@ -218,6 +230,37 @@ def cpu_baseline_prefill_backward(inp, dout, dlse, budget_s):
             "cpu": cpu_model(), "calls_per_s": round(flops / dt / prefill_bwd_flops(c), 6)}
 
 
+def cpu_baseline_gist_prefill(inp, budget_s):
+    """Time the fp64 CPU oracle (as it stands) on a seeded sample of query rows of instance 0,
+    scaled to algorithmic TFLOP/s (4 d per attended pair)."""
+    import numpy as np
+    import oracle
+    from top_chunk_sparse_amd.synth import bf16_bits
+    c = inp.cfg
+    args = dict(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, M=c.M, L=c.L, g=c.g, q=bf16_bits(inp.q),
+                k_=bf16_bits(inp.k), v=bf16_bits(inp.v))
+    total = c.B * c.Hq * c.Tp
+    order = np.random.default_rng(12345).permutation(total).astype(np.int32)
+    def pairs(rows):
+        pos = rows % c.Tp
+        ch, off = pos // c.W, pos % c.W
+        n = np.where(off < c.L, ch * c.g + off + 1, ch * c.g + (off - c.L) + 1 + c.L)
+        return int(n.sum())
+    oracle.gist_prefill(rows=order[:8], **args)      # untimed: library load, first touch
+    n, t0 = 256, time.perf_counter()
+    oracle.gist_prefill(rows=order[:n], **args)
+    dt = time.perf_counter() - t0
+    while dt < budget_s * 0.5 and n < total:
+        n = min(total, int(n * max(2.0, budget_s / max(dt, 1e-3) * 0.9)))
+        t0 = time.perf_counter()
+        oracle.gist_prefill(rows=order[:n], **args)
+        dt = time.perf_counter() - t0
+    flops = 4 * c.d * pairs(order[:n])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "sample": f"{n} of {total} query rows of instance 0, seeded random "
+            "choice", "seconds": round(dt, 3), "cpu": cpu_model()}
+
+
 def load_traffic(kernel_name, workload):
     """HBM traffic per launch from committed rocprofv3 counter runs, only if the kernel
     sources are unchanged since the counters were taken."""
@@ -309,6 +352,88 @@ def run_prefill(args, torch, configs, ops):
         "algorithmic_flops_per_call": flops,
         "attended_pairs_per_call": prefill_pairs(cfg),
         "algorithmic_bytes_per_call": prefill_bytes(cfg),
+        "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 5),
+        "stage_ms": [round(x, 5) for x in stage_ms],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def run_gist_prefill(args, torch, configs, ops):
+    from top_chunk_sparse_amd.synth import make_gist_prefill
+    import ctypes
+    cfg = configs.GIST_PREFILL_CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    R = max(1, min(args.instances, 2))
+    print(f"# generating {R} instance(s) of {cfg.name}", file=sys.stderr, flush=True)
+    insts = [make_gist_prefill(cfg, configs.seed_for(cfg.name, r), device=dev) for r in range(R)]
+    calls = [ops.GistPrefillCall(inp) for inp in insts]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        calls[i % R]()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        calls[i % R]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    nst = 3   # gist gather, raw query rows, gist query rows
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+           for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        arr = (ctypes.c_void_p * (nst + 1))(*[e.cuda_event for e in evs[i]])
+        calls[i % R](events=arr)
+    torch.cuda.synchronize()
+    stage_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+                for j in range(nst)]
+    print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
+    raw_pairs, gist_pairs = gist_prefill_pairs(cfg)
+    flops = 4 * cfg.d * (raw_pairs + gist_pairs)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kflops = 4 * cfg.d * raw_pairs
+    ach = kflops / (stage_ms[1] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": "gist_prefill_mfma_kernel<false> (raw query rows)",
+            "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": load_traffic("gist_prefill_raw_rows", cfg.name),
+            "algorithmic_flops": kflops, "avg_ms": round(stage_ms[1], 5)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_gist_prefill(insts[0], args.cpu_seconds)
+    rec = {
+        "metric": GIST_PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
+                   "M": cfg.M, "L": cfg.L, "g": cfg.g, "positions": cfg.Tp, "inputs": "bf16",
+                   "accumulation": "fp32", "instances_rotated": R},
+        "calls_per_s": round(args.steps / wall, 2),
+        "algorithmic_flops_per_call": flops,
+        "attended_pairs_per_call": raw_pairs + gist_pairs,
+        "dense_causal_pairs_per_call": cfg.B * cfg.Hq * cfg.Tp * (cfg.Tp + 1) // 2,
         "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 5),
         "stage_ms": [round(x, 5) for x in stage_ms],
         "roofline": roof,
@@ -450,6 +575,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload in configs.GIST_PREFILL_CONFIGS:
+        return run_gist_prefill(args, torch, configs, ops)
     if args.workload in configs.PREFILL_CONFIGS:
         if args.backward:
             return run_prefill_backward(args, torch, configs, ops)

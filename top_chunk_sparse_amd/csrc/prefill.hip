@@ -969,12 +969,15 @@ hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s) {
 // which the keys a raw query block sees are two dense runs -- the gist prefix [0, c g) and the
 // causal part of its own chunk -- and every other key block is skipped.  The block list is a
 // closed form of (chunk, block), so no mask is stored.
-//   gist_prefill_raw_kernel   raw query rows: the forward's MFMA machinery over the diagonal
-//                             block (token-causal), the chunk's earlier raw blocks and the
-//                             gist prefix blocks (the last one cut at column c g).
-//   gist_prefill_gist_kernel  gist query rows (g per chunk, a g / L share of the work): one
-//                             wave per row over the gist prefix [0, c g + t] and its chunk's
-//                             raw rows, online softmax in fp32.
+//   gist_prefill_mfma_kernel<false>  raw query rows: the forward's MFMA machinery over the
+//                             diagonal block (token-causal), the chunk's earlier raw blocks and
+//                             the gist prefix blocks (the last one cut at column c g).
+//   gist_prefill_mfma_kernel<true>   gist query rows, in gathered order: gist t of chunk c is
+//                             gathered row c g + t and sees the gathered gists up to itself --
+//                             causal attention over the gathered gists -- plus its own chunk's
+//                             L raw rows, one block list per 32-row tile: gist blocks up to the
+//                             tile's diagonal, then the raw blocks of the chunks the tile spans,
+//                             each visible only to its chunk's rows.
 // =============================================================================================
 
 __global__ void __launch_bounds__(256) gist_gather_kernel(GistPrefillLaunch a) {
@@ -1002,12 +1005,15 @@ __global__ void __launch_bounds__(256) gist_gather_kernel(GistPrefillLaunch a) {
     }
 }
 
-__global__ void __launch_bounds__(256, 2) gist_prefill_raw_kernel(GistPrefillLaunch a) {
+template <bool GROWS>
+__global__ void __launch_bounds__(256, 2) gist_prefill_mfma_kernel(GistPrefillLaunch a) {
     extern __shared__ __align__(16) char lds[];
     const int G = a.Hq / a.Hkv;
     const int nhg = (G + 3) >> 2;
     const int nrb = a.L / kPBlk;                 // raw blocks per chunk
-    const int nq = a.M * nrb;                    // raw query blocks per (unit, head group)
+    // query blocks per (unit, head group): raw blocks of every chunk, or 64-row blocks of the
+    // gathered gists
+    const int nq = GROWS ? a.Gp / kPBlk : a.M * nrb;
     const int W = a.L + a.g;
     const size_t Tp = (size_t)a.M * W;
     // XCD-contiguous ranges as in the forward; within a range the last chunks (longest gist
@@ -1017,11 +1023,18 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_raw_kernel(GistPrefillLau
     if ((Wg & 7) == 0) bid = (bid & 7) * (Wg >> 3) + (bid >> 3);
     const int rh = bid & 1;
     const int qb = nq - 1 - (bid >> 1) % nq;
-    const int c = qb / nrb, rb = qb % nrb;
     const int rest = (bid >> 1) / nq;
     const int hg = rest % nhg;
     const int unit = rest / nhg;
     const int b = unit / a.Hkv, kv = unit % a.Hkv;
+    const int ngtot = a.M * a.g;                 // gathered gist rows
+    // raw rows: chunk c, block rb.  Gist rows: gathered rows R0 .. R0 + 31 of chunks
+    // c_lo .. c_hi.
+    const int c = GROWS ? 0 : qb / nrb, rb = GROWS ? 0 : qb % nrb;
+    const int R0 = GROWS ? qb * kPBlk + 32 * rh : 0;
+    if (GROWS && R0 >= ngtot) return;            // padding rows only (uniform per workgroup)
+    const int c_lo = GROWS ? R0 / a.g : 0;
+    const int c_hi = GROWS ? min(R0 + 31, ngtot - 1) / a.g : 0;
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -1033,29 +1046,46 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_raw_kernel(GistPrefillLau
     const uint16_t* vraw = a.v + ((size_t)unit * Tp + (size_t)c * W) * kPD;
     const uint16_t* kgst = a.gk + (size_t)unit * a.Gp * kPD;
     const uint16_t* vgst = a.gv + (size_t)unit * a.Gp * kPD;
-    const int ngist = c * a.g;                         // visible gist columns
-    const int nbg = (ngist + kPBlk - 1) / kPBlk;       // gist prefix blocks
+    const int ngist = c * a.g;                         // raw rows: visible gist columns
+    const int nbg = (ngist + kPBlk - 1) / kPBlk;       // raw rows: gist prefix blocks
     const int last_valid = ngist - (nbg - 1) * kPBlk;  // columns of the last gist block
-    const int nblk = 1 + rb + nbg;
-    // block t: 0 = the diagonal (raw block rb, token-causal), 1..rb = raw blocks 0..rb-1,
-    // rb+1.. = gist prefix blocks
+    // Raw rows, block t: 0 = the diagonal (raw block rb, token-causal), 1..rb = raw blocks
+    // 0..rb-1, rb+1.. = gist prefix blocks.  Gist rows, block t: 0..qb = gathered gist blocks
+    // (qb is the diagonal, causal in gathered order), then raw block u = t - qb - 1 of chunk
+    // c_lo + u / nrb.
+    const int nblk = GROWS ? qb + 1 + (c_hi - c_lo + 1) * nrb : 1 + rb + nbg;
+    auto blk_row = [&](int t) -> size_t {   // first row of block t in its array
+        if (GROWS) {
+            if (t <= qb) return (size_t)t * kPBlk;
+            const int u = t - qb - 1;
+            return (size_t)(c_lo + u / nrb) * W + (size_t)(u % nrb) * kPBlk;
+        }
+        return t == 0 ? (size_t)rb * kPBlk : t <= rb ? (size_t)(t - 1) * kPBlk
+                                                     : (size_t)(t - 1 - rb) * kPBlk;
+    };
+    auto in_gathered = [&](int t) { return GROWS ? t <= qb : t > rb; };
+    const uint16_t* kall = a.k + (size_t)unit * Tp * kPD;   // the interleaved rows of the unit
+    const uint16_t* vall = a.v + (size_t)unit * Tp * kPD;
     auto kblock = [&](int t) -> const uint16_t* {
-        return t == 0 ? kraw + (size_t)rb * kPBlk * kPD
-               : t <= rb ? kraw + (size_t)(t - 1) * kPBlk * kPD
-                         : kgst + (size_t)(t - 1 - rb) * kPBlk * kPD;
+        return (in_gathered(t) ? kgst : GROWS ? kall : kraw) + blk_row(t) * kPD;
     };
     auto vblock = [&](int t) -> const uint16_t* {
-        return t == 0 ? vraw + (size_t)rb * kPBlk * kPD
-               : t <= rb ? vraw + (size_t)(t - 1) * kPBlk * kPD
-                         : vgst + (size_t)(t - 1 - rb) * kPBlk * kPD;
+        return (in_gathered(t) ? vgst : GROWS ? vall : vraw) + blk_row(t) * kPD;
     };
 
     const CopyOffsets gk = copy_offsets(false, w, lane), gv = copy_offsets(true, w, lane);
     uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
     TCS_STAGE_LOAD(kblock(0), vblock(0));
 
-    const size_t qrow = (size_t)(b * a.Hq + kv * G + (active ? head : 0)) * Tp +
-                        (size_t)c * W + (size_t)rb * kPBlk + 32 * rh + c32;
+    // this lane's query row: raw row 64 rb + 32 rh + c32 of chunk c, or gathered gist row
+    // r = R0 + c32 (clamped for loading when r is padding; nothing is written for it)
+    const int r = R0 + c32;
+    const bool row_ok = !GROWS || r < ngtot;
+    const int rq = GROWS ? min(r, ngtot - 1) : 0;
+    const int rchunk = GROWS ? rq / a.g : c;
+    const size_t qpos = GROWS ? (size_t)rchunk * W + a.L + rq % a.g
+                              : (size_t)c * W + (size_t)rb * kPBlk + 32 * rh + c32;
+    const size_t qrow = (size_t)(b * a.Hq + kv * G + (active ? head : 0)) * Tp + qpos;
     bf16x8 qf[8];
     {
         const uint16_t* qp = a.q + qrow * kPD + 8 * h;
@@ -1083,8 +1113,8 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_raw_kernel(GistPrefillLau
         const int buf = t & 1;
         if (t + 1 < nblk) TCS_STAGE_LOAD(kblock(t + 1), vblock(t + 1));
         if (active) {
-            const bool half = (t == 0) && rh == 0;
-            const int cut = (t == nblk - 1 && t > rb) ? last_valid : kPBlk;   // valid keys
+            const bool half = !GROWS && (t == 0) && rh == 0;
+            const int cut = (!GROWS && t == nblk - 1 && t > rb) ? last_valid : kPBlk;
             const char* kt = lds + buf * kPTile;
             const char* vt = lds + (2 + buf) * kPTile + voff;
             f32x16 s[2];
@@ -1098,21 +1128,35 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_raw_kernel(GistPrefillLau
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) va[st][dt] = v_operand(vt, dt, st);
             }
-            const int q = 32 * rh + c32;
+            if constexpr (GROWS) {
+                // gathered gist blocks: causal in gathered order on the diagonal block; a raw
+                // block: visible only to the rows of its chunk
+                const bool own = t <= qb || c_lo + (t - qb - 1) / nrb == rchunk;
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+                for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = 32 * x + 8 * (e >> 2) + 4 * h + (e & 3);
-                    if ((t == 0 && key > q) || key >= cut) s[x][e] = -INFINITY;
-                }
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = 32 * x + 8 * (e >> 2) + 4 * h + (e & 3);
+                        if (!own || (t == qb && t * kPBlk + key > rq)) s[x][e] = -INFINITY;
+                    }
+            } else {
+                const int q = 32 * rh + c32;
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = 32 * x + 8 * (e >> 2) + 4 * h + (e & 3);
+                        if ((t == 0 && key > q) || key >= cut) s[x][e] = -INFINITY;
+                    }
+            }
             float mx = s[0][0];
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[x][e]);
             mx = pair_max(mx);
-            const float mb = mx * cs;
+            // a raw block of another chunk leaves a gist row without keys: no update
+            const float mb = mx == -INFINITY ? m : mx * cs;
             if (t == 0) {
                 m = mb;
             } else if (__builtin_amdgcn_ballot_w64(mb > m + kRescaleSlack)) {
@@ -1160,7 +1204,7 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_raw_kernel(GistPrefillLau
         }
         if (t + 1 < nblk) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
     }
-    if (!active) return;
+    if (!active || !row_ok) return;
     const float lt = pair_sum(l);
     const float inv = 1.f / lt;
     float* op = a.out + qrow * kPD;
@@ -1176,88 +1220,6 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_raw_kernel(GistPrefillLau
             *reinterpret_cast<float4*>(op + 32 * dt + 8 * e4 + 4 * h) = v;
         }
     if (a.lse && h == 0) a.lse[qrow] = (m + log2f(lt)) * kLn2;
-}
-
-// Gist query rows: wave w of the workgroup for (unit, chunk c) takes rows (head, gist t) in
-// turn.  Keys: the gist prefix [0, c g + t] of the gathered arrays, then chunk c's L raw rows.
-// Keys go in pieces of 64, one per lane: logit of the lane's key, piece max and sum over the
-// wave, then every lane accumulates its two output dims over the piece's keys.
-constexpr int kGistRowsKeysPerPiece = 64;
-
-__global__ void __launch_bounds__(256) gist_prefill_gist_kernel(GistPrefillLaunch a) {
-    __shared__ float qs[4][kPD];                       // the wave's query row (fp32)
-    __shared__ float ps[4][kGistRowsKeysPerPiece];     // the piece's weights
-    const int G = a.Hq / a.Hkv;
-    const int unit = blockIdx.x / a.M, c = blockIdx.x % a.M;
-    const int b = unit / a.Hkv, kv = unit % a.Hkv;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int W = a.L + a.g;
-    const size_t Tp = (size_t)a.M * W;
-    const uint16_t* kraw = a.k + ((size_t)unit * Tp + (size_t)c * W) * kPD;
-    const uint16_t* vraw = a.v + ((size_t)unit * Tp + (size_t)c * W) * kPD;
-    const uint16_t* kgst = a.gk + (size_t)unit * a.Gp * kPD;
-    const uint16_t* vgst = a.gv + (size_t)unit * a.Gp * kPD;
-    const float cs = a.sigma * kLog2e;
-    for (int r = w; r < G * a.g; r += 4) {
-        const int hd = r / a.g, t = r % a.g;
-        const size_t qrow = (size_t)(b * a.Hq + kv * G + hd) * Tp + (size_t)c * W + a.L + t;
-        {
-            const uint32_t qw = reinterpret_cast<const uint32_t*>(a.q + qrow * kPD)[lane];
-            qs[w][2 * lane] = bf16_lo(qw);
-            qs[w][2 * lane + 1] = bf16_hi(qw);
-        }
-        wait_lds();
-        __builtin_amdgcn_wave_barrier();
-        const int ngk = c * a.g + t + 1;     // visible gists (gathered order)
-        const int nk = ngk + a.L;            // then the chunk's raw rows
-        float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-        for (int k0 = 0; k0 < nk; k0 += kGistRowsKeysPerPiece) {
-            const int x = k0 + lane;
-            float lg = -INFINITY;
-            if (x < nk) {
-                const uint16_t* kr = x < ngk ? kgst + (size_t)x * kPD : kraw + (size_t)(x - ngk) * kPD;
-                float acc = 0.f;
-#pragma unroll 4
-                for (int e = 0; e < kPD; e += 8) {
-                    const uint4 u = *reinterpret_cast<const uint4*>(kr + e);
-                    acc += bf16_lo(u.x) * qs[w][e + 0] + bf16_hi(u.x) * qs[w][e + 1] +
-                           bf16_lo(u.y) * qs[w][e + 2] + bf16_hi(u.y) * qs[w][e + 3] +
-                           bf16_lo(u.z) * qs[w][e + 4] + bf16_hi(u.z) * qs[w][e + 5] +
-                           bf16_lo(u.w) * qs[w][e + 6] + bf16_hi(u.w) * qs[w][e + 7];
-                }
-                lg = acc * cs;
-            }
-            const float pm = wave_max(lg);
-            const float mn = fmaxf(m, pm);
-            const float al = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first piece
-            const float p = x < nk ? __builtin_amdgcn_exp2f(lg - mn) : 0.f;
-            l = l * al + wave_sum(p);
-            o0 *= al;
-            o1 *= al;
-            m = mn;
-            ps[w][lane] = p;
-            wait_lds();
-            __builtin_amdgcn_wave_barrier();
-            const int np = min(kGistRowsKeysPerPiece, nk - k0);
-            for (int y = 0; y < np; ++y) {
-                const int xk = k0 + y;
-                const uint16_t* vr = xk < ngk ? vgst + (size_t)xk * kPD : vraw + (size_t)(xk - ngk) * kPD;
-                const uint32_t vw = reinterpret_cast<const uint32_t*>(vr)[lane];
-                const float py = ps[w][y];
-                o0 += py * bf16_lo(vw);
-                o1 += py * bf16_hi(vw);
-            }
-            wait_lds();
-            __builtin_amdgcn_wave_barrier();   // ps is rewritten by the next piece
-        }
-        const float inv = 1.f / l;
-        float2 ov;
-        ov.x = o0 * inv;
-        ov.y = o1 * inv;
-        *reinterpret_cast<float2*>(a.out + qrow * kPD + 2 * lane) = ov;
-        if (a.lse && lane == 0) a.lse[qrow] = (m + log2f(l)) * kLn2;
-    }
 }
 
 static hipError_t gist_check(const GistPrefillLaunch& a) {
@@ -1284,20 +1246,24 @@ hipError_t launch_gist_prefill_raw(const GistPrefillLaunch& a, hipStream_t s) {
     const long long W = 2LL * a.B * a.Hkv * a.M * (a.L / kPBlk) * ((G + 3) / 4);
     if (W <= 0) return hipSuccess;
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    e = hipFuncSetAttribute((const void*)gist_prefill_raw_kernel,
+    e = hipFuncSetAttribute((const void*)gist_prefill_mfma_kernel<false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
     if (e != hipSuccess) return e;
-    gist_prefill_raw_kernel<<<(unsigned)W, 256, kPLds, s>>>(a);
+    gist_prefill_mfma_kernel<false><<<(unsigned)W, 256, kPLds, s>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_gist_prefill_gists(const GistPrefillLaunch& a, hipStream_t s) {
     hipError_t e = gist_check(a);
     if (e != hipSuccess) return e;
-    const long long W = (long long)a.B * a.Hkv * a.M;
+    const int G = a.Hq / a.Hkv;
+    const long long W = 2LL * a.B * a.Hkv * (a.Gp / kPBlk) * ((G + 3) / 4);
     if (W <= 0) return hipSuccess;
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    gist_prefill_gist_kernel<<<(unsigned)W, 256, 0, s>>>(a);
+    e = hipFuncSetAttribute((const void*)gist_prefill_mfma_kernel<true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
+    if (e != hipSuccess) return e;
+    gist_prefill_mfma_kernel<true><<<(unsigned)W, 256, kPLds, s>>>(a);
     return hipGetLastError();
 }
 
