@@ -78,7 +78,10 @@ __global__ void __launch_bounds__(256) prefill_bwd_inverse_kernel(PrefillBwdLaun
     if (threadIdx.x == 0) a.inv_n[row] = base;
 }
 
-__global__ void __launch_bounds__(256, 1) prefill_bwd_dq_kernel(PrefillBwdLaunch a) {
+// Two workgroups per CU (one would leave one wave per SIMD with nothing to hide its latency):
+// the register budget is then 256 per lane and about 37 values spill to scratch, which still
+// measures 16% faster than one workgroup per CU without spills.
+__global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch a) {
     extern __shared__ __align__(16) char lds[];
     const int G = a.Hq / a.Hkv;
     const int nb = a.T / kPBlk;
