@@ -278,10 +278,20 @@ def load_traffic(kernel_name, workload):
     return rec.get("bytes_per_launch")
 
 
+def prefill_cfg(args, configs):
+    """The prefill workload, with --tokens (T, a multiple of the block) and --k overrides."""
+    cfg = configs.PREFILL_CONFIGS[args.workload]
+    if args.tokens > 0:
+        cfg = cfg.with_(T=args.tokens)
+    if args.k >= 0:
+        cfg = cfg.with_(k=args.k)
+    return cfg
+
+
 def run_prefill(args, torch, configs, ops):
     from top_chunk_sparse_amd.synth import make_prefill
     import ctypes
-    cfg = configs.PREFILL_CONFIGS[args.workload]
+    cfg = prefill_cfg(args, configs)
     dev = torch.device("cuda:0")
     R = max(1, min(args.instances, 2))
     print(f"# generating {R} instance(s) of {cfg.name}", file=sys.stderr, flush=True)
@@ -345,7 +355,9 @@ def run_prefill(args, torch, configs, ops):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
+        "config": {"workload": cfg.name + ("" if args.tokens <= 0 and args.k < 0 else
+                                           f"@T={cfg.T},k={cfg.k}"),
+                   "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "T": cfg.T, "blk": cfg.blk, "k": cfg.k, "gate": "sas" if cfg.gate else "none",
                    "inputs": "bf16", "accumulation": "fp32", "instances_rotated": R},
         "calls_per_s": round(args.steps / wall, 2),
@@ -445,7 +457,7 @@ def run_gist_prefill(args, torch, configs, ops):
 def run_prefill_backward(args, torch, configs, ops):
     from top_chunk_sparse_amd.synth import make_prefill, make_prefill_grads
     import ctypes
-    cfg = configs.PREFILL_CONFIGS[args.workload]
+    cfg = prefill_cfg(args, configs)
     dev = torch.device("cuda:0")
     R = max(1, min(args.instances, 2))
     print(f"# generating {R} instance(s) of {cfg.name} (+ upstream gradients)", file=sys.stderr,
@@ -541,9 +553,9 @@ def main():
                     help="decode softmax set: every historical gist (default) or only the "
                          "selected chunks' gists")
     ap.add_argument("--tokens", type=int, default=0,
-                    help="decode: override the workload's context length N (tokens)")
+                    help="override the workload's context length (decode N, prefill T)")
     ap.add_argument("--k", type=int, default=-1,
-                    help="decode: override k (a value >= the chunk count selects every chunk)")
+                    help="override k (a value >= the chunk or block count selects all of them)")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="decode selection: 0 = top-k; in (0, 1] = top-p with a cap of k")
     ap.add_argument("--head-select", action="store_true",
