@@ -35,13 +35,22 @@ __global__ void __launch_bounds__(256) prefill_select_kernel(PrefillSelectLaunch
         z = block_sum(z, red);
         lse = mx + logf(z);
     }
-    const int ke = block_topk(
-        i, a.k, [&](int j) { return s[j]; },
-        [&](int x, int j) {
-            sel[x] = j;
-            if (gam) gam[x] = s[j] - lse;
-        },
-        sm);
+    int ke;
+    if (a.k >= i) {   // every earlier block is chosen: no ranking needed
+        for (int j = threadIdx.x; j < i; j += 256) {
+            sel[j] = j;
+            if (gam) gam[j] = s[j] - lse;
+        }
+        ke = i;
+    } else {
+        ke = block_topk(
+            i, a.k, [&](int j) { return s[j]; },
+            [&](int x, int j) {
+                sel[x] = j;
+                if (gam) gam[x] = s[j] - lse;
+            },
+            sm);
+    }
     for (int x = ke + threadIdx.x; x < a.k; x += 256) {
         sel[x] = -1;
         if (gam) gam[x] = 0.f;
