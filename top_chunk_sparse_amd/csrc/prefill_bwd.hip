@@ -78,9 +78,9 @@ __global__ void __launch_bounds__(256) prefill_bwd_inverse_kernel(PrefillBwdLaun
     if (threadIdx.x == 0) a.inv_n[row] = base;
 }
 
-// Two workgroups per CU (one would leave one wave per SIMD with nothing to hide its latency):
-// the register budget is then 256 per lane and about 37 values spill to scratch, which still
-// measures 16% faster than one workgroup per CU without spills.
+// Two workgroups per CU (one would leave one wave per SIMD with nothing to hide its latency),
+// so 256 registers per lane: the dO^T operand is re-read for every block from L1 / L2 rather
+// than held for the whole loop, which keeps the kernel free of spills.
 __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch a) {
     extern __shared__ __align__(16) char lds[];
     const int G = a.Hq / a.Hkv;
@@ -126,15 +126,12 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
 
     const size_t qrow = ((size_t)(b * a.Hq + kv * G + (active ? head : 0)) * a.T +
                          (size_t)i * kPBlk + 32 * rh + c32);
-    bf16x8 qf[8], gf[8];   // Q^T and dO^T operands of this lane's query row
+    bf16x8 qf[8];   // Q^T operand of this lane's query row (dO^T is re-read per block)
+    const uint16_t* gp = a.dout + qrow * kPD + 8 * h;
     {
         const uint16_t* qp = a.q + qrow * kPD + 8 * h;
-        const uint16_t* gp = a.dout + qrow * kPD + 8 * h;
 #pragma unroll
-        for (int kd = 0; kd < 8; ++kd) {
-            qf[kd] = *reinterpret_cast<const bf16x8*>(qp + 16 * kd);
-            gf[kd] = *reinterpret_cast<const bf16x8*>(gp + 16 * kd);
-        }
+        for (int kd = 0; kd < 8; ++kd) qf[kd] = *reinterpret_cast<const bf16x8*>(qp + 16 * kd);
     }
     const float lse2 = a.lse[qrow] * kLog2e;
     const float Dq = a.D[qrow];
@@ -169,6 +166,9 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
             const bool half = (t == 0) && rh == 0;   // diagonal, first row half: keys 0..31
             const char* kt = lds + buf * kPTile;
             const char* vt = lds + (2 + buf) * kPTile;
+            bf16x8 gf[8];   // dO^T operand (L1 / L2 resident across the blocks)
+#pragma unroll
+            for (int kd = 0; kd < 8; ++kd) gf[kd] = *reinterpret_cast<const bf16x8*>(gp + 16 * kd);
             f32x16 s[2], dp[2];
             s[0] = s[1] = dp[0] = dp[1] = f32x16{};
             if (half) {
