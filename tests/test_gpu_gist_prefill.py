@@ -82,3 +82,17 @@ def test_gist_prefill_deterministic():
     a()
     torch.cuda.synchronize()
     assert torch.equal(first[0], a.out) and torch.equal(first[1], a.lse)
+
+
+def test_gist_prefill_workspace_garbage():
+    """The gathered gist arrays (the padding rows included) are written before they are read: a
+    workspace full of 0xFF bytes gives the same bits as a fresh one."""
+    cfg = SMALL.with_(M=11, g=4)      # 44 gists: the gathered arrays end in 20 padding rows
+    inp = make_gist_prefill(cfg, 1210, device=DEV)
+    a = GistPrefillCall(inp)()
+    torch.cuda.synchronize()
+    out, lse = a.out.clone(), a.lse.clone()
+    a.ws.fill_(255)
+    a()
+    torch.cuda.synchronize()
+    assert torch.equal(out, a.out) and torch.equal(lse, a.lse)

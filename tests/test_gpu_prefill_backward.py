@@ -123,3 +123,20 @@ def test_prefill_backward_full_size_identities():
     torch.cuda.synchronize()
     for a, b in zip(first, (bwd.dq, bwd.dk, bwd.dv, bwd.dS)):
         assert torch.equal(a, b)
+
+
+def test_prefill_backward_workspace_garbage_and_reuse():
+    """The backward reads only workspace it wrote in the same call: a workspace full of 0xFF
+    bytes (NaN patterns), first used by a call of another shape, gives the same bits."""
+    big = BASE.with_(T=64 * 9, k=4, Hq=16)
+    inp, dout, dlse, fwd, bwd = run_bwd(BASE.with_(k=3), seed=940)
+    ref = [t.clone() for t in (bwd.dq, bwd.dk, bwd.dv, bwd.dS)]
+    inp2, dout2, dlse2, fwd2, bwd2 = run_bwd(big, seed=941)
+    ws = torch.full((max(bwd.ws.numel(), bwd2.ws.numel()),), 255, dtype=torch.uint8, device=DEV)
+    bwd2.ws = ws
+    bwd2()                      # another shape first, on the shared workspace
+    bwd.ws = ws
+    bwd()
+    torch.cuda.synchronize()
+    for a, b in zip(ref, (bwd.dq, bwd.dk, bwd.dv, bwd.dS)):
+        assert torch.equal(a, b)
