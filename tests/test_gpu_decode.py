@@ -68,6 +68,9 @@ VARIANTS = [
     SMALL.with_(levels=2, J=3, k2=0, k=4, n_plant=0),
     SMALL.with_(levels=2, J=4, k2=2, k=0, n_plant=4, plant_groups=2),
     SMALL.with_(levels=2, J=8, k2=64, k=10 ** 4, n_plant=4, plant_groups=2, Hq=16),
+    SMALL.with_(N=32, C=32, n_plant=0),            # exactly one full chunk: no history
+    SMALL.with_(N=64, C=32, gate=1, n_plant=1),    # one full historical chunk + a full current
+    SMALL.with_(levels=2, J=2, k2=1, k=1, N=3 * 32, n_plant=1, plant_groups=1),   # 2 chunks, 1 group
 ]
 
 
