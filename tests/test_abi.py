@@ -32,6 +32,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert ops.lib().tcs_abi_version() == 6
+    # the header's constant, which the build entry point checks the library against
+    with open(os.path.join(os.path.dirname(__file__), "..", "include", "tcsparse.h")) as f:
+        assert "#define TCS_ABI_VERSION 6\n" in f.read()
     for code in range(6):
         assert ops.status_str(code)
     assert ops.status_str(99) == "unknown status"
