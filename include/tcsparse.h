@@ -26,11 +26,12 @@
  *   the selected chunks only, each next to its chunk's raw tokens: the set section 3.3
  *   describes, in which an unselected chunk contributes nothing.  The scores and the selection
  *   (steps 1-4) are unchanged.
- *   top_p in (0, 1] (one level) replaces step 3: rank H as in step 3 and keep the shortest
- *   ranked prefix whose shares p[c] = exp(s[c] - log sum_{c' in H} exp(s[c'])) add up to at
- *   least top_p (top_p = 1 keeps every chunk), at most k of them, reported ascending.  The
- *   pages compare against top-p (SSA figure 2) without spelling the rule out; this is the
- *   reading used here.  The shares are summed in fp32 in rank order, so a selection may differ
+ *   top_p in (0, 1] replaces step 3: rank H as in step 3 and keep the shortest ranked prefix
+ *   whose shares p[c] = exp(s[c] - log sum_{c' in H} exp(s[c'])) add up to at least top_p
+ *   (top_p = 1 keeps every chunk), at most k of them, reported ascending.  At two levels H is
+ *   the candidate set (the chosen groups' member chunks, the only chunks scored) and the
+ *   groups are still the top k2.  The pages compare against top-p (SSA figure 2) without
+ *   spelling the rule out; this is the reading used here.  The shares are summed in fp32 in rank order, so a selection may differ
  *   from an exact evaluation when the running share crosses top_p within rounding.
  *   select_mode = TCS_SELECT_PER_HEAD (one level, no gate, top_p = 0) replaces steps 2-3 by
  *   per-head selection (appendix A: each head selects its chunks on its own and their union is
@@ -123,8 +124,8 @@
  *   no floating-point atomics; the same inputs give bitwise-identical outputs.
  *
  * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024;
- * B * Hkv <= 16384; TCS_GISTS_SELECTED: C + g <= 1024; top_p > 0: one level
- * and k <= 256; TCS_SELECT_PER_HEAD: one level, no gate, top_p = 0, M - 1 <= 65536; two levels:
+ * B * Hkv <= 16384; TCS_GISTS_SELECTED: C + g <= 1024; top_p > 0: k <= 256;
+ * TCS_SELECT_PER_HEAD: one level, no gate, top_p = 0, M - 1 <= 65536; two levels:
  * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk; gist
  * prefill d = 128, L a multiple of 64, 1 <= g <= 64 with 64 a multiple of g.
  * Other shapes return TCS_ERR_UNSUPPORTED.
@@ -170,7 +171,7 @@ typedef struct {
     int32_t num_pages;     /* pages in k_pages / v_pages                                  */
     int32_t gist_cap;      /* chunk capacity of gist_k/v per (b, kv); 0 means M-1          */
     float scale;           /* logit scale; 0 means 1/sqrt(d)                              */
-    float top_p;           /* 0: top-k.  In (0, 1]: top-p with a cap of k (one level)     */
+    float top_p;           /* 0: top-k.  In (0, 1]: top-p with a cap of k                 */
     int32_t select_mode;   /* TCS_SELECT_KV_HEAD or TCS_SELECT_PER_HEAD                   */
 } tcs_decode_params;
 

@@ -385,7 +385,7 @@ int or_decode(const or_decode_shape* p, const or_decode_io* io)
     if (p->Hkv <= 0 || p->Hq % p->Hkv || p->C <= 0 || p->g <= 0 || p->N < 1) return 2;
     if (p->levels == 2 && (p->J <= 0 || p->gate)) return 3;
     if (p->gists_in_softmax < 0 || p->gists_in_softmax > 2) return 4;
-    if (!(p->top_p >= 0.0 && p->top_p <= 1.0) || (p->top_p > 0.0 && p->levels != 1)) return 5;
+    if (!(p->top_p >= 0.0 && p->top_p <= 1.0)) return 5;
     if (p->head_select < 0 || p->head_select > 1 ||
         (p->head_select && (p->levels != 1 || p->gate || p->top_p > 0.0)))
         return 6;

@@ -36,7 +36,8 @@ typedef struct {
     int gist_cap;
     double scale;         /* <= 0: 1/sqrt(d)                                          */
     double top_p;         /* 0: top-k; in (0, 1]: shortest ranked prefix with softmax
-                             mass >= top_p, at most k chunks (one level)               */
+                             mass >= top_p, at most k chunks (at two levels: over the
+                             candidates, with the groups still the top k2)             */
     int head_select;      /* 0: one selection per KV head from the group-pooled score;
                              1: every query head picks its own top-k by its own score and
                                 the union is unfolded for the whole group (one level, no

@@ -103,7 +103,7 @@ def test_workspace_size_grows_with_work():
     (dict(top_p=-0.1), ops.TCS_ERR_SHAPE),
     (dict(top_p=1.5), ops.TCS_ERR_SHAPE),
     (dict(top_p=float("nan")), ops.TCS_ERR_SHAPE),
-    (dict(top_p=0.5, levels=2, J=4, k2=2), ops.TCS_ERR_UNSUPPORTED),
+    (dict(top_p=0.5, levels=2, J=4, k2=2, k=257), ops.TCS_ERR_UNSUPPORTED),
     (dict(top_p=0.5, k=257), ops.TCS_ERR_UNSUPPORTED),
     (dict(gist_mode=1, C_=1024, g=8, N=5000), ops.TCS_ERR_UNSUPPORTED),  # C + g > 1024
     (dict(select_mode=1, gate=1), ops.TCS_ERR_UNSUPPORTED),       # per-head selection: no gate

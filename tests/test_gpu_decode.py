@@ -162,7 +162,25 @@ def test_top_p_variants(cfg, tp):
     run_case(cfg, seed=400 + [c for c, _ in TOP_P].index(cfg), top_p=tp)
 
 
-@pytest.mark.parametrize("name,tp", [("llama32_1b_decode_32k", 0.9), ("llama31_8b_decode_128k", 0.5)])
+# top-p at two levels: the cut runs over the chosen groups' member chunks (their shares of the
+# softmax over the candidates' scores); the groups are still the top k2
+TOP_P_L2 = [
+    (SMALL.with_(levels=2, J=4, k2=3, k=10, n_plant=6, plant_groups=3), 0, 0.5),   # keeps 6
+    (SMALL.with_(levels=2, J=5, k2=100, k=30, n_plant=4, plant_groups=2, d=64), 0, 0.9),  # cap
+    (SMALL.with_(levels=2, J=4, k2=2, k=8, n_plant=4, plant_groups=2), 1, 0.7),    # keeps 6
+    (SMALL.with_(levels=2, J=7, k2=5, k=9, n_plant=6, plant_groups=3, g=8, Hq=16), 0, 1.0),
+    (SMALL.with_(levels=2, J=4, k2=3, k=10, n_plant=6, plant_groups=3), 1, 1e-6),  # keeps 1
+]
+
+
+@pytest.mark.parametrize("idx", range(len(TOP_P_L2)), ids=[f"tpl2_{i}" for i in range(len(TOP_P_L2))])
+def test_top_p_two_levels(idx):
+    cfg, gmode, tp = TOP_P_L2[idx]
+    run_case(cfg, seed=430 + idx, gist_mode=gmode, top_p=tp)
+
+
+@pytest.mark.parametrize("name,tp", [("llama32_1b_decode_32k", 0.9), ("llama31_8b_decode_128k", 0.5),
+                                     ("hssa_decode_512k", 0.5)])   # keeps 28-29 of 32
 def test_top_p_full(name, tp):
     cfg = configs.DECODE_CONFIGS[name]
     inp, call, st = run_case(cfg, configs.seed_for(name), top_p=tp)

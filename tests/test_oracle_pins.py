@@ -693,6 +693,58 @@ def pin_top_p_equal_scores_closed_form():
     assert r.sel[0, 0].tolist() == [0, 1, 2, 3]
 
 
+def pin_top_p_two_levels_all_groups_is_one_level():
+    """Two levels with every group chosen: the candidates are all historical chunks, so top-p
+    keeps what it keeps at one level (the two softmax sets differ by the level-2 gists only)."""
+    cfg = SMALL_L2.with_(k=12)
+    inp = make_decode(cfg, seed=21)
+    kept = set()
+    for tp in (0.2, 0.6, 0.97):
+        two = oracle_decode(inp, top_p=tp, k2=cfg.nG)
+        one = oracle_decode(inp, top_p=tp, levels=1)
+        assert np.array_equal(two.sel, one.sel), tp
+        kept.add(int((two.sel >= 0).sum()))
+    assert len(kept) > 1   # the cut, not only the cap, decides
+
+
+def pin_top_p_two_levels_one_is_top_k():
+    cfg = SMALL_L2.with_(k=6)
+    inp = make_decode(cfg, seed=22)
+    a, b = oracle_decode(inp), oracle_decode(inp, top_p=1.0)
+    assert np.array_equal(a.sel, b.sel) and np.array_equal(a.sel_groups, b.sel_groups)
+    assert np.abs(a.out - b.out).max() == 0.0
+
+
+def pin_top_p_two_levels_over_candidates():
+    """Two levels, two of ten groups chosen: the shares are those of the softmax over the
+    chosen groups' member chunks, the only chunks scored.  A tiny p keeps the best candidate;
+    p = 0.5 keeps the shortest ranked prefix of candidates reaching half their mass (numpy),
+    which differs from the prefix over all historical chunks' scores."""
+    cfg = SMALL_L2.with_(k=8)
+    inp = make_decode(cfg, seed=23)
+    r = oracle_decode(inp, top_p=0.5)
+    full = oracle_decode(inp, k=cfg.H, levels=1)   # every chunk's score, no groups
+    cand = [c for grp in r.sel_groups[0, 0] if grp >= 0
+            for c in range(grp * cfg.J, min((grp + 1) * cfg.J, cfg.H))]
+    sc = full.chunk_scores[0, 0]
+    assert np.array_equal(r.chunk_scores[0, 0][cand], sc[cand])
+    assert np.isinf(np.delete(r.chunk_scores[0, 0], cand)).all()
+
+    def prefix(ids, p):
+        order = sorted(ids, key=lambda c: (-sc[c], c))
+        sh = np.exp(sc[order] - np.logaddexp.reduce(sc[ids]))
+        n = int(np.argmax(np.cumsum(sh) >= p)) + 1
+        return sorted(order[:min(n, cfg.k)])
+
+    want = prefix(cand, 0.5)
+    got = [c for c in r.sel[0, 0].tolist() if c >= 0]
+    assert got == want and 1 < len(got) < cfg.k
+    assert prefix(list(range(cfg.H)), 0.5) != want
+    tiny = oracle_decode(inp, top_p=1e-12)
+    best = max(cand, key=lambda c: (sc[c], -c))
+    assert tiny.sel[0, 0].tolist() == [best] + [-1] * (cfg.k - 1)
+
+
 def pin_top_p_tiny_is_argmax():
     cfg = SMALL.with_(k=5)
     inp = make_decode(cfg, seed=20)

@@ -94,7 +94,7 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (p->g > 64 || p->C > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
     const bool sel_gists = p->gist_mode == TCS_GISTS_SELECTED;
     if (sel_gists && p->C + p->g > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
-    if (p->top_p > 0.f && (p->levels != 1 || p->k > kMaxTopPK)) return TCS_ERR_UNSUPPORTED;
+    if (p->top_p > 0.f && p->k > kMaxTopPK) return TCS_ERR_UNSUPPORTED;
     const bool heads = p->select_mode == TCS_SELECT_PER_HEAD;
     if (heads && (p->levels != 1 || p->gate_mode != TCS_GATE_NONE || p->top_p > 0.f ||
                   H > kMaxHeadSelectChunks))
@@ -389,9 +389,10 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
             if (e != hipSuccess) return TCS_ERR_HIP;
         }
 
-        // level 1: the member chunks of the chosen groups
+        // level 1: the member chunks of the chosen groups; top-p's shares are taken over them
         chunk_sel.gamma = nullptr;
-        chunk_sel.slice_lse = nullptr;
+        chunk_sel.slice_lse = p->top_p > 0.f ? (float*)(ws + pl.off_lse1) : nullptr;
+        chunk_sel.top_p = p->top_p;
         chunk_sel.counter = cnt;
         ga.gk = (const uint16_t*)gist_k;
         ga.gv = (const uint16_t*)gist_v;
