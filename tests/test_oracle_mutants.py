@@ -41,6 +41,9 @@ MUTANTS = [
     ("top_p_unranked", "    qsort(v, (size_t)n, sizeof(scored), by_rank);\n    const double lse = logsumexp(s, n);",
      "    const double lse = logsumexp(s, n);"),
     ("top_p_shares_of_first_half", "    const double lse = logsumexp(s, n);", "    const double lse = logsumexp(s, (n + 1) / 2);"),
+    # at two levels top-p silently falls back to the top-k chunk choice
+    ("top_p_one_level_only", "    } else if (p->top_p > 0.0) {\n        ke = top_p(",
+     "    } else if (p->top_p > 0.0 && p->levels == 1) {\n        ke = top_p("),
     ("selected_gists_first_only", "tk[n].k = gk + ((size_t)c * g + t) * d;",
      "tk[n].k = gk + ((size_t)c * g + 0) * d;"),
     ("selected_gists_gated", "                tk[n].v = gv + ((size_t)c * g + t) * d;\n                tk[n++].bias = 0.0;",
