@@ -170,6 +170,8 @@ TOP_P_L2 = [
     (SMALL.with_(levels=2, J=4, k2=2, k=8, n_plant=4, plant_groups=2), 1, 0.7),    # keeps 6
     (SMALL.with_(levels=2, J=7, k2=5, k=9, n_plant=6, plant_groups=3, g=8, Hq=16), 0, 1.0),
     (SMALL.with_(levels=2, J=4, k2=3, k=10, n_plant=6, plant_groups=3), 1, 1e-6),  # keeps 1
+    (SMALL.with_(levels=2, J=3, k2=0, k=4, n_plant=0), 0, 0.5),      # no group chosen
+    (SMALL.with_(levels=2, J=4, k2=2, k=0, n_plant=4, plant_groups=2), 0, 0.5),   # k = 0
 ]
 
 
