@@ -74,6 +74,28 @@ def test_gist_prefill_full_size_sampled():
     run(cfg, configs.seed_for(cfg.name), rows=sorted(set(rows)))
 
 
+# Two more shapes at full size (33,792 positions each): long chunks with many gists, and many
+# short chunks, whose gist prefix spans 16 gathered blocks.
+LARGE = [
+    GistPrefillConfig("gist_prefill_long_chunks", B=2, Hq=32, Hkv=8, d=128, M=64, L=512, g=16),
+    GistPrefillConfig("gist_prefill_many_chunks", B=1, Hq=32, Hkv=8, d=128, M=512, L=64, g=2),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(LARGE)), ids=[c.name for c in LARGE])
+def test_gist_prefill_large_shapes_sampled(idx):
+    cfg = LARGE[idx]
+    rng = np.random.default_rng(12 + idx)
+    rows = []
+    for bh in rng.choice(cfg.B * cfg.Hq, size=4, replace=False):
+        for c in (0, 1, cfg.M // 2, cfg.M - 1):
+            base = int(bh) * cfg.Tp + c * cfg.W
+            rows += [base, base + 63, base + cfg.L - 64, base + cfg.L - 1]   # raw rows
+            rows += [base + cfg.L, base + cfg.L + cfg.g - 1]                   # gist rows
+        rows += (int(bh) * cfg.Tp + rng.choice(cfg.Tp, size=30, replace=False)).tolist()
+    run(cfg, 6100 + idx, rows=sorted(set(rows)))
+
+
 def test_gist_prefill_deterministic():
     cfg = SMALL.with_(M=12)
     inp = make_gist_prefill(cfg, 1200, device=DEV)
