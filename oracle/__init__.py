@@ -35,7 +35,8 @@ class _DecodeShape(C.Structure):
                                        "gists_in_softmax", "levels", "J", "k2", "max_chunks",
                                        "num_pages", "gist_cap")] + [("scale", C.c_double),
                                                                     ("top_p", C.c_double),
-                                                                    ("head_select", C.c_int)]
+                                                                    ("head_select", C.c_int),
+                                                                    ("adaptive_k", C.c_int)]
 
 
 _P = C.c_void_p
@@ -86,6 +87,7 @@ def _open(path):
     h.or_prefill_backward.argtypes = [C.POINTER(_PrefillShape), C.POINTER(_PrefillBwdIO)]
     h.or_gist_prefill.argtypes = [C.POINTER(_GistPrefillShape), C.POINTER(_GistPrefillIO)]
     h.or_decode_token_count.argtypes = [C.POINTER(_DecodeShape), C.c_int, C.c_int, C.c_int]
+    h.or_adaptive_k.argtypes = [C.POINTER(_DecodeShape)]
     return h
 
 
@@ -145,10 +147,11 @@ def _gist_mode(x) -> int:
 def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_k, gist_v,
            gate=0, levels=1, J=0, k2=0, gist2_k=None, gist2_v=None, scale=0.0,
            gists_in_softmax=True, gist_cap=0, forced_sel=None, forced_groups=None,
-           units=None, weights_cap=0, top_p=0.0, head_select=0) -> DecodeResult:
+           units=None, weights_cap=0, top_p=0.0, head_select=0, adaptive_k=0) -> DecodeResult:
     """Decode attention for every (b, kv) (or the flat ids in ``units``).  head_select = 1:
     per-head selection with the union unfolded; sel then holds G * k entries per unit and
-    chunk_scores one row per query head."""
+    chunk_scores one row per query head.  adaptive_k = 1: each level selects
+    min(cap, adaptive_k_budget(...)) with caps k (chunks) and k2 (groups)."""
     M = -(-N // C_)
     H = M - 1
     nG = -(-H // J) if levels == 2 else 0
@@ -156,7 +159,8 @@ def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_
     sh = _DecodeShape(B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, C=C_, g=g, k=k, gate=gate,
                       gists_in_softmax=_gist_mode(gists_in_softmax), levels=levels, J=J, k2=k2,
                       max_chunks=page_table.shape[-1], num_pages=k_pages.shape[0],
-                      gist_cap=gist_cap, scale=scale, top_p=top_p, head_select=head_select)
+                      gist_cap=gist_cap, scale=scale, top_p=top_p, head_select=head_select,
+                      adaptive_k=adaptive_k)
     G = Hq // Hkv
     sk = G * k if head_select else k
     out = np.full((B, Hq, d), np.nan)
@@ -181,6 +185,13 @@ def decode(*, B, Hq, Hkv, d, N, C_, g, k, q, k_pages, v_pages, page_table, gist_
         raise ValueError(f"oracle decode rejected the arguments (code {rc})")
     return DecodeResult(out, lse, sel[..., :sk], None if selg is None else selg[..., :k2],
                         cs[..., :H], gs, w, nt)
+
+
+def adaptive_k_budget(*, N, C_, Hq, Hkv, levels=1, J=0) -> int:
+    """Per-level selection budget of adaptive top-k (SSA appendix A; the reading is stated
+    in oracle.c at or_adaptive_k)."""
+    sh = _DecodeShape(N=N, C=C_, Hq=Hq, Hkv=Hkv, levels=levels, J=J)
+    return int(lib().or_adaptive_k(C.byref(sh)))
 
 
 def token_count(*, N, C_, g, k_eff, levels=1, J=0, n_cand=0, k2_eff=0, gists_in_softmax=True) -> int:

@@ -188,6 +188,24 @@ int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand, int k
     return summaries + k_eff * p->C + cur;
 }
 
+/* Adaptive top-k ("SSA", appendix A "More Details on Adaptive Top-k").  The appendix builds
+ * one selection budget per routing level from the KV positions available n_kv, the effective
+ * compression L_eff (the chunk size L at one level, L * J at two levels), the group size G and
+ * L, divides by G because each head selects before the union is unfolded into the shared KV,
+ * adds 1 so that at least one chunk is selected, and uses the same budget at both levels.  It
+ * does not print the formula.  Reading used here: the compressed cache holds n_kv / L_eff
+ * summary positions; the raw tokens unfolded by the G heads together (G * k chunks of L
+ * tokens) are to match that count, so k = floor(n_kv / (L_eff * G * L)) + 1, with n_kv = N,
+ * the tokens in the cache.  Unfolded tokens then stay proportional to n_kv at every
+ * compression ratio.  PARITY UNPINNED against the paper's own (unprinted) formula: only the
+ * properties the appendix states are pinned. */
+int or_adaptive_k(const or_decode_shape* p)
+{
+    const long long G = p->Hq / p->Hkv;
+    const long long l_eff = p->levels == 2 ? (long long)p->C * p->J : (long long)p->C;
+    return (int)((long long)p->N / (l_eff * G * p->C)) + 1;
+}
+
 /* Decode for one unit (b, kv). */
 static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, int kv)
 {
@@ -201,6 +219,13 @@ static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, 
     const uint16_t* gv = io->gist_v + ((size_t)b * p->Hkv + kv) * (size_t)gcap * g * d;
     const int32_t* pt = io->page_table + (size_t)b * p->max_chunks;
     const size_t unit = (size_t)b * p->Hkv + kv;
+    /* chunks (k1) and groups (k2) to select; sel and sel_groups keep the strides k and k2 */
+    int k1 = p->k, k2 = p->k2;
+    if (p->adaptive_k) {
+        const int ka = or_adaptive_k(p);
+        if (ka < k1) k1 = ka;
+        if (ka < k2) k2 = ka;
+    }
 
     /* Candidate chunks: every historical chunk, or at two levels the members of the
      * selected level-2 groups. */
@@ -228,7 +253,7 @@ static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, 
                 if (r >= 0) groups[k2e++] = r;
             }
         } else {
-            k2e = top_k(s2, ids, nG, p->k2, groups);
+            k2e = top_k(s2, ids, nG, k2, groups);
         }
         if (io->sel_groups)
             for (int i = 0; i < p->k2; ++i)
@@ -273,7 +298,7 @@ static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, 
                 if (io->chunk_scores)
                     io->chunk_scores[(unit * G + h) * (size_t)H + cand[i]] = sh[i];
             }
-            const int kh = top_k(sh, cand, n_cand, p->k, pick);
+            const int kh = top_k(sh, cand, n_cand, k1, pick);
             for (int j = 0; j < kh; ++j) in_union[pick[j]] = 1;
         }
         for (int c = 0; c < H; ++c)
@@ -282,9 +307,9 @@ static int decode_unit(const or_decode_shape* p, const or_decode_io* io, int b, 
         free(sh);
         free(in_union);
     } else if (p->top_p > 0.0) {
-        ke = top_p(s, cand, n_cand, p->top_p, p->k, sel);
+        ke = top_p(s, cand, n_cand, p->top_p, k1, sel);
     } else {
-        ke = top_k(s, cand, n_cand, p->k, sel);
+        ke = top_k(s, cand, n_cand, k1, sel);
     }
     if (io->sel)
         for (int i = 0; i < sk; ++i) io->sel[unit * sk + i] = i < ke ? sel[i] : -1;
@@ -389,6 +414,7 @@ int or_decode(const or_decode_shape* p, const or_decode_io* io)
     if (p->head_select < 0 || p->head_select > 1 ||
         (p->head_select && (p->levels != 1 || p->gate || p->top_p > 0.0)))
         return 6;
+    if (p->adaptive_k < 0 || p->adaptive_k > 1 || (p->adaptive_k && p->top_p > 0.0)) return 7;
     const int total = p->B * p->Hkv;
     const int n = io->units ? io->n_units : total;
     int rc = 0;

@@ -42,6 +42,9 @@ typedef struct {
                              1: every query head picks its own top-k by its own score and
                                 the union is unfolded for the whole group (one level, no
                                 gate, no top-p)                                          */
+    int adaptive_k;       /* 0: select k chunks (k2 groups).  1: adaptive top-k (SSA
+                             appendix A): every level selects min(cap, or_adaptive_k(p))
+                             with cap = k for chunks and k2 for groups; no top-p           */
 } or_decode_shape;
 
 typedef struct {
@@ -121,6 +124,7 @@ int or_decode(const or_decode_shape* p, const or_decode_io* io);
 int or_prefill(const or_prefill_shape* p, const or_prefill_io* io);
 int or_prefill_backward(const or_prefill_shape* p, const or_prefill_bwd_io* io);
 int or_decode_token_count(const or_decode_shape* p, int k_eff, int n_cand, int k2_eff);
+int or_adaptive_k(const or_decode_shape* p);
 int or_threads(void);
 
 #endif

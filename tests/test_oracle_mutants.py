@@ -70,6 +70,14 @@ MUTANTS = [
     ("gist_prefill_no_earlier_gists", "if (cx == cp || is_gist) {", "if (cx == cp) {"),
     ("gist_prefill_first_gist_as_raw", "const int is_gist = (x % W) >= p->L;",
      "const int is_gist = (x % W) > p->L;"),
+    ("adaptive_k_no_plus_one", "return (int)((long long)p->N / (l_eff * G * p->C)) + 1;",
+     "return (int)((long long)p->N / (l_eff * G * p->C));"),
+    ("adaptive_k_not_divided_by_group", "return (int)((long long)p->N / (l_eff * G * p->C)) + 1;",
+     "return (int)((long long)p->N / (l_eff * p->C)) + 1;"),
+    ("adaptive_k_two_levels_compress_like_one",
+     "p->levels == 2 ? (long long)p->C * p->J : (long long)p->C;", "(long long)p->C;"),
+    ("adaptive_k_groups_not_adapted", "        if (ka < k2) k2 = ka;\n", ""),
+    ("adaptive_k_ignored", "        if (ka < k1) k1 = ka;\n", ""),
 ]
 
 

@@ -758,6 +758,76 @@ def pin_top_p_tiny_is_argmax():
 
 
 # ----------------------------------------------------------------------------------------
+# adaptive top-k (SSA appendix A).  The appendix names the budget's ingredients and its
+# properties but prints no formula and no values, so only those properties are pinned here:
+# at least one chunk; grows with the KV positions n_kv; divided among the G heads whose picks
+# are unioned; unfolded raw tokens proportional to n_kv with the effective compression L_eff
+# = L (one level) or L J (two levels); the same budget at both levels.
+# ----------------------------------------------------------------------------------------
+def _budget(N, C_, G, levels=1, J=0):
+    return oracle.adaptive_k_budget(N=N, C_=C_, Hq=8 * G, Hkv=8, levels=levels, J=J)
+
+
+def pin_adaptive_k_stated_properties():
+    for C_ in (8, 64, 128):
+        for levels, J in ((1, 0), (2, 4), (2, 16)):
+            l_eff = C_ * (J if levels == 2 else 1)
+            for G in (1, 2, 4, 8):
+                prev = 0
+                for N in sorted({1, 2, C_, C_ + 1, l_eff * G * C_ - 1, l_eff * G * C_,
+                                 3 * l_eff * G * C_ + 7, 131072, 524288, 1 << 21}):
+                    b = _budget(N, C_, G, levels, J)
+                    assert b >= 1, (C_, levels, J, G, N)            # at least one chunk
+                    assert b >= prev, (C_, levels, J, G, N)         # grows with n_kv
+                    prev = b
+                    # the G heads' picks together unfold G k chunks of L tokens: within one
+                    # chunk per head of the n_kv / L_eff positions of the compressed cache
+                    assert G * (b - 1) * C_ <= N / l_eff < G * b * C_, (C_, levels, J, G, N)
+                    # dividing by G: the group's budget, G times its per-head share, stays within
+                    # G - 1 chunks of the budget one head alone would get
+                    one = _budget(N, C_, 1, levels, J)
+                    assert G * (b - 1) <= one - 1 < G * b, (C_, levels, J, G, N)
+    # proportional to n_kv: doubling a large cache doubles the unfolded tokens (to one chunk)
+    for levels, J in ((1, 0), (2, 16)):
+        a, b2 = _budget(1 << 20, 64, 4, levels, J), _budget(1 << 21, 64, 4, levels, J)
+        assert abs((b2 - 1) - 2 * (a - 1)) <= 1
+
+
+def pin_adaptive_k_reduces_to_fixed_k():
+    """With the budget b, adaptive decode selects exactly what fixed k = min(cap, b) (and
+    k2 = min(k2 cap, b) at two levels) selects, bit for bit, and the same budget serves both
+    levels."""
+    one = SMALL.with_(gate=1, k=6)                       # b = 173 // (8 * 2 * 8) + 1 = 2
+    two = SMALL_L2.with_(N=130 * 8 + 3, k=6, k2=5)       # b = 1043 // (32 * 4 * 8) + 1 = 2
+    cases = ((one, {}), (one.with_(k=1), {}), (SMALL.with_(k=5, gate=0), {"head_select": 1}),
+             (two, {}), (two.with_(k2=1), {}))
+    for cfg, kw in cases:
+        inp = make_decode(cfg, seed=41)
+        b = _budget(cfg.N, cfg.C, cfg.G, cfg.levels, cfg.J)
+        assert b == 2, cfg.name
+        r = oracle_decode(inp, adaptive_k=1, **kw)
+        k1 = min(cfg.k, b)
+        lv = {"k2": min(cfg.k2, b)} if cfg.levels == 2 else {}
+        ref = oracle_decode(inp, k=k1, **lv, **kw)
+        G = cfg.G if kw.get("head_select") else 1
+        assert r.sel.shape[-1] == G * cfg.k      # the caller's stride is kept
+        pad = np.full(r.sel.shape, -1, np.int32)
+        pad[..., : G * k1] = ref.sel
+        assert np.array_equal(r.sel, pad), cfg.name
+        assert np.array_equal(r.out, ref.out) and np.array_equal(r.lse, ref.lse), cfg.name
+        if cfg.levels == 2:
+            gpad = np.full(r.sel_groups.shape, -1, np.int32)
+            gpad[..., : lv["k2"]] = ref.sel_groups
+            assert np.array_equal(r.sel_groups, gpad), cfg.name
+            k2e = min(cfg.k2, b, cfg.nG)
+            assert ((r.sel_groups >= 0).sum(-1) == k2e).all()
+            if cfg.k2 >= b and cfg.k >= b:       # the same budget at both levels
+                assert ((r.sel >= 0).sum(-1) == b).all() and k2e == b
+        elif not kw:
+            assert ((r.sel >= 0).sum(-1) == min(cfg.k, b, cfg.H)).all()
+
+
+# ----------------------------------------------------------------------------------------
 # prefill backward
 # ----------------------------------------------------------------------------------------
 PFB = PrefillConfig("pin_prefill_bwd", B=1, Hq=4, Hkv=2, d=16, T=8 * 6, blk=8, k=2, gate=1)
