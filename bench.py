@@ -111,6 +111,75 @@ def prefill_bytes(cfg):
             + cfg.B * cfg.Hkv * nb * cfg.k * 4)
 
 
+LOOPS = 5            # timed loops of exactly --steps calls; the median is reported
+SUSTAIN_MS = 200.0   # the sustained figure repeats the loop until at least this long
+
+
+def timed_loops(torch, stream, step, steps, loops=LOOPS):
+    """``loops`` timed loops of exactly ``steps`` calls, each bracketed by a device
+    synchronisation on both sides.  Returns [(wall_ms, event_ms)] per loop; step(i) enqueues
+    call i."""
+    out = []
+    for _ in range(loops):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(((time.perf_counter() - t0) * 1e3, e0.elapsed_time(e1)))
+    return out
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def timing_summary(torch, stream, step, steps):
+    """The reported timing: the median over LOOPS loops of exactly ``steps`` calls (host wall
+    clock between synchronisations), the event-timed median beside it, and a sustained figure
+    from one loop of at least SUSTAIN_MS (whole multiples of ``steps`` calls)."""
+    loops = timed_loops(torch, stream, step, steps)
+    wall = median([w for w, _ in loops])
+    ev = median([e for _, e in loops])
+    reps = max(1, int(SUSTAIN_MS / max(wall, 1e-3)) + 1)
+    (sw, se), = timed_loops(torch, stream, step, steps * reps, loops=1)
+    return {"ms_per_step": wall / steps, "event_ms_per_step": ev / steps,
+            "loops_ms": [round(w, 4) for w, _ in loops],
+            "sustained": {"steps": steps * reps, "ms_per_step": round(sw / (steps * reps), 5),
+                          "event_ms_per_step": round(se / (steps * reps), 5)}}
+
+
+def stream_read_ceiling(torch, ops, dev, gib=2, reps=5):
+    """HBM read ceiling on this machine: the library's plain streaming-read kernel over ``gib`` GiB
+    (8x the 256 MB last-level cache), median of ``reps`` timed passes, in GB/s."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(ops.STREAM_READ_BLOCKS, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ops.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ops.stream_read(buf, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res.append(buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    g = median(res)
+    return {"GBps": round(g, 1), "frac_of_peak": round(g / HBM_PEAK_GBPS, 4),
+            "bytes": gib << 30, "passes": reps, "kernel": "stream_read_kernel"}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -303,17 +372,8 @@ def run_prefill(args, torch, configs, ops):
         calls[i % R]()
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        calls[i % R]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    tm = timing_summary(torch, stream, lambda i: calls[i % R](), args.steps)
+    ms_per_step = tm["ms_per_step"]
     # per-kernel durations: back-to-back calls with events between the two kernels
     evs = []
     for _ in range(args.steps):
@@ -360,11 +420,14 @@ def run_prefill(args, torch, configs, ops):
                    "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "T": cfg.T, "blk": cfg.blk, "k": cfg.k, "gate": "sas" if cfg.gate else "none",
                    "inputs": "bf16", "accumulation": "fp32", "instances_rotated": R},
-        "calls_per_s": round(args.steps / wall, 2),
+        "calls_per_s": round(1e3 / ms_per_step, 2),
+        "timing": f"median of {LOOPS} loops of {args.steps} calls, {R} instances rotated",
+        "loops_ms": tm["loops_ms"],
+        "sustained": tm["sustained"],
         "algorithmic_flops_per_call": flops,
         "attended_pairs_per_call": prefill_pairs(cfg),
         "algorithmic_bytes_per_call": prefill_bytes(cfg),
-        "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 5),
+        "event_ms_per_step": round(tm["event_ms_per_step"], 5),
         "stage_ms": [round(x, 5) for x in stage_ms],
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -387,17 +450,8 @@ def run_gist_prefill(args, torch, configs, ops):
         calls[i % R]()
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        calls[i % R]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    tm = timing_summary(torch, stream, lambda i: calls[i % R](), args.steps)
+    ms_per_step = tm["ms_per_step"]
     nst = 3   # gist gather, raw query rows, gist query rows
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
            for _ in range(args.steps)]
@@ -442,11 +496,14 @@ def run_gist_prefill(args, torch, configs, ops):
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "M": cfg.M, "L": cfg.L, "g": cfg.g, "positions": cfg.Tp, "inputs": "bf16",
                    "accumulation": "fp32", "instances_rotated": R},
-        "calls_per_s": round(args.steps / wall, 2),
+        "calls_per_s": round(1e3 / ms_per_step, 2),
+        "timing": f"median of {LOOPS} loops of {args.steps} calls, {R} instances rotated",
+        "loops_ms": tm["loops_ms"],
+        "sustained": tm["sustained"],
         "algorithmic_flops_per_call": flops,
         "attended_pairs_per_call": raw_pairs + gist_pairs,
         "dense_causal_pairs_per_call": cfg.B * cfg.Hq * cfg.Tp * (cfg.Tp + 1) // 2,
-        "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 5),
+        "event_ms_per_step": round(tm["event_ms_per_step"], 5),
         "stage_ms": [round(x, 5) for x in stage_ms],
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -472,17 +529,8 @@ def run_prefill_backward(args, torch, configs, ops):
         calls[i % R]()
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        calls[i % R]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    tm = timing_summary(torch, stream, lambda i: calls[i % R](), args.steps)
+    ms_per_step = tm["ms_per_step"]
     # per-kernel durations: events between the stages (select, prep, dq, dk / dv, dS)
     nst = 5
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
@@ -531,10 +579,13 @@ def run_prefill_backward(args, torch, configs, ops):
                    "d": cfg.d, "T": cfg.T, "blk": cfg.blk, "k": cfg.k,
                    "gate": "sas" if cfg.gate else "none", "inputs": "bf16",
                    "accumulation": "fp32", "instances_rotated": R},
-        "calls_per_s": round(args.steps / wall, 2),
+        "calls_per_s": round(1e3 / ms_per_step, 2),
+        "timing": f"median of {LOOPS} loops of {args.steps} calls, {R} instances rotated",
+        "loops_ms": tm["loops_ms"],
+        "sustained": tm["sustained"],
         "algorithmic_flops_per_call": flops,
         "attended_pairs_per_call": prefill_pairs(cfg),
-        "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 5),
+        "event_ms_per_step": round(tm["event_ms_per_step"], 5),
         "stage_ms": [round(x, 5) for x in stage_ms],
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -561,6 +612,8 @@ def main():
     ap.add_argument("--head-select", action="store_true",
                     help="decode selection: every query head picks its own top-k and the union "
                          "is unfolded (one level; runs the workload with the gate off)")
+    ap.add_argument("--adaptive-k", action="store_true",
+                    help="decode selection: adaptive top-k, one budget per level (k, k2 caps)")
     ap.add_argument("--backward", action="store_true",
                     help="prefill workloads: time the gradients (dq, dk, dv, dS) instead of "
                          "the forward")
@@ -607,7 +660,7 @@ def main():
     insts = [make_decode(cfg, configs.seed_for(cfg.name, r), device=dev) for r in range(R)]
     gmode = ops.GISTS_SELECTED if args.gist_mode == "selected" else ops.GISTS_ALL
     calls = [ops.DecodeCall(inp, with_scores=False, gist_mode=gmode, top_p=args.top_p,
-                            head_select=int(args.head_select))
+                            head_select=int(args.head_select), adaptive_k=int(args.adaptive_k))
              for inp in insts]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
@@ -617,20 +670,12 @@ def main():
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
 
-    # ---- timed region: K whole calls --------------------------------------------------
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        calls[i % R]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = e0.elapsed_time(e1)
-    ms_per_step = wall * 1e3 / args.steps
-    value = args.steps / wall
+    # ---- timed region: LOOPS loops of exactly K calls, rotating over the R instances ----
+    tm = timing_summary(torch, stream, lambda i: calls[i % R](), args.steps)
+    ms_per_step = tm["ms_per_step"]
+    value = 1e3 / ms_per_step
+    # warm: the same loops on instance 0 alone (its data partly held by the 256 MB cache)
+    warm = timing_summary(torch, stream, lambda i: calls[0](), args.steps)
 
     # ---- per-kernel durations: the same K calls with events between the kernels ------
     nst = ops.decode_stage_count(calls[0].p)
@@ -651,7 +696,7 @@ def main():
     print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
 
     k_eff_mean = None
-    if args.top_p > 0 or args.head_select:   # chunks each unit kept, from the calls' own selections
+    if args.top_p > 0 or args.head_select or args.adaptive_k:   # chunks each unit kept
         import numpy as np
         k_eff_mean = float(np.mean([(c.sel >= 0).sum(-1).float().mean().item() for c in calls]))
     total_bytes, parts = decode_bytes(cfg, gist_mode=args.gist_mode, k_eff_mean=k_eff_mean)
@@ -667,12 +712,14 @@ def main():
                 "traffic": load_traffic("gist_kernel", cfg.name) if args.gist_mode == "all" else None,
                 "algorithmic_bytes": gk_bytes, "avg_ms": round(gk_ms, 5)}
 
+    ceiling = stream_read_ceiling(torch, ops, dev)
     cpu = None
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         cpu = cpu_baseline(insts[0], args.cpu_seconds,
                            gists_in_softmax="selected" if args.gist_mode == "selected" else True,
-                           top_p=args.top_p, head_select=int(args.head_select))
+                           top_p=args.top_p, head_select=int(args.head_select),
+                           adaptive_k=int(args.adaptive_k))
 
     rec = {
         "metric": METRIC,
@@ -685,7 +732,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name + ("" if args.tokens <= 0 and args.k < 0 else
                                            f"@N={cfg.N},k={cfg.k}"),
@@ -694,13 +741,23 @@ def main():
                    "none", "levels": cfg.levels, "paged": cfg.paged, "gists": args.gist_mode,
                    "top_p": args.top_p or None,
                    "select": "per-head union" if args.head_select else "per KV head",
-                   "inputs": "bf16",
+                   "k_mode": "adaptive" if args.adaptive_k else "fixed",
+                   "inputs": "bf16", "accumulation": "fp32",
                    "instances_rotated": R},
+        "timing": f"median of {LOOPS} loops of {args.steps} calls, cold: {R} instances rotated "
+                  f"({R * total_bytes / 2 ** 30:.2f} GiB of algorithmic bytes per rotation)",
         "effective_GBps": round(eff_gbps, 1),
         "chunks_selected_mean": k_eff_mean,
         "pct_of_hbm_peak": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
+        "pct_of_stream_read_ceiling": round(100 * eff_gbps / ceiling["GBps"], 2),
+        "stream_read_ceiling": ceiling,
         "algorithmic_bytes_per_call": total_bytes,
-        "event_ms_per_step": round(ev_ms / args.steps, 5),
+        "event_ms_per_step": round(tm["event_ms_per_step"], 5),
+        "loops_ms": tm["loops_ms"],
+        "sustained": tm["sustained"],
+        "warm": {"label": "warm: instance 0 only, partly cache-resident",
+                 "calls_per_s": round(1e3 / warm["ms_per_step"], 2),
+                 "ms_per_step": round(warm["ms_per_step"], 5)},
         "stage_ms": [round(x, 5) for x in stage_ms],
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -40,6 +40,17 @@
  *   head of the group attends, in step 5, to the raw tokens of the union U of the G heads'
  *   choices (k_eff <= |U| <= min(G k, |H|)).  sel then holds U ascending with G * k entries per
  *   (b, kv) (-1 padded), and chunk_scores holds s_h, one row per query head.
+ *   k_mode = TCS_K_ADAPTIVE (adaptive top-k, appendix A "More Details on Adaptive Top-k")
+ *   replaces the fixed counts by one budget per routing level,
+ *     k_a = floor(N / (L_eff * G * C)) + 1,   L_eff = C (one level) or C * J (two levels),
+ *   so that the raw tokens the G heads' choices unfold together (G k_a chunks of C tokens)
+ *   match the N / L_eff summary positions of the compressed cache, and at least one chunk is
+ *   kept.  Step 3 then selects min(k, k_a) chunks, and at two levels min(k2, k_a) groups: the
+ *   same budget at both levels.  k and k2 stay the strides of sel and sel_groups (entries
+ *   past the selection are -1).  The appendix names the budget's ingredients (the KV
+ *   positions, the effective compression, the group size and the chunk size, the division by
+ *   G for the union of the heads' choices, the +1, the same k at both levels) but not the
+ *   formula; the one above is the reading used here.  Not with top_p > 0.
  *   Two levels (levels = 2; section 3.5 and appendix B.2): level-2 gists summarise groups of J
  *   consecutive historical chunks.  The group scores s2[r] (step 2 over gist2_k) pick the top
  *   k2 groups; the member chunks of the chosen groups are the candidates; steps 1-3 run over
@@ -125,7 +136,8 @@
  *
  * Supported shapes: d in {64, 128}; G = Hq / Hkv in {1, 2, 4, 8}; g <= 64; C <= 1024;
  * B * Hkv <= 16384; TCS_GISTS_SELECTED: C + g <= 1024; top_p > 0: k <= 256;
- * TCS_SELECT_PER_HEAD: one level, no gate, top_p = 0, M - 1 <= 65536; two levels:
+ * TCS_SELECT_PER_HEAD: one level, no gate, top_p = 0, M - 1 <= 65536; TCS_K_ADAPTIVE:
+ * top_p = 0; two levels:
  * J * g <= 1024 and min(k2, nG) <= 64; prefill d = 128, blk = 64 and T a multiple of blk; gist
  * prefill d = 128, L a multiple of 64, 1 <= g <= 64 with 64 a multiple of g.
  * Other shapes return TCS_ERR_UNSUPPORTED.
@@ -140,7 +152,7 @@
 extern "C" {
 #endif
 
-#define TCS_ABI_VERSION 6
+#define TCS_ABI_VERSION 7
 
 typedef enum {
     TCS_OK = 0,
@@ -154,6 +166,7 @@ typedef enum {
 enum { TCS_GATE_NONE = 0, TCS_GATE_SAS = 1 };
 enum { TCS_GISTS_ALL = 0, TCS_GISTS_SELECTED = 1 };   /* which gists enter the softmax */
 enum { TCS_SELECT_KV_HEAD = 0, TCS_SELECT_PER_HEAD = 1 };   /* who selects the chunks      */
+enum { TCS_K_FIXED = 0, TCS_K_ADAPTIVE = 1 };   /* how many chunks (groups) are selected  */
 
 typedef struct {
     int32_t struct_size;   /* = sizeof(tcs_decode_params) */
@@ -173,6 +186,7 @@ typedef struct {
     float scale;           /* logit scale; 0 means 1/sqrt(d)                              */
     float top_p;           /* 0: top-k.  In (0, 1]: top-p with a cap of k                 */
     int32_t select_mode;   /* TCS_SELECT_KV_HEAD or TCS_SELECT_PER_HEAD                   */
+    int32_t k_mode;        /* TCS_K_FIXED, or TCS_K_ADAPTIVE: k and k2 become caps         */
 } tcs_decode_params;
 
 /* Host-only: bytes of workspace sparse_attn_decode needs for these parameters. */
@@ -293,6 +307,14 @@ tcs_status sparse_attn_gist_prefill_timed(const tcs_gist_prefill_params* p,
                                           float* out, float* lse, void* workspace,
                                           size_t workspace_bytes, void* stream,
                                           void* const* events, int n_events);
+
+/* Measurement aid, not part of the method: a plain streaming read of `bytes` bytes at `src`
+ * (16-byte aligned, a multiple of 16) by one kernel on `stream`, each byte loaded once, the
+ * HBM read ceiling the decode kernels' bandwidth is compared with.  `sink` (device memory of
+ * TCS_STREAM_READ_BLOCKS 32-bit words) receives one word per workgroup so the loads cannot be
+ * elided.  TCS_ERR_NULL for a null pointer, TCS_ERR_SHAPE for misalignment. */
+#define TCS_STREAM_READ_BLOCKS 2048
+tcs_status tcs_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 /* Static string naming a status code. */
 const char* tcs_status_str(tcs_status s);

@@ -99,16 +99,22 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
     gmode = "selected" if getattr(call, "gist_mode", 0) == 1 else True
     top_p = float(call.p.top_p)
     heads = int(getattr(call, "head_select", 0))
+    adaptive = int(getattr(call, "adaptive_k", 0))
     if ref is None:
         ref = oracle_decode(inp, k=call.p.k, units=units, scale=float(call.p.scale),
-                            gists_in_softmax=gmode, top_p=top_p, head_select=heads)
+                            gists_in_softmax=gmode, top_p=top_p, head_select=heads,
+                            adaptive_k=adaptive)
     all_units = list(range(c.B * c.Hkv)) if units is None else list(units)
     gsel = call.sel.cpu().numpy()
     gout = call.out.cpu().double().numpy()
     glse = call.lse.cpu().double().numpy()
     ggrp = call.sel_groups.cpu().numpy() if call.sel_groups is not None else None
     excused = []
-    k = call.p.k
+    k, k2 = call.p.k, c.k2
+    if adaptive:   # the boundary sits at the selected count, min(cap, budget), at each level
+        budget = oracle.adaptive_k_budget(N=c.N, C_=c.C, Hq=c.Hq, Hkv=c.Hkv, levels=c.levels,
+                                          J=c.J)
+        k, k2 = min(k, budget), min(k2, budget)
     for u in all_units:
         b, kv = divmod(u, c.Hkv)
         ok = np.array_equal(gsel[b, kv], ref.sel[b, kv])
@@ -118,7 +124,7 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
             continue
         gaps = []
         if c.levels == 2:
-            gaps.append(boundary_gap(ref.group_scores[b, kv], c.k2))
+            gaps.append(boundary_gap(ref.group_scores[b, kv], k2))
         if heads:   # every head's own boundary decides its part of the union
             gaps += [boundary_gap(ref.chunk_scores[b, kv * G + h], k) for h in range(G)]
         elif top_p > 0:
@@ -134,7 +140,7 @@ def check_decode(inp: DecodeInputs, call, ref=None, units=None, tol=OUT_TOL, rep
     if excused:
         forced = np.ascontiguousarray(gsel.astype(np.int32))
         fg = np.ascontiguousarray(ggrp.astype(np.int32)) if ggrp is not None else None
-        ref2 = oracle_decode(inp, k=k, units=excused, forced_sel=forced, forced_groups=fg,
+        ref2 = oracle_decode(inp, k=call.p.k, units=excused, forced_sel=forced, forced_groups=fg,
                              scale=float(call.p.scale), gists_in_softmax=gmode,
                              head_select=heads)
         for u in excused:

@@ -31,10 +31,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ops.lib().tcs_abi_version() == 6
+    assert ops.lib().tcs_abi_version() == 7
     # the header's constant, which the build entry point checks the library against
     with open(os.path.join(os.path.dirname(__file__), "..", "include", "tcsparse.h")) as f:
-        assert "#define TCS_ABI_VERSION 6\n" in f.read()
+        assert "#define TCS_ABI_VERSION 7\n" in f.read()
     for code in range(6):
         assert ops.status_str(code)
     assert ops.status_str(99) == "unknown status"
@@ -69,6 +69,14 @@ def test_per_head_selection_workspace():
     b = ops.decode_workspace_size(P(N=64 * 500, select_mode=1))
     assert 0 < a < b
     assert ops.decode_workspace_size(P(select_mode=1, C_=16, g=1, N=16 * 65536 + 1)) > 0
+
+
+def test_adaptive_k_keeps_the_caller_strides():
+    # the budget only lowers the selected count: sel / sel_groups / gamma keep k and k2
+    for kw in (dict(N=64 * 500, k=40, gate=1), dict(N=64 * 500, levels=2, J=8, k2=9, k=40)):
+        a = ops.decode_workspace_size(P(**kw))
+        b = ops.decode_workspace_size(P(k_mode=1, **kw))
+        assert 0 < b <= a
 
 
 def test_workspace_size_grows_with_work():
@@ -111,6 +119,9 @@ def test_workspace_size_grows_with_work():
     (dict(select_mode=1, levels=2, J=4, k2=2), ops.TCS_ERR_UNSUPPORTED),   # ... one level
     (dict(select_mode=1, C_=16, g=1, N=16 * 65537 + 1), ops.TCS_ERR_UNSUPPORTED),   # H > 65536
     (dict(select_mode=2), ops.TCS_ERR_SHAPE),
+    (dict(k_mode=2), ops.TCS_ERR_SHAPE),
+    (dict(k_mode=-1), ops.TCS_ERR_SHAPE),
+    (dict(k_mode=1, top_p=0.5), ops.TCS_ERR_UNSUPPORTED),     # adaptive k: no top-p
 ])
 def test_decode_rejects_bad_params(kw, code):
     p = P(**kw)

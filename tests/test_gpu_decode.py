@@ -24,12 +24,14 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_case(cfg, seed, units=None, gist_mode=0, top_p=0.0, head_select=0, **kw):
+def run_case(cfg, seed, units=None, gist_mode=0, top_p=0.0, head_select=0, adaptive_k=0, **kw):
     say(f"[decode] {cfg.name} seed={seed} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} "
         f"N={cfg.N} C={cfg.C} g={cfg.g} k={cfg.k} gate={cfg.gate} levels={cfg.levels} "
-        f"gist_mode={gist_mode} top_p={top_p} head_select={head_select} {kw}")
+        f"gist_mode={gist_mode} top_p={top_p} head_select={head_select} "
+        f"adaptive_k={adaptive_k} {kw}")
     inp = make_decode(cfg, seed, device=DEV, **kw)
-    call = DecodeCall(inp, gist_mode=gist_mode, top_p=top_p, head_select=head_select)()
+    call = DecodeCall(inp, gist_mode=gist_mode, top_p=top_p, head_select=head_select,
+                      adaptive_k=adaptive_k)()
     torch.cuda.synchronize()
     st = check_decode(inp, call, units=units)
     say("   ", st)
@@ -355,4 +357,54 @@ def test_repeated_calls_bitwise_identical_full_size():
             assert torch.equal(c.out, o) and torch.equal(c.lse, l) and torch.equal(c.sel, s), it
     torch.cuda.synchronize()
     del calls, insts
+    torch.cuda.empty_cache()
+
+
+# adaptive top-k: each level selects min(cap, floor(N / (L_eff G C)) + 1)
+ADAPTIVE = [
+    (SMALL.with_(N=300 * 32 + 5, k=6, gate=1), {}),                  # budget 3, under the cap
+    (SMALL.with_(N=300 * 32 + 5, k=6, Hq=2, Hkv=2), {}),             # G = 1: budget 10, cap 6
+    (SMALL.with_(N=300 * 32 + 5, k=6), dict(head_select=1)),         # per-head picks, union
+    (SMALL.with_(N=300 * 32 + 5, k=6, gate=1), dict(gist_mode=1)),   # selected summaries
+    (SMALL.with_(levels=2, J=4, k2=5, k=6, N=1250 * 32, n_plant=6, plant_groups=3), {}),
+    (SMALL.with_(levels=2, J=4, k2=5, k=6, N=1250 * 32, n_plant=6, plant_groups=3),
+     dict(gist_mode=1)),
+    (SMALL.with_(N=100, k=3), {}),                                   # budget 1
+]
+
+
+def _adaptive_count(cfg):
+    import oracle
+    b = oracle.adaptive_k_budget(N=cfg.N, C_=cfg.C, Hq=cfg.Hq, Hkv=cfg.Hkv, levels=cfg.levels,
+                                 J=cfg.J)
+    return b, min(cfg.k, b), min(cfg.k2, b)
+
+
+@pytest.mark.parametrize("idx", range(len(ADAPTIVE)), ids=[f"ak{i}" for i in range(len(ADAPTIVE))])
+def test_adaptive_k_variants(idx):
+    cfg, kw = ADAPTIVE[idx]
+    inp, call, st = run_case(cfg, 800 + idx, adaptive_k=1, max_chunks=cfg.M + 2, **kw)
+    b, k1, k2 = _adaptive_count(cfg)
+    sel = call.sel.cpu().numpy()
+    assert sel.shape[-1] == cfg.k * (cfg.G if kw.get("head_select") else 1)
+    n = (sel >= 0).sum(-1)
+    if cfg.levels == 2:
+        assert ((call.sel_groups.cpu().numpy() >= 0).sum(-1) == min(k2, cfg.nG)).all()
+        assert (n <= k1).all()
+    elif kw.get("head_select"):
+        assert ((n >= min(k1, cfg.H)) & (n <= min(cfg.G * k1, cfg.H))).all()
+    else:
+        assert (n == min(k1, cfg.H)).all()
+
+
+@pytest.mark.parametrize("name", ["llama32_1b_decode_32k", "llama31_8b_decode_128k",
+                                  "hssa_decode_512k"])
+def test_adaptive_k_full(name):
+    cfg = configs.DECODE_CONFIGS[name]
+    inp, call, st = run_case(cfg, configs.seed_for(name), adaptive_k=1)
+    assert st["excused"] <= max(1, st["units"] // 100)
+    b, k1, k2 = _adaptive_count(cfg)
+    n = (call.sel.cpu().numpy() >= 0).sum(-1)
+    assert (n == (k1 if cfg.levels == 1 else min(k1, k2 * cfg.J))).all(), (b, k1, k2)
+    del inp, call
     torch.cuda.empty_cache()

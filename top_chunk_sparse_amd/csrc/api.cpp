@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "api_internal.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -62,6 +63,7 @@ void plan_slices(long long units, int nchunks, int g, int* slices, int* cps) {
 struct DecodePlan {
     int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, cpw, nslots, kcap1, kcap2;
     int sk;   // entries per unit in sel: k, or G * k with per-head selection
+    int ku, k2u;   // chunks and groups selected: k and k2, or min(cap, budget) when adaptive
     float sigma;
     // workspace offsets (bytes)
     size_t off_cnt, off_cs1, off_ci1, off_lse1, off_cs2, off_ci2, off_sel, off_gamma, off_gsel,
@@ -82,6 +84,7 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (!(p->top_p >= 0.f && p->top_p <= 1.f)) return TCS_ERR_SHAPE;
     if (p->select_mode != TCS_SELECT_KV_HEAD && p->select_mode != TCS_SELECT_PER_HEAD)
         return TCS_ERR_SHAPE;
+    if (p->k_mode != TCS_K_FIXED && p->k_mode != TCS_K_ADAPTIVE) return TCS_ERR_SHAPE;
     const int G = p->Hq / p->Hkv;
     const long long units = (long long)p->B * p->Hkv;
     const int M = (int)(((long long)p->N + p->C - 1) / p->C);
@@ -99,6 +102,19 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     if (heads && (p->levels != 1 || p->gate_mode != TCS_GATE_NONE || p->top_p > 0.f ||
                   H > kMaxHeadSelectChunks))
         return TCS_ERR_UNSUPPORTED;
+    if (p->k_mode == TCS_K_ADAPTIVE && p->top_p > 0.f) return TCS_ERR_UNSUPPORTED;
+    if (p->levels == 2 && p->J < 1) return TCS_ERR_SHAPE;
+    // Adaptive top-k ("Simplified Sparse Attention via Gist Tokens", appendix A): one budget
+    // per routing level, floor(N / (L_eff G C)) + 1 with L_eff = C (one level) or C J (two);
+    // both levels select min(cap, budget).  Otherwise k and k2 as given.
+    pl->ku = p->k;
+    pl->k2u = p->k2;
+    if (p->k_mode == TCS_K_ADAPTIVE) {
+        const long long l_eff = (long long)p->C * (p->levels == 2 ? p->J : 1);
+        const long long budget = (long long)p->N / (l_eff * G * p->C) + 1;
+        pl->ku = (int)std::min<long long>(p->k, budget);
+        pl->k2u = (int)std::min<long long>(p->k2, budget);
+    }
     pl->G = G;
     pl->M = M;
     pl->H = H;
@@ -109,15 +125,15 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
         if (p->gate_mode != TCS_GATE_NONE) return TCS_ERR_UNSUPPORTED;
         if ((long long)p->J * p->g > kMaxSliceRows) return TCS_ERR_UNSUPPORTED;
         pl->nG = (H + p->J - 1) / p->J;
-        pl->k2e = p->k2 < pl->nG ? p->k2 : pl->nG;
+        pl->k2e = pl->k2u < pl->nG ? pl->k2u : pl->nG;
         if (pl->k2e > 64) return TCS_ERR_UNSUPPORTED;   // chosen groups held in LDS
         plan_slices(units, pl->nG, p->g, &pl->S2, &pl->cps2);
         pl->S1 = 0;
         pl->cps1 = 1;
         const long long ncand = (long long)pl->k2e * p->J;
-        ksel = (int)(p->k < ncand ? p->k : ncand);
-        pl->kcap2 = p->k2 < pl->cps2 ? p->k2 : pl->cps2;
-        pl->kcap1 = p->k < p->J ? p->k : p->J;
+        ksel = (int)(pl->ku < ncand ? pl->ku : ncand);
+        pl->kcap2 = pl->k2u < pl->cps2 ? pl->k2u : pl->cps2;
+        pl->kcap1 = pl->ku < p->J ? pl->ku : p->J;
     } else {
         pl->nG = 0;
         pl->k2e = 0;
@@ -125,9 +141,9 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
         pl->cps2 = 1;
         // per-head selection keeps G scores per chunk of a slice in LDS
         plan_slices(units, H, heads ? std::max(p->g, G) : p->g, &pl->S1, &pl->cps1);
-        ksel = p->k < H ? p->k : H;
+        ksel = pl->ku < H ? pl->ku : H;
         pl->kcap2 = 0;
-        pl->kcap1 = p->k < pl->cps1 ? p->k : pl->cps1;
+        pl->kcap1 = pl->ku < pl->cps1 ? pl->ku : pl->cps1;
         if (heads) ksel = (int)std::min<long long>((long long)G * ksel, H);   // union size bound
     }
     pl->kslots = ksel;
@@ -281,18 +297,38 @@ tcs_status tcs_decode_workspace_size(const tcs_decode_params* p, size_t* bytes) 
     return TCS_OK;
 }
 
-static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_pages,
-                              const void* v_pages, const int32_t* page_table, const void* gist_k,
-                              const void* gist_v, const void* gist2_k, const void* gist2_v,
-                              float* out, float* lse, int32_t* sel, int32_t* sel_groups,
-                              float* chunk_scores, void* workspace, size_t workspace_bytes,
-                              void* stream, void* const* events, int n_events) {
+}  // extern "C"
+
+namespace tcs {
+
+tcs_status decode_check(const tcs_decode_params* p, const void* q, const void* k_pages,
+                        const void* v_pages, const int32_t* page_table, const void* gist_k,
+                        const void* gist_v, const void* gist2_k, const void* gist2_v,
+                        const float* out, size_t* workspace_bytes) {
     DecodePlan pl;
     tcs_status st = plan_decode(p, &pl);
     if (st != TCS_OK) return st;
     if (!q || !k_pages || !v_pages || !page_table || !out) return TCS_ERR_NULL;
     if (pl.H > 0 && (!gist_k || !gist_v)) return TCS_ERR_NULL;
     if (p->levels == 2 && pl.nG > 0 && (!gist2_k || !gist2_v)) return TCS_ERR_NULL;
+    *workspace_bytes = pl.total;
+    return TCS_OK;
+}
+
+size_t decode_counter_bytes() { return sizeof(unsigned) * kCounterWords; }
+
+tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_pages,
+                       const void* v_pages, const int32_t* page_table, const void* gist_k,
+                       const void* gist_v, const void* gist2_k, const void* gist2_v, float* out,
+                       float* lse, int32_t* sel, int32_t* sel_groups, float* chunk_scores,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       void* const* events, int n_events) {
+    size_t need = 0;
+    tcs_status st = decode_check(p, q, k_pages, v_pages, page_table, gist_k, gist_v, gist2_k,
+                                 gist2_v, out, &need);
+    if (st != TCS_OK) return st;
+    DecodePlan pl;
+    plan_decode(p, &pl);
     st = check_ws(workspace, workspace_bytes, pl.total);
     if (st != TCS_OK) return st;
 
@@ -324,7 +360,8 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     ga.J = p->J; ga.k2 = p->k2; ga.H = pl.H;
 
     tcs::SelectOut chunk_sel{};   // the pass that chooses chunks
-    chunk_sel.k = p->k;
+    chunk_sel.k = pl.ku;
+    chunk_sel.stride = p->k;
     chunk_sel.sel = sel_p;
     chunk_sel.cand_score = (float*)(ws + pl.off_cs1);
     chunk_sel.cand_idx = (int32_t*)(ws + pl.off_ci1);
@@ -360,7 +397,8 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
         int32_t* gsel = sel_groups ? sel_groups : (int32_t*)(ws + pl.off_gsel);
         // level 2: every group, choosing k2 of them
         tcs::SelectOut gs{};
-        gs.k = p->k2;
+        gs.k = pl.k2u;
+        gs.stride = p->k2;
         gs.sel = gsel;
         gs.cand_score = (float*)(ws + pl.off_cs2);
         gs.cand_idx = (int32_t*)(ws + pl.off_ci2);
@@ -444,13 +482,17 @@ static tcs_status decode_impl(const tcs_decode_params* p, const void* q, const v
     return TCS_OK;
 }
 
+}  // namespace tcs
+
+extern "C" {
+
 tcs_status sparse_attn_decode(const tcs_decode_params* p, const void* q, const void* k_pages,
                               const void* v_pages, const int32_t* page_table, const void* gist_k,
                               const void* gist_v, const void* gist2_k, const void* gist2_v,
                               float* out, float* lse, int32_t* sel, int32_t* sel_groups,
                               float* chunk_scores, void* workspace, size_t workspace_bytes,
                               void* stream) {
-    return decode_impl(p, q, k_pages, v_pages, page_table, gist_k, gist_v, gist2_k, gist2_v, out,
+    return tcs::decode_impl(p, q, k_pages, v_pages, page_table, gist_k, gist_v, gist2_k, gist2_v, out,
                        lse, sel, sel_groups, chunk_scores, workspace, workspace_bytes, stream,
                        nullptr, 0);
 }
@@ -463,7 +505,7 @@ tcs_status sparse_attn_decode_timed(const tcs_decode_params* p, const void* q,
                                     float* chunk_scores, void* workspace, size_t workspace_bytes,
                                     void* stream, void* const* events, int n_events) {
     if (n_events < 0) return TCS_ERR_SHAPE;
-    return decode_impl(p, q, k_pages, v_pages, page_table, gist_k, gist_v, gist2_k, gist2_v, out,
+    return tcs::decode_impl(p, q, k_pages, v_pages, page_table, gist_k, gist_v, gist2_k, gist2_v, out,
                        lse, sel, sel_groups, chunk_scores, workspace, workspace_bytes, stream,
                        events, n_events);
 }
@@ -478,6 +520,16 @@ tcs_status tcs_workspace_init(void* workspace, size_t workspace_bytes, void* str
     if (workspace_bytes == 0) return TCS_OK;
     if (!workspace || ((uintptr_t)workspace % kAlign)) return TCS_ERR_WORKSPACE;
     if (tcs::launch_zero(workspace, workspace_bytes, (hipStream_t)stream) != hipSuccess)
+        return TCS_ERR_HIP;
+    return TCS_OK;
+}
+
+tcs_status tcs_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+    if (bytes == 0) return TCS_OK;
+    if (!src || !sink) return TCS_ERR_NULL;
+    if ((uintptr_t)src % 16 || bytes % 16) return TCS_ERR_SHAPE;
+    if (tcs::launch_stream_read(src, bytes, (unsigned*)sink, TCS_STREAM_READ_BLOCKS,
+                                (hipStream_t)stream) != hipSuccess)
         return TCS_ERR_HIP;
     return TCS_OK;
 }

@@ -341,8 +341,8 @@ __device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int 
         __syncthreads();
         lse = *lse_part_lds;
     }
-    int32_t* sel = so.sel + (long long)u * so.k;
-    float* gam = so.gamma ? so.gamma + (long long)u * so.k : nullptr;
+    int32_t* sel = so.sel + (long long)u * so.stride;
+    float* gam = so.gamma ? so.gamma + (long long)u * so.stride : nullptr;
     auto score_at = [&](int i) { return staged ? mc.score[i] : ld_shared_dev(ucs + i); };
     const bool top_p = so.top_p > 0.f;
     auto emit2 = [&](int j, int i) {
@@ -402,7 +402,7 @@ __device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int 
         }
         ke = keep;
     }
-    for (int j = ke + tid; j < so.k; j += 256) {
+    for (int j = ke + tid; j < so.stride; j += 256) {
         sel[j] = -1;
         if (gam) gam[j] = 0.f;
     }
@@ -483,7 +483,7 @@ __device__ __forceinline__ void select_epilogue_heads(const SelectOut& so, int u
     }
     // compaction: thread t owns a run of bitmap words; its first position is the number of
     // chosen chunks in the words before its run
-    const int sk = G * so.k;
+    const int sk = G * so.stride;
     int32_t* sel = so.sel + (long long)u * sk;
     const int wpt = (nw + 255) / 256;
     const int w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
@@ -910,6 +910,39 @@ __global__ void fill_kernel(int32_t* p, long long n, int32_t v) {
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
          i += (long long)gridDim.x * blockDim.x)
         p[i] = v;
+}
+
+// Plain streaming read: every 16-byte unit of [p, p + n16) is loaded once (non-temporal, four
+// in flight per lane) and folded into one word per workgroup, so that nothing is skipped.  The
+// HBM ceiling the decode kernels are measured against.
+__global__ void __launch_bounds__(256) stream_read_kernel(const uint16_t* p, long long n16,
+                                                          unsigned* sink) {
+    const long long stride = (long long)gridDim.x * 256;
+    long long i = blockIdx.x * 256LL + threadIdx.x;
+    unsigned acc = 0u;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = ld16(p + 8 * i), b = ld16(p + 8 * (i + stride));
+        const uint4 c = ld16(p + 8 * (i + 2 * stride)), d = ld16(p + 8 * (i + 3 * stride));
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+        acc ^= c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = ld16(p + 8 * i);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    __shared__ unsigned red[4];
+    for (int off = 32; off >= 1; off >>= 1) acc ^= (unsigned)__shfl_xor((int)acc, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t launch_stream_read(const void* p, size_t bytes, unsigned* sink, int blocks,
+                              hipStream_t s) {
+    const long long n16 = (long long)(bytes / 16);
+    if (n16 <= 0) return hipSuccess;
+    stream_read_kernel<<<blocks, 256, 0, s>>>((const uint16_t*)p, n16, sink);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------

@@ -15,9 +15,10 @@ struct Partials {
 
 // Selection done by the last workgroup of each unit (see select_epilogue).
 struct SelectOut {
-    int k;                    // entries per unit in sel / gamma
-    int32_t* sel;             // [units][k] ascending item ids, -1 padded
-    float* gamma;             // [units][k] SAS gate (log of the softmax over all items) or null
+    int k;                    // items to select per unit (per query head with per-head selection)
+    int stride;               // entries per unit in sel / gamma (>= k; G * stride per-head)
+    int32_t* sel;             // [units][stride] ascending item ids, -1 padded
+    float* gamma;             // [units][stride] SAS gate (log of the softmax over all items) or null
     float* cand_score;        // [units][slices][kcap] per-slice candidates
     int32_t* cand_idx;        // [units][slices][kcap]
     int kcap;                 // min(k, items per slice)
@@ -86,6 +87,8 @@ hipError_t launch_gist(const GistLaunch& a, hipStream_t s);
 hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t v, hipStream_t s);
+hipError_t launch_stream_read(const void* p, size_t bytes, unsigned* sink, int blocks,
+                              hipStream_t s);
 
 struct PrefillSelectLaunch {
     const float* S;           // [units][nb][nb]

@@ -28,7 +28,8 @@ class DecodeParams(C.Structure):
                                          "max_chunks",
                                          "num_pages", "gist_cap")] + [("scale", C.c_float),
                                                                       ("top_p", C.c_float),
-                                                                      ("select_mode", C.c_int32)]
+                                                                      ("select_mode", C.c_int32),
+                                                                      ("k_mode", C.c_int32)]
 
 
 class GistPrefillParams(C.Structure):
@@ -49,7 +50,7 @@ EXPORTS = ("tcs_abi_version", "tcs_status_str", "tcs_decode_workspace_size", "sp
            "tcs_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_prefill_timed",
            "tcs_prefill_backward_workspace_size", "sparse_attn_prefill_backward",
            "sparse_attn_prefill_backward_timed", "tcs_gist_prefill_workspace_size",
-           "sparse_attn_gist_prefill", "sparse_attn_gist_prefill_timed")
+           "sparse_attn_gist_prefill", "sparse_attn_gist_prefill_timed", "tcs_stream_read")
 
 
 def lib():
@@ -83,8 +84,21 @@ def lib():
                                                          [_V, C.c_int])
         h.tcs_decode_stage_count.argtypes = [C.POINTER(DecodeParams)]
         h.tcs_workspace_init.argtypes = [_V, C.c_size_t, _V]
+        h.tcs_stream_read.argtypes = [_V, C.c_size_t, _V, _V]
         _lib = h
     return _lib
+
+
+STREAM_READ_BLOCKS = 2048   # TCS_STREAM_READ_BLOCKS
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Enqueue a plain streaming read of ``src`` (the HBM read ceiling; measurement only)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device)
+    assert sink.numel() * sink.element_size() >= 4 * STREAM_READ_BLOCKS
+    _check(lib().tcs_stream_read(_p(src), src.numel() * src.element_size(), _p(sink),
+                                 stream.cuda_stream))
 
 
 def status_str(code: int) -> str:
@@ -102,17 +116,18 @@ def _p(t: Optional[torch.Tensor]):
 
 GISTS_ALL, GISTS_SELECTED = 0, 1   # TCS_GISTS_*
 SELECT_KV_HEAD, SELECT_PER_HEAD = 0, 1   # TCS_SELECT_*
+K_FIXED, K_ADAPTIVE = 0, 1   # TCS_K_*
 
 
 def decode_params(*, B, Hq, Hkv, d, N, C_, g, k, gate=0, levels=1, J=0, k2=0, max_chunks=None,
                   num_pages, gist_cap=0, scale=0.0, gist_mode=GISTS_ALL,
-                  top_p=0.0, select_mode=SELECT_KV_HEAD) -> DecodeParams:
+                  top_p=0.0, select_mode=SELECT_KV_HEAD, k_mode=K_FIXED) -> DecodeParams:
     M = -(-N // C_) if C_ > 0 else 1
     return DecodeParams(struct_size=C.sizeof(DecodeParams), B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, C=C_,
                         g=g, k=k, gate_mode=gate, gist_mode=gist_mode, levels=levels, J=J, k2=k2,
                         max_chunks=M if max_chunks is None else max_chunks,
                         num_pages=num_pages, gist_cap=gist_cap, scale=scale, top_p=top_p,
-                        select_mode=select_mode)
+                        select_mode=select_mode, k_mode=k_mode)
 
 
 def decode_workspace_size(p: DecodeParams) -> int:
@@ -232,18 +247,20 @@ class DecodeCall:
     """Outputs and workspace for repeated decode calls on one input bundle."""
 
     def __init__(self, inp, with_scores=True, k=None, scale=0.0, gist_mode=GISTS_ALL,
-                 top_p=0.0, head_select=0):
+                 top_p=0.0, head_select=0, adaptive_k=0):
         c = inp.cfg
         dev = inp.q.device
         self.inp = inp
         self.gist_mode = gist_mode
         self.head_select = head_select
+        self.adaptive_k = adaptive_k
         self.p = decode_params(B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, N=c.N, C_=c.C, g=c.g,
                                k=c.k if k is None else k, gate=c.gate, levels=c.levels, J=c.J,
                                k2=c.k2, max_chunks=inp.page_table.shape[1],
                                num_pages=inp.num_pages, gist_cap=inp.gist_k.shape[2],
                                scale=scale, gist_mode=gist_mode, top_p=top_p,
-                               select_mode=SELECT_PER_HEAD if head_select else SELECT_KV_HEAD)
+                               select_mode=SELECT_PER_HEAD if head_select else SELECT_KV_HEAD,
+                               k_mode=K_ADAPTIVE if adaptive_k else K_FIXED)
         kk = self.p.k * (c.G if head_select else 1)   # sel entries per (b, kv)
         self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
