@@ -160,7 +160,8 @@ typedef enum {
     TCS_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes                  */
     TCS_ERR_UNSUPPORTED = 3,  /* valid, but not built (see supported shapes above)   */
     TCS_ERR_WORKSPACE = 4,    /* workspace NULL, misaligned or smaller than required  */
-    TCS_ERR_HIP = 5           /* a kernel launch failed                               */
+    TCS_ERR_HIP = 5,          /* a kernel launch failed                               */
+    TCS_ERR_TOO_LARGE = 6     /* needs more than the static scratch of the _noalloc call */
 } tcs_status;
 
 enum { TCS_GATE_NONE = 0, TCS_GATE_SAS = 1 };
@@ -221,6 +222,28 @@ tcs_status sparse_attn_decode_timed(const tcs_decode_params* p,
                                     int32_t* sel, int32_t* sel_groups, float* chunk_scores,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     void* const* events, int n_events);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): sparse_attn_decode with no workspace argument.  Its
+ * workspace is a static device array of TCS_NOALLOC_SCRATCH_BYTES bytes, one per GPU the
+ * library runs on, held until the process ends; its address is looked up once per device on
+ * the first call made with that device current.  The call allocates and frees nothing.  Every
+ * call clears the array's arrival counters (one small fill kernel on `stream`) and leaves the
+ * rest of the array holding the call's intermediates.  Shapes whose workspace
+ * (tcs_decode_workspace_size) exceeds TCS_NOALLOC_SCRATCH_BYTES return TCS_ERR_TOO_LARGE
+ * before any device work; other argument errors as sparse_attn_decode.  All calls on one GPU
+ * share its array: calls that overlap on one GPU (other streams, other threads) race, so
+ * order them on one stream.  Results are bitwise those of sparse_attn_decode. */
+#define TCS_NOALLOC_SCRATCH_BYTES (16u << 20)
+tcs_status sparse_attn_decode_noalloc(const tcs_decode_params* p,
+                                      const void* q,
+                                      const void* k_pages, const void* v_pages,
+                                      const int32_t* page_table,
+                                      const void* gist_k, const void* gist_v,
+                                      const void* gist2_k, const void* gist2_v,
+                                      float* out, float* lse,
+                                      int32_t* sel, int32_t* sel_groups, float* chunk_scores,
+                                      void* stream);
 
 /* Number of stages sparse_attn_decode_timed brackets with events for these parameters
  * (2 for one level, 3 for two levels), -1 if the parameters are invalid.  Host-only. */

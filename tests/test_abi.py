@@ -35,7 +35,7 @@ def test_abi_version_and_status_strings():
     # the header's constant, which the build entry point checks the library against
     with open(os.path.join(os.path.dirname(__file__), "..", "include", "tcsparse.h")) as f:
         assert "#define TCS_ABI_VERSION 7\n" in f.read()
-    for code in range(6):
+    for code in range(7):
         assert ops.status_str(code)
     assert ops.status_str(99) == "unknown status"
 
@@ -279,3 +279,14 @@ def test_stage_counts():
     assert ops.decode_stage_count(P()) == 2
     assert ops.decode_stage_count(P(levels=2, J=4, k2=2)) == 3
     assert ops.decode_stage_count(P(d=96)) == -1
+
+
+def test_noalloc_rejects_beyond_its_scratch_before_device_work():
+    # the shape check comes before any device call: placeholder (never dereferenced) pointers
+    big = P(B=256, Hq=32, Hkv=8, N=131072, C_=128, g=4, k=16, num_pages=256 * 1024)
+    assert ops.decode_workspace_size(big) > ops.NOALLOC_SCRATCH_BYTES
+    fake = C.c_void_p(4096)
+    st = ops.lib().sparse_attn_decode_noalloc(C.byref(big), *([fake] * 10), None, None, None, None)
+    assert st == ops.TCS_ERR_TOO_LARGE
+    assert "scratch" in ops.status_str(st)
+    assert ops.lib().sparse_attn_decode_noalloc(C.byref(P()), *([None] * 14)) == ops.TCS_ERR_NULL

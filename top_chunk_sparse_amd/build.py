@@ -20,7 +20,8 @@ LIB = os.path.join(HERE, "libtcsparse.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["decode.hip", "prefill.hip", "prefill_bwd.hip", "gist_prefill.hip", "api.cpp"]
+SOURCES = ["decode.hip", "prefill.hip", "prefill_bwd.hip", "gist_prefill.hip", "api.cpp",
+           "noalloc.hip"]
 
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function",

@@ -284,6 +284,7 @@ const char* tcs_status_str(tcs_status s) {
         case TCS_ERR_UNSUPPORTED: return "unsupported configuration";
         case TCS_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case TCS_ERR_HIP: return "HIP kernel launch failed";
+        case TCS_ERR_TOO_LARGE: return "shape needs more than the static scratch of the no-alloc entry point";
     }
     return "unknown status";
 }

@@ -12,7 +12,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("TCS_LIB_PATH") or os.path.join(_HERE, "libtcsparse.so")
 
-TCS_OK, TCS_ERR_NULL, TCS_ERR_SHAPE, TCS_ERR_UNSUPPORTED, TCS_ERR_WORKSPACE, TCS_ERR_HIP = range(6)
+(TCS_OK, TCS_ERR_NULL, TCS_ERR_SHAPE, TCS_ERR_UNSUPPORTED, TCS_ERR_WORKSPACE, TCS_ERR_HIP,
+ TCS_ERR_TOO_LARGE) = range(7)
+NOALLOC_SCRATCH_BYTES = 16 << 20   # TCS_NOALLOC_SCRATCH_BYTES
 GATE_NONE, GATE_SAS = 0, 1
 
 
@@ -50,7 +52,8 @@ EXPORTS = ("tcs_abi_version", "tcs_status_str", "tcs_decode_workspace_size", "sp
            "tcs_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_prefill_timed",
            "tcs_prefill_backward_workspace_size", "sparse_attn_prefill_backward",
            "sparse_attn_prefill_backward_timed", "tcs_gist_prefill_workspace_size",
-           "sparse_attn_gist_prefill", "sparse_attn_gist_prefill_timed", "tcs_stream_read")
+           "sparse_attn_gist_prefill", "sparse_attn_gist_prefill_timed", "tcs_stream_read",
+           "sparse_attn_decode_noalloc")
 
 
 def lib():
@@ -85,6 +88,7 @@ def lib():
         h.tcs_decode_stage_count.argtypes = [C.POINTER(DecodeParams)]
         h.tcs_workspace_init.argtypes = [_V, C.c_size_t, _V]
         h.tcs_stream_read.argtypes = [_V, C.c_size_t, _V, _V]
+        h.sparse_attn_decode_noalloc.argtypes = [C.POINTER(DecodeParams)] + [_V] * 14
         _lib = h
     return _lib
 
@@ -153,6 +157,19 @@ def sparse_attn_decode(p: DecodeParams, q, k_pages, v_pages, page_table, gist_k,
     else:
         code = lib().sparse_attn_decode_timed(*args, C.cast(events, _V), len(events))
     _check(code)
+
+
+def sparse_attn_decode_noalloc(p: DecodeParams, q, k_pages, v_pages, page_table, gist_k,
+                               gist_v, gist2_k=None, gist2_v=None, *, out, lse=None, sel=None,
+                               sel_groups=None, chunk_scores=None, stream=None) -> None:
+    """sparse_attn_decode without a workspace: the library's static per-GPU scratch serves
+    instead (for callers that cannot allocate)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device)
+    _check(lib().sparse_attn_decode_noalloc(
+        C.byref(p), _p(q), _p(k_pages), _p(v_pages), _p(page_table), _p(gist_k), _p(gist_v),
+        _p(gist2_k), _p(gist2_v), _p(out), _p(lse), _p(sel), _p(sel_groups), _p(chunk_scores),
+        stream.cuda_stream))
 
 
 def decode_stage_count(p: DecodeParams) -> int:
@@ -271,6 +288,16 @@ class DecodeCall:
                                          dtype=torch.float32, device=dev)
                              if with_scores else None)
         self.ws = workspace(decode_workspace_size(self.p), dev)
+
+    def noalloc(self, stream=None):
+        """The same call through the allocation-free entry point (no workspace)."""
+        i = self.inp
+        sparse_attn_decode_noalloc(self.p, i.q, i.k_pages, i.v_pages, i.page_table, i.gist_k,
+                                   i.gist_v, i.gist2_k, i.gist2_v, out=self.out, lse=self.lse,
+                                   sel=self.sel if self.p.k > 0 else None,
+                                   sel_groups=self.sel_groups, chunk_scores=self.chunk_scores,
+                                   stream=stream)
+        return self
 
     def __call__(self, stream=None, events=None):
         i = self.inp
