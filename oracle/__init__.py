@@ -16,7 +16,8 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+# TCS_ORACLE_LIB: another build of oracle.c (the sanitizer test runs the pins against one)
+_SO = os.environ.get("TCS_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 
 def build(force: bool = True) -> str:

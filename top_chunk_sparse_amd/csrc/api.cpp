@@ -9,6 +9,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "api_internal.hpp"
 #include "launch.hpp"
@@ -277,7 +278,11 @@ extern "C" {
 int tcs_abi_version(void) { return TCS_ABI_VERSION; }
 
 const char* tcs_status_str(tcs_status s) {
-    switch (s) {
+    // callers may pass any int (the C enum is an int); read it as one, never as the C++ enum,
+    // whose values outside the declared ones are undefined
+    int code;
+    std::memcpy(&code, &s, sizeof code);
+    switch (code) {
         case TCS_OK: return "ok";
         case TCS_ERR_NULL: return "null pointer argument";
         case TCS_ERR_SHAPE: return "invalid sizes";
