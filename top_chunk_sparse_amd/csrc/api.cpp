@@ -62,9 +62,13 @@ void plan_slices(long long units, int nchunks, int g, int* slices, int* cps) {
 }
 
 struct DecodePlan {
-    int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, cpw, nslots, kcap1, kcap2;
+    int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, cpw, rpw, nwx, nslots, kcap1, kcap2;
     int sk;   // entries per unit in sel: k, or G * k with per-head selection
     int ku, k2u;   // chunks and groups selected: k and k2, or min(cap, budget) when adaptive
+    // one level, one list per slice, no top-p: the chunk pass ranks the slices' candidate lists
+    // itself (ncand1 of them per unit) and the scoring pass has no last-workgroup merge
+    bool defer1;
+    int ncand1;
     float sigma;
     // workspace offsets (bytes)
     size_t off_cnt, off_cs1, off_ci1, off_lse1, off_cs2, off_ci2, off_sel, off_gamma, off_gsel,
@@ -147,6 +151,17 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
         pl->kcap1 = pl->ku < pl->cps1 ? pl->ku : pl->cps1;
         if (heads) ksel = (int)std::min<long long>((long long)G * ksel, H);   // union size bound
     }
+    pl->defer1 = false;
+    pl->ncand1 = 0;
+    if (p->levels == 1 && !heads && p->top_p == 0.f && pl->S1 > 0 && pl->ku >= 1) {
+        const long long last_items = H - (long long)(pl->S1 - 1) * pl->cps1;
+        const long long ncand =
+            (long long)(pl->S1 - 1) * pl->kcap1 + std::min<long long>(pl->ku, last_items);
+        if (ncand <= 256 && (pl->cps1 <= 256 || pl->kcap1 == pl->cps1)) {
+            pl->defer1 = true;
+            pl->ncand1 = (int)ncand;
+        }
+    }
     pl->kslots = ksel;
     pl->sk = heads ? G * p->k : p->k;
     // chunk attention: enough workgroups to fill the GPU, one or more chunks each
@@ -157,10 +172,24 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
     // (dispatch, query load, partial write, arrival) then pay for twice the bytes.
     const long long cpw_min = units * (ksel + 1) >= 512 ? 2 : 1;
     pl->cpw = (int)std::max<long long>(std::min(cpw_min, cpw_max), std::min(cpw, cpw_max));
+    pl->rpw = 0;
+    pl->nwx = (ksel + 1 + pl->cpw - 1) / pl->cpw;
+    if (!sel_gists) {
+        // Row mode: the slots' rows laid end to end and cut into equal runs, so that the grid
+        // comes to about kChunkTargetWorkgroups equal workgroups (a CU then holds whole
+        // workgroups of equal work) of at least cpw_min chunks' rows each.
+        const long long R = (long long)ksel * p->C + (p->N - (long long)(M - 1) * p->C);
+        long long rpw = (units * R + kChunkTargetWorkgroups - 1) / kChunkTargetWorkgroups;
+        rpw = std::max<long long>(rpw, std::min(cpw_min, cpw_max) * p->C);
+        rpw = (rpw + 15) / 16 * 16;
+        rpw = std::min<long long>(rpw, std::min<long long>(kMaxSliceRows, 15LL * p->C));
+        pl->rpw = (int)rpw;
+        pl->nwx = (int)((R + rpw - 1) / rpw);
+    }
     // softmax partial slots per query head: gist slices and level-2 slices (none with selected
     // gists), one per chosen level-2 group (its members' gists, or with selected gists its own
     // level-2 gists), then the chunk-attention workgroups
-    pl->nslots = (sel_gists ? 0 : pl->S1 + pl->S2) + pl->k2e + (ksel + 1 + pl->cpw - 1) / pl->cpw;
+    pl->nslots = (sel_gists ? 0 : pl->S1 + pl->S2) + pl->k2e + pl->nwx;
     const long long BH = (long long)p->B * p->Hq;
     const long long s1 = p->levels == 2 ? pl->k2e : pl->S1;     // slices of the chunk pass
     auto n1 = [](long long x) { return x > 0 ? x : 1; };
@@ -382,6 +411,7 @@ tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_
         chunk_sel.slice_lse = (gamma || p->top_p > 0.f) ? (float*)(ws + pl.off_lse1) : nullptr;
         chunk_sel.top_p = p->top_p;
         chunk_sel.counter = cnt;
+        chunk_sel.defer = pl.defer1;
         ga.gk = (const uint16_t*)gist_k;
         ga.gv = (const uint16_t*)gist_v;
         ga.unit_stride = (long long)cap * p->g * p->d;
@@ -473,10 +503,22 @@ tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_
     ca.B = p->B; ca.Hq = p->Hq; ca.Hkv = p->Hkv; ca.d = p->d; ca.C = p->C; ca.N = p->N;
     ca.M = pl.M; ca.max_chunks = p->max_chunks; ca.num_pages = p->num_pages;
     ca.sel = sel_p; ca.gamma = gamma; ca.k = pl.sk; ca.kslots = pl.kslots; ca.cpw = pl.cpw;
+    ca.rpw = pl.rpw;
     ca.sigma = pl.sigma; ca.part = part; ca.slot0 = slot;
     ca.counter = cnt + kCntChunk;
     ca.out = out;
     ca.lse = lse;
+    if (pl.defer1) {
+        ca.cand_score = chunk_sel.cand_score;
+        ca.cand_idx = chunk_sel.cand_idx;
+        ca.slice_lse = chunk_sel.slice_lse;
+        ca.nslices = pl.S1;
+        ca.kcap = pl.kcap1;
+        ca.ncand = pl.ncand1;
+        ca.ksel = pl.kslots;
+        ca.sel_out = sel_p;
+        ca.sel_stride = pl.sk;
+    }
     if (p->gist_mode == TCS_GISTS_SELECTED) {
         ca.gk = (const uint16_t*)gist_k;
         ca.gv = (const uint16_t*)gist_v;

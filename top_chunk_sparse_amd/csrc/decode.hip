@@ -4,13 +4,17 @@
 //                 its group through the chunk's gist keys ("Simplified Sparse Attention via
 //                 Gist Tokens", section 3.2), pools them into one log-sum-exp score per chunk,
 //                 and -- because gists are tokens of the softmax set themselves -- folds the
-//                 same gist rows into per-slice softmax partials with the gist values.  The
-//                 last workgroup of a unit to finish merges the slices' candidate lists into
-//                 the unit's top-k (section 3.3; ties to the lower index) and, with the SAS
-//                 gate on, the gate log p_c over all historical scores ("SAS", abstract).
+//                 same gist rows into per-slice softmax partials with the gist values.  Each
+//                 slice publishes its best k items; the unit's top-k (section 3.3; ties to the
+//                 lower index) and, with the SAS gate on, the gate log p_c over all historical
+//                 scores ("SAS", abstract) are taken from those lists either by the unit's last
+//                 slice to finish or -- one routing level, plain top-k -- by every chunk_kernel
+//                 workgroup of the unit as it starts, so that no gist workgroup waits.
 //   chunk_kernel  split-K attention over the selected chunks and the current chunk, read
 //                 through the page table (section 3.6: only the selected keys are touched);
-//                 the last workgroup of a unit merges all partials in a fixed order.
+//                 with every gist in the token set, the rows of all slots, laid end to end,
+//                 are cut into equal runs, one per workgroup; the last workgroup of a unit
+//                 merges all partials in a fixed order.
 //
 // Layout of the work: one 256-thread workgroup streams runs of d-element bf16 rows (gist rows
 // or the rows of a page).  A row is read by d/8 lanes with one 16-byte load each, so a wave
@@ -276,10 +280,12 @@ struct TopPSmem {             // the capped top-k of one unit, for the top-p cut
     int rank[256];            // by position
 };
 
-__device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
-                                const float* s_score, int item0, int nitems, int last_items,
-                                float* lse_part_lds, void* scratch, MergeCand& mc, int* s_flag,
-                                int* s_chosen, ReduceSmem& red, TopPSmem& tps, int* s_keep) {
+// A slice's share of the selection: the statistics of its scores for the gate (max and sum of
+// exp) and its best min(k, nitems) items, ascending, with their scores.  `scratch` holds a
+// TopkSmem, or only a SmallTopkSmem when nitems <= 256 or k >= nitems.
+__device__ __forceinline__ void publish_slice(const SelectOut& so, int u, int slot, int nslices,
+                                              const float* s_score, int item0, int nitems,
+                                              void* scratch, ReduceSmem& red) {
     const int tid = threadIdx.x;
     const int kc = so.k < nitems ? so.k : nitems;
     float* cs = so.cand_score + ((long long)u * nslices + slot) * so.kcap;
@@ -309,6 +315,14 @@ __device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int 
     } else {
         block_topk(nitems, so.k, sc, emit, *reinterpret_cast<TopkSmem*>(scratch));
     }
+}
+
+__device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
+                                const float* s_score, int item0, int nitems, int last_items,
+                                float* lse_part_lds, void* scratch, MergeCand& mc, int* s_flag,
+                                int* s_chosen, ReduceSmem& red, TopPSmem& tps, int* s_keep) {
+    const int tid = threadIdx.x;
+    publish_slice(so, u, slot, nslices, s_score, item0, nitems, scratch, red);
     if (!arrive_last(so.counter + u, (unsigned)nslices, s_flag)) return;
 
     // ---- last workgroup of the unit: merge ------------------------------------------------
@@ -517,7 +531,10 @@ struct GistSmem {
         SmallTopkSmem small;
     } x;
     float score[kMaxSliceRows];   // also the top-p staging of the last workgroup
-    MergeCand mc;
+    union {
+        MergeCand mc;             // the last workgroup's staged candidates
+        SmallTopkSmem pub;        // deferred selection: the slice top-k, taken before the V rows
+    } m;
     HeadStatsSmem<G> hs;
     ReduceSmem red;
     float lse;
@@ -625,6 +642,17 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
         sm.score[c] = s;
         if (a.scores_out) a.scores_out[(long long)u * a.score_stride + c0 + c] = s;
     }
+    if constexpr (MODE == kGistPlain) {
+        if (a.selo.defer) {
+            // The chunk pass ranks the slices' lists itself: publish this slice's list now,
+            // while the first V batch travels, and end with the gist partial -- no workgroup
+            // waits for the others here.
+            __syncthreads();   // every pooled score is in sm.score
+            publish_slice(a.selo, u, y, a.slices, sm.score, c0, nit, &sm.m.pub, sm.red);
+            if (!a.scores_only) fold_rows<D, G>(sm, a.part, V, nrows, vfirst, bh0, a.slot0 + y);
+            return;
+        }
+    }
     if (!a.scores_only) {   // the gists are tokens of the softmax set: fold them in here
         fold_rows<D, G>(sm, a.part, V, nrows, vfirst, bh0, a.slot0 + y);
     } else if constexpr (MODE == kGistMeta) {
@@ -644,10 +672,10 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
     __syncthreads();
     if constexpr (MODE == kGistHeads) {
         select_epilogue_heads<G>(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.x,
-                                 sm.mc, &sm.flag, bits);
+                                 sm.m.mc, &sm.flag, bits);
     } else {
         select_epilogue(a.selo, u, y, a.slices, sm.score, c0, nit, last_items, &sm.lse, &sm.x,
-                        sm.mc, &sm.flag, sm.chosen, sm.red,
+                        sm.m.mc, &sm.flag, sm.chosen, sm.red,
                         // the slice scores are dead once the slice's list is out: the unit's
                         // top-p cut reuses their space
                         *reinterpret_cast<TopPSmem*>(sm.score), &sm.tp_keep);
@@ -784,20 +812,91 @@ __device__ __forceinline__ void merge_partials(const Partials& P, int bh0, float
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxCpw = 16;
 
+constexpr int kMaxDeferCand = 256;   // deferred selection: candidates ranked in LDS
+
+struct RankSmem {
+    MergeCand mc;
+    SmallTopkSmem st;
+    ReduceSmem red;
+};
+
 template <int D, int G>
 struct ChunkSmem {
     union {
         float lg[kMaxSliceRows * G];
         float fin[RowStream<D, G>::NW * G * D];
         MergeSmem<G> merge;
+        RankSmem rank;
     } x;
     HeadStatsSmem<G> hs;
     int page[kMaxCpw];
     float bias[kMaxCpw];
-    int rows[kMaxCpw];
+    int rb[kMaxCpw];      // first row of the slot's chunk this workgroup reads
+    int rows[kMaxCpw];    // rows read from it
+    int lrow[kMaxCpw];    // their place in the logits
     int chunk[kMaxCpw];   // selected chunk of the slot, -1 for the current chunk
     int flag;
 };
+
+// Deferred selection: every workgroup of the unit ranks the scoring pass's per-slice lists
+// (ascending chunk ids, slice after slice) as that pass's last workgroup would -- the top
+// min(k, n) by score, ties to the lower chunk id, gate log p = score - log-sum-exp of every
+// historical score -- and keeps the chunks and gate biases of its own slots [j0, j0 + nj) in
+// sm.chunk / sm.bias.  Workgroup 0 also writes the unit's selection out.
+template <int D, int G>
+__device__ __forceinline__ void rank_candidates(const ChunkLaunch& a, ChunkSmem<D, G>& sm, int u,
+                                                int wx, int j0, int nj) {
+    RankSmem& rk = sm.x.rank;
+    const int tid = threadIdx.x;
+    const int n = a.ncand;
+    // every hand-off value in one round trip: thread t holds candidate t and slice t's
+    // (max, sum exp) pair
+    const long long base = (long long)u * a.nslices * a.kcap;
+    float cs = 0.f;
+    int32_t ci = 0;
+    float2 pr = make_float2(-INFINITY, 0.f);
+    if (tid < n) {
+        cs = a.cand_score[base + tid];
+        ci = a.cand_idx[base + tid];
+    }
+    if (a.slice_lse && tid < a.nslices)
+        pr = *reinterpret_cast<const float2*>(a.slice_lse + ((long long)u * a.nslices + tid) * 2);
+    if (tid < n) {
+        rk.mc.score[tid] = cs;
+        rk.mc.idx[tid] = ci;
+    }
+    if (tid < nj) {
+        sm.chunk[tid] = -1;
+        sm.bias[tid] = 0.f;
+    }
+    float lse = 0.f;
+    if (a.slice_lse) {   // log-sum-exp of every historical score, from the slices' statistics
+        const float mx = block_max(pr.x, rk.red);
+        const float z = block_sum(tid < a.nslices ? pr.y * expf(pr.x - mx) : 0.f, rk.red);
+        lse = mx + logf(z);
+    } else {
+        __syncthreads();
+    }
+    int32_t* sel = a.sel_out + (long long)u * a.sel_stride;
+    auto emit = [&](int j, int i) {
+        const int32_t c = rk.mc.idx[i];
+        if (wx == 0) sel[j] = c;
+        if (j >= j0 && j < j0 + nj) {
+            sm.chunk[j - j0] = c;
+            sm.bias[j - j0] = a.slice_lse ? rk.mc.score[i] - lse : 0.f;
+        }
+    };
+    int ke;
+    if (a.ksel >= n) {
+        for (int i = tid; i < n; i += 256) emit(i, i);
+        ke = n;
+    } else {
+        ke = small_topk(n, a.ksel, [&](int i) { return rk.mc.score[i]; }, emit, rk.st);
+    }
+    if (wx == 0)
+        for (int j = ke + tid; j < a.sel_stride; j += 256) sel[j] = -1;
+    __syncthreads();   // sm.chunk / sm.bias complete; the union is free again
+}
 
 // Workgroup wx of unit u (nwx workgroups per unit).
 template <int D, int G>
@@ -806,15 +905,34 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, ChunkSmem<D, G>
     using RS = RowStream<D, G>;
     const int b = u / a.Hkv, kv = u % a.Hkv;
     const int bh0 = b * a.Hq + kv * G;
-    const int j0 = wx * a.cpw, nj = min(a.cpw, a.kslots + 1 - j0);
-    // this workgroup's chunks: page, gate bias and row count (page -1: none, -2: out of range)
+    const int rows_cur = a.N - (a.M - 1) * a.C;
+    // Row mode (rpw > 0): the slots' rows laid end to end -- slot j < kslots is C rows from
+    // j C, the current chunk rows_cur rows from kslots C -- and this workgroup takes rows
+    // [r0, r1).  Slot mode: whole slots [j0, j0 + nj).
+    int j0, nj, r0 = 0, r1 = 0;
+    if (a.rpw > 0) {
+        r0 = wx * a.rpw;
+        r1 = min(a.kslots * a.C + rows_cur, r0 + a.rpw);
+        j0 = r0 / a.C;
+        nj = (r1 - 1) / a.C - j0 + 1;
+    } else {
+        j0 = wx * a.cpw;
+        nj = min(a.cpw, a.kslots + 1 - j0);
+    }
+    if (a.cand_score) rank_candidates<D, G>(a, sm, u, wx, j0, nj);
+    // this workgroup's chunks: page, gate bias and rows (page -1: none, -2: out of range)
     if (threadIdx.x < nj) {
         const int j = j0 + threadIdx.x;
         int c, rows;
         float bias = 0.f;
         if (j < a.kslots) {
-            c = a.sel[(long long)u * a.k + j];
-            if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
+            if (a.cand_score) {
+                c = sm.chunk[threadIdx.x];
+                bias = sm.bias[threadIdx.x];
+            } else {
+                c = a.sel[(long long)u * a.k + j];
+                if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
+            }
             rows = a.C;
         } else {
             c = a.M - 1;
@@ -825,14 +943,22 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, ChunkSmem<D, G>
             page = a.page_table[(long long)b * a.max_chunks + c];
             if (page < 0 || page >= a.num_pages) page = -2;
         }
+        int rb = 0, lrow = threadIdx.x * a.C;
+        if (a.rpw > 0) {   // clip the slot's rows to [r0, r1)
+            rb = max(r0 - j * a.C, 0);
+            rows = min(r1 - j * a.C, rows) - rb;
+            lrow = j * a.C + rb - r0;
+        }
         sm.page[threadIdx.x] = page;
         sm.bias[threadIdx.x] = bias;
+        sm.rb[threadIdx.x] = rb;
         sm.rows[threadIdx.x] = rows;
+        sm.lrow[threadIdx.x] = lrow;
         sm.chunk[threadIdx.x] = j < a.kslots ? c : -1;
     }
-    // LDS rows: the raw rows of slot jj at [jj C, jj C + rows), then (selected-gist token set)
-    // the g gist rows of slot jj at [nj C + jj g, nj C + jj g + g)
-    const int graw = nj * a.C;
+    // LDS rows: row mode, row r0 + i at i; slot mode, the raw rows of slot jj at [jj C, jj C +
+    // rows), then (selected-gist token set) the g gist rows of slot jj at [nj C + jj g, ... + g)
+    const int graw = a.rpw > 0 ? r1 - r0 : nj * a.C;
     const int nrows_all = graw + (a.gk ? nj * a.g : 0);
     for (int i = threadIdx.x; i < nrows_all * G; i += 256) sm.x.lg[i] = -INFINITY;
     __syncthreads();
@@ -852,9 +978,10 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, ChunkSmem<D, G>
             rs.load_q(a.q + (long long)bh0 * D, q2);
             for (int jj = 0; jj < nj; ++jj) {
                 if (sm.page[jj] < 0) continue;
-                const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
+                const long long off =
+                    (((long long)sm.page[jj] * a.Hkv + kv) * a.C + sm.rb[jj]) * D;
                 rs.template logits<TCS_CK_U>(q2, a.kp + off, sm.rows[jj], a.sigma, sm.bias[jj],
-                                            sm.x.lg, jj * a.C);
+                                            sm.x.lg, sm.lrow[jj]);
                 if (a.gk && sm.chunk[jj] >= 0)
                     rs.template logits<TCS_CK_U>(
                         q2, a.gk + (long long)u * a.gist_stride + (long long)sm.chunk[jj] * a.g * D,
@@ -866,7 +993,8 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, ChunkSmem<D, G>
         while (sm.page[jfirst] < 0) ++jfirst;   // `any` holds: some slot has a page
         uint4 vb[TCS_CV_U];
         rs.template prefetch<TCS_CV_U>(
-            a.vp + ((long long)sm.page[jfirst] * a.Hkv + kv) * a.C * D, sm.rows[jfirst], vb);
+            a.vp + (((long long)sm.page[jfirst] * a.Hkv + kv) * a.C + sm.rb[jfirst]) * D,
+            sm.rows[jfirst], vb);
         __syncthreads();
         head_stats<G>(sm.x.lg, nrows_all, sm.hs);
         float acc[G][8];
@@ -876,9 +1004,9 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, ChunkSmem<D, G>
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
         for (int jj = jfirst; jj < nj; ++jj) {
             if (sm.page[jj] < 0) continue;
-            const long long off = ((long long)sm.page[jj] * a.Hkv + kv) * a.C * D;
-            rs.template accumulate<TCS_CV_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, jj * a.C, vb,
-                                             jj == jfirst);
+            const long long off = (((long long)sm.page[jj] * a.Hkv + kv) * a.C + sm.rb[jj]) * D;
+            rs.template accumulate<TCS_CV_U>(acc, a.vp + off, sm.rows[jj], sm.x.lg, sm.lrow[jj],
+                                             vb, jj == jfirst);
             if (a.gk && sm.chunk[jj] >= 0)
                 rs.template accumulate<TCS_CV_U>(
                     acc, a.gv + (long long)u * a.gist_stride + (long long)sm.chunk[jj] * a.g * D,
@@ -972,6 +1100,10 @@ hipError_t launch_gist(const GistLaunch& a, hipStream_t s) {
         if (!a.groups || !a.scores_only || !a.pv || a.heads) return hipErrorInvalidValue;
         return gist_mode<kGistMeta>(a, s, grid);
     }
+    if (a.selo.defer &&
+        (a.groups || a.heads || a.selo.top_p > 0.f || a.selo.fill_scores ||
+         (a.items_per_slice > 256 && a.selo.kcap < a.items_per_slice)))
+        return hipErrorInvalidValue;
     if (a.heads) {
         // range mode only; every head's scores of a slice fit the score buffer; the union
         // bitmap covers every chunk
@@ -999,7 +1131,18 @@ static hipError_t chunk_d(const ChunkLaunch& a, hipStream_t s, dim3 grid) {
 hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s) {
     if (a.cpw < 1 || a.cpw > kMaxCpw || (long long)a.cpw * a.C > kMaxSliceRows)
         return hipErrorInvalidValue;
-    dim3 grid((a.kslots + 1 + a.cpw - 1) / a.cpw, a.B * a.Hkv);
+    if (a.cand_score && (!a.cand_idx || !a.sel_out || a.ncand < 1 || a.ncand > kMaxDeferCand ||
+                         a.nslices < 1 || a.nslices > kMaxDeferCand || a.kcap < 1 ||
+                         a.ksel != a.kslots || a.sel_stride < a.ksel))
+        return hipErrorInvalidValue;
+    int nwx = (a.kslots + 1 + a.cpw - 1) / a.cpw;
+    if (a.rpw > 0) {   // row mode: no selected gists; a workgroup spans at most kMaxCpw slots
+        const long long R = (long long)a.kslots * a.C + (a.N - (long long)(a.M - 1) * a.C);
+        if (a.gk || a.rpw > kMaxSliceRows || (long long)(a.rpw + a.C - 1) / a.C + 1 > kMaxCpw)
+            return hipErrorInvalidValue;
+        nwx = (int)((R + a.rpw - 1) / a.rpw);
+    }
+    dim3 grid(nwx, a.B * a.Hkv);
     return a.d == 128 ? chunk_d<128>(a, s, grid) : chunk_d<64>(a, s, grid);
 }
 

@@ -77,14 +77,23 @@ __device__ __forceinline__ uint32_t ordered_key(float x) {
 // ---- block scans (blockDim.x == 256) ------------------------------------------------------
 struct ScanSmem { int w[4]; };
 
+// Inclusive prefix sum over the 64 lanes of a wave, all lanes active: DPP row shifts by 1, 2,
+// 4 and 8 lanes within each 16-lane row (lanes shifted in from outside the row add 0), then
+// row_bcast:15 adds the last lane of rows 0 and 2 to rows 1 and 3, and row_bcast:31 the last
+// lane of row 1 to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return x;
+}
+
 __device__ __forceinline__ int block_exclusive_scan(int v, ScanSmem& sm) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const int x = wave_inclusive_scan(v);
     if (lane == 63) sm.w[w] = x;
     __syncthreads();
     int before = 0;
@@ -294,7 +303,14 @@ __device__ int small_topk(int n, int k, ScoreFn score, EmitFn emit, SmallTopkSme
         }
         take = rank < ke;
     }
-    const int pos = block_exclusive_scan(take ? 1 : 0, sm.scan);
+    // position among the chosen: chosen lanes below in this wave (ballot), then earlier waves
+    const unsigned long long m = __ballot(take);
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+    if ((t & 63) == 0) sm.scan.w[t >> 6] = __popcll(m);
+    __syncthreads();
+    int pos = below;
+    for (int i = 0; i < (t >> 6); ++i) pos += sm.scan.w[i];
     if (take) emit(pos, t);
     __syncthreads();
     return ke;
@@ -336,10 +352,9 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, i
     }
     __syncthreads();
     const bool last = *s_flag != 0;
-    if (last) {
-        wait_vmem();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
+    // The counter was read before the barrier, so every load issued from here on follows it;
+    // the reset above needs no wait (the kernel's end drains it).
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     return last;
 }
 

@@ -27,6 +27,9 @@ struct SelectOut {
     float* fill_scores;       // optional [units][H]: -inf outside the chosen groups (level 2)
     int J, H;
     float top_p;              // > 0: keep the shortest ranked prefix with this share (k <= 256)
+    // 1: the slices only publish their lists and statistics (range mode, one list per slice,
+    // every slice ranked with the small top-k); the chunk pass ranks them (ChunkLaunch.cand_*)
+    int defer;
 };
 
 struct GistLaunch {
@@ -69,7 +72,8 @@ struct ChunkLaunch {
     const float* gamma;       // [units][k] or null
     int k;                    // stride of sel / gamma
     int kslots;               // selected-chunk slots launched (current chunk is slot kslots)
-    int cpw;                  // slots streamed per workgroup
+    int cpw;                  // slot mode: slots streamed per workgroup
+    int rpw;                  // > 0: row mode, this many rows of the slots laid end to end
     float sigma;
     Partials part;
     int slot0;
@@ -81,6 +85,16 @@ struct ChunkLaunch {
     const uint16_t* gv;
     long long gist_stride;    // elements between consecutive units' gists
     int g;
+    // deferred selection (cand_score not null): the scoring pass's per-slice lists, ranked by
+    // every workgroup of the unit in place of sel / gamma
+    const float* cand_score;  // [units][nslices][kcap]
+    const int32_t* cand_idx;
+    const float* slice_lse;   // [units][nslices][2] or null (gate off)
+    int nslices, kcap;
+    int ncand;                // candidates per unit, <= 256
+    int ksel;                 // chunks to select
+    int32_t* sel_out;         // [units][sel_stride]: written by workgroup 0 of each unit
+    int sel_stride;
 };
 
 hipError_t launch_gist(const GistLaunch& a, hipStream_t s);
