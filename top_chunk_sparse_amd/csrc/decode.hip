@@ -717,31 +717,37 @@ __device__ __forceinline__ void merge_partials(const Partials& P, int bh0, float
                                MergeSmem<G>& sm) {
     const int ns = P.nslots;
     const int tid = threadIdx.x;
-    constexpr int PPT = (G * D + 255) / 256;   // (head, column) outputs per thread
-    // slots whose values one batch holds: the unit's whole set in one round trip for the
-    // usual slot counts (up to 24 for G = 4, d = 128)
-    constexpr int SB = 48 / PPT < 32 ? 48 / PPT : 32;
+    // Thread t owns the column pairs t, t + 256, ... of the unit's G heads (pair p: head
+    // 2p / D, columns 2p % D and the next), read with 8-byte loads.  Every load is issued
+    // unconditionally, with the slot clamped to the last one (its weight is then zero), so
+    // that the whole batch is straight-line code in flight at once.
+    constexpr int NP = G * D / 2;
+    constexpr int PPT = (NP + 255) / 256;
+    constexpr int SB = 32 / PPT;   // slots per batch: the unit's whole set for the usual counts
     const bool staged = G * ns <= kMergeStage;
-    float v[PPT][SB];
+    unsigned long long v[PPT][SB];
+    auto pair_ptr = [&](int q) {
+        const int p = min(tid + q * 256, NP - 1);
+        const int h = 2 * p / D, col = 2 * p % D;
+        return reinterpret_cast<const unsigned long long*>(P.acc + (long long)(bh0 + h) * ns * D +
+                                                           col);
+    };
     auto load_batch = [&](int s0) {
 #pragma unroll
         for (int q = 0; q < PPT; ++q) {
-            const int p = tid + q * 256;
+            const unsigned long long* b = pair_ptr(q);
 #pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const int s = s0 + j;
-                v[q][j] = (p < G * D && s < ns)
-                              ? ld_shared_dev(P.acc + ((long long)(bh0 + p / D) * ns + s) * D + p % D)
-                              : 0.f;
-            }
+            for (int j = 0; j < SB; ++j)
+                v[q][j] = ld_shared_dev(b + (long long)min(s0 + j, ns - 1) * (D / 2));
         }
     };
     load_batch(0);   // in flight together with the statistics below
     if (staged) {
         for (int i = tid; i < G * ns; i += 256) {
-            const float* ml = P.ml + ((long long)(bh0 + i / ns) * ns + i % ns) * 2;
-            sm.w[i] = ld_shared_dev(ml);
-            sm.l[i] = ld_shared_dev(ml + 1);
+            const unsigned long long ml = ld_shared_dev(reinterpret_cast<const unsigned long long*>(
+                P.ml + ((long long)(bh0 + i / ns) * ns + i % ns) * 2));
+            sm.w[i] = __uint_as_float((unsigned)ml);
+            sm.l[i] = __uint_as_float((unsigned)(ml >> 32));
         }
         __syncthreads();
     }
@@ -772,23 +778,21 @@ __device__ __forceinline__ void merge_partials(const Partials& P, int bh0, float
         for (int i = tid; i < G * ns; i += 256) sm.w[i] = __expf(sm.w[i] - sm.M[i / ns]);
         __syncthreads();
     }
-    float o[PPT];
+    float o[PPT][2];
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) o[q] = 0.f;
+    for (int q = 0; q < PPT; ++q) o[q][0] = o[q][1] = 0.f;
     for (int s0 = 0; s0 < ns; s0 += SB) {
         if (s0 > 0) load_batch(s0);
 #pragma unroll
         for (int q = 0; q < PPT; ++q) {
-            const int p = tid + q * 256;
-            if (p < G * D) {
-                const int h = p / D;
+            const int h = 2 * min(tid + q * 256, NP - 1) / D;
 #pragma unroll
-                for (int j = 0; j < SB; ++j) {
-                    const int s = s0 + j;
-                    if (s < ns) {
-                        const float w = staged ? sm.w[h * ns + s] : __expf(m_at(h, s) - sm.M[h]);
-                        o[q] = fmaf(w, v[q][j], o[q]);
-                    }
+            for (int j = 0; j < SB; ++j) {
+                const int s = s0 + j;
+                if (s < ns) {
+                    const float w = staged ? sm.w[h * ns + s] : __expf(m_at(h, s) - sm.M[h]);
+                    o[q][0] = fmaf(w, __uint_as_float((unsigned)v[q][j]), o[q][0]);
+                    o[q][1] = fmaf(w, __uint_as_float((unsigned)(v[q][j] >> 32)), o[q][1]);
                 }
             }
         }
@@ -796,9 +800,11 @@ __device__ __forceinline__ void merge_partials(const Partials& P, int bh0, float
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
         const int p = tid + q * 256;
-        if (p < G * D) {
-            const int h = p / D, col = p % D;
-            out[(long long)(bh0 + h) * D + col] = o[q] / sm.L[h];
+        if (p < NP) {
+            const int h = 2 * p / D, col = 2 * p % D;
+            float* op = out + (long long)(bh0 + h) * D + col;
+            op[0] = o[q][0] / sm.L[h];
+            op[1] = o[q][1] / sm.L[h];
             if (lse && col == 0) lse[bh0 + h] = sm.M[h] + logf(sm.L[h]);
         }
     }
