@@ -65,10 +65,9 @@ struct DecodePlan {
     int G, M, H, nG, k2e, S1, cps1, S2, cps2, kslots, cpw, rpw, nwx, nslots, kcap1, kcap2;
     int sk;   // entries per unit in sel: k, or G * k with per-head selection
     int ku, k2u;   // chunks and groups selected: k and k2, or min(cap, budget) when adaptive
-    // one level, one list per slice, no top-p: the chunk pass ranks the slices' candidate lists
-    // itself (ncand1 of them per unit) and the scoring pass has no last-workgroup merge
+    // one level, one list per slice, no top-p, at most 256 candidates per unit: the slices
+    // publish their lists before their V rows and the first to finish merges them
     bool defer1;
-    int ncand1;
     float sigma;
     // workspace offsets (bytes)
     size_t off_cnt, off_cs1, off_ci1, off_lse1, off_cs2, off_ci2, off_sel, off_gamma, off_gsel,
@@ -152,14 +151,12 @@ tcs_status plan_decode(const tcs_decode_params* p, DecodePlan* pl) {
         if (heads) ksel = (int)std::min<long long>((long long)G * ksel, H);   // union size bound
     }
     pl->defer1 = false;
-    pl->ncand1 = 0;
     if (p->levels == 1 && !heads && p->top_p == 0.f && pl->S1 > 0 && pl->ku >= 1) {
         const long long last_items = H - (long long)(pl->S1 - 1) * pl->cps1;
         const long long ncand =
             (long long)(pl->S1 - 1) * pl->kcap1 + std::min<long long>(pl->ku, last_items);
-        if (ncand <= 256 && (pl->cps1 <= 256 || pl->kcap1 == pl->cps1)) {
+        if (ncand <= 256 && pl->cps1 <= 256) {
             pl->defer1 = true;
-            pl->ncand1 = (int)ncand;
         }
     }
     pl->kslots = ksel;
@@ -508,17 +505,6 @@ tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_
     ca.counter = cnt + kCntChunk;
     ca.out = out;
     ca.lse = lse;
-    if (pl.defer1) {
-        ca.cand_score = chunk_sel.cand_score;
-        ca.cand_idx = chunk_sel.cand_idx;
-        ca.slice_lse = chunk_sel.slice_lse;
-        ca.nslices = pl.S1;
-        ca.kcap = pl.kcap1;
-        ca.ncand = pl.ncand1;
-        ca.ksel = pl.kslots;
-        ca.sel_out = sel_p;
-        ca.sel_stride = pl.sk;
-    }
     if (p->gist_mode == TCS_GISTS_SELECTED) {
         ca.gk = (const uint16_t*)gist_k;
         ca.gv = (const uint16_t*)gist_v;

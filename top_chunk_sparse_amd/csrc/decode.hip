@@ -7,9 +7,9 @@
 //                 same gist rows into per-slice softmax partials with the gist values.  Each
 //                 slice publishes its best k items; the unit's top-k (section 3.3; ties to the
 //                 lower index) and, with the SAS gate on, the gate log p_c over all historical
-//                 scores ("SAS", abstract) are taken from those lists either by the unit's last
-//                 slice to finish or -- one routing level, plain top-k -- by every chunk_kernel
-//                 workgroup of the unit as it starts, so that no gist workgroup waits.
+//                 scores ("SAS", abstract) are taken from those lists by one slice of the unit:
+//                 the last to finish, or -- one routing level, plain top-k, lists published
+//                 before the V rows -- the first to finish, so that no gist workgroup waits.
 //   chunk_kernel  split-K attention over the selected chunks and the current chunk, read
 //                 through the page table (section 3.6: only the selected keys are touched);
 //                 with every gist in the token set, the rows of all slots, laid end to end,
@@ -317,15 +317,13 @@ __device__ __forceinline__ void publish_slice(const SelectOut& so, int u, int sl
     }
 }
 
-__device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
-                                const float* s_score, int item0, int nitems, int last_items,
-                                float* lse_part_lds, void* scratch, MergeCand& mc, int* s_flag,
-                                int* s_chosen, ReduceSmem& red, TopPSmem& tps, int* s_keep) {
+// The unit's selection from every slice's published list, by one workgroup that has seen all
+// of them published: the top-k of the candidates (ties to the lower item), the gate, top-p.
+__device__ __forceinline__ void merge_selection(const SelectOut& so, int u, int nslices,
+                                                int last_items, float* lse_part_lds,
+                                                void* scratch, MergeCand& mc, int* s_chosen,
+                                                TopPSmem& tps, int* s_keep) {
     const int tid = threadIdx.x;
-    publish_slice(so, u, slot, nslices, s_score, item0, nitems, scratch, red);
-    if (!arrive_last(so.counter + u, (unsigned)nslices, s_flag)) return;
-
-    // ---- last workgroup of the unit: merge ------------------------------------------------
     const float* ucs = so.cand_score + (long long)u * nslices * so.kcap;
     const int32_t* uci = so.cand_idx + (long long)u * nslices * so.kcap;
     const int ncand = (nslices - 1) * so.kcap + (so.k < last_items ? so.k : last_items);
@@ -433,6 +431,16 @@ __device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int 
     }
 }
 
+// Publish, then the last slice of the unit to arrive merges.
+__device__ __forceinline__ void select_epilogue(const SelectOut& so, int u, int slot, int nslices,
+                                const float* s_score, int item0, int nitems, int last_items,
+                                float* lse_part_lds, void* scratch, MergeCand& mc, int* s_flag,
+                                int* s_chosen, ReduceSmem& red, TopPSmem& tps, int* s_keep) {
+    publish_slice(so, u, slot, nslices, s_score, item0, nitems, scratch, red);
+    if (!arrive_last(so.counter + u, (unsigned)nslices, s_flag)) return;
+    merge_selection(so, u, nslices, last_items, lse_part_lds, scratch, mc, s_chosen, tps, s_keep);
+}
+
 // Per-head selection.  Each slice keeps, for every head h of the group, that head's top-k of
 // its items in the hand-off lists [unit][h][slice][kcap] (one head's lists are contiguous).
 // The last workgroup of the unit merges each head's lists into that head's top-k, marks the
@@ -532,7 +540,7 @@ struct GistSmem {
     } x;
     float score[kMaxSliceRows];   // also the top-p staging of the last workgroup
     union {
-        MergeCand mc;             // the last workgroup's staged candidates
+        MergeCand mc;             // the merging workgroup's staged candidates
         SmallTopkSmem pub;        // deferred selection: the slice top-k, taken before the V rows
     } m;
     HeadStatsSmem<G> hs;
@@ -644,12 +652,36 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
     }
     if constexpr (MODE == kGistPlain) {
         if (a.selo.defer) {
-            // The chunk pass ranks the slices' lists itself: publish this slice's list now,
-            // while the first V batch travels, and end with the gist partial -- no workgroup
-            // waits for the others here.
+            // Publish this slice's list now, while the first V batch travels; the unit's
+            // selection is merged by its first slice to finish (which has seen every list
+            // published), so no workgroup waits for another.  The unit's counter word holds
+            // the published slices in its low half and the finished ones in its high half.
             __syncthreads();   // every pooled score is in sm.score
             publish_slice(a.selo, u, y, a.slices, sm.score, c0, nit, &sm.m.pub, sm.red);
+            unsigned* cnt = a.selo.counter + u;
+            const unsigned S = (unsigned)a.slices;
+            // count the list once every wave's part of it is out
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            wait_vmem();
+            __syncthreads();
+            unsigned old_p = 0u;
+            if (threadIdx.x == 0) old_p = atomicAdd(cnt, 1u);
             if (!a.scores_only) fold_rows<D, G>(sm, a.part, V, nrows, vfirst, bh0, a.slot0 + y);
+            if (threadIdx.x == 0) {
+                const unsigned old_f = atomicAdd(cnt, 1u << 16);
+                // the first to finish once every list is out merges; if some slice finished
+                // before the last list was out, the slice that put it out merges instead
+                const bool merge = ((old_f >> 16) == 0u && (old_f & 0xFFFFu) == S) ||
+                                   ((old_p & 0xFFFFu) == S - 1u && (old_p >> 16) != 0u);
+                if ((old_f >> 16) == S - 1u) atomicExch(cnt, 0u);   // every slice is through
+                sm.flag = merge;
+            }
+            __syncthreads();
+            if (sm.flag) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                merge_selection(a.selo, u, a.slices, last_items, &sm.lse, &sm.x, sm.m.mc,
+                                sm.chosen, *reinterpret_cast<TopPSmem*>(sm.score), &sm.tp_keep);
+            }
             return;
         }
     }
@@ -818,21 +850,12 @@ __device__ __forceinline__ void merge_partials(const Partials& P, int bh0, float
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxCpw = 16;
 
-constexpr int kMaxDeferCand = 256;   // deferred selection: candidates ranked in LDS
-
-struct RankSmem {
-    MergeCand mc;
-    SmallTopkSmem st;
-    ReduceSmem red;
-};
-
 template <int D, int G>
 struct ChunkSmem {
     union {
         float lg[kMaxSliceRows * G];
         float fin[RowStream<D, G>::NW * G * D];
         MergeSmem<G> merge;
-        RankSmem rank;
     } x;
     HeadStatsSmem<G> hs;
     int page[kMaxCpw];
@@ -843,66 +866,6 @@ struct ChunkSmem {
     int chunk[kMaxCpw];   // selected chunk of the slot, -1 for the current chunk
     int flag;
 };
-
-// Deferred selection: every workgroup of the unit ranks the scoring pass's per-slice lists
-// (ascending chunk ids, slice after slice) as that pass's last workgroup would -- the top
-// min(k, n) by score, ties to the lower chunk id, gate log p = score - log-sum-exp of every
-// historical score -- and keeps the chunks and gate biases of its own slots [j0, j0 + nj) in
-// sm.chunk / sm.bias.  Workgroup 0 also writes the unit's selection out.
-template <int D, int G>
-__device__ __forceinline__ void rank_candidates(const ChunkLaunch& a, ChunkSmem<D, G>& sm, int u,
-                                                int wx, int j0, int nj) {
-    RankSmem& rk = sm.x.rank;
-    const int tid = threadIdx.x;
-    const int n = a.ncand;
-    // every hand-off value in one round trip: thread t holds candidate t and slice t's
-    // (max, sum exp) pair
-    const long long base = (long long)u * a.nslices * a.kcap;
-    float cs = 0.f;
-    int32_t ci = 0;
-    float2 pr = make_float2(-INFINITY, 0.f);
-    if (tid < n) {
-        cs = a.cand_score[base + tid];
-        ci = a.cand_idx[base + tid];
-    }
-    if (a.slice_lse && tid < a.nslices)
-        pr = *reinterpret_cast<const float2*>(a.slice_lse + ((long long)u * a.nslices + tid) * 2);
-    if (tid < n) {
-        rk.mc.score[tid] = cs;
-        rk.mc.idx[tid] = ci;
-    }
-    if (tid < nj) {
-        sm.chunk[tid] = -1;
-        sm.bias[tid] = 0.f;
-    }
-    float lse = 0.f;
-    if (a.slice_lse) {   // log-sum-exp of every historical score, from the slices' statistics
-        const float mx = block_max(pr.x, rk.red);
-        const float z = block_sum(tid < a.nslices ? pr.y * expf(pr.x - mx) : 0.f, rk.red);
-        lse = mx + logf(z);
-    } else {
-        __syncthreads();
-    }
-    int32_t* sel = a.sel_out + (long long)u * a.sel_stride;
-    auto emit = [&](int j, int i) {
-        const int32_t c = rk.mc.idx[i];
-        if (wx == 0) sel[j] = c;
-        if (j >= j0 && j < j0 + nj) {
-            sm.chunk[j - j0] = c;
-            sm.bias[j - j0] = a.slice_lse ? rk.mc.score[i] - lse : 0.f;
-        }
-    };
-    int ke;
-    if (a.ksel >= n) {
-        for (int i = tid; i < n; i += 256) emit(i, i);
-        ke = n;
-    } else {
-        ke = small_topk(n, a.ksel, [&](int i) { return rk.mc.score[i]; }, emit, rk.st);
-    }
-    if (wx == 0)
-        for (int j = ke + tid; j < a.sel_stride; j += 256) sel[j] = -1;
-    __syncthreads();   // sm.chunk / sm.bias complete; the union is free again
-}
 
 // Workgroup wx of unit u (nwx workgroups per unit).
 template <int D, int G>
@@ -925,20 +888,14 @@ __device__ __forceinline__ void chunk_item(const ChunkLaunch& a, ChunkSmem<D, G>
         j0 = wx * a.cpw;
         nj = min(a.cpw, a.kslots + 1 - j0);
     }
-    if (a.cand_score) rank_candidates<D, G>(a, sm, u, wx, j0, nj);
     // this workgroup's chunks: page, gate bias and rows (page -1: none, -2: out of range)
     if (threadIdx.x < nj) {
         const int j = j0 + threadIdx.x;
         int c, rows;
         float bias = 0.f;
         if (j < a.kslots) {
-            if (a.cand_score) {
-                c = sm.chunk[threadIdx.x];
-                bias = sm.bias[threadIdx.x];
-            } else {
-                c = a.sel[(long long)u * a.k + j];
-                if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
-            }
+            c = a.sel[(long long)u * a.k + j];
+            if (c >= 0 && a.gamma) bias = a.gamma[(long long)u * a.k + j];
             rows = a.C;
         } else {
             c = a.M - 1;
@@ -1106,9 +1063,8 @@ hipError_t launch_gist(const GistLaunch& a, hipStream_t s) {
         if (!a.groups || !a.scores_only || !a.pv || a.heads) return hipErrorInvalidValue;
         return gist_mode<kGistMeta>(a, s, grid);
     }
-    if (a.selo.defer &&
-        (a.groups || a.heads || a.selo.top_p > 0.f || a.selo.fill_scores ||
-         (a.items_per_slice > 256 && a.selo.kcap < a.items_per_slice)))
+    if (a.selo.defer && (a.groups || a.heads || a.selo.top_p > 0.f || a.selo.fill_scores ||
+                         a.items_per_slice > 256 || a.slices > 0xFFFF))
         return hipErrorInvalidValue;
     if (a.heads) {
         // range mode only; every head's scores of a slice fit the score buffer; the union
@@ -1136,10 +1092,6 @@ static hipError_t chunk_d(const ChunkLaunch& a, hipStream_t s, dim3 grid) {
 
 hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s) {
     if (a.cpw < 1 || a.cpw > kMaxCpw || (long long)a.cpw * a.C > kMaxSliceRows)
-        return hipErrorInvalidValue;
-    if (a.cand_score && (!a.cand_idx || !a.sel_out || a.ncand < 1 || a.ncand > kMaxDeferCand ||
-                         a.nslices < 1 || a.nslices > kMaxDeferCand || a.kcap < 1 ||
-                         a.ksel != a.kslots || a.sel_stride < a.ksel))
         return hipErrorInvalidValue;
     int nwx = (a.kslots + 1 + a.cpw - 1) / a.cpw;
     if (a.rpw > 0) {   // row mode: no selected gists; a workgroup spans at most kMaxCpw slots

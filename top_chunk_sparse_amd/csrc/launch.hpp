@@ -27,8 +27,9 @@ struct SelectOut {
     float* fill_scores;       // optional [units][H]: -inf outside the chosen groups (level 2)
     int J, H;
     float top_p;              // > 0: keep the shortest ranked prefix with this share (k <= 256)
-    // 1: the slices only publish their lists and statistics (range mode, one list per slice,
-    // every slice ranked with the small top-k); the chunk pass ranks them (ChunkLaunch.cand_*)
+    // 1: each slice publishes its list and statistics before its V rows (range mode, at most
+    // 256 items a slice), and the unit's first slice to finish merges them: counter[u] then
+    // counts published slices in its low half and finished ones in its high half
     int defer;
 };
 
@@ -85,16 +86,6 @@ struct ChunkLaunch {
     const uint16_t* gv;
     long long gist_stride;    // elements between consecutive units' gists
     int g;
-    // deferred selection (cand_score not null): the scoring pass's per-slice lists, ranked by
-    // every workgroup of the unit in place of sel / gamma
-    const float* cand_score;  // [units][nslices][kcap]
-    const int32_t* cand_idx;
-    const float* slice_lse;   // [units][nslices][2] or null (gate off)
-    int nslices, kcap;
-    int ncand;                // candidates per unit, <= 256
-    int ksel;                 // chunks to select
-    int32_t* sel_out;         // [units][sel_stride]: written by workgroup 0 of each unit
-    int sel_stride;
 };
 
 hipError_t launch_gist(const GistLaunch& a, hipStream_t s);
