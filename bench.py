@@ -330,6 +330,24 @@ def cpu_baseline_gist_prefill(inp, budget_s):
             "choice", "seconds": round(dt, 3), "cpu": cpu_model()}
 
 
+def kernel_times(torch, stream, call, steps, nst):
+    """Average duration (ms) of each of a call's nst kernels over `steps` calls: the library
+    records a pair of events at each kernel's own start and end (the timed entry points)."""
+    import ctypes
+    evs = []
+    for _ in range(steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)]
+        for e in row:
+            e.record(stream)             # creates the underlying hipEvent_t
+        evs.append(row)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        call(i, (ctypes.c_void_p * (2 * nst))(*[e.cuda_event for e in evs[i]]))
+    torch.cuda.synchronize()
+    return [sum(evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(steps)) / steps
+            for j in range(nst)]
+
+
 def load_traffic(kernel_name, workload):
     """HBM traffic per launch from committed rocprofv3 counter runs, only if the kernel
     sources are unchanged since the counters were taken."""
@@ -374,20 +392,7 @@ def run_prefill(args, torch, configs, ops):
     print("# warmup done", file=sys.stderr, flush=True)
     tm = timing_summary(torch, stream, lambda i: calls[i % R](), args.steps)
     ms_per_step = tm["ms_per_step"]
-    # per-kernel durations: back-to-back calls with events between the two kernels
-    evs = []
-    for _ in range(args.steps):
-        row = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        for e in row:
-            e.record(stream)
-        evs.append(row)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        arr = (ctypes.c_void_p * 3)(*[e.cuda_event for e in evs[i]])
-        calls[i % R](events=arr)
-    torch.cuda.synchronize()
-    stage_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-                for j in range(2)]
+    stage_ms = kernel_times(torch, stream, lambda i, arr: calls[i % R](events=arr), args.steps, 2)
     print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
     flops = prefill_flops(cfg)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -452,19 +457,8 @@ def run_gist_prefill(args, torch, configs, ops):
     print("# warmup done", file=sys.stderr, flush=True)
     tm = timing_summary(torch, stream, lambda i: calls[i % R](), args.steps)
     ms_per_step = tm["ms_per_step"]
-    nst = 3   # gist gather, raw query rows, gist query rows
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
-           for _ in range(args.steps)]
-    for row in evs:
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        arr = (ctypes.c_void_p * (nst + 1))(*[e.cuda_event for e in evs[i]])
-        calls[i % R](events=arr)
-    torch.cuda.synchronize()
-    stage_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-                for j in range(nst)]
+    # gist gather, raw query rows, gist query rows
+    stage_ms = kernel_times(torch, stream, lambda i, arr: calls[i % R](events=arr), args.steps, 3)
     print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
     raw_pairs, gist_pairs = gist_prefill_pairs(cfg)
     flops = 4 * cfg.d * (raw_pairs + gist_pairs)
@@ -531,20 +525,8 @@ def run_prefill_backward(args, torch, configs, ops):
     print("# warmup done", file=sys.stderr, flush=True)
     tm = timing_summary(torch, stream, lambda i: calls[i % R](), args.steps)
     ms_per_step = tm["ms_per_step"]
-    # per-kernel durations: events between the stages (select, prep, dq, dk / dv, dS)
-    nst = 5
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
-           for _ in range(args.steps)]
-    for row in evs:
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        arr = (ctypes.c_void_p * (nst + 1))(*[e.cuda_event for e in evs[i]])
-        calls[i % R](events=arr)
-    torch.cuda.synchronize()
-    stage_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-                for j in range(nst)]
+    # per-kernel durations: select, prep, dq, dk / dv, dS
+    stage_ms = kernel_times(torch, stream, lambda i, arr: calls[i % R](events=arr), args.steps, 5)
     print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
     flops = prefill_bwd_flops(cfg)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -677,22 +659,9 @@ def main():
     # warm: the same loops on instance 0 alone (its data partly held by the 256 MB cache)
     warm = timing_summary(torch, stream, lambda i: calls[0](), args.steps)
 
-    # ---- per-kernel durations: the same K calls with events between the kernels ------
+    # ---- per-kernel durations: the same K calls, each kernel bracketed by its own events ----
     nst = ops.decode_stage_count(calls[0].p)
-    import ctypes
-    evs = []
-    for _ in range(args.steps):
-        row = [torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
-        for e in row:
-            e.record(stream)             # creates the underlying hipEvent_t
-        evs.append(row)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        arr = (ctypes.c_void_p * (nst + 1))(*[e.cuda_event for e in evs[i]])
-        calls[i % R](events=arr)
-    torch.cuda.synchronize()
-    stage_ms = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-                for j in range(nst)]
+    stage_ms = kernel_times(torch, stream, lambda i, arr: calls[i % R](events=arr), args.steps, nst)
     print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
 
     k_eff_mean = None

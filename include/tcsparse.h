@@ -152,7 +152,7 @@
 extern "C" {
 #endif
 
-#define TCS_ABI_VERSION 7
+#define TCS_ABI_VERSION 8
 
 typedef enum {
     TCS_OK = 0,
@@ -205,13 +205,14 @@ tcs_status sparse_attn_decode(const tcs_decode_params* p,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Profiling variant of sparse_attn_decode: identical work and results, and in addition it
- * records caller-created HIP events (hipEvent_t, passed as void*) on `stream`: events[0]
- * before the first kernel and events[i] after the i-th stage.  levels = 1: stage 1 gist
- * scoring with chunk selection, stage 2 chunk attention with the final merge.  levels = 2:
- * stage 1 level-2 scoring with group selection, stage 2 candidate scoring with chunk
- * selection, stage 3 chunk attention with the final merge.  Entries beyond n_events, or NULL
- * entries, are skipped.  For profiling tools: recording events between kernels adds a
- * little time to the call. */
+ * has caller-created HIP events (hipEvent_t, passed as void*) recorded at the start and the
+ * end of each stage's kernel: events[2 i] and events[2 i + 1] for stage i, taken by the kernel
+ * launch itself (hipExtLaunchKernel), so that they bracket that kernel alone; a stage that
+ * runs no kernel (nothing to score) records both at that point of `stream`.  levels = 1:
+ * stage 0 gist scoring with chunk selection, stage 1 chunk attention with the final merge.
+ * levels = 2: stage 0 level-2 scoring with group selection, stage 1 candidate scoring with
+ * chunk selection, stage 2 chunk attention with the final merge.  Entries beyond n_events,
+ * or NULL entries, are skipped. */
 tcs_status sparse_attn_decode_timed(const tcs_decode_params* p,
                                     const void* q,
                                     const void* k_pages, const void* v_pages,
@@ -245,7 +246,7 @@ tcs_status sparse_attn_decode_noalloc(const tcs_decode_params* p,
                                       int32_t* sel, int32_t* sel_groups, float* chunk_scores,
                                       void* stream);
 
-/* Number of stages sparse_attn_decode_timed brackets with events for these parameters
+/* Number of stages sparse_attn_decode_timed brackets with event pairs for these parameters
  * (2 for one level, 3 for two levels), -1 if the parameters are invalid.  Host-only. */
 int tcs_decode_stage_count(const tcs_decode_params* p);
 
@@ -272,8 +273,8 @@ tcs_status sparse_attn_prefill(const tcs_prefill_params* p,
                                float* out, float* lse, int32_t* sel,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Profiling variant of sparse_attn_prefill (see sparse_attn_decode_timed): events[0] before
- * the first kernel, events[1] after block selection, events[2] after the attention forward. */
+/* Profiling variant of sparse_attn_prefill (events as in sparse_attn_decode_timed, a pair per
+ * stage): stage 0 block selection (no kernel when k = 0), stage 1 the attention forward. */
 tcs_status sparse_attn_prefill_timed(const tcs_prefill_params* p,
                                      const void* q, const void* k, const void* v,
                                      const float* S,
@@ -294,9 +295,11 @@ tcs_status sparse_attn_prefill_backward(const tcs_prefill_params* p,
                                         float* dq, float* dk, float* dv, float* dS,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Profiling variant of sparse_attn_prefill_backward: events[0] before the first kernel, then
- * after block selection (1), the row terms D and the chosen-by lists (2), the dq kernel (3),
- * the dk / dv kernel (4) and the dS kernel (5). */
+/* Profiling variant of sparse_attn_prefill_backward (a pair of events per stage, as in
+ * sparse_attn_decode_timed): stage 0 block selection, stage 1 the row terms D and the
+ * chosen-by lists (two kernels, from the start of the first to the end of the second),
+ * stage 2 the dq kernel, stage 3 the dk / dv kernel, stage 4 the dS kernel (none without
+ * dS). */
 tcs_status sparse_attn_prefill_backward_timed(const tcs_prefill_params* p,
                                               const void* q, const void* k, const void* v,
                                               const float* S, const float* out,
@@ -323,8 +326,8 @@ tcs_status sparse_attn_gist_prefill(const tcs_gist_prefill_params* p,
                                     float* out, float* lse,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Profiling variant: events[0] before the first kernel, then after the gist gather (1), the
- * raw query rows (2) and the gist query rows (3). */
+/* Profiling variant (a pair of events per stage, as in sparse_attn_decode_timed): stage 0 the
+ * gist gather, stage 1 the raw query rows, stage 2 the gist query rows. */
 tcs_status sparse_attn_gist_prefill_timed(const tcs_gist_prefill_params* p,
                                           const void* q, const void* k, const void* v,
                                           float* out, float* lse, void* workspace,

@@ -43,6 +43,22 @@ constexpr int kMaxHeadSelectChunks = 65536;   // per-head selection: union bitma
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Events of the profiling entry points: events[2 i] and events[2 i + 1] are recorded by the
+// launch of stage i at its kernel's own start and end (hipExtLaunchKernel); entries past
+// n_events or null are skipped.
+struct StageEvents {
+    void* const* ev;
+    int n;
+    int stage = 0;
+    tcs::KernelEvents next() {
+        tcs::KernelEvents k;
+        const int i = 2 * stage++;
+        if (ev && i < n && ev[i]) k.start = (hipEvent_t)ev[i];
+        if (ev && i + 1 < n && ev[i + 1]) k.stop = (hipEvent_t)ev[i + 1];
+        return k;
+    }
+};
+
 bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 
 // Split `nchunks` chunks of `g` rows into slices for the gist kernel: enough workgroups to
@@ -365,15 +381,7 @@ tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_
     if (st != TCS_OK) return st;
 
     hipStream_t s = (hipStream_t)stream;
-    int stage = 0;
-    auto mark = [&]() -> bool {   // record events[stage] (if the caller gave one)
-        if (stage < n_events && events && events[stage]) {
-            if (hipEventRecord((hipEvent_t)events[stage], s) != hipSuccess) return false;
-        }
-        ++stage;
-        return true;
-    };
-    if (!mark()) return TCS_ERR_HIP;
+    StageEvents clk{events, n_events};
     char* ws = (char*)workspace;
     const int units = p->B * p->Hkv;
     const int cap = p->gist_cap > 0 ? p->gist_cap : pl.H;
@@ -422,8 +430,8 @@ tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_
         ga.selo = chunk_sel;
         ga.scores_only = p->gist_mode == TCS_GISTS_SELECTED;
         ga.heads = p->select_mode == TCS_SELECT_PER_HEAD;
-        e = tcs::launch_gist(ga, s);
-        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+        e = tcs::launch_gist(ga, s, clk.next());
+        if (e != hipSuccess) return TCS_ERR_HIP;
         if (!ga.scores_only) slot += pl.S1;
         chunks_chosen = pl.S1 > 0;
     } else {
@@ -452,8 +460,8 @@ tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_
         ga.slot0 = slot;
         ga.selo = gs;
         ga.scores_only = p->gist_mode == TCS_GISTS_SELECTED;
-        e = tcs::launch_gist(ga, s);
-        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+        e = tcs::launch_gist(ga, s, clk.next());
+        if (e != hipSuccess) return TCS_ERR_HIP;
         if (!ga.scores_only) slot += pl.S2;
         if (pl.S2 == 0 && sel_groups && p->k2 > 0) {
             e = tcs::launch_fill(sel_groups, (long long)units * p->k2, -1, s);
@@ -481,8 +489,8 @@ tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_
             ga.pv = (const uint16_t*)gist2_v;
             ga.p_unit_stride = (long long)pl.nG * p->g * p->d;
         }
-        e = tcs::launch_gist(ga, s);
-        if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+        e = tcs::launch_gist(ga, s, clk.next());
+        if (e != hipSuccess) return TCS_ERR_HIP;
         slot += pl.k2e;
         chunks_chosen = pl.k2e > 0;
     }
@@ -511,8 +519,8 @@ tcs_status decode_impl(const tcs_decode_params* p, const void* q, const void* k_
         ca.gist_stride = (long long)cap * p->g * p->d;
         ca.g = p->g;
     }
-    e = tcs::launch_chunks(ca, s);
-    if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+    e = tcs::launch_chunks(ca, s, clk.next());
+    if (e != hipSuccess) return TCS_ERR_HIP;
     return TCS_OK;
 }
 
@@ -589,25 +597,16 @@ static tcs_status prefill_impl(const tcs_prefill_params* p, const void* q, const
     st = check_ws(workspace, workspace_bytes, pl.total);
     if (st != TCS_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    int stage = 0;
-    auto mark = [&]() -> bool {
-        if (stage < n_events && events && events[stage]) {
-            if (hipEventRecord((hipEvent_t)events[stage], s) != hipSuccess) return false;
-        }
-        ++stage;
-        return true;
-    };
-    if (!mark()) return TCS_ERR_HIP;
+    StageEvents clk{events, n_events};
     char* ws = (char*)workspace;
     const int units = p->B * p->Hkv;
     const int kk = p->k > 0 ? p->k : 0;
     int32_t* sel_p = sel ? sel : (int32_t*)(ws + pl.off_sel);
     float* gamma = p->gate_mode == TCS_GATE_SAS ? (float*)(ws + pl.off_gamma) : nullptr;
-    if (kk > 0) {
+    {   // with k = 0 no selection kernel runs (its events are still recorded)
         tcs::PrefillSelectLaunch ps{S, units, pl.nb, kk, sel_p, gamma};
-        if (tcs::launch_prefill_select(ps, s) != hipSuccess) return TCS_ERR_HIP;
+        if (tcs::launch_prefill_select(ps, s, clk.next()) != hipSuccess) return TCS_ERR_HIP;
     }
-    if (!mark()) return TCS_ERR_HIP;
     tcs::PrefillLaunch pa{};
     pa.q = (const uint16_t*)q;
     pa.k = (const uint16_t*)k;
@@ -619,9 +618,9 @@ static tcs_status prefill_impl(const tcs_prefill_params* p, const void* q, const
     pa.sigma = pl.sigma;
     pa.out = out;
     pa.lse = lse;
-    hipError_t e = tcs::launch_prefill(pa, s);
+    hipError_t e = tcs::launch_prefill(pa, s, clk.next());
     if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
-    if (e != hipSuccess || !mark()) return TCS_ERR_HIP;
+    if (e != hipSuccess) return TCS_ERR_HIP;
     return TCS_OK;
 }
 
@@ -645,15 +644,7 @@ static tcs_status gist_prefill_impl(const tcs_gist_prefill_params* p, const void
     st = check_ws(workspace, workspace_bytes, pl.total);
     if (st != TCS_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    int stage = 0;
-    auto mark = [&]() -> bool {
-        if (stage < n_events && events && events[stage]) {
-            if (hipEventRecord((hipEvent_t)events[stage], s) != hipSuccess) return false;
-        }
-        ++stage;
-        return true;
-    };
-    if (!mark()) return TCS_ERR_HIP;
+    StageEvents clk{events, n_events};
     char* ws = (char*)workspace;
     tcs::GistPrefillLaunch a{};
     a.q = (const uint16_t*)q;
@@ -666,12 +657,9 @@ static tcs_status gist_prefill_impl(const tcs_gist_prefill_params* p, const void
     a.sigma = pl.sigma;
     a.out = out;
     a.lse = lse;
-    hipError_t e = tcs::launch_gist_gather(a, s);
-    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
-    if (e == hipSuccess) e = tcs::launch_gist_prefill_raw(a, s);
-    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
-    if (e == hipSuccess) e = tcs::launch_gist_prefill_gists(a, s);
-    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
+    hipError_t e = tcs::launch_gist_gather(a, s, clk.next());
+    if (e == hipSuccess) e = tcs::launch_gist_prefill_raw(a, s, clk.next());
+    if (e == hipSuccess) e = tcs::launch_gist_prefill_gists(a, s, clk.next());
     if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
     return e == hipSuccess ? TCS_OK : TCS_ERR_HIP;
 }
@@ -715,25 +703,16 @@ static tcs_status prefill_backward_impl(const tcs_prefill_params* p, const void*
     st = check_ws(workspace, workspace_bytes, pl.total);
     if (st != TCS_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    int stage = 0;
-    auto mark = [&]() -> bool {
-        if (stage < n_events && events && events[stage]) {
-            if (hipEventRecord((hipEvent_t)events[stage], s) != hipSuccess) return false;
-        }
-        ++stage;
-        return true;
-    };
-    if (!mark()) return TCS_ERR_HIP;
+    StageEvents clk{events, n_events};
     char* ws = (char*)workspace;
     const int units = p->B * p->Hkv;
     const int kk = p->k > 0 ? p->k : 0;
     int32_t* sel = (int32_t*)(ws + pl.f.off_sel);
     float* gamma = p->gate_mode == TCS_GATE_SAS ? (float*)(ws + pl.f.off_gamma) : nullptr;
-    if (kk > 0) {
+    {   // with k = 0 no selection kernel runs (its events are still recorded)
         tcs::PrefillSelectLaunch ps{S, units, pl.f.nb, kk, sel, gamma};
-        if (tcs::launch_prefill_select(ps, s) != hipSuccess) return TCS_ERR_HIP;
+        if (tcs::launch_prefill_select(ps, s, clk.next()) != hipSuccess) return TCS_ERR_HIP;
     }
-    if (!mark()) return TCS_ERR_HIP;
     tcs::PrefillBwdLaunch a{};
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
@@ -758,14 +737,10 @@ static tcs_status prefill_backward_impl(const tcs_prefill_params* p, const void*
     a.dk = dk;
     a.dv = dv;
     a.dS = dS;
-    hipError_t e = tcs::launch_prefill_bwd_prep(a, s);
-    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
-    if (e == hipSuccess) e = tcs::launch_prefill_bwd_dq(a, s);
-    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
-    if (e == hipSuccess) e = tcs::launch_prefill_bwd_dkv(a, s);
-    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
-    if (e == hipSuccess) e = tcs::launch_prefill_bwd_ds(a, s);
-    if (e == hipSuccess && !mark()) e = hipErrorUnknown;
+    hipError_t e = tcs::launch_prefill_bwd_prep(a, s, clk.next());
+    if (e == hipSuccess) e = tcs::launch_prefill_bwd_dq(a, s, clk.next());
+    if (e == hipSuccess) e = tcs::launch_prefill_bwd_dkv(a, s, clk.next());
+    if (e == hipSuccess) e = tcs::launch_prefill_bwd_ds(a, s, clk.next());
     if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
     return e == hipSuccess ? TCS_OK : TCS_ERR_HIP;
 }

@@ -1040,28 +1040,28 @@ hipError_t launch_stream_read(const void* p, size_t bytes, unsigned* sink, int b
 // launchers
 // ---------------------------------------------------------------------------------------
 template <int D, int MODE>
-static hipError_t gist_d(const GistLaunch& a, hipStream_t s, dim3 grid) {
+static hipError_t gist_d(const GistLaunch& a, hipStream_t s, dim3 grid, const KernelEvents& ev) {
     switch (a.Hq / a.Hkv) {
-        case 1: gist_kernel<D, 1, MODE><<<grid, 256, 0, s>>>(a); break;
-        case 2: gist_kernel<D, 2, MODE><<<grid, 256, 0, s>>>(a); break;
-        case 4: gist_kernel<D, 4, MODE><<<grid, 256, 0, s>>>(a); break;
-        case 8: gist_kernel<D, 8, MODE><<<grid, 256, 0, s>>>(a); break;
+        case 1: return dispatch(gist_kernel<D, 1, MODE>, grid, dim3(256), 0, s, ev, a);
+        case 2: return dispatch(gist_kernel<D, 2, MODE>, grid, dim3(256), 0, s, ev, a);
+        case 4: return dispatch(gist_kernel<D, 4, MODE>, grid, dim3(256), 0, s, ev, a);
+        case 8: return dispatch(gist_kernel<D, 8, MODE>, grid, dim3(256), 0, s, ev, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int MODE>
-static hipError_t gist_mode(const GistLaunch& a, hipStream_t s, dim3 grid) {
-    return a.d == 128 ? gist_d<128, MODE>(a, s, grid) : gist_d<64, MODE>(a, s, grid);
+static hipError_t gist_mode(const GistLaunch& a, hipStream_t s, dim3 grid,
+                            const KernelEvents& ev) {
+    return a.d == 128 ? gist_d<128, MODE>(a, s, grid, ev) : gist_d<64, MODE>(a, s, grid, ev);
 }
 
-hipError_t launch_gist(const GistLaunch& a, hipStream_t s) {
-    if (a.slices <= 0) return hipSuccess;
+hipError_t launch_gist(const GistLaunch& a, hipStream_t s, const KernelEvents& ev) {
+    if (a.slices <= 0) return no_kernel(ev, s);
     dim3 grid(a.slices, a.B * a.Hkv);
     if (a.pk) {   // only group mode with scores_only carries level-2 gists for the partials
         if (!a.groups || !a.scores_only || !a.pv || a.heads) return hipErrorInvalidValue;
-        return gist_mode<kGistMeta>(a, s, grid);
+        return gist_mode<kGistMeta>(a, s, grid, ev);
     }
     if (a.selo.defer && (a.groups || a.heads || a.selo.top_p > 0.f || a.selo.fill_scores ||
                          a.items_per_slice > 256 || a.slices > 0xFFFF))
@@ -1073,24 +1073,24 @@ hipError_t launch_gist(const GistLaunch& a, hipStream_t s) {
         if (a.groups || (long long)a.items_per_slice * G > kMaxSliceRows ||
             a.nitems > kMaxHeadWords * 32 || a.selo.H != a.nitems)
             return hipErrorInvalidValue;
-        return gist_mode<kGistHeads>(a, s, grid);
+        return gist_mode<kGistHeads>(a, s, grid, ev);
     }
-    return gist_mode<kGistPlain>(a, s, grid);
+    return gist_mode<kGistPlain>(a, s, grid, ev);
 }
 
 template <int D>
-static hipError_t chunk_d(const ChunkLaunch& a, hipStream_t s, dim3 grid) {
+static hipError_t chunk_d(const ChunkLaunch& a, hipStream_t s, dim3 grid,
+                          const KernelEvents& ev) {
     switch (a.Hq / a.Hkv) {
-        case 1: chunk_kernel<D, 1><<<grid, 256, 0, s>>>(a); break;
-        case 2: chunk_kernel<D, 2><<<grid, 256, 0, s>>>(a); break;
-        case 4: chunk_kernel<D, 4><<<grid, 256, 0, s>>>(a); break;
-        case 8: chunk_kernel<D, 8><<<grid, 256, 0, s>>>(a); break;
+        case 1: return dispatch(chunk_kernel<D, 1>, grid, dim3(256), 0, s, ev, a);
+        case 2: return dispatch(chunk_kernel<D, 2>, grid, dim3(256), 0, s, ev, a);
+        case 4: return dispatch(chunk_kernel<D, 4>, grid, dim3(256), 0, s, ev, a);
+        case 8: return dispatch(chunk_kernel<D, 8>, grid, dim3(256), 0, s, ev, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
-hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s) {
+hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s, const KernelEvents& ev) {
     if (a.cpw < 1 || a.cpw > kMaxCpw || (long long)a.cpw * a.C > kMaxSliceRows)
         return hipErrorInvalidValue;
     int nwx = (a.kslots + 1 + a.cpw - 1) / a.cpw;
@@ -1101,7 +1101,7 @@ hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s) {
         nwx = (int)((R + a.rpw - 1) / a.rpw);
     }
     dim3 grid(nwx, a.B * a.Hkv);
-    return a.d == 128 ? chunk_d<128>(a, s, grid) : chunk_d<64>(a, s, grid);
+    return a.d == 128 ? chunk_d<128>(a, s, grid, ev) : chunk_d<64>(a, s, grid, ev);
 }
 
 hipError_t launch_fill(int32_t* p, long long n, int32_t v, hipStream_t s) {

@@ -2,6 +2,7 @@
 // bf16 unpacking, DPP row reductions, order-preserving float keys, block-wide scans and the
 // deterministic top-k used for chunk / block selection.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -356,6 +357,30 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, i
     // the reset above needs no wait (the kernel's end drains it).
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     return last;
+}
+
+// ---- launches --------------------------------------------------------------------------------
+// Launch kernel(a) on s; with an event of ev set, through hipExtLaunchKernel, which records
+// the events at the kernel's own start and end.
+template <class A, class E>
+inline hipError_t dispatch(void (*kernel)(A), dim3 grid, dim3 block, uint32_t shmem,
+                           hipStream_t s, const E& ev, const A& a) {
+    if (ev.start || ev.stop) {
+        void* args[] = {const_cast<A*>(&a)};
+        return hipExtLaunchKernel((const void*)kernel, grid, block, args, shmem, s, ev.start,
+                                  ev.stop, 0);
+    }
+    kernel<<<grid, block, shmem, s>>>(a);
+    return hipGetLastError();
+}
+
+// A launcher that runs no kernel records ev's events back to back.
+template <class E>
+inline hipError_t no_kernel(const E& ev, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    if (ev.start) e = hipEventRecord(ev.start, s);
+    if (e == hipSuccess && ev.stop) e = hipEventRecord(ev.stop, s);
+    return e;
 }
 
 }  // namespace tcs

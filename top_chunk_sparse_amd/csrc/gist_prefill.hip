@@ -276,42 +276,44 @@ static hipError_t gist_check(const GistPrefillLaunch& a) {
     return hipSuccess;
 }
 
-hipError_t launch_gist_gather(const GistPrefillLaunch& a, hipStream_t s) {
+hipError_t launch_gist_gather(const GistPrefillLaunch& a, hipStream_t s,
+                              const KernelEvents& ev) {
     hipError_t e = gist_check(a);
     if (e != hipSuccess) return e;
     const long long W = (long long)a.B * a.Hkv * (a.Gp / kPBlk);
-    if (W <= 0) return hipSuccess;
+    if (W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    gist_gather_kernel<<<(unsigned)W, 256, 0, s>>>(a);
-    return hipGetLastError();
+    return dispatch(gist_gather_kernel, dim3((unsigned)W), dim3(256), 0, s, ev, a);
 }
 
-hipError_t launch_gist_prefill_raw(const GistPrefillLaunch& a, hipStream_t s) {
+hipError_t launch_gist_prefill_raw(const GistPrefillLaunch& a, hipStream_t s,
+                                   const KernelEvents& ev) {
     hipError_t e = gist_check(a);
     if (e != hipSuccess) return e;
     const int G = a.Hq / a.Hkv;
     const long long W = 2LL * a.B * a.Hkv * a.M * (a.L / kPBlk) * ((G + 3) / 4);
-    if (W <= 0) return hipSuccess;
+    if (W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
     e = hipFuncSetAttribute((const void*)gist_prefill_mfma_kernel<false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
     if (e != hipSuccess) return e;
-    gist_prefill_mfma_kernel<false><<<(unsigned)W, 256, kPLds, s>>>(a);
-    return hipGetLastError();
+    return dispatch(gist_prefill_mfma_kernel<false>, dim3((unsigned)W), dim3(256), kPLds, s, ev,
+                    a);
 }
 
-hipError_t launch_gist_prefill_gists(const GistPrefillLaunch& a, hipStream_t s) {
+hipError_t launch_gist_prefill_gists(const GistPrefillLaunch& a, hipStream_t s,
+                                     const KernelEvents& ev) {
     hipError_t e = gist_check(a);
     if (e != hipSuccess) return e;
     const int G = a.Hq / a.Hkv;
     const long long W = 2LL * a.B * a.Hkv * (a.Gp / kPBlk) * ((G + 3) / 4);
-    if (W <= 0) return hipSuccess;
+    if (W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
     e = hipFuncSetAttribute((const void*)gist_prefill_mfma_kernel<true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
     if (e != hipSuccess) return e;
-    gist_prefill_mfma_kernel<true><<<(unsigned)W, 256, kPLds, s>>>(a);
-    return hipGetLastError();
+    return dispatch(gist_prefill_mfma_kernel<true>, dim3((unsigned)W), dim3(256), kPLds, s, ev,
+                    a);
 }
 
 }  // namespace tcs

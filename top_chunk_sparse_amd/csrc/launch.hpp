@@ -6,6 +6,14 @@
 
 namespace tcs {
 
+// Events a launcher has recorded at its kernel's own start and end (hipExtLaunchKernel's
+// start and stop events, so that they bracket the kernel alone); null members are skipped.
+// A launcher that runs no kernel records both where the kernel would have been.
+struct KernelEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // Per-slot softmax partial: unnormalised acc[d] plus (running max m, sum l).
 struct Partials {
     float* acc;   // [B*Hq][nslots][d]
@@ -88,8 +96,8 @@ struct ChunkLaunch {
     int g;
 };
 
-hipError_t launch_gist(const GistLaunch& a, hipStream_t s);
-hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s);
+hipError_t launch_gist(const GistLaunch& a, hipStream_t s, const KernelEvents& ev = {});
+hipError_t launch_chunks(const ChunkLaunch& a, hipStream_t s, const KernelEvents& ev = {});
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t v, hipStream_t s);
 hipError_t launch_stream_read(const void* p, size_t bytes, unsigned* sink, int blocks,
@@ -153,14 +161,22 @@ struct GistPrefillLaunch {
     float* lse;               // [B][Hq][T'] or null
 };
 
-hipError_t launch_gist_gather(const GistPrefillLaunch& a, hipStream_t s);
-hipError_t launch_gist_prefill_raw(const GistPrefillLaunch& a, hipStream_t s);
-hipError_t launch_gist_prefill_gists(const GistPrefillLaunch& a, hipStream_t s);
-hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s);
-hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s);
-hipError_t launch_prefill_bwd_prep(const PrefillBwdLaunch& a, hipStream_t s);
-hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s);
-hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s);
-hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s);
+hipError_t launch_gist_gather(const GistPrefillLaunch& a, hipStream_t s,
+                              const KernelEvents& ev = {});
+hipError_t launch_gist_prefill_raw(const GistPrefillLaunch& a, hipStream_t s,
+                                   const KernelEvents& ev = {});
+hipError_t launch_gist_prefill_gists(const GistPrefillLaunch& a, hipStream_t s,
+                                     const KernelEvents& ev = {});
+hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s,
+                                 const KernelEvents& ev = {});
+hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s, const KernelEvents& ev = {});
+hipError_t launch_prefill_bwd_prep(const PrefillBwdLaunch& a, hipStream_t s,
+                                   const KernelEvents& ev = {});
+hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s,
+                                 const KernelEvents& ev = {});
+hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s,
+                                  const KernelEvents& ev = {});
+hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s,
+                                 const KernelEvents& ev = {});
 
 }  // namespace tcs

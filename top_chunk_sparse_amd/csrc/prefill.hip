@@ -57,10 +57,10 @@ __global__ void __launch_bounds__(256) prefill_select_kernel(PrefillSelectLaunch
     }
 }
 
-hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s) {
-    if (a.units <= 0 || a.nb <= 0 || a.k <= 0) return hipSuccess;
-    prefill_select_kernel<<<a.units * a.nb, 256, 0, s>>>(a);
-    return hipGetLastError();
+hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s,
+                                 const KernelEvents& ev) {
+    if (a.units <= 0 || a.nb <= 0 || a.k <= 0) return no_kernel(ev, s);
+    return dispatch(prefill_select_kernel, dim3(a.units * a.nb), dim3(256), 0, s, ev, a);
 }
 
 // ---- block-sparse forward ------------------------------------------------------------------
@@ -308,19 +308,18 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
     if (a.lse && h == 0) a.lse[qrow] = (m + log2f(lt)) * kLn2;
 }
 
-hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s) {
+hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s, const KernelEvents& ev) {
     if (a.d != kPD || a.blk != kPBlk || a.T % kPBlk) return hipErrorNotSupported;
     const int G = a.Hq / a.Hkv;
     const long long W = 2LL * a.B * a.Hkv * (a.T / kPBlk) * ((G + 3) / 4);
-    if (W <= 0) return hipSuccess;
+    if (W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
     // the dynamic LDS (tiles + ring) is above the 64 KB default limit; set on every call (no
     // library state, and it holds for whichever device is current)
     const hipError_t e = hipFuncSetAttribute((const void*)prefill_fwd_kernel,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, kPLdsAll);
     if (e != hipSuccess) return e;
-    prefill_fwd_kernel<<<(unsigned)W, 256, kPLdsAll, s>>>(a);
-    return hipGetLastError();
+    return dispatch(prefill_fwd_kernel, dim3((unsigned)W), dim3(256), kPLdsAll, s, ev, a);
 }
 
 }  // namespace tcs

@@ -481,54 +481,64 @@ static hipError_t bwd_check(const PrefillBwdLaunch& a) {
     return hipSuccess;
 }
 
-hipError_t launch_prefill_bwd_prep(const PrefillBwdLaunch& a, hipStream_t s) {
+hipError_t launch_prefill_bwd_prep(const PrefillBwdLaunch& a, hipStream_t s,
+                                   const KernelEvents& ev) {
     hipError_t e = bwd_check(a);
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.B * a.Hq * a.T;
     const long long g1 = (rows * 16 + 255) / 256;
     const long long g2 = (long long)a.B * a.Hkv * (a.T / kPBlk);
     if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorNotSupported;
-    if (g1 > 0) prefill_bwd_prep_kernel<<<(unsigned)g1, 256, 0, s>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (g2 > 0) prefill_bwd_inverse_kernel<<<(unsigned)g2, 256, 0, s>>>(a);
-    return hipGetLastError();
+    if (g1 <= 0 && g2 <= 0) return no_kernel(ev, s);
+    // the events bracket both kernels: start with the first launched, stop with the last
+    if (g1 > 0) {
+        const KernelEvents e1{ev.start, g2 > 0 ? nullptr : ev.stop};
+        if ((e = dispatch(prefill_bwd_prep_kernel, dim3((unsigned)g1), dim3(256), 0, s, e1, a)) !=
+            hipSuccess)
+            return e;
+    }
+    if (g2 > 0) {
+        const KernelEvents e2{g1 > 0 ? nullptr : ev.start, ev.stop};
+        return dispatch(prefill_bwd_inverse_kernel, dim3((unsigned)g2), dim3(256), 0, s, e2, a);
+    }
+    return hipSuccess;
 }
 
-hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s) {
+hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s,
+                                 const KernelEvents& ev) {
     hipError_t e = bwd_check(a);
     if (e != hipSuccess) return e;
     const int G = a.Hq / a.Hkv;
     const long long W = 2LL * a.B * a.Hkv * (a.T / kPBlk) * ((G + 3) / 4);
-    if (W <= 0) return hipSuccess;
+    if (W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
     e = hipFuncSetAttribute((const void*)prefill_bwd_dq_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kPLdsAll);
     if (e != hipSuccess) return e;
-    prefill_bwd_dq_kernel<<<(unsigned)W, 256, kPLdsAll, s>>>(a);
-    return hipGetLastError();
+    return dispatch(prefill_bwd_dq_kernel, dim3((unsigned)W), dim3(256), kPLdsAll, s, ev, a);
 }
 
-hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s) {
+hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s,
+                                  const KernelEvents& ev) {
     hipError_t e = bwd_check(a);
     if (e != hipSuccess) return e;
     const long long W = (long long)a.B * a.Hkv * (a.T / kPBlk);
-    if (W <= 0) return hipSuccess;
+    if (W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
     e = hipFuncSetAttribute((const void*)prefill_bwd_dkv_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kBwdDkvLds);
     if (e != hipSuccess) return e;
-    prefill_bwd_dkv_kernel<<<(unsigned)W, 128, kBwdDkvLds, s>>>(a);
-    return hipGetLastError();
+    return dispatch(prefill_bwd_dkv_kernel, dim3((unsigned)W), dim3(128), kBwdDkvLds, s, ev, a);
 }
 
-hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s) {
+hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s,
+                                 const KernelEvents& ev) {
     hipError_t e = bwd_check(a);
-    if (e != hipSuccess || !a.dS) return e;
+    if (e != hipSuccess) return e;
     const long long W = (long long)a.B * a.Hkv * (a.T / kPBlk);
-    if (W <= 0) return hipSuccess;
+    if (!a.dS || W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    prefill_bwd_ds_kernel<<<(unsigned)W, 256, 0, s>>>(a);
-    return hipGetLastError();
+    return dispatch(prefill_bwd_ds_kernel, dim3((unsigned)W), dim3(256), 0, s, ev, a);
 }
 
 }  // namespace tcs
