@@ -94,30 +94,44 @@ struct RowStream {
         }
     }
 
-    // The first batch of rows, issued early (pre = true in the streaming call that follows).
+    // The first batch of rows, issued early (pre = 1 in the streaming call that follows).
     template <int U>
     __device__ __forceinline__ void prefetch(const uint16_t* __restrict__ X, int nrows,
                                              uint4 (&r)[U]) const {
         if (nrows > 0) load_batch<U>(X, nrows, 0, r);
     }
+    // The first two batches (pre = 2).
+    template <int U>
+    __device__ __forceinline__ void prefetch2(const uint16_t* __restrict__ X, int nrows,
+                                              uint4 (&ra)[U], uint4 (&rb)[U]) const {
+        if (nrows > 0) load_batch<U>(X, nrows, 0, ra);
+        if (nrows > U * RPP) load_batch<U>(X, nrows, U * RPP, rb);
+    }
 
+    // pre: how many of the first batches (0, 1 or 2) ra and rb already hold.
     template <int U, class Use>
     __device__ __forceinline__ void stream_rows(const uint16_t* __restrict__ X, int nrows,
-                                                Use use, uint4 (&ra)[U], bool pre) const {
+                                                Use use, uint4 (&ra)[U], uint4 (&rb)[U],
+                                                int pre) const {
         constexpr int STEP = U * RPP;
-        uint4 rb[U];
         auto load = [&](uint4 (&r)[U], int base) __attribute__((always_inline)) {
             load_batch<U>(X, nrows, base, r);
         };
         if (nrows <= 0) return;
-        if (!pre) load(ra, 0);
+        if (pre < 1) load(ra, 0);
         for (int base = 0; base < nrows; base += 2 * STEP) {
-            if (base + STEP < nrows) load(rb, base + STEP);
+            if (base + STEP < nrows && (pre < 2 || base > 0)) load(rb, base + STEP);
             use(ra, base);
             if (base + STEP >= nrows) break;
             if (base + 2 * STEP < nrows) load(ra, base + 2 * STEP);
             use(rb, base + STEP);
         }
+    }
+    template <int U, class Use>
+    __device__ __forceinline__ void stream_rows(const uint16_t* __restrict__ X, int nrows,
+                                                Use use, uint4 (&ra)[U], bool pre) const {
+        uint4 rb[U];
+        stream_rows<U>(X, nrows, use, ra, rb, pre ? 1 : 0);
     }
 
     // K phase: lg[(row0 + r) * G + h] = sigma * q_h . K[r] + bias for rows r < nrows.
@@ -148,6 +162,15 @@ struct RowStream {
     __device__ __forceinline__ void accumulate(float (&acc)[G][8], const uint16_t* __restrict__ V,
                                                int nrows, const float* w, int row0,
                                                uint4 (&first)[U], bool pre = false) const {
+        uint4 second[U];
+        accumulate2<U>(acc, V, nrows, w, row0, first, second, pre ? 1 : 0);
+    }
+    // The same with the second batch too (pre = 2: both prefetched).
+    template <int U>
+    __device__ __forceinline__ void accumulate2(float (&acc)[G][8], const uint16_t* __restrict__ V,
+                                                int nrows, const float* w, int row0,
+                                                uint4 (&first)[U], uint4 (&second)[U],
+                                                int pre) const {
         stream_rows<U>(V, nrows, [&](const uint4 (&vr)[U], int base) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -164,7 +187,7 @@ struct RowStream {
                     }
                 }
             }
-        }, first, pre);
+        }, first, second, pre);
     }
 
     // Sum the lane groups' accumulators and write one partial per head:
@@ -556,7 +579,8 @@ struct GistSmem {
 template <int D, int G>
 __device__ __forceinline__ void fold_rows(GistSmem<D, G>& sm, const Partials& part,
                                           const uint16_t* V, int nrows,
-                                          uint4 (&vfirst)[TCS_V_U], int bh0, int slot) {
+                                          uint4 (&vfirst)[TCS_V_U], uint4 (&vsecond)[TCS_V_U],
+                                          int npre, int bh0, int slot) {
     using RS = RowStream<D, G>;
     const RS rs;
     head_stats<G>(sm.x.lg, nrows, sm.hs);
@@ -565,7 +589,7 @@ __device__ __forceinline__ void fold_rows(GistSmem<D, G>& sm, const Partials& pa
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    rs.template accumulate<TCS_V_U>(acc, V, nrows, sm.x.lg, 0, vfirst, true);
+    rs.template accumulate2<TCS_V_U>(acc, V, nrows, sm.x.lg, 0, vfirst, vsecond, npre);
     __syncthreads();   // weights dead: fin may reuse the space
     rs.finish(acc, sm.hs.M, sm.hs.L, sm.x.fin, part, bh0, slot);
 }
@@ -605,8 +629,13 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
         rs.template logits<TCS_K_U>(q2, K, nrows, a.sigma, 0.f, sm.x.lg, 0);
     }
     // the first V batch travels while the scores and the softmax statistics are computed
-    uint4 vfirst[TCS_V_U];
-    if (!a.scores_only) rs.template prefetch<TCS_V_U>(V, nrows, vfirst);
+    // (two with the selection published first: pooling, the slice top-k and the statistics)
+    uint4 vfirst[TCS_V_U], vsecond[TCS_V_U];
+    const int npre = MODE == kGistPlain && a.selo.defer ? 2 : 1;
+    if (!a.scores_only) {
+        if (npre == 2) rs.template prefetch2<TCS_V_U>(V, nrows, vfirst, vsecond);
+        else rs.template prefetch<TCS_V_U>(V, nrows, vfirst);
+    }
     __syncthreads();
     const int ng = a.g * G;   // logits per item
     if constexpr (MODE == kGistHeads) {
@@ -666,7 +695,8 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
             __syncthreads();
             unsigned old_p = 0u;
             if (threadIdx.x == 0) old_p = atomicAdd(cnt, 1u);
-            if (!a.scores_only) fold_rows<D, G>(sm, a.part, V, nrows, vfirst, bh0, a.slot0 + y);
+            if (!a.scores_only)
+                fold_rows<D, G>(sm, a.part, V, nrows, vfirst, vsecond, npre, bh0, a.slot0 + y);
             if (threadIdx.x == 0) {
                 const unsigned old_f = atomicAdd(cnt, 1u << 16);
                 // the first to finish once every list is out merges; if some slice finished
@@ -686,7 +716,7 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
         }
     }
     if (!a.scores_only) {   // the gists are tokens of the softmax set: fold them in here
-        fold_rows<D, G>(sm, a.part, V, nrows, vfirst, bh0, a.slot0 + y);
+        fold_rows<D, G>(sm, a.part, V, nrows, vfirst, vsecond, npre, bh0, a.slot0 + y);
     } else if constexpr (MODE == kGistMeta) {
         // selected summaries at two levels: this group's own level-2 gists are the tokens
         const int r = a.groups[(long long)u * a.k2 + y];
@@ -699,7 +729,7 @@ __device__ __forceinline__ void gist_item(const GistLaunch& a, GistSmem<D, G>& s
         }
         rs.template prefetch<TCS_V_U>(a.pv + off, a.g, vfirst);
         __syncthreads();
-        fold_rows<D, G>(sm, a.part, a.pv + off, a.g, vfirst, bh0, a.slot0 + y);
+        fold_rows<D, G>(sm, a.part, a.pv + off, a.g, vfirst, vsecond, 1, bh0, a.slot0 + y);
     }
     __syncthreads();
     if constexpr (MODE == kGistHeads) {
