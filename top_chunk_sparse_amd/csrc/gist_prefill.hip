@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_mfma_kernel(GistPrefillLa
         return (in_gathered(t) ? vgst : GROWS ? vall : vraw) + blk_row(t) * kPD;
     };
 
-    const CopyOffsets gk = copy_offsets(false, w, lane), gv = copy_offsets(true, w, lane);
+    const CopyOffsets gk = copy_offsets(kSwzK, w, lane), gv = copy_offsets(kSwzV, w, lane);
     uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
     TCS_STAGE_LOAD(kblock(0), vblock(0));
 

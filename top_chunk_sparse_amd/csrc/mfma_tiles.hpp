@@ -13,6 +13,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -29,6 +30,13 @@ constexpr float kRescaleSlack = 8.f;         // log2 units a stale running max m
 
 __device__ __forceinline__ int swz_k(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_v(int r) { return r & 2; }
+// Tiles read both row-major and transposed (the backward's Q, dO and K tiles) need both
+// properties at once: (r & 2) keeps rows r and r + 2 of a transposing read apart, and the
+// (r >> 2) term makes the even rows (and the odd rows) of any 8 consecutive rows, and the rows
+// of one residue mod 4 among any 16, take four different units, so a 128-bit row read is
+// conflict-free as with swz_k.
+__device__ __forceinline__ int swz_t(int r) { return (r & 2) ^ ((r >> 2) & 3); }
+enum TileSwizzle { kSwzK, kSwzV, kSwzT };
 
 // Copy one block (64 rows x 128 bf16, rows contiguous in global memory) into an LDS tile.
 // Slot s (16 B) of the tile is sub-tile s / 256, row (s / 4) % 64, stored unit s % 4.  Wave w
@@ -41,9 +49,9 @@ struct CopyOffsets { uint32_t c[4]; };   // per-lane source byte offsets, one pe
 // s = (4 c + w) * 64 + lane: sub-tile c, row 16 w + lane / 4, stored unit lane % 4, so the
 // LDS writes of one instruction are 1 KB contiguous and a lane's source offsets differ only by
 // c * 64 bytes.
-__device__ __forceinline__ CopyOffsets copy_offsets(bool is_v, int w, int lane) {
+__device__ __forceinline__ CopyOffsets copy_offsets(TileSwizzle sw, int w, int lane) {
     const int r = 16 * w + (lane >> 2);
-    const int lu = (lane & 3) ^ (is_v ? swz_v(r) : swz_k(r));
+    const int lu = (lane & 3) ^ (sw == kSwzK ? swz_k(r) : sw == kSwzV ? swz_v(r) : swz_t(r));
     CopyOffsets o;
 #pragma unroll
     for (int c = 0; c < 4; ++c) o.c[c] = (uint32_t)(r * kPD * 2 + c * 64 + lu * 16);
@@ -129,11 +137,24 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // s_waitcnt lgkmcnt(0) with vmcnt / expcnt left free (gfx9 encoding)
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
-// Per-lane LDS offset of the transposing operand reads (the forward's V^T pattern) in a tile
-// stored in the transposable layout.
-__device__ __forceinline__ int tr_offset(int lane) {
+// Per-lane LDS offsets of the transposing operand reads (the forward's V^T pattern) in a tile
+// stored with swz_t.  The first read of a step covers rows 16 st + 4 h + rr, the second the
+// same rows plus 8, whose swizzle differs by 2, so each read has its own offset.
+struct TrOffsets { int lo, hi; };
+__device__ __forceinline__ TrOffsets tr_offsets_t(int lane) {
     const int h = lane >> 5, g = lane >> 4, L = lane & 15, rr = L >> 2, cc = L & 3;
-    return (4 * h + rr) * 64 + (((2 * (g & 1) + (cc >> 1)) ^ swz_v(rr)) << 4) + ((cc & 1) << 3);
+    const int u = (2 * (g & 1) + (cc >> 1)) ^ swz_t(4 * h + rr);
+    const int base = (4 * h + rr) * 64 + ((cc & 1) << 3);
+    return {base + (u << 4), base + ((u ^ 2) << 4)};
+}
+
+// V^T-style operand of (dim tile dt, key step st) from a swz_t tile: lo and hi are the tile
+// plus the two per-lane offsets of tr_offsets_t.
+__device__ __forceinline__ bf16x8 t_operand(const char* lo, const char* hi, int dt, int st) {
+    const int o = dt * kPSub + st * 1024;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lo + o));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(hi + o + 512));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 }  // namespace tcs

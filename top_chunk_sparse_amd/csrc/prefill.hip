@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
     fill_ring(kRing / 2);
 
     // Block 0 of the list is the diagonal block; blocks 1..ke are the chosen earlier ones.
-    const CopyOffsets gk = copy_offsets(false, w, lane), gv = copy_offsets(true, w, lane);
+    const CopyOffsets gk = copy_offsets(kSwzK, w, lane), gv = copy_offsets(kSwzV, w, lane);
     uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
     TCS_STAGE_LOAD(kbase + (size_t)i * kPBlk * kPD, vbase + (size_t)i * kPBlk * kPD);
 

@@ -23,9 +23,10 @@ namespace tcs {
 //   prefill_bwd_dq_kernel       the forward's work split (unit, i, row half, head group): per
 //                               visible block S^T = K Q^T and dP^T = V dO^T, dS^T = P^T (dP^T - D),
 //                               dQ^T += K^T dS^T, and the block's sum of dS^T (gate partial).
-//   prefill_bwd_dkv_kernel      per (unit, key block j), a wave per 32 keys: for each head and
-//                               each query block that sees j, S = Q K^T and dP = dO V^T with a
-//                               lane per key, dV^T += dO^T P and dK^T += Q^T dS, in registers.
+//   prefill_bwd_dkv_kernel      per (unit, key block j), two waves per 32 keys: for each head
+//                               and each query block that sees j, one wave forms S = Q K^T, P
+//                               and dV^T += dO^T P, the other dP = dO V^T, dS and
+//                               dK^T += Q^T dS, with a lane per key, in registers.
 //   prefill_bwd_ds_kernel       per (unit, i): dS[i][j'] = [j' chosen] dg_ij' -
 //                               softmax(S[i][. < i])_j' sum_j dg_ij.
 // =============================================================================================
@@ -120,7 +121,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
     fill_ring(kRing / 2);
 
     // K tiles in the transposable layout (read as K and as K^T), V tiles in the row layout.
-    const CopyOffsets gk = copy_offsets(true, w, lane), gv = copy_offsets(false, w, lane);
+    const CopyOffsets gk = copy_offsets(kSwzT, w, lane), gv = copy_offsets(kSwzK, w, lane);
     uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
     TCS_STAGE_LOAD(kbase + (size_t)i * kPBlk * kPD, vbase + (size_t)i * kPBlk * kPD);
 
@@ -137,11 +138,11 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
     const float Dq = a.D[qrow];
     TCS_STAGE_STORE(lds, lds + 2 * kPTile);
 
-    const int koff0 = c32 * 64 + (((0 + h) ^ swz_v(c32)) << 4);
-    const int koff1 = c32 * 64 + (((2 + h) ^ swz_v(c32)) << 4);
+    const int koff0 = c32 * 64 + (((0 + h) ^ swz_t(c32)) << 4);
+    const int koff1 = c32 * 64 + (((2 + h) ^ swz_t(c32)) << 4);
     const int voff0 = c32 * 64 + (((0 + h) ^ swz_k(c32)) << 4);
     const int voff1 = c32 * 64 + (((2 + h) ^ swz_k(c32)) << 4);
-    const int toff = tr_offset(lane);
+    const TrOffsets toff = tr_offsets_t(lane);
     wait_vmem();
 
     const float cs = a.sigma * kLog2e;
@@ -197,7 +198,8 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
                 if (lane == 0) dg[t - 1] = gsum;
             }
             // dQ^T += K^T dS^T over the block's keys (16 per step)
-            const char* ktT = kt + toff;
+            const char* ktlo = kt + toff.lo;
+            const char* kthi = kt + toff.hi;
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 if (half && st >= 2) break;
@@ -206,8 +208,8 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
                 for (int e = 0; e < 8; ++e) db[e] = (__bf16)dp[st >> 1][8 * (st & 1) + e];
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
-                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(ktT, dt, st), db,
-                                                                     dq[dt], 0, 0, 0);
+                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        t_operand(ktlo, kthi, dt, st), db, dq[dt], 0, 0, 0);
             }
         }
         if (t < ke) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
@@ -227,14 +229,23 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
         }
 }
 
-// dk / dv: a workgroup of two waves per (unit, key block j); wave w owns keys 32 w .. 32 w + 31
-// of the block and accumulates their dK^T and dV^T over every (head, query block) pair that
-// sees j, in registers, to the end.  The two waves share each pair's Q and dO tiles; the next
-// pair's tiles travel into registers while the current pair is computed (two LDS buffers).
+// dk / dv: a workgroup of four waves per (unit, key block j).  Wave w works on keys
+// 32 kh .. 32 kh + 31 of the block (kh = w & 1) in one of two roles, so that each wave holds
+// one key-row operand and one accumulator set and two workgroups fit on a CU:
+//   role A (w < 2): S = Q K^T, P = exp2(S - lse) (token-causal on the diagonal block),
+//                   dV^T += dO^T P;
+//   role B (w >= 2): dP = dO V^T, dS = P (dP - D) with the P that role A left in LDS,
+//                   dK^T += Q^T dS.
+// Every (head, query block) pair that sees j is one item; the four waves share its Q and dO
+// tiles, and the next item's tiles travel into registers while the current one is computed
+// (two LDS buffers).  An item has two phases: the S / dP products (with the exponentials of
+// role A), a barrier, then the dV / dK products.  Both roles accumulate in registers to the
+// end of the list.
 constexpr int kBwdBuf = 2 * kPTile + 2 * kPBlk * 4;   // Q tile, dO tile, lse2 and D of 64 rows
-constexpr int kBwdDkvLds = 2 * kBwdBuf;
+constexpr int kBwdP = 4 * 64 * 16;                    // P of 32 keys x 64 rows, fp16
+constexpr int kBwdDkvLds = 2 * kBwdBuf + 2 * kBwdP + 16;   // + two list slots
 
-__global__ void __launch_bounds__(128, 1) prefill_bwd_dkv_kernel(PrefillBwdLaunch a) {
+__global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunch a) {
     extern __shared__ __align__(16) char lds[];
     const int G = a.Hq / a.Hkv;
     const int nb = a.T / kPBlk;
@@ -248,103 +259,84 @@ __global__ void __launch_bounds__(128, 1) prefill_bwd_dkv_kernel(PrefillBwdLaunc
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int h = lane >> 5, c32 = lane & 31;
+    const int kh = w & 1;
+    const bool roleA = w < 2;
 
-    // K^T and V^T operands of this lane's key row (kept for the whole kernel)
-    const size_t kfirst = (size_t)unit * a.T + (size_t)j * kPBlk + 32 * w;
-    bf16x8 kf[8], vf[8];
+    // K^T (role A) or V^T (role B) operand of this lane's key row, kept for the whole kernel
+    const size_t kfirst = (size_t)unit * a.T + (size_t)j * kPBlk + 32 * kh;
+    bf16x8 kvf[8];
     {
-        const uint16_t* kp = a.k + (kfirst + c32) * kPD + 8 * h;
-        const uint16_t* vp = a.v + (kfirst + c32) * kPD + 8 * h;
+        const uint16_t* kp = (roleA ? a.k : a.v) + (kfirst + c32) * kPD + 8 * h;
 #pragma unroll
-        for (int kd = 0; kd < 8; ++kd) {
-            kf[kd] = *reinterpret_cast<const bf16x8*>(kp + 16 * kd);
-            vf[kd] = *reinterpret_cast<const bf16x8*>(vp + 16 * kd);
-        }
+        for (int kd = 0; kd < 8; ++kd) kvf[kd] = *reinterpret_cast<const bf16x8*>(kp + 16 * kd);
     }
-    const int qoff0 = c32 * 64 + (((0 + h) ^ swz_v(c32)) << 4);
-    const int qoff1 = c32 * 64 + (((2 + h) ^ swz_v(c32)) << 4);
-    const int toff = tr_offset(lane);
+    // Q and dO tiles are stored in the transposable layout and read both row-major (the S / dP
+    // products) and transposed (the dV / dK products).
+    const int qoff0 = c32 * 64 + (((0 + h) ^ swz_t(c32)) << 4);
+    const int qoff1 = c32 * 64 + (((2 + h) ^ swz_t(c32)) << 4);
+    const TrOffsets toff = tr_offsets_t(lane);
     const size_t lrow = (size_t)unit * nb + j;
     const int nlist = 1 + a.inv_n[lrow];     // the diagonal block, then the choosers
     const int nitems = G * nlist;             // (head, query block) pairs, head-major
     const float cs = a.sigma * kLog2e;
-    const int key = 32 * w + c32;             // this lane's key row within block j
-    // Tile slot c * 128 + tid (c < 8) of a 64-row block: sub-tile c / 2, row 32 (c % 2) +
-    // tid / 4, stored unit tid % 4 holding source unit (tid % 4) ^ swz_v(row), swz_v(row) =
-    // (tid >> 2) & 2; thread tid's source offset is the same for every c but for the row and
-    // sub-tile terms.
-    const int src_t = (tid >> 2) * kPD * 2 + (((tid & 3) ^ ((tid >> 2) & 2)) << 4);
+    const int key = 32 * kh + c32;            // this lane's key row within block j
+    // P of this key half: step st of lane l at (64 st + l) * 16 bytes, the same lane and step
+    // layout in which role B holds dP, so the hand-over needs no shuffle
+    char* pbuf = lds + 2 * kBwdBuf + kh * kBwdP + lane * 16;
+    const CopyOffsets gk = copy_offsets(kSwzT, w, lane), gv = gk;
 
-    // (head, query block) pair it: head it / nlist; query block j itself first, then the
-    // choosers of j in ascending order
-#define TCS_BWD_ITEM(it, i, bias, qrow0)                                                        \
-    do {                                                                                        \
-        const int hd_ = (it) / nlist, t_ = (it) - hd_ * nlist;                                  \
-        i = t_ == 0 ? j : a.inv_i[lrow * nb + t_ - 1];                                          \
-        bias = t_ == 0 ? 0.f : a.inv_g[lrow * nb + t_ - 1] * kLog2e;                            \
-        qrow0 = (size_t)(b * a.Hq + kv * G + hd_) * a.T + (size_t)i * kPBlk;                    \
-    } while (0)
-    // staged copy of a pair's Q and dO tiles (8 + 8 chunks of 16 B per thread) and of its
-    // rows' lse2 (threads 0..63) or D (threads 64..127)
+    // (head, query block) pair it: head it / nlist; list position t = it % nlist: query block j
+    // itself (t = 0), then the choosers of j in ascending order.  A pair's query block and
+    // gate come from LDS slot it & 1: the lists are read two pairs ahead, with the tiles of the
+    // next pair, and thread 0 writes the slot with the tiles at the end of an iteration, so no
+    // list read waits in the loop.
+    int* slot_i = reinterpret_cast<int*>(lds + 2 * kBwdBuf + 2 * kBwdP);
+    float* slot_g = reinterpret_cast<float*>(slot_i + 2);
+    int xi = 0;        // raw list entries of a pair (loaded by every thread from one address)
+    float xg = 0.f;
+    auto list_load = [&](int it) {
+        const size_t e = lrow * nb + max(it % nlist - 1, 0);
+        xi = a.inv_i[e];
+        xg = a.inv_g[e];
+    };
+    auto list_store = [&](int it, int sl) {   // pair it's query block and gate (log2 units)
+        const bool first = it % nlist == 0;
+        slot_i[sl] = first ? j : xi;
+        slot_g[sl] = first ? 0.f : xg * kLog2e;
+    };
+    auto qrow_of = [&](int it, int i) {
+        return (size_t)(b * a.Hq + kv * G + it / nlist) * a.T + (size_t)i * kPBlk;
+    };
+    // staged copy of a pair's Q and dO tiles (4 + 4 chunks of 16 B per thread) and of its rows'
+    // lse (threads 0..63, stored as lse2) and D (threads 64..127)
 #define TCS_BWD_LOAD(qrow0)                                                                     \
     do {                                                                                        \
-        const char* qs_ = reinterpret_cast<const char*>(a.q + (qrow0) * kPD) + src_t;           \
-        const char* gs_ = reinterpret_cast<const char*>(a.dout + (qrow0) * kPD) + src_t;        \
-        xq0 = *reinterpret_cast<const uint4*>(qs_ + 0 * 8192 + 0 * 64);                         \
-        xq1 = *reinterpret_cast<const uint4*>(qs_ + 1 * 8192 + 0 * 64);                         \
-        xq2 = *reinterpret_cast<const uint4*>(qs_ + 0 * 8192 + 1 * 64);                         \
-        xq3 = *reinterpret_cast<const uint4*>(qs_ + 1 * 8192 + 1 * 64);                         \
-        xq4 = *reinterpret_cast<const uint4*>(qs_ + 0 * 8192 + 2 * 64);                         \
-        xq5 = *reinterpret_cast<const uint4*>(qs_ + 1 * 8192 + 2 * 64);                         \
-        xq6 = *reinterpret_cast<const uint4*>(qs_ + 0 * 8192 + 3 * 64);                         \
-        xq7 = *reinterpret_cast<const uint4*>(qs_ + 1 * 8192 + 3 * 64);                         \
-        xg0 = *reinterpret_cast<const uint4*>(gs_ + 0 * 8192 + 0 * 64);                         \
-        xg1 = *reinterpret_cast<const uint4*>(gs_ + 1 * 8192 + 0 * 64);                         \
-        xg2 = *reinterpret_cast<const uint4*>(gs_ + 0 * 8192 + 1 * 64);                         \
-        xg3 = *reinterpret_cast<const uint4*>(gs_ + 1 * 8192 + 1 * 64);                         \
-        xg4 = *reinterpret_cast<const uint4*>(gs_ + 0 * 8192 + 2 * 64);                         \
-        xg5 = *reinterpret_cast<const uint4*>(gs_ + 1 * 8192 + 2 * 64);                         \
-        xg6 = *reinterpret_cast<const uint4*>(gs_ + 0 * 8192 + 3 * 64);                         \
-        xg7 = *reinterpret_cast<const uint4*>(gs_ + 1 * 8192 + 3 * 64);                         \
-        xl = tid < 64 ? a.lse[(qrow0) + tid] * kLog2e : a.D[(qrow0) + tid - 64];                \
+        TCS_STAGE_LOAD(a.q + (qrow0) * kPD, a.dout + (qrow0) * kPD);                            \
+        if (tid < 2 * kPBlk) xl = tid < kPBlk ? a.lse[(qrow0) + tid] : a.D[(qrow0) + tid - kPBlk]; \
     } while (0)
 #define TCS_BWD_STORE(buf)                                                                      \
     do {                                                                                        \
-        char* d_ = (buf) + tid * 16;                                                            \
-        *reinterpret_cast<uint4*>(d_ + 0 * 2048) = xq0;                                         \
-        *reinterpret_cast<uint4*>(d_ + 1 * 2048) = xq1;                                         \
-        *reinterpret_cast<uint4*>(d_ + 2 * 2048) = xq2;                                         \
-        *reinterpret_cast<uint4*>(d_ + 3 * 2048) = xq3;                                         \
-        *reinterpret_cast<uint4*>(d_ + 4 * 2048) = xq4;                                         \
-        *reinterpret_cast<uint4*>(d_ + 5 * 2048) = xq5;                                         \
-        *reinterpret_cast<uint4*>(d_ + 6 * 2048) = xq6;                                         \
-        *reinterpret_cast<uint4*>(d_ + 7 * 2048) = xq7;                                         \
-        *reinterpret_cast<uint4*>(d_ + kPTile + 0 * 2048) = xg0;                                \
-        *reinterpret_cast<uint4*>(d_ + kPTile + 1 * 2048) = xg1;                                \
-        *reinterpret_cast<uint4*>(d_ + kPTile + 2 * 2048) = xg2;                                \
-        *reinterpret_cast<uint4*>(d_ + kPTile + 3 * 2048) = xg3;                                \
-        *reinterpret_cast<uint4*>(d_ + kPTile + 4 * 2048) = xg4;                                \
-        *reinterpret_cast<uint4*>(d_ + kPTile + 5 * 2048) = xg5;                                \
-        *reinterpret_cast<uint4*>(d_ + kPTile + 6 * 2048) = xg6;                                \
-        *reinterpret_cast<uint4*>(d_ + kPTile + 7 * 2048) = xg7;                                \
-        reinterpret_cast<float*>((buf) + 2 * kPTile)[tid] = xl;                                 \
+        TCS_STAGE_STORE((buf), (buf) + kPTile);                                                 \
+        if (tid < 2 * kPBlk)                                                                    \
+            reinterpret_cast<float*>((buf) + 2 * kPTile)[tid] = tid < kPBlk ? xl * kLog2e : xl; \
     } while (0)
-    uint4 xq0, xq1, xq2, xq3, xq4, xq5, xq6, xq7, xg0, xg1, xg2, xg3, xg4, xg5, xg6, xg7;
-    float xl;   // thread < 64: lse2 of row tid; thread >= 64: D of row tid - 64
+    uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;   // Q chunks (sk), dO chunks (sv)
+    float xl = 0.f;
 
-    f32x16 dk[4], dv[4];
+    f32x16 acc[4];   // role A: dV^T, role B: dK^T (32 dims per tile x 32 keys)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dk[dt] = dv[dt] = f32x16{};
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-    int i_cur;
-    float bias_cur;
-    size_t qrow_cur;
-    TCS_BWD_ITEM(0, i_cur, bias_cur, qrow_cur);
-    TCS_BWD_LOAD(qrow_cur);
+    // pair 0 is (head 0, block j); pair 1's list entry goes to its slot before the loop
+    int i_cur = j;
+    float bias_cur = 0.f;
+    TCS_BWD_LOAD(qrow_of(0, j));
+    list_load(min(1, nitems - 1));
     TCS_BWD_STORE(lds);
+    if (tid == 0) list_store(min(1, nitems - 1), 1);
     wait_vmem();
     for (int it = 0; it < nitems; ++it) {
-        __syncthreads();   // buffer it & 1 is filled; both waves are done with the other one
+        __syncthreads();   // buffer and slot it & 1 are filled; every wave is done with the others
         const char* qt = lds + (it & 1) * kBwdBuf;
         const char* gt = qt + kPTile;
         const float* l2 = reinterpret_cast<const float*>(gt + kPTile);
@@ -353,77 +345,102 @@ __global__ void __launch_bounds__(128, 1) prefill_bwd_dkv_kernel(PrefillBwdLaunc
         const float bias = bias_cur;
         int i_nx = 0;
         float bias_nx = 0.f;
-        size_t qrow_nx = 0;
         if (it + 1 < nitems) {
-            TCS_BWD_ITEM(it + 1, i_nx, bias_nx, qrow_nx);
-            TCS_BWD_LOAD(qrow_nx);
+            i_nx = __builtin_amdgcn_readfirstlane(slot_i[(it + 1) & 1]);
+            bias_nx = __int_as_float(
+                __builtin_amdgcn_readfirstlane(__float_as_int(slot_g[(it + 1) & 1])));
+            TCS_BWD_LOAD(qrow_of(it + 1, i_nx));
+            list_load(min(it + 2, nitems - 1));
         }
 
-        f32x16 s[2], dp[2];
-        s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-        qk_product<2>(qt, qoff0, qoff1, kf, s);    // S = Q K^T (lane: key; rows: queries)
-        qk_product<2>(gt, qoff0, qoff1, vf, dp);   // dP = dO V^T
+        // ---- phase 1: S = Q K^T (A) or dP = dO V^T (B); lane: key, rows: queries ----
+        f32x16 s[2];
+        s[0] = s[1] = f32x16{};
+        qk_product<2>(roleA ? qt : gt, qoff0, qoff1, kvf, s);
+        bf16x8 ob[4];   // the B operands of phase 2: P (A) or dS (B), 16 query rows per step
+        if (roleA) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int q0 = 32 * x + 8 * e4 + 4 * h;   // query rows q0 .. q0 + 3
-                const float4 lq = *reinterpret_cast<const float4*>(l2 + q0);
-                const float4 dd = *reinterpret_cast<const float4*>(Dl + q0);
-                const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
-                const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int q0 = 32 * x + 8 * e4 + 4 * h;   // query rows q0 .. q0 + 3
+                    const float4 lq = *reinterpret_cast<const float4*>(l2 + q0);
+                    const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int e = 4 * e4 + jj;
-                    float p = __builtin_amdgcn_exp2f(s[x][e] * cs + bias - lv[jj]);
-                    if (diag && key > q0 + jj) p = 0.f;   // diagonal block: token-causal
-                    s[x][e] = p;
-                    dp[x][e] = p * (dp[x][e] - dv4[jj]);
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int e = 4 * e4 + jj;
+                        float p = __builtin_amdgcn_exp2f(s[x][e] * cs + bias - lv[jj]);
+                        if (diag && key > q0 + jj) p = 0.f;   // diagonal block: token-causal
+                        s[x][e] = p;
+                    }
                 }
-            }
-        // dV^T += dO^T P and dK^T += Q^T dS over the block's queries (16 per step)
-        const char* gtT = gt + toff;
-        const char* qtT = qt + toff;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            bf16x8 pb, db;
+            for (int st = 0; st < 4; ++st) {
+                half8 ph;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pb[e] = (__bf16)s[st >> 1][8 * (st & 1) + e];
-                db[e] = (__bf16)dp[st >> 1][8 * (st & 1) + e];
-            }
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(gtT, dt, st), pb,
-                                                                 dv[dt], 0, 0, 0);
-                dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(qtT, dt, st), db,
-                                                                 dk[dt], 0, 0, 0);
+                for (int e = 0; e < 8; ++e) {
+                    ob[st][e] = (__bf16)s[st >> 1][8 * (st & 1) + e];
+                    ph[e] = (_Float16)s[st >> 1][8 * (st & 1) + e];
+                }
+                *reinterpret_cast<half8*>(pbuf + st * 1024) = ph;
             }
         }
+        __syncthreads();   // P of this item is in LDS
+        if (!roleA) {
+            half8 ph[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) ph[st] = *reinterpret_cast<const half8*>(pbuf + st * 1024);
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int q0 = 32 * x + 8 * e4 + 4 * h;
+                    const float4 dd = *reinterpret_cast<const float4*>(Dl + q0);
+                    const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int e = 4 * e4 + jj;   // step 2 x + e / 8, element e % 8
+                        const float p = (float)ph[2 * x + (e >> 3)][e & 7];
+                        s[x][e] = p * (s[x][e] - dv4[jj]);
+                    }
+                }
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ob[st][e] = (__bf16)s[st >> 1][8 * (st & 1) + e];
+        }
+
+        // ---- phase 2: dV^T += dO^T P (A) or dK^T += Q^T dS (B), 16 query rows per step ----
+        const char* tt = roleA ? gt : qt;
+        const char* tlo = tt + toff.lo;
+        const char* thi = tt + toff.hi;
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_operand(tlo, thi, dt, st),
+                                                                  ob[st], acc[dt], 0, 0, 0);
         if (it + 1 < nitems) {
             TCS_BWD_STORE(lds + ((it + 1) & 1) * kBwdBuf);
+            if (tid == 0) list_store(min(it + 2, nitems - 1), it & 1);
             i_cur = i_nx;
             bias_cur = bias_nx;
-            qrow_cur = qrow_nx;
         }
     }
 
-    // this wave's 32 key rows: dK = sigma dK^T, dV = dV^T (lane: key row; registers: dims)
-    float* kp = a.dk + (kfirst + c32) * kPD;
-    float* vp = a.dv + (kfirst + c32) * kPD;
+    // this wave's 32 key rows: dV = dV^T (A) or dK = sigma dK^T (B); lane: key row, registers:
+    // dims
+    const float sc = roleA ? 1.f : a.sigma;
+    float* op = (roleA ? a.dv : a.dk) + (kfirst + c32) * kPD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-            float4 x, y;
-            x.x = dk[dt][4 * e4 + 0] * a.sigma; x.y = dk[dt][4 * e4 + 1] * a.sigma;
-            x.z = dk[dt][4 * e4 + 2] * a.sigma; x.w = dk[dt][4 * e4 + 3] * a.sigma;
-            y.x = dv[dt][4 * e4 + 0]; y.y = dv[dt][4 * e4 + 1];
-            y.z = dv[dt][4 * e4 + 2]; y.w = dv[dt][4 * e4 + 3];
-            *reinterpret_cast<float4*>(kp + 32 * dt + 8 * e4 + 4 * h) = x;
-            *reinterpret_cast<float4*>(vp + 32 * dt + 8 * e4 + 4 * h) = y;
+            float4 x;
+            x.x = acc[dt][4 * e4 + 0] * sc; x.y = acc[dt][4 * e4 + 1] * sc;
+            x.z = acc[dt][4 * e4 + 2] * sc; x.w = acc[dt][4 * e4 + 3] * sc;
+            *reinterpret_cast<float4*>(op + 32 * dt + 8 * e4 + 4 * h) = x;
         }
-#undef TCS_BWD_ITEM
 #undef TCS_BWD_LOAD
 #undef TCS_BWD_STORE
 }
@@ -528,7 +545,7 @@ hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s,
     e = hipFuncSetAttribute((const void*)prefill_bwd_dkv_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kBwdDkvLds);
     if (e != hipSuccess) return e;
-    return dispatch(prefill_bwd_dkv_kernel, dim3((unsigned)W), dim3(128), kBwdDkvLds, s, ev, a);
+    return dispatch(prefill_bwd_dkv_kernel, dim3((unsigned)W), dim3(256), kBwdDkvLds, s, ev, a);
 }
 
 hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s,
