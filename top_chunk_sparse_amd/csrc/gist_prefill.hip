@@ -251,6 +251,15 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_mfma_kernel(GistPrefillLa
         }
         if (t + 1 < nblk) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
     }
+    if constexpr (!GROWS) {
+        // raw rows: a wave's 32 rows are consecutive positions, stored as whole rows
+        __syncthreads();   // every wave is done with the last block's tiles
+        if (!active) return;
+        const float lt = pair_sum(l);
+        store_rows_f32(o, 1.f / lt, lds + w * kORowsLds, a.out + (qrow - c32) * kPD, lane);
+        if (a.lse && h == 0) a.lse[qrow] = (m + log2f(lt)) * kLn2;
+        return;
+    }
     if (!active || !row_ok) return;
     const float lt = pair_sum(l);
     const float inv = 1.f / lt;

@@ -157,4 +157,34 @@ __device__ __forceinline__ bf16x8 t_operand(const char* lo, const char* hi, int 
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Output of one wave: 32 query rows x 128 dims, O^T accumulators in the product layout (lane
+// l: row l % 32, dims 32 dt + 8 e4 + 4 (l / 32) .. + 3 in o[dt][4 e4 ..]).  Written scaled by
+// the lane's inv through this wave's 16 KB of LDS (row r at 512 r, 16-byte unit u at u ^ r,
+// conflict-free both ways) and stored from there two whole rows per instruction, so each store
+// instruction covers 1 KB of consecutive output instead of 32 B pieces of 32 rows.
+constexpr int kORowsLds = 32 * kPD * 4;
+__device__ __forceinline__ void store_rows_f32(const f32x16 (&o)[4], float inv, char* lds_w,
+                                               float* out_rows, int lane) {
+    const int h = lane >> 5, c32 = lane & 31;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int u = 8 * dt + 2 * e4 + h;
+            float4 v;
+            v.x = o[dt][4 * e4 + 0] * inv;
+            v.y = o[dt][4 * e4 + 1] * inv;
+            v.z = o[dt][4 * e4 + 2] * inv;
+            v.w = o[dt][4 * e4 + 3] * inv;
+            *reinterpret_cast<float4*>(lds_w + c32 * 512 + ((u ^ c32) << 4)) = v;
+        }
+    const int u = lane & 31;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int row = 2 * k + h;
+        const float4 v = *reinterpret_cast<const float4*>(lds_w + row * 512 + ((u ^ row) << 4));
+        *reinterpret_cast<float4*>(out_rows + row * kPD + 4 * u) = v;
+    }
+}
+
 }  // namespace tcs

@@ -288,23 +288,12 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
         }
         if (t < ke) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
     }
-    if (!active) return;
-
     // ---- epilogue: O = O^T / l, lse = m + log2 l (back to natural log) ----
+    __syncthreads();   // every wave is done with the last block's tiles
+    if (!active) return;
     const float lt = pair_sum(l);
     const float inv = 1.f / lt;
-    float* op = a.out + qrow * kPD;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            float4 v;
-            v.x = o[dt][4 * e4 + 0] * inv;
-            v.y = o[dt][4 * e4 + 1] * inv;
-            v.z = o[dt][4 * e4 + 2] * inv;
-            v.w = o[dt][4 * e4 + 3] * inv;
-            *reinterpret_cast<float4*>(op + 32 * dt + 8 * e4 + 4 * h) = v;
-        }
+    store_rows_f32(o, inv, lds + w * kORowsLds, a.out + (qrow - c32) * kPD, lane);
     if (a.lse && h == 0) a.lse[qrow] = (m + log2f(lt)) * kLn2;
 }
 

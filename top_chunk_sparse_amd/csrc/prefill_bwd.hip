@@ -214,19 +214,9 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
         }
         if (t < ke) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
     }
+    __syncthreads();   // every wave is done with the last block's tiles
     if (!active) return;
-    float* op = a.dq + qrow * kPD;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            float4 v;
-            v.x = dq[dt][4 * e4 + 0] * a.sigma;
-            v.y = dq[dt][4 * e4 + 1] * a.sigma;
-            v.z = dq[dt][4 * e4 + 2] * a.sigma;
-            v.w = dq[dt][4 * e4 + 3] * a.sigma;
-            *reinterpret_cast<float4*>(op + 32 * dt + 8 * e4 + 4 * h) = v;
-        }
+    store_rows_f32(dq, a.sigma, lds + w * kORowsLds, a.dq + (qrow - c32) * kPD, lane);
 }
 
 // dk / dv: a workgroup of four waves per (unit, key block j).  Wave w works on keys
@@ -430,17 +420,9 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
 
     // this wave's 32 key rows: dV = dV^T (A) or dK = sigma dK^T (B); lane: key row, registers:
     // dims
-    const float sc = roleA ? 1.f : a.sigma;
-    float* op = (roleA ? a.dv : a.dk) + (kfirst + c32) * kPD;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            float4 x;
-            x.x = acc[dt][4 * e4 + 0] * sc; x.y = acc[dt][4 * e4 + 1] * sc;
-            x.z = acc[dt][4 * e4 + 2] * sc; x.w = acc[dt][4 * e4 + 3] * sc;
-            *reinterpret_cast<float4*>(op + 32 * dt + 8 * e4 + 4 * h) = x;
-        }
+    __syncthreads();   // every wave is done with the last pair's tiles
+    store_rows_f32(acc, roleA ? 1.f : a.sigma, lds + w * kORowsLds,
+                   (roleA ? a.dv : a.dk) + kfirst * kPD, lane);
 #undef TCS_BWD_LOAD
 #undef TCS_BWD_STORE
 }
