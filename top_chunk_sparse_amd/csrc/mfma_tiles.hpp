@@ -12,6 +12,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -161,7 +162,9 @@ __device__ __forceinline__ bf16x8 t_operand(const char* lo, const char* hi, int 
 // l: row l % 32, dims 32 dt + 8 e4 + 4 (l / 32) .. + 3 in o[dt][4 e4 ..]).  Written scaled by
 // the lane's inv through this wave's 16 KB of LDS (row r at 512 r, 16-byte unit u at u ^ r,
 // conflict-free both ways) and stored from there two whole rows per instruction, so each store
-// instruction covers 1 KB of consecutive output instead of 32 B pieces of 32 rows.
+// instruction covers 1 KB of consecutive output instead of 32 B pieces of 32 rows.  The stores
+// are non-temporal: whole lines written once, which then leave the L2 to the K / V blocks that
+// other workgroups read again.
 constexpr int kORowsLds = 32 * kPD * 4;
 __device__ __forceinline__ void store_rows_f32(const f32x16 (&o)[4], float inv, char* lds_w,
                                                float* out_rows, int lane) {
@@ -182,8 +185,8 @@ __device__ __forceinline__ void store_rows_f32(const f32x16 (&o)[4], float inv, 
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int row = 2 * k + h;
-        const float4 v = *reinterpret_cast<const float4*>(lds_w + row * 512 + ((u ^ row) << 4));
-        *reinterpret_cast<float4*>(out_rows + row * kPD + 4 * u) = v;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lds_w + row * 512 + ((u ^ row) << 4));
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out_rows + row * kPD + 4 * u));
     }
 }
 
