@@ -134,7 +134,9 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_mfma_kernel(GistPrefillLa
                               : (size_t)c * W + (size_t)rb * kPBlk + 32 * rh + c32;
     const size_t qrow = (size_t)(b * a.Hq + kv * G + (active ? head : 0)) * Tp + qpos;
     bf16x8 qf[8];
-    {
+    if constexpr (!GROWS) {   // raw rows: the wave's 32 rows are consecutive positions
+        load_q_operand(a.q + (qrow - c32) * kPD, q_stage_lds(lds, w), lane, qf);
+    } else {
         const uint16_t* qp = a.q + qrow * kPD + 8 * h;
 #pragma unroll
         for (int kd = 0; kd < 8; ++kd) qf[kd] = *reinterpret_cast<const bf16x8*>(qp + 16 * kd);

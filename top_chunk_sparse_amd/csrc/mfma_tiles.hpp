@@ -158,6 +158,36 @@ __device__ __forceinline__ bf16x8 t_operand(const char* lo, const char* hi, int 
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// The Q^T operand of one wave (32 consecutive rows of 128 bf16; lane l: row l % 32, elements
+// 16 kd + 8 (l / 32) .. + 7 in qf[kd]).  Loaded 1 KB per instruction (non-temporal: read once)
+// into this wave's 8 KB of LDS (row r at 256 r, 16-byte unit u at u ^ (r & 15), conflict-free
+// both ways), then read in the operand layout; a direct operand load would fetch 32-byte
+// pieces of 32 rows per instruction.
+constexpr int kQRowsLds = 32 * kPD * 2;
+__device__ __forceinline__ void load_q_operand(const uint16_t* rows, char* lds_w, int lane,
+                                               bf16x8 (&qf)[8]) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const char* src = reinterpret_cast<const char*>(rows);
+    u32x4 x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        x[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + k * 1024 + lane * 16));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + (lane >> 4), u = lane & 15;
+        *reinterpret_cast<u32x4*>(lds_w + r * 256 + ((u ^ (r & 15)) << 4)) = x[k];
+    }
+    const int c32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int kd = 0; kd < 8; ++kd)
+        qf[kd] = *reinterpret_cast<const bf16x8*>(lds_w + c32 * 256 + (((2 * kd + h) ^ (c32 & 15)) << 4));
+}
+// LDS of wave w's query transpose inside tile buffer 1 (K1 for waves 0, 1; V1 for 2, 3), free
+// while block 0 is staged into buffer 0
+__device__ __forceinline__ char* q_stage_lds(char* lds, int w) {
+    return lds + (w < 2 ? kPTile + w * kQRowsLds : 3 * kPTile + (w - 2) * kQRowsLds);
+}
+
 // Output of one wave: 32 query rows x 128 dims, O^T accumulators in the product layout (lane
 // l: row l % 32, dims 32 dt + 8 e4 + 4 (l / 32) .. + 3 in o[dt][4 e4 ..]).  Written scaled by
 // the lane's inv through this wave's 16 KB of LDS (row r at 512 r, 16-byte unit u at u ^ r,

@@ -145,11 +145,7 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
     const size_t qrow = ((size_t)(b * a.Hq + kv * G + (active ? head : 0)) * a.T +
                          (size_t)i * kPBlk + 32 * rh + c32);
     bf16x8 qf[8];
-    {
-        const uint16_t* qp = a.q + qrow * kPD + 8 * h;
-#pragma unroll
-        for (int kd = 0; kd < 8; ++kd) qf[kd] = *reinterpret_cast<const bf16x8*>(qp + 16 * kd);
-    }
+    load_q_operand(a.q + (qrow - c32) * kPD, q_stage_lds(lds, w), lane, qf);
     TCS_STAGE_STORE(lds, lds + 2 * kPTile);
 
     // Per-lane LDS offsets (bytes) of the operand reads; everything else is an immediate.

@@ -129,11 +129,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
                          (size_t)i * kPBlk + 32 * rh + c32);
     bf16x8 qf[8];   // Q^T operand of this lane's query row (dO^T is re-read per block)
     const uint16_t* gp = a.dout + qrow * kPD + 8 * h;
-    {
-        const uint16_t* qp = a.q + qrow * kPD + 8 * h;
-#pragma unroll
-        for (int kd = 0; kd < 8; ++kd) qf[kd] = *reinterpret_cast<const bf16x8*>(qp + 16 * kd);
-    }
+    load_q_operand(a.q + (qrow - c32) * kPD, q_stage_lds(lds, w), lane, qf);
     const float lse2 = a.lse[qrow] * kLog2e;
     const float Dq = a.D[qrow];
     TCS_STAGE_STORE(lds, lds + 2 * kPTile);
