@@ -152,7 +152,7 @@
 extern "C" {
 #endif
 
-#define TCS_ABI_VERSION 8
+#define TCS_ABI_VERSION 9
 
 typedef enum {
     TCS_OK = 0,
@@ -327,7 +327,7 @@ tcs_status sparse_attn_gist_prefill(const tcs_gist_prefill_params* p,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Profiling variant (a pair of events per stage, as in sparse_attn_decode_timed): stage 0 the
- * gist gather, stage 1 the raw query rows, stage 2 the gist query rows. */
+ * gist gather, stage 1 the query rows (gist rows and raw rows, one launch). */
 tcs_status sparse_attn_gist_prefill_timed(const tcs_gist_prefill_params* p,
                                           const void* q, const void* k, const void* v,
                                           float* out, float* lse, void* workspace,

@@ -658,8 +658,7 @@ static tcs_status gist_prefill_impl(const tcs_gist_prefill_params* p, const void
     a.out = out;
     a.lse = lse;
     hipError_t e = tcs::launch_gist_gather(a, s, clk.next());
-    if (e == hipSuccess) e = tcs::launch_gist_prefill_raw(a, s, clk.next());
-    if (e == hipSuccess) e = tcs::launch_gist_prefill_gists(a, s, clk.next());
+    if (e == hipSuccess) e = tcs::launch_gist_prefill_rows(a, s, clk.next());
     if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
     return e == hipSuccess ? TCS_OK : TCS_ERR_HIP;
 }

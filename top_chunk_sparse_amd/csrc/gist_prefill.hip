@@ -52,8 +52,9 @@ __global__ void __launch_bounds__(256) gist_gather_kernel(GistPrefillLaunch a) {
     }
 }
 
+// Workgroup bid0 of a grid of Wg workgroups of one row kind.
 template <bool GROWS>
-__global__ void __launch_bounds__(256, 2) gist_prefill_mfma_kernel(GistPrefillLaunch a) {
+__device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, int bid0, int Wg) {
     extern __shared__ __align__(16) char lds[];
     const int G = a.Hq / a.Hkv;
     const int nhg = (G + 3) >> 2;
@@ -65,8 +66,7 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_mfma_kernel(GistPrefillLa
     const size_t Tp = (size_t)a.M * W;
     // XCD-contiguous ranges as in the forward; within a range the last chunks (longest gist
     // prefix) first, the two row halves of a block side by side
-    int bid = blockIdx.x;
-    const int Wg = gridDim.x;
+    int bid = bid0;
     if ((Wg & 7) == 0) bid = (bid & 7) * (Wg >> 3) + (bid >> 3);
     const int rh = bid & 1;
     const int qb = nq - 1 - (bid >> 1) % nq;
@@ -280,6 +280,16 @@ __global__ void __launch_bounds__(256, 2) gist_prefill_mfma_kernel(GistPrefillLa
     if (a.lse && h == 0) a.lse[qrow] = (m + log2f(lt)) * kLn2;
 }
 
+// One launch for both row kinds: the gist rows' workgroups first (few, with long block lists:
+// on their own they fill half the CUs), then the raw rows' workgroups, which take every CU
+// slot the gist rows leave.  The gist-row share is a multiple of 8, so both shares keep the
+// XCD-contiguous ranges.
+__global__ void __launch_bounds__(256, 2) gist_prefill_mfma_kernel(GistPrefillLaunch a) {
+    const int wg = a.w_gist_rows;
+    if ((int)blockIdx.x < wg) gist_prefill_rows<true>(a, blockIdx.x, wg);
+    else gist_prefill_rows<false>(a, blockIdx.x - wg, gridDim.x - wg);
+}
+
 static hipError_t gist_check(const GistPrefillLaunch& a) {
     if (a.d != kPD || a.L % kPBlk || a.g < 1 || a.g > kPBlk || kPBlk % a.g || a.Hkv <= 0 ||
         a.Hq % a.Hkv || a.Gp % kPBlk || a.Gp < a.M * a.g)
@@ -297,34 +307,20 @@ hipError_t launch_gist_gather(const GistPrefillLaunch& a, hipStream_t s,
     return dispatch(gist_gather_kernel, dim3((unsigned)W), dim3(256), 0, s, ev, a);
 }
 
-hipError_t launch_gist_prefill_raw(const GistPrefillLaunch& a, hipStream_t s,
-                                   const KernelEvents& ev) {
+hipError_t launch_gist_prefill_rows(GistPrefillLaunch a, hipStream_t s, const KernelEvents& ev) {
     hipError_t e = gist_check(a);
     if (e != hipSuccess) return e;
     const int G = a.Hq / a.Hkv;
-    const long long W = 2LL * a.B * a.Hkv * a.M * (a.L / kPBlk) * ((G + 3) / 4);
-    if (W <= 0) return no_kernel(ev, s);
-    if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    e = hipFuncSetAttribute((const void*)gist_prefill_mfma_kernel<false>,
+    const long long Wr = 2LL * a.B * a.Hkv * a.M * (a.L / kPBlk) * ((G + 3) / 4);
+    const long long Wgs = 2LL * a.B * a.Hkv * (a.Gp / kPBlk) * ((G + 3) / 4);
+    if (Wr + Wgs <= 0) return no_kernel(ev, s);
+    if (Wr + Wgs > 0x7fffffffLL) return hipErrorNotSupported;
+    a.w_gist_rows = (int)Wgs;
+    e = hipFuncSetAttribute((const void*)gist_prefill_mfma_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
     if (e != hipSuccess) return e;
-    return dispatch(gist_prefill_mfma_kernel<false>, dim3((unsigned)W), dim3(256), kPLds, s, ev,
-                    a);
-}
-
-hipError_t launch_gist_prefill_gists(const GistPrefillLaunch& a, hipStream_t s,
-                                     const KernelEvents& ev) {
-    hipError_t e = gist_check(a);
-    if (e != hipSuccess) return e;
-    const int G = a.Hq / a.Hkv;
-    const long long W = 2LL * a.B * a.Hkv * (a.Gp / kPBlk) * ((G + 3) / 4);
-    if (W <= 0) return no_kernel(ev, s);
-    if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    e = hipFuncSetAttribute((const void*)gist_prefill_mfma_kernel<true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
-    if (e != hipSuccess) return e;
-    return dispatch(gist_prefill_mfma_kernel<true>, dim3((unsigned)W), dim3(256), kPLds, s, ev,
-                    a);
+    return dispatch(gist_prefill_mfma_kernel, dim3((unsigned)(Wr + Wgs)), dim3(256), kPLds, s,
+                    ev, a);
 }
 
 }  // namespace tcs

@@ -159,14 +159,13 @@ struct GistPrefillLaunch {
     float sigma;
     float* out;               // [B][Hq][T'][d]
     float* lse;               // [B][Hq][T'] or null
+    int w_gist_rows;          // set by the launcher: the gist-row workgroups of the row grid
 };
 
 hipError_t launch_gist_gather(const GistPrefillLaunch& a, hipStream_t s,
                               const KernelEvents& ev = {});
-hipError_t launch_gist_prefill_raw(const GistPrefillLaunch& a, hipStream_t s,
-                                   const KernelEvents& ev = {});
-hipError_t launch_gist_prefill_gists(const GistPrefillLaunch& a, hipStream_t s,
-                                     const KernelEvents& ev = {});
+hipError_t launch_gist_prefill_rows(GistPrefillLaunch a, hipStream_t s,
+                                    const KernelEvents& ev = {});
 hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s,
                                  const KernelEvents& ev = {});
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s, const KernelEvents& ev = {});
