@@ -339,7 +339,7 @@ tcs_status sparse_attn_gist_prefill_timed(const tcs_gist_prefill_params* p,
  * HBM read ceiling the decode kernels' bandwidth is compared with.  `sink` (device memory of
  * TCS_STREAM_READ_BLOCKS 32-bit words) receives one word per workgroup so the loads cannot be
  * elided.  TCS_ERR_NULL for a null pointer, TCS_ERR_SHAPE for misalignment. */
-#define TCS_STREAM_READ_BLOCKS 2048
+#define TCS_STREAM_READ_BLOCKS 4096
 tcs_status tcs_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 /* Static string naming a status code. */

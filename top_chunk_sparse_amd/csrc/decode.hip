@@ -37,7 +37,10 @@ constexpr int kMaxSliceRows = 1024;   // rows (gists, or page rows) one workgrou
 #define TCS_K_U 2       // row passes per batch of loads in the K phase (two batches in flight)
 #endif
 #ifndef TCS_V_U
-#define TCS_V_U 2       // row passes per batch of loads in the V phase (two batches in flight)
+// row passes per batch of loads in the V phase (two batches in flight).  At 128K tokens 4 beats
+// 2 (gist kernel 51.8 -> 49.0 us): the V phase has no logits to compute, so only the depth of
+// the loads in flight limits it; 6 and 8 cost occupancy (registers) and lose.
+#define TCS_V_U 4
 #endif
 #ifndef TCS_CK_U
 #define TCS_CK_U TCS_K_U   // the same, for the chunk kernel's K phase
@@ -1038,18 +1041,22 @@ __global__ void fill_kernel(int32_t* p, long long n, int32_t v) {
 // HBM ceiling the decode kernels are measured against.
 __global__ void __launch_bounds__(256) stream_read_kernel(const uint16_t* p, long long n16,
                                                           unsigned* sink) {
-    const long long stride = (long long)gridDim.x * 256;
-    long long i = blockIdx.x * 256LL + threadIdx.x;
+    // Each workgroup reads one contiguous range, 8 loads of 16 B per thread in flight (a wave
+    // covers 8 KB per step): on gfx950 this reads faster than a grid-stride walk of the same
+    // bytes (6.2 against 5.6 TB/s for 2 GiB, measured on one box).
+    constexpr int U = 8, STEP = 256 * U;
+    const long long per = ((n16 + gridDim.x - 1) / gridDim.x + STEP - 1) / STEP * STEP;
+    const long long lo = blockIdx.x * per, hi = min(lo + per, n16);
     unsigned acc = 0u;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = ld16(p + 8 * i), b = ld16(p + 8 * (i + stride));
-        const uint4 c = ld16(p + 8 * (i + 2 * stride)), d = ld16(p + 8 * (i + 3 * stride));
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
-        acc ^= c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-    }
-    for (; i < n16; i += stride) {
-        const uint4 a = ld16(p + 8 * i);
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    for (long long base = lo; base < hi; base += STEP) {
+        uint4 r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long i = base + u * 256 + threadIdx.x;
+            r[u] = i < hi ? ld16(p + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
     }
     __shared__ unsigned red[4];
     for (int off = 32; off >= 1; off >>= 1) acc ^= (unsigned)__shfl_xor((int)acc, off);

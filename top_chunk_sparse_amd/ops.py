@@ -93,7 +93,7 @@ def lib():
     return _lib
 
 
-STREAM_READ_BLOCKS = 2048   # TCS_STREAM_READ_BLOCKS
+STREAM_READ_BLOCKS = 4096   # TCS_STREAM_READ_BLOCKS
 
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
