@@ -80,10 +80,16 @@ __global__ void __launch_bounds__(256) prefill_bwd_inverse_kernel(PrefillBwdLaun
 }
 
 // Two workgroups per CU (one would leave one wave per SIMD with nothing to hide its latency),
-// so 256 registers per lane: the dO^T operand is re-read for every block from L1 / L2 rather
-// than held for the whole loop, which keeps the kernel free of spills.
+// so 256 registers per lane.  Blocks are copied global -> LDS directly (no staging registers)
+// into two buffers that are distinct LDS objects, the block loop unrolled by two so that every
+// copy and every operand read names its buffer: the compiler's wait counting then lets the
+// operand reads of one buffer run while the next block's copy into the other is in flight.
+// The registers this frees hold the dO^T operand for the whole loop.
 __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch a) {
-    extern __shared__ __align__(16) char lds[];
+    __shared__ __align__(16) char tile_a[2 * kPTile];   // K then V of one block
+    __shared__ __align__(16) char tile_b[2 * kPTile];
+    __shared__ int ring_j[kRing];
+    __shared__ float ring_g[kRing];
     const int G = a.Hq / a.Hkv;
     const int nb = a.T / kPBlk;
     const int nhg = (G + 3) >> 2;
@@ -108,8 +114,6 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
     const int ke = a.ksel > 0 ? min(a.ksel, i) : 0;
     const int32_t* selrow = a.sel ? a.sel + ((size_t)unit * nb + i) * a.ksel : nullptr;
     const float* grow = a.gamma ? a.gamma + ((size_t)unit * nb + i) * a.ksel : nullptr;
-    int* ring_j = reinterpret_cast<int*>(lds + kPLds);
-    float* ring_g = reinterpret_cast<float*>(lds + kPLds + kRing * 4);
     auto fill_ring = [&](int x0) {
         const int x = x0 + threadIdx.x;
         if (threadIdx.x < kRing / 2 && x < ke) {
@@ -120,26 +124,40 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
     fill_ring(0);
     fill_ring(kRing / 2);
 
-    // K tiles in the transposable layout (read as K and as K^T), V tiles in the row layout.
+    // K tiles in the transposable layout (read as K and as K^T), V tiles in the row layout;
+    // block j's K tile at buf, its V tile at buf + kPTile, chunk c of wave w the 1 KB at
+    // (4 c + w) KB of each
     const CopyOffsets gk = copy_offsets(kSwzT, w, lane), gv = copy_offsets(kSwzK, w, lane);
-    uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
-    TCS_STAGE_LOAD(kbase + (size_t)i * kPBlk * kPD, vbase + (size_t)i * kPBlk * kPD);
+    auto dma = [&](int j, char* buf) {
+        const char* kc = reinterpret_cast<const char*>(kbase + (size_t)j * kPBlk * kPD);
+        const char* vc = reinterpret_cast<const char*>(vbase + (size_t)j * kPBlk * kPD);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            __builtin_amdgcn_global_load_lds(kc + gk.c[c], (lds_void*)(buf + (4 * c + w) * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vc + gv.c[c],
+                                             (lds_void*)(buf + kPTile + (4 * c + w) * 1024), 16,
+                                             0, 0);
+        }
+    };
+    dma(i, tile_a);
 
     const size_t qrow = ((size_t)(b * a.Hq + kv * G + (active ? head : 0)) * a.T +
                          (size_t)i * kPBlk + 32 * rh + c32);
-    bf16x8 qf[8];   // Q^T operand of this lane's query row (dO^T is re-read per block)
-    const uint16_t* gp = a.dout + qrow * kPD + 8 * h;
-    load_q_operand(a.q + (qrow - c32) * kPD, q_stage_lds(lds, w), lane, qf);
+    // Q^T and dO^T operands of this lane's query row, both for the whole loop, read whole
+    // through this wave's 8 KB of tile_b (free until the first block copy into it)
+    char* stage = tile_b + w * kQRowsLds;
+    bf16x8 qf[8], gf[8];
+    load_q_operand(a.q + (qrow - c32) * kPD, stage, lane, qf);
+    load_q_operand(a.dout + (qrow - c32) * kPD, stage, lane, gf);
     const float lse2 = a.lse[qrow] * kLog2e;
     const float Dq = a.D[qrow];
-    TCS_STAGE_STORE(lds, lds + 2 * kPTile);
 
     const int koff0 = c32 * 64 + (((0 + h) ^ swz_t(c32)) << 4);
     const int koff1 = c32 * 64 + (((2 + h) ^ swz_t(c32)) << 4);
     const int voff0 = c32 * 64 + (((0 + h) ^ swz_k(c32)) << 4);
     const int voff1 = c32 * 64 + (((2 + h) ^ swz_k(c32)) << 4);
     const TrOffsets toff = tr_offsets_t(lane);
-    wait_vmem();
 
     const float cs = a.sigma * kLog2e;
     float* dg = a.dgp + ((((size_t)unit * nb + i) * 2 + rh) * (size_t)(nhg * 4) + head) * a.ksel;
@@ -147,25 +165,21 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) dq[dt] = f32x16{};
 
-    for (int t = 0; t <= ke; ++t) {
-        __syncthreads();
-        const int buf = t & 1;
+    // block t is in cur; the copy of block t + 1 goes into nxt once every wave is past block
+    // t - 1 (which was in nxt)
+    auto block = [&](int t, char* cur, char* nxt) {
+        wait_vmem();       // this wave's part of block t has landed
+        __syncthreads();   // and every wave's; every wave is done with nxt
         const float bias = t > 0 ? __int_as_float(__builtin_amdgcn_readfirstlane(
                                        __float_as_int(ring_g[(t - 1) & (kRing - 1)])))
                                  : 0.f;
-        if (t < ke) {
-            const int jn = __builtin_amdgcn_readfirstlane(ring_j[t & (kRing - 1)]);
-            TCS_STAGE_LOAD(kbase + (size_t)jn * kPBlk * kPD, vbase + (size_t)jn * kPBlk * kPD);
-        }
+        if (t < ke) dma(__builtin_amdgcn_readfirstlane(ring_j[t & (kRing - 1)]), nxt);
         if (t > kRing / 2 && ((t - 1) & (kRing / 2 - 1)) == 0 && t - 1 + kRing / 2 < ke)
             fill_ring(t - 1 + kRing / 2);
         if (active) {
             const bool half = (t == 0) && rh == 0;   // diagonal, first row half: keys 0..31
-            const char* kt = lds + buf * kPTile;
-            const char* vt = lds + (2 + buf) * kPTile;
-            bf16x8 gf[8];   // dO^T operand (L1 / L2 resident across the blocks)
-#pragma unroll
-            for (int kd = 0; kd < 8; ++kd) gf[kd] = *reinterpret_cast<const bf16x8*>(gp + 16 * kd);
+            const char* kt = cur;
+            const char* vt = cur + kPTile;
             f32x16 s[2], dp[2];
             s[0] = s[1] = dp[0] = dp[1] = f32x16{};
             if (half) {
@@ -208,11 +222,16 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
                         t_operand(ktlo, kthi, dt, st), db, dq[dt], 0, 0, 0);
             }
         }
-        if (t < ke) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
+    };
+    for (int t = 0; t <= ke; t += 2) {
+        block(t, tile_a, tile_b);
+        if (t + 1 <= ke) block(t + 1, tile_b, tile_a);
     }
     __syncthreads();   // every wave is done with the last block's tiles
     if (!active) return;
-    store_rows_f32(dq, a.sigma, lds + w * kORowsLds, a.dq + (qrow - c32) * kPD, lane);
+    // the output through this wave's 16 KB: waves 0, 1 in tile_a, waves 2, 3 in tile_b
+    store_rows_f32(dq, a.sigma, (w < 2 ? tile_a : tile_b) + (w & 1) * kORowsLds,
+                   a.dq + (qrow - c32) * kPD, lane);
 }
 
 // dk / dv: a workgroup of four waves per (unit, key block j).  Wave w works on keys
@@ -507,10 +526,7 @@ hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s,
     const long long W = 2LL * a.B * a.Hkv * (a.T / kPBlk) * ((G + 3) / 4);
     if (W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    e = hipFuncSetAttribute((const void*)prefill_bwd_dq_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kPLdsAll);
-    if (e != hipSuccess) return e;
-    return dispatch(prefill_bwd_dq_kernel, dim3((unsigned)W), dim3(256), kPLdsAll, s, ev, a);
+    return dispatch(prefill_bwd_dq_kernel, dim3((unsigned)W), dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s,
