@@ -84,13 +84,16 @@ hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s,
 // sub-row the 16-byte unit u of row r is stored at u ^ swz(r): for K, ((r >> 1) & 3) ^
 // ((r >> 3) & 1) puts the 16 rows that one 128-bit read serves per cycle (and each half of
 // them) on distinct banks; for V, (r & 2) keeps the 4 rows x 32 B of a transposing read on
-// distinct banks.  Blocks are double buffered: the next block's global loads are issued into
-// registers at the top of an iteration and written to the other LDS buffer at its end.  (A
-// direct global-to-LDS copy would save those registers, but the compiler then cannot count
-// LDS reads precisely and makes every operand read wait for all earlier ones.)
+// distinct banks.  Blocks are double buffered and copied global -> LDS directly (no staging
+// registers): the two buffers are distinct LDS objects and the block loop is unrolled by two,
+// so every copy and operand read names its buffer and the compiler's wait counting lets the
+// operand reads of one buffer run while the next block's copy into the other is in flight.
 
 __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
-    extern __shared__ __align__(16) char lds[];
+    __shared__ __align__(16) char tile_a[2 * kPTile];   // K then V of one block
+    __shared__ __align__(16) char tile_b[2 * kPTile];
+    __shared__ int ring_j[kRing];
+    __shared__ float ring_g[kRing];
     const int G = a.Hq / a.Hkv;
     const int nb = a.T / kPBlk;
     const int nhg = (G + 3) >> 2;
@@ -116,7 +119,6 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
 
     const uint16_t* kbase = a.k + (size_t)unit * a.T * kPD;
     const uint16_t* vbase = a.v + (size_t)unit * a.T * kPD;
-    // LDS: K tiles at [0, 2 kPTile), V tiles at [2 kPTile, 4 kPTile), then the ring.
 
     const int ke = a.ksel > 0 ? min(a.ksel, i) : 0;
     const int32_t* selrow = a.sel ? a.sel + ((size_t)unit * nb + i) * a.ksel : nullptr;
@@ -124,8 +126,6 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
 
     // The chosen blocks and their gates pass through a ring of kRing entries in LDS, refilled
     // kRing / 2 entries at a time well ahead of use.
-    int* ring_j = reinterpret_cast<int*>(lds + kPLds);
-    float* ring_g = reinterpret_cast<float*>(lds + kPLds + kRing * 4);
     auto fill_ring = [&](int x0) {   // entries x0 .. x0 + kRing/2 - 1 (those < ke)
         const int x = x0 + threadIdx.x;
         if (threadIdx.x < kRing / 2 && x < ke) {
@@ -137,16 +137,28 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
     fill_ring(kRing / 2);
 
     // Block 0 of the list is the diagonal block; blocks 1..ke are the chosen earlier ones.
+    // Block j's K tile goes to buf, its V tile to buf + kPTile; chunk c of wave w is the 1 KB
+    // at (4 c + w) KB of each.
     const CopyOffsets gk = copy_offsets(kSwzK, w, lane), gv = copy_offsets(kSwzV, w, lane);
-    uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
-    TCS_STAGE_LOAD(kbase + (size_t)i * kPBlk * kPD, vbase + (size_t)i * kPBlk * kPD);
+    auto dma = [&](int j, char* buf) {
+        const char* kc = reinterpret_cast<const char*>(kbase + (size_t)j * kPBlk * kPD);
+        const char* vc = reinterpret_cast<const char*>(vbase + (size_t)j * kPBlk * kPD);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            __builtin_amdgcn_global_load_lds(kc + gk.c[c], (lds_void*)(buf + (4 * c + w) * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vc + gv.c[c],
+                                             (lds_void*)(buf + kPTile + (4 * c + w) * 1024), 16,
+                                             0, 0);
+        }
+    };
+    dma(i, tile_a);
 
     // Q^T operand: qf[kd] = Q[32 rh + c32][16 kd + 8 h .. +7] of this wave's head.
     const size_t qrow = ((size_t)(b * a.Hq + kv * G + (active ? head : 0)) * a.T +
                          (size_t)i * kPBlk + 32 * rh + c32);
-    bf16x8 qf[8];
-    load_q_operand(a.q + (qrow - c32) * kPD, q_stage_lds(lds, w), lane, qf);
-    TCS_STAGE_STORE(lds, lds + 2 * kPTile);
+    bf16x8 qf[8];   // read whole through this wave's 8 KB of tile_b (free until block 1)
+    load_q_operand(a.q + (qrow - c32) * kPD, tile_b + w * kQRowsLds, lane, qf);
 
     // Per-lane LDS offsets (bytes) of the operand reads; everything else is an immediate.
     //   K: row r = 32 x + c32, d = 16 kd + 8 h: sub-tile kd / 2, unit (2 (kd & 1) + h) ^ swz.
@@ -157,10 +169,6 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
     const int g = lane >> 4, L = lane & 15, rr = L >> 2, cc = L & 3;
     const int voff = (4 * h + rr) * 64 + (((2 * (g & 1) + (cc >> 1)) ^ swz_v(rr)) << 4) + ((cc & 1) << 3);
 
-    // The query operands must have landed before the loop: otherwise the compiler's wait
-    // counting at the loop head cannot tell them from the next block's loads and makes every
-    // iteration's first products wait for that block's global loads.
-    wait_vmem();
 
     const float cs = a.sigma * kLog2e;
     f32x16 o[4];
@@ -169,17 +177,15 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
     float m = 0.f, l = 0.f;
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-    for (int t = 0; t <= ke; ++t) {
-        // Block t is in buffer t & 1; every wave is done with buffer (t + 1) & 1.
-        __syncthreads();
-        const int buf = t & 1;
-        const float bias = t > 0 ? __int_as_float(__builtin_amdgcn_readfirstlane(
-                                       __float_as_int(ring_g[(t - 1) & (kRing - 1)])))
-                                 : 0.f;
-        if (t < ke) {
-            const int jn = __builtin_amdgcn_readfirstlane(ring_j[t & (kRing - 1)]);
-            TCS_STAGE_LOAD(kbase + (size_t)jn * kPBlk * kPD, vbase + (size_t)jn * kPBlk * kPD);
-        }
+    // block t is in cur; the copy of block t + 1 goes into nxt once every wave is past block
+    // t - 1 (which was in nxt)
+    auto block = [&](int t, bool first, const char* cur, char* nxt) {   // first: t == 0
+        wait_vmem();       // this wave's part of block t has landed
+        __syncthreads();   // and every wave's; every wave is done with nxt
+        const float bias = first ? 0.f
+                                 : __int_as_float(__builtin_amdgcn_readfirstlane(
+                                       __float_as_int(ring_g[(t - 1) & (kRing - 1)])));
+        if (t < ke) dma(__builtin_amdgcn_readfirstlane(ring_j[t & (kRing - 1)]), nxt);
         // Iteration t reads entries t - 1 and t.  Past this iteration's barrier every entry
         // below t is dead, so at t = 1 + n kRing/2 (n >= 1) the slots of entries
         // t - 1 - kRing/2 .. t - 2 take entries t - 1 + kRing/2 .. t - 2 + kRing, first read
@@ -188,9 +194,9 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
             fill_ring(t - 1 + kRing / 2);
         if (active) {
             // On the diagonal block, rows of the first half see only keys 0..31.
-            const bool half = (t == 0) && rh == 0;
-            const char* kt = lds + buf * kPTile;
-            const char* vt = lds + (2 + buf) * kPTile + voff;
+            const bool half = first && rh == 0;
+            const char* kt = cur;
+            const char* vt = cur + kPTile + voff;
 
             // ---- S^T = K Q^T ----
             f32x16 s[2];
@@ -207,7 +213,7 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
             }
 
             // ---- online softmax (log2 domain) ----
-            if (t == 0) {   // diagonal block: key row r sees query row q only if r <= q
+            if (first) {   // diagonal block: key row r sees query row q only if r <= q
                 const int q = 32 * rh + c32;
 #pragma unroll
                 for (int x = 0; x < 2; ++x)
@@ -224,7 +230,7 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
                 for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[x][e]);
             mx = pair_max(mx);
             const float mb = mx * cs + bias;
-            if (t == 0) {
+            if (first) {
                 m = mb;
             } else if (__builtin_amdgcn_ballot_w64(mb > m + kRescaleSlack)) {
                 const float mn = fmaxf(m, mb);
@@ -282,14 +288,19 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
             }
             l += sum;
         }
-        if (t < ke) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
+    };
+    block(0, true, tile_a, tile_b);
+    for (int t = 1; t <= ke; t += 2) {
+        block(t, false, tile_b, tile_a);
+        if (t + 1 <= ke) block(t + 1, false, tile_a, tile_b);
     }
     // ---- epilogue: O = O^T / l, lse = m + log2 l (back to natural log) ----
     __syncthreads();   // every wave is done with the last block's tiles
     if (!active) return;
     const float lt = pair_sum(l);
     const float inv = 1.f / lt;
-    store_rows_f32(o, inv, lds + w * kORowsLds, a.out + (qrow - c32) * kPD, lane);
+    store_rows_f32(o, inv, (w < 2 ? tile_a : tile_b) + (w & 1) * kORowsLds,
+                   a.out + (qrow - c32) * kPD, lane);
     if (a.lse && h == 0) a.lse[qrow] = (m + log2f(lt)) * kLn2;
 }
 
@@ -299,12 +310,7 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s, const KernelEve
     const long long W = 2LL * a.B * a.Hkv * (a.T / kPBlk) * ((G + 3) / 4);
     if (W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    // the dynamic LDS (tiles + ring) is above the 64 KB default limit; set on every call (no
-    // library state, and it holds for whichever device is current)
-    const hipError_t e = hipFuncSetAttribute((const void*)prefill_fwd_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kPLdsAll);
-    if (e != hipSuccess) return e;
-    return dispatch(prefill_fwd_kernel, dim3((unsigned)W), dim3(256), kPLdsAll, s, ev, a);
+    return dispatch(prefill_fwd_kernel, dim3((unsigned)W), dim3(256), 0, s, ev, a);
 }
 
 }  // namespace tcs
