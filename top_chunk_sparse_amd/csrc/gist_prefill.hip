@@ -52,10 +52,13 @@ __global__ void __launch_bounds__(256) gist_gather_kernel(GistPrefillLaunch a) {
     }
 }
 
-// Workgroup bid0 of a grid of Wg workgroups of one row kind.
+// Workgroup bid0 of a grid of Wg workgroups of one row kind.  tile_a and tile_b are the
+// kernel's two block buffers (distinct LDS objects, K then V of one block each): blocks are
+// copied global -> LDS directly, and the loop is unrolled by two so that every copy and operand
+// read names its buffer, as in the SAS forward.
 template <bool GROWS>
-__device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, int bid0, int Wg) {
-    extern __shared__ __align__(16) char lds[];
+__device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, int bid0, int Wg,
+                                                  char* tile_a, char* tile_b) {
     const int G = a.Hq / a.Hkv;
     const int nhg = (G + 3) >> 2;
     const int nrb = a.L / kPBlk;                 // raw blocks per chunk
@@ -121,8 +124,19 @@ __device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, in
     };
 
     const CopyOffsets gk = copy_offsets(kSwzK, w, lane), gv = copy_offsets(kSwzV, w, lane);
-    uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
-    TCS_STAGE_LOAD(kblock(0), vblock(0));
+    auto dma = [&](int t, char* buf) {   // block t: K tile at buf, V tile at buf + kPTile
+        const char* kc = reinterpret_cast<const char*>(kblock(t));
+        const char* vc = reinterpret_cast<const char*>(vblock(t));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            __builtin_amdgcn_global_load_lds(kc + gk.c[c], (lds_void*)(buf + (4 * c + w) * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vc + gv.c[c],
+                                             (lds_void*)(buf + kPTile + (4 * c + w) * 1024), 16,
+                                             0, 0);
+        }
+    };
+    dma(0, tile_a);
 
     // this lane's query row: raw row 64 rb + 32 rh + c32 of chunk c, or gathered gist row
     // r = R0 + c32 (clamped for loading when r is padding; nothing is written for it)
@@ -135,20 +149,18 @@ __device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, in
     const size_t qrow = (size_t)(b * a.Hq + kv * G + (active ? head : 0)) * Tp + qpos;
     bf16x8 qf[8];
     if constexpr (!GROWS) {   // raw rows: the wave's 32 rows are consecutive positions
-        load_q_operand(a.q + (qrow - c32) * kPD, q_stage_lds(lds, w), lane, qf);
+        load_q_operand(a.q + (qrow - c32) * kPD, tile_b + w * kQRowsLds, lane, qf);
     } else {
         const uint16_t* qp = a.q + qrow * kPD + 8 * h;
 #pragma unroll
         for (int kd = 0; kd < 8; ++kd) qf[kd] = *reinterpret_cast<const bf16x8*>(qp + 16 * kd);
     }
-    TCS_STAGE_STORE(lds, lds + 2 * kPTile);
 
     const int koff0 = c32 * 64 + (((0 + h) ^ swz_k(c32)) << 4);
     const int koff1 = c32 * 64 + (((2 + h) ^ swz_k(c32)) << 4);
     const int g16 = lane >> 4, L16 = lane & 15, rr = L16 >> 2, cc = L16 & 3;
     const int voff = (4 * h + rr) * 64 + (((2 * (g16 & 1) + (cc >> 1)) ^ swz_v(rr)) << 4) +
                      ((cc & 1) << 3);
-    wait_vmem();
 
     const float cs = a.sigma * kLog2e;
     f32x16 o[4];
@@ -157,15 +169,17 @@ __device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, in
     float m = 0.f, l = 0.f;
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-    for (int t = 0; t < nblk; ++t) {
-        __syncthreads();
-        const int buf = t & 1;
-        if (t + 1 < nblk) TCS_STAGE_LOAD(kblock(t + 1), vblock(t + 1));
+    // block t is in cur; the copy of block t + 1 goes into nxt once every wave is past block
+    // t - 1 (which was in nxt); first: t == 0
+    auto block = [&](int t, bool first, const char* cur, char* nxt) {
+        wait_vmem();       // this wave's part of block t has landed
+        __syncthreads();   // and every wave's; every wave is done with nxt
+        if (t + 1 < nblk) dma(t + 1, nxt);
         if (active) {
-            const bool half = !GROWS && (t == 0) && rh == 0;
+            const bool half = !GROWS && first && rh == 0;
             const int cut = (!GROWS && t == nblk - 1 && t > rb) ? last_valid : kPBlk;
-            const char* kt = lds + buf * kPTile;
-            const char* vt = lds + (2 + buf) * kPTile + voff;
+            const char* kt = cur;
+            const char* vt = cur + kPTile + voff;
             f32x16 s[2];
             s[0] = s[1] = f32x16{};
             if (half) qk_product<1>(kt, koff0, koff1, qf, s);
@@ -195,7 +209,7 @@ __device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, in
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = 32 * x + 8 * (e >> 2) + 4 * h + (e & 3);
-                        if ((t == 0 && key > q) || key >= cut) s[x][e] = -INFINITY;
+                        if ((first && key > q) || key >= cut) s[x][e] = -INFINITY;
                     }
             }
             float mx = s[0][0];
@@ -206,7 +220,7 @@ __device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, in
             mx = pair_max(mx);
             // a raw block of another chunk leaves a gist row without keys: no update
             const float mb = mx == -INFINITY ? m : mx * cs;
-            if (t == 0) {
+            if (first) {
                 m = mb;
             } else if (__builtin_amdgcn_ballot_w64(mb > m + kRescaleSlack)) {
                 const float mn = fmaxf(m, mb);
@@ -251,14 +265,19 @@ __device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, in
             }
             l += sum;
         }
-        if (t + 1 < nblk) TCS_STAGE_STORE(lds + (buf ^ 1) * kPTile, lds + (2 + (buf ^ 1)) * kPTile);
+    };
+    block(0, true, tile_a, tile_b);
+    for (int t = 1; t < nblk; t += 2) {
+        block(t, false, tile_b, tile_a);
+        if (t + 1 < nblk) block(t + 1, false, tile_a, tile_b);
     }
     if constexpr (!GROWS) {
         // raw rows: a wave's 32 rows are consecutive positions, stored as whole rows
         __syncthreads();   // every wave is done with the last block's tiles
         if (!active) return;
         const float lt = pair_sum(l);
-        store_rows_f32(o, 1.f / lt, lds + w * kORowsLds, a.out + (qrow - c32) * kPD, lane);
+        store_rows_f32(o, 1.f / lt, (w < 2 ? tile_a : tile_b) + (w & 1) * kORowsLds,
+                       a.out + (qrow - c32) * kPD, lane);
         if (a.lse && h == 0) a.lse[qrow] = (m + log2f(lt)) * kLn2;
         return;
     }
@@ -285,9 +304,11 @@ __device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, in
 // slot the gist rows leave.  The gist-row share is a multiple of 8, so both shares keep the
 // XCD-contiguous ranges.
 __global__ void __launch_bounds__(256, 2) gist_prefill_mfma_kernel(GistPrefillLaunch a) {
+    __shared__ __align__(16) char tile_a[2 * kPTile];
+    __shared__ __align__(16) char tile_b[2 * kPTile];
     const int wg = a.w_gist_rows;
-    if ((int)blockIdx.x < wg) gist_prefill_rows<true>(a, blockIdx.x, wg);
-    else gist_prefill_rows<false>(a, blockIdx.x - wg, gridDim.x - wg);
+    if ((int)blockIdx.x < wg) gist_prefill_rows<true>(a, blockIdx.x, wg, tile_a, tile_b);
+    else gist_prefill_rows<false>(a, blockIdx.x - wg, gridDim.x - wg, tile_a, tile_b);
 }
 
 static hipError_t gist_check(const GistPrefillLaunch& a) {
@@ -316,11 +337,7 @@ hipError_t launch_gist_prefill_rows(GistPrefillLaunch a, hipStream_t s, const Ke
     if (Wr + Wgs <= 0) return no_kernel(ev, s);
     if (Wr + Wgs > 0x7fffffffLL) return hipErrorNotSupported;
     a.w_gist_rows = (int)Wgs;
-    e = hipFuncSetAttribute((const void*)gist_prefill_mfma_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
-    if (e != hipSuccess) return e;
-    return dispatch(gist_prefill_mfma_kernel, dim3((unsigned)(Wr + Wgs)), dim3(256), kPLds, s,
-                    ev, a);
+    return dispatch(gist_prefill_mfma_kernel, dim3((unsigned)(Wr + Wgs)), dim3(256), 0, s, ev, a);
 }
 
 }  // namespace tcs
