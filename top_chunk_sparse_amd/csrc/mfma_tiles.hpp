@@ -138,6 +138,19 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // s_waitcnt lgkmcnt(0) with vmcnt / expcnt left free (gfx9 encoding)
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
+// Workgroup barrier for a hand-off through LDS written by ordinary LDS stores, while global ->
+// LDS copies into another buffer are still in flight: __syncthreads() would also wait for
+// those copies (its fence covers every LDS write).  LDS operations of all waves execute in
+// one order, so the writer's stores, issued before its barrier, precede the reader's loads,
+// issued after it; the empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_handoff_barrier() {
+    wait_lds();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Per-lane LDS offsets of the transposing operand reads (the forward's V^T pattern) in a tile
 // stored with swz_t.  The first read of a step covers rows 16 st + 4 h + rr, the second the
 // same rows plus 8, whose swizzle differs by 2, so each read has its own offset.

@@ -242,16 +242,20 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
 //   role B (w >= 2): dP = dO V^T, dS = P (dP - D) with the P that role A left in LDS,
 //                   dK^T += Q^T dS.
 // Every (head, query block) pair that sees j is one item; the four waves share its Q and dO
-// tiles, and the next item's tiles travel into registers while the current one is computed
-// (two LDS buffers).  An item has two phases: the S / dP products (with the exponentials of
+// tiles, and the next item's tiles are copied global -> LDS directly while the current one is
+// computed (two LDS buffers, distinct objects, the loop unrolled by two as in the dq kernel).  An item has two phases: the S / dP products (with the exponentials of
 // role A), a barrier, then the dV / dK products.  Both roles accumulate in registers to the
 // end of the list.
 constexpr int kBwdBuf = 2 * kPTile + 2 * kPBlk * 4;   // Q tile, dO tile, lse2 and D of 64 rows
 constexpr int kBwdP = 4 * 64 * 16;                    // P of 32 keys x 64 rows, fp16
-constexpr int kBwdDkvLds = 2 * kBwdBuf + 2 * kBwdP + 16;   // + two list slots
 
 __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunch a) {
-    extern __shared__ __align__(16) char lds[];
+    // two pair buffers (distinct LDS objects: see the dq kernel), the P hand-over, the list slots
+    __shared__ __align__(16) char buf_a[kBwdBuf];
+    __shared__ __align__(16) char buf_b[kBwdBuf];
+    __shared__ __align__(16) char pshare[2 * kBwdP];
+    __shared__ int slot_i[2];
+    __shared__ float slot_g[2];
     const int G = a.Hq / a.Hkv;
     const int nb = a.T / kPBlk;
     const int units = a.B * a.Hkv;
@@ -287,7 +291,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
     const int key = 32 * kh + c32;            // this lane's key row within block j
     // P of this key half: step st of lane l at (64 st + l) * 16 bytes, the same lane and step
     // layout in which role B holds dP, so the hand-over needs no shuffle
-    char* pbuf = lds + 2 * kBwdBuf + kh * kBwdP + lane * 16;
+    char* pbuf = pshare + kh * kBwdP + lane * 16;
     const CopyOffsets gk = copy_offsets(kSwzT, w, lane), gv = gk;
 
     // (head, query block) pair it: head it / nlist; list position t = it % nlist: query block j
@@ -295,8 +299,6 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
     // gate come from LDS slot it & 1: the lists are read two pairs ahead, with the tiles of the
     // next pair, and thread 0 writes the slot with the tiles at the end of an iteration, so no
     // list read waits in the loop.
-    int* slot_i = reinterpret_cast<int*>(lds + 2 * kBwdBuf + 2 * kBwdP);
-    float* slot_g = reinterpret_cast<float*>(slot_i + 2);
     int xi = 0;        // raw list entries of a pair (loaded by every thread from one address)
     float xg = 0.f;
     auto list_load = [&](int it) {
@@ -312,21 +314,28 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
     auto qrow_of = [&](int it, int i) {
         return (size_t)(b * a.Hq + kv * G + it / nlist) * a.T + (size_t)i * kPBlk;
     };
-    // staged copy of a pair's Q and dO tiles (4 + 4 chunks of 16 B per thread) and of its rows'
-    // lse (threads 0..63, stored as lse2) and D (threads 64..127)
-#define TCS_BWD_LOAD(qrow0)                                                                     \
-    do {                                                                                        \
-        TCS_STAGE_LOAD(a.q + (qrow0) * kPD, a.dout + (qrow0) * kPD);                            \
-        if (tid < 2 * kPBlk) xl = tid < kPBlk ? a.lse[(qrow0) + tid] : a.D[(qrow0) + tid - kPBlk]; \
-    } while (0)
-#define TCS_BWD_STORE(buf)                                                                      \
-    do {                                                                                        \
-        TCS_STAGE_STORE((buf), (buf) + kPTile);                                                 \
-        if (tid < 2 * kPBlk)                                                                    \
-            reinterpret_cast<float*>((buf) + 2 * kPTile)[tid] = tid < kPBlk ? xl * kLog2e : xl; \
-    } while (0)
-    uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;   // Q chunks (sk), dO chunks (sv)
+    // a pair's Q and dO tiles straight into LDS buffer buf (Q at buf, dO at buf + kPTile; chunk
+    // c of wave w is the 1 KB at (4 c + w) KB of each); its rows' lse (threads 0..63) and D
+    // (threads 64..127) go through registers (xl) and are stored after the pair's products
+    auto dma = [&](size_t qrow0, char* buf) {
+        const char* qc = reinterpret_cast<const char*>(a.q + qrow0 * kPD);
+        const char* gc = reinterpret_cast<const char*>(a.dout + qrow0 * kPD);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            __builtin_amdgcn_global_load_lds(qc + gk.c[c], (lds_void*)(buf + (4 * c + w) * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gc + gv.c[c],
+                                             (lds_void*)(buf + kPTile + (4 * c + w) * 1024), 16,
+                                             0, 0);
+        }
+    };
     float xl = 0.f;
+    auto rows_load = [&](size_t qrow0) {
+        if (tid < 2 * kPBlk) xl = tid < kPBlk ? a.lse[qrow0 + tid] : a.D[qrow0 + tid - kPBlk];
+    };
+    auto rows_store = [&](char* buf) {
+        if (tid < 2 * kPBlk) reinterpret_cast<float*>(buf + 2 * kPTile)[tid] = xl;
+    };
 
     f32x16 acc[4];   // role A: dV^T, role B: dK^T (32 dims per tile x 32 keys)
 #pragma unroll
@@ -335,17 +344,21 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
     // pair 0 is (head 0, block j); pair 1's list entry goes to its slot before the loop
     int i_cur = j;
     float bias_cur = 0.f;
-    TCS_BWD_LOAD(qrow_of(0, j));
     list_load(min(1, nitems - 1));
-    TCS_BWD_STORE(lds);
+    rows_load(qrow_of(0, j));
+    dma(qrow_of(0, j), buf_a);
+    rows_store(buf_a);
     if (tid == 0) list_store(min(1, nitems - 1), 1);
-    wait_vmem();
-    for (int it = 0; it < nitems; ++it) {
-        __syncthreads();   // buffer and slot it & 1 are filled; every wave is done with the others
-        const char* qt = lds + (it & 1) * kBwdBuf;
+
+    // pair it is in cur; pair it + 1 is copied into nxt once every wave is past pair it - 1
+    // (which was in nxt)
+    auto pair = [&](int it, const char* cur, char* nxt) {
+        wait_vmem();       // this wave's part of pair it has landed
+        __syncthreads();   // and every wave's; slot it & 1 is written; nxt is free
+        const char* qt = cur;
         const char* gt = qt + kPTile;
-        const float* l2 = reinterpret_cast<const float*>(gt + kPTile);
-        const float* Dl = l2 + kPBlk;
+        const float* lsel = reinterpret_cast<const float*>(gt + kPTile);   // lse of the rows
+        const float* Dl = lsel + kPBlk;
         const bool diag = i_cur == j;
         const float bias = bias_cur;
         int i_nx = 0;
@@ -354,14 +367,17 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
             i_nx = __builtin_amdgcn_readfirstlane(slot_i[(it + 1) & 1]);
             bias_nx = __int_as_float(
                 __builtin_amdgcn_readfirstlane(__float_as_int(slot_g[(it + 1) & 1])));
-            TCS_BWD_LOAD(qrow_of(it + 1, i_nx));
-            list_load(min(it + 2, nitems - 1));
+            list_load(min(it + 2, nitems - 1));   // before the copy: their waits leave the copy
+            rows_load(qrow_of(it + 1, i_nx));
+            dma(qrow_of(it + 1, i_nx), nxt);
         }
 
         // ---- phase 1: S = Q K^T (A) or dP = dO V^T (B); lane: key, rows: queries ----
         f32x16 s[2];
         s[0] = s[1] = f32x16{};
-        qk_product<2>(roleA ? qt : gt, qoff0, qoff1, kvf, s);
+        // (offsets on cur rather than a select of two pointers keep the reads' LDS object
+        // visible to the compiler's wait counting)
+        qk_product<2>(cur + (roleA ? 0 : kPTile), qoff0, qoff1, kvf, s);
         bf16x8 ob[4];   // the B operands of phase 2: P (A) or dS (B), 16 query rows per step
         if (roleA) {
 #pragma unroll
@@ -369,12 +385,13 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int q0 = 32 * x + 8 * e4 + 4 * h;   // query rows q0 .. q0 + 3
-                    const float4 lq = *reinterpret_cast<const float4*>(l2 + q0);
+                    const float4 lq = *reinterpret_cast<const float4*>(lsel + q0);
                     const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int e = 4 * e4 + jj;
-                        float p = __builtin_amdgcn_exp2f(s[x][e] * cs + bias - lv[jj]);
+                        float p = __builtin_amdgcn_exp2f(
+                            fmaf(s[x][e], cs, fmaf(-lv[jj], kLog2e, bias)));
                         if (diag && key > q0 + jj) p = 0.f;   // diagonal block: token-causal
                         s[x][e] = p;
                     }
@@ -390,7 +407,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
                 *reinterpret_cast<half8*>(pbuf + st * 1024) = ph;
             }
         }
-        __syncthreads();   // P of this item is in LDS
+        lds_handoff_barrier();   // P of this item is in LDS (the next pair's copy flies on)
         if (!roleA) {
             half8 ph[4];
 #pragma unroll
@@ -416,7 +433,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
         }
 
         // ---- phase 2: dV^T += dO^T P (A) or dK^T += Q^T dS (B), 16 query rows per step ----
-        const char* tt = roleA ? gt : qt;
+        const char* tt = cur + (roleA ? kPTile : 0);
         const char* tlo = tt + toff.lo;
         const char* thi = tt + toff.hi;
 #pragma unroll
@@ -426,20 +443,22 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_operand(tlo, thi, dt, st),
                                                                   ob[st], acc[dt], 0, 0, 0);
         if (it + 1 < nitems) {
-            TCS_BWD_STORE(lds + ((it + 1) & 1) * kBwdBuf);
+            rows_store(nxt);
             if (tid == 0) list_store(min(it + 2, nitems - 1), it & 1);
             i_cur = i_nx;
             bias_cur = bias_nx;
         }
+    };
+    for (int it = 0; it < nitems; it += 2) {
+        pair(it, buf_a, buf_b);
+        if (it + 1 < nitems) pair(it + 1, buf_b, buf_a);
     }
 
     // this wave's 32 key rows: dV = dV^T (A) or dK = sigma dK^T (B); lane: key row, registers:
     // dims
     __syncthreads();   // every wave is done with the last pair's tiles
-    store_rows_f32(acc, roleA ? 1.f : a.sigma, lds + w * kORowsLds,
+    store_rows_f32(acc, roleA ? 1.f : a.sigma, (w < 2 ? buf_a : buf_b) + (w & 1) * kORowsLds,
                    (roleA ? a.dv : a.dk) + kfirst * kPD, lane);
-#undef TCS_BWD_LOAD
-#undef TCS_BWD_STORE
 }
 
 __global__ void __launch_bounds__(256) prefill_bwd_ds_kernel(PrefillBwdLaunch a) {
@@ -536,10 +555,7 @@ hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s,
     const long long W = (long long)a.B * a.Hkv * (a.T / kPBlk);
     if (W <= 0) return no_kernel(ev, s);
     if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    e = hipFuncSetAttribute((const void*)prefill_bwd_dkv_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kBwdDkvLds);
-    if (e != hipSuccess) return e;
-    return dispatch(prefill_bwd_dkv_kernel, dim3((unsigned)W), dim3(256), kBwdDkvLds, s, ev, a);
+    return dispatch(prefill_bwd_dkv_kernel, dim3((unsigned)W), dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s,
