@@ -103,7 +103,7 @@ def test_prefill_backward_2k_workload_heads():
 def test_prefill_backward_full_size_identities():
     """At 16K tokens: per KV head the dv rows add up to the group's dout rows and the dk rows to
     sigma sum dlse q (each query row's weights sum to one); every dS row sums to zero and dS is
-    zero on and above the diagonal; two calls give the same bits."""
+    zero on and above the diagonal; repeated calls give the same bits."""
     cfg = configs.PREFILL
     inp, dout, dlse, fwd, bwd = run_bwd(cfg, seed=configs.seed_for(cfg.name))
     G, sig = cfg.G, 1.0 / np.sqrt(cfg.d)
@@ -119,11 +119,15 @@ def test_prefill_backward_full_size_identities():
     upper = torch.triu(dS, 0).abs().max().item()
     say(f"    identities: dv {e_dv:.2e}  dk {e_dk:.2e}  dS row sums {rows:.2e}  upper {upper}")
     assert e_dv < 1e-3 and e_dk < 2e-2 and rows < 1e-4 and upper == 0.0
+    # every call gives the same bits (a hand-off through LDS that races shows up here first)
+    names = ("dq", "dk", "dv", "dS")
     first = [t.clone() for t in (bwd.dq, bwd.dk, bwd.dv, bwd.dS)]
-    bwd()
-    torch.cuda.synchronize()
-    for a, b in zip(first, (bwd.dq, bwd.dk, bwd.dv, bwd.dS)):
-        assert torch.equal(a, b)
+    for call in range(3):
+        bwd()
+        torch.cuda.synchronize()
+        for n, a, b in zip(names, first, (bwd.dq, bwd.dk, bwd.dv, bwd.dS)):
+            bad = (a != b).nonzero()
+            assert bad.shape[0] == 0, (call, n, bad.shape[0], bad[:4].tolist())
 
 
 def test_prefill_backward_workspace_garbage_and_reuse():

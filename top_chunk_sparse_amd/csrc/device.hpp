@@ -337,6 +337,15 @@ __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
 }
 
+// s_waitcnt vmcnt(0) lgkmcnt(0): this wave's global -> LDS copies have landed and its own LDS
+// stores are done.  Written out before the barrier of a copy loop rather than left to
+// __syncthreads(): at a loop header the compiler's wait for the LDS stores of the previous
+// iteration (reached over the back edge) has been seen to go missing next to an explicit
+// vmcnt wait, so that other waves could pass the barrier and read them early.
+__device__ __forceinline__ void wait_vmem_lds() {
+    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0x0 << 8));
+}
+
 // Every workgroup of a unit calls arrive_last() after writing its hand-off data with
 // st_shared_dev; exactly one -- the last to arrive -- gets true and may then read the others'
 // data with ld_shared_dev.  The last workgroup returns the counter to zero, so a zeroed

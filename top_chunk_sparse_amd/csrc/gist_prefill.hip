@@ -172,7 +172,7 @@ __device__ __forceinline__ void gist_prefill_rows(const GistPrefillLaunch& a, in
     // block t is in cur; the copy of block t + 1 goes into nxt once every wave is past block
     // t - 1 (which was in nxt); first: t == 0
     auto block = [&](int t, bool first, const char* cur, char* nxt) {
-        wait_vmem();       // this wave's part of block t has landed
+        wait_vmem_lds();   // this wave's part of block t has landed
         __syncthreads();   // and every wave's; every wave is done with nxt
         if (t + 1 < nblk) dma(t + 1, nxt);
         if (active) {

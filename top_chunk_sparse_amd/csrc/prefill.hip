@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillLaunch a) {
     // block t is in cur; the copy of block t + 1 goes into nxt once every wave is past block
     // t - 1 (which was in nxt)
     auto block = [&](int t, bool first, const char* cur, char* nxt) {   // first: t == 0
-        wait_vmem();       // this wave's part of block t has landed
+        wait_vmem_lds();   // this wave's part of block t has landed
         __syncthreads();   // and every wave's; every wave is done with nxt
         const float bias = first ? 0.f
                                  : __int_as_float(__builtin_amdgcn_readfirstlane(

@@ -168,7 +168,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
     // block t is in cur; the copy of block t + 1 goes into nxt once every wave is past block
     // t - 1 (which was in nxt)
     auto block = [&](int t, char* cur, char* nxt) {
-        wait_vmem();       // this wave's part of block t has landed
+        wait_vmem_lds();   // this wave's part of block t has landed
         __syncthreads();   // and every wave's; every wave is done with nxt
         const float bias = t > 0 ? __int_as_float(__builtin_amdgcn_readfirstlane(
                                        __float_as_int(ring_g[(t - 1) & (kRing - 1)])))
@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
     // pair it is in cur; pair it + 1 is copied into nxt once every wave is past pair it - 1
     // (which was in nxt)
     auto pair = [&](int it, const char* cur, char* nxt) {
-        wait_vmem();       // this wave's part of pair it has landed
+        wait_vmem_lds();   // this wave's part of pair it has landed
         __syncthreads();   // and every wave's; slot it & 1 is written; nxt is free
         const char* qt = cur;
         const char* gt = qt + kPTile;
