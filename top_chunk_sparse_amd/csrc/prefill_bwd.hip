@@ -355,10 +355,6 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
     auto pair = [&](int it, const char* cur, char* nxt) {
         wait_vmem_lds();   // this wave's part of pair it has landed
         __syncthreads();   // and every wave's; slot it & 1 is written; nxt is free
-        const char* qt = cur;
-        const char* gt = qt + kPTile;
-        const float* lsel = reinterpret_cast<const float*>(gt + kPTile);   // lse of the rows
-        const float* Dl = lsel + kPBlk;
         const bool diag = i_cur == j;
         const float bias = bias_cur;
         int i_nx = 0;
@@ -377,6 +373,19 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
         s[0] = s[1] = f32x16{};
         // (offsets on cur rather than a select of two pointers keep the reads' LDS object
         // visible to the compiler's wait counting)
+        // the rows' lse (A) or D (B), read ahead of the products so that they have landed by
+        // the time the products are done
+        float4 rs[2][4];
+        {
+            const float* rsl = reinterpret_cast<const float*>(cur + 2 * kPTile +
+                                                              (roleA ? 0 : kPBlk * 4));
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4)
+                    rs[x][e4] = *reinterpret_cast<const float4*>(rsl + 32 * x + 8 * e4 + 4 * h);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         qk_product<2>(cur + (roleA ? 0 : kPTile), qoff0, qoff1, kvf, s);
         bf16x8 ob[4];   // the B operands of phase 2: P (A) or dS (B), 16 query rows per step
         if (roleA) {
@@ -385,7 +394,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int q0 = 32 * x + 8 * e4 + 4 * h;   // query rows q0 .. q0 + 3
-                    const float4 lq = *reinterpret_cast<const float4*>(lsel + q0);
+                    const float4 lq = rs[x][e4];
                     const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
@@ -412,12 +421,12 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
             half8 ph[4];
 #pragma unroll
             for (int st = 0; st < 4; ++st) ph[st] = *reinterpret_cast<const half8*>(pbuf + st * 1024);
+            __builtin_amdgcn_sched_barrier(0);   // all four reads in flight before the first use
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
-                    const int q0 = 32 * x + 8 * e4 + 4 * h;
-                    const float4 dd = *reinterpret_cast<const float4*>(Dl + q0);
+                    const float4 dd = rs[x][e4];
                     const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
@@ -436,12 +445,23 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
         const char* tt = cur + (roleA ? kPTile : 0);
         const char* tlo = tt + toff.lo;
         const char* thi = tt + toff.hi;
+        // the transposing operand reads run a step ahead of the products (left to itself the
+        // compiler read each product's operand just before it and waited for it there)
+        bf16x8 opr[2][4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
+        for (int dt = 0; dt < 4; ++dt) opr[0][dt] = t_operand(tlo, thi, dt, 0);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if (st + 1 < 4) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) opr[(st + 1) & 1][dt] = t_operand(tlo, thi, dt, st + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_operand(tlo, thi, dt, st),
-                                                                  ob[st], acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opr[st & 1][dt], ob[st], acc[dt],
+                                                                  0, 0, 0);
+        }
         if (it + 1 < nitems) {
             rows_store(nxt);
             if (tid == 0) list_store(min(it + 2, nitems - 1), it & 1);
