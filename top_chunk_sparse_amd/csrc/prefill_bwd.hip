@@ -17,9 +17,9 @@ namespace tcs {
 // P is recomputed from the forward's lse, so no running max is needed.  Every sum is taken in
 // a fixed order (no floating-point atomics): the same inputs give the same bits.
 //
-//   prefill_bwd_prep_kernel     D for every query row.
-//   prefill_bwd_inverse_kernel  per key block j: the query blocks i > j that chose it,
-//                               ascending, with their gates.
+//   prefill_bwd_prep_kernel     one grid: per key block j the query blocks i > j that chose
+//                               it, ascending, with their gates (the first workgroups); then D
+//                               for every query row.
 //   prefill_bwd_dq_kernel       the forward's work split (unit, i, row half, head group): per
 //                               visible block S^T = K Q^T and dP^T = V dO^T, dS^T = P^T (dP^T - D),
 //                               dQ^T += K^T dS^T, and the block's sum of dS^T (gate partial).
@@ -31,29 +31,50 @@ namespace tcs {
 //                               softmax(S[i][. < i])_j' sum_j dg_ij.
 // =============================================================================================
 
-__global__ void __launch_bounds__(256) prefill_bwd_prep_kernel(PrefillBwdLaunch a) {
+// D of 16 * kPrepU consecutive query rows per workgroup: 16 lanes per row, 16 rows per pass,
+// the loads of all passes issued before the first sum (read once: non-temporal).
+constexpr int kPrepU = 4;
+
+__device__ __forceinline__ void prep_rows(const PrefillBwdLaunch& a, long long wg) {
     const long long rows = (long long)a.B * a.Hq * a.T;
-    const long long row = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4;
     const int l16 = threadIdx.x & 15;
-    if (row >= rows) return;   // whole 16-lane groups leave together
-    const uint4 g = *reinterpret_cast<const uint4*>(a.dout + row * kPD + l16 * 8);
-    const float4 o0 = *reinterpret_cast<const float4*>(a.out + row * kPD + l16 * 8);
-    const float4 o1 = *reinterpret_cast<const float4*>(a.out + row * kPD + l16 * 8 + 4);
-    float x = bf16_lo(g.x) * o0.x + bf16_hi(g.x) * o0.y + bf16_lo(g.y) * o0.z +
-              bf16_hi(g.y) * o0.w + bf16_lo(g.z) * o1.x + bf16_hi(g.z) * o1.y +
-              bf16_lo(g.w) * o1.z + bf16_hi(g.w) * o1.w;
-    x += __shfl_xor(x, 8, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 1, 16);
-    if (l16 == 0) a.D[row] = x - (a.dlse ? a.dlse[row] : 0.f);
+    const long long r0 = wg * (16 * kPrepU) + (threadIdx.x >> 4);
+    u32x4 g[kPrepU], o0[kPrepU], o1[kPrepU];
+#pragma unroll
+    for (int u = 0; u < kPrepU; ++u) {
+        const long long row = min(r0 + 16 * u, rows - 1);   // in bounds; the store is guarded
+        g[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(a.dout + row * kPD + l16 * 8));
+        o0[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(a.out + row * kPD + l16 * 8));
+        o1[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(a.out + row * kPD + l16 * 8 + 4));
+    }
+#pragma unroll
+    for (int u = 0; u < kPrepU; ++u) {
+        const long long row = r0 + 16 * u;
+        float x = bf16_lo(g[u].x) * __uint_as_float(o0[u].x) +
+                  bf16_hi(g[u].x) * __uint_as_float(o0[u].y) +
+                  bf16_lo(g[u].y) * __uint_as_float(o0[u].z) +
+                  bf16_hi(g[u].y) * __uint_as_float(o0[u].w) +
+                  bf16_lo(g[u].z) * __uint_as_float(o1[u].x) +
+                  bf16_hi(g[u].z) * __uint_as_float(o1[u].y) +
+                  bf16_lo(g[u].w) * __uint_as_float(o1[u].z) +
+                  bf16_hi(g[u].w) * __uint_as_float(o1[u].w);
+        x += __shfl_xor(x, 8, 16);
+        x += __shfl_xor(x, 4, 16);
+        x += __shfl_xor(x, 2, 16);
+        x += __shfl_xor(x, 1, 16);
+        if (l16 == 0 && row < rows) a.D[row] = x - (a.dlse ? a.dlse[row] : 0.f);
+    }
 }
 
-__global__ void __launch_bounds__(256) prefill_bwd_inverse_kernel(PrefillBwdLaunch a) {
-    __shared__ ScanSmem scan;
-    __shared__ int total;
+// Per key block j (row = unit * nb + j): the query blocks i > j that chose j, ascending, with
+// the gate of that choice, compacted by a workgroup scan over i.
+__device__ __forceinline__ void inverse_lists(const PrefillBwdLaunch& a, int wg, ScanSmem& scan,
+                                              int& total) {
     const int nb = a.T / kPBlk;
-    const int unit = blockIdx.x / nb, j = blockIdx.x % nb;
+    const int unit = wg / nb, j = wg % nb;
     const long long row = (long long)unit * nb + j;
     int base = 0;
     for (int i0 = j + 1; i0 < nb; i0 += 256) {
@@ -77,6 +98,19 @@ __global__ void __launch_bounds__(256) prefill_bwd_inverse_kernel(PrefillBwdLaun
         __syncthreads();
     }
     if (threadIdx.x == 0) a.inv_n[row] = base;
+}
+
+// One grid for both: the inverse lists' workgroups first (few and latency-bound), then the D
+// rows' (bandwidth-bound), which start as the first lists finish.  (Spread evenly through the
+// grid instead, the lists' workgroups made the launch slower.)
+__global__ void __launch_bounds__(256) prefill_bwd_prep_kernel(PrefillBwdLaunch a) {
+    __shared__ ScanSmem scan;
+    __shared__ int total;
+    const int n_inv = a.B * a.Hkv * (a.T / kPBlk);
+    if ((int)blockIdx.x < n_inv)
+        inverse_lists(a, blockIdx.x, scan, total);
+    else
+        prep_rows(a, (long long)blockIdx.x - n_inv);
 }
 
 // Two workgroups per CU (one would leave one wave per SIMD with nothing to hide its latency),
@@ -539,22 +573,11 @@ hipError_t launch_prefill_bwd_prep(const PrefillBwdLaunch& a, hipStream_t s,
     hipError_t e = bwd_check(a);
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.B * a.Hq * a.T;
-    const long long g1 = (rows * 16 + 255) / 256;
-    const long long g2 = (long long)a.B * a.Hkv * (a.T / kPBlk);
-    if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorNotSupported;
-    if (g1 <= 0 && g2 <= 0) return no_kernel(ev, s);
-    // the events bracket both kernels: start with the first launched, stop with the last
-    if (g1 > 0) {
-        const KernelEvents e1{ev.start, g2 > 0 ? nullptr : ev.stop};
-        if ((e = dispatch(prefill_bwd_prep_kernel, dim3((unsigned)g1), dim3(256), 0, s, e1, a)) !=
-            hipSuccess)
-            return e;
-    }
-    if (g2 > 0) {
-        const KernelEvents e2{g1 > 0 ? nullptr : ev.start, ev.stop};
-        return dispatch(prefill_bwd_inverse_kernel, dim3((unsigned)g2), dim3(256), 0, s, e2, a);
-    }
-    return hipSuccess;
+    const long long g1 = (rows + 16 * kPrepU - 1) / (16 * kPrepU);   // D rows
+    const long long g2 = (long long)a.B * a.Hkv * (a.T / kPBlk);      // inverse lists
+    if (g1 + g2 > 0x7fffffffLL) return hipErrorNotSupported;
+    if (g1 + g2 <= 0) return no_kernel(ev, s);
+    return dispatch(prefill_bwd_prep_kernel, dim3((unsigned)(g1 + g2)), dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s,
