@@ -524,15 +524,16 @@ def run_prefill_backward(args, torch, configs, ops):
     print("# warmup done", file=sys.stderr, flush=True)
     tm = timing_summary(torch, stream, lambda i: calls[i % R](), args.steps)
     ms_per_step = tm["ms_per_step"]
-    # per-kernel durations: select, prep, dq, dk / dv, dS
-    stage_ms = kernel_times(torch, stream, lambda i, arr: calls[i % R](events=arr), args.steps, 5)
+    # per-kernel durations: select, prep (D rows and chosen-by lists), gradients (dq, dk, dv
+    # in one grid), dS
+    stage_ms = kernel_times(torch, stream, lambda i, arr: calls[i % R](events=arr), args.steps, 4)
     print("# stage ms:", [round(x, 4) for x in stage_ms], file=sys.stderr, flush=True)
     flops = prefill_bwd_flops(cfg)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    # dominant kernel: the dk / dv kernel or the dq kernel, whichever takes longer
-    dom = 3 if stage_ms[3] >= stage_ms[2] else 2
-    name, kflops = (("prefill_bwd_dkv_kernel", prefill_bwd_flops(cfg, 4)) if dom == 3 else
-                    ("prefill_bwd_dq_kernel", prefill_bwd_flops(cfg, 3)))
+    # dominant kernel: the gradient kernel, credited with the algorithmic five products per
+    # pair (it executes seven: q.k and dout.v are formed once for dq and once for dk / dv)
+    dom = 2
+    name, kflops = "prefill_bwd_grad_kernel", prefill_bwd_flops(cfg, 5)
     ach = kflops / (stage_ms[dom] * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": name, "achieved": round(ach, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -297,9 +297,8 @@ tcs_status sparse_attn_prefill_backward(const tcs_prefill_params* p,
 
 /* Profiling variant of sparse_attn_prefill_backward (a pair of events per stage, as in
  * sparse_attn_decode_timed): stage 0 block selection, stage 1 the row terms D and the
- * chosen-by lists (two kernels, from the start of the first to the end of the second),
- * stage 2 the dq kernel, stage 3 the dk / dv kernel, stage 4 the dS kernel (none without
- * dS). */
+ * chosen-by lists (one kernel), stage 2 the gradient kernel (dq, dk and dv in one grid),
+ * stage 3 the dS kernel (none without dS). */
 tcs_status sparse_attn_prefill_backward_timed(const tcs_prefill_params* p,
                                               const void* q, const void* k, const void* v,
                                               const float* S, const float* out,

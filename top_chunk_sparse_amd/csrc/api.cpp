@@ -737,8 +737,7 @@ static tcs_status prefill_backward_impl(const tcs_prefill_params* p, const void*
     a.dv = dv;
     a.dS = dS;
     hipError_t e = tcs::launch_prefill_bwd_prep(a, s, clk.next());
-    if (e == hipSuccess) e = tcs::launch_prefill_bwd_dq(a, s, clk.next());
-    if (e == hipSuccess) e = tcs::launch_prefill_bwd_dkv(a, s, clk.next());
+    if (e == hipSuccess) e = tcs::launch_prefill_bwd_grad(a, s, clk.next());
     if (e == hipSuccess) e = tcs::launch_prefill_bwd_ds(a, s, clk.next());
     if (e == hipErrorNotSupported) return TCS_ERR_UNSUPPORTED;
     return e == hipSuccess ? TCS_OK : TCS_ERR_HIP;

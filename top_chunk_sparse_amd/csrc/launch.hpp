@@ -145,6 +145,7 @@ struct PrefillBwdLaunch {
     float* dk;                // [B][Hkv][T][d]
     float* dv;                // [B][Hkv][T][d]
     float* dS;                // [B*Hkv][nb][nb] or null
+    int w_dkv;                // gradient grid: the leading dk / dv workgroups (set by the launch)
 };
 
 // SSA gist-masked prefill over the interleaved sequence (M chunks of L raw + g gist rows).
@@ -171,10 +172,8 @@ hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s,
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t s, const KernelEvents& ev = {});
 hipError_t launch_prefill_bwd_prep(const PrefillBwdLaunch& a, hipStream_t s,
                                    const KernelEvents& ev = {});
-hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s,
-                                 const KernelEvents& ev = {});
-hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s,
-                                  const KernelEvents& ev = {});
+hipError_t launch_prefill_bwd_grad(PrefillBwdLaunch a, hipStream_t s,
+                                   const KernelEvents& ev = {});
 hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s,
                                  const KernelEvents& ev = {});
 

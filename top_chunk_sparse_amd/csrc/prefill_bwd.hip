@@ -119,16 +119,14 @@ __global__ void __launch_bounds__(256) prefill_bwd_prep_kernel(PrefillBwdLaunch 
 // copy and every operand read names its buffer: the compiler's wait counting then lets the
 // operand reads of one buffer run while the next block's copy into the other is in flight.
 // The registers this frees hold the dO^T operand for the whole loop.
-__global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch a) {
-    __shared__ __align__(16) char tile_a[2 * kPTile];   // K then V of one block
-    __shared__ __align__(16) char tile_b[2 * kPTile];
-    __shared__ int ring_j[kRing];
-    __shared__ float ring_g[kRing];
+// One dq item: workgroup bid of the W dq workgroups.  tile_a and tile_b (each 2 kPTile bytes)
+// are two distinct LDS objects of the calling kernel; ring_j and ring_g hold kRing entries.
+__device__ __forceinline__ void bwd_dq_item(const PrefillBwdLaunch& a, int bid, const int W,
+                                            char* tile_a, char* tile_b, int* ring_j,
+                                            float* ring_g) {
     const int G = a.Hq / a.Hkv;
     const int nb = a.T / kPBlk;
     const int nhg = (G + 3) >> 2;
-    int bid = blockIdx.x;
-    const int W = gridDim.x;
     if ((W & 7) == 0) bid = (bid & 7) * (W >> 3) + (bid >> 3);
     const int rh = bid & 1;
     const int i = nb - 1 - (bid >> 1) % nb;
@@ -283,20 +281,19 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dq_kernel(PrefillBwdLaunch
 constexpr int kBwdBuf = 2 * kPTile + 2 * kPBlk * 4;   // Q tile, dO tile, lse2 and D of 64 rows
 constexpr int kBwdP = 4 * 64 * 16;                    // P of 32 keys x 64 rows, fp16
 
-__global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunch a) {
-    // two pair buffers (distinct LDS objects: see the dq kernel), the P hand-over, the list slots
-    __shared__ __align__(16) char buf_a[kBwdBuf];
-    __shared__ __align__(16) char buf_b[kBwdBuf];
-    __shared__ __align__(16) char pshare[2 * kBwdP];
-    __shared__ int slot_i[2];
-    __shared__ float slot_g[2];
+// One dk / dv item: workgroup bid of the B Hkv nb dk / dv workgroups.  buf_a and buf_b (each
+// kBwdBuf bytes: two pair buffers, distinct LDS objects of the calling kernel, see the dq
+// item), pshare (2 kBwdP bytes: the P hand-over) and the two list slots.
+__device__ __forceinline__ void bwd_dkv_item(const PrefillBwdLaunch& a, const int bid,
+                                             char* buf_a, char* buf_b, char* pshare,
+                                             int* slot_i, float* slot_g) {
     const int G = a.Hq / a.Hkv;
     const int nb = a.T / kPBlk;
     const int units = a.B * a.Hkv;
     // key-block major: the blocks that most query blocks choose (low j) start first, and with
     // eight KV heads each XCD keeps one head's queries in its L2
-    const int j = blockIdx.x / units;
-    const int unit = blockIdx.x % units;
+    const int j = bid / units;
+    const int unit = bid % units;
     const int b = unit / a.Hkv, kv = unit % a.Hkv;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -515,6 +512,30 @@ __global__ void __launch_bounds__(256, 2) prefill_bwd_dkv_kernel(PrefillBwdLaunc
                    (roleA ? a.dv : a.dk) + kfirst * kPD, lane);
 }
 
+// dq and dk / dv in one grid.  Neither reads what the other writes (both take the row terms D
+// and the chosen-by lists of the prep pass), so no workgroup waits for another.  The dk / dv
+// workgroups come first: they are the long items (the most-chosen key blocks lead), and the
+// shorter dq workgroups then fill the CU slots they leave, so neither part's tail runs on an
+// otherwise idle GPU and one launch boundary goes.  Both parts use the same LDS objects, so the
+// kernel keeps two workgroups per CU.
+static_assert(kBwdBuf >= 2 * kPTile, "a dk / dv pair buffer holds a dq K / V block");
+static_assert(2 * kBwdP >= kRing * (int)(sizeof(int) + sizeof(float)), "dq block-list ring");
+__global__ void __launch_bounds__(256, 2) prefill_bwd_grad_kernel(PrefillBwdLaunch a) {
+    __shared__ __align__(16) char buf_a[kBwdBuf];
+    __shared__ __align__(16) char buf_b[kBwdBuf];
+    __shared__ __align__(16) char pshare[2 * kBwdP];   // dk / dv: P hand-over; dq: block list
+    __shared__ int slot_i[2];
+    __shared__ float slot_g[2];
+    const int wk = a.w_dkv;
+    if ((int)blockIdx.x < wk) {
+        bwd_dkv_item(a, blockIdx.x, buf_a, buf_b, pshare, slot_i, slot_g);
+    } else {
+        bwd_dq_item(a, blockIdx.x - wk, gridDim.x - wk, buf_a, buf_b,
+                    reinterpret_cast<int*>(pshare),
+                    reinterpret_cast<float*>(pshare + kRing * sizeof(int)));
+    }
+}
+
 __global__ void __launch_bounds__(256) prefill_bwd_ds_kernel(PrefillBwdLaunch a) {
     __shared__ ReduceSmem red;
     const int G = a.Hq / a.Hkv;
@@ -580,25 +601,16 @@ hipError_t launch_prefill_bwd_prep(const PrefillBwdLaunch& a, hipStream_t s,
     return dispatch(prefill_bwd_prep_kernel, dim3((unsigned)(g1 + g2)), dim3(256), 0, s, ev, a);
 }
 
-hipError_t launch_prefill_bwd_dq(const PrefillBwdLaunch& a, hipStream_t s,
-                                 const KernelEvents& ev) {
+hipError_t launch_prefill_bwd_grad(PrefillBwdLaunch a, hipStream_t s, const KernelEvents& ev) {
     hipError_t e = bwd_check(a);
     if (e != hipSuccess) return e;
     const int G = a.Hq / a.Hkv;
-    const long long W = 2LL * a.B * a.Hkv * (a.T / kPBlk) * ((G + 3) / 4);
-    if (W <= 0) return no_kernel(ev, s);
-    if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    return dispatch(prefill_bwd_dq_kernel, dim3((unsigned)W), dim3(256), 0, s, ev, a);
-}
-
-hipError_t launch_prefill_bwd_dkv(const PrefillBwdLaunch& a, hipStream_t s,
-                                  const KernelEvents& ev) {
-    hipError_t e = bwd_check(a);
-    if (e != hipSuccess) return e;
-    const long long W = (long long)a.B * a.Hkv * (a.T / kPBlk);
-    if (W <= 0) return no_kernel(ev, s);
-    if (W > 0x7fffffffLL) return hipErrorNotSupported;
-    return dispatch(prefill_bwd_dkv_kernel, dim3((unsigned)W), dim3(256), 0, s, ev, a);
+    const long long Wq = 2LL * a.B * a.Hkv * (a.T / kPBlk) * ((G + 3) / 4);   // dq
+    const long long Wk = (long long)a.B * a.Hkv * (a.T / kPBlk);               // dk / dv
+    if (Wq + Wk <= 0) return no_kernel(ev, s);
+    if (Wq + Wk > 0x7fffffffLL) return hipErrorNotSupported;
+    a.w_dkv = (int)Wk;
+    return dispatch(prefill_bwd_grad_kernel, dim3((unsigned)(Wq + Wk)), dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_prefill_bwd_ds(const PrefillBwdLaunch& a, hipStream_t s,
