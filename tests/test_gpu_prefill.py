@@ -87,6 +87,13 @@ VARIANTS = [
     SMALL.with_(Hq=16, Hkv=2),                 # G = 8: two head groups per block
     SMALL.with_(T=64),                         # a single block
     SMALL.with_(B=3, Hq=4, Hkv=1, T=640, k=7),
+    # More workgroups than the GPU holds at once (two per CU): 1,024 (2,048 with two head
+    # groups), compared in full.
+    SMALL.with_(T=8192),
+    SMALL.with_(T=8192, gate=0),
+    SMALL.with_(T=8192, k=0),
+    SMALL.with_(T=8192, k=200, gate=0),        # every earlier block: lists of up to 127
+    SMALL.with_(T=8192, Hq=16),                # G = 8: the head group changes between items
 ]
 
 

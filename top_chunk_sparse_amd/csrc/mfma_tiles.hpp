@@ -177,6 +177,12 @@ __device__ __forceinline__ bf16x8 t_operand(const char* lo, const char* hi, int 
 // both ways), then read in the operand layout; a direct operand load would fetch 32-byte
 // pieces of 32 rows per instruction.
 constexpr int kQRowsLds = 32 * kPD * 2;
+// Lanes read what other lanes of the wave wrote to LDS: the wavefront-scope fence says so to
+// the compiler (without it a lane may take its read from an earlier read of the same bytes,
+// as if only it wrote them).  It emits no instruction.
+__device__ __forceinline__ void wave_lds_handoff() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+}
 __device__ __forceinline__ void load_q_operand(const uint16_t* rows, char* lds_w, int lane,
                                                bf16x8 (&qf)[8]) {
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -190,6 +196,7 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* rows, char* lds_w
         const int r = 4 * k + (lane >> 4), u = lane & 15;
         *reinterpret_cast<u32x4*>(lds_w + r * 256 + ((u ^ (r & 15)) << 4)) = x[k];
     }
+    wave_lds_handoff();
     const int c32 = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int kd = 0; kd < 8; ++kd)
@@ -224,6 +231,7 @@ __device__ __forceinline__ void store_rows_f32(const f32x16 (&o)[4], float inv, 
             v.w = o[dt][4 * e4 + 3] * inv;
             *reinterpret_cast<float4*>(lds_w + c32 * 512 + ((u ^ c32) << 4)) = v;
         }
+    wave_lds_handoff();
     const int u = lane & 31;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
