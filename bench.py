@@ -87,8 +87,8 @@ def prefill_flops(cfg):
 
 def prefill_bwd_flops(cfg, products=5):
     """Algorithmic FLOPs of the gradients: 2 d per attended pair for each product -- q.k and
-    dout.v recomputed, and the dq, dk and dv products (5; the dq kernel alone does 3: q.k,
-    dout.v, dq; the dk / dv kernel 4: q.k, dout.v, dk, dv)."""
+    dout.v recomputed, and the dq, dk and dv products (5; the gradient kernel's dq part alone
+    does 3: q.k, dout.v, dq; its dk / dv part 4: q.k, dout.v, dk, dv)."""
     return 2 * products * cfg.d * prefill_pairs(cfg)
 
 

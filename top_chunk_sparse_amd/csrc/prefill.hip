@@ -57,9 +57,105 @@ __global__ void __launch_bounds__(256) prefill_select_kernel(PrefillSelectLaunch
     }
 }
 
+// The same selection with one wave per query block, for rows of at most 256 candidates (four
+// per lane, candidate j on lane j % 64, register j / 64): no workgroup barrier anywhere.
+// The k-th largest ordered key T is found bit by bit from the top (a bit is kept when at
+// least k keys reach the prefix with it set), counted with ballots; every key above T is
+// taken, then the keys equal to T in ascending position until k are taken.  Positions are
+// written in ascending order: a chosen candidate's slot is the number of chosen ones before
+// it, from the ballots' prefix counts.
+__global__ void __launch_bounds__(256) prefill_select_wave_kernel(PrefillSelectLaunch a) {
+    const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);   // (unit * nb + i)
+    if (row >= a.units * a.nb) return;                          // wave-uniform, no barriers
+    const int lane = threadIdx.x & 63;
+    const int i = row % a.nb;
+    const float* s = a.S + (long long)row * a.nb;   // S[unit][i][0..nb)
+    int32_t* sel = a.sel + (long long)row * a.k;
+    float* gam = a.gamma ? a.gamma + (long long)row * a.k : nullptr;
+    float v[4];
+    bool ok[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int j = 64 * m + lane;
+        ok[m] = j < i;
+        v[m] = ok[m] ? s[j] : 0.f;
+    }
+    float lse = 0.f;
+    if (gam && i > 0) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) mx = fmaxf(mx, ok[m] ? v[m] : -INFINITY);
+        mx = wave_max(mx);
+        float z = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) z += ok[m] ? expf(v[m] - mx) : 0.f;
+        z = wave_sum(z);
+        lse = mx + logf(z);
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;   // lanes before this one
+    if (a.k >= i) {   // every earlier block is chosen: no ranking needed
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (ok[m]) {
+                const int j = 64 * m + lane;
+                sel[j] = j;
+                if (gam) gam[j] = v[m] - lse;
+            }
+    } else {
+        const int ke = a.k;   // < i
+        uint32_t key[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) key[m] = ordered_key(v[m]);
+        auto count_ge = [&](uint32_t t) {
+            int c = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok[m] && key[m] >= t));
+            return c;
+        };
+        uint32_t T = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            if (count_ge(cand) >= ke) T = cand;
+        }
+        int gt = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            gt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok[m] && key[m] > T));
+        const int take_eq = ke - gt;   // >= 1: at least ke keys reach T, fewer exceed it
+        int base = 0, eq_base = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const unsigned long long eqm = __builtin_amdgcn_ballot_w64(ok[m] && key[m] == T);
+            const bool tie_taken =
+                ((eqm >> lane) & 1ull) && eq_base + __builtin_popcountll(eqm & below) < take_eq;
+            const bool take = (ok[m] && key[m] > T) || tie_taken;
+            const unsigned long long tm = __builtin_amdgcn_ballot_w64(take);
+            if (take) {
+                const int pos = base + __builtin_popcountll(tm & below);
+                const int j = 64 * m + lane;
+                sel[pos] = j;
+                if (gam) gam[pos] = v[m] - lse;
+            }
+            base += __builtin_popcountll(tm);
+            eq_base += __builtin_popcountll(eqm);
+        }
+    }
+    const int ke = a.k < i ? a.k : i;
+    for (int x = ke + lane; x < a.k; x += 64) {
+        sel[x] = -1;
+        if (gam) gam[x] = 0.f;
+    }
+}
+
 hipError_t launch_prefill_select(const PrefillSelectLaunch& a, hipStream_t s,
                                  const KernelEvents& ev) {
     if (a.units <= 0 || a.nb <= 0 || a.k <= 0) return no_kernel(ev, s);
+    if (a.nb <= 257) {   // at most 256 candidates per row
+        const long long rows = (long long)a.units * a.nb;
+        return dispatch(prefill_select_wave_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                        0, s, ev, a);
+    }
     return dispatch(prefill_select_kernel, dim3(a.units * a.nb), dim3(256), 0, s, ev, a);
 }
 

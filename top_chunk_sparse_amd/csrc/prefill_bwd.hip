@@ -119,8 +119,12 @@ __global__ void __launch_bounds__(256) prefill_bwd_prep_kernel(PrefillBwdLaunch 
 // copy and every operand read names its buffer: the compiler's wait counting then lets the
 // operand reads of one buffer run while the next block's copy into the other is in flight.
 // The registers this frees hold the dO^T operand for the whole loop.
+//
 // One dq item: workgroup bid of the W dq workgroups.  tile_a and tile_b (each 2 kPTile bytes)
 // are two distinct LDS objects of the calling kernel; ring_j and ring_g hold kRing entries.
+// The XCD-contiguous ranges below take bid's XCD as bid % 8, which holds in the gradient grid
+// when the dk / dv workgroups ahead of it are a multiple of 8 (8 KV heads or B Hkv nb % 8 == 0;
+// otherwise only the L2 grouping is lost).
 __device__ __forceinline__ void bwd_dq_item(const PrefillBwdLaunch& a, int bid, const int W,
                                             char* tile_a, char* tile_b, int* ring_j,
                                             float* ring_g) {
