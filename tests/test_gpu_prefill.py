@@ -60,6 +60,21 @@ def test_prefill_full_size_sampled():
     torch.cuda.empty_cache()
 
 
+def test_prefill_rows_past_256_candidates():
+    # 272 blocks: rows of more than 256 earlier blocks are ranked by the workgroup selection
+    # kernel (shorter rows by the one-wave kernel); the selection property is checked on every
+    # row, selections and outputs on sampled blocks of both kinds against the oracle
+    cfg = PrefillConfig("gpu_prefill_272_blocks", B=1, Hq=4, Hkv=2, d=128, T=272 * 64, blk=64,
+                        k=20, gate=1)
+    nb = cfg.nb
+    blocks = [u * nb + i for u in range(cfg.B * cfg.Hkv)
+              for i in (0, 5, 21, 100, 255, 256, 257, 258, 263, nb - 1)]
+    inp, call, st = run_case(cfg, 89, blocks=blocks)
+    assert st["excused"] == 0
+    del inp, call
+    torch.cuda.empty_cache()
+
+
 def test_prefill_long_block_lists():
     # more than 128 chosen blocks per query block: the kernel's block-list ring (128 entries) is
     # refilled while it runs; sampled late blocks (up to 150 chosen) against the oracle
