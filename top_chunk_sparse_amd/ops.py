@@ -98,11 +98,9 @@ STREAM_READ_BLOCKS = 4096   # TCS_STREAM_READ_BLOCKS
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     """Enqueue a plain streaming read of ``src`` (the HBM read ceiling; measurement only)."""
-    if stream is None:
-        stream = torch.cuda.current_stream(src.device)
     assert sink.numel() * sink.element_size() >= 4 * STREAM_READ_BLOCKS
     _check(lib().tcs_stream_read(_p(src), src.numel() * src.element_size(), _p(sink),
-                                 stream.cuda_stream))
+                                 _stream_handle(stream, src)))
 
 
 def status_str(code: int) -> str:
@@ -116,6 +114,18 @@ def _check(code):
 
 def _p(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream, like: torch.Tensor) -> int:
+    """The raw hipStream_t of ``stream``, or of torch's current stream on ``like``'s device (read
+    without building a Stream object: this lookup is most of a call's host time otherwise)."""
+    if stream is not None:
+        return stream.cuda_stream
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get is None:
+        return torch.cuda.current_stream(like.device).cuda_stream
+    idx = like.device.index
+    return get(idx if idx is not None else torch.cuda.current_device())
 
 
 GISTS_ALL, GISTS_SELECTED = 0, 1   # TCS_GISTS_*
@@ -145,13 +155,11 @@ def sparse_attn_decode(p: DecodeParams, q, k_pages, v_pages, page_table, gist_k,
                        chunk_scores=None, workspace, stream=None, events=None) -> None:
     """Enqueue one decode call on ``stream`` (default: torch's current stream).  ``events``:
     optional ctypes array of raw hipEvent_t handles for the per-kernel timing variant."""
-    if stream is None:
-        stream = torch.cuda.current_stream(out.device)
     args = (C.byref(p), _p(q), _p(k_pages), _p(v_pages), _p(page_table), _p(gist_k), _p(gist_v),
             _p(gist2_k), _p(gist2_v), _p(out), _p(lse), _p(sel), _p(sel_groups), _p(chunk_scores),
             _p(workspace),
             workspace.numel() * workspace.element_size() if workspace is not None else 0,
-            stream.cuda_stream)
+            _stream_handle(stream, out))
     if events is None:
         code = lib().sparse_attn_decode(*args)
     else:
@@ -164,12 +172,10 @@ def sparse_attn_decode_noalloc(p: DecodeParams, q, k_pages, v_pages, page_table,
                                sel_groups=None, chunk_scores=None, stream=None) -> None:
     """sparse_attn_decode without a workspace: the library's static per-GPU scratch serves
     instead (for callers that cannot allocate)."""
-    if stream is None:
-        stream = torch.cuda.current_stream(out.device)
     _check(lib().sparse_attn_decode_noalloc(
         C.byref(p), _p(q), _p(k_pages), _p(v_pages), _p(page_table), _p(gist_k), _p(gist_v),
         _p(gist2_k), _p(gist2_v), _p(out), _p(lse), _p(sel), _p(sel_groups), _p(chunk_scores),
-        stream.cuda_stream))
+        _stream_handle(stream, out)))
 
 
 def decode_stage_count(p: DecodeParams) -> int:
@@ -189,11 +195,9 @@ def prefill_workspace_size(p: PrefillParams) -> int:
 
 def sparse_attn_prefill(p: PrefillParams, q, k, v, S, *, out, lse=None, sel=None, workspace,
                         stream=None, events=None) -> None:
-    if stream is None:
-        stream = torch.cuda.current_stream(out.device)
     args = (C.byref(p), _p(q), _p(k), _p(v), _p(S), _p(out), _p(lse), _p(sel), _p(workspace),
             workspace.numel() * workspace.element_size() if workspace is not None else 0,
-            stream.cuda_stream)
+            _stream_handle(stream, out))
     if events is None:
         code = lib().sparse_attn_prefill(*args)
     else:
@@ -211,12 +215,10 @@ def sparse_attn_prefill_backward(p: PrefillParams, q, k, v, S, out, lse, dout, d
                                  dq, dk, dv, dS=None, workspace, stream=None,
                                  events=None) -> None:
     """Enqueue the prefill gradients on ``stream`` (default: torch's current stream)."""
-    if stream is None:
-        stream = torch.cuda.current_stream(dq.device)
     args = (C.byref(p), _p(q), _p(k), _p(v), _p(S), _p(out), _p(lse), _p(dout), _p(dlse),
             _p(dq), _p(dk), _p(dv), _p(dS), _p(workspace),
             workspace.numel() * workspace.element_size() if workspace is not None else 0,
-            stream.cuda_stream)
+            _stream_handle(stream, dq))
     if events is None:
         code = lib().sparse_attn_prefill_backward(*args)
     else:
@@ -237,11 +239,9 @@ def gist_prefill_workspace_size(p: GistPrefillParams) -> int:
 
 def sparse_attn_gist_prefill(p: GistPrefillParams, q, k, v, *, out, lse=None, workspace,
                              stream=None, events=None) -> None:
-    if stream is None:
-        stream = torch.cuda.current_stream(out.device)
     args = (C.byref(p), _p(q), _p(k), _p(v), _p(out), _p(lse), _p(workspace),
             workspace.numel() * workspace.element_size() if workspace is not None else 0,
-            stream.cuda_stream)
+            _stream_handle(stream, out))
     if events is None:
         code = lib().sparse_attn_gist_prefill(*args)
     else:
@@ -253,9 +253,7 @@ def workspace(nbytes: int, device, stream=None) -> torch.Tensor:
     """A caller-owned workspace (256-byte aligned by the torch allocator), zero-filled by the
     library's init kernel as a new decode workspace must be."""
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
-    if stream is None:
-        stream = torch.cuda.current_stream(ws.device)
-    _check(lib().tcs_workspace_init(ws.data_ptr(), ws.numel(), stream.cuda_stream))
+    _check(lib().tcs_workspace_init(ws.data_ptr(), ws.numel(), _stream_handle(stream, ws)))
     return ws
 
 
