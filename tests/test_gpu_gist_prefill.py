@@ -53,6 +53,9 @@ CASES = [
     SMALL.with_(B=2, M=3),
     SMALL.with_(M=40, g=4),                  # 160 gists: a prefix of 3 blocks, the last partial
     SMALL.with_(M=17, L=192, g=16),
+    # 1,024 raw-row workgroups (B = 2, two head groups) behind the gist rows': more than the
+    # GPU holds at once, every row compared
+    SMALL.with_(B=2, Hq=16, M=64),
 ]
 
 

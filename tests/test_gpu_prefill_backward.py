@@ -75,6 +75,9 @@ CASES = [
     (BASE, False),                                  # no dlse
     (BASE.with_(B=2, T=64 * 4), True),
     (BASE.with_(T=64), True),                       # one block
+    # 128 dk / dv and 512 dq workgroups with two head groups: more than the GPU holds at
+    # once, so the gradient grid's dq part starts as the dk / dv part drains
+    (BASE.with_(Hq=16, T=64 * 64, k=4), True),
 ]
 
 
