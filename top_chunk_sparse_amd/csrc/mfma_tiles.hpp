@@ -23,8 +23,6 @@ constexpr int kPBlk = 64;                    // block rows
 constexpr int kPSub = 64 * 64;               // bytes per 32-dim sub-tile (64 rows x 64 B)
 constexpr int kPTile = 4 * kPSub;            // bytes per K or V block
 constexpr int kRing = 128;                   // entries of the chosen-block ring (power of 2)
-constexpr int kPLds = 4 * kPTile;            // K0 K1 V0 V1
-constexpr int kPLdsAll = kPLds + kRing * 8;  // + the ring (block ids, gates)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;         // log2 units a stale running max may lag
@@ -202,12 +200,6 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* rows, char* lds_w
     for (int kd = 0; kd < 8; ++kd)
         qf[kd] = *reinterpret_cast<const bf16x8*>(lds_w + c32 * 256 + (((2 * kd + h) ^ (c32 & 15)) << 4));
 }
-// LDS of wave w's query transpose inside tile buffer 1 (K1 for waves 0, 1; V1 for 2, 3), free
-// while block 0 is staged into buffer 0
-__device__ __forceinline__ char* q_stage_lds(char* lds, int w) {
-    return lds + (w < 2 ? kPTile + w * kQRowsLds : 3 * kPTile + (w - 2) * kQRowsLds);
-}
-
 // Output of one wave: 32 query rows x 128 dims, O^T accumulators in the product layout (lane
 // l: row l % 32, dims 32 dt + 8 e4 + 4 (l / 32) .. + 3 in o[dt][4 e4 ..]).  Written scaled by
 // the lane's inv through this wave's 16 KB of LDS (row r at 512 r, 16-byte unit u at u ^ r,
