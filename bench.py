@@ -11,8 +11,17 @@ last-level cache cannot serve them.  Prints one JSON line.
 --workload sas_prefill_16k: one step = one sparse_attn_prefill call (block selection + the
 MFMA block-sparse causal forward) on B=1, Hq=32, Hkv=8, d=128, T=16384, 64-token blocks,
 top-16 earlier blocks + the diagonal block, SAS gate; reported as algorithmic TFLOP/s.
+Add --backward for one sparse_attn_prefill_backward call per step (dq, dk, dv, dS).
 
-    python bench.py [--steps K] [--warmup W] [--instances R] [--workload NAME]
+--workload ssa_gist_prefill_16k: one step = one sparse_attn_gist_prefill call over 128 chunks
+of 128 raw tokens + 4 gists (16,896 positions), same heads; algorithmic TFLOP/s, with the row
+launch measured against the HBM roofline.
+
+Every workload: a sustained loop first, then the median of 5 loops of exactly --steps calls
+(wall clock between device synchronisations), per-kernel event times, the roofline of the
+dominant kernel, and the fp64 CPU oracle timed on the host.
+
+    python bench.py [--steps K] [--warmup W] [--instances R] [--workload NAME] [--backward]
                     [--no-cpu-baseline] [--cpu-seconds S]
 """
 import argparse
@@ -134,11 +143,11 @@ def timed_loops(torch, stream, step, steps, loops=LOOPS):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        e0.record(stream)   # instrumentation, outside the wall-clock bracket of the K steps
         t0 = time.perf_counter()
-        e0.record(stream)
         for i in range(steps):
             step(i)
-        e1.record(stream)
+        e1.record(stream)   # queued behind the steps while the GPU is still busy with them
         torch.cuda.synchronize()
         out.append(((time.perf_counter() - t0) * 1e3, e0.elapsed_time(e1)))
     return out
